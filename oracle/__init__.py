@@ -1,0 +1,183 @@
+"""Reference SGEMM oracle -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library under
+``fp32_gemm_major_amd/`` and its binding) never imports it, and the two share
+no code.
+
+This module is argument marshalling around ``sgemm_oracle.c`` (plain C, FP64
+accumulation, compiled with gcc -O2 and no fast-math).  What it computes is
+the definition of the operation on the page "GEMM 优化之路", section on the
+problem statement and performance limit: ``C = alpha*A*B + beta*C`` with
+row-major FP32 operands, A M x K, B K x N, C M x N.  See the C source for the
+exact arithmetic.  Results come back unrounded (FP64) as ``r``; the FP32
+result of the operation is ``r`` rounded to nearest-even (``to_f32``).
+
+Pins (tests/test_oracle_pins.py) tie it to exact rational brute force, integer
+arithmetic, identity and permutation matrices, the rank-1 closed form and the
+alpha/beta semantics, none of which share code with it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "sgemm_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+# gcc flags: plain -O2, IEEE semantics (no -ffast-math, no FMA contraction
+# of the additions is possible since every product is exact in FP64).
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-pthread", "-fno-fast-math"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def compile_library(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile ``source`` with gcc into the shared library ``output``."""
+    tmp = output + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, "-o", tmp, source, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, output)
+    return output
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle in place (always, unless ``force`` is False and it exists)."""
+    global _lib
+    with _lock:
+        if force or not os.path.exists(LIBRARY):
+            compile_library()
+        _lib = None
+    return LIBRARY
+
+
+def _bind(lib):
+    f = ctypes.c_float
+    i = ctypes.c_int
+    p = ctypes.c_void_p
+    lib.oracle_sgemm.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p, i, p, i, i]
+    lib.oracle_sgemm.restype = i
+    lib.oracle_sgemm_points.argtypes = [i, i, i, f, p, i, p, i, f, p, i, i, p, p,
+                                        p, p, i]
+    lib.oracle_sgemm_points.restype = i
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the compiled oracle (building it first only if it is missing)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                compile_library()
+            _lib = _bind(ctypes.CDLL(LIBRARY))
+        return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f32(x, name):
+    a = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data if a is not None and a.size else None
+
+
+def _need(buf, rows, ld, cols, name):
+    """Size a flat operand must have to hold ``rows`` rows of ``cols`` at stride ``ld``."""
+    need = 0 if rows == 0 or cols == 0 else (rows - 1) * ld + cols
+    if buf.size < need:
+        raise ValueError(f"{name}: {buf.size} elements, need {need}")
+
+
+def gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
+         nthreads=None, lib=None):
+    """Full product.  Returns ``(r, t)``: FP64 arrays of shape (M, N).
+
+    ``A``, ``B``, ``C`` are flat (or any-shape contiguous) FP32 buffers read at
+    the given leading dimensions; ``C`` may be None when ``beta == 0``.
+    ``t`` is None when ``with_t`` is False.
+    """
+    lib = lib or load()
+    A = _f32(A, "A")
+    B = _f32(B, "B")
+    _need(A, M, lda, K, "A")
+    _need(B, K, ldb, N, "B")
+    if C is not None:
+        C = _f32(C, "C")
+        if beta != 0:
+            _need(C, M, ldc, N, "C")
+    elif beta != 0:
+        raise ValueError("C is required when beta != 0")
+    R = np.zeros((M, N), dtype=np.float64)
+    T = np.zeros((M, N), dtype=np.float64) if with_t else None
+    rc = lib.oracle_sgemm(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                          float(beta), _ptr(C), ldc, _ptr(R), max(N, 1),
+                          _ptr(T), max(N, 1), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_sgemm rejected the arguments (code {rc})")
+    return R, T
+
+
+def gemm_points(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
+                nthreads=None, lib=None):
+    """Outputs at (rows[p], cols[p]) only.  Returns ``(r, t)`` FP64 vectors."""
+    lib = lib or load()
+    A = _f32(A, "A")
+    B = _f32(B, "B")
+    _need(A, M, lda, K, "A")
+    _need(B, K, ldb, N, "B")
+    if C is not None:
+        C = _f32(C, "C")
+    elif beta != 0:
+        raise ValueError("C is required when beta != 0")
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1)
+    cols = np.ascontiguousarray(cols, dtype=np.int32).reshape(-1)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    n = rows.size
+    r = np.zeros(n, dtype=np.float64)
+    t = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_sgemm_points(M, N, K, float(alpha), _ptr(A), lda, _ptr(B),
+                                 ldb, float(beta), _ptr(C), ldc, n, _ptr(rows),
+                                 _ptr(cols), _ptr(r), _ptr(t),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_sgemm_points rejected the arguments (code {rc})")
+    return r, t
+
+
+def to_f32(r):
+    """Round FP64 results to FP32, nearest-even (the oracle's FP32 output)."""
+    return np.asarray(r, dtype=np.float64).astype(np.float32)
+
+
+def error_bound(K, alpha, beta, t, c_in):
+    """Per-element acceptance bound for an FP32 result against unrounded r.
+
+    |C_gpu - r| <= 4 * max(K, 1) * 2**-24 * (|alpha| * t + |beta * c|), with the
+    beta term taken as 0 when beta == 0 (C is then not read and may hold NaN).
+    The form is the standard a-priori bound for a length-K FP32 dot product
+    (gamma_K = K*u/(1 - K*u), u = 2**-24) widened to cover the few roundings of
+    the alpha/beta update.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    scale = abs(float(alpha)) * t
+    if beta != 0:
+        scale = scale + np.abs(float(beta) * np.asarray(c_in, dtype=np.float64))
+    return 4.0 * max(int(K), 1) * 2.0 ** -24 * scale

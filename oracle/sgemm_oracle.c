@@ -1,0 +1,174 @@
+/*
+ * Reference SGEMM oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the CPU-baseline leg of the benchmark
+ * may load this library.  The product path (the HIP library and its Python
+ * binding) never calls it and shares no code with it.
+ *
+ * What it computes is the plain definition of the operation from the page
+ * "GEMM 优化之路" (section on the problem statement and performance limit):
+ * C = alpha * A * B + beta * C, with A of size M x K, B of size K x N and C of
+ * size M x N, all row-major FP32.  Leading dimensions are explicit here
+ * (A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j]); the
+ * page uses the minimal ones (K, N, N).
+ *
+ * Arithmetic is FP64 throughout:
+ *   s_ij = sum over k = 0 .. K-1, ascending, of (double)A(i,k) * (double)B(k,j)
+ *          with one accumulator per output element;
+ *   t_ij = sum over the same k of |(double)A(i,k) * (double)B(k,j)|;
+ *   r_ij = (double)alpha * s_ij            if beta == 0 (C is not read),
+ *          (double)alpha * s_ij + (double)beta * (double)C(i,j)   otherwise.
+ * The product of two FP32 numbers is exact in FP64 (24 + 24 <= 53 bits), so
+ * only the additions round.  r_ij is returned unrounded; the caller rounds it
+ * to FP32 when it needs the FP32 result.
+ *
+ * The loop nest follows the CPU reference on the same page (its complete
+ * listing): rows outer, then k, then columns, with a row of accumulators.
+ * Threads split the rows; nothing else is blocked, fused or reordered.
+ * Build with plain -O2 and no -ffast-math so the compiler may not reassociate
+ * the per-element sums.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int M, N, K;
+  double alpha, beta;
+  const float *A, *B, *C;
+  long lda, ldb, ldc;
+  double *R, *T;
+  long ldr, ldt;
+  /* point mode */
+  int npts;
+  const int *rows, *cols;
+  /* work split */
+  int first, last;
+} job_t;
+
+/* Rows [first, last) of the full product. */
+static void *full_rows(void *arg) {
+  job_t *j = (job_t *)arg;
+  for (int i = j->first; i < j->last; ++i) {
+    double *r = j->R + (long)i * j->ldr;
+    double *t = j->T ? j->T + (long)i * j->ldt : NULL;
+    for (int c = 0; c < j->N; ++c) r[c] = 0.0;
+    if (t)
+      for (int c = 0; c < j->N; ++c) t[c] = 0.0;
+    for (int k = 0; k < j->K; ++k) {
+      const double a = (double)j->A[(long)i * j->lda + k];
+      const float *brow = j->B + (long)k * j->ldb;
+      for (int c = 0; c < j->N; ++c) {
+        const double p = a * (double)brow[c];
+        r[c] += p;
+        if (t) t[c] += fabs(p);
+      }
+    }
+    for (int c = 0; c < j->N; ++c) {
+      double v = j->alpha * r[c];
+      if (j->beta != 0.0) v += j->beta * (double)j->C[(long)i * j->ldc + c];
+      r[c] = v;
+    }
+  }
+  return NULL;
+}
+
+/* Points [first, last) of the point list: one dot product each. */
+static void *points(void *arg) {
+  job_t *j = (job_t *)arg;
+  for (int p = j->first; p < j->last; ++p) {
+    const int i = j->rows[p], c = j->cols[p];
+    double s = 0.0, a = 0.0;
+    for (int k = 0; k < j->K; ++k) {
+      const double q = (double)j->A[(long)i * j->lda + k] *
+                       (double)j->B[(long)k * j->ldb + c];
+      s += q;
+      a += fabs(q);
+    }
+    double v = j->alpha * s;
+    if (j->beta != 0.0) v += j->beta * (double)j->C[(long)i * j->ldc + c];
+    j->R[p] = v;
+    if (j->T) j->T[p] = a;
+  }
+  return NULL;
+}
+
+static int check_args(int M, int N, int K, int lda, int ldb, int ldc) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  if (lda < (K > 1 ? K : 1)) return -2;
+  if (ldb < (N > 1 ? N : 1)) return -2;
+  if (ldc < (N > 1 ? N : 1)) return -2;
+  return 0;
+}
+
+static void run_split(void *(*fn)(void *), job_t *proto, int count,
+                      int nthreads) {
+  if (count <= 0) return;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > count) nthreads = count;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t tid[256];
+  job_t jobs[256];
+  int started[256];
+  for (int w = 0; w < nthreads; ++w) {
+    jobs[w] = *proto;
+    jobs[w].first = (int)((long)count * w / nthreads);
+    jobs[w].last = (int)((long)count * (w + 1) / nthreads);
+    started[w] = (w > 0) && pthread_create(&tid[w], NULL, fn, &jobs[w]) == 0;
+    if (w > 0 && !started[w]) fn(&jobs[w]); /* no thread: run inline */
+  }
+  fn(&jobs[0]);
+  for (int w = 1; w < nthreads; ++w)
+    if (started[w]) pthread_join(tid[w], NULL);
+}
+
+/*
+ * Full product.  R receives r_ij (ldr >= N), T receives t_ij (ldt >= N) or is
+ * NULL to skip the magnitude sum (the timing mode).  Returns 0, or -1 for a
+ * negative size, -2 for a leading dimension that is too small.
+ */
+int oracle_sgemm(int M, int N, int K, float alpha, const float *A, int lda,
+                 const float *B, int ldb, float beta, const float *C, int ldc,
+                 double *R, int ldr, double *T, int ldt, int nthreads) {
+  int e = check_args(M, N, K, lda, ldb, ldc);
+  if (e) return e;
+  if (ldr < N || (T && ldt < N)) return -2;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.M = M; j.N = N; j.K = K;
+  j.alpha = (double)alpha; j.beta = (double)beta;
+  j.A = A; j.B = B; j.C = C;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.R = R; j.T = T; j.ldr = ldr; j.ldt = ldt;
+  if (N > 0) run_split(full_rows, &j, M, nthreads);
+  return 0;
+}
+
+/*
+ * Selected outputs (rows[p], cols[p]) for p < npts, each an independent dot
+ * product with the same definition as above; r_out[p] = r_ij, t_out[p] = t_ij
+ * (t_out may be NULL).  Used where the full product would take too long.
+ * Returns 0, -1/-2 as above, or -3 for a point outside the M x N window.
+ */
+int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
+                        int lda, const float *B, int ldb, float beta,
+                        const float *C, int ldc, int npts, const int *rows,
+                        const int *cols, double *r_out, double *t_out,
+                        int nthreads) {
+  int e = check_args(M, N, K, lda, ldb, ldc);
+  if (e) return e;
+  for (int p = 0; p < npts; ++p)
+    if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -3;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.M = M; j.N = N; j.K = K;
+  j.alpha = (double)alpha; j.beta = (double)beta;
+  j.A = A; j.B = B; j.C = C;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.R = r_out; j.T = t_out;
+  j.npts = npts; j.rows = rows; j.cols = cols;
+  run_split(points, &j, npts, nthreads);
+  return 0;
+}

@@ -1,0 +1,255 @@
+"""Pins for the CPU oracle: checks against facts fixed by mathematics.
+
+Each pin takes a loaded oracle library (``lib``) and raises AssertionError on
+a mismatch, so the same pins run against the real oracle and against mutants
+with planted mistakes (tests/test_oracle_mutants.py).  None of them re-types
+the oracle's loop: they use exact rational arithmetic, Python integers,
+closed forms of special matrices, and invariants such as (AB)^T = B^T A^T.
+
+What the oracle computes is C = alpha*A*B + beta*C for row-major FP32 operands
+("GEMM 优化之路", problem statement), with beta == 0 meaning C is not read.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+U = 2.0 ** -53  # unit roundoff of FP64
+
+
+def f32_of_fraction(q: Fraction) -> np.float32:
+    """Round an exact rational to FP32, nearest-even, with no double rounding."""
+    if q == 0:
+        return np.float32(0.0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    # exponent e with 2**23 <= a / 2**e < 2**24
+    e = a.numerator.bit_length() - a.denominator.bit_length() - 24
+    while a / Fraction(2) ** e >= 2 ** 24:
+        e += 1
+    while a / Fraction(2) ** e < 2 ** 23:
+        e -= 1
+    e = max(e, -149)  # FP32 subnormal quantum
+    scaled = a / Fraction(2) ** e
+    m = scaled.numerator // scaled.denominator
+    rem = scaled - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    return np.float32(sign * float(m) * 2.0 ** e)
+
+
+def _dyadic(rng, shape, bits=24):
+    """FP32 values exactly representable, in [-1, 1)."""
+    return (2.0 * rng.random(shape, dtype=np.float32) - np.float32(1.0))
+
+
+def _run(lib, A, B, C, alpha, beta, lda=None, ldb=None, ldc=None, with_t=True):
+    M, K = A.shape
+    N = B.shape[1]
+    return oracle.gemm(M, N, K, alpha, A, lda or max(K, 1), B, ldb or max(N, 1),
+                       beta, C, ldc or max(N, 1), with_t=with_t, lib=lib)
+
+
+# --------------------------------------------------------------------------
+def pin_bruteforce_exact(lib, seed=7, cases=60):
+    """Random tiny problems against exact rational arithmetic.
+
+    |r - exact| <= (K + 3) * 2**-53 * (|alpha| * t + |beta * c|), t matches the
+    exact sum of |a*b| to K*2**-53 relative, and r rounded to FP32 equals the
+    exact value rounded to FP32.  Covers both the full and the point modes.
+    """
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        M, N, K = (int(x) for x in rng.integers(1, 9, size=3))
+        alpha = float(rng.choice([1.0, 1.5, -0.75, 0.0, 2.0 ** -3]))
+        beta = float(rng.choice([0.0, 0.5, 1.0, -1.25]))
+        A = _dyadic(rng, (M, K))
+        B = _dyadic(rng, (K, N))
+        C = _dyadic(rng, (M, N))
+        R, T = _run(lib, A, B, C, alpha, beta)
+        rows = np.repeat(np.arange(M), N)
+        cols = np.tile(np.arange(N), M)
+        rp, tp = oracle.gemm_points(M, N, K, alpha, A, K, B, N, beta, C, N,
+                                    rows, cols, lib=lib)
+        qa, qb = Fraction(alpha), Fraction(beta)
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(float(A[i, k])) * Fraction(float(B[k, j]))
+                         for k in range(K)]
+                s = sum(terms, Fraction(0))
+                t = sum((abs(x) for x in terms), Fraction(0))
+                cterm = qb * Fraction(float(C[i, j])) if beta != 0 else Fraction(0)
+                exact = qa * s + cterm
+                scale = abs(alpha) * float(t) + abs(float(cterm))
+                tol = (K + 3) * U * scale
+                for r, tt, mode in ((R[i, j], T[i, j], "full"),
+                                    (rp[i * N + j], tp[i * N + j], "points")):
+                    err = abs(Fraction(float(r)) - exact)
+                    assert err <= Fraction(tol) + Fraction(0), (
+                        f"case {case} {mode} ({i},{j}) M,N,K={M},{N},{K}: "
+                        f"err {float(err):.3e} > {tol:.3e}")
+                    terr = abs(Fraction(float(tt)) - t)
+                    assert terr <= Fraction(K * U * float(t)), (
+                        f"case {case} {mode} t mismatch at ({i},{j})")
+                    assert np.float32(r) == f32_of_fraction(exact), (
+                        f"case {case} {mode} ({i},{j}): FP32 rounding differs")
+
+
+def pin_integer_exact(lib, seed=11):
+    """Integer inputs: every partial sum is exact, so r equals integer math."""
+    rng = np.random.default_rng(seed)
+    # small: Python ints, element by element
+    M, N, K = 7, 5, 9
+    A = rng.integers(-4, 5, (M, K))
+    B = rng.integers(-4, 5, (K, N))
+    C = rng.integers(-4, 5, (M, N))
+    R, _ = _run(lib, A.astype(np.float32), B.astype(np.float32),
+                C.astype(np.float32), 1.0, 1.0)
+    for i in range(M):
+        for j in range(N):
+            want = sum(int(A[i, k]) * int(B[k, j]) for k in range(K)) + int(C[i, j])
+            assert R[i, j] == want, f"({i},{j}) {R[i, j]} != {want}"
+    # larger, several tiles' worth: int64 matrix product is exact
+    M, N, K = 67, 45, 131
+    A = rng.integers(-4, 5, (M, K))
+    B = rng.integers(-4, 5, (K, N))
+    C = rng.integers(-4, 5, (M, N))
+    R, _ = _run(lib, A.astype(np.float32), B.astype(np.float32),
+                C.astype(np.float32), 3.0, -2.0)
+    want = 3 * (A.astype(np.int64) @ B.astype(np.int64)) - 2 * C
+    assert np.array_equal(R, want.astype(np.float64))
+
+
+def pin_identity(lib, seed=13):
+    """A = I gives alpha*B + beta*C; B = I gives alpha*A + beta*C (exact here)."""
+    rng = np.random.default_rng(seed)
+    n, N = 19, 23
+    alpha, beta = 1.5, 0.5
+    B = _dyadic(rng, (n, N))
+    C = _dyadic(rng, (n, N))
+    R, _ = _run(lib, np.eye(n, dtype=np.float32), B, C, alpha, beta)
+    assert np.array_equal(R, alpha * B.astype(np.float64) + beta * C.astype(np.float64))
+    M = 17
+    A = _dyadic(rng, (M, n))
+    C2 = _dyadic(rng, (M, n))
+    R, _ = _run(lib, A, np.eye(n, dtype=np.float32), C2, alpha, beta)
+    assert np.array_equal(R, alpha * A.astype(np.float64) + beta * C2.astype(np.float64))
+
+
+def pin_permutation(lib, seed=17):
+    """A = P permutes the rows of B; B = P permutes the columns of A."""
+    rng = np.random.default_rng(seed)
+    n, N, M = 21, 13, 11
+    perm = rng.permutation(n)
+    P = np.zeros((n, n), dtype=np.float32)
+    P[np.arange(n), perm] = 1.0  # (P B)[i] = B[perm[i]]
+    B = _dyadic(rng, (n, N))
+    C = np.full((n, N), np.nan, dtype=np.float32)
+    R, _ = _run(lib, P, B, C, 1.0, 0.0)
+    assert np.array_equal(R, B[perm].astype(np.float64))
+    A = _dyadic(rng, (M, n))
+    # (A P)[:, j] = sum_k A[:, k] P[k, j] = A[:, perm^-1[j]]
+    R, _ = _run(lib, A, P, np.zeros((M, n), np.float32), -2.0, 0.0)
+    inv = np.argsort(perm)
+    assert np.array_equal(R, -2.0 * A[:, inv].astype(np.float64))
+
+
+def pin_rank1(lib, seed=19):
+    """K = 1: r = alpha*a_i*b_j + beta*c_ij; and A = u p^T, B = q w^T."""
+    rng = np.random.default_rng(seed)
+    M, N = 9, 14
+    alpha, beta = 1.5, 0.5
+    a = _dyadic(rng, (M, 1))
+    b = _dyadic(rng, (1, N))
+    C = _dyadic(rng, (M, N))
+    R, _ = _run(lib, a, b, C, alpha, beta)
+    want = alpha * (a.astype(np.float64) * b.astype(np.float64)) + beta * C.astype(np.float64)
+    assert np.array_equal(R, want)
+    # small-integer outer products: C_ij = alpha * u_i * (p . q) * w_j + beta * c_ij
+    K = 33
+    u = rng.integers(-3, 4, M)
+    p = rng.integers(-3, 4, K)
+    q = rng.integers(-3, 4, K)
+    w = rng.integers(-3, 4, N)
+    c = rng.integers(-3, 4, (M, N))
+    A = np.outer(u, p).astype(np.float32)
+    B = np.outer(q, w).astype(np.float32)
+    R, _ = _run(lib, A, B, c.astype(np.float32), -1.0, 2.0)
+    pq = int(np.dot(p, q))
+    for i in range(M):
+        for j in range(N):
+            assert R[i, j] == -1 * int(u[i]) * pq * int(w[j]) + 2 * int(c[i, j])
+
+
+def pin_alpha_beta(lib, seed=23):
+    """alpha = 0 gives beta*C; beta = 0 never reads C; B = 0 with beta = 1 keeps C;
+    K = 0 gives beta*C (zeros when beta = 0, even over a NaN C)."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 6, 10, 12
+    A = _dyadic(rng, (M, K))
+    B = _dyadic(rng, (K, N))
+    C = _dyadic(rng, (M, N))
+    R, _ = _run(lib, A, B, C, 0.0, 0.5)
+    assert np.array_equal(R, 0.5 * C.astype(np.float64))
+    Cn = np.full((M, N), np.nan, dtype=np.float32)
+    R1, _ = _run(lib, A, B, Cn, 1.0, 0.0)
+    assert np.all(np.isfinite(R1))
+    R2, _ = _run(lib, A, B, C, 1.0, 0.0)
+    assert np.array_equal(R1, R2), "beta == 0 must not depend on C"
+    R, _ = _run(lib, A, np.zeros((K, N), np.float32), C, 1.0, 1.0)
+    assert np.array_equal(R, C.astype(np.float64))
+    A0 = np.zeros((M, 0), np.float32)
+    B0 = np.zeros((0, N), np.float32)
+    R, _ = _run(lib, A0, B0, C, 1.0, -2.0)
+    assert np.array_equal(R, -2.0 * C.astype(np.float64))
+    R, _ = _run(lib, A0, B0, Cn, 1.0, 0.0)
+    assert np.array_equal(R, np.zeros((M, N)))
+    # alpha scales linearly: r(alpha=2^-3) == 2^-3 * r(alpha=1) exactly (power of 2)
+    R8, _ = _run(lib, A, B, C, 0.125, 0.0)
+    assert np.array_equal(R8, 0.125 * R2)
+
+
+def pin_transpose(lib, seed=29):
+    """(A B)^T = B^T A^T, bit for bit: the same products summed in the same order."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 13, 7, 29
+    A = _dyadic(rng, (M, K))
+    B = _dyadic(rng, (K, N))
+    R, T = _run(lib, A, B, None, 1.0, 0.0)
+    Rt, Tt = _run(lib, np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), None, 1.0, 0.0)
+    assert np.array_equal(R, Rt.T)
+    assert np.array_equal(T, Tt.T)
+
+
+def pin_leading_dims(lib, seed=31):
+    """Padding beyond the M x N / M x K / K x N windows is never read (NaN pads)."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 11, 9, 15
+    alpha, beta = 1.5, 0.5
+    A = _dyadic(rng, (M, K))
+    B = _dyadic(rng, (K, N))
+    C = _dyadic(rng, (M, N))
+    R, T = _run(lib, A, B, C, alpha, beta)
+    lda, ldb, ldc = K + 5, N + 3, N + 7
+
+    def pad(x, ld):
+        y = np.full((x.shape[0], ld), np.nan, np.float32)
+        y[:, :x.shape[1]] = x
+        return y
+
+    Rp, Tp = oracle.gemm(M, N, K, alpha, pad(A, lda), lda, pad(B, ldb), ldb, beta,
+                         pad(C, ldc), ldc, lib=lib)
+    assert np.array_equal(R, Rp) and np.array_equal(T, Tp)
+    rows = np.array([0, M - 1, 5, 3])
+    cols = np.array([N - 1, 0, 4, 8])
+    rp, tp = oracle.gemm_points(M, N, K, alpha, pad(A, lda), lda, pad(B, ldb), ldb,
+                                beta, pad(C, ldc), ldc, rows, cols, lib=lib)
+    assert np.array_equal(rp, R[rows, cols]) and np.array_equal(tp, T[rows, cols])
+
+
+ALL_PINS = [pin_bruteforce_exact, pin_integer_exact, pin_identity,
+            pin_permutation, pin_rank1, pin_alpha_beta, pin_transpose,
+            pin_leading_dims]

@@ -1,0 +1,76 @@
+"""Planted mistakes in the oracle must fail at least one pin.
+
+Each mutant is a one-spot textual change to oracle/sgemm_oracle.c of the kind
+a plausible slip would make (a dropped term, a wrong sign or index, a
+transposed operand, a lost scale, an FP32 accumulator).  It is compiled on the
+CPU into a temporary library and every pin runs against it; the test passes
+only if some pin rejects the mutant.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+MUTANTS = {
+    "drop_last_k_full": ("for (int k = 0; k < j->K; ++k) {\n      const double a",
+                         "for (int k = 0; k < j->K - 1; ++k) {\n      const double a"),
+    "drop_last_k_points": ("for (int k = 0; k < j->K; ++k) {\n      const double q",
+                           "for (int k = 0; k < j->K - 1; ++k) {\n      const double q"),
+    "beta_sign": ("v += j->beta * (double)j->C[(long)i * j->ldc + c];\n      r[c] = v;",
+                  "v -= j->beta * (double)j->C[(long)i * j->ldc + c];\n      r[c] = v;"),
+    "beta_sign_points": ("v += j->beta * (double)j->C[(long)i * j->ldc + c];\n    j->R[p] = v;",
+                         "v -= j->beta * (double)j->C[(long)i * j->ldc + c];\n    j->R[p] = v;"),
+    "reads_c_when_beta_zero": ("      if (j->beta != 0.0) v += j->beta * (double)j->C[(long)i * j->ldc + c];\n      r[c] = v;",
+                               "      v += j->beta * (double)j->C[(long)i * j->ldc + c];\n      r[c] = v;"),
+    "ldb_for_lda": ("const double a = (double)j->A[(long)i * j->lda + k];",
+                    "const double a = (double)j->A[(long)i * j->ldb + k];"),
+    "b_transposed_points": ("(double)j->B[(long)k * j->ldb + c];",
+                            "(double)j->B[(long)c * j->ldb + k];"),
+    "alpha_dropped": ("double v = j->alpha * r[c];", "double v = r[c];"),
+    "float_accumulator": ("r[c] += p;", "r[c] = (float)(r[c] + p);"),
+    "float_product": ("const double p = a * (double)brow[c];",
+                      "const double p = (float)(a * (double)brow[c]);"),
+    "t_signed": ("if (t) t[c] += fabs(p);", "if (t) t[c] += p;"),
+    "row_offset": ("double *r = j->R + (long)i * j->ldr;",
+                   "double *r = j->R + (long)(i > 0 ? i - 1 : 0) * j->ldr;"),
+}
+
+
+_RUNNER = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import oracle
+from tests import oracle_pins as pins
+lib = oracle.load(sys.argv[2])
+caught = []
+for pin in pins.ALL_PINS:
+    try:
+        pin(lib)
+    except (AssertionError, ValueError):
+        caught.append(pin.__name__)
+print("CAUGHT " + ",".join(caught))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(oracle.SOURCE, encoding="utf-8").read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new), encoding="utf-8")
+    lib_path = oracle.compile_library(str(path), str(tmp_path / f"lib{name}.so"))
+    # A mutant may read out of bounds and crash: run the pins in a child process,
+    # where a crash also counts as the mutant being caught.
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    proc = subprocess.run([sys.executable, "-c", _RUNNER, root, lib_path],
+                          capture_output=True, text=True, timeout=300)
+    if proc.returncode != 0:
+        return  # crashed or raised: caught
+    line = [l for l in proc.stdout.splitlines() if l.startswith("CAUGHT")][-1]
+    caught = [c for c in line[len("CAUGHT "):].split(",") if c]
+    assert caught, f"mutant {name} passed every pin"
