@@ -1,0 +1,245 @@
+"""Benchmark: FP32 SGEMM GFLOPS on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_4096]
+                    [--variant mfma|valu] [--no-cpu-baseline] [--no-per-config]
+
+A step is one SGEMM call, C = alpha*A*B + beta*C, on the headline workload
+(M = N = K = 4096, alpha = 1.5, beta = 0.5, uniform [-1, 1) inputs, C
+prefilled), with every operand already resident in device memory.  W untimed
+steps run first, then exactly K timed steps bracketed by device
+synchronisations.  The work count is 2*M*N*K per step ("GEMM 优化之路",
+problem statement; the alpha/beta update is not counted).
+
+Output: one JSON line with the throughput, the kernel's roofline position
+(HIP events around every launch on the stream the kernel runs on), the CPU
+oracle timed on a bounded sample of the same workload, and per-workload
+GFLOPS for the other problem shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM GFLOPS and % of MI355X FP32 peak at M=N=K=4096 (1 GPU)"
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "fp32_gemm_major_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for e in data.get("entries", []):
+        if (e.get("workload") == workload and e.get("kernel") == kernel
+                and e.get("source_hash") == kernel_source_hash()):
+            return e.get("hbm_bytes_per_launch")
+    return None
+
+
+def time_launches(launch, steps, warmup, torch):
+    """Run `launch` warmup + steps times; return (total_ms, per-launch ms list)."""
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record()
+        launch()
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total = starts[0].elapsed_time(ends[-1])
+    return total, per
+
+
+def cpu_baseline(ops, target_s: float):
+    """Time the CPU oracle (FP64 triple loop, no error-bound pass) on the first
+    rows of the same problem, all host cores, about `target_s` seconds."""
+    import oracle
+
+    M, N, K = ops.M, ops.N, ops.K
+    cores = oracle.default_threads()
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.gemm(rows, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb, ops.beta,
+                    ops.C, ops.ldc, with_t=False, nthreads=cores)
+        return time.perf_counter() - t0
+
+    rows = min(cores, M)
+    t = run(rows)
+    for _ in range(3):  # grow the sample until it takes about target_s
+        if t >= 0.6 * target_s or rows >= M:
+            break
+        want = int(rows * target_s / max(t, 1e-6))
+        rows = max(rows + cores, min(M, (want // cores) * cores))
+        rows = min(rows, M)
+        t = run(rows)
+    flops = 2.0 * rows * N * K
+    return {
+        "value": round(flops / t / 1e9, 3),
+        "unit": "GFLOPS",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} problem ({rows}x{N} outputs, "
+                  f"full K), FP64 accumulation, {t:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_4096")
+    ap.add_argument("--variant", choices=["mfma", "valu"], default="mfma")
+    ap.add_argument("--kernel", type=int, default=-1, help="force a kernel id")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this SGEMM runs on one GPU only; multi-GPU runs are not "
+              "part of this build (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import fp32_gemm_major_amd as sg
+    from fp32_gemm_major_amd import roofline as rf
+    from fp32_gemm_major_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    variant = sg.SGEMM_VARIANT_MFMA if args.variant == "mfma" else sg.SGEMM_VARIANT_VALU
+    h = sg.Handle(variant=variant, kernel=args.kernel)
+
+    def prepare(name):
+        w = wl.WORKLOADS[name]
+        ops = wl.operands(w)
+        dev = [torch.from_numpy(x).cuda() for x in (ops.A, ops.B, ops.C)]
+        kid = args.kernel if args.kernel >= 0 else sg.sgemm_select_kernel(
+            variant, w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(),
+            ops.ldb, dev[2].data_ptr(), ops.ldc)
+
+        def launch():
+            h.gemm(dev[0], dev[1], dev[2], w.alpha, w.beta, M=w.M, N=w.N, K=w.K,
+                   lda=ops.lda, ldb=ops.ldb, ldc=ops.ldc)
+        return w, ops, dev, kid, launch
+
+    w, ops, dev, kid, launch = prepare(args.workload)
+    kname = sg.sgemm_kernel_name(kid)
+    total_ms, per = time_launches(launch, args.steps, args.warmup, torch)
+    flops = rf.flops(w.M, w.N, w.K)
+    ms_per_step = total_ms / args.steps
+    kernel_ms = sum(per) / len(per)
+    value = flops / (ms_per_step * 1e-3) / 1e9
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = rf.PEAK_FP32_FLOPS / 1e12
+    roof = {
+        "bound": "mfma" if variant == sg.SGEMM_VARIANT_MFMA else "alu",
+        "achieved": round(achieved, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": measured_traffic(w.label, kname),
+        "kernel": kname,
+        "kernel_ms_mean": round(kernel_ms, 5),
+        "kernel_ms_min": round(min(per), 5),
+        "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta),
+        "flops_per_launch": flops,
+    }
+    del dev
+
+    per_config = None
+    if not args.no_per_config:
+        per_config = {}
+        reps = {"c1_128": 200, "c2_1024": 200, "c4_edge": 200, "c5_mlp": 30}
+        for name, n in reps.items():
+            w2, _, dev2, kid2, launch2 = prepare(name)
+            _, per2 = time_launches(launch2, n, 5, torch)
+            ms = sum(per2) / len(per2)
+            gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
+            per_config[name] = {"gflops": round(gf, 1),
+                                "frac_of_peak": round(gf * 1e9 / rf.PEAK_FP32_FLOPS, 4),
+                                "kernel_ms": round(ms, 5),
+                                "kernel": sg.sgemm_kernel_name(kid2)}
+            del dev2
+        per_config[args.workload] = {"gflops": round(achieved * 1e3, 1),
+                                     "frac_of_peak": roof["frac"],
+                                     "kernel_ms": roof["kernel_ms_mean"],
+                                     "kernel": kname}
+        if variant == sg.SGEMM_VARIANT_MFMA:
+            h.set_variant(sg.SGEMM_VARIANT_VALU)
+            w3, _, dev3, _, launch3 = prepare(args.workload)
+            kid3 = sg.sgemm_select_kernel(sg.SGEMM_VARIANT_VALU, w3.M, w3.N, w3.K,
+                                          dev3[0].data_ptr(), w3.K, dev3[1].data_ptr(),
+                                          w3.N, dev3[2].data_ptr(), w3.N)
+            _, per3 = time_launches(launch3, 20, 3, torch)
+            ms = sum(per3) / len(per3)
+            gf = rf.flops(w3.M, w3.N, w3.K) / (ms * 1e-3) / 1e9
+            per_config[args.workload + "_valu"] = {
+                "gflops": round(gf, 1),
+                "frac_of_peak": round(gf * 1e9 / rf.PEAK_FP32_FLOPS, 4),
+                "frac_of_unpacked_valu_peak": round(
+                    gf * 1e9 / rf.PEAK_FP32_VALU_UNPACKED_FLOPS, 4),
+                "kernel_ms": round(ms, 5), "kernel": sg.sgemm_kernel_name(kid3)}
+            h.set_variant(variant)
+            del dev3
+    h.close()
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(ops, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": round(100.0 * value * 1e9 / rf.PEAK_FP32_FLOPS, 2),
+        "config": {"workload": w.label, "M": w.M, "N": w.N, "K": w.K,
+                   "alpha": w.alpha, "beta": w.beta, "kernel": kname,
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,230 @@
+"""MI355X (gfx950) FP32 GEMM: Python binding of the C ABI in include/sgemm.h.
+
+C = alpha * A * B + beta * C for row-major FP32 operands ("GEMM 优化之路",
+problem statement).  Every step runs in the HIP library ``libsgemm.so``; this
+module only marshals arguments.  PyTorch provides device memory and streams.
+There is no fallback: if the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (load torch's HIP runtime before the library)
+
+from .build import LIBRARY
+
+SGEMM_OK = 0
+SGEMM_ERR_HANDLE = -1
+SGEMM_ERR_SIZE = -2
+SGEMM_ERR_LD = -3
+SGEMM_ERR_NULL = -4
+SGEMM_ERR_HIP = -5
+SGEMM_ERR_DEVICE = -6
+SGEMM_ERR_VALUE = -7
+SGEMM_ERR_ALIAS = -8
+SGEMM_ERR_UNSUPPORTED = -9
+
+SGEMM_VARIANT_AUTO = 0
+SGEMM_VARIANT_MFMA = 1
+SGEMM_VARIANT_VALU = 2
+
+EXPORTED = [
+    "sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
+    "sgemm_status_string", "sgemm_num_kernels", "sgemm_kernel_name",
+    "sgemm_kernel_info", "sgemm_select_kernel", "sgemm_tile_coords",
+    "sgemm_set_variant", "sgemm_set_kernel",
+]
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def _bind(lib):
+    i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.sgemm_create.argtypes = [ctypes.POINTER(p)]
+    lib.sgemm_run.argtypes = [p, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_destroy.argtypes = [p]
+    lib.sgemm_validate.argtypes = [i, i, i, p, i, p, i, f, p, i]
+    lib.sgemm_status_string.argtypes = [i]
+    lib.sgemm_status_string.restype = ctypes.c_char_p
+    lib.sgemm_num_kernels.argtypes = []
+    lib.sgemm_kernel_name.argtypes = [i]
+    lib.sgemm_kernel_name.restype = ctypes.c_char_p
+    lib.sgemm_kernel_info.argtypes = [i, ip, ip, ip, ip, ip, ip]
+    lib.sgemm_select_kernel.argtypes = [i, i, i, i, p, i, p, i, p, i]
+    lib.sgemm_tile_coords.argtypes = [i, i, i, i, ip, ip]
+    lib.sgemm_tile_coords.restype = None
+    lib.sgemm_set_variant.argtypes = [p, i]
+    lib.sgemm_set_kernel.argtypes = [p, i]
+    for name in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
+                 "sgemm_num_kernels", "sgemm_kernel_info", "sgemm_select_kernel",
+                 "sgemm_set_variant", "sgemm_set_kernel"):
+        getattr(lib, name).restype = i
+    return lib
+
+
+def library(path: str = LIBRARY):
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is missing: build it with `python -m fp32_gemm_major_amd.build`"
+                " (or __graft_entry__.build()); there is no fallback path")
+        _lib = _bind(ctypes.CDLL(path))
+    return _lib
+
+
+def _check(status: int, what: str) -> int:
+    if status < 0:
+        raise SgemmError(status, what)
+    return status
+
+
+# ---- the C ABI, name for name -------------------------------------------------
+
+def sgemm_create() -> int:
+    h = ctypes.c_void_p()
+    _check(library().sgemm_create(ctypes.byref(h)), "sgemm_create")
+    return h.value
+
+
+def sgemm_run(h, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """Enqueue on ``stream`` (an int hipStream_t); A, B, C are device addresses."""
+    return _check(library().sgemm_run(h, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                      ldc, stream), "sgemm_run")
+
+
+def sgemm_destroy(h) -> int:
+    return library().sgemm_destroy(h)
+
+
+def sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc) -> int:
+    return library().sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc)
+
+
+def sgemm_status_string(status: int) -> str:
+    return library().sgemm_status_string(status).decode()
+
+
+status_string = sgemm_status_string
+
+
+def sgemm_num_kernels() -> int:
+    return library().sgemm_num_kernels()
+
+
+def sgemm_kernel_name(kernel_id: int):
+    s = library().sgemm_kernel_name(kernel_id)
+    return s.decode() if s is not None else None
+
+
+def sgemm_kernel_info(kernel_id: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(6)]
+    _check(library().sgemm_kernel_info(kernel_id, *[ctypes.byref(v) for v in vals]),
+           "sgemm_kernel_info")
+    keys = ("variant", "bm", "bn", "bk", "threads", "guarded")
+    d = {k: v.value for k, v in zip(keys, vals)}
+    d["name"] = sgemm_kernel_name(kernel_id)
+    d["id"] = kernel_id
+    return d
+
+
+def sgemm_select_kernel(variant, M, N, K, A, lda, B, ldb, C, ldc) -> int:
+    return library().sgemm_select_kernel(variant, M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def sgemm_tile_coords(wg, nwg, tiles_m, tiles_n):
+    tm, tn = ctypes.c_int(), ctypes.c_int()
+    library().sgemm_tile_coords(wg, nwg, tiles_m, tiles_n, ctypes.byref(tm),
+                                ctypes.byref(tn))
+    return tm.value, tn.value
+
+
+def sgemm_set_variant(h, variant: int) -> int:
+    return _check(library().sgemm_set_variant(h, variant), "sgemm_set_variant")
+
+
+def sgemm_set_kernel(h, kernel_id: int) -> int:
+    return _check(library().sgemm_set_kernel(h, kernel_id), "sgemm_set_kernel")
+
+
+# ---- torch-tensor convenience ------------------------------------------------
+
+class Handle:
+    """Owns one sgemm handle; usable as a context manager."""
+
+    def __init__(self, variant: int = SGEMM_VARIANT_AUTO, kernel: int = -1):
+        self.h = sgemm_create()
+        if variant != SGEMM_VARIANT_AUTO:
+            sgemm_set_variant(self.h, variant)
+        if kernel >= 0:
+            sgemm_set_kernel(self.h, kernel)
+
+    def close(self):
+        if self.h:
+            sgemm_destroy(self.h)
+            self.h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_variant(self, variant: int):
+        sgemm_set_variant(self.h, variant)
+
+    def set_kernel(self, kernel_id: int):
+        sgemm_set_kernel(self.h, kernel_id)
+
+    def gemm(self, A, B, C, alpha=1.0, beta=0.0, M=None, N=None, K=None,
+             lda=None, ldb=None, ldc=None, stream=None):
+        """C[:M, :N] = alpha * A[:M, :K] @ B[:K, :N] + beta * C on ``stream``.
+
+        A, B, C are float32 CUDA tensors.  2-D tensors with unit column stride
+        give their sizes and leading dimensions; 1-D buffers need explicit
+        sizes and leading dimensions.  ``stream`` defaults to torch's current
+        stream.  Returns immediately (the work is queued on the stream).
+        """
+        for name, t in (("A", A), ("B", B), ("C", C)):
+            if t.dtype != torch.float32 or not t.is_cuda:
+                raise TypeError(f"{name} must be a float32 CUDA tensor")
+            if t.dim() == 2 and t.numel() and t.stride(1) != 1:
+                raise ValueError(f"{name} must be row-major (unit column stride)")
+        if A.dim() == 2:
+            M = A.shape[0] if M is None else M
+            K = A.shape[1] if K is None else K
+            lda = max(A.stride(0), 1) if lda is None else lda
+        if B.dim() == 2:
+            K = B.shape[0] if K is None else K
+            N = B.shape[1] if N is None else N
+            ldb = max(B.stride(0), 1) if ldb is None else ldb
+        if C.dim() == 2:
+            ldc = max(C.stride(0), 1) if ldc is None else ldc
+        if None in (M, N, K, lda, ldb, ldc):
+            raise ValueError("sizes and leading dimensions are needed for 1-D buffers")
+        if stream is None:
+            stream = torch.cuda.current_stream(C.device).cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        return sgemm_run(self.h, M, N, K, float(alpha), A.data_ptr(), lda,
+                         B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, stream)
+
+
+def kernel_table() -> list:
+    return [sgemm_kernel_info(i) for i in range(sgemm_num_kernels())]

@@ -1,0 +1,308 @@
+// C ABI of the MI355X SGEMM library: handle, argument checks, kernel table,
+// kernel selection and launch on the caller's stream.  Declarations and the
+// full contract are in include/sgemm.h.
+//
+// The host side follows the launchers of "GEMM 优化之路" (its complete
+// listing: one grid of ceil(M/BM) x ceil(N/BN) blocks per call) but adds what a
+// library needs: explicit leading dimensions, status codes instead of aborts,
+// the caller's stream, and a choice of tile shape per problem.
+#include "sgemm.h"
+
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "mfma_sgemm.hpp"
+#include "tile_map.hpp"
+#include "valu_sgemm.hpp"
+
+using namespace sgemm;
+
+struct sgemm_handle_s {
+  int device;
+  int cus;
+  int variant;       // SGEMM_VARIANT_*
+  int forced_kernel; // -1 = automatic
+};
+
+namespace {
+
+struct RunArgs {
+  int M, N, K;
+  float alpha, beta;
+  const float* A;
+  int lda;
+  const float* B;
+  int ldb;
+  float* C;
+  int ldc;
+};
+
+typedef hipError_t (*launch_fn)(const RunArgs&, int tiles_m, int tiles_n,
+                                hipStream_t);
+
+struct KernelDesc {
+  const char* name;
+  int variant;
+  int bm, bn, bk, threads, guarded;
+  int wgs_per_cu;  // resident workgroups per CU the tile is sized for
+  float rel_rate;  // relative per-CU throughput, used by the tile choice
+  launch_fn launch;
+};
+
+template <class T, bool G>
+hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
+                       hipStream_t s) {
+  hipLaunchKernelGGL((mfma_sgemm_kernel<T, G>), dim3(tiles_m * tiles_n),
+                     dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
+                     a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <class T, bool G>
+hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
+                       hipStream_t s) {
+  hipLaunchKernelGGL((valu_sgemm_kernel<T, G>), dim3(tiles_m * tiles_n),
+                     dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
+                     a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// Tile shapes.  MfmaTile<BM, BN, BK, WM, WN>: block tile, K step, wave tile.
+// The last parameter is the number of waves per SIMD the register budget is
+// sized for (2 waves of 256 registers, 4 of 128, ...).
+typedef MfmaTile<256, 256, 16, 128, 64, 2> M256x256;  // 8 waves, 1 WG/CU
+typedef MfmaTile<256, 128, 16, 128, 64, 2> M256x128;  // 4 waves, 2 WG/CU
+typedef MfmaTile<128, 128, 16, 64, 64, 2> M128x128;   // 4 waves, 2 WG/CU
+typedef MfmaTile<64, 64, 16, 32, 32, 4> M64x64;       // 4 waves, 4 WG/CU
+typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
+
+#define MFMA_PAIR(T, occ, rate)                                            \
+  {"mfma_" #T "_aligned", SGEMM_VARIANT_MFMA, T::BM, T::BN, T::BK,        \
+   T::THREADS, 0, occ, rate, launch_mfma<T, false>},                      \
+  {"mfma_" #T "_guarded", SGEMM_VARIANT_MFMA, T::BM, T::BN, T::BK,        \
+   T::THREADS, 1, occ, rate, launch_mfma<T, true>}
+
+const KernelDesc kKernels[] = {
+    MFMA_PAIR(M256x256, 1, 1.00f),
+    MFMA_PAIR(M256x128, 2, 0.95f),
+    MFMA_PAIR(M128x128, 2, 0.80f),
+    MFMA_PAIR(M64x64, 4, 0.40f),
+    {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
+     V128x128::BK, V128x128::THREADS, 0, 2, 1.0f,
+     launch_valu<V128x128, false>},
+    {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
+     V128x128::BK, V128x128::THREADS, 1, 2, 1.0f,
+     launch_valu<V128x128, true>},
+};
+constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
+constexpr int kChipCus = 256;
+
+bool ptr_aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Can kernel k run these arguments?
+bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
+  if (k.guarded) return true;
+  return a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
+         a.lda % 4 == 0 && a.ldb % 4 == 0 && ptr_aligned16(a.A) &&
+         ptr_aligned16(a.B);
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Modelled time of a tile shape.  A CU holds wgs_per_cu tiles at once and
+// finishes them together, so one round costs wgs_per_cu * bm * bn of work at
+// the tile's relative per-CU rate; the grid takes ceil(tiles / slots) rounds.
+double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
+  const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
+  const long long slots = (long long)cus * k.wgs_per_cu;
+  const long long rounds = ceil_div(tiles, slots);
+  return (double)rounds * k.wgs_per_cu * k.bm * k.bn / k.rel_rate;
+}
+
+int select_kernel(int variant, const RunArgs& a, int cus) {
+  if (variant == SGEMM_VARIANT_AUTO) variant = SGEMM_VARIANT_MFMA;
+  if (variant != SGEMM_VARIANT_MFMA && variant != SGEMM_VARIANT_VALU)
+    return SGEMM_ERR_VALUE;
+  // Pick the tile shape with the lowest modelled cost, then its aligned
+  // instance when the arguments allow it, else its guarded instance.
+  int best = -1;
+  double best_cost = 0.0;
+  for (int i = 0; i < kNumKernels; ++i) {
+    const KernelDesc& k = kKernels[i];
+    if (k.variant != variant || k.guarded) continue;
+    const double c = tile_cost(k, a, cus);
+    if (best < 0 || c < best_cost) {
+      best = i;
+      best_cost = c;
+    }
+  }
+  if (best < 0) return SGEMM_ERR_VALUE;
+  if (kernel_fits(kKernels[best], a)) return best;
+  for (int i = 0; i < kNumKernels; ++i) {
+    const KernelDesc& k = kKernels[i];
+    if (k.guarded && k.variant == variant && k.bm == kKernels[best].bm &&
+        k.bn == kKernels[best].bn && k.bk == kKernels[best].bk)
+      return i;
+  }
+  return SGEMM_ERR_VALUE;
+}
+
+// Half-open byte range of a row-major window, or empty.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range window(const void* p, int rows, int cols, int ld) {
+  Range r = {0, 0};
+  if (p == nullptr || rows <= 0 || cols <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + ((uintptr_t)(rows - 1) * (uintptr_t)ld + (uintptr_t)cols) * 4u;
+  return r;
+}
+bool overlap(Range x, Range y) {
+  return x.lo < x.hi && y.lo < y.hi && x.lo < y.hi && y.lo < x.hi;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm_validate(int M, int N, int K, const float* A, int lda,
+                   const float* B, int ldb, float beta, const float* C,
+                   int ldc) {
+  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SIZE;
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    return SGEMM_ERR_LD;
+  if (M == 0 || N == 0) return SGEMM_OK;  // nothing is touched
+  if (C == nullptr) return SGEMM_ERR_NULL;
+  if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_NULL;
+  const Range rc = window(C, M, N, ldc);
+  if (K > 0 && (overlap(rc, window(A, M, K, lda)) ||
+                overlap(rc, window(B, K, N, ldb))))
+    return SGEMM_ERR_ALIAS;
+  (void)beta;
+  return SGEMM_OK;
+}
+
+const char* sgemm_status_string(int status) {
+  switch (status) {
+    case SGEMM_OK: return "ok";
+    case SGEMM_ERR_HANDLE: return "null handle";
+    case SGEMM_ERR_SIZE: return "negative size";
+    case SGEMM_ERR_LD: return "leading dimension too small";
+    case SGEMM_ERR_NULL: return "null operand pointer";
+    case SGEMM_ERR_HIP: return "HIP runtime error";
+    case SGEMM_ERR_DEVICE: return "device not usable (needs gfx950, the handle's device)";
+    case SGEMM_ERR_VALUE: return "unknown variant or kernel id";
+    case SGEMM_ERR_ALIAS: return "C overlaps A or B";
+    case SGEMM_ERR_UNSUPPORTED: return "forced kernel cannot run these arguments";
+    default: return "unknown status";
+  }
+}
+
+int sgemm_num_kernels(void) { return kNumKernels; }
+
+const char* sgemm_kernel_name(int id) {
+  return (id >= 0 && id < kNumKernels) ? kKernels[id].name : nullptr;
+}
+
+int sgemm_kernel_info(int id, int* variant, int* bm, int* bn, int* bk,
+                      int* threads, int* guarded) {
+  if (id < 0 || id >= kNumKernels) return SGEMM_ERR_VALUE;
+  const KernelDesc& k = kKernels[id];
+  if (variant) *variant = k.variant;
+  if (bm) *bm = k.bm;
+  if (bn) *bn = k.bn;
+  if (bk) *bk = k.bk;
+  if (threads) *threads = k.threads;
+  if (guarded) *guarded = k.guarded;
+  return SGEMM_OK;
+}
+
+int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
+                        int lda, const float* B, int ldb, const float* C,
+                        int ldc) {
+  const RunArgs a = {M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
+                     const_cast<float*>(C), ldc};
+  return select_kernel(variant, a, kChipCus);
+}
+
+void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
+                       int* tn) {
+  int m = 0, n = 0;
+  tile_coords(wg, nwg, tiles_m, tiles_n, m, n);
+  *tm = m;
+  *tn = n;
+}
+
+int sgemm_create(sgemm_handle_t* out) {
+  if (out == nullptr) return SGEMM_ERR_HANDLE;
+  *out = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SGEMM_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SGEMM_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SGEMM_ERR_DEVICE;
+  sgemm_handle_s* h = new (std::nothrow) sgemm_handle_s;
+  if (h == nullptr) return SGEMM_ERR_HIP;
+  h->device = dev;
+  h->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kChipCus;
+  h->variant = SGEMM_VARIANT_AUTO;
+  h->forced_kernel = -1;
+  *out = h;
+  return SGEMM_OK;
+}
+
+int sgemm_destroy(sgemm_handle_t h) {
+  delete h;
+  return SGEMM_OK;
+}
+
+int sgemm_set_variant(sgemm_handle_t h, int variant) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  if (variant != SGEMM_VARIANT_AUTO && variant != SGEMM_VARIANT_MFMA &&
+      variant != SGEMM_VARIANT_VALU)
+    return SGEMM_ERR_VALUE;
+  h->variant = variant;
+  return SGEMM_OK;
+}
+
+int sgemm_set_kernel(sgemm_handle_t h, int kernel_id) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  if (kernel_id < -1 || kernel_id >= kNumKernels) return SGEMM_ERR_VALUE;
+  h->forced_kernel = kernel_id;
+  return SGEMM_OK;
+}
+
+int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
+              const float* A, int lda, const float* B, int ldb, float beta,
+              float* C, int ldc, hipStream_t stream) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  const int st = sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  const RunArgs a = {M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+  int id;
+  if (h->forced_kernel >= 0) {
+    id = h->forced_kernel;
+    if (!kernel_fits(kKernels[id], a)) return SGEMM_ERR_UNSUPPORTED;
+  } else {
+    id = select_kernel(h->variant, a, h->cus);
+    if (id < 0) return id;
+  }
+  const KernelDesc& k = kKernels[id];
+  const long long tm = ceil_div(M, k.bm), tn = ceil_div(N, k.bn);
+  if (tm * tn > INT_MAX) return SGEMM_ERR_UNSUPPORTED;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return SGEMM_ERR_DEVICE;
+  return k.launch(a, (int)tm, (int)tn, stream) == hipSuccess ? SGEMM_OK
+                                                             : SGEMM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+/*
+ * sgemm.h -- FP32 GEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * Operation (page "GEMM 优化之路", problem statement and performance limit):
+ *
+ *     C = alpha * A * B + beta * C
+ *
+ * with A of size M x K, B of size K x N and C of size M x N, all row-major
+ * FP32.  This ABI adds explicit leading dimensions (the page uses K, N, N):
+ *     A(i,k) = A[i*lda + k],  B(k,j) = B[k*ldb + j],  C(i,j) = C[i*ldc + j].
+ * Only the M x N window of C is written; every other element of the C buffer
+ * is left untouched.
+ *
+ * Conventions (the page always evaluates beta*C; the library follows BLAS):
+ *   - beta == 0: C is not read, so it may hold anything, NaN included.
+ *   - K == 0: C = beta*C (zeros when beta == 0).
+ *   - M == 0 or N == 0: nothing is launched; the call returns SGEMM_OK.
+ *   - The summation order inside each output is unspecified but fixed: the
+ *     same inputs on the same device give the same bits on every call.
+ *     Accuracy: |C - exact| <= 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj|
+ *     + |beta*c_ij|) elementwise; results are exact whenever every partial
+ *     sum is an integer below 2^24.
+ *
+ * Memory: A, B and C are device pointers owned by the caller, who also owns
+ * the stream.  C must not overlap A or B.  The library allocates no device
+ * memory: the handle holds only host-side state (device id, properties,
+ * kernel choice).
+ *
+ * Errors: every function returns SGEMM_OK (0) or a negative status; no
+ * function aborts or prints.  Argument errors are found on the host before
+ * any HIP call.  sgemm_run is asynchronous: a fault during execution shows
+ * up at the next synchronisation of the stream, as for any HIP kernel.
+ *
+ * Threading: sgemm_run does not modify the handle, so concurrent calls on one
+ * handle are allowed.  sgemm_set_variant / sgemm_set_kernel / sgemm_destroy
+ * must not race with sgemm_run on the same handle.
+ */
+#ifndef SGEMM_H_
+#define SGEMM_H_
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sgemm_handle_s* sgemm_handle_t;
+
+enum sgemm_status {
+  SGEMM_OK = 0,
+  SGEMM_ERR_HANDLE = -1, /* null handle, or null out-pointer in sgemm_create */
+  SGEMM_ERR_SIZE = -2,   /* M, N or K negative */
+  SGEMM_ERR_LD = -3,     /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+  SGEMM_ERR_NULL = -4,   /* null A/B/C where it would be read or written */
+  SGEMM_ERR_HIP = -5,    /* a HIP runtime call failed (launch, device query) */
+  SGEMM_ERR_DEVICE = -6, /* no device, not gfx950, or not the handle's device */
+  SGEMM_ERR_VALUE = -7,  /* unknown variant or kernel id */
+  SGEMM_ERR_ALIAS = -8,  /* the C window overlaps the A or B window */
+  SGEMM_ERR_UNSUPPORTED = -9 /* forced kernel cannot run these arguments */
+};
+
+/* Kernel families.  MFMA uses the FP32 matrix cores (v_mfma_f32_32x32x2_f32);
+ * VALU uses per-lane FMA outer products on the vector ALUs.  AUTO = MFMA. */
+enum sgemm_variant {
+  SGEMM_VARIANT_AUTO = 0,
+  SGEMM_VARIANT_MFMA = 1,
+  SGEMM_VARIANT_VALU = 2
+};
+
+/* Create a handle bound to the current HIP device, which must be gfx950.
+ * On success *out receives the handle.  Returns SGEMM_ERR_HANDLE if out is
+ * NULL, SGEMM_ERR_DEVICE or SGEMM_ERR_HIP if the device cannot be used. */
+int sgemm_create(sgemm_handle_t* out);
+
+/* Enqueue C = alpha*A*B + beta*C on `stream` (0 = the null stream) and
+ * return without waiting.  The current device must be the handle's device.
+ * Sizes and leading dimensions are in elements.  Arguments are checked as in
+ * sgemm_validate before anything is launched. */
+int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
+              const float* A, int lda, const float* B, int ldb, float beta,
+              float* C, int ldc, hipStream_t stream);
+
+/* Free the handle.  NULL is a no-op returning SGEMM_OK. */
+int sgemm_destroy(sgemm_handle_t h);
+
+/* ---- host-only helpers (no HIP call, no device needed) ---------------- */
+
+/* The argument checks of sgemm_run: sizes, leading dimensions, null
+ * pointers (only where an operand is actually touched) and C overlapping
+ * A or B.  Returns SGEMM_OK or the status sgemm_run would return. */
+int sgemm_validate(int M, int N, int K, const float* A, int lda,
+                   const float* B, int ldb, float beta, const float* C,
+                   int ldc);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* sgemm_status_string(int status);
+
+/* Kernel table.  Ids run from 0 to sgemm_num_kernels()-1. */
+int sgemm_num_kernels(void);
+const char* sgemm_kernel_name(int kernel_id); /* NULL for a bad id */
+/* Tile shape and properties of a kernel; any out-pointer may be NULL.
+ * `guarded` = 1 for kernels that accept any size and alignment, 0 for
+ * kernels that need M%bm == N%bn == K%bk == 0, lda and ldb multiples of 4
+ * and 16-byte aligned A and B. */
+int sgemm_kernel_info(int kernel_id, int* variant, int* bm, int* bn, int* bk,
+                      int* threads, int* guarded);
+
+/* The kernel sgemm_run would launch for these arguments and variant
+ * (SGEMM_VARIANT_*), or a negative status.  Pure function of its inputs. */
+int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
+                        int lda, const float* B, int ldb, const float* C,
+                        int ldc);
+
+/* Diagnostics: the workgroup -> output-tile mapping every kernel uses
+ * (XCD-contiguous renumbering, then bands of tile rows).  For wg in
+ * [0, tiles_m*tiles_n) it stores the tile's row and column indices. */
+void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
+                       int* tn);
+
+/* ---- handle options ----------------------------------------------------- */
+
+/* Choose the kernel family used by sgemm_run on this handle. */
+int sgemm_set_variant(sgemm_handle_t h, int variant);
+
+/* Force one kernel of the table (kernel_id >= 0), or go back to automatic
+ * selection (-1).  A forced unguarded kernel makes sgemm_run return
+ * SGEMM_ERR_UNSUPPORTED for arguments it cannot handle. */
+int sgemm_set_kernel(sgemm_handle_t h, int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_H_ */

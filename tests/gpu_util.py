@@ -1,0 +1,108 @@
+"""Helpers for the GPU parity tests: move seeded operands to the device, run
+the HIP library through its C ABI, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import fp32_gemm_major_amd as sg
+import oracle
+from fp32_gemm_major_amd import workloads as wl
+
+
+def to_device(ops: wl.Operands):
+    dev = torch.device("cuda", 0)
+    A = torch.from_numpy(ops.A).to(dev) if ops.A.size else torch.empty(1, device=dev)
+    B = torch.from_numpy(ops.B).to(dev) if ops.B.size else torch.empty(1, device=dev)
+    C = torch.from_numpy(ops.C).to(dev) if ops.C.size else torch.empty(1, device=dev)
+    return A, B, C
+
+
+def run(h: sg.Handle, ops: wl.Operands, dev=None, stream=None):
+    """Run C = alpha*A*B + beta*C on the GPU; returns the whole C buffer (flat numpy)."""
+    A, B, C = dev if dev is not None else to_device(ops)
+    h.gemm(A, B, C, ops.alpha, ops.beta, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
+           ldb=ops.ldb, ldc=ops.ldc, stream=stream)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()[: ops.C.size].copy()
+
+
+def window(flat, rows, cols, ld):
+    return flat[: rows * ld].reshape(rows, ld)[:, :cols] if rows and cols else \
+        np.zeros((rows, cols), np.float32)
+
+
+def check(got, r, t, K, alpha, beta, c_in, exact=False, what=""):
+    """Elementwise acceptance: within the FP32 bound of the unrounded FP64 r,
+    and equal to r rounded to FP32 when ``exact``.  Returns max(err/bound)."""
+    got = np.asarray(got, np.float32)
+    r = np.asarray(r, np.float64)
+    assert got.shape == r.shape, (got.shape, r.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    if exact:
+        ref = oracle.to_f32(r)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, (f"{what}: {len(bad)} elements differ from the exact "
+                               f"result, first at {bad[0].tolist()}: "
+                               f"{got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}")
+    bound = oracle.error_bound(K, alpha, beta, t, c_in)
+    err = np.abs(got.astype(np.float64) - r)
+    zero = bound == 0
+    assert np.all(err[zero] == 0), f"{what}: nonzero error where the bound is 0"
+    ratio = np.zeros_like(err)
+    ratio[~zero] = err[~zero] / bound[~zero]
+    worst = float(ratio.max()) if ratio.size else 0.0
+    if worst > 1.0:
+        idx = np.unravel_index(np.argmax(ratio), ratio.shape)
+        raise AssertionError(f"{what}: error {err[idx]:.3e} exceeds bound "
+                             f"{bound[idx]:.3e} at {idx} (ratio {worst:.3f})")
+    return worst
+
+
+def check_full(ops: wl.Operands, out_flat, exact=False, what=""):
+    """Compare the whole M x N window with the full oracle; also check that
+    the padding of C (columns N..ldc-1) was not touched."""
+    M, N, K = ops.M, ops.N, ops.K
+    R, T = oracle.gemm(M, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb, ops.beta,
+                       ops.C, ops.ldc)
+    got = window(out_flat, M, N, ops.ldc)
+    c_in = window(ops.C, M, N, ops.ldc)
+    worst = check(got, R, T, K, ops.alpha, ops.beta, c_in, exact, what)
+    if ops.ldc > N and M:
+        pad_in = ops.C[: M * ops.ldc].reshape(M, ops.ldc)[:, N:]
+        pad_out = out_flat[: M * ops.ldc].reshape(M, ops.ldc)[:, N:]
+        assert np.array_equal(pad_in.view(np.uint32), pad_out.view(np.uint32)), \
+            f"{what}: C padding was written"
+    return worst
+
+
+def check_sampled(ops: wl.Operands, out_flat, rows, cols, npoints=4096, seed=0,
+                  exact=False, what=""):
+    """Full rows ``rows``, full columns ``cols`` and random points, each from the
+    oracle's definition (row slabs use the full mode, the rest the point mode)."""
+    M, N, K = ops.M, ops.N, ops.K
+    got_all = window(out_flat, M, N, ops.ldc)
+    c_all = window(ops.C, M, N, ops.ldc)
+    rows = np.asarray(sorted(set(int(x) for x in rows)), np.int64)
+    A2 = ops.A[: M * ops.lda].reshape(M, ops.lda)[rows]
+    C2 = ops.C[: M * ops.ldc].reshape(M, ops.ldc)[rows]
+    R, T = oracle.gemm(len(rows), N, K, ops.alpha, A2, ops.lda, ops.B, ops.ldb,
+                       ops.beta, C2, ops.ldc)
+    worst = check(got_all[rows], R, T, K, ops.alpha, ops.beta, c_all[rows], exact,
+                  what + " rows")
+    rng = np.random.default_rng(seed)
+    pr = np.concatenate([np.repeat(np.arange(M), len(cols)), rng.integers(0, M, npoints)])
+    pc = np.concatenate([np.tile(np.asarray(cols), M), rng.integers(0, N, npoints)])
+    r, t = oracle.gemm_points(M, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb,
+                              ops.beta, ops.C, ops.ldc, pr, pc)
+    worst = max(worst, check(got_all[pr, pc], r, t, K, ops.alpha, ops.beta,
+                             c_all[pr, pc], exact, what + " points"))
+    return worst
+
+
+def edge_rows(M, extra=12, seed=1):
+    base = {0, 1, 2, 31, 32, 33, 63, 64, 127, 128, 129, 255, 256, 257, 511, 512,
+            M // 2, M - 2, M - 1}
+    rng = np.random.default_rng(seed)
+    base |= set(int(x) for x in rng.integers(0, M, extra))
+    return sorted(x for x in base if 0 <= x < M)

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI library (no GPU needed, no kernel launched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import fp32_gemm_major_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgemm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sg.library()
+    names = declared_functions()
+    assert "sgemm_create" in names and "sgemm_run" in names and "sgemm_destroy" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/sgemm.h but not exported"
+    assert set(names) == set(sg.EXPORTED)
+
+
+def test_null_handle_and_destroy():
+    lib = sg.library()
+    assert lib.sgemm_destroy(None) == 0
+    assert lib.sgemm_run(None, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 4096, 4, None) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_set_variant(None, 1) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_set_kernel(None, 0) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_create(None) == sg.SGEMM_ERR_HANDLE
+
+
+def test_validate():
+    v = sg.sgemm_validate
+    A, B, C = 0x10000, 0x20000, 0x40000  # disjoint fake addresses (never touched)
+    assert v(4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_OK
+    assert v(-1, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_SIZE
+    assert v(4, -5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_SIZE
+    assert v(4, 5, -6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_SIZE
+    assert v(4, 5, 6, A, 5, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD
+    assert v(4, 5, 6, A, 6, B, 4, 0.0, C, 5) == sg.SGEMM_ERR_LD
+    assert v(4, 5, 6, A, 6, B, 5, 0.0, C, 4) == sg.SGEMM_ERR_LD
+    assert v(4, 5, 0, None, 1, None, 5, 1.0, C, 5) == sg.SGEMM_OK  # K == 0: A, B unused
+    assert v(4, 5, 0, None, 0, None, 5, 1.0, C, 5) == sg.SGEMM_ERR_LD  # lda >= 1
+    assert v(0, 5, 6, None, 6, None, 5, 1.0, None, 5) == sg.SGEMM_OK  # empty: nothing touched
+    assert v(4, 0, 6, None, 6, None, 1, 1.0, None, 1) == sg.SGEMM_OK
+    assert v(4, 5, 6, None, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_NULL
+    assert v(4, 5, 6, A, 6, None, 5, 0.0, C, 5) == sg.SGEMM_ERR_NULL
+    assert v(4, 5, 6, A, 6, B, 5, 0.0, None, 5) == sg.SGEMM_ERR_NULL
+    # C overlapping A or B
+    assert v(4, 5, 6, A, 6, B, 5, 0.0, A + 4, 5) == sg.SGEMM_ERR_ALIAS
+    assert v(4, 5, 6, A, 6, B, 5, 0.0, B + 4 * 19, 5) == sg.SGEMM_ERR_ALIAS
+    # adjacent but not overlapping: C starts right after A's last element
+    assert v(4, 5, 6, A, 6, B, 5, 0.0, A + 4 * 24, 5) == sg.SGEMM_OK
+
+
+def test_status_strings():
+    for code in range(-9, 1):
+        s = sg.sgemm_status_string(code)
+        assert s and s != "unknown status"
+    assert sg.sgemm_status_string(-100) == "unknown status"
+
+
+def test_kernel_table():
+    table = sg.kernel_table()
+    assert len(table) == sg.sgemm_num_kernels() >= 4
+    assert sg.sgemm_kernel_name(-1) is None and sg.sgemm_kernel_name(len(table)) is None
+    variants = {k["variant"] for k in table}
+    assert variants == {sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU}
+    for k in table:
+        assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
+    # every tile shape has both an aligned and a guarded instance
+    shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table}
+    for s in shapes:
+        g = {k["guarded"] for k in table if (k["variant"], k["bm"], k["bn"], k["bk"]) == s}
+        assert g == {0, 1}, s
+
+
+def test_select_kernel():
+    sel = sg.sgemm_select_kernel
+    A, B, C = 0x10000, 0x20000, 0x40000
+    for variant in (sg.SGEMM_VARIANT_AUTO, sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU):
+        want = sg.SGEMM_VARIANT_MFMA if variant != sg.SGEMM_VARIANT_VALU else variant
+        k = sg.sgemm_kernel_info(sel(variant, 4096, 4096, 4096, A, 4096, B, 4096, C, 4096))
+        assert k["variant"] == want and k["guarded"] == 0
+        assert 4096 % k["bm"] == 0 and 4096 % k["bn"] == 0
+        # K = 777 rows are not 16-byte aligned: guarded instance
+        k = sg.sgemm_kernel_info(sel(variant, 1000, 1500, 777, A, 777, B, 1500, C, 1500))
+        assert k["guarded"] == 1
+        # misaligned base pointer
+        k = sg.sgemm_kernel_info(sel(variant, 1024, 1024, 1024, A + 4, 1024, B, 1024, C, 1024))
+        assert k["guarded"] == 1
+    assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
+    # the headline problem runs on the largest tile; the 11008-wide one fills the chip
+    big = sg.sgemm_kernel_info(sel(0, 4096, 4096, 4096, A, 4096, B, 4096, C, 4096))
+    assert big["bm"] * big["bn"] >= 128 * 256
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (16, 16), (16, 43), (7, 9), (3, 1),
+                                             (1, 5), (8, 8), (13, 86), (32, 32)])
+def test_tile_map_is_a_bijection(tiles_m, tiles_n):
+    nwg = tiles_m * tiles_n
+    seen = set()
+    for wg in range(nwg):
+        tm, tn = sg.sgemm_tile_coords(wg, nwg, tiles_m, tiles_n)
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == nwg
+
+
+def test_tile_map_groups_each_xcd():
+    # 16 x 16 tiles: each XCD (ids congruent mod 8) should own a compact
+    # 4 x 8 block of tiles, i.e. touch only 4 tile rows and 8 tile columns.
+    nwg = 256
+    for x in range(8):
+        coords = [sg.sgemm_tile_coords(wg, nwg, 16, 16) for wg in range(x, nwg, 8)]
+        assert len({c[0] for c in coords}) == 4
+        assert len({c[1] for c in coords}) == 8
+
+
+def test_create_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    rc = sg.library().sgemm_create(ctypes.byref(h))
+    assert rc in (sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_HIP) and not h.value

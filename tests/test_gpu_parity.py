@@ -1,0 +1,281 @@
+"""Parity of the HIP SGEMM (through the C ABI) with the FP64 CPU oracle.
+
+Acceptance, elementwise over the M x N window:
+|C_gpu - r| <= 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj| + |beta*c_ij|), with
+r the unrounded FP64 result; bit-exact (== r rounded to FP32) for integer
+inputs, whose partial sums are all exact in FP32.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import fp32_gemm_major_amd as sg  # noqa: E402
+import oracle  # noqa: E402
+from fp32_gemm_major_amd import workloads as wl  # noqa: E402
+from tests import gpu_util as gu  # noqa: E402
+
+W = wl.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    h = sg.Handle()
+    yield h
+    h.close()
+
+
+@pytest.fixture(autouse=True)
+def _auto_kernel(handle):
+    handle.set_kernel(-1)
+    handle.set_variant(sg.SGEMM_VARIANT_AUTO)
+    yield
+    handle.set_kernel(-1)
+    handle.set_variant(sg.SGEMM_VARIANT_AUTO)
+
+
+KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.kernel_table()
+
+
+# ---- every kernel of the table, on problems spanning several tiles ----------
+
+@pytest.mark.parametrize("k", KERNELS, ids=[k["name"] for k in KERNELS])
+@pytest.mark.parametrize("dist", ["uniform", "int4"])
+def test_each_kernel(handle, k, dist):
+    handle.set_kernel(k["id"])
+    if k["guarded"]:
+        M, N, K = 2 * k["bm"] + 37, k["bn"] + 19, 3 * k["bk"] + 5
+        lda, ldb, ldc = K + 3, N + 1, N + 5
+    else:
+        M, N, K = 2 * k["bm"], 3 * k["bn"], 4 * k["bk"]
+        lda, ldb, ldc = K, N, N + 4
+    w = wl.Workload("case", 900 + k["id"], M, N, K, 1.5, 0.5, dist)
+    ops = wl.operands(w, lda=lda, ldb=ldb, ldc=ldc)
+    out = gu.run(handle, ops)
+    gu.check_full(ops, out, exact=(dist == "int4"), what=k["name"])
+
+
+# ---- the five workloads, in the configuration the benchmark runs ------------
+
+def test_c1_uniform(handle):
+    ops = wl.operands(W["c1_128"])
+    gu.check_full(ops, gu.run(handle, ops), what="c1")
+
+
+def test_c1_integer_bit_exact(handle):
+    ops = wl.operands(W["c1_128_int"])
+    gu.check_full(ops, gu.run(handle, ops), exact=True, what="c1 int")
+
+
+def test_c2_nan_c_beta_zero(handle):
+    ops = wl.operands(W["c2_1024"])
+    assert np.all(np.isnan(ops.C))
+    gu.check_full(ops, gu.run(handle, ops), what="c2")
+
+
+def test_c3_headline_sampled(handle):
+    w = W["c3_4096"]
+    ops = wl.operands(w)
+    out = gu.run(handle, ops)
+    gu.check_sampled(ops, out, gu.edge_rows(w.M), cols=[0, 1, 127, 128, 2047, 4095],
+                     what="c3")
+
+
+def test_c3_integer_sampled_bit_exact(handle):
+    w = W["c3_4096_int"]
+    ops = wl.operands(w)
+    out = gu.run(handle, ops)
+    gu.check_sampled(ops, out, gu.edge_rows(w.M, extra=4), cols=[0, 255, 256, 4095],
+                     exact=True, what="c3 int")
+
+
+def test_c4_edge_full(handle):
+    ops = wl.operands(W["c4_edge"])
+    gu.check_full(ops, gu.run(handle, ops), what="c4")
+
+
+def test_c4_edge_integer_bit_exact(handle):
+    ops = wl.operands(W["c4_edge_int"])
+    gu.check_full(ops, gu.run(handle, ops), exact=True, what="c4 int")
+
+
+def test_c5_mlp_sampled(handle):
+    w = W["c5_mlp"]
+    ops = wl.operands(w)
+    out = gu.run(handle, ops)
+    gu.check_sampled(ops, out, gu.edge_rows(w.M, extra=4),
+                     cols=[0, 255, 256, 5503, 11007], what="c5")
+
+
+@pytest.mark.parametrize("name", ["c3_4096", "c4_edge"])
+def test_valu_variant(handle, name):
+    handle.set_variant(sg.SGEMM_VARIANT_VALU)
+    w = W[name]
+    ops = wl.operands(w)
+    out = gu.run(handle, ops)
+    if w.M * w.N * w.K > 2e9:
+        gu.check_sampled(ops, out, gu.edge_rows(w.M, extra=2), cols=[0, 4095],
+                         what=name + " valu")
+    else:
+        gu.check_full(ops, out, what=name + " valu")
+
+
+# ---- edge cases -----------------------------------------------------------------
+
+TINY = sorted({(m, n, k) for m in (1, 2, 31, 32, 33, 64, 65, 70)
+               for n in (1, 3, 32, 63, 64, 70) for k in (1, 4, 15, 16, 17, 70)
+               if (m * 7 + n * 3 + k) % 4 == 0} | {(1, 1, 1), (70, 70, 70), (5, 9, 0)})
+
+
+@pytest.mark.parametrize("variant", [sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU])
+def test_tiny_sizes_integer_exact(handle, variant):
+    handle.set_variant(variant)
+    for i, (M, N, K) in enumerate(TINY):
+        w = wl.Workload("tiny", 2000 + i, M, N, K, 1.0, -1.0, "int4")
+        ops = wl.operands(w)
+        gu.check_full(ops, gu.run(handle, ops), exact=True, what=f"tiny {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("variant", [sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU])
+def test_tiny_sizes_uniform(handle, variant):
+    handle.set_variant(variant)
+    for i, (M, N, K) in enumerate(TINY[::3]):
+        w = wl.Workload("tiny", 3000 + i, M, N, K, 1.5, 0.5, "uniform")
+        ops = wl.operands(w)
+        gu.check_full(ops, gu.run(handle, ops), what=f"tiny {M}x{N}x{K}")
+
+
+def test_every_guarded_kernel_on_tiny_tails(handle):
+    for k in (k for k in KERNELS if k["guarded"]):
+        handle.set_kernel(k["id"])
+        for i, (M, N, K) in enumerate([(1, 1, 1), (k["bm"] - 1, k["bn"] + 1, k["bk"] - 1),
+                                       (k["bm"] + 1, k["bn"] - 1, k["bk"] + 1),
+                                       (3, 70, 33)]):
+            w = wl.Workload("tail", 4000 + i, M, N, K, 1.0, 1.0, "int4")
+            ops = wl.operands(w, lda=K + 1, ldb=N + 2, ldc=N + 3)
+            gu.check_full(ops, gu.run(handle, ops), exact=True,
+                          what=f"{k['name']} {M}x{N}x{K}")
+
+
+def test_empty_problems_touch_nothing(handle):
+    for M, N in ((0, 16), (16, 0), (0, 0)):
+        C = torch.full((64,), 7.0, device="cuda")
+        A = torch.ones(256, device="cuda")
+        B = torch.ones(256, device="cuda")
+        handle.gemm(A, B, C, 1.0, 0.0, M=M, N=N, K=8, lda=8, ldb=max(N, 1),
+                    ldc=max(N, 1))
+        torch.cuda.synchronize()
+        assert torch.all(C == 7.0)
+
+
+def test_k_zero(handle):
+    w = wl.Workload("k0", 5001, 37, 45, 0, 1.0, -2.0, "uniform")
+    ops = wl.operands(w)
+    out = gu.run(handle, ops)
+    got = gu.window(out, 37, 45, 45)
+    assert np.array_equal(got, (np.float32(-2.0) * gu.window(ops.C, 37, 45, 45)))
+    w = wl.Workload("k0", 5002, 37, 45, 0, 1.0, 0.0, "uniform", "nan")
+    ops = wl.operands(w)
+    got = gu.window(gu.run(handle, ops), 37, 45, 45)
+    assert np.array_equal(got, np.zeros((37, 45), np.float32))
+
+
+def test_alpha_zero_beta_one_keeps_c(handle):
+    w = wl.Workload("ab", 5003, 300, 260, 40, 0.0, 1.0, "uniform")
+    ops = wl.operands(w)
+    got = gu.window(gu.run(handle, ops), 300, 260, 260)
+    assert np.array_equal(got, gu.window(ops.C, 300, 260, 260))
+
+
+def test_precision_canary(handle):
+    """K <= 4, B = 1, A = 1 + m*2^-23: a product path with fewer than 24
+    mantissa bits errs by >= 2^-12 per term, far above the bound (<= 2^-18)."""
+    rng = np.random.default_rng(77)
+    for variant in (sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU):
+        handle.set_variant(variant)
+        for K in (1, 2, 3, 4):
+            M, N = 96, 80
+            m = rng.integers(1, 2 ** 23, size=(M, K)) | 0x7FF  # low bits set
+            a = (1.0 + m * 2.0 ** -23).astype(np.float32)
+            b = np.ones((K, N), np.float32)
+            c = np.full((M, N), np.nan, np.float32)
+            ops = wl.Operands(M, N, K, 1.0, 0.0, a.reshape(-1), K, b.reshape(-1), N,
+                              c.reshape(-1), N)
+            out = gu.run(handle, ops)
+            gu.check_full(ops, out, what=f"canary K={K}")
+            if K == 1:
+                assert np.array_equal(gu.window(out, M, N, N), np.repeat(a, N, axis=1))
+
+
+def test_strided_operands_and_sentinels(handle):
+    """lda/ldb/ldc beyond the minimum: NaN padding of A and B must not leak
+    into the result and the padding of C must stay as it was."""
+    w = wl.Workload("strided", 5004, 513, 301, 129, 1.5, 0.5, "uniform")
+    ops = wl.operands(w, lda=129 + 7, ldb=301 + 11, ldc=301 + 13)
+    gu.check_full(ops, gu.run(handle, ops), what="strided")
+    # aligned sizes with padded leading dimensions (multiples of 4) stay aligned
+    w = wl.Workload("strided", 5005, 512, 512, 256, 1.0, 0.0, "int4")
+    ops = wl.operands(w, lda=256 + 4, ldb=512 + 8, ldc=512 + 12)
+    gu.check_full(ops, gu.run(handle, ops), exact=True, what="strided aligned")
+
+
+def test_misaligned_base_pointers(handle):
+    w = wl.Workload("mis", 5006, 256, 256, 256, 1.0, 0.0, "int4")
+    ops = wl.operands(w)
+    A, B, C = gu.to_device(ops)
+    A1 = torch.empty(A.numel() + 1, device="cuda")
+    A1[1:] = A
+    B1 = torch.empty(B.numel() + 3, device="cuda")
+    B1[3:] = B
+    sel = sg.sgemm_select_kernel(0, 256, 256, 256, A1[1:].data_ptr(), 256,
+                                 B1[3:].data_ptr(), 256, C.data_ptr(), 256)
+    assert sg.sgemm_kernel_info(sel)["guarded"] == 1
+    out = gu.run(handle, ops, dev=(A1[1:], B1[3:], C))
+    gu.check_full(ops, out, exact=True, what="misaligned")
+
+
+def test_deterministic(handle):
+    ops = wl.operands(wl.Workload("det", 2, 1024, 1024, 1024, 1.0, 0.0, "uniform"))
+    A, B, C = gu.to_device(ops)
+    outs = []
+    for _ in range(3):
+        C.fill_(0.0)
+        handle.gemm(A, B, C, 1.0, 0.0, M=1024, N=1024, K=1024, lda=1024, ldb=1024,
+                    ldc=1024)
+        torch.cuda.synchronize()
+        outs.append(C.cpu().numpy().view(np.uint32).copy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_runs_on_a_side_stream(handle):
+    w = wl.Workload("stream", 5007, 384, 512, 96, 1.0, 1.0, "int4")
+    ops = wl.operands(w)
+    dev = gu.to_device(ops)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    out = gu.run(handle, ops, dev=dev, stream=s)
+    gu.check_full(ops, out, exact=True, what="side stream")
+
+
+def test_errors_launch_nothing(handle):
+    A = torch.ones(64 * 64, device="cuda")
+    B = torch.ones(64 * 64, device="cuda")
+    with pytest.raises(sg.SgemmError) as e:
+        handle.gemm(A, B, A, 1.0, 0.0, M=64, N=64, K=64, lda=64, ldb=64, ldc=64)
+    assert e.value.status == sg.SGEMM_ERR_ALIAS
+    with pytest.raises(sg.SgemmError) as e:
+        handle.gemm(A, B, torch.ones(64 * 64, device="cuda"), 1.0, 0.0, M=64, N=64,
+                    K=64, lda=63, ldb=64, ldc=64)
+    assert e.value.status == sg.SGEMM_ERR_LD
+    aligned = [k for k in KERNELS if not k["guarded"]][0]
+    handle.set_kernel(aligned["id"])
+    C = torch.ones(64 * 64, device="cuda")
+    with pytest.raises(sg.SgemmError) as e:
+        handle.gemm(A, B, C, 1.0, 0.0, M=63, N=64, K=64, lda=64, ldb=64, ldc=64)
+    assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(C == 1.0)
