@@ -119,6 +119,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this "
+                         "many bytes (a reference dispatch for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -176,6 +179,14 @@ def main(argv=None):
         "flops_per_launch": flops,
     }
     del dev
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     per_config = None
     if not args.no_per_config:
@@ -207,8 +218,6 @@ def main(argv=None):
             per_config[args.workload + "_valu"] = {
                 "gflops": round(gf, 1),
                 "frac_of_peak": round(gf * 1e9 / rf.PEAK_FP32_FLOPS, 4),
-                "frac_of_unpacked_valu_peak": round(
-                    gf * 1e9 / rf.PEAK_FP32_VALU_UNPACKED_FLOPS, 4),
                 "kernel_ms": round(ms, 5), "kernel": sg.sgemm_kernel_name(kid3)}
             h.set_variant(variant)
             del dev3

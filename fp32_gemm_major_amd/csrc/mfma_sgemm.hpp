@@ -33,6 +33,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 #include "tile_map.hpp"
 
@@ -99,13 +100,21 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 
   f32x4 ra[T::A_VEC], rb[T::B_VEC];
 
+  // Guarded kernels still use 16-byte loads for pieces that lie wholly inside
+  // the operand and start on a 16-byte boundary (every piece starts at a
+  // multiple of 4 elements from the tile corner, so row alignment decides).
+  const bool a_vec_ok =
+      (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15u) == 0);
+  const bool b_vec_ok =
+      (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
+
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v) {
       const int gm = m0 + a_row0 + v * A_ROWS_PER_PASS;
       const int gk = k0 + a_col;
       const float* p = A + (size_t)gm * lda + gk;
-      if (!GUARD) {
+      if (!GUARD || (a_vec_ok && gm < M && gk + 3 < K)) {
         ra[v] = *reinterpret_cast<const f32x4*>(p);
       } else {
 #pragma unroll
@@ -118,7 +127,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       const int gk = k0 + b_row0 + v * B_ROWS_PER_PASS;
       const int gn = n0 + b_col;
       const float* p = B + (size_t)gk * ldb + gn;
-      if (!GUARD) {
+      if (!GUARD || (b_vec_ok && gk < K && gn + 3 < N)) {
         rb[v] = *reinterpret_cast<const f32x4*>(p);
       } else {
 #pragma unroll

@@ -48,7 +48,6 @@ struct KernelDesc {
   const char* name;
   int variant;
   int bm, bn, bk, threads, guarded;
-  int wgs_per_cu;  // resident workgroups per CU the tile is sized for
   float rel_rate;  // relative per-CU throughput, used by the tile choice
   launch_fn launch;
 };
@@ -76,27 +75,27 @@ hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
 // sized for (2 waves of 256 registers, 4 of 128, ...).
 typedef MfmaTile<256, 256, 16, 128, 64, 2> M256x256;  // 8 waves, 1 WG/CU
 typedef MfmaTile<256, 128, 16, 128, 64, 2> M256x128;  // 4 waves, 2 WG/CU
-typedef MfmaTile<128, 128, 16, 64, 64, 2> M128x128;   // 4 waves, 2 WG/CU
-typedef MfmaTile<64, 64, 16, 32, 32, 4> M64x64;       // 4 waves, 4 WG/CU
+typedef MfmaTile<128, 128, 16, 64, 64, 2> M128x128;   // 4 waves, 4 WG/CU
+typedef MfmaTile<64, 64, 16, 32, 32, 4> M64x64;       // 4 waves, 8 WG/CU
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
-#define MFMA_PAIR(T, occ, rate)                                            \
+#define MFMA_PAIR(T, rate)                                                 \
   {"mfma_" #T "_aligned", SGEMM_VARIANT_MFMA, T::BM, T::BN, T::BK,        \
-   T::THREADS, 0, occ, rate, launch_mfma<T, false>},                      \
+   T::THREADS, 0, rate, launch_mfma<T, false>},                           \
   {"mfma_" #T "_guarded", SGEMM_VARIANT_MFMA, T::BM, T::BN, T::BK,        \
-   T::THREADS, 1, occ, rate, launch_mfma<T, true>}
+   T::THREADS, 1, rate, launch_mfma<T, true>}
 
+// Relative rates: throughput of each shape on 4096^3 (a grid that fills the
+// chip for all of them), normalised to the best.
 const KernelDesc kKernels[] = {
-    MFMA_PAIR(M256x256, 1, 1.00f),
-    MFMA_PAIR(M256x128, 2, 0.95f),
-    MFMA_PAIR(M128x128, 2, 0.80f),
-    MFMA_PAIR(M64x64, 4, 0.40f),
+    MFMA_PAIR(M256x256, 0.95f),
+    MFMA_PAIR(M256x128, 0.97f),
+    MFMA_PAIR(M128x128, 1.00f),
+    MFMA_PAIR(M64x64, 0.90f),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
-     V128x128::BK, V128x128::THREADS, 0, 2, 1.0f,
-     launch_valu<V128x128, false>},
+     V128x128::BK, V128x128::THREADS, 0, 1.0f, launch_valu<V128x128, false>},
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
-     V128x128::BK, V128x128::THREADS, 1, 2, 1.0f,
-     launch_valu<V128x128, true>},
+     V128x128::BK, V128x128::THREADS, 1, 1.0f, launch_valu<V128x128, true>},
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -115,14 +114,14 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Modelled time of a tile shape.  A CU holds wgs_per_cu tiles at once and
-// finishes them together, so one round costs wgs_per_cu * bm * bn of work at
-// the tile's relative per-CU rate; the grid takes ceil(tiles / slots) rounds.
+// Modelled time of a tile shape: the busiest CU runs ceil(tiles / cus)
+// tiles, each of bm*bn outputs, at the shape's relative per-CU rate (measured
+// on MI355X with the grid filling the chip; it folds in how well the shape's
+// occupancy hides latency).  Ties keep the earlier, larger shape.
 double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
-  const long long slots = (long long)cus * k.wgs_per_cu;
-  const long long rounds = ceil_div(tiles, slots);
-  return (double)rounds * k.wgs_per_cu * k.bm * k.bn / k.rel_rate;
+  const long long per_cu = ceil_div(tiles, cus);
+  return (double)per_cu * k.bm * k.bn / k.rel_rate;
 }
 
 int select_kernel(int variant, const RunArgs& a, int cus) {

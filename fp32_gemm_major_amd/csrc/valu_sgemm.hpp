@@ -10,12 +10,12 @@
 // lanes of a row group read one contiguous 256-byte span of B per run.
 //
 // It exists to be measured against the MFMA kernel.  Each multiply-add is one
-// v_fma_f32 (one FMA per lane per clock); packed FP32 arithmetic is disabled
-// for this build, so its ceiling is half of the chip's FP32 peak.
+// unpacked v_fmac_f32: packed FP32 arithmetic is disabled for this build.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 #include "mfma_sgemm.hpp"  // f32x4
 #include "tile_map.hpp"
@@ -70,13 +70,21 @@ __global__ void __launch_bounds__(T::THREADS)
 
   f32x4 ra[T::A_VEC], rb[T::B_VEC];
 
+  // Guarded kernels still use 16-byte loads for pieces that lie wholly inside
+  // the operand and start on a 16-byte boundary (every piece starts at a
+  // multiple of 4 elements from the tile corner, so row alignment decides).
+  const bool a_vec_ok =
+      (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15u) == 0);
+  const bool b_vec_ok =
+      (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
+
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v) {
       const int gm = m0 + a_row0 + v * A_ROWS_PER_PASS;
       const int gk = k0 + a_col;
       const float* p = A + (size_t)gm * lda + gk;
-      if (!GUARD) {
+      if (!GUARD || (a_vec_ok && gm < M && gk + 3 < K)) {
         ra[v] = *reinterpret_cast<const f32x4*>(p);
       } else {
 #pragma unroll
@@ -89,7 +97,7 @@ __global__ void __launch_bounds__(T::THREADS)
       const int gk = k0 + b_row0 + v * B_ROWS_PER_PASS;
       const int gn = n0 + b_col;
       const float* p = B + (size_t)gk * ldb + gn;
-      if (!GUARD) {
+      if (!GUARD || (b_vec_ok && gk < K && gn + 3 < N)) {
         rb[v] = *reinterpret_cast<const f32x4*>(p);
       } else {
 #pragma unroll

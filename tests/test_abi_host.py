@@ -97,9 +97,16 @@ def test_select_kernel():
         k = sg.sgemm_kernel_info(sel(variant, 1024, 1024, 1024, A + 4, 1024, B, 1024, C, 1024))
         assert k["guarded"] == 1
     assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
-    # the headline problem runs on the largest tile; the 11008-wide one fills the chip
-    big = sg.sgemm_kernel_info(sel(0, 4096, 4096, 4096, A, 4096, B, 4096, C, 4096))
-    assert big["bm"] * big["bn"] >= 128 * 256
+    # tile shapes the cost model picks for the measured workloads: the large
+    # problems on 128 x 128 tiles, the ones that would leave CUs idle on 64 x 64
+    def shape(M, N, K):
+        k = sg.sgemm_kernel_info(sel(0, M, N, K, A, K, B, N, C, N))
+        return k["bm"], k["bn"]
+    assert shape(4096, 4096, 4096) == (128, 128)
+    assert shape(4096, 11008, 4096) == (128, 128)
+    assert shape(1024, 1024, 1024) == (64, 64)
+    assert shape(128, 128, 128) == (64, 64)
+    assert shape(1000, 1500, 777) == (64, 64)
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (16, 16), (16, 43), (7, 9), (3, 1),
