@@ -1,34 +1,38 @@
 // FP32 SGEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
 //
-// C = alpha*A*B + beta*C, row-major, as stated on "GEMM 优化之路" (problem
-// statement).  The structure keeps the page's data-reuse ladder -- block tile
-// in LDS, per-wave tile in registers, double-buffered K loop, fused alpha/beta
-// update -- but each level is shaped for gfx950 rather than for an FP32 CUDA
-// core:
+// C = alpha*A*B + beta*C, row-major ("GEMM 优化之路", problem statement).
+// The structure keeps the page's data-reuse ladder -- block tile staged in
+// LDS, per-wave register tile, two LDS stages with one barrier per K step,
+// fused alpha/beta update -- with each level shaped for gfx950:
 //
-// * Block tile BM x BN, K step BK.  Global loads are 16-byte (dwordx4) and
-//   coalesced: consecutive lanes read consecutive 16-byte pieces of an A row
-//   (K-contiguous) or a B row (N-contiguous).
-// * LDS keeps A as [m][k] (row stride BK+4 floats) and B as [k][n] (row stride
-//   BN+4).  The A tile is not transposed: an MFMA lane consumes A values of one
-//   row m over several k, so the K-contiguous layout lets one ds_read_b128
-//   feed four MFMAs.  The +4 padding moves successive rows by 4 banks so the
-//   16-byte reads of 16 consecutive rows hit distinct banks.
-// * Each wave owns a WM x WN sub-tile made of 32x32 MFMA blocks, accumulated
-//   in 16 registers per lane per block.
+// * Block tile BM x BN, K step 16.  Each wave owns a WM x WN sub-tile of
+//   32x32 MFMA blocks (16 accumulators per lane per block).
+// * LDS holds A as [m][k] and B as [k][n] with no padding; 16-byte units are
+//   XOR-swizzled instead.  A: unit (row r, column group c) sits at
+//   4r + (c ^ ((r >> 2) & 3)), so the 16-byte reads of 16 consecutive rows at
+//   one column group hit 16 distinct bank groups.  B: the second half of the
+//   k rows is stored with its 32-float halves exchanged, so lanes 0-31 (first
+//   k half) and lanes 32-63 (second half) read different banks.
+// * Lane l of a wave moves 16-byte unit (v*WAVES + wave)*64 + l of a stage.
+//   Its global source is the inverse of the swizzle, so four consecutive lanes
+//   read one 64-byte piece of an A row and consecutive lanes read consecutive
+//   pieces of a B row: loads stay coalesced.
+// * Loader, aligned kernels (GUARD = false): global_load_lds_dwordx4, which
+//   writes lane l's 16 bytes to LDS at M0 + 16*l with no register staging.
+//   The loads of tile t+1 go out before the MFMAs of tile t and are waited for
+//   (vmcnt) just before the barrier that ends tile t.
+// * Loader, guarded kernels (GUARD = true): the same units through registers,
+//   16-byte loads where a piece is inside the operand and 16-byte aligned,
+//   element loads with zero fill elsewhere ("GEMM 优化之路", exercise 2:
+//   out-of-range loads become zeros; no thread leaves before the barriers).
+// * MFMA operands are swapped (B block as the first operand): the 32x32
+//   result is then the transpose of the C block, and each lane holds four
+//   consecutive columns of one C row per register quad.  The epilogue reads C
+//   (only when beta != 0) and writes it with 16-byte accesses when ldc and C
+//   allow, one 32x32 block at a time.
 // * Which k an MFMA lane half uses is free as long as A and B agree: lanes
-//   0-31 take k in [0, BK/2) of the tile and lanes 32-63 take [BK/2, BK), so
-//   both halves read 16-byte runs of A.
-// * Two LDS stages ("double buffering", page section on next optimisation
-//   directions and exercise 3): the global loads of tile t+1 are issued into
-//   registers before the MFMAs of tile t and written to the other stage after
-//   them, with one barrier per K step.
-// * Epilogue: out = alpha*acc + beta*C, C read only when beta != 0.
-// * GUARD = true zero-fills every load outside the M x K / K x N windows and
-//   masks stores outside M x N, so any size, leading dimension and alignment
-//   works ("GEMM 优化之路", exercise 2: out-of-range loads become zeros and
-//   no thread leaves before the barriers).  GUARD = false needs tile-multiple
-//   sizes and 16-byte aligned A/B rows.
+//   0-31 take k in [0, 8) of the K step and lanes 32-63 take [8, 16), so an A
+//   fragment is one 16-byte LDS read per four MFMAs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -41,30 +45,53 @@ namespace sgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int OCC_>
+template <int BM_, int BN_, int WM_, int WN_, int OCC_>
 struct MfmaTile {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
   static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 blocks per wave
-  static constexpr int KH = BK / 2;                 // k per lane half per tile
-  static constexpr int AS = BK + 4;                 // LDS row stride of A
-  static constexpr int BS = BN + 4;                 // LDS row stride of B
-  static constexpr int A_ELEMS = BM * AS;
-  static constexpr int B_ELEMS = BK * BS;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;  // floats per LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE * 4;
-  static constexpr int A_VEC = BM * BK / 4 / THREADS;  // float4 per thread
-  static constexpr int B_VEC = BK * BN / 4 / THREADS;
+  static constexpr int A_UNITS = BM * BK / 4, B_UNITS = BK * BN / 4;
+  static constexpr int A_VEC = A_UNITS / THREADS;  // 16-byte units per lane
+  static constexpr int B_VEC = B_UNITS / THREADS;
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-  static_assert(BK % 8 == 0, "each lane half reads whole float4 runs");
-  static_assert(A_VEC >= 1 && A_VEC * THREADS * 4 == BM * BK, "A loader");
-  static_assert(B_VEC >= 1 && B_VEC * THREADS * 4 == BK * BN, "B loader");
+  static_assert(BN >= 64 && (BN & (BN - 1)) == 0, "B swizzle exchanges 32-float halves");
+  static_assert(A_VEC >= 1 && A_VEC * THREADS == A_UNITS, "A loader");
+  static_assert(B_VEC >= 1 && B_VEC * THREADS == B_UNITS, "B loader");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
 };
+
+// Float offset of A unit (row r, column group c) in a stage.
+__device__ __forceinline__ int a_unit_off(int r, int c) {
+  return 4 * (4 * r + (c ^ ((r >> 2) & 3)));
+}
+// Float offset of B element (k, n) in a stage's B part (row length BN).
+template <int BN>
+__device__ __forceinline__ int b_elem_off(int k, int n) {
+  return k * BN + (n ^ (((k >> 3) & 1) << 5));
+}
+
+// One global_load_lds_dwordx4: this lane's 16 bytes at `src` go to LDS at
+// `lds_base` + 16 * lane.  `lds_base` must be the same for the whole wave.
+// Writing M0 and then issuing a load that writes LDS through M0 needs one
+// wait state in between.
+__device__ __forceinline__ void dma16(const float* src, unsigned lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_base), "v"(src)
+      : "memory", "m0");
+}
 
 template <class T, bool GUARD>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
@@ -72,25 +99,103 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
                       const float* __restrict__ A, int lda,
                       const float* __restrict__ B, int ldb, float beta,
                       float* __restrict__ C, int ldc, int tiles_m,
-                      int tiles_n) {
-  __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
+                      int tiles_n, int band) {
+  __shared__ __attribute__((aligned(1024))) float lds[2 * T::STAGE];
 
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int li = lane & 31, lh = lane >> 5;
 
-  // Loader coordinates: float4 number v of this thread covers
-  // A row a_row[v], columns a_col..a_col+3 of the tile; B likewise.
-  constexpr int A_PER_ROW = T::BK / 4, B_PER_ROW = T::BN / 4;
-  constexpr int A_ROWS_PER_PASS = T::THREADS / A_PER_ROW;
-  constexpr int B_ROWS_PER_PASS = T::THREADS / B_PER_ROW;
-  const int a_row0 = tid / A_PER_ROW, a_col = (tid % A_PER_ROW) * 4;
-  const int b_row0 = tid / B_PER_ROW, b_col = (tid % B_PER_ROW) * 4;
+  // Global coordinates of the units this lane moves (relative to the tile
+  // corner): A unit v covers row a_r[v], columns a_c[v]..+3 of the K step;
+  // B unit v covers k row b_k[v], columns b_n[v]..+3.
+  int a_r[T::A_VEC], a_c[T::A_VEC], b_k[T::B_VEC], b_n[T::B_VEC];
+#pragma unroll
+  for (int v = 0; v < T::A_VEC; ++v) {
+    const int u = (v * T::WAVES + wave) * 64 + lane;
+    a_r[v] = u >> 2;
+    a_c[v] = 4 * ((u & 3) ^ ((a_r[v] >> 2) & 3));
+  }
+#pragma unroll
+  for (int v = 0; v < T::B_VEC; ++v) {
+    const int u = (v * T::WAVES + wave) * 64 + lane;
+    b_k[v] = u / (T::BN / 4);
+    b_n[v] = 4 * ((u % (T::BN / 4)) ^ (((b_k[v] >> 3) & 1) << 3));
+  }
+
+  // Aligned kernels: per-lane global pointers at k0 = 0, and the LDS byte
+  // address of each unit group (wave-uniform).
+  const float* a_ptr[T::A_VEC];
+  const float* b_ptr[T::B_VEC];
+  if (!GUARD) {
+#pragma unroll
+    for (int v = 0; v < T::A_VEC; ++v)
+      a_ptr[v] = A + (size_t)(m0 + a_r[v]) * lda + a_c[v];
+#pragma unroll
+    for (int v = 0; v < T::B_VEC; ++v)
+      b_ptr[v] = B + (size_t)b_k[v] * ldb + n0 + b_n[v];
+  }
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
+
+  auto issue_dma = [&](int kt, int stage) {
+    const unsigned st = lds_u + 4u * (unsigned)(stage * T::STAGE);
+    const size_t k0 = (size_t)kt * T::BK;
+#pragma unroll
+    for (int v = 0; v < T::A_VEC; ++v)
+      dma16(a_ptr[v] + k0, st + 1024u * (unsigned)(v * T::WAVES + wave_u));
+#pragma unroll
+    for (int v = 0; v < T::B_VEC; ++v)
+      dma16(b_ptr[v] + k0 * (size_t)ldb,
+            st + 4u * T::A_ELEMS + 1024u * (unsigned)(v * T::WAVES + wave_u));
+  };
+
+  // Guarded kernels: registers in between, 16-byte loads where possible.
+  const bool a_vec_ok =
+      (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15u) == 0);
+  const bool b_vec_ok =
+      (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
+  f32x4 ra[GUARD ? T::A_VEC : 1], rb[GUARD ? T::B_VEC : 1];
+  auto load_regs = [&](int kt) {
+    const int k0 = kt * T::BK;
+#pragma unroll
+    for (int v = 0; v < T::A_VEC; ++v) {
+      const int gm = m0 + a_r[v], gk = k0 + a_c[v];
+      const float* p = A + (size_t)gm * lda + gk;
+      if (a_vec_ok && gm < M && gk + 3 < K) {
+        ra[v] = *reinterpret_cast<const f32x4*>(p);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ra[v][e] = (gm < M && gk + e < K) ? p[e] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < T::B_VEC; ++v) {
+      const int gk = k0 + b_k[v], gn = n0 + b_n[v];
+      const float* p = B + (size_t)gk * ldb + gn;
+      if (b_vec_ok && gk < K && gn + 3 < N) {
+        rb[v] = *reinterpret_cast<const f32x4*>(p);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rb[v][e] = (gk < K && gn + e < N) ? p[e] : 0.0f;
+      }
+    }
+  };
+  auto store_regs = [&](int stage) {
+    float* st = lds + stage * T::STAGE;
+#pragma unroll
+    for (int v = 0; v < T::A_VEC; ++v)
+      *reinterpret_cast<f32x4*>(st + 256 * (v * T::WAVES + wave) + 4 * lane) = ra[v];
+#pragma unroll
+    for (int v = 0; v < T::B_VEC; ++v)
+      *reinterpret_cast<f32x4*>(st + T::A_ELEMS + 256 * (v * T::WAVES + wave) +
+                                4 * lane) = rb[v];
+  };
 
   f32x16 acc[T::FM][T::FN];
 #pragma unroll
@@ -98,118 +203,115 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x16(0.0f);
 
-  f32x4 ra[T::A_VEC], rb[T::B_VEC];
-
-  // Guarded kernels still use 16-byte loads for pieces that lie wholly inside
-  // the operand and start on a 16-byte boundary (every piece starts at a
-  // multiple of 4 elements from the tile corner, so row alignment decides).
-  const bool a_vec_ok =
-      (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15u) == 0);
-  const bool b_vec_ok =
-      (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v) {
-      const int gm = m0 + a_row0 + v * A_ROWS_PER_PASS;
-      const int gk = k0 + a_col;
-      const float* p = A + (size_t)gm * lda + gk;
-      if (!GUARD || (a_vec_ok && gm < M && gk + 3 < K)) {
-        ra[v] = *reinterpret_cast<const f32x4*>(p);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          ra[v][e] = (gm < M && gk + e < K) ? p[e] : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v) {
-      const int gk = k0 + b_row0 + v * B_ROWS_PER_PASS;
-      const int gn = n0 + b_col;
-      const float* p = B + (size_t)gk * ldb + gn;
-      if (!GUARD || (b_vec_ok && gk < K && gn + 3 < N)) {
-        rb[v] = *reinterpret_cast<const f32x4*>(p);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          rb[v][e] = (gk < K && gn + e < N) ? p[e] : 0.0f;
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    float* As = lds + stage * T::STAGE;
-    float* Bs = As + T::A_ELEMS;
-#pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v)
-      *reinterpret_cast<f32x4*>(As + (a_row0 + v * A_ROWS_PER_PASS) * T::AS +
-                                a_col) = ra[v];
-#pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v)
-      *reinterpret_cast<f32x4*>(Bs + (b_row0 + v * B_ROWS_PER_PASS) * T::BS +
-                                b_col) = rb[v];
-  };
-
-  auto compute_tile = [&](int stage) {
+  auto compute = [&](int stage) {
     const float* As = lds + stage * T::STAGE;
     const float* Bs = As + T::A_ELEMS;
-    const float* a_base = As + (wm * T::WM + li) * T::AS + lh * T::KH;
-    const float* b_base = Bs + (lh * T::KH) * T::BS + wn * T::WN + li;
 #pragma unroll
-    for (int q = 0; q < T::KH / 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       f32x4 a[T::FM];
       float b[T::FN][4];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
-        a[i] = *reinterpret_cast<const f32x4*>(a_base + i * 32 * T::AS + q * 4);
+        a[i] = *reinterpret_cast<const f32x4*>(
+            As + a_unit_off(wm * T::WM + i * 32 + li, lh * 2 + q));
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) b[j][u] = b_base[(q * 4 + u) * T::BS + j * 32];
+        for (int u = 0; u < 4; ++u)
+          b[j][u] = Bs[b_elem_off<T::BN>(lh * 8 + q * 4 + u, wn * T::WN + j * 32 + li)];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
           for (int j = 0; j < T::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][u], b[j][u],
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j][u], a[i][u],
                                                             acc[i][j], 0, 0, 0);
     }
   };
 
+  // Wait until this wave's LDS-bound loads have landed (vmcnt(0); the other
+  // counters are left at their maxima).
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
+
   const int ktiles = (K + T::BK - 1) / T::BK;
   if (ktiles > 0) {
-    load_tile(0);
-    store_tile(0);
+    if (GUARD) {
+      load_regs(0);
+      store_regs(0);
+    } else {
+      issue_dma(0, 0);
+      wait_loads();
+    }
   }
   __syncthreads();
   for (int kt = 0; kt < ktiles; ++kt) {
     const int stage = kt & 1;
     const bool more = kt + 1 < ktiles;
-    if (more) load_tile((kt + 1) * T::BK);
-    compute_tile(stage);
-    if (more) store_tile(stage ^ 1);
+    if (more) {
+      if (GUARD) load_regs(kt + 1);
+      else issue_dma(kt + 1, stage ^ 1);
+    }
+    compute(stage);
+    if (GUARD) {
+      if (more) store_regs(stage ^ 1);
+    } else {
+      wait_loads();
+    }
     __syncthreads();
   }
 
-  // Epilogue.  Block (i, j), register r of lane (li, lh) holds
-  // C(row, col) with row = 8*(r/4) + 4*lh + r%4 and col = li inside the block.
-  const int row_base = m0 + wm * T::WM + lh * 4;
-  const int col_base = n0 + wn * T::WN + li;
+  // Epilogue.  Block (i, j), register 4g + e of lane (li, lh) holds
+  // C(row, col) with row = li and col = 8g + 4lh + e inside the block.
+  const int crow = m0 + wm * T::WM + li;
+  const int ccol = n0 + wn * T::WN + lh * 4;
+  const bool c_vec =
+      (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j)
+    for (int j = 0; j < T::FN; ++j) {
+      const int row = crow + i * 32;
+      const int col = ccol + j * 32;
+      float* p = C + (size_t)row * ldc + col;
+      if (!GUARD && c_vec) {
+        f32x4 cin[4];
+        if (beta != 0.0f) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + (r >> 2) * 8 + (r & 3);
-        const int col = col_base + j * 32;
-        if (GUARD && (row >= M || col >= N)) continue;
-        float* p = C + (size_t)row * ldc + col;
-        float v = alpha * acc[i][j][r];
-        if (beta != 0.0f) v = fmaf(beta, *p, v);
-        *p = v;
+          for (int g = 0; g < 4; ++g) cin[g] = *reinterpret_cast<const f32x4*>(p + 8 * g);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = alpha * acc[i][j][4 * g + e];
+            if (beta != 0.0f) o[e] = fmaf(beta, cin[g][e], o[e]);
+          }
+          *reinterpret_cast<f32x4*>(p + 8 * g) = o;
+        }
+      } else if (!GUARD || row < M) {
+        float cin[16];
+        if (beta != 0.0f) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (!GUARD || col + 8 * g + e < N) cin[4 * g + e] = p[8 * g + e];
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (GUARD && col + 8 * g + e >= N) continue;
+            float o = alpha * acc[i][j][4 * g + e];
+            if (beta != 0.0f) o = fmaf(beta, cin[4 * g + e], o);
+            p[8 * g + e] = o;
+          }
       }
+      // keep one block's C traffic in registers at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 }  // namespace sgemm

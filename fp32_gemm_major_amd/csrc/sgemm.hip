@@ -55,28 +55,31 @@ struct KernelDesc {
 template <class T, bool G>
 hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
                        hipStream_t s) {
-  hipLaunchKernelGGL((mfma_sgemm_kernel<T, G>), dim3(tiles_m * tiles_n),
-                     dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
-                     a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n);
+  const int nwg = tiles_m * tiles_n;
+  hipLaunchKernelGGL((mfma_sgemm_kernel<T, G>), dim3(nwg), dim3(T::THREADS),
+                     0, s, a.M, a.N, a.K, a.alpha, a.A, a.lda, a.B, a.ldb,
+                     a.beta, a.C, a.ldc, tiles_m, tiles_n,
+                     band_rows(tiles_m, nwg));
   return hipGetLastError();
 }
 
 template <class T, bool G>
 hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
                        hipStream_t s) {
-  hipLaunchKernelGGL((valu_sgemm_kernel<T, G>), dim3(tiles_m * tiles_n),
-                     dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
-                     a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n);
+  const int nwg = tiles_m * tiles_n;
+  hipLaunchKernelGGL((valu_sgemm_kernel<T, G>), dim3(nwg), dim3(T::THREADS),
+                     0, s, a.M, a.N, a.K, a.alpha, a.A, a.lda, a.B, a.ldb,
+                     a.beta, a.C, a.ldc, tiles_m, tiles_n,
+                     band_rows(tiles_m, nwg));
   return hipGetLastError();
 }
 
-// Tile shapes.  MfmaTile<BM, BN, BK, WM, WN>: block tile, K step, wave tile.
-// The last parameter is the number of waves per SIMD the register budget is
-// sized for (2 waves of 256 registers, 4 of 128, ...).
-typedef MfmaTile<256, 256, 16, 128, 64, 2> M256x256;  // 8 waves, 1 WG/CU
-typedef MfmaTile<256, 128, 16, 128, 64, 2> M256x128;  // 4 waves, 2 WG/CU
-typedef MfmaTile<128, 128, 16, 64, 64, 2> M128x128;   // 4 waves, 4 WG/CU
-typedef MfmaTile<64, 64, 16, 32, 32, 4> M64x64;       // 4 waves, 8 WG/CU
+// Tile shapes.  MfmaTile<BM, BN, WM, WN, OCC>: block tile, wave tile, and the
+// waves per SIMD the register budget is sized for.
+typedef MfmaTile<256, 256, 128, 64, 2> M256x256;  // 8 waves, 1 WG/CU
+typedef MfmaTile<256, 128, 64, 64, 4> M256x128;   // 8 waves, 2 WG/CU
+typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
+typedef MfmaTile<64, 64, 32, 32, 8> M64x64;       // 4 waves, 8 WG/CU
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
 #define MFMA_PAIR(T, rate)                                                 \
@@ -88,10 +91,10 @@ typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 // Relative rates: throughput of each shape on 4096^3 (a grid that fills the
 // chip for all of them), normalised to the best.
 const KernelDesc kKernels[] = {
-    MFMA_PAIR(M256x256, 0.95f),
-    MFMA_PAIR(M256x128, 0.97f),
-    MFMA_PAIR(M128x128, 1.00f),
-    MFMA_PAIR(M64x64, 0.90f),
+    MFMA_PAIR(M256x256, 1.00f),
+    MFMA_PAIR(M256x128, 0.985f),
+    MFMA_PAIR(M128x128, 0.94f),
+    MFMA_PAIR(M64x64, 0.85f),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
      V128x128::BK, V128x128::THREADS, 0, 1.0f, launch_valu<V128x128, false>},
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
@@ -234,7 +237,7 @@ int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
 void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
                        int* tn) {
   int m = 0, n = 0;
-  tile_coords(wg, nwg, tiles_m, tiles_n, m, n);
+  tile_coords(wg, nwg, tiles_m, tiles_n, band_rows(tiles_m, nwg), m, n);
   *tm = m;
   *tn = n;
 }

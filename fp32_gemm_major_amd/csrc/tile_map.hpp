@@ -3,9 +3,10 @@
 // MI355X has 8 XCDs, each with its own L2, and the dispatcher hands
 // consecutive workgroup ids to the XCDs round-robin (id % 8).  The mapping
 // first renumbers ids so that each XCD owns one contiguous run of the tile
-// sequence, then walks the tile grid in bands of kGroupM tile rows
-// (column-major inside a band).  Tiles that run at the same time on one XCD
-// then share A rows and B columns in that XCD's L2.
+// sequence, then walks the tile grid in bands of `band` tile rows
+// (column-major inside a band).  With `band` near the square root of one
+// XCD's share, that share is a near-square block of tiles, so the XCD reads
+// few A rows and B columns and reuses them from its own L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,22 +14,31 @@
 namespace sgemm {
 
 constexpr int kXcds = 8;
-constexpr int kGroupM = 4;
+
+// Tile rows per band: the largest power of two whose square fits in one
+// XCD's share of the tiles (and that does not exceed the tile rows).
+__host__ __device__ inline int band_rows(int tiles_m, int nwg) {
+  const int per_xcd = (nwg + kXcds - 1) / kXcds;
+  int g = 1;
+  while (2 * g <= tiles_m && 4 * g * g <= per_xcd) g *= 2;
+  return g;
+}
 
 // Bijection from workgroup id `wg` in [0, nwg) to tile (tm, tn), with
-// nwg == tiles_m * tiles_n.
+// nwg == tiles_m * tiles_n and band >= 1.
 __host__ __device__ inline void tile_coords(int wg, int nwg, int tiles_m,
-                                            int tiles_n, int& tm, int& tn) {
+                                            int tiles_n, int band, int& tm,
+                                            int& tn) {
   const int q = nwg / kXcds, r = nwg % kXcds;
   const int xcd = wg % kXcds, idx = wg / kXcds;
   // XCD x owns ids [start(x), start(x) + count(x)), count = q + (x < r).
   const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
   const int lin = start + idx;
-  const int per_band = kGroupM * tiles_n;
-  const int band = lin / per_band;
-  const int first = band * kGroupM;
-  const int rows = tiles_m - first < kGroupM ? tiles_m - first : kGroupM;
-  const int in = lin - band * per_band;
+  const int per_band = band * tiles_n;
+  const int b = lin / per_band;
+  const int first = b * band;
+  const int rows = tiles_m - first < band ? tiles_m - first : band;
+  const int in = lin - b * per_band;
   tm = first + in % rows;
   tn = in / rows;
 }

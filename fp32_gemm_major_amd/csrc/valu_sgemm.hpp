@@ -47,11 +47,11 @@ __global__ void __launch_bounds__(T::THREADS)
                       const float* __restrict__ A, int lda,
                       const float* __restrict__ B, int ldb, float beta,
                       float* __restrict__ C, int ldc, int tiles_m,
-                      int tiles_n) {
+                      int tiles_n, int band) {
   __shared__ __attribute__((aligned(16))) float lds[2 * T::STAGE];
 
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
   const int m0 = tm * T::BM, n0 = tn * T::BN;
   const int tid = threadIdx.x;
   const int ty = tid / T::TX, tx = tid % T::TX;
@@ -157,17 +157,41 @@ __global__ void __launch_bounds__(T::THREADS)
     __syncthreads();
   }
 
+  // Epilogue: lane rows ty*4+i and BM/2+ty*4+i, column runs tx*4..+3 and
+  // BN/2+tx*4..+3; C is read only when beta != 0.
+  const bool c_vec =
+      (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = m0 + (i < 4 ? ty * 4 + i : T::BM / 2 + ty * 4 + (i - 4));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = n0 + (j < 4 ? tx * 4 + j : T::BN / 2 + tx * 4 + (j - 4));
-      if (GUARD && (row >= M || col >= N)) continue;
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0 + h * (T::BN / 2) + tx * 4;
       float* p = C + (size_t)row * ldc + col;
-      float v = alpha * acc[i][j];
-      if (beta != 0.0f) v = fmaf(beta, *p, v);
-      *p = v;
+      if (!GUARD && c_vec) {
+        f32x4 o;
+        f32x4 cin = beta != 0.0f ? *reinterpret_cast<const f32x4*>(p) : f32x4(0.0f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = alpha * acc[i][4 * h + e];
+          if (beta != 0.0f) o[e] = fmaf(beta, cin[e], o[e]);
+        }
+        *reinterpret_cast<f32x4*>(p) = o;
+      } else if (!GUARD || row < M) {
+        float cin[4];
+        if (beta != 0.0f) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!GUARD || col + e < N) cin[e] = p[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (GUARD && col + e >= N) continue;
+          float o = alpha * acc[i][4 * h + e];
+          if (beta != 0.0f) o = fmaf(beta, cin[e], o);
+          p[e] = o;
+        }
+      }
     }
   }
 }

@@ -112,8 +112,10 @@ int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
                         int ldc);
 
 /* Diagnostics: the workgroup -> output-tile mapping every kernel uses
- * (XCD-contiguous renumbering, then bands of tile rows).  For wg in
- * [0, tiles_m*tiles_n) it stores the tile's row and column indices. */
+ * (XCD-contiguous renumbering, then bands of tile rows sized so one XCD's
+ * share of the tiles is a near-square block).  nwg must equal
+ * tiles_m*tiles_n; for wg in [0, nwg) it stores the tile's row and column
+ * indices. */
 void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
                        int* tn);
 

@@ -97,12 +97,13 @@ def test_select_kernel():
         k = sg.sgemm_kernel_info(sel(variant, 1024, 1024, 1024, A + 4, 1024, B, 1024, C, 1024))
         assert k["guarded"] == 1
     assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
-    # tile shapes the cost model picks for the measured workloads: the large
-    # problems on 128 x 128 tiles, the ones that would leave CUs idle on 64 x 64
+    # tile shapes the cost model picks for the measured workloads: 4096^3 on one
+    # 256 x 256 tile per CU, 4096 x 11008 on 128 x 128 (finer rounds), and the
+    # problems that would leave CUs idle on 64 x 64
     def shape(M, N, K):
         k = sg.sgemm_kernel_info(sel(0, M, N, K, A, K, B, N, C, N))
         return k["bm"], k["bn"]
-    assert shape(4096, 4096, 4096) == (128, 128)
+    assert shape(4096, 4096, 4096) == (256, 256)
     assert shape(4096, 11008, 4096) == (128, 128)
     assert shape(1024, 1024, 1024) == (64, 64)
     assert shape(128, 128, 128) == (64, 64)
@@ -121,14 +122,15 @@ def test_tile_map_is_a_bijection(tiles_m, tiles_n):
     assert len(seen) == nwg
 
 
-def test_tile_map_groups_each_xcd():
-    # 16 x 16 tiles: each XCD (ids congruent mod 8) should own a compact
-    # 4 x 8 block of tiles, i.e. touch only 4 tile rows and 8 tile columns.
-    nwg = 256
+@pytest.mark.parametrize("tiles,rows,cols", [(16, 4, 8), (32, 8, 16)])
+def test_tile_map_groups_each_xcd(tiles, rows, cols):
+    # each XCD (workgroup ids congruent mod 8) owns a near-square block of tiles:
+    # 16 x 16 tiles -> 4 x 8 per XCD; 32 x 32 tiles (4096^3 on 128 x 128) -> 8 x 16
+    nwg = tiles * tiles
     for x in range(8):
-        coords = [sg.sgemm_tile_coords(wg, nwg, 16, 16) for wg in range(x, nwg, 8)]
-        assert len({c[0] for c in coords}) == 4
-        assert len({c[1] for c in coords}) == 8
+        coords = [sg.sgemm_tile_coords(wg, nwg, tiles, tiles) for wg in range(x, nwg, 8)]
+        assert len({c[0] for c in coords}) == rows
+        assert len({c[1] for c in coords}) == cols
 
 
 def test_create_without_gpu_fails_cleanly():
