@@ -32,7 +32,7 @@ SGEMM_VARIANT_VALU = 2
 EXPORTED = [
     "sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
     "sgemm_status_string", "sgemm_num_kernels", "sgemm_kernel_name",
-    "sgemm_kernel_info", "sgemm_select_kernel", "sgemm_tile_coords",
+    "sgemm_kernel_info", "sgemm_plan", "sgemm_select_kernel", "sgemm_tile_coords",
     "sgemm_set_variant", "sgemm_set_kernel",
 ]
 
@@ -60,12 +60,14 @@ def _bind(lib):
     lib.sgemm_kernel_name.restype = ctypes.c_char_p
     lib.sgemm_kernel_info.argtypes = [i, ip, ip, ip, ip, ip, ip]
     lib.sgemm_select_kernel.argtypes = [i, i, i, i, p, i, p, i, p, i]
+    lib.sgemm_plan.argtypes = [i, i, i, i, p, i, p, i, p, i, ip, ip]
     lib.sgemm_tile_coords.argtypes = [i, i, i, i, ip, ip]
     lib.sgemm_tile_coords.restype = None
     lib.sgemm_set_variant.argtypes = [p, i]
     lib.sgemm_set_kernel.argtypes = [p, i]
     for name in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
                  "sgemm_num_kernels", "sgemm_kernel_info", "sgemm_select_kernel",
+                 "sgemm_plan",
                  "sgemm_set_variant", "sgemm_set_kernel"):
         getattr(lib, name).restype = i
     return lib
@@ -140,6 +142,17 @@ def sgemm_kernel_info(kernel_id: int) -> dict:
 
 def sgemm_select_kernel(variant, M, N, K, A, lda, B, ldb, C, ldc) -> int:
     return library().sgemm_select_kernel(variant, M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc):
+    """Launches sgemm_run would make: a list of (kernel id, first column, columns)."""
+    kernels = (ctypes.c_int * 2)()
+    split = ctypes.c_int()
+    n = _check(library().sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc,
+                                    kernels, ctypes.byref(split)), "sgemm_plan")
+    if n == 1:
+        return [(kernels[0], 0, N)]
+    return [(kernels[0], 0, split.value), (kernels[1], split.value, N - split.value)]
 
 
 def sgemm_tile_coords(wg, nwg, tiles_m, tiles_n):

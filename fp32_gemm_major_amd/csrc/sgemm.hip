@@ -127,12 +127,48 @@ double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   return (double)per_cu * k.bm * k.bn / k.rel_rate;
 }
 
-int select_kernel(int variant, const RunArgs& a, int cus) {
+// Instance of tile shape `shape` (an aligned kernel id) for these arguments:
+// the aligned kernel when it can run them, else the guarded one.
+int instance_for(int shape, const RunArgs& a) {
+  if (kernel_fits(kKernels[shape], a)) return shape;
+  for (int i = 0; i < kNumKernels; ++i) {
+    const KernelDesc& k = kKernels[i];
+    if (k.guarded && k.variant == kKernels[shape].variant &&
+        k.bm == kKernels[shape].bm && k.bn == kKernels[shape].bn &&
+        k.bk == kKernels[shape].bk)
+      return i;
+  }
+  return SGEMM_ERR_VALUE;
+}
+
+// Columns [n0, n0 + n) of the problem as a problem of its own.
+RunArgs column_part(const RunArgs& a, int n0, int n) {
+  RunArgs p = a;
+  p.N = n;
+  p.B = a.B + n0;
+  p.C = a.C + n0;
+  return p;
+}
+
+// One sgemm_run is one or two launches over column ranges of C.
+struct Launch {
+  int kernel, n0, n;
+};
+struct Plan {
+  int count;
+  Launch part[2];
+};
+
+// Pick the launch plan with the lowest modelled cost.  A single launch uses
+// the best tile shape.  When that leaves the last round of workgroups part
+// empty, the columns can instead be split: the first launch covers whole
+// rounds of a large tile (a multiple of `cus` tiles) and the second the
+// remaining columns with any shape.  A second launch costs about 4 us, which
+// the model converts into output units at this K.
+int make_plan(int variant, const RunArgs& a, int cus, Plan* plan) {
   if (variant == SGEMM_VARIANT_AUTO) variant = SGEMM_VARIANT_MFMA;
   if (variant != SGEMM_VARIANT_MFMA && variant != SGEMM_VARIANT_VALU)
     return SGEMM_ERR_VALUE;
-  // Pick the tile shape with the lowest modelled cost, then its aligned
-  // instance when the arguments allow it, else its guarded instance.
   int best = -1;
   double best_cost = 0.0;
   for (int i = 0; i < kNumKernels; ++i) {
@@ -145,14 +181,38 @@ int select_kernel(int variant, const RunArgs& a, int cus) {
     }
   }
   if (best < 0) return SGEMM_ERR_VALUE;
-  if (kernel_fits(kKernels[best], a)) return best;
+  plan->count = 1;
+  plan->part[0] = Launch{instance_for(best, a), 0, a.N};
+  if (a.K <= 0 || a.M <= 0) return plan->part[0].kernel < 0 ? plan->part[0].kernel : SGEMM_OK;
+  // time of one output unit ~ 2K flops at ~0.55 TFLOP/s per CU
+  const double second_launch = 4e-6 / (2.0 * a.K / 5.5e11);
   for (int i = 0; i < kNumKernels; ++i) {
-    const KernelDesc& k = kKernels[i];
-    if (k.guarded && k.variant == variant && k.bm == kKernels[best].bm &&
-        k.bn == kKernels[best].bn && k.bk == kKernels[best].bk)
-      return i;
+    const KernelDesc& k1 = kKernels[i];
+    if (k1.variant != variant || k1.guarded) continue;
+    const long long tm1 = ceil_div(a.M, k1.bm);
+    const int tn1 = a.N / k1.bn;
+    for (int nt = 1; nt < tn1; ++nt) {
+      if ((tm1 * nt) % cus != 0) continue;
+      const int n1 = nt * k1.bn;
+      const RunArgs p1 = column_part(a, 0, n1);
+      const RunArgs p2 = column_part(a, n1, a.N - n1);
+      const double c1 = tile_cost(k1, p1, cus);
+      for (int j = 0; j < kNumKernels; ++j) {
+        const KernelDesc& k2 = kKernels[j];
+        if (k2.variant != variant || k2.guarded) continue;
+        const double c = c1 + tile_cost(k2, p2, cus) + second_launch;
+        if (c < best_cost) {
+          best_cost = c;
+          plan->count = 2;
+          plan->part[0] = Launch{instance_for(i, p1), 0, n1};
+          plan->part[1] = Launch{instance_for(j, p2), n1, a.N - n1};
+        }
+      }
+    }
   }
-  return SGEMM_ERR_VALUE;
+  for (int p = 0; p < plan->count; ++p)
+    if (plan->part[p].kernel < 0) return plan->part[p].kernel;
+  return SGEMM_OK;
 }
 
 // Half-open byte range of a row-major window, or empty.
@@ -226,12 +286,29 @@ int sgemm_kernel_info(int id, int* variant, int* bm, int* bn, int* bk,
   return SGEMM_OK;
 }
 
+int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
+               const float* B, int ldb, const float* C, int ldc,
+               int* kernels, int* n_split) {
+  const RunArgs a = {M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
+                     const_cast<float*>(C), ldc};
+  Plan plan;
+  const int st = make_plan(variant, a, kChipCus, &plan);
+  if (st != SGEMM_OK) return st;
+  if (kernels) {
+    kernels[0] = plan.part[0].kernel;
+    kernels[1] = plan.count > 1 ? plan.part[1].kernel : -1;
+  }
+  if (n_split) *n_split = plan.count > 1 ? plan.part[1].n0 : N;
+  return plan.count;
+}
+
 int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
                         int lda, const float* B, int ldb, const float* C,
                         int ldc) {
-  const RunArgs a = {M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
-                     const_cast<float*>(C), ldc};
-  return select_kernel(variant, a, kChipCus);
+  int kernels[2];
+  const int n = sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc, kernels,
+                           nullptr);
+  return n < 0 ? n : kernels[0];
 }
 
 void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
@@ -289,22 +366,32 @@ int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
   if (st != SGEMM_OK) return st;
   if (M == 0 || N == 0) return SGEMM_OK;
   const RunArgs a = {M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
-  int id;
+  Plan plan;
   if (h->forced_kernel >= 0) {
-    id = h->forced_kernel;
-    if (!kernel_fits(kKernels[id], a)) return SGEMM_ERR_UNSUPPORTED;
+    if (!kernel_fits(kKernels[h->forced_kernel], a)) return SGEMM_ERR_UNSUPPORTED;
+    plan.count = 1;
+    plan.part[0] = Launch{h->forced_kernel, 0, N};
   } else {
-    id = select_kernel(h->variant, a, h->cus);
-    if (id < 0) return id;
+    const int ps = make_plan(h->variant, a, h->cus, &plan);
+    if (ps != SGEMM_OK) return ps;
   }
-  const KernelDesc& k = kKernels[id];
-  const long long tm = ceil_div(M, k.bm), tn = ceil_div(N, k.bn);
-  if (tm * tn > INT_MAX) return SGEMM_ERR_UNSUPPORTED;
+  for (int p = 0; p < plan.count; ++p) {
+    const KernelDesc& k = kKernels[plan.part[p].kernel];
+    if (ceil_div(M, k.bm) * ceil_div(plan.part[p].n, k.bn) > INT_MAX)
+      return SGEMM_ERR_UNSUPPORTED;
+  }
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return SGEMM_ERR_DEVICE;
-  return k.launch(a, (int)tm, (int)tn, stream) == hipSuccess ? SGEMM_OK
-                                                             : SGEMM_ERR_HIP;
+  for (int p = 0; p < plan.count; ++p) {
+    const Launch& l = plan.part[p];
+    const KernelDesc& k = kKernels[l.kernel];
+    const RunArgs part = column_part(a, l.n0, l.n);
+    if (k.launch(part, (int)ceil_div(M, k.bm), (int)ceil_div(l.n, k.bn),
+                 stream) != hipSuccess)
+      return SGEMM_ERR_HIP;
+  }
+  return SGEMM_OK;
 }
 
 }  // extern "C"

@@ -105,7 +105,18 @@ const char* sgemm_kernel_name(int kernel_id); /* NULL for a bad id */
 int sgemm_kernel_info(int kernel_id, int* variant, int* bm, int* bn, int* bk,
                       int* threads, int* guarded);
 
-/* The kernel sgemm_run would launch for these arguments and variant
+/* How sgemm_run splits a call: it returns the number of launches (1 or 2)
+ * or a negative status.  kernels[0] (and kernels[1], else -1) receive the
+ * kernel ids; *n_split receives the first column of the second launch (N
+ * when there is one launch).  A second launch covers columns
+ * [n_split, N) after the first covers [0, n_split); it is used when whole
+ * rounds of a large tile plus a finer tile for the rest beat one launch.
+ * kernels and n_split may be NULL.  Pure function of its inputs. */
+int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
+               const float* B, int ldb, const float* C, int ldc,
+               int* kernels, int* n_split);
+
+/* The kernel of sgemm_run's first launch for these arguments and variant
  * (SGEMM_VARIANT_*), or a negative status.  Pure function of its inputs. */
 int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
                         int lda, const float* B, int ldb, const float* C,

@@ -98,16 +98,37 @@ def test_select_kernel():
         assert k["guarded"] == 1
     assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
     # tile shapes the cost model picks for the measured workloads: 4096^3 on one
-    # 256 x 256 tile per CU, 4096 x 11008 on 128 x 128 (finer rounds), and the
-    # problems that would leave CUs idle on 64 x 64
+    # 256 x 256 tile per CU, and the problems that would leave CUs idle on
+    # 64 x 64 (4096 x 11008 is covered by the launch-plan test)
     def shape(M, N, K):
         k = sg.sgemm_kernel_info(sel(0, M, N, K, A, K, B, N, C, N))
         return k["bm"], k["bn"]
     assert shape(4096, 4096, 4096) == (256, 256)
-    assert shape(4096, 11008, 4096) == (128, 128)
     assert shape(1024, 1024, 1024) == (64, 64)
     assert shape(128, 128, 128) == (64, 64)
     assert shape(1000, 1500, 777) == (64, 64)
+
+
+def test_plan_splits_only_when_rounds_are_ragged():
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    plan = lambda M, N, K: sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N)
+    # 4096^3 on 256 x 256 tiles is exactly one round: one launch
+    assert len(plan(4096, 4096, 4096)) == 1
+    for M, N, K in [(128, 128, 128), (1024, 1024, 1024), (1000, 1500, 777)]:
+        assert len(plan(M, N, K)) == 1
+    # 4096 x 11008: whole rounds of a large tile, then the remaining columns
+    p = plan(4096, 11008, 4096)
+    assert len(p) == 2
+    (k0, c0, n0), (k1, c1, n1) = p
+    i0, i1 = sg.sgemm_kernel_info(k0), sg.sgemm_kernel_info(k1)
+    assert c0 == 0 and c1 == n0 and n0 + n1 == 11008
+    assert n0 % i0["bn"] == 0 and (4096 // i0["bm"]) * (n0 // i0["bn"]) % 256 == 0
+    assert i0["guarded"] == 0 and i1["guarded"] == (0 if n1 % i1["bn"] == 0 else 1)
+    assert i0["bm"] * i0["bn"] >= i1["bm"] * i1["bn"]
+    # the first launch's kernel is what sgemm_select_kernel reports
+    assert sg.sgemm_select_kernel(0, 4096, 11008, 4096, A, 4096, B, 11008, C, 11008) == k0
+    # tiny K: a second launch never pays
+    assert len(plan(4096, 11008, 16)) == 1
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (16, 16), (16, 43), (7, 9), (3, 1),
