@@ -33,10 +33,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp"),
+                  "valu": ("valu_sgemm.hpp", "tile_map.hpp")}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources that define a kernel family's code and tile order."""
     csrc = os.path.join(ROOT, "fp32_gemm_major_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel.split("_")[0]]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -52,7 +57,7 @@ def measured_traffic(workload: str, kernel: str):
         return None
     for e in data.get("entries", []):
         if (e.get("workload") == workload and e.get("kernel") == kernel
-                and e.get("source_hash") == kernel_source_hash()):
+                and e.get("source_hash") == kernel_source_hash(kernel)):
             return e.get("hbm_bytes_per_launch")
     return None
 
@@ -177,6 +182,8 @@ def main(argv=None):
         "kernel_ms_min": round(min(per), 5),
         "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta),
         "flops_per_launch": flops,
+        # sustained rate of an MFMA chain with no memory traffic, measured now
+        "mfma_chain_tflops": round(sg.mfma_chain_tflops(), 2),
     }
     del dev
     if args.copy_bytes > 0:

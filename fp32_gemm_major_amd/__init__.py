@@ -33,7 +33,7 @@ EXPORTED = [
     "sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
     "sgemm_status_string", "sgemm_num_kernels", "sgemm_kernel_name",
     "sgemm_kernel_info", "sgemm_plan", "sgemm_select_kernel", "sgemm_tile_coords",
-    "sgemm_set_variant", "sgemm_set_kernel",
+    "sgemm_set_variant", "sgemm_set_kernel", "sgemm_diag_mfma_chain",
 ]
 
 
@@ -65,9 +65,10 @@ def _bind(lib):
     lib.sgemm_tile_coords.restype = None
     lib.sgemm_set_variant.argtypes = [p, i]
     lib.sgemm_set_kernel.argtypes = [p, i]
+    lib.sgemm_diag_mfma_chain.argtypes = [i, i, p, p]
     for name in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
                  "sgemm_num_kernels", "sgemm_kernel_info", "sgemm_select_kernel",
-                 "sgemm_plan",
+                 "sgemm_plan", "sgemm_diag_mfma_chain",
                  "sgemm_set_variant", "sgemm_set_kernel"):
         getattr(lib, name).restype = i
     return lib
@@ -168,6 +169,33 @@ def sgemm_set_variant(h, variant: int) -> int:
 
 def sgemm_set_kernel(h, kernel_id: int) -> int:
     return _check(library().sgemm_set_kernel(h, kernel_id), "sgemm_set_kernel")
+
+
+def sgemm_diag_mfma_chain(workgroups, iterations, out, stream=0) -> int:
+    return _check(library().sgemm_diag_mfma_chain(workgroups, iterations, out, stream),
+                  "sgemm_diag_mfma_chain")
+
+
+CHAIN_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 2  # eight 32x32x2 MFMAs
+
+
+def mfma_chain_tflops(workgroups=1024, iterations=4096, reps=3):
+    """Sustained FP32 MFMA TFLOP/s of the device (best of ``reps`` timed runs)."""
+    out = torch.empty(workgroups * 256, device="cuda")
+    stream = torch.cuda.current_stream()
+    sgemm_diag_mfma_chain(workgroups, iterations, out.data_ptr(), stream.cuda_stream)
+    best = None
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        sgemm_diag_mfma_chain(workgroups, iterations, out.data_ptr(), stream.cuda_stream)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e)
+        best = ms if best is None else min(best, ms)
+    flops = CHAIN_FLOPS_PER_WAVE_ITER * iterations * workgroups * 4
+    return flops / (best * 1e-3) / 1e12
 
 
 # ---- torch-tensor convenience ------------------------------------------------

@@ -15,6 +15,7 @@
 
 #include <new>
 
+#include "diag.hpp"
 #include "mfma_sgemm.hpp"
 #include "tile_map.hpp"
 #include "valu_sgemm.hpp"
@@ -317,6 +318,15 @@ void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
   tile_coords(wg, nwg, tiles_m, tiles_n, band_rows(tiles_m, nwg), m, n);
   *tm = m;
   *tn = n;
+}
+
+int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
+                          hipStream_t stream) {
+  if (workgroups <= 0 || iterations < 0) return SGEMM_ERR_SIZE;
+  if (out == nullptr) return SGEMM_ERR_NULL;
+  hipLaunchKernelGGL(mfma_chain_kernel, dim3(workgroups), dim3(kChainThreads),
+                     0, stream, out, iterations, 1.0f, 1.0f);
+  return hipGetLastError() == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 
 int sgemm_create(sgemm_handle_t* out) {

@@ -130,6 +130,17 @@ int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
 void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
                        int* tn);
 
+/* Diagnostics: launch `workgroups` workgroups of 256 lanes that each run
+ * `iterations` rounds of eight independent v_mfma_f32_32x32x2_f32 with no
+ * memory traffic (4096 flops per MFMA per wave, 4 waves per workgroup), then
+ * write one float per lane to `out` (device memory of workgroups*256 floats,
+ * owned by the caller).  Timing it on `stream` gives the matrix-core rate
+ * the device sustains, the ceiling for the SGEMM kernels.  Asynchronous;
+ * returns SGEMM_ERR_SIZE / SGEMM_ERR_NULL / SGEMM_ERR_HIP on bad input or a
+ * failed launch. */
+int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
+                          hipStream_t stream);
+
 /* ---- handle options ----------------------------------------------------- */
 
 /* Choose the kernel family used by sgemm_run on this handle. */
