@@ -5,14 +5,14 @@
 // LDS, per-wave register tile, two LDS stages with one barrier per K step,
 // fused alpha/beta update -- with each level shaped for gfx950:
 //
-// * Block tile BM x BN, K step 16.  Each wave owns a WM x WN sub-tile of
-//   32x32 MFMA blocks (16 accumulators per lane per block).
+// * Block tile BM x BN, K step BK (16, 32 or 64).  Each wave owns a WM x WN
+//   sub-tile of 32x32 MFMA blocks (16 accumulators per lane per block).
 // * LDS holds A as [m][k] and B as [k][n] with no padding; 16-byte units are
-//   XOR-swizzled instead.  A: unit (row r, column group c) sits at
-//   4r + (c ^ ((r >> 2) & 3)), so the 16-byte reads of 16 consecutive rows at
-//   one column group hit 16 distinct bank groups.  B: the second half of the
-//   k rows is stored with its 32-float halves exchanged, so lanes 0-31 (first
-//   k half) and lanes 32-63 (second half) read different banks.
+//   XOR-swizzled instead.  A: unit c of row r (BK/4 units per row) sits at
+//   c ^ ((r / (64/BK)) & (BK/4 - 1)), so the 16-byte reads of 16 consecutive
+//   rows at one column group hit 16 distinct bank groups.  B: the second half
+//   of the k rows is stored with its 32-float halves exchanged, so lanes 0-31
+//   (first k half) and lanes 32-63 (second half) read different banks.
 // * Lane l of a wave moves 16-byte unit (v*WAVES + wave)*64 + l of a stage.
 //   Its global source is the inverse of the swizzle, so four consecutive lanes
 //   read one 64-byte piece of an A row and consecutive lanes read consecutive
@@ -31,8 +31,8 @@
 //   (only when beta != 0) and writes it with 16-byte accesses when ldc and C
 //   allow, one 32x32 block at a time.
 // * Which k an MFMA lane half uses is free as long as A and B agree: lanes
-//   0-31 take k in [0, 8) of the K step and lanes 32-63 take [8, 16), so an A
-//   fragment is one 16-byte LDS read per four MFMAs.
+//   0-31 take k in [0, BK/2) of the K step and lanes 32-63 take [BK/2, BK),
+//   so an A fragment is one 16-byte LDS read per four MFMAs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,36 +47,52 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2, int BK_ = 16>
 struct MfmaTile {
-  static constexpr int BM = BM_, BN = BN_, BK = 16, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
+  // LDS stages of the aligned (direct-load) kernels: loads run S-1 K steps
+  // ahead of the MFMAs.  Small tiles do little work per K step, so they need
+  // more steps in flight to cover the memory latency.  Guarded kernels use 2.
+  static constexpr int S = S_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 blocks per wave
   static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;  // floats per LDS stage
-  static constexpr int LDS_BYTES = 2 * STAGE * 4;
+  static constexpr int LDS_BYTES = S * STAGE * 4;
   static constexpr int A_UNITS = BM * BK / 4, B_UNITS = BK * BN / 4;
   static constexpr int A_VEC = A_UNITS / THREADS;  // 16-byte units per lane
   static constexpr int B_VEC = B_UNITS / THREADS;
+  static constexpr int KH = BK / 2;    // k values per MFMA lane half per K step
+  static constexpr int QN = KH / 4;    // 16-byte A fragments per lane half
+  static constexpr int UPR = BK / 4;   // 16-byte units per A row
+  static constexpr int RPG = 16 / UPR; // A rows per 256-byte bank sweep
+  static_assert(BK == 16 || BK == 32 || BK == 64, "K step");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
   static_assert(BN >= 64 && (BN & (BN - 1)) == 0, "B swizzle exchanges 32-float halves");
   static_assert(A_VEC >= 1 && A_VEC * THREADS == A_UNITS, "A loader");
   static_assert(B_VEC >= 1 && B_VEC * THREADS == B_UNITS, "B loader");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
+  static_assert(S >= 2, "stages");
+  // direct loads in flight per lane when S-1 K steps are outstanding
+  static_assert((S - 1) * (A_VEC + B_VEC) <= 63, "vmcnt range");
 };
 
-// Float offset of A unit (row r, column group c) in a stage.
+// Float offset of A unit (row r, column group c) in a stage: rows of UPR
+// units, unit c of row r stored at c ^ ((r / RPG) & (UPR - 1)), so 16
+// consecutive rows at one column group cover all 16 bank groups.
+template <class T>
 __device__ __forceinline__ int a_unit_off(int r, int c) {
-  return 4 * (4 * r + (c ^ ((r >> 2) & 3)));
+  return 4 * (T::UPR * r + (c ^ ((r / T::RPG) & (T::UPR - 1))));
 }
-// Float offset of B element (k, n) in a stage's B part (row length BN).
-template <int BN>
+// Float offset of B element (k, n) in a stage's B part (row length BN): the
+// second k half has its 32-float halves exchanged.
+template <class T>
 __device__ __forceinline__ int b_elem_off(int k, int n) {
-  return k * BN + (n ^ (((k >> 3) & 1) << 5));
+  return k * T::BN + (n ^ (((k / T::KH) & 1) << 5));
 }
 
 // One global_load_lds_dwordx4: this lane's 16 bytes at `src` go to LDS at
@@ -100,7 +116,8 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
                       const float* __restrict__ B, int ldb, float beta,
                       float* __restrict__ C, int ldc, int tiles_m,
                       int tiles_n, int band) {
-  __shared__ __attribute__((aligned(1024))) float lds[2 * T::STAGE];
+  constexpr int NST = GUARD ? 2 : T::S;  // LDS stages in use
+  __shared__ __attribute__((aligned(1024))) float lds[NST * T::STAGE];
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
@@ -119,14 +136,14 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
   for (int v = 0; v < T::A_VEC; ++v) {
     const int u = (v * T::WAVES + wave) * 64 + lane;
-    a_r[v] = u >> 2;
-    a_c[v] = 4 * ((u & 3) ^ ((a_r[v] >> 2) & 3));
+    a_r[v] = u / T::UPR;
+    a_c[v] = 4 * ((u % T::UPR) ^ ((a_r[v] / T::RPG) & (T::UPR - 1)));
   }
 #pragma unroll
   for (int v = 0; v < T::B_VEC; ++v) {
     const int u = (v * T::WAVES + wave) * 64 + lane;
     b_k[v] = u / (T::BN / 4);
-    b_n[v] = 4 * ((u % (T::BN / 4)) ^ (((b_k[v] >> 3) & 1) << 3));
+    b_n[v] = 4 * ((u % (T::BN / 4)) ^ (((b_k[v] / T::KH) & 1) << 3));
   }
 
   // Aligned kernels: per-lane global pointers at k0 = 0, and the LDS byte
@@ -207,18 +224,18 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     const float* As = lds + stage * T::STAGE;
     const float* Bs = As + T::A_ELEMS;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < T::QN; ++q) {
       f32x4 a[T::FM];
       float b[T::FN][4];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
         a[i] = *reinterpret_cast<const f32x4*>(
-            As + a_unit_off(wm * T::WM + i * 32 + li, lh * 2 + q));
+            As + a_unit_off<T>(wm * T::WM + i * 32 + li, lh * T::QN + q));
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          b[j][u] = Bs[b_elem_off<T::BN>(lh * 8 + q * 4 + u, wn * T::WN + j * 32 + li)];
+          b[j][u] = Bs[b_elem_off<T>(lh * T::KH + q * 4 + u, wn * T::WN + j * 32 + li)];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -230,35 +247,49 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     }
   };
 
-  // Wait until this wave's LDS-bound loads have landed (vmcnt(0); the other
-  // counters are left at their maxima).
-  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  // Wait until at most N of this wave's LDS-bound loads are still in flight
+  // (vmcnt(N); the other counters are left at their maxima).
+  constexpr int PER_STEP = T::A_VEC + T::B_VEC;  // direct loads per K step
+  constexpr int AHEAD = (NST - 2) * PER_STEP;
+  constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
+  auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   const int ktiles = (K + T::BK - 1) / T::BK;
-  if (ktiles > 0) {
-    if (GUARD) {
+  if (GUARD) {
+    if (ktiles > 0) {
       load_regs(0);
       store_regs(0);
-    } else {
-      issue_dma(0, 0);
-      wait_loads();
-    }
-  }
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int stage = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      if (GUARD) load_regs(kt + 1);
-      else issue_dma(kt + 1, stage ^ 1);
-    }
-    compute(stage);
-    if (GUARD) {
-      if (more) store_regs(stage ^ 1);
-    } else {
-      wait_loads();
     }
     __syncthreads();
+    for (int kt = 0; kt < ktiles; ++kt) {
+      const int stage = kt & 1;
+      const bool more = kt + 1 < ktiles;
+      if (more) load_regs(kt + 1);
+      compute(stage);
+      if (more) store_regs(stage ^ 1);
+      __syncthreads();
+    }
+  } else {
+    // Prologue: K steps 0 .. NST-2 in flight, wait for step 0.
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+      if (s < ktiles) issue_dma(s, s);
+    if (ktiles >= NST - 1) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
+    else wait_all();
+    __syncthreads();
+    int stage = 0, next = NST - 1;  // next = stage that receives step kt+NST-1
+    for (int kt = 0; kt < ktiles; ++kt) {
+      // next's previous contents (step kt-1) were read before the last barrier
+      const bool issue = kt + NST - 1 < ktiles;
+      if (issue) issue_dma(kt + NST - 1, next);
+      compute(stage);
+      // step kt+1 must be in LDS: steps kt+2 .. kt+NST-1 may still be in flight
+      if (issue) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
+      else wait_all();
+      __syncthreads();
+      stage = stage + 1 == NST ? 0 : stage + 1;
+      next = next + 1 == NST ? 0 : next + 1;
+    }
   }
 
   // Epilogue.  Block (i, j), register 4g + e of lane (li, lh) holds
