@@ -61,11 +61,12 @@ def _bind(lib):
     f = ctypes.c_float
     i = ctypes.c_int
     p = ctypes.c_void_p
-    lib.oracle_sgemm.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p, i, p, i, i]
-    lib.oracle_sgemm.restype = i
-    lib.oracle_sgemm_points.argtypes = [i, i, i, f, p, i, p, i, f, p, i, i, p, p,
-                                        p, p, i]
-    lib.oracle_sgemm_points.restype = i
+    lib.oracle_sgemm_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i, p, i,
+                                    p, i, i]
+    lib.oracle_sgemm_ex.restype = i
+    lib.oracle_sgemm_points_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i,
+                                           i, p, p, p, p, i]
+    lib.oracle_sgemm_points_ex.restype = i
     return lib
 
 
@@ -105,19 +106,30 @@ def _need(buf, rows, ld, cols, name):
         raise ValueError(f"{name}: {buf.size} elements, need {need}")
 
 
+def _need_ops(A, B, M, N, K, lda, ldb, ta, tb):
+    if ta:
+        _need(A, K, lda, M, "A (stored K x M)")
+    else:
+        _need(A, M, lda, K, "A")
+    if tb:
+        _need(B, N, ldb, K, "B (stored N x K)")
+    else:
+        _need(B, K, ldb, N, "B")
+
+
 def gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
-         nthreads=None, lib=None):
+         nthreads=None, lib=None, ta=False, tb=False):
     """Full product.  Returns ``(r, t)``: FP64 arrays of shape (M, N).
 
     ``A``, ``B``, ``C`` are flat (or any-shape contiguous) FP32 buffers read at
     the given leading dimensions; ``C`` may be None when ``beta == 0``.
-    ``t`` is None when ``with_t`` is False.
+    ``t`` is None when ``with_t`` is False.  ``ta`` / ``tb``: A is stored
+    K x M (A(i,k) = A[k*lda + i]) / B is stored N x K (B(k,j) = B[j*ldb + k]).
     """
     lib = lib or load()
     A = _f32(A, "A")
     B = _f32(B, "B")
-    _need(A, M, lda, K, "A")
-    _need(B, K, ldb, N, "B")
+    _need_ops(A, B, M, N, K, lda, ldb, ta, tb)
     if C is not None:
         C = _f32(C, "C")
         if beta != 0:
@@ -126,22 +138,22 @@ def gemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
         raise ValueError("C is required when beta != 0")
     R = np.zeros((M, N), dtype=np.float64)
     T = np.zeros((M, N), dtype=np.float64) if with_t else None
-    rc = lib.oracle_sgemm(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb,
-                          float(beta), _ptr(C), ldc, _ptr(R), max(N, 1),
-                          _ptr(T), max(N, 1), nthreads or default_threads())
+    rc = lib.oracle_sgemm_ex(int(bool(ta)), int(bool(tb)), M, N, K, float(alpha),
+                             _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                             _ptr(R), max(N, 1), _ptr(T), max(N, 1),
+                             nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle_sgemm rejected the arguments (code {rc})")
     return R, T
 
 
 def gemm_points(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
-                nthreads=None, lib=None):
+                nthreads=None, lib=None, ta=False, tb=False):
     """Outputs at (rows[p], cols[p]) only.  Returns ``(r, t)`` FP64 vectors."""
     lib = lib or load()
     A = _f32(A, "A")
     B = _f32(B, "B")
-    _need(A, M, lda, K, "A")
-    _need(B, K, ldb, N, "B")
+    _need_ops(A, B, M, N, K, lda, ldb, ta, tb)
     if C is not None:
         C = _f32(C, "C")
     elif beta != 0:
@@ -153,10 +165,11 @@ def gemm_points(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
     n = rows.size
     r = np.zeros(n, dtype=np.float64)
     t = np.zeros(n, dtype=np.float64)
-    rc = lib.oracle_sgemm_points(M, N, K, float(alpha), _ptr(A), lda, _ptr(B),
-                                 ldb, float(beta), _ptr(C), ldc, n, _ptr(rows),
-                                 _ptr(cols), _ptr(r), _ptr(t),
-                                 nthreads or default_threads())
+    rc = lib.oracle_sgemm_points_ex(int(bool(ta)), int(bool(tb)), M, N, K,
+                                    float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                                    float(beta), _ptr(C), ldc, n, _ptr(rows),
+                                    _ptr(cols), _ptr(r), _ptr(t),
+                                    nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle_sgemm_points rejected the arguments (code {rc})")
     return r, t

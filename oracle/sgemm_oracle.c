@@ -12,6 +12,11 @@
  * (A(i,k) = A[i*lda + k], B(k,j) = B[k*ldb + j], C(i,j) = C[i*ldc + j]); the
  * page uses the minimal ones (K, N, N).
  *
+ * Transposed operands (the A^T*B and A*B^T cases of the gsyq.cn guide,
+ * section 6.4 step 8): with transa set, the stored matrix is K x M and
+ * A(i,k) = A[k*lda + i]; with transb set, the stored matrix is N x K and
+ * B(k,j) = B[j*ldb + k].  Only the indexing changes; the sums are the same.
+ *
  * Arithmetic is FP64 throughout:
  *   s_ij = sum over k = 0 .. K-1, ascending, of (double)A(i,k) * (double)B(k,j)
  *          with one accumulator per output element;
@@ -36,6 +41,7 @@
 
 typedef struct {
   int M, N, K;
+  int ta, tb;  /* transposed storage of A / B */
   double alpha, beta;
   const float *A, *B, *C;
   long lda, ldb, ldc;
@@ -48,6 +54,14 @@ typedef struct {
   int first, last;
 } job_t;
 
+/* Element (i,k) of A and (k,j) of B under the storage flags. */
+static double a_at(const job_t *j, int i, int k) {
+  return (double)(j->ta ? j->A[(long)k * j->lda + i] : j->A[(long)i * j->lda + k]);
+}
+static double b_at(const job_t *j, int k, int c) {
+  return (double)(j->tb ? j->B[(long)c * j->ldb + k] : j->B[(long)k * j->ldb + c]);
+}
+
 /* Rows [first, last) of the full product. */
 static void *full_rows(void *arg) {
   job_t *j = (job_t *)arg;
@@ -58,10 +72,9 @@ static void *full_rows(void *arg) {
     if (t)
       for (int c = 0; c < j->N; ++c) t[c] = 0.0;
     for (int k = 0; k < j->K; ++k) {
-      const double a = (double)j->A[(long)i * j->lda + k];
-      const float *brow = j->B + (long)k * j->ldb;
+      const double a = a_at(j, i, k);
       for (int c = 0; c < j->N; ++c) {
-        const double p = a * (double)brow[c];
+        const double p = a * b_at(j, k, c);
         r[c] += p;
         if (t) t[c] += fabs(p);
       }
@@ -82,8 +95,7 @@ static void *points(void *arg) {
     const int i = j->rows[p], c = j->cols[p];
     double s = 0.0, a = 0.0;
     for (int k = 0; k < j->K; ++k) {
-      const double q = (double)j->A[(long)i * j->lda + k] *
-                       (double)j->B[(long)k * j->ldb + c];
+      const double q = a_at(j, i, k) * b_at(j, k, c);
       s += q;
       a += fabs(q);
     }
@@ -95,10 +107,12 @@ static void *points(void *arg) {
   return NULL;
 }
 
-static int check_args(int M, int N, int K, int lda, int ldb, int ldc) {
+static int check_args(int ta, int tb, int M, int N, int K, int lda, int ldb,
+                      int ldc) {
   if (M < 0 || N < 0 || K < 0) return -1;
-  if (lda < (K > 1 ? K : 1)) return -2;
-  if (ldb < (N > 1 ? N : 1)) return -2;
+  const int a_cols = ta ? M : K, b_cols = tb ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1)) return -2;
+  if (ldb < (b_cols > 1 ? b_cols : 1)) return -2;
   if (ldc < (N > 1 ? N : 1)) return -2;
   return 0;
 }
@@ -126,18 +140,21 @@ static void run_split(void *(*fn)(void *), job_t *proto, int count,
 
 /*
  * Full product.  R receives r_ij (ldr >= N), T receives t_ij (ldt >= N) or is
- * NULL to skip the magnitude sum (the timing mode).  Returns 0, or -1 for a
- * negative size, -2 for a leading dimension that is too small.
+ * NULL to skip the magnitude sum (the timing mode).  ta / tb select the
+ * transposed storage of A / B.  Returns 0, or -1 for a negative size, -2 for
+ * a leading dimension that is too small.
  */
-int oracle_sgemm(int M, int N, int K, float alpha, const float *A, int lda,
-                 const float *B, int ldb, float beta, const float *C, int ldc,
-                 double *R, int ldr, double *T, int ldt, int nthreads) {
-  int e = check_args(M, N, K, lda, ldb, ldc);
+int oracle_sgemm_ex(int ta, int tb, int M, int N, int K, float alpha,
+                    const float *A, int lda, const float *B, int ldb,
+                    float beta, const float *C, int ldc, double *R, int ldr,
+                    double *T, int ldt, int nthreads) {
+  int e = check_args(ta, tb, M, N, K, lda, ldb, ldc);
   if (e) return e;
   if (ldr < N || (T && ldt < N)) return -2;
   job_t j;
   memset(&j, 0, sizeof j);
   j.M = M; j.N = N; j.K = K;
+  j.ta = ta != 0; j.tb = tb != 0;
   j.alpha = (double)alpha; j.beta = (double)beta;
   j.A = A; j.B = B; j.C = C;
   j.lda = lda; j.ldb = ldb; j.ldc = ldc;
@@ -146,18 +163,25 @@ int oracle_sgemm(int M, int N, int K, float alpha, const float *A, int lda,
   return 0;
 }
 
+int oracle_sgemm(int M, int N, int K, float alpha, const float *A, int lda,
+                 const float *B, int ldb, float beta, const float *C, int ldc,
+                 double *R, int ldr, double *T, int ldt, int nthreads) {
+  return oracle_sgemm_ex(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         R, ldr, T, ldt, nthreads);
+}
+
 /*
  * Selected outputs (rows[p], cols[p]) for p < npts, each an independent dot
  * product with the same definition as above; r_out[p] = r_ij, t_out[p] = t_ij
  * (t_out may be NULL).  Used where the full product would take too long.
  * Returns 0, -1/-2 as above, or -3 for a point outside the M x N window.
  */
-int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
-                        int lda, const float *B, int ldb, float beta,
-                        const float *C, int ldc, int npts, const int *rows,
-                        const int *cols, double *r_out, double *t_out,
-                        int nthreads) {
-  int e = check_args(M, N, K, lda, ldb, ldc);
+int oracle_sgemm_points_ex(int ta, int tb, int M, int N, int K, float alpha,
+                           const float *A, int lda, const float *B, int ldb,
+                           float beta, const float *C, int ldc, int npts,
+                           const int *rows, const int *cols, double *r_out,
+                           double *t_out, int nthreads) {
+  int e = check_args(ta, tb, M, N, K, lda, ldb, ldc);
   if (e) return e;
   for (int p = 0; p < npts; ++p)
     if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -3;
@@ -167,8 +191,18 @@ int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
   j.alpha = (double)alpha; j.beta = (double)beta;
   j.A = A; j.B = B; j.C = C;
   j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.ta = ta != 0; j.tb = tb != 0;
   j.R = r_out; j.T = t_out;
   j.npts = npts; j.rows = rows; j.cols = cols;
   run_split(points, &j, npts, nthreads);
   return 0;
+}
+
+int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
+                        int lda, const float *B, int ldb, float beta,
+                        const float *C, int ldc, int npts, const int *rows,
+                        const int *cols, double *r_out, double *t_out,
+                        int nthreads) {
+  return oracle_sgemm_points_ex(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                ldc, npts, rows, cols, r_out, t_out, nthreads);
 }

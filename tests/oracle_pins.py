@@ -250,6 +250,60 @@ def pin_leading_dims(lib, seed=31):
     assert np.array_equal(rp, R[rows, cols]) and np.array_equal(tp, T[rows, cols])
 
 
+def pin_transposed_storage(lib, seed=37):
+    """Storing A as A^T (K x M) or B as B^T (N x K) and setting the matching
+    flag gives the untransposed result bit for bit (same products, same order);
+    padding of the transposed storage is never read."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 13, 11, 17
+    alpha, beta = 1.5, 0.5
+    A = _dyadic(rng, (M, K))
+    B = _dyadic(rng, (K, N))
+    C = _dyadic(rng, (M, N))
+    R, T = _run(lib, A, B, C, alpha, beta)
+
+    def pad(x, extra):
+        y = np.full((x.shape[0], x.shape[1] + extra), np.nan, np.float32)
+        y[:, :x.shape[1]] = x
+        return y
+
+    At = pad(np.ascontiguousarray(A.T), 3)  # K x (M+3)
+    Bt = pad(np.ascontiguousarray(B.T), 5)  # N x (K+5)
+    for ta, tb in ((True, False), (False, True), (True, True)):
+        a, lda = (At, M + 3) if ta else (A, K)
+        b, ldb = (Bt, K + 5) if tb else (B, N)
+        R2, T2 = oracle.gemm(M, N, K, alpha, a, lda, b, ldb, beta, C, N, lib=lib,
+                             ta=ta, tb=tb)
+        assert np.array_equal(R, R2) and np.array_equal(T, T2), (ta, tb)
+        rows, cols = np.array([0, 5, M - 1]), np.array([N - 1, 3, 0])
+        rp, tp = oracle.gemm_points(M, N, K, alpha, a, lda, b, ldb, beta, C, N, rows,
+                                    cols, lib=lib, ta=ta, tb=tb)
+        assert np.array_equal(rp, R[rows, cols]) and np.array_equal(tp, T[rows, cols])
+
+
+def pin_transposed_bruteforce(lib, seed=41, cases=12):
+    """Transposed storage against exact rational sums on tiny problems."""
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        M, N, K = (int(x) for x in rng.integers(1, 7, size=3))
+        ta, tb = bool(case & 1), bool(case & 2)
+        A = _dyadic(rng, (M, K))
+        B = _dyadic(rng, (K, N))
+        a = np.ascontiguousarray(A.T) if ta else A
+        b = np.ascontiguousarray(B.T) if tb else B
+        R, _ = oracle.gemm(M, N, K, -0.75, a, M if ta else K, b, K if tb else N, 0.0,
+                           None, N, lib=lib, ta=ta, tb=tb)
+        for i in range(M):
+            for j in range(N):
+                exact = Fraction(-0.75) * sum(
+                    (Fraction(float(A[i, k])) * Fraction(float(B[k, j])) for k in range(K)),
+                    Fraction(0))
+                assert abs(Fraction(float(R[i, j])) - exact) <= Fraction(
+                    (K + 3) * U * 0.75 * float(sum(abs(Fraction(float(A[i, k])) *
+                                                       Fraction(float(B[k, j])))
+                                                   for k in range(K)))), (case, i, j)
+
+
 ALL_PINS = [pin_bruteforce_exact, pin_integer_exact, pin_identity,
             pin_permutation, pin_rank1, pin_alpha_beta, pin_transpose,
-            pin_leading_dims]
+            pin_leading_dims, pin_transposed_storage, pin_transposed_bruteforce]

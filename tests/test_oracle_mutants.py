@@ -26,14 +26,16 @@ MUTANTS = {
                          "v -= j->beta * (double)j->C[(long)i * j->ldc + c];\n    j->R[p] = v;"),
     "reads_c_when_beta_zero": ("      if (j->beta != 0.0) v += j->beta * (double)j->C[(long)i * j->ldc + c];\n      r[c] = v;",
                                "      v += j->beta * (double)j->C[(long)i * j->ldc + c];\n      r[c] = v;"),
-    "ldb_for_lda": ("const double a = (double)j->A[(long)i * j->lda + k];",
-                    "const double a = (double)j->A[(long)i * j->ldb + k];"),
-    "b_transposed_points": ("(double)j->B[(long)k * j->ldb + c];",
-                            "(double)j->B[(long)c * j->ldb + k];"),
+    "ldb_for_lda": ("j->A[(long)i * j->lda + k]", "j->A[(long)i * j->ldb + k]"),
+    "b_index_transposed": (": j->B[(long)k * j->ldb + c]", ": j->B[(long)c * j->ldb + k]"),
+    "ta_ignored": ("j->ta ? j->A[(long)k * j->lda + i]", "j->ta ? j->A[(long)i * j->lda + k]"),
+    "tb_ignored": ("j->tb ? j->B[(long)c * j->ldb + k]", "j->tb ? j->B[(long)k * j->ldb + c]"),
+    "flags_swapped": ("return (double)(j->ta ? j->A", "return (double)(j->tb ? j->A"),
+    "points_drop_flags": ("  j.ta = ta != 0; j.tb = tb != 0;\n  j.R = r_out;", "  j.R = r_out;"),
     "alpha_dropped": ("double v = j->alpha * r[c];", "double v = r[c];"),
     "float_accumulator": ("r[c] += p;", "r[c] = (float)(r[c] + p);"),
-    "float_product": ("const double p = a * (double)brow[c];",
-                      "const double p = (float)(a * (double)brow[c]);"),
+    "float_product": ("const double p = a * b_at(j, k, c);",
+                      "const double p = (float)(a * b_at(j, k, c));"),
     "t_signed": ("if (t) t[c] += fabs(p);", "if (t) t[c] += p;"),
     "row_offset": ("double *r = j->R + (long)i * j->ldr;",
                    "double *r = j->R + (long)(i > 0 ? i - 1 : 0) * j->ldr;"),
