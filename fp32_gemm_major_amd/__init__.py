@@ -25,12 +25,16 @@ SGEMM_ERR_VALUE = -7
 SGEMM_ERR_ALIAS = -8
 SGEMM_ERR_UNSUPPORTED = -9
 
+SGEMM_OP_N = 0
+SGEMM_OP_T = 1
+
 SGEMM_VARIANT_AUTO = 0
 SGEMM_VARIANT_MFMA = 1
 SGEMM_VARIANT_VALU = 2
 
 EXPORTED = [
-    "sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
+    "sgemm_create", "sgemm_run", "sgemm_run_ex", "sgemm_destroy", "sgemm_validate",
+    "sgemm_validate_ex", "sgemm_plan_ex",
     "sgemm_status_string", "sgemm_num_kernels", "sgemm_kernel_name",
     "sgemm_kernel_info", "sgemm_plan", "sgemm_select_kernel", "sgemm_tile_coords",
     "sgemm_set_variant", "sgemm_set_kernel", "sgemm_diag_mfma_chain",
@@ -51,6 +55,9 @@ def _bind(lib):
     ip = ctypes.POINTER(ctypes.c_int)
     lib.sgemm_create.argtypes = [ctypes.POINTER(p)]
     lib.sgemm_run.argtypes = [p, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_run_ex.argtypes = [p, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_validate_ex.argtypes = [i, i, i, i, i, p, i, p, i, f, p, i]
+    lib.sgemm_plan_ex.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, ip, ip]
     lib.sgemm_destroy.argtypes = [p]
     lib.sgemm_validate.argtypes = [i, i, i, p, i, p, i, f, p, i]
     lib.sgemm_status_string.argtypes = [i]
@@ -58,7 +65,7 @@ def _bind(lib):
     lib.sgemm_num_kernels.argtypes = []
     lib.sgemm_kernel_name.argtypes = [i]
     lib.sgemm_kernel_name.restype = ctypes.c_char_p
-    lib.sgemm_kernel_info.argtypes = [i, ip, ip, ip, ip, ip, ip]
+    lib.sgemm_kernel_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip, ip]
     lib.sgemm_select_kernel.argtypes = [i, i, i, i, p, i, p, i, p, i]
     lib.sgemm_plan.argtypes = [i, i, i, i, p, i, p, i, p, i, ip, ip]
     lib.sgemm_tile_coords.argtypes = [i, i, i, i, ip, ip]
@@ -68,7 +75,8 @@ def _bind(lib):
     lib.sgemm_diag_mfma_chain.argtypes = [i, i, p, p]
     for name in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
                  "sgemm_num_kernels", "sgemm_kernel_info", "sgemm_select_kernel",
-                 "sgemm_plan", "sgemm_diag_mfma_chain",
+                 "sgemm_plan", "sgemm_diag_mfma_chain", "sgemm_run_ex",
+                 "sgemm_validate_ex", "sgemm_plan_ex",
                  "sgemm_set_variant", "sgemm_set_kernel"):
         getattr(lib, name).restype = i
     return lib
@@ -106,12 +114,25 @@ def sgemm_run(h, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
                                       ldc, stream), "sgemm_run")
 
 
+def sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                 stream=0) -> int:
+    """sgemm_run with operand storage flags (SGEMM_OP_N / SGEMM_OP_T)."""
+    return _check(library().sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda,
+                                         B, ldb, beta, C, ldc, stream),
+                  "sgemm_run_ex")
+
+
 def sgemm_destroy(h) -> int:
     return library().sgemm_destroy(h)
 
 
 def sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc) -> int:
     return library().sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc)
+
+
+def sgemm_validate_ex(transa, transb, M, N, K, A, lda, B, ldb, beta, C, ldc) -> int:
+    return library().sgemm_validate_ex(transa, transb, M, N, K, A, lda, B, ldb, beta,
+                                       C, ldc)
 
 
 def sgemm_status_string(status: int) -> str:
@@ -131,10 +152,10 @@ def sgemm_kernel_name(kernel_id: int):
 
 
 def sgemm_kernel_info(kernel_id: int) -> dict:
-    vals = [ctypes.c_int() for _ in range(6)]
+    vals = [ctypes.c_int() for _ in range(8)]
     _check(library().sgemm_kernel_info(kernel_id, *[ctypes.byref(v) for v in vals]),
            "sgemm_kernel_info")
-    keys = ("variant", "bm", "bn", "bk", "threads", "guarded")
+    keys = ("variant", "bm", "bn", "bk", "threads", "guarded", "transa", "transb")
     d = {k: v.value for k, v in zip(keys, vals)}
     d["name"] = sgemm_kernel_name(kernel_id)
     d["id"] = kernel_id
@@ -145,12 +166,13 @@ def sgemm_select_kernel(variant, M, N, K, A, lda, B, ldb, C, ldc) -> int:
     return library().sgemm_select_kernel(variant, M, N, K, A, lda, B, ldb, C, ldc)
 
 
-def sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc):
-    """Launches sgemm_run would make: a list of (kernel id, first column, columns)."""
+def sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc, transa=0, transb=0):
+    """Launches sgemm_run(_ex) would make: a list of (kernel id, first column, columns)."""
     kernels = (ctypes.c_int * 2)()
     split = ctypes.c_int()
-    n = _check(library().sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc,
-                                    kernels, ctypes.byref(split)), "sgemm_plan")
+    n = _check(library().sgemm_plan_ex(variant, transa, transb, M, N, K, A, lda, B,
+                                       ldb, C, ldc, kernels, ctypes.byref(split)),
+               "sgemm_plan")
     if n == 1:
         return [(kernels[0], 0, N)]
     return [(kernels[0], 0, split.value), (kernels[1], split.value, N - split.value)]
@@ -234,13 +256,15 @@ class Handle:
         sgemm_set_kernel(self.h, kernel_id)
 
     def gemm(self, A, B, C, alpha=1.0, beta=0.0, M=None, N=None, K=None,
-             lda=None, ldb=None, ldc=None, stream=None):
-        """C[:M, :N] = alpha * A[:M, :K] @ B[:K, :N] + beta * C on ``stream``.
+             lda=None, ldb=None, ldc=None, stream=None, transa=False, transb=False):
+        """C[:M, :N] = alpha * op(A) @ op(B) + beta * C on ``stream``.
 
-        A, B, C are float32 CUDA tensors.  2-D tensors with unit column stride
-        give their sizes and leading dimensions; 1-D buffers need explicit
-        sizes and leading dimensions.  ``stream`` defaults to torch's current
-        stream.  Returns immediately (the work is queued on the stream).
+        A, B, C are float32 CUDA tensors.  op(A) is A, or A^T when ``transa``
+        (A stored K x M); op(B) likewise (B stored N x K when ``transb``).
+        2-D tensors with unit column stride give their sizes and leading
+        dimensions; 1-D buffers need explicit sizes and leading dimensions.
+        ``stream`` defaults to torch's current stream.  Returns immediately
+        (the work is queued on the stream).
         """
         for name, t in (("A", A), ("B", B), ("C", C)):
             if t.dtype != torch.float32 or not t.is_cuda:
@@ -248,12 +272,14 @@ class Handle:
             if t.dim() == 2 and t.numel() and t.stride(1) != 1:
                 raise ValueError(f"{name} must be row-major (unit column stride)")
         if A.dim() == 2:
-            M = A.shape[0] if M is None else M
-            K = A.shape[1] if K is None else K
+            ra, ca = A.shape
+            M = (ca if transa else ra) if M is None else M
+            K = (ra if transa else ca) if K is None else K
             lda = max(A.stride(0), 1) if lda is None else lda
         if B.dim() == 2:
-            K = B.shape[0] if K is None else K
-            N = B.shape[1] if N is None else N
+            rb, cb = B.shape
+            K = (cb if transb else rb) if K is None else K
+            N = (rb if transb else cb) if N is None else N
             ldb = max(B.stride(0), 1) if ldb is None else ldb
         if C.dim() == 2:
             ldc = max(C.stride(0), 1) if ldc is None else ldc
@@ -263,8 +289,9 @@ class Handle:
             stream = torch.cuda.current_stream(C.device).cuda_stream
         elif isinstance(stream, torch.cuda.Stream):
             stream = stream.cuda_stream
-        return sgemm_run(self.h, M, N, K, float(alpha), A.data_ptr(), lda,
-                         B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, stream)
+        return sgemm_run_ex(self.h, int(bool(transa)), int(bool(transb)), M, N, K,
+                            float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                            float(beta), C.data_ptr(), ldc, stream)
 
 
 def kernel_table() -> list:

@@ -1,26 +1,31 @@
 // FP32 SGEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
 //
-// C = alpha*A*B + beta*C, row-major ("GEMM 优化之路", problem statement).
-// The structure keeps the page's data-reuse ladder -- block tile staged in
-// LDS, per-wave register tile, two LDS stages with one barrier per K step,
-// fused alpha/beta update -- with each level shaped for gfx950:
+// C = alpha*op(A)*op(B) + beta*C, row-major ("GEMM 优化之路", problem
+// statement), where op(A) = A (stored M x K) or A^T (A stored K x M), and
+// op(B) = B (stored K x N) or B^T (B stored N x K) -- the transposed cases of
+// the gsyq.cn guide (section 6.4, step 8).  The structure keeps the page's
+// data-reuse ladder -- block tile staged in LDS, per-wave register tile, LDS
+// stages with one barrier per K step, fused alpha/beta update -- with each
+// level shaped for gfx950:
 //
 // * Block tile BM x BN, K step BK (16, 32 or 64).  Each wave owns a WM x WN
 //   sub-tile of 32x32 MFMA blocks (16 accumulators per lane per block).
-// * LDS holds A as [m][k] and B as [k][n] with no padding; 16-byte units are
-//   XOR-swizzled instead.  A: unit c of row r (BK/4 units per row) sits at
-//   c ^ ((r / (64/BK)) & (BK/4 - 1)), so the 16-byte reads of 16 consecutive
-//   rows at one column group hit 16 distinct bank groups.  B: the second half
-//   of the k rows is stored with its 32-float halves exchanged, so lanes 0-31
-//   (first k half) and lanes 32-63 (second half) read different banks.
+// * An operand tile in LDS has one of two unpadded layouts, chosen by how the
+//   operand is stored, with 16-byte units XOR-swizzled instead of padding:
+//   - K-contiguous (A as stored, or B^T): rows of the outer index (m or n)
+//     holding BK/4 units of four consecutive k; unit c of row r sits at
+//     c ^ ((r / (64/BK)) & (BK/4 - 1)), so the 16-byte reads of 16
+//     consecutive rows at one column group hit 16 distinct bank groups.
+//   - outer-contiguous (B as stored, or A^T): rows of k holding the outer
+//     index; the second k half of every K step has its 32-float halves
+//     exchanged, so the two MFMA lane halves read different banks.
 // * Lane l of a wave moves 16-byte unit (v*WAVES + wave)*64 + l of a stage.
-//   Its global source is the inverse of the swizzle, so four consecutive lanes
-//   read one 64-byte piece of an A row and consecutive lanes read consecutive
-//   pieces of a B row: loads stay coalesced.
+//   Its global source is the inverse of the swizzle, so consecutive lanes
+//   read consecutive 16-byte pieces of a stored row: loads stay coalesced.
 // * Loader, aligned kernels (GUARD = false): global_load_lds_dwordx4, which
 //   writes lane l's 16 bytes to LDS at M0 + 16*l with no register staging.
-//   The loads of tile t+1 go out before the MFMAs of tile t and are waited for
-//   (vmcnt) just before the barrier that ends tile t.
+//   The loads of step t+S-1 go out before the MFMAs of step t and are waited
+//   for (vmcnt) before the barrier that ends step t+S-2.
 // * Loader, guarded kernels (GUARD = true): the same units through registers,
 //   16-byte loads where a piece is inside the operand and 16-byte aligned,
 //   element loads with zero fill elsewhere ("GEMM 优化之路", exercise 2:
@@ -31,8 +36,9 @@
 //   (only when beta != 0) and writes it with 16-byte accesses when ldc and C
 //   allow, one 32x32 block at a time.
 // * Which k an MFMA lane half uses is free as long as A and B agree: lanes
-//   0-31 take k in [0, BK/2) of the K step and lanes 32-63 take [BK/2, BK),
-//   so an A fragment is one 16-byte LDS read per four MFMAs.
+//   0-31 take k in [0, BK/2) of the K step and lanes 32-63 take [BK/2, BK).
+//   A K-contiguous fragment is then one 16-byte LDS read per four MFMAs; an
+//   outer-contiguous one is one 4-byte read per MFMA.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,17 +57,16 @@ template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2, int BK_ = 16
           int KG_ = 1>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
+  // LDS stages of the aligned (direct-load) kernels: loads run S-1 K steps
+  // ahead of the MFMAs.  Guarded kernels use 2.
+  static constexpr int S = S_;
   // K groups: KG groups of waves split every stage's K range (KG*BK values)
   // and their partial sums are added through LDS at the end, group 1 first.
   // This multiplies the waves per tile for problems with few tiles without a
   // workspace or a second pass.
   static constexpr int KG = KG_;
   static constexpr int BKS = KG * BK;  // K values per LDS stage
-  static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
-  // LDS stages of the aligned (direct-load) kernels: loads run S-1 K steps
-  // ahead of the MFMAs.  Small tiles do little work per K step, so they need
-  // more steps in flight to cover the memory latency.  Guarded kernels use 2.
-  static constexpr int S = S_;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int WAVES_MN = WAVES_M * WAVES_N;  // waves of one K group
   static constexpr int WAVES = WAVES_MN * KG;
@@ -74,38 +79,49 @@ struct MfmaTile {
   static constexpr int A_VEC = A_UNITS / THREADS;  // 16-byte units per lane
   static constexpr int B_VEC = B_UNITS / THREADS;
   static constexpr int KH = BK / 2;    // k values per MFMA lane half per K step
-  static constexpr int QN = KH / 4;    // 16-byte A fragments per lane half
-  static constexpr int UPR = BKS / 4;  // 16-byte units per A row
-  static constexpr int RPG = 16 / UPR; // A rows per 256-byte bank sweep
-  static_assert(BK == 16 || BK == 32 || BK == 64, "K step");
-  static_assert(BKS <= 64, "A rows of at most 16 units");
-  static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
-  // floats the K groups 1..KG-1 leave in LDS for group 0
-  static constexpr int RED_ELEMS = (KG - 1) * WAVES_MN * 64 * 16 * FM * FN;
-  static_assert(RED_ELEMS <= (S_ < 2 ? 2 : S_) * STAGE, "reduction fits in LDS");
+  static constexpr int QN = KH / 4;    // four-k fragments per lane half
+  static constexpr int UPR = BKS / 4;  // 16-byte units per K-contiguous row
+  static constexpr int RPG = 16 / UPR; // such rows per 256-byte bank sweep
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-  static_assert(BN >= 64 && (BN & (BN - 1)) == 0, "B swizzle exchanges 32-float halves");
+  static_assert(BM >= 64 && (BM & (BM - 1)) == 0, "outer-contiguous A swizzle");
+  static_assert(BN >= 64 && (BN & (BN - 1)) == 0, "outer-contiguous B swizzle");
   static_assert(A_VEC >= 1 && A_VEC * THREADS == A_UNITS, "A loader");
   static_assert(B_VEC >= 1 && B_VEC * THREADS == B_UNITS, "B loader");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
   static_assert(S >= 2, "stages");
-  // direct loads in flight per lane when S-1 K steps are outstanding
   static_assert((S - 1) * (A_VEC + B_VEC) <= 63, "vmcnt range");
+  static_assert(BK == 16 || BK == 32 || BK == 64, "K step");
+  static_assert(BKS <= 64, "K-contiguous rows of at most 16 units");
+  static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
+  // floats the K groups 1..KG-1 leave in LDS for group 0
+  static constexpr int RED_ELEMS = (KG - 1) * WAVES_MN * 64 * 16 * FM * FN;
+  static_assert(RED_ELEMS <= 2 * STAGE, "reduction fits in LDS");
 };
 
-// Float offset of A unit (row r, column group c) in a stage: rows of UPR
-// units, unit c of row r stored at c ^ ((r / RPG) & (UPR - 1)), so 16
-// consecutive rows at one column group cover all 16 bank groups.
+// K-contiguous tile: float offset of unit c (four k) of outer row r.
 template <class T>
-__device__ __forceinline__ int a_unit_off(int r, int c) {
+__device__ __forceinline__ int kc_unit_off(int r, int c) {
   return 4 * (T::UPR * r + (c ^ ((r / T::RPG) & (T::UPR - 1))));
 }
-// Float offset of B element (k, n) in a stage's B part (row length BN): the
-// second k half has its 32-float halves exchanged.
-template <class T>
-__device__ __forceinline__ int b_elem_off(int k, int n) {
-  return k * T::BN + (n ^ (((k / T::KH) & 1) << 5));
+// Outer-contiguous tile of width X: float offset of element (k, x).
+template <class T, int X>
+__device__ __forceinline__ int oc_elem_off(int k, int x) {
+  return k * X + (x ^ (((k / T::KH) & 1) << 5));
+}
+
+// Tile-relative coordinates of 16-byte unit u of an operand tile with outer
+// size X: the unit covers (outer, k..k+3) in a K-contiguous tile and
+// (outer..outer+3, k) in an outer-contiguous one.
+template <class T, int X, bool KCONTIG>
+__device__ __forceinline__ void unit_coords(int u, int& outer, int& k) {
+  if (KCONTIG) {
+    outer = u / T::UPR;
+    k = 4 * ((u % T::UPR) ^ ((outer / T::RPG) & (T::UPR - 1)));
+  } else {
+    k = u / (X / 4);
+    outer = 4 * ((u % (X / 4)) ^ (((k / T::KH) & 1) << 3));
+  }
 }
 
 // One global_load_lds_dwordx4: this lane's 16 bytes at `src` go to LDS at
@@ -122,13 +138,16 @@ __device__ __forceinline__ void dma16(const float* src, unsigned lds_base) {
       : "memory", "m0");
 }
 
-template <class T, bool GUARD>
+// TA: A stored K x M (op(A) = A^T).  TB: B stored N x K (op(B) = B^T).
+template <class T, bool GUARD, bool TA, bool TB>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
     mfma_sgemm_kernel(int M, int N, int K, float alpha,
                       const float* __restrict__ A, int lda,
                       const float* __restrict__ B, int ldb, float beta,
                       float* __restrict__ C, int ldc, int tiles_m,
                       int tiles_n, int band) {
+  constexpr bool A_KC = !TA;  // A tile K-contiguous
+  constexpr bool B_KC = TB;   // B tile K-contiguous
   constexpr int NST = GUARD ? 2 : T::S;  // LDS stages in use
   __shared__ __attribute__((aligned(1024))) float lds[NST * T::STAGE];
 
@@ -144,46 +163,46 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   const int wm = wmn / T::WAVES_N, wn = wmn % T::WAVES_N;
   const int li = lane & 31, lh = lane >> 5;
 
-  // Global coordinates of the units this lane moves (relative to the tile
-  // corner): A unit v covers row a_r[v], columns a_c[v]..+3 of the K step;
-  // B unit v covers k row b_k[v], columns b_n[v]..+3.
-  int a_r[T::A_VEC], a_c[T::A_VEC], b_k[T::B_VEC], b_n[T::B_VEC];
+  // Tile coordinates of the units this lane moves.
+  int a_o[T::A_VEC], a_k[T::A_VEC], b_o[T::B_VEC], b_k[T::B_VEC];
 #pragma unroll
-  for (int v = 0; v < T::A_VEC; ++v) {
-    const int u = (v * T::WAVES + wave) * 64 + lane;
-    a_r[v] = u / T::UPR;
-    a_c[v] = 4 * ((u % T::UPR) ^ ((a_r[v] / T::RPG) & (T::UPR - 1)));
-  }
+  for (int v = 0; v < T::A_VEC; ++v)
+    unit_coords<T, T::BM, A_KC>((v * T::WAVES + wave) * 64 + lane, a_o[v], a_k[v]);
 #pragma unroll
-  for (int v = 0; v < T::B_VEC; ++v) {
-    const int u = (v * T::WAVES + wave) * 64 + lane;
-    b_k[v] = u / (T::BN / 4);
-    b_n[v] = 4 * ((u % (T::BN / 4)) ^ (((b_k[v] / T::KH) & 1) << 3));
-  }
+  for (int v = 0; v < T::B_VEC; ++v)
+    unit_coords<T, T::BN, B_KC>((v * T::WAVES + wave) * 64 + lane, b_o[v], b_k[v]);
 
-  // Aligned kernels: per-lane global pointers at k0 = 0, and the LDS byte
-  // address of each unit group (wave-uniform).
+  // Address of a stored element: (outer, k) of A or B at K offset k0.
+  auto a_addr = [&](int o, int k) -> const float* {
+    return TA ? A + (size_t)k * lda + (m0 + o) : A + (size_t)(m0 + o) * lda + k;
+  };
+  auto b_addr = [&](int o, int k) -> const float* {
+    return TB ? B + (size_t)(n0 + o) * ldb + k : B + (size_t)k * ldb + (n0 + o);
+  };
+
+  // Aligned kernels: per-lane pointers at K step 0, advanced by a fixed
+  // stride per step; LDS destinations are wave-uniform.
   const float* a_ptr[T::A_VEC];
   const float* b_ptr[T::B_VEC];
   if (!GUARD) {
 #pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v)
-      a_ptr[v] = A + (size_t)(m0 + a_r[v]) * lda + a_c[v];
+    for (int v = 0; v < T::A_VEC; ++v) a_ptr[v] = a_addr(a_o[v], a_k[v]);
 #pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v)
-      b_ptr[v] = B + (size_t)b_k[v] * ldb + n0 + b_n[v];
+    for (int v = 0; v < T::B_VEC; ++v) b_ptr[v] = b_addr(b_o[v], b_k[v]);
   }
+  const size_t a_step = TA ? (size_t)T::BKS * lda : (size_t)T::BKS;
+  const size_t b_step = TB ? (size_t)T::BKS : (size_t)T::BKS * ldb;
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
 
   auto issue_dma = [&](int kt, int stage) {
     const unsigned st = lds_u + 4u * (unsigned)(stage * T::STAGE);
-    const size_t k0 = (size_t)kt * T::BKS;
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v)
-      dma16(a_ptr[v] + k0, st + 1024u * (unsigned)(v * T::WAVES + wave_u));
+      dma16(a_ptr[v] + (size_t)kt * a_step,
+            st + 1024u * (unsigned)(v * T::WAVES + wave_u));
 #pragma unroll
     for (int v = 0; v < T::B_VEC; ++v)
-      dma16(b_ptr[v] + k0 * (size_t)ldb,
+      dma16(b_ptr[v] + (size_t)kt * b_step,
             st + 4u * T::A_ELEMS + 1024u * (unsigned)(v * T::WAVES + wave_u));
   };
 
@@ -193,30 +212,34 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   const bool b_vec_ok =
       (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
   f32x4 ra[GUARD ? T::A_VEC : 1], rb[GUARD ? T::B_VEC : 1];
+  // Load one unit: KCONTIG runs over k (bounds: outer < OUTER, k < K), else
+  // over the outer index (bounds: k < K, outer < OUTER).
+  auto load_unit = [&](const float* p, bool kcontig, bool vec_ok, int outer,
+                       int outer_n, int k) -> f32x4 {
+    f32x4 x;
+    if (kcontig) {
+      if (vec_ok && outer < outer_n && k + 3 < K)
+        return *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (outer < outer_n && k + e < K) ? p[e] : 0.0f;
+    } else {
+      if (vec_ok && k < K && outer + 3 < outer_n)
+        return *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (k < K && outer + e < outer_n) ? p[e] : 0.0f;
+    }
+    return x;
+  };
   auto load_regs = [&](int kt) {
     const int k0 = kt * T::BKS;
 #pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v) {
-      const int gm = m0 + a_r[v], gk = k0 + a_c[v];
-      const float* p = A + (size_t)gm * lda + gk;
-      if (a_vec_ok && gm < M && gk + 3 < K) {
-        ra[v] = *reinterpret_cast<const f32x4*>(p);
-      } else {
+    for (int v = 0; v < T::A_VEC; ++v)
+      ra[v] = load_unit(a_addr(a_o[v], k0 + a_k[v]), A_KC, a_vec_ok, m0 + a_o[v],
+                        M, k0 + a_k[v]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ra[v][e] = (gm < M && gk + e < K) ? p[e] : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v) {
-      const int gk = k0 + b_k[v], gn = n0 + b_n[v];
-      const float* p = B + (size_t)gk * ldb + gn;
-      if (b_vec_ok && gk < K && gn + 3 < N) {
-        rb[v] = *reinterpret_cast<const f32x4*>(p);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rb[v][e] = (gk < K && gn + e < N) ? p[e] : 0.0f;
-      }
-    }
+    for (int v = 0; v < T::B_VEC; ++v)
+      rb[v] = load_unit(b_addr(b_o[v], k0 + b_k[v]), B_KC, b_vec_ok, n0 + b_o[v],
+                        N, k0 + b_k[v]);
   };
   auto store_regs = [&](int stage) {
     float* st = lds + stage * T::STAGE;
@@ -240,18 +263,29 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     const float* Bs = As + T::A_ELEMS;
 #pragma unroll
     for (int q = 0; q < T::QN; ++q) {
-      f32x4 a[T::FM];
-      float b[T::FN][4];
+      // lane half lh of K group kg covers k = kg*BK + lh*KH + 4q .. +3
+      const int kq = kg * T::BK + lh * T::KH + q * 4;
+      f32x4 a[T::FM], b[T::FN];
 #pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-        a[i] = *reinterpret_cast<const f32x4*>(As + a_unit_off<T>(
-            wm * T::WM + i * 32 + li, kg * (T::BK / 4) + lh * T::QN + q));
+      for (int i = 0; i < T::FM; ++i) {
+        const int m = wm * T::WM + i * 32 + li;
+        if (A_KC) {
+          a[i] = *reinterpret_cast<const f32x4*>(As + kc_unit_off<T>(m, kq / 4));
+        } else {
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j)
+          for (int u = 0; u < 4; ++u) a[i][u] = As[oc_elem_off<T, T::BM>(kq + u, m)];
+        }
+      }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          b[j][u] = Bs[b_elem_off<T>(kg * T::BK + lh * T::KH + q * 4 + u,
-                                     wn * T::WN + j * 32 + li)];
+      for (int j = 0; j < T::FN; ++j) {
+        const int n = wn * T::WN + j * 32 + li;
+        if (B_KC) {
+          b[j] = *reinterpret_cast<const f32x4*>(Bs + kc_unit_off<T>(n, kq / 4));
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) b[j][u] = Bs[oc_elem_off<T, T::BN>(kq + u, n)];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -338,7 +372,8 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int e4 = (i * T::FN + j) * 4 + g;
-            const f32x4 v = red[(((src - 1) * T::WAVES_MN + wmn) * PER_WAVE + e4) * 64 + lane];
+            const f32x4 v =
+                red[(((src - 1) * T::WAVES_MN + wmn) * PER_WAVE + e4) * 64 + lane];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
           }

@@ -32,6 +32,7 @@ struct sgemm_handle_s {
 namespace {
 
 struct RunArgs {
+  int ta, tb;  // A stored K x M / B stored N x K
   int M, N, K;
   float alpha, beta;
   const float* A;
@@ -48,18 +49,21 @@ typedef hipError_t (*launch_fn)(const RunArgs&, int tiles_m, int tiles_n,
 struct KernelDesc {
   const char* name;
   int variant;
-  int bm, bn, bk, threads, guarded;
+  int ta, tb;  // operand storage the kernel reads
+  int bm, bn;
+  int bk;      // K values per LDS stage: K must be a multiple when aligned
+  int threads, guarded;
   float rel_rate;  // relative per-CU throughput, used by the tile choice
   launch_fn launch;
 };
 
-template <class T, bool G>
+template <class T, bool G, bool TA, bool TB>
 hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
                        hipStream_t s) {
   const int nwg = tiles_m * tiles_n;
-  hipLaunchKernelGGL((mfma_sgemm_kernel<T, G>), dim3(nwg), dim3(T::THREADS),
-                     0, s, a.M, a.N, a.K, a.alpha, a.A, a.lda, a.B, a.ldb,
-                     a.beta, a.C, a.ldc, tiles_m, tiles_n,
+  hipLaunchKernelGGL((mfma_sgemm_kernel<T, G, TA, TB>), dim3(nwg),
+                     dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
+                     a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n,
                      band_rows(tiles_m, nwg));
   return hipGetLastError();
 }
@@ -75,8 +79,9 @@ hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
   return hipGetLastError();
 }
 
-// Tile shapes.  MfmaTile<BM, BN, WM, WN, OCC, S, BK>: block tile, wave tile,
-// the waves per SIMD the register budget is sized for, LDS stages and K step.
+// Tile shapes.  MfmaTile<BM, BN, WM, WN, OCC, S, BK, KG>: block tile, wave
+// tile, the waves per SIMD the register budget is sized for, LDS stages, K
+// step and K groups.
 typedef MfmaTile<256, 256, 128, 64, 2> M256x256;  // 8 waves, 1 WG/CU
 typedef MfmaTile<256, 128, 64, 64, 4> M256x128;   // 8 waves, 2 WG/CU
 typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
@@ -87,23 +92,32 @@ typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
 typedef MfmaTile<64, 64, 32, 32, 4, 2, 16, 4> M64x64;  // 16 waves
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
-#define MFMA_PAIR(T, rate)                                                 \
-  {"mfma_" #T "_aligned", SGEMM_VARIANT_MFMA, T::BM, T::BN, T::BK,        \
-   T::THREADS, 0, rate, launch_mfma<T, false>},                           \
-  {"mfma_" #T "_guarded", SGEMM_VARIANT_MFMA, T::BM, T::BN, T::BK,        \
-   T::THREADS, 1, rate, launch_mfma<T, true>}
+#define MFMA_ONE(T, TAG, TA, TB, G, rate)                                    \
+  {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
+   T::THREADS, G, rate, launch_mfma<T, G, TA, TB>}
+#define MFMA_SET(T, rate)                                                    \
+  MFMA_ONE(T, "aligned", false, false, false, rate),                         \
+  MFMA_ONE(T, "guarded", false, false, true, rate),                          \
+  MFMA_ONE(T, "tn_aligned", true, false, false, rate),                       \
+  MFMA_ONE(T, "tn_guarded", true, false, true, rate),                        \
+  MFMA_ONE(T, "nt_aligned", false, true, false, rate),                       \
+  MFMA_ONE(T, "nt_guarded", false, true, true, rate),                        \
+  MFMA_ONE(T, "tt_aligned", true, true, false, rate),                        \
+  MFMA_ONE(T, "tt_guarded", true, true, true, rate)
 
 // Relative rates: throughput of each shape on 4096^3 (a grid that fills the
 // chip for all of them), normalised to the best.
 const KernelDesc kKernels[] = {
-    MFMA_PAIR(M256x256, 1.00f),
-    MFMA_PAIR(M256x128, 0.99f),
-    MFMA_PAIR(M128x128, 0.94f),
-    MFMA_PAIR(M64x64, 0.87f),
-    {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
-     V128x128::BK, V128x128::THREADS, 0, 1.0f, launch_valu<V128x128, false>},
-    {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, V128x128::BM, V128x128::BN,
-     V128x128::BK, V128x128::THREADS, 1, 1.0f, launch_valu<V128x128, true>},
+    MFMA_SET(M256x256, 1.00f),
+    MFMA_SET(M256x128, 0.99f),
+    MFMA_SET(M128x128, 0.94f),
+    MFMA_SET(M64x64, 0.87f),
+    {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
+     V128x128::BN, V128x128::BK, V128x128::THREADS, 0, 1.0f,
+     launch_valu<V128x128, false>},
+    {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
+     V128x128::BN, V128x128::BK, V128x128::THREADS, 1, 1.0f,
+     launch_valu<V128x128, true>},
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -114,6 +128,7 @@ bool ptr_aligned16(const void* p) {
 
 // Can kernel k run these arguments?
 bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
+  if (k.ta != a.ta || k.tb != a.tb) return false;
   if (k.guarded) return true;
   return a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
          a.lda % 4 == 0 && a.ldb % 4 == 0 && ptr_aligned16(a.A) &&
@@ -132,25 +147,31 @@ double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   return (double)per_cu * k.bm * k.bn / k.rel_rate;
 }
 
+// Aligned kernels of the variant and operand storage (the tile shapes).
+bool is_shape(const KernelDesc& k, int variant, const RunArgs& a) {
+  return k.variant == variant && !k.guarded && k.ta == a.ta && k.tb == a.tb;
+}
+
 // Instance of tile shape `shape` (an aligned kernel id) for these arguments:
 // the aligned kernel when it can run them, else the guarded one.
 int instance_for(int shape, const RunArgs& a) {
   if (kernel_fits(kKernels[shape], a)) return shape;
   for (int i = 0; i < kNumKernels; ++i) {
     const KernelDesc& k = kKernels[i];
-    if (k.guarded && k.variant == kKernels[shape].variant &&
-        k.bm == kKernels[shape].bm && k.bn == kKernels[shape].bn &&
-        k.bk == kKernels[shape].bk)
+    if (k.guarded && k.variant == kKernels[shape].variant && k.ta == a.ta &&
+        k.tb == a.tb && k.bm == kKernels[shape].bm &&
+        k.bn == kKernels[shape].bn && k.bk == kKernels[shape].bk &&
+        k.threads == kKernels[shape].threads)
       return i;
   }
-  return SGEMM_ERR_VALUE;
+  return SGEMM_ERR_UNSUPPORTED;
 }
 
 // Columns [n0, n0 + n) of the problem as a problem of its own.
 RunArgs column_part(const RunArgs& a, int n0, int n) {
   RunArgs p = a;
   p.N = n;
-  p.B = a.B + n0;
+  p.B = a.tb ? a.B + (size_t)n0 * a.ldb : a.B + n0;
   p.C = a.C + n0;
   return p;
 }
@@ -177,23 +198,23 @@ int make_plan(int variant, const RunArgs& a, int cus, Plan* plan) {
   int best = -1;
   double best_cost = 0.0;
   for (int i = 0; i < kNumKernels; ++i) {
-    const KernelDesc& k = kKernels[i];
-    if (k.variant != variant || k.guarded) continue;
-    const double c = tile_cost(k, a, cus);
+    if (!is_shape(kKernels[i], variant, a)) continue;
+    const double c = tile_cost(kKernels[i], a, cus);
     if (best < 0 || c < best_cost) {
       best = i;
       best_cost = c;
     }
   }
-  if (best < 0) return SGEMM_ERR_VALUE;
+  if (best < 0) return SGEMM_ERR_UNSUPPORTED;  // e.g. VALU with transposes
   plan->count = 1;
   plan->part[0] = Launch{instance_for(best, a), 0, a.N};
-  if (a.K <= 0 || a.M <= 0) return plan->part[0].kernel < 0 ? plan->part[0].kernel : SGEMM_OK;
+  if (plan->part[0].kernel < 0) return plan->part[0].kernel;
+  if (a.K <= 0 || a.M <= 0) return SGEMM_OK;
   // time of one output unit ~ 2K flops at ~0.55 TFLOP/s per CU
   const double second_launch = 4e-6 / (2.0 * a.K / 5.5e11);
   for (int i = 0; i < kNumKernels; ++i) {
     const KernelDesc& k1 = kKernels[i];
-    if (k1.variant != variant || k1.guarded) continue;
+    if (!is_shape(k1, variant, a)) continue;
     const long long tm1 = ceil_div(a.M, k1.bm);
     const int tn1 = a.N / k1.bn;
     for (int nt = 1; nt < tn1; ++nt) {
@@ -204,19 +225,19 @@ int make_plan(int variant, const RunArgs& a, int cus, Plan* plan) {
       const double c1 = tile_cost(k1, p1, cus);
       for (int j = 0; j < kNumKernels; ++j) {
         const KernelDesc& k2 = kKernels[j];
-        if (k2.variant != variant || k2.guarded) continue;
+        if (!is_shape(k2, variant, a)) continue;
         const double c = c1 + tile_cost(k2, p2, cus) + second_launch;
         if (c < best_cost) {
+          const int i1 = instance_for(i, p1), i2 = instance_for(j, p2);
+          if (i1 < 0 || i2 < 0) continue;
           best_cost = c;
           plan->count = 2;
-          plan->part[0] = Launch{instance_for(i, p1), 0, n1};
-          plan->part[1] = Launch{instance_for(j, p2), n1, a.N - n1};
+          plan->part[0] = Launch{i1, 0, n1};
+          plan->part[1] = Launch{i2, n1, a.N - n1};
         }
       }
     }
   }
-  for (int p = 0; p < plan->count; ++p)
-    if (plan->part[p].kernel < 0) return plan->part[p].kernel;
   return SGEMM_OK;
 }
 
@@ -239,21 +260,35 @@ bool overlap(Range x, Range y) {
 
 extern "C" {
 
-int sgemm_validate(int M, int N, int K, const float* A, int lda,
-                   const float* B, int ldb, float beta, const float* C,
-                   int ldc) {
+int sgemm_validate_ex(int transa, int transb, int M, int N, int K,
+                      const float* A, int lda, const float* B, int ldb,
+                      float beta, const float* C, int ldc) {
+  if ((transa != SGEMM_OP_N && transa != SGEMM_OP_T) ||
+      (transb != SGEMM_OP_N && transb != SGEMM_OP_T))
+    return SGEMM_ERR_VALUE;
   if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SIZE;
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+  // stored shapes: A is M x K (or K x M), B is K x N (or N x K)
+  const int a_rows = transa ? K : M, a_cols = transa ? M : K;
+  const int b_rows = transb ? N : K, b_cols = transb ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+      ldc < (N > 1 ? N : 1))
     return SGEMM_ERR_LD;
   if (M == 0 || N == 0) return SGEMM_OK;  // nothing is touched
   if (C == nullptr) return SGEMM_ERR_NULL;
   if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_NULL;
   const Range rc = window(C, M, N, ldc);
-  if (K > 0 && (overlap(rc, window(A, M, K, lda)) ||
-                overlap(rc, window(B, K, N, ldb))))
+  if (K > 0 && (overlap(rc, window(A, a_rows, a_cols, lda)) ||
+                overlap(rc, window(B, b_rows, b_cols, ldb))))
     return SGEMM_ERR_ALIAS;
   (void)beta;
   return SGEMM_OK;
+}
+
+int sgemm_validate(int M, int N, int K, const float* A, int lda,
+                   const float* B, int ldb, float beta, const float* C,
+                   int ldc) {
+  return sgemm_validate_ex(SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B, ldb,
+                           beta, C, ldc);
 }
 
 const char* sgemm_status_string(int status) {
@@ -279,10 +314,12 @@ const char* sgemm_kernel_name(int id) {
 }
 
 int sgemm_kernel_info(int id, int* variant, int* bm, int* bn, int* bk,
-                      int* threads, int* guarded) {
+                      int* threads, int* guarded, int* transa, int* transb) {
   if (id < 0 || id >= kNumKernels) return SGEMM_ERR_VALUE;
   const KernelDesc& k = kKernels[id];
   if (variant) *variant = k.variant;
+  if (transa) *transa = k.ta;
+  if (transb) *transb = k.tb;
   if (bm) *bm = k.bm;
   if (bn) *bn = k.bn;
   if (bk) *bk = k.bk;
@@ -291,10 +328,13 @@ int sgemm_kernel_info(int id, int* variant, int* bm, int* bn, int* bk,
   return SGEMM_OK;
 }
 
-int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
-               const float* B, int ldb, const float* C, int ldc,
-               int* kernels, int* n_split) {
-  const RunArgs a = {M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
+int sgemm_plan_ex(int variant, int transa, int transb, int M, int N, int K,
+                  const float* A, int lda, const float* B, int ldb,
+                  const float* C, int ldc, int* kernels, int* n_split) {
+  if ((transa != SGEMM_OP_N && transa != SGEMM_OP_T) ||
+      (transb != SGEMM_OP_N && transb != SGEMM_OP_T))
+    return SGEMM_ERR_VALUE;
+  const RunArgs a = {transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
                      const_cast<float*>(C), ldc};
   Plan plan;
   const int st = make_plan(variant, a, kChipCus, &plan);
@@ -307,10 +347,17 @@ int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
   return plan.count;
 }
 
+int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
+               const float* B, int ldb, const float* C, int ldc,
+               int* kernels, int* n_split) {
+  return sgemm_plan_ex(variant, SGEMM_OP_N, SGEMM_OP_N, M, N, K, A, lda, B,
+                       ldb, C, ldc, kernels, n_split);
+}
+
 int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
                         int lda, const float* B, int ldb, const float* C,
                         int ldc) {
-  int kernels[2];
+  int kernels[2] = {-1, -1};
   const int n = sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, ldc, kernels,
                            nullptr);
   return n < 0 ? n : kernels[0];
@@ -372,14 +419,16 @@ int sgemm_set_kernel(sgemm_handle_t h, int kernel_id) {
   return SGEMM_OK;
 }
 
-int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
-              const float* A, int lda, const float* B, int ldb, float beta,
-              float* C, int ldc, hipStream_t stream) {
+int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
+                 int K, float alpha, const float* A, int lda, const float* B,
+                 int ldb, float beta, float* C, int ldc, hipStream_t stream) {
   if (h == nullptr) return SGEMM_ERR_HANDLE;
-  const int st = sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc);
+  const int st = sgemm_validate_ex(transa, transb, M, N, K, A, lda, B, ldb,
+                                   beta, C, ldc);
   if (st != SGEMM_OK) return st;
   if (M == 0 || N == 0) return SGEMM_OK;
-  const RunArgs a = {M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+  const RunArgs a = {transa, transb, M, N, K, alpha, beta, A, lda, B, ldb,
+                     C, ldc};
   Plan plan;
   if (h->forced_kernel >= 0) {
     if (!kernel_fits(kKernels[h->forced_kernel], a)) return SGEMM_ERR_UNSUPPORTED;
@@ -406,6 +455,13 @@ int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
       return SGEMM_ERR_HIP;
   }
   return SGEMM_OK;
+}
+
+int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
+              const float* A, int lda, const float* B, int ldb, float beta,
+              float* C, int ldc, hipStream_t stream) {
+  return sgemm_run_ex(h, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B,
+                      ldb, beta, C, ldc, stream);
 }
 
 }  // extern "C"

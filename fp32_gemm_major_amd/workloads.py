@@ -98,25 +98,35 @@ class Operands:
     K: int
     alpha: float
     beta: float
-    A: np.ndarray  # flat, M*lda
+    A: np.ndarray  # flat: M rows of lda (K rows of lda when ta)
     lda: int
-    B: np.ndarray  # flat, K*ldb
+    B: np.ndarray  # flat: K rows of ldb (N rows of ldb when tb)
     ldb: int
     C: np.ndarray  # flat, M*ldc (C_in)
     ldc: int
+    ta: bool = False  # A stored transposed (K x M)
+    tb: bool = False  # B stored transposed (N x K)
 
 
 def operands(w: Workload, lda=None, ldb=None, ldc=None, pad_value=np.nan,
-             M=None, N=None, K=None) -> Operands:
-    """Inputs of workload ``w`` (optionally with other sizes or leading dims)."""
+             M=None, N=None, K=None, ta=False, tb=False) -> Operands:
+    """Inputs of workload ``w`` (optionally with other sizes or leading dims).
+
+    ``ta`` / ``tb`` store A as its transpose (K x M) / B as its transpose
+    (N x K); the logical values are the same as without them.
+    """
     if M is not None or N is not None or K is not None:
         w = replace(w, M=w.M if M is None else M, N=w.N if N is None else N,
                     K=w.K if K is None else K)
-    lda = max(w.K, 1) if lda is None else lda
-    ldb = max(w.N, 1) if ldb is None else ldb
+    lda = max(w.M if ta else w.K, 1) if lda is None else lda
+    ldb = max(w.K if tb else w.N, 1) if ldb is None else ldb
     ldc = max(w.N, 1) if ldc is None else ldc
     a = draw(w.cfg_id, ROLE_A, w.M, w.K, w.dist)
     b = draw(w.cfg_id, ROLE_B, w.K, w.N, w.dist)
+    if ta:
+        a = np.ascontiguousarray(a.T)
+    if tb:
+        b = np.ascontiguousarray(b.T)
     if w.c_fill == "nan":
         c = np.full((w.M, w.N), np.nan, dtype=np.float32)
     else:
@@ -124,4 +134,4 @@ def operands(w: Workload, lda=None, ldb=None, ldc=None, pad_value=np.nan,
     return Operands(w.M, w.N, w.K, w.alpha, w.beta,
                     place(a, lda, pad_value), lda,
                     place(b, ldb, pad_value), ldb,
-                    place(c, ldc, pad_value), ldc)
+                    place(c, ldc, pad_value), ldc, ta, tb)

@@ -8,6 +8,10 @@
  * with A of size M x K, B of size K x N and C of size M x N, all row-major
  * FP32.  This ABI adds explicit leading dimensions (the page uses K, N, N):
  *     A(i,k) = A[i*lda + k],  B(k,j) = B[k*ldb + j],  C(i,j) = C[i*ldc + j].
+ * sgemm_run_ex also takes transposed storage (the A^T*B and A*B^T cases of
+ * the gsyq.cn GEMM guide, section 6.4 step 8): with transa = SGEMM_OP_T, A is
+ * stored K x M and A(i,k) = A[k*lda + i]; with transb = SGEMM_OP_T, B is
+ * stored N x K and B(k,j) = B[j*ldb + k].
  * Only the M x N window of C is written; every other element of the C buffer
  * is left untouched.
  *
@@ -59,8 +63,15 @@ enum sgemm_status {
   SGEMM_ERR_UNSUPPORTED = -9 /* forced kernel cannot run these arguments */
 };
 
+/* Operand storage for sgemm_run_ex: as stated (N) or transposed (T). */
+enum sgemm_op {
+  SGEMM_OP_N = 0,
+  SGEMM_OP_T = 1
+};
+
 /* Kernel families.  MFMA uses the FP32 matrix cores (v_mfma_f32_32x32x2_f32);
- * VALU uses per-lane FMA outer products on the vector ALUs.  AUTO = MFMA. */
+ * VALU uses per-lane FMA outer products on the vector ALUs (stored operands
+ * only, no transposes).  AUTO = MFMA. */
 enum sgemm_variant {
   SGEMM_VARIANT_AUTO = 0,
   SGEMM_VARIANT_MFMA = 1,
@@ -80,6 +91,15 @@ int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
               const float* A, int lda, const float* B, int ldb, float beta,
               float* C, int ldc, hipStream_t stream);
 
+/* As sgemm_run, with operand storage transa / transb (SGEMM_OP_N or
+ * SGEMM_OP_T, else SGEMM_ERR_VALUE).  Leading dimensions must cover the
+ * stored rows: lda >= max(1, transa ? M : K), ldb >= max(1, transb ? K : N).
+ * SGEMM_ERR_UNSUPPORTED if the handle's variant or forced kernel has no
+ * kernel for this storage (the VALU family reads stored operands only). */
+int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
+                 int K, float alpha, const float* A, int lda, const float* B,
+                 int ldb, float beta, float* C, int ldc, hipStream_t stream);
+
 /* Free the handle.  NULL is a no-op returning SGEMM_OK. */
 int sgemm_destroy(sgemm_handle_t h);
 
@@ -91,6 +111,10 @@ int sgemm_destroy(sgemm_handle_t h);
 int sgemm_validate(int M, int N, int K, const float* A, int lda,
                    const float* B, int ldb, float beta, const float* C,
                    int ldc);
+/* The checks of sgemm_run_ex (storage flags, stored shapes). */
+int sgemm_validate_ex(int transa, int transb, int M, int N, int K,
+                      const float* A, int lda, const float* B, int ldb,
+                      float beta, const float* C, int ldc);
 
 /* Static text for a status code ("unknown status" for other values). */
 const char* sgemm_status_string(int status);
@@ -99,11 +123,12 @@ const char* sgemm_status_string(int status);
 int sgemm_num_kernels(void);
 const char* sgemm_kernel_name(int kernel_id); /* NULL for a bad id */
 /* Tile shape and properties of a kernel; any out-pointer may be NULL.
- * `guarded` = 1 for kernels that accept any size and alignment, 0 for
- * kernels that need M%bm == N%bn == K%bk == 0, lda and ldb multiples of 4
- * and 16-byte aligned A and B. */
+ * bk is the K granularity (K values per LDS stage).  `guarded` = 1 for
+ * kernels that accept any size and alignment, 0 for kernels that need
+ * M%bm == N%bn == K%bk == 0, lda and ldb multiples of 4 and 16-byte aligned
+ * A and B.  transa / transb give the operand storage the kernel reads. */
 int sgemm_kernel_info(int kernel_id, int* variant, int* bm, int* bn, int* bk,
-                      int* threads, int* guarded);
+                      int* threads, int* guarded, int* transa, int* transb);
 
 /* How sgemm_run splits a call: it returns the number of launches (1 or 2)
  * or a negative status.  kernels[0] (and kernels[1], else -1) receive the
@@ -115,6 +140,10 @@ int sgemm_kernel_info(int kernel_id, int* variant, int* bm, int* bn, int* bk,
 int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
                const float* B, int ldb, const float* C, int ldc,
                int* kernels, int* n_split);
+/* sgemm_plan for sgemm_run_ex's operand storage. */
+int sgemm_plan_ex(int variant, int transa, int transb, int M, int N, int K,
+                  const float* A, int lda, const float* B, int ldb,
+                  const float* C, int ldc, int* kernels, int* n_split);
 
 /* The kernel of sgemm_run's first launch for these arguments and variant
  * (SGEMM_VARIANT_*), or a negative status.  Pure function of its inputs. */

@@ -22,7 +22,7 @@ def run(h: sg.Handle, ops: wl.Operands, dev=None, stream=None):
     """Run C = alpha*A*B + beta*C on the GPU; returns the whole C buffer (flat numpy)."""
     A, B, C = dev if dev is not None else to_device(ops)
     h.gemm(A, B, C, ops.alpha, ops.beta, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
-           ldb=ops.ldb, ldc=ops.ldc, stream=stream)
+           ldb=ops.ldb, ldc=ops.ldc, stream=stream, transa=ops.ta, transb=ops.tb)
     torch.cuda.synchronize()
     return C.cpu().numpy()[: ops.C.size].copy()
 
@@ -64,7 +64,7 @@ def check_full(ops: wl.Operands, out_flat, exact=False, what=""):
     the padding of C (columns N..ldc-1) was not touched."""
     M, N, K = ops.M, ops.N, ops.K
     R, T = oracle.gemm(M, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb, ops.beta,
-                       ops.C, ops.ldc)
+                       ops.C, ops.ldc, ta=ops.ta, tb=ops.tb)
     got = window(out_flat, M, N, ops.ldc)
     c_in = window(ops.C, M, N, ops.ldc)
     worst = check(got, R, T, K, ops.alpha, ops.beta, c_in, exact, what)
@@ -83,18 +83,19 @@ def check_sampled(ops: wl.Operands, out_flat, rows, cols, npoints=4096, seed=0,
     M, N, K = ops.M, ops.N, ops.K
     got_all = window(out_flat, M, N, ops.ldc)
     c_all = window(ops.C, M, N, ops.ldc)
+    assert not ops.ta, "row slabs need A stored untransposed"
     rows = np.asarray(sorted(set(int(x) for x in rows)), np.int64)
     A2 = ops.A[: M * ops.lda].reshape(M, ops.lda)[rows]
     C2 = ops.C[: M * ops.ldc].reshape(M, ops.ldc)[rows]
     R, T = oracle.gemm(len(rows), N, K, ops.alpha, A2, ops.lda, ops.B, ops.ldb,
-                       ops.beta, C2, ops.ldc)
+                       ops.beta, C2, ops.ldc, tb=ops.tb)
     worst = check(got_all[rows], R, T, K, ops.alpha, ops.beta, c_all[rows], exact,
                   what + " rows")
     rng = np.random.default_rng(seed)
     pr = np.concatenate([np.repeat(np.arange(M), len(cols)), rng.integers(0, M, npoints)])
     pc = np.concatenate([np.tile(np.asarray(cols), M), rng.integers(0, N, npoints)])
     r, t = oracle.gemm_points(M, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb,
-                              ops.beta, ops.C, ops.ldc, pr, pc)
+                              ops.beta, ops.C, ops.ldc, pr, pc, tb=ops.tb)
     worst = max(worst, check(got_all[pr, pc], r, t, K, ops.alpha, ops.beta,
                              c_all[pr, pc], exact, what + " points"))
     return worst

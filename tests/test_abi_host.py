@@ -60,6 +60,52 @@ def test_validate():
     assert v(4, 5, 6, A, 6, B, 5, 0.0, A + 4 * 24, 5) == sg.SGEMM_OK
 
 
+def test_validate_transposed():
+    v = sg.sgemm_validate_ex
+    A, B, C = 0x10000, 0x20000, 0x40000
+    N_, T_ = sg.SGEMM_OP_N, sg.SGEMM_OP_T
+    # op(A) = A^T: A stored K x M, lda >= M
+    assert v(T_, N_, 4, 5, 6, A, 4, B, 5, 0.0, C, 5) == sg.SGEMM_OK
+    assert v(T_, N_, 4, 5, 6, A, 3, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD
+    assert v(T_, N_, 8, 5, 2, A, 8, B, 5, 0.0, C, 5) == sg.SGEMM_OK  # lda < K is fine
+    # op(B) = B^T: B stored N x K, ldb >= K
+    assert v(N_, T_, 4, 5, 6, A, 6, B, 6, 0.0, C, 5) == sg.SGEMM_OK
+    assert v(N_, T_, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD
+    assert v(2, N_, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(N_, -1, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    # alias windows follow the stored shapes: A^T is 6 rows of lda 4
+    assert v(T_, N_, 4, 5, 6, A, 4, B, 5, 0.0, A + 4 * 20, 5) == sg.SGEMM_ERR_ALIAS
+    assert v(T_, N_, 4, 5, 6, A, 4, B, 5, 0.0, A + 4 * 24, 5) == sg.SGEMM_OK
+    # the plain entry points are the N/N case
+    assert v(N_, N_, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.sgemm_validate(
+        4, 5, 6, A, 6, B, 5, 0.0, C, 5)
+
+
+def test_plan_transposed():
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    for ta in (0, 1):
+        for tb in (0, 1):
+            p = sg.sgemm_plan(0, 4096, 4096, 4096, A, 4096, B, 4096, C, 4096,
+                              transa=ta, transb=tb)
+            info = sg.sgemm_kernel_info(p[0][0])
+            assert len(p) == 1 and (info["transa"], info["transb"]) == (ta, tb)
+            assert info["guarded"] == 0 and info["bm"] == 256
+    with pytest.raises(sg.SgemmError) as e:
+        sg.sgemm_plan(sg.SGEMM_VARIANT_VALU, 64, 64, 64, A, 64, B, 64, C, 64, transa=1)
+    assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+
+
+def test_aligned_kernels_need_whole_stages_of_k():
+    """An aligned kernel is chosen only when K is a multiple of its stage."""
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    for K in (16, 48, 80, 1040, 1024, 4096):
+        for M, N in ((256, 192), (1024, 1024), (4096, 4096)):
+            for kid, _, _ in sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N):
+                info = sg.sgemm_kernel_info(kid)
+                if not info["guarded"]:
+                    assert K % info["bk"] == 0 and M % info["bm"] == 0, (M, N, K, info)
+
+
 def test_status_strings():
     for code in range(-9, 1):
         s = sg.sgemm_status_string(code)
@@ -75,11 +121,14 @@ def test_kernel_table():
     assert variants == {sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU}
     for k in table:
         assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
-    # every tile shape has both an aligned and a guarded instance
+    # every tile shape has an aligned and a guarded instance for each storage
     shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table}
     for s in shapes:
-        g = {k["guarded"] for k in table if (k["variant"], k["bm"], k["bn"], k["bk"]) == s}
-        assert g == {0, 1}, s
+        inst = {(k["transa"], k["transb"], k["guarded"]) for k in table
+                if (k["variant"], k["bm"], k["bn"], k["bk"]) == s}
+        ops = {(0, 0)} if s[0] == sg.SGEMM_VARIANT_VALU else \
+            {(0, 0), (0, 1), (1, 0), (1, 1)}
+        assert inst == {(a, b, g) for a, b in ops for g in (0, 1)}, s
 
 
 def test_select_kernel():

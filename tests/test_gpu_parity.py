@@ -53,8 +53,13 @@ def test_each_kernel(handle, k, dist):
     else:
         M, N, K = 2 * k["bm"], 3 * k["bn"], 4 * k["bk"]
         lda, ldb, ldc = K, N, N + 4
+    ta, tb = bool(k["transa"]), bool(k["transb"])
+    if ta:  # stored K x M
+        lda = M + (lda - K)
+    if tb:  # stored N x K
+        ldb = K + (ldb - N)
     w = wl.Workload("case", 900 + k["id"], M, N, K, 1.5, 0.5, dist)
-    ops = wl.operands(w, lda=lda, ldb=ldb, ldc=ldc)
+    ops = wl.operands(w, lda=lda, ldb=ldb, ldc=ldc, ta=ta, tb=tb)
     out = gu.run(handle, ops)
     gu.check_full(ops, out, exact=(dist == "int4"), what=k["name"])
 
@@ -116,6 +121,56 @@ def test_valu_variant(handle, name):
         gu.check_full(ops, out, what=name + " valu")
 
 
+# ---- transposed operands (op(A) = A^T, op(B) = B^T) ---------------------------
+
+OPS = [(False, True), (True, False), (True, True)]
+
+
+@pytest.mark.parametrize("ta,tb", OPS, ids=["nt", "tn", "tt"])
+def test_transposed_aligned(handle, ta, tb):
+    w = wl.Workload("trans", 6000, 1024, 1536, 768, 1.5, 0.5, "uniform")
+    ops = wl.operands(w, ta=ta, tb=tb)
+    gu.check_full(ops, gu.run(handle, ops), what=f"trans {ta}{tb}")
+
+
+@pytest.mark.parametrize("ta,tb", OPS, ids=["nt", "tn", "tt"])
+def test_transposed_edges_integer(handle, ta, tb):
+    w = wl.Workload("trans", 6001, 1000, 1500, 777, 1.0, 1.0, "int4")
+    ops = wl.operands(w, ta=ta, tb=tb)
+    gu.check_full(ops, gu.run(handle, ops), exact=True, what=f"trans edge {ta}{tb}")
+
+
+@pytest.mark.parametrize("ta,tb", OPS, ids=["nt", "tn", "tt"])
+def test_transposed_4096_split_plan(handle, ta, tb):
+    """4096 x 11008 x 512 runs as two column launches; op(B) = B^T offsets B by rows."""
+    w = wl.Workload("trans", 6002, 4096, 11008, 512, 1.0, 0.0, "normal", "nan")
+    ops = wl.operands(w, ta=ta, tb=tb)
+    plan = sg.sgemm_plan(0, w.M, w.N, w.K, 0x10000000, ops.lda, 0x20000000, ops.ldb,
+                         0x40000000, ops.ldc, transa=int(ta), transb=int(tb))
+    assert len(plan) == 2
+    gu.check_full(ops, gu.run(handle, ops), what=f"trans split {ta}{tb}")
+
+
+def test_valu_has_no_transposes(handle):
+    handle.set_variant(sg.SGEMM_VARIANT_VALU)
+    A = torch.ones(64 * 64, device="cuda")
+    B = torch.ones(64 * 64, device="cuda")
+    C = torch.zeros(64 * 64, device="cuda")
+    with pytest.raises(sg.SgemmError) as e:
+        handle.gemm(A, B, C, 1.0, 0.0, M=64, N=64, K=64, lda=64, ldb=64, ldc=64,
+                    transa=True)
+    assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+
+
+def test_k_not_a_multiple_of_the_stage(handle):
+    """K a multiple of 16 but not of 64: the 64x64 tile's stage holds 64 k, so
+    its aligned instance must not be used (it would read past K)."""
+    for K in (1040, 80, 16):
+        w = wl.Workload("kstage", 6003, 256, 192, K, 1.0, 0.0, "int4", "nan")
+        ops = wl.operands(w)
+        gu.check_full(ops, gu.run(handle, ops), exact=True, what=f"K={K}")
+
+
 # ---- edge cases -----------------------------------------------------------------
 
 TINY = sorted({(m, n, k) for m in (1, 2, 31, 32, 33, 64, 65, 70)
@@ -147,8 +202,10 @@ def test_every_guarded_kernel_on_tiny_tails(handle):
         for i, (M, N, K) in enumerate([(1, 1, 1), (k["bm"] - 1, k["bn"] + 1, k["bk"] - 1),
                                        (k["bm"] + 1, k["bn"] - 1, k["bk"] + 1),
                                        (3, 70, 33)]):
+            ta, tb = bool(k["transa"]), bool(k["transb"])
             w = wl.Workload("tail", 4000 + i, M, N, K, 1.0, 1.0, "int4")
-            ops = wl.operands(w, lda=K + 1, ldb=N + 2, ldc=N + 3)
+            ops = wl.operands(w, lda=(M if ta else K) + 1, ldb=(K if tb else N) + 2,
+                              ldc=N + 3, ta=ta, tb=tb)
             gu.check_full(ops, gu.run(handle, ops), exact=True,
                           what=f"{k['name']} {M}x{N}x{K}")
 
