@@ -79,6 +79,31 @@ def time_launches(launch, steps, warmup, torch):
     return total, per
 
 
+def time_graph(launch, reps, torch):
+    """Mean time of one launch, from `reps` launches captured in a HIP graph and
+    replayed back to back, so host launch overhead is not in the figure."""
+    launch()  # compile-free warm start outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            launch()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        best = ms if best is None else min(best, ms)
+    del g
+    return best
+
+
 def cpu_baseline(ops, target_s: float):
     """Time the CPU oracle (FP64 triple loop, no error-bound pass) on the first
     rows of the same problem, all host cores, about `target_s` seconds."""
@@ -148,17 +173,17 @@ def main(argv=None):
     variant = sg.SGEMM_VARIANT_MFMA if args.variant == "mfma" else sg.SGEMM_VARIANT_VALU
     h = sg.Handle(variant=variant, kernel=args.kernel)
 
-    def prepare(name):
+    def prepare(name, ta=False, tb=False):
         w = wl.WORKLOADS[name]
-        ops = wl.operands(w)
+        ops = wl.operands(w, ta=ta, tb=tb)
         dev = [torch.from_numpy(x).cuda() for x in (ops.A, ops.B, ops.C)]
-        kid = args.kernel if args.kernel >= 0 else sg.sgemm_select_kernel(
+        kid = args.kernel if args.kernel >= 0 else sg.sgemm_plan(
             variant, w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(),
-            ops.ldb, dev[2].data_ptr(), ops.ldc)
+            ops.ldb, dev[2].data_ptr(), ops.ldc, transa=int(ta), transb=int(tb))[0][0]
 
         def launch():
             h.gemm(dev[0], dev[1], dev[2], w.alpha, w.beta, M=w.M, N=w.N, K=w.K,
-                   lda=ops.lda, ldb=ops.ldb, ldc=ops.ldc)
+                   lda=ops.lda, ldb=ops.ldb, ldc=ops.ldc, transa=ta, transb=tb)
         return w, ops, dev, kid, launch
 
     w, ops, dev, kid, launch = prepare(args.workload)
@@ -197,35 +222,39 @@ def main(argv=None):
 
     per_config = None
     if not args.no_per_config:
+        # Each workload's launches are captured in a HIP graph and replayed, so
+        # the small problems are timed without host launch overhead.
         per_config = {}
-        reps = {"c1_128": 200, "c2_1024": 200, "c4_edge": 200, "c5_mlp": 30}
+
+        def entry(w2, kid2, ms, peak=rf.PEAK_FP32_FLOPS):
+            gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
+            return {"gflops": round(gf, 1), "frac_of_peak": round(gf * 1e9 / peak, 4),
+                    "kernel_ms": round(ms, 5), "kernel": sg.sgemm_kernel_name(kid2)}
+
+        reps = {"c1_128": 200, "c2_1024": 200, "c4_edge": 100, "c5_mlp": 20}
         for name, n in reps.items():
             w2, _, dev2, kid2, launch2 = prepare(name)
-            _, per2 = time_launches(launch2, n, 5, torch)
-            ms = sum(per2) / len(per2)
-            gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
-            per_config[name] = {"gflops": round(gf, 1),
-                                "frac_of_peak": round(gf * 1e9 / rf.PEAK_FP32_FLOPS, 4),
-                                "kernel_ms": round(ms, 5),
-                                "kernel": sg.sgemm_kernel_name(kid2)}
+            per_config[name] = entry(w2, kid2, time_graph(launch2, n, torch))
             del dev2
         per_config[args.workload] = {"gflops": round(achieved * 1e3, 1),
                                      "frac_of_peak": roof["frac"],
                                      "kernel_ms": roof["kernel_ms_mean"],
                                      "kernel": kname}
         if variant == sg.SGEMM_VARIANT_MFMA:
+            # the headline problem with transposed operand storage
+            for ta, tb, tag in ((False, True, "nt"), (True, False, "tn"),
+                                (True, True, "tt")):
+                w3, _, dev3, kid3, launch3 = prepare(args.workload, ta, tb)
+                per_config[f"{args.workload}_{tag}"] = entry(
+                    w3, kid3, time_graph(launch3, 20, torch))
+                del dev3
             h.set_variant(sg.SGEMM_VARIANT_VALU)
             w3, _, dev3, _, launch3 = prepare(args.workload)
             kid3 = sg.sgemm_select_kernel(sg.SGEMM_VARIANT_VALU, w3.M, w3.N, w3.K,
                                           dev3[0].data_ptr(), w3.K, dev3[1].data_ptr(),
                                           w3.N, dev3[2].data_ptr(), w3.N)
-            _, per3 = time_launches(launch3, 20, 3, torch)
-            ms = sum(per3) / len(per3)
-            gf = rf.flops(w3.M, w3.N, w3.K) / (ms * 1e-3) / 1e9
-            per_config[args.workload + "_valu"] = {
-                "gflops": round(gf, 1),
-                "frac_of_peak": round(gf * 1e9 / rf.PEAK_FP32_FLOPS, 4),
-                "kernel_ms": round(ms, 5), "kernel": sg.sgemm_kernel_name(kid3)}
+            per_config[args.workload + "_valu"] = entry(
+                w3, kid3, time_graph(launch3, 10, torch))
             h.set_variant(variant)
             del dev3
     h.close()
