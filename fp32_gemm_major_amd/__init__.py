@@ -32,6 +32,10 @@ SGEMM_VARIANT_AUTO = 0
 SGEMM_VARIANT_MFMA = 1
 SGEMM_VARIANT_VALU = 2
 
+SGEMM_MODE_ALIGNED = 0
+SGEMM_MODE_EDGE = 1
+SGEMM_MODE_GUARDED = 2
+
 EXPORTED = [
     "sgemm_create", "sgemm_run", "sgemm_run_ex", "sgemm_destroy", "sgemm_validate",
     "sgemm_validate_ex", "sgemm_plan_ex",
@@ -155,7 +159,7 @@ def sgemm_kernel_info(kernel_id: int) -> dict:
     vals = [ctypes.c_int() for _ in range(8)]
     _check(library().sgemm_kernel_info(kernel_id, *[ctypes.byref(v) for v in vals]),
            "sgemm_kernel_info")
-    keys = ("variant", "bm", "bn", "bk", "threads", "guarded", "transa", "transb")
+    keys = ("variant", "bm", "bn", "bk", "threads", "mode", "transa", "transb")
     d = {k: v.value for k, v in zip(keys, vals)}
     d["name"] = sgemm_kernel_name(kernel_id)
     d["id"] = kernel_id

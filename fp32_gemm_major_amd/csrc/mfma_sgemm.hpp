@@ -22,14 +22,30 @@
 // * Lane l of a wave moves 16-byte unit (v*WAVES + wave)*64 + l of a stage.
 //   Its global source is the inverse of the swizzle, so consecutive lanes
 //   read consecutive 16-byte pieces of a stored row: loads stay coalesced.
-// * Loader, aligned kernels (GUARD = false): global_load_lds_dwordx4, which
+// * Loader, aligned and edge kernels: global_load_lds_dwordx4, which
 //   writes lane l's 16 bytes to LDS at M0 + 16*l with no register staging.
 //   The loads of step t+S-1 go out before the MFMAs of step t and are waited
 //   for (vmcnt) before the barrier that ends step t+S-2.
-// * Loader, guarded kernels (GUARD = true): the same units through registers,
-//   16-byte loads where a piece is inside the operand and 16-byte aligned,
-//   element loads with zero fill elsewhere ("GEMM 优化之路", exercise 2:
-//   out-of-range loads become zeros; no thread leaves before the barriers).
+// * Three modes per tile shape:
+//   - aligned (MODE 0): M, N and K are whole multiples of the tile and of the
+//     stage's K range; every load is a direct load.
+//   - edge (MODE 1): any M, N, K.  Whole K steps still use direct loads.  A
+//     unit that lies past the last row or column of an operand is loaded from
+//     the last valid row or column instead: it only feeds outputs outside
+//     M x N, which are never stored, so clamping the address is enough and no
+//     zero fill is needed.  The partial K step at the end (K not a multiple of
+//     the stage's K range) goes through registers with zero fill, since there
+//     both operands must be exactly zero past K.  A unit that runs along M or N
+//     (B as stored, or A^T) must not be split by the edge, so this mode needs
+//     that extent to be a multiple of 4.
+//   - guarded (MODE 2): every unit through registers, 16-byte loads where the
+//     whole unit is inside the operand, element loads with zero fill elsewhere
+//     ("GEMM 优化之路", exercise 2: out-of-range loads become zeros; no thread
+//     leaves before the barriers).
+//   16-byte global loads (plain and direct-to-LDS) need only 4-byte aligned
+//   addresses on gfx950 (checked with an in-bounds probe), so neither the
+//   leading dimensions nor the base pointers of A and B have to be multiples
+//   of 4 floats.
 // * MFMA operands are swapped (B block as the first operand): the 32x32
 //   result is then the transpose of the C block, and each lane holds four
 //   consecutive columns of one C row per register quad.  The epilogue reads C
@@ -50,6 +66,8 @@
 namespace sgemm {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// a 16-byte operand piece that may be only 4-byte aligned
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -138,8 +156,10 @@ __device__ __forceinline__ void dma16(const float* src, unsigned lds_base) {
       : "memory", "m0");
 }
 
+enum { MODE_ALIGNED = 0, MODE_EDGE = 1, MODE_GUARDED = 2 };
+
 // TA: A stored K x M (op(A) = A^T).  TB: B stored N x K (op(B) = B^T).
-template <class T, bool GUARD, bool TA, bool TB>
+template <class T, int MODE, bool TA, bool TB>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
     mfma_sgemm_kernel(int M, int N, int K, float alpha,
                       const float* __restrict__ A, int lda,
@@ -148,6 +168,8 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
                       int tiles_n, int band) {
   constexpr bool A_KC = !TA;  // A tile K-contiguous
   constexpr bool B_KC = TB;   // B tile K-contiguous
+  constexpr bool GUARD = MODE == MODE_GUARDED;  // no direct loads
+  constexpr bool EDGE = MODE == MODE_EDGE;
   constexpr int NST = GUARD ? 2 : T::S;  // LDS stages in use
   __shared__ __attribute__((aligned(1024))) float lds[NST * T::STAGE];
 
@@ -180,15 +202,25 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     return TB ? B + (size_t)(n0 + o) * ldb + k : B + (size_t)k * ldb + (n0 + o);
   };
 
-  // Aligned kernels: per-lane pointers at K step 0, advanced by a fixed
-  // stride per step; LDS destinations are wave-uniform.
+  // Direct loads: per-lane pointers at K step 0, advanced by a fixed stride
+  // per step; LDS destinations are wave-uniform.  Edge kernels move a unit
+  // past the last row (K-contiguous) or column (outer-contiguous, whose
+  // extent is a multiple of 4) onto the last valid one.
   const float* a_ptr[T::A_VEC];
   const float* b_ptr[T::B_VEC];
   if (!GUARD) {
 #pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v) a_ptr[v] = a_addr(a_o[v], a_k[v]);
+    for (int v = 0; v < T::A_VEC; ++v) {
+      int o = a_o[v];
+      if (EDGE && m0 + o >= M) o = (A_KC ? M - 1 : M - 4) - m0;
+      a_ptr[v] = a_addr(o, a_k[v]);
+    }
 #pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v) b_ptr[v] = b_addr(b_o[v], b_k[v]);
+    for (int v = 0; v < T::B_VEC; ++v) {
+      int o = b_o[v];
+      if (EDGE && n0 + o >= N) o = (B_KC ? N - 1 : N - 4) - n0;
+      b_ptr[v] = b_addr(o, b_k[v]);
+    }
   }
   const size_t a_step = TA ? (size_t)T::BKS * lda : (size_t)T::BKS;
   const size_t b_step = TB ? (size_t)T::BKS : (size_t)T::BKS * ldb;
@@ -206,25 +238,28 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
             st + 4u * T::A_ELEMS + 1024u * (unsigned)(v * T::WAVES + wave_u));
   };
 
-  // Guarded kernels: registers in between, 16-byte loads where possible.
-  const bool a_vec_ok =
-      (lda % 4 == 0) && ((reinterpret_cast<uintptr_t>(A) & 15u) == 0);
-  const bool b_vec_ok =
-      (ldb % 4 == 0) && ((reinterpret_cast<uintptr_t>(B) & 15u) == 0);
-  f32x4 ra[GUARD ? T::A_VEC : 1], rb[GUARD ? T::B_VEC : 1];
+  // Register-staged loads (guarded kernels, and the partial last K step of
+  // edge kernels): 16-byte loads where the whole unit is inside the operand,
+  // element loads with zero fill elsewhere.
+  constexpr bool STAGED = GUARD || EDGE;
+  f32x4 ra[STAGED ? T::A_VEC : 1], rb[STAGED ? T::B_VEC : 1];
   // Load one unit: KCONTIG runs over k (bounds: outer < OUTER, k < K), else
   // over the outer index (bounds: k < K, outer < OUTER).
-  auto load_unit = [&](const float* p, bool kcontig, bool vec_ok, int outer,
-                       int outer_n, int k) -> f32x4 {
+  auto load_unit = [&](const float* p, bool kcontig, int outer, int outer_n,
+                       int k) -> f32x4 {
     f32x4 x;
     if (kcontig) {
-      if (vec_ok && outer < outer_n && k + 3 < K)
-        return *reinterpret_cast<const f32x4*>(p);
+      if (outer < outer_n && k + 3 < K) {
+        const f32x4u v = *reinterpret_cast<const f32x4u*>(p);
+        return f32x4{v[0], v[1], v[2], v[3]};
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (outer < outer_n && k + e < K) ? p[e] : 0.0f;
     } else {
-      if (vec_ok && k < K && outer + 3 < outer_n)
-        return *reinterpret_cast<const f32x4*>(p);
+      if (k < K && outer + 3 < outer_n) {
+        const f32x4u v = *reinterpret_cast<const f32x4u*>(p);
+        return f32x4{v[0], v[1], v[2], v[3]};
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = (k < K && outer + e < outer_n) ? p[e] : 0.0f;
     }
@@ -234,12 +269,12 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     const int k0 = kt * T::BKS;
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v)
-      ra[v] = load_unit(a_addr(a_o[v], k0 + a_k[v]), A_KC, a_vec_ok, m0 + a_o[v],
-                        M, k0 + a_k[v]);
+      ra[v] = load_unit(a_addr(a_o[v], k0 + a_k[v]), A_KC, m0 + a_o[v], M,
+                        k0 + a_k[v]);
 #pragma unroll
     for (int v = 0; v < T::B_VEC; ++v)
-      rb[v] = load_unit(b_addr(b_o[v], k0 + b_k[v]), B_KC, b_vec_ok, n0 + b_o[v],
-                        N, k0 + b_k[v]);
+      rb[v] = load_unit(b_addr(b_o[v], k0 + b_k[v]), B_KC, n0 + b_o[v], N,
+                        k0 + b_k[v]);
   };
   auto store_regs = [&](int stage) {
     float* st = lds + stage * T::STAGE;
@@ -304,7 +339,9 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
   auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  const int ktiles = (K + T::BKS - 1) / T::BKS;
+  // K steps: all of them for guarded kernels; the whole ones for the direct
+  // loads (aligned kernels have no partial step).
+  const int ktiles = GUARD ? (K + T::BKS - 1) / T::BKS : K / T::BKS;
   if (GUARD) {
     if (ktiles > 0) {
       load_regs(0);
@@ -339,6 +376,15 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       __syncthreads();
       stage = stage + 1 == NST ? 0 : stage + 1;
       next = next + 1 == NST ? 0 : next + 1;
+    }
+    // Edge kernels: the partial last K step, zero-filled past K.  The stages
+    // are free after the loop's last barrier.
+    if (EDGE && ktiles * T::BKS < K) {
+      load_regs(ktiles);
+      store_regs(0);
+      __syncthreads();
+      compute(0);
+      if (T::KG > 1) __syncthreads();  // the K-group reduction reuses the LDS
     }
   }
 
@@ -385,6 +431,9 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   const int ccol = n0 + wn * T::WN + lh * 4;
   const bool c_vec =
       (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+  // stores need bounds checks: guarded kernels, and edge tiles of edge kernels
+  const bool masked =
+      GUARD || (EDGE && (m0 + T::BM > M || n0 + T::BN > N));
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -392,7 +441,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       const int row = crow + i * 32;
       const int col = ccol + j * 32;
       float* p = C + (size_t)row * ldc + col;
-      if (!GUARD && c_vec) {
+      if (!masked && c_vec) {
         f32x4 cin[4];
         if (beta != 0.0f) {
 #pragma unroll
@@ -408,20 +457,20 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
           }
           *reinterpret_cast<f32x4*>(p + 8 * g) = o;
         }
-      } else if (!GUARD || row < M) {
+      } else if (!masked || row < M) {
         float cin[16];
         if (beta != 0.0f) {
 #pragma unroll
           for (int g = 0; g < 4; ++g)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (!GUARD || col + 8 * g + e < N) cin[4 * g + e] = p[8 * g + e];
+              if (!masked || col + 8 * g + e < N) cin[4 * g + e] = p[8 * g + e];
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (GUARD && col + 8 * g + e >= N) continue;
+            if (masked && col + 8 * g + e >= N) continue;
             float o = alpha * acc[i][j][4 * g + e];
             if (beta != 0.0f) o = fmaf(beta, cin[4 * g + e], o);
             p[8 * g + e] = o;

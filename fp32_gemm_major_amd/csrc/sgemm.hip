@@ -52,16 +52,17 @@ struct KernelDesc {
   int ta, tb;  // operand storage the kernel reads
   int bm, bn;
   int bk;      // K values per LDS stage: K must be a multiple when aligned
-  int threads, guarded;
+  int threads;
+  int mode;    // SGEMM_MODE_*: which problem sizes the kernel takes
   float rel_rate;  // relative per-CU throughput, used by the tile choice
   launch_fn launch;
 };
 
-template <class T, bool G, bool TA, bool TB>
+template <class T, int MODE, bool TA, bool TB>
 hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
                        hipStream_t s) {
   const int nwg = tiles_m * tiles_n;
-  hipLaunchKernelGGL((mfma_sgemm_kernel<T, G, TA, TB>), dim3(nwg),
+  hipLaunchKernelGGL((mfma_sgemm_kernel<T, MODE, TA, TB>), dim3(nwg),
                      dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
                      a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n,
                      band_rows(tiles_m, nwg));
@@ -92,18 +93,18 @@ typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
 typedef MfmaTile<64, 64, 32, 32, 4, 2, 16, 4> M64x64;  // 16 waves
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
-#define MFMA_ONE(T, TAG, TA, TB, G, rate)                                    \
+#define MFMA_ONE(T, TAG, TA, TB, MODE, rate)                                 \
   {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
-   T::THREADS, G, rate, launch_mfma<T, G, TA, TB>}
+   T::THREADS, MODE, rate, launch_mfma<T, MODE, TA, TB>}
+#define MFMA_STORAGE(T, PRE, TA, TB, rate)                                   \
+  MFMA_ONE(T, PRE "aligned", TA, TB, SGEMM_MODE_ALIGNED, rate),              \
+  MFMA_ONE(T, PRE "edge", TA, TB, SGEMM_MODE_EDGE, rate),                    \
+  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED, rate)
 #define MFMA_SET(T, rate)                                                    \
-  MFMA_ONE(T, "aligned", false, false, false, rate),                         \
-  MFMA_ONE(T, "guarded", false, false, true, rate),                          \
-  MFMA_ONE(T, "tn_aligned", true, false, false, rate),                       \
-  MFMA_ONE(T, "tn_guarded", true, false, true, rate),                        \
-  MFMA_ONE(T, "nt_aligned", false, true, false, rate),                       \
-  MFMA_ONE(T, "nt_guarded", false, true, true, rate),                        \
-  MFMA_ONE(T, "tt_aligned", true, true, false, rate),                        \
-  MFMA_ONE(T, "tt_guarded", true, true, true, rate)
+  MFMA_STORAGE(T, "", false, false, rate),                                   \
+  MFMA_STORAGE(T, "tn_", true, false, rate),                                 \
+  MFMA_STORAGE(T, "nt_", false, true, rate),                                 \
+  MFMA_STORAGE(T, "tt_", true, true, rate)
 
 // Relative rates: throughput of each shape on 4096^3 (a grid that fills the
 // chip for all of them), normalised to the best.
@@ -113,10 +114,10 @@ const KernelDesc kKernels[] = {
     MFMA_SET(M128x128, 0.94f),
     MFMA_SET(M64x64, 0.87f),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
-     V128x128::BN, V128x128::BK, V128x128::THREADS, 0, 1.0f,
+     V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_ALIGNED, 1.0f,
      launch_valu<V128x128, false>},
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
-     V128x128::BN, V128x128::BK, V128x128::THREADS, 1, 1.0f,
+     V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED, 1.0f,
      launch_valu<V128x128, true>},
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
@@ -126,13 +127,25 @@ bool ptr_aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-// Can kernel k run these arguments?
+// Can kernel k run these arguments?  MFMA kernels read A and B with 16-byte
+// loads that need only 4-byte alignment; the VALU kernel's aligned instance
+// wants 16-byte aligned rows.
 bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
   if (k.ta != a.ta || k.tb != a.tb) return false;
-  if (k.guarded) return true;
-  return a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
-         a.lda % 4 == 0 && a.ldb % 4 == 0 && ptr_aligned16(a.A) &&
-         ptr_aligned16(a.B);
+  switch (k.mode) {
+    case SGEMM_MODE_GUARDED:
+      return true;
+    case SGEMM_MODE_EDGE:
+      // 16-byte units along M (A^T) or N (B as stored) must not straddle
+      // the edge
+      return (!a.ta || a.M % 4 == 0) && (a.tb || a.N % 4 == 0);
+    default:
+      if (a.M % k.bm != 0 || a.N % k.bn != 0 || a.K % k.bk != 0) return false;
+      if (k.variant == SGEMM_VARIANT_VALU)
+        return a.lda % 4 == 0 && a.ldb % 4 == 0 && ptr_aligned16(a.A) &&
+               ptr_aligned16(a.B);
+      return true;
+  }
 }
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
@@ -149,20 +162,22 @@ double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
 
 // Aligned kernels of the variant and operand storage (the tile shapes).
 bool is_shape(const KernelDesc& k, int variant, const RunArgs& a) {
-  return k.variant == variant && !k.guarded && k.ta == a.ta && k.tb == a.tb;
+  return k.variant == variant && k.mode == SGEMM_MODE_ALIGNED && k.ta == a.ta &&
+         k.tb == a.tb;
 }
 
 // Instance of tile shape `shape` (an aligned kernel id) for these arguments:
-// the aligned kernel when it can run them, else the guarded one.
+// the first of its aligned, edge and guarded instances that can run them.
 int instance_for(int shape, const RunArgs& a) {
-  if (kernel_fits(kKernels[shape], a)) return shape;
-  for (int i = 0; i < kNumKernels; ++i) {
-    const KernelDesc& k = kKernels[i];
-    if (k.guarded && k.variant == kKernels[shape].variant && k.ta == a.ta &&
-        k.tb == a.tb && k.bm == kKernels[shape].bm &&
-        k.bn == kKernels[shape].bn && k.bk == kKernels[shape].bk &&
-        k.threads == kKernels[shape].threads)
-      return i;
+  const KernelDesc& s = kKernels[shape];
+  for (int mode = SGEMM_MODE_ALIGNED; mode <= SGEMM_MODE_GUARDED; ++mode) {
+    for (int i = 0; i < kNumKernels; ++i) {
+      const KernelDesc& k = kKernels[i];
+      if (k.mode == mode && k.variant == s.variant && k.ta == s.ta &&
+          k.tb == s.tb && k.bm == s.bm && k.bn == s.bn && k.bk == s.bk &&
+          k.threads == s.threads && kernel_fits(k, a))
+        return i;
+    }
   }
   return SGEMM_ERR_UNSUPPORTED;
 }
@@ -314,7 +329,7 @@ const char* sgemm_kernel_name(int id) {
 }
 
 int sgemm_kernel_info(int id, int* variant, int* bm, int* bn, int* bk,
-                      int* threads, int* guarded, int* transa, int* transb) {
+                      int* threads, int* mode, int* transa, int* transb) {
   if (id < 0 || id >= kNumKernels) return SGEMM_ERR_VALUE;
   const KernelDesc& k = kKernels[id];
   if (variant) *variant = k.variant;
@@ -324,7 +339,7 @@ int sgemm_kernel_info(int id, int* variant, int* bm, int* bn, int* bk,
   if (bn) *bn = k.bn;
   if (bk) *bk = k.bk;
   if (threads) *threads = k.threads;
-  if (guarded) *guarded = k.guarded;
+  if (mode) *mode = k.mode;
   return SGEMM_OK;
 }
 

@@ -78,6 +78,27 @@ enum sgemm_variant {
   SGEMM_VARIANT_VALU = 2
 };
 
+/* Problem sizes a kernel takes (sgemm_kernel_info).  Every tile shape comes
+ * in these instances; sgemm_run uses the first that fits.
+ *   ALIGNED: M % bm == N % bn == K % bk == 0 (the VALU kernel also needs lda
+ *            and ldb multiples of 4 and 16-byte aligned A and B).  All
+ *            operand tiles move by direct global-to-LDS loads.
+ *   EDGE:    any M, N, K as long as a 16-byte piece along M or N never
+ *            straddles the edge: M % 4 == 0 when A is stored transposed,
+ *            N % 4 == 0 when B is stored as stated.  Whole K steps use
+ *            direct loads (rows and columns past the edge read the last valid
+ *            one, which only feeds outputs that are never stored); a partial
+ *            last K step goes through registers with zero fill.
+ *   GUARDED: any sizes; every operand tile goes through registers with zero
+ *            fill past the edges ("GEMM 优化之路", exercise 2).
+ * MFMA kernels need only 4-byte aligned A and B (16-byte global loads on
+ * gfx950 take any 4-byte aligned address). */
+enum sgemm_mode {
+  SGEMM_MODE_ALIGNED = 0,
+  SGEMM_MODE_EDGE = 1,
+  SGEMM_MODE_GUARDED = 2
+};
+
 /* Create a handle bound to the current HIP device, which must be gfx950.
  * On success *out receives the handle.  Returns SGEMM_ERR_HANDLE if out is
  * NULL, SGEMM_ERR_DEVICE or SGEMM_ERR_HIP if the device cannot be used. */
@@ -123,12 +144,11 @@ const char* sgemm_status_string(int status);
 int sgemm_num_kernels(void);
 const char* sgemm_kernel_name(int kernel_id); /* NULL for a bad id */
 /* Tile shape and properties of a kernel; any out-pointer may be NULL.
- * bk is the K granularity (K values per LDS stage).  `guarded` = 1 for
- * kernels that accept any size and alignment, 0 for kernels that need
- * M%bm == N%bn == K%bk == 0, lda and ldb multiples of 4 and 16-byte aligned
- * A and B.  transa / transb give the operand storage the kernel reads. */
+ * bk is the K granularity (K values per LDS stage).  *mode receives the
+ * SGEMM_MODE_* of the instance (which sizes it takes).  transa / transb give
+ * the operand storage the kernel reads. */
 int sgemm_kernel_info(int kernel_id, int* variant, int* bm, int* bn, int* bk,
-                      int* threads, int* guarded, int* transa, int* transb);
+                      int* threads, int* mode, int* transa, int* transb);
 
 /* How sgemm_run splits a call: it returns the number of launches (1 or 2)
  * or a negative status.  kernels[0] (and kernels[1], else -1) receive the
@@ -176,8 +196,8 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
 int sgemm_set_variant(sgemm_handle_t h, int variant);
 
 /* Force one kernel of the table (kernel_id >= 0), or go back to automatic
- * selection (-1).  A forced unguarded kernel makes sgemm_run return
- * SGEMM_ERR_UNSUPPORTED for arguments it cannot handle. */
+ * selection (-1).  A forced kernel makes sgemm_run return
+ * SGEMM_ERR_UNSUPPORTED for arguments its mode or storage cannot handle. */
 int sgemm_set_kernel(sgemm_handle_t h, int kernel_id);
 
 #ifdef __cplusplus

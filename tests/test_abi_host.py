@@ -89,7 +89,7 @@ def test_plan_transposed():
                               transa=ta, transb=tb)
             info = sg.sgemm_kernel_info(p[0][0])
             assert len(p) == 1 and (info["transa"], info["transb"]) == (ta, tb)
-            assert info["guarded"] == 0 and info["bm"] == 256
+            assert info["mode"] == sg.SGEMM_MODE_ALIGNED and info["bm"] == 256
     with pytest.raises(sg.SgemmError) as e:
         sg.sgemm_plan(sg.SGEMM_VARIANT_VALU, 64, 64, 64, A, 64, B, 64, C, 64, transa=1)
     assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
@@ -102,7 +102,7 @@ def test_aligned_kernels_need_whole_stages_of_k():
         for M, N in ((256, 192), (1024, 1024), (4096, 4096)):
             for kid, _, _ in sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N):
                 info = sg.sgemm_kernel_info(kid)
-                if not info["guarded"]:
+                if info["mode"] == sg.SGEMM_MODE_ALIGNED:
                     assert K % info["bk"] == 0 and M % info["bm"] == 0, (M, N, K, info)
 
 
@@ -121,14 +121,19 @@ def test_kernel_table():
     assert variants == {sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU}
     for k in table:
         assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
-    # every tile shape has an aligned and a guarded instance for each storage
+    # every MFMA tile shape has an aligned, an edge and a guarded instance for
+    # each storage; the VALU shape an aligned and a guarded one
     shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table}
     for s in shapes:
-        inst = {(k["transa"], k["transb"], k["guarded"]) for k in table
+        inst = {(k["transa"], k["transb"], k["mode"]) for k in table
                 if (k["variant"], k["bm"], k["bn"], k["bk"]) == s}
-        ops = {(0, 0)} if s[0] == sg.SGEMM_VARIANT_VALU else \
-            {(0, 0), (0, 1), (1, 0), (1, 1)}
-        assert inst == {(a, b, g) for a, b in ops for g in (0, 1)}, s
+        if s[0] == sg.SGEMM_VARIANT_VALU:
+            want = {(0, 0, sg.SGEMM_MODE_ALIGNED), (0, 0, sg.SGEMM_MODE_GUARDED)}
+        else:
+            want = {(a, b, m) for a in (0, 1) for b in (0, 1)
+                    for m in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE,
+                              sg.SGEMM_MODE_GUARDED)}
+        assert inst == want, s
 
 
 def test_select_kernel():
@@ -137,14 +142,18 @@ def test_select_kernel():
     for variant in (sg.SGEMM_VARIANT_AUTO, sg.SGEMM_VARIANT_MFMA, sg.SGEMM_VARIANT_VALU):
         want = sg.SGEMM_VARIANT_MFMA if variant != sg.SGEMM_VARIANT_VALU else variant
         k = sg.sgemm_kernel_info(sel(variant, 4096, 4096, 4096, A, 4096, B, 4096, C, 4096))
-        assert k["variant"] == want and k["guarded"] == 0
+        assert k["variant"] == want and k["mode"] == sg.SGEMM_MODE_ALIGNED
         assert 4096 % k["bm"] == 0 and 4096 % k["bn"] == 0
-        # K = 777 rows are not 16-byte aligned: guarded instance
+        mfma = want == sg.SGEMM_VARIANT_MFMA
+        # ragged sizes, rows of A only 4-byte aligned: the MFMA edge instance
         k = sg.sgemm_kernel_info(sel(variant, 1000, 1500, 777, A, 777, B, 1500, C, 1500))
-        assert k["guarded"] == 1
-        # misaligned base pointer
+        assert k["mode"] == (sg.SGEMM_MODE_EDGE if mfma else sg.SGEMM_MODE_GUARDED)
+        # N not a multiple of 4 with B as stored: only the guarded instance
+        k = sg.sgemm_kernel_info(sel(variant, 1000, 1501, 777, A, 777, B, 1501, C, 1501))
+        assert k["mode"] == sg.SGEMM_MODE_GUARDED
+        # a base pointer off 16-byte alignment: MFMA direct loads take it
         k = sg.sgemm_kernel_info(sel(variant, 1024, 1024, 1024, A + 4, 1024, B, 1024, C, 1024))
-        assert k["guarded"] == 1
+        assert k["mode"] == (sg.SGEMM_MODE_ALIGNED if mfma else sg.SGEMM_MODE_GUARDED)
     assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
     # tile shapes the cost model picks for the measured workloads: 4096^3 on one
     # 256 x 256 tile per CU, and the problems that would leave CUs idle on
@@ -172,7 +181,8 @@ def test_plan_splits_only_when_rounds_are_ragged():
     i0, i1 = sg.sgemm_kernel_info(k0), sg.sgemm_kernel_info(k1)
     assert c0 == 0 and c1 == n0 and n0 + n1 == 11008
     assert n0 % i0["bn"] == 0 and (4096 // i0["bm"]) * (n0 // i0["bn"]) % 256 == 0
-    assert i0["guarded"] == 0 and i1["guarded"] == (0 if n1 % i1["bn"] == 0 else 1)
+    assert i0["mode"] == sg.SGEMM_MODE_ALIGNED
+    assert i1["mode"] == (sg.SGEMM_MODE_ALIGNED if n1 % i1["bn"] == 0 else sg.SGEMM_MODE_EDGE)
     assert i0["bm"] * i0["bn"] >= i1["bm"] * i1["bn"]
     # the first launch's kernel is what sgemm_select_kernel reports
     assert sg.sgemm_select_kernel(0, 4096, 11008, 4096, A, 4096, B, 11008, C, 11008) == k0

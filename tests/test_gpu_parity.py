@@ -41,18 +41,32 @@ def _auto_kernel(handle):
 KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.kernel_table()
 
 
+def edge_fit(k, M, N):
+    """Round M / N up to what an edge instance takes: a multiple of 4 along
+    the operand whose 16-byte pieces run along M (A^T) or N (B as stored)."""
+    if k["mode"] == sg.SGEMM_MODE_EDGE:
+        if k["transa"]:
+            M = (M + 3) // 4 * 4
+        if not k["transb"]:
+            N = (N + 3) // 4 * 4
+    return M, N
+
+
 # ---- every kernel of the table, on problems spanning several tiles ----------
 
 @pytest.mark.parametrize("k", KERNELS, ids=[k["name"] for k in KERNELS])
 @pytest.mark.parametrize("dist", ["uniform", "int4"])
 def test_each_kernel(handle, k, dist):
     handle.set_kernel(k["id"])
-    if k["guarded"]:
-        M, N, K = 2 * k["bm"] + 37, k["bn"] + 19, 3 * k["bk"] + 5
+    if k["mode"] != sg.SGEMM_MODE_ALIGNED:
+        M, N = edge_fit(k, 2 * k["bm"] + 37, k["bn"] + 19)
+        K = 3 * k["bk"] + 5
         lda, ldb, ldc = K + 3, N + 1, N + 5
     else:
         M, N, K = 2 * k["bm"], 3 * k["bn"], 4 * k["bk"]
-        lda, ldb, ldc = K, N, N + 4
+        # MFMA direct loads take rows that are only 4-byte aligned
+        pad = 1 if k["variant"] == sg.SGEMM_VARIANT_MFMA else 0
+        lda, ldb, ldc = K + pad, N + 3 * pad, N + 4
     ta, tb = bool(k["transa"]), bool(k["transb"])
     if ta:  # stored K x M
         lda = M + (lda - K)
@@ -196,12 +210,16 @@ def test_tiny_sizes_uniform(handle, variant):
         gu.check_full(ops, gu.run(handle, ops), what=f"tiny {M}x{N}x{K}")
 
 
-def test_every_guarded_kernel_on_tiny_tails(handle):
-    for k in (k for k in KERNELS if k["guarded"]):
+def test_every_edge_and_guarded_kernel_on_tiny_tails(handle):
+    """Sizes below one tile and one K step, and one past them, on every
+    instance that takes ragged sizes (edge instances: only a partial K step,
+    or one whole step plus one)."""
+    for k in (k for k in KERNELS if k["mode"] != sg.SGEMM_MODE_ALIGNED):
         handle.set_kernel(k["id"])
         for i, (M, N, K) in enumerate([(1, 1, 1), (k["bm"] - 1, k["bn"] + 1, k["bk"] - 1),
                                        (k["bm"] + 1, k["bn"] - 1, k["bk"] + 1),
-                                       (3, 70, 33)]):
+                                       (3, 70, 33), (k["bm"] + 5, 2 * k["bn"] - 3, k["bk"])]):
+            M, N = edge_fit(k, M, N)
             ta, tb = bool(k["transa"]), bool(k["transb"])
             w = wl.Workload("tail", 4000 + i, M, N, K, 1.0, 1.0, "int4")
             ops = wl.operands(w, lda=(M if ta else K) + 1, ldb=(K if tb else N) + 2,
@@ -282,7 +300,8 @@ def test_misaligned_base_pointers(handle):
     B1[3:] = B
     sel = sg.sgemm_select_kernel(0, 256, 256, 256, A1[1:].data_ptr(), 256,
                                  B1[3:].data_ptr(), 256, C.data_ptr(), 256)
-    assert sg.sgemm_kernel_info(sel)["guarded"] == 1
+    # MFMA direct loads need only 4-byte aligned operands
+    assert sg.sgemm_kernel_info(sel)["mode"] == sg.SGEMM_MODE_ALIGNED
     out = gu.run(handle, ops, dev=(A1[1:], B1[3:], C))
     gu.check_full(ops, out, exact=True, what="misaligned")
 
@@ -320,7 +339,7 @@ def test_errors_launch_nothing(handle):
         handle.gemm(A, B, torch.ones(64 * 64, device="cuda"), 1.0, 0.0, M=64, N=64,
                     K=64, lda=63, ldb=64, ldc=64)
     assert e.value.status == sg.SGEMM_ERR_LD
-    aligned = [k for k in KERNELS if not k["guarded"]][0]
+    aligned = [k for k in KERNELS if k["mode"] == sg.SGEMM_MODE_ALIGNED][0]
     handle.set_kernel(aligned["id"])
     C = torch.ones(64 * 64, device="cuda")
     with pytest.raises(sg.SgemmError) as e:
