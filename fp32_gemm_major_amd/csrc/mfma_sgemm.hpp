@@ -142,17 +142,20 @@ __device__ __forceinline__ void unit_coords(int u, int& outer, int& k) {
   }
 }
 
-// One global_load_lds_dwordx4: this lane's 16 bytes at `src` go to LDS at
-// `lds_base` + 16 * lane.  `lds_base` must be the same for the whole wave.
-// Writing M0 and then issuing a load that writes LDS through M0 needs one
-// wait state in between.
-__device__ __forceinline__ void dma16(const float* src, unsigned lds_base) {
+// One global_load_lds_dwordx4: this lane's 16 bytes at `base` + `voff`
+// bytes go to LDS at `lds_base` + 16 * lane.  `base` (scalar registers) and
+// `lds_base` must be the same for the whole wave; `voff` is the lane's byte
+// offset.  Writing M0 and then issuing a load that writes LDS through M0
+// needs one wait state in between.  A wave-uniform base keeps the per-step
+// address update scalar: the lanes' offsets stay fixed for the whole loop.
+__device__ __forceinline__ void dma16(const float* base, unsigned voff,
+                                      unsigned lds_base) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
+      "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds_base), "v"(src)
+      : "s"(lds_base), "v"(voff), "s"(base)
       : "memory", "m0");
 }
 
@@ -202,40 +205,49 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     return TB ? B + (size_t)(n0 + o) * ldb + k : B + (size_t)k * ldb + (n0 + o);
   };
 
-  // Direct loads: per-lane pointers at K step 0, advanced by a fixed stride
-  // per step; LDS destinations are wave-uniform.  Edge kernels move a unit
-  // past the last row (K-contiguous) or column (outer-contiguous, whose
-  // extent is a multiple of 4) onto the last valid one.
-  const float* a_ptr[T::A_VEC];
-  const float* b_ptr[T::B_VEC];
+  // Direct loads: a wave-uniform base per operand (the tile's origin at K
+  // step 0, advanced by a fixed stride per step) and per-lane byte offsets
+  // that stay fixed; LDS destinations are wave-uniform.  The host keeps every
+  // offset below 2^32.  Edge kernels move a unit past the last row
+  // (K-contiguous) or column (outer-contiguous, whose extent is a multiple
+  // of 4) onto the last valid one.
+  const float* a_base = TA ? A + m0 : A + (size_t)m0 * lda;
+  const float* b_base = TB ? B + (size_t)n0 * ldb : B + n0;
+  unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
   if (!GUARD) {
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v) {
       int o = a_o[v];
       if (EDGE && m0 + o >= M) o = (A_KC ? M - 1 : M - 4) - m0;
-      a_ptr[v] = a_addr(o, a_k[v]);
+      a_voff[v] = 4u * (TA ? (unsigned)a_k[v] * (unsigned)lda + (unsigned)o
+                           : (unsigned)o * (unsigned)lda + (unsigned)a_k[v]);
     }
 #pragma unroll
     for (int v = 0; v < T::B_VEC; ++v) {
       int o = b_o[v];
       if (EDGE && n0 + o >= N) o = (B_KC ? N - 1 : N - 4) - n0;
-      b_ptr[v] = b_addr(o, b_k[v]);
+      b_voff[v] = 4u * (TB ? (unsigned)o * (unsigned)ldb + (unsigned)b_k[v]
+                           : (unsigned)b_k[v] * (unsigned)ldb + (unsigned)o);
     }
   }
   const size_t a_step = TA ? (size_t)T::BKS * lda : (size_t)T::BKS;
   const size_t b_step = TB ? (size_t)T::BKS : (size_t)T::BKS * ldb;
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
 
-  auto issue_dma = [&](int kt, int stage) {
+  // Direct load d of K step kt (the A units first, then the B units).
+  auto issue_one = [&](int d, int kt, int stage) {
     const unsigned st = lds_u + 4u * (unsigned)(stage * T::STAGE);
+    if (d < T::A_VEC)
+      dma16(a_base + (size_t)kt * a_step, a_voff[d],
+            st + 1024u * (unsigned)(d * T::WAVES + wave_u));
+    else
+      dma16(b_base + (size_t)kt * b_step, b_voff[d - T::A_VEC],
+            st + 4u * T::A_ELEMS +
+                1024u * (unsigned)((d - T::A_VEC) * T::WAVES + wave_u));
+  };
+  auto issue_dma = [&](int kt, int stage) {
 #pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v)
-      dma16(a_ptr[v] + (size_t)kt * a_step,
-            st + 1024u * (unsigned)(v * T::WAVES + wave_u));
-#pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v)
-      dma16(b_ptr[v] + (size_t)kt * b_step,
-            st + 4u * T::A_ELEMS + 1024u * (unsigned)(v * T::WAVES + wave_u));
+    for (int d = 0; d < T::A_VEC + T::B_VEC; ++d) issue_one(d, kt, stage);
   };
 
   // Register-staged loads (guarded kernels, and the partial last K step of
@@ -293,6 +305,14 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x16(0.0f);
 
+  // Wait until at most N of this wave's LDS-bound loads are still in flight
+  // (vmcnt(N); the other counters are left at their maxima).
+  constexpr int PER_STEP = T::A_VEC + T::B_VEC;  // direct loads per K step
+  constexpr int AHEAD = (NST - 2) * PER_STEP;
+  constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
+  auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
+
+  // MFMAs of one LDS stage.
   auto compute = [&](int stage) {
     const float* As = lds + stage * T::STAGE;
     const float* Bs = As + T::A_ELEMS;
@@ -332,12 +352,6 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     }
   };
 
-  // Wait until at most N of this wave's LDS-bound loads are still in flight
-  // (vmcnt(N); the other counters are left at their maxima).
-  constexpr int PER_STEP = T::A_VEC + T::B_VEC;  // direct loads per K step
-  constexpr int AHEAD = (NST - 2) * PER_STEP;
-  constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
-  auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   // K steps: all of them for guarded kernels; the whole ones for the direct
   // loads (aligned kernels have no partial step).
@@ -363,6 +377,13 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       if (s < ktiles) issue_dma(s, s);
     if (ktiles >= NST - 1) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
     else wait_all();
+    // Nothing but these loads may be outstanding when the loop starts.  The
+    // epilogue's kernel arguments are otherwise fetched (scalar loads, which
+    // complete out of order) just before the loop, and a scalar load in
+    // flight there turns every LDS-read wait inside the loop into a full
+    // lgkmcnt(0): make them live here, then wait.
+    asm volatile("" ::"s"(C), "s"(ldc), "s"(alpha), "s"(beta));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __syncthreads();
     int stage = 0, next = NST - 1;  // next = stage that receives step kt+NST-1
     for (int kt = 0; kt < ktiles; ++kt) {

@@ -127,6 +127,17 @@ bool ptr_aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// Direct loads address an operand tile as a wave-uniform base plus 32-bit
+// per-lane byte offsets: the farthest element of one K step of a tile must
+// lie within 4 GiB of the tile's origin.
+bool offsets_fit(const KernelDesc& k, const RunArgs& a) {
+  const long long a_far = a.ta ? (long long)(k.bk - 1) * a.lda + k.bm
+                               : (long long)(k.bm - 1) * a.lda + k.bk;
+  const long long b_far = a.tb ? (long long)(k.bn - 1) * a.ldb + k.bk
+                               : (long long)(k.bk - 1) * a.ldb + k.bn;
+  return 4 * a_far < (1LL << 32) && 4 * b_far < (1LL << 32);
+}
+
 // Can kernel k run these arguments?  MFMA kernels read A and B with 16-byte
 // loads that need only 4-byte alignment; the VALU kernel's aligned instance
 // wants 16-byte aligned rows.
@@ -138,13 +149,14 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
     case SGEMM_MODE_EDGE:
       // 16-byte units along M (A^T) or N (B as stored) must not straddle
       // the edge
-      return (!a.ta || a.M % 4 == 0) && (a.tb || a.N % 4 == 0);
+      return (!a.ta || a.M % 4 == 0) && (a.tb || a.N % 4 == 0) &&
+             offsets_fit(k, a);
     default:
       if (a.M % k.bm != 0 || a.N % k.bn != 0 || a.K % k.bk != 0) return false;
       if (k.variant == SGEMM_VARIANT_VALU)
         return a.lda % 4 == 0 && a.ldb % 4 == 0 && ptr_aligned16(a.A) &&
                ptr_aligned16(a.B);
-      return true;
+      return offsets_fit(k, a);
   }
 }
 
