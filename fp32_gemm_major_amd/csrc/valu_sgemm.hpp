@@ -143,6 +143,10 @@ __global__ void __launch_bounds__(T::THREADS)
   };
 
   const int ktiles = (K + T::BK - 1) / T::BK;
+  // The epilogue's kernel arguments are fetched here, not inside the K loop:
+  // a scalar load in flight in the loop forces full LDS waits there.
+  asm volatile("" ::"s"(C), "s"(ldc), "s"(alpha), "s"(beta), "s"(M), "s"(N));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   if (ktiles > 0) {
     load_tile(0);
     store_tile(0);
