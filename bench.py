@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -104,37 +105,54 @@ def time_graph(launch, reps, torch):
     return best
 
 
-def cpu_baseline(ops, target_s: float):
+def time_oracle(ops, target_s: float, threads: int):
     """Time the CPU oracle (FP64 triple loop, no error-bound pass) on the first
-    rows of the same problem, all host cores, about `target_s` seconds."""
+    rows of a problem with `threads` threads, growing the row count until one
+    run takes about `target_s` seconds.  Returns (GFLOPS, rows, seconds)."""
     import oracle
 
     M, N, K = ops.M, ops.N, ops.K
-    cores = oracle.default_threads()
 
     def run(rows):
         t0 = time.perf_counter()
         oracle.gemm(rows, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb, ops.beta,
-                    ops.C, ops.ldc, with_t=False, nthreads=cores)
+                    ops.C, ops.ldc, with_t=False, nthreads=threads)
         return time.perf_counter() - t0
 
-    rows = min(cores, M)
+    rows = min(threads, M)
     t = run(rows)
     for _ in range(3):  # grow the sample until it takes about target_s
         if t >= 0.6 * target_s or rows >= M:
             break
         want = int(rows * target_s / max(t, 1e-6))
-        rows = max(rows + cores, min(M, (want // cores) * cores))
+        rows = max(rows + threads, min(M, (want // threads) * threads))
         rows = min(rows, M)
         t = run(rows)
-    flops = 2.0 * rows * N * K
+    return 2.0 * rows * N * K / t / 1e9, rows, t
+
+
+def cpu_baseline(ops, target_s: float):
+    """The oracle on the host cores: all of them on a row slab of the timed
+    problem, and one core on the small workloads (whole or a row slab)."""
+    import oracle
+    from fp32_gemm_major_amd import workloads as wl
+
+    cores = oracle.default_threads()
+    gf, rows, t = time_oracle(ops, target_s, cores)
+    single = {}
+    for name in ("c1_128", "c2_1024", "c4_edge"):
+        w = wl.WORKLOADS[name]
+        g1, r1, t1 = time_oracle(wl.operands(w), 1.5, 1)
+        single[name] = {"gflops": round(g1, 3), "rows": r1, "of_rows": w.M,
+                        "seconds": round(t1, 2)}
     return {
-        "value": round(flops / t / 1e9, 3),
+        "value": round(gf, 3),
         "unit": "GFLOPS",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} problem ({rows}x{N} outputs, "
-                  f"full K), FP64 accumulation, {t:.1f} s",
+        "sample": f"rows 0..{rows - 1} of the {ops.M}x{ops.N}x{ops.K} problem ({rows}x{ops.N} "
+                  f"outputs, full K), FP64 accumulation, {t:.1f} s",
+        "single_core": single,
     }
 
 
@@ -155,8 +173,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this SGEMM runs on one GPU only; multi-GPU runs are not "
-              "part of this build (--gpus must be 1)", file=sys.stderr)
+        print("bench.py: this SGEMM library runs on one GPU; multi-GPU runs are not "
+              "supported (--gpus must be 1)", file=sys.stderr)
         return 2
 
     import numpy as np  # noqa: F401
@@ -205,6 +223,7 @@ def main(argv=None):
         "kernel": kname,
         "kernel_ms_mean": round(kernel_ms, 5),
         "kernel_ms_min": round(min(per), 5),
+        "kernel_ms_median": round(statistics.median(per), 5),
         "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta),
         "flops_per_launch": flops,
         # sustained rate of an MFMA chain with no memory traffic, measured now

@@ -10,7 +10,8 @@
 // lanes of a row group read one contiguous 256-byte span of B per run.
 //
 // It exists to be measured against the MFMA kernel.  Each multiply-add is one
-// unpacked v_fmac_f32: packed FP32 arithmetic is disabled for this build.
+// unpacked v_fmac_f32: the library is compiled with packed FP32 arithmetic
+// turned off (-packed-fp32-ops), so the compiler makes no v_pk_fma_f32.
 #pragma once
 
 #include <hip/hip_runtime.h>
