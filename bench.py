@@ -34,8 +34,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 
 
-KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp"),
-                  "valu": ("valu_sgemm.hpp", "tile_map.hpp")}
+# sgemm.hip holds the tile shapes and launch parameters of every kernel
+KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp", "sgemm.hip"),
+                  "valu": ("valu_sgemm.hpp", "tile_map.hpp", "sgemm.hip")}
 
 
 def kernel_source_hash(kernel: str) -> str:
