@@ -220,3 +220,19 @@ def test_create_without_gpu_fails_cleanly():
     h = ctypes.c_void_p()
     rc = sg.library().sgemm_create(ctypes.byref(h))
     assert rc in (sg.SGEMM_ERR_DEVICE, sg.SGEMM_ERR_HIP) and not h.value
+
+
+def test_huge_strides_go_to_the_guarded_instance():
+    """Direct loads address a tile with 32-bit lane offsets: when one K step of
+    every MFMA tile spans 4 GiB or more, only the guarded instance fits."""
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    M, N, K = 70, 160, 40
+    small = sg.sgemm_kernel_info(sg.sgemm_select_kernel(0, M, N, K, A, 1 << 19, B, N, C, N))
+    assert small["mode"] == sg.SGEMM_MODE_EDGE
+    lda = (1 << 24) + (1 << 20) + 3  # 63 rows of it exceed 4 GiB
+    huge = sg.sgemm_kernel_info(sg.sgemm_select_kernel(0, M, N, K, A, lda, B, N, C, N))
+    assert huge["mode"] == sg.SGEMM_MODE_GUARDED
+    # the same through B's stride (B stored as K x N: K-step rows of ldb)
+    ldb = (1 << 28) + 3
+    huge_b = sg.sgemm_kernel_info(sg.sgemm_select_kernel(0, M, N, K, A, K, B, ldb, C, N))
+    assert huge_b["mode"] == sg.SGEMM_MODE_GUARDED

@@ -290,6 +290,52 @@ def test_strided_operands_and_sentinels(handle):
     gu.check_full(ops, gu.run(handle, ops), exact=True, what="strided aligned")
 
 
+@pytest.mark.parametrize("case", ["rows_past_2_31", "tile_span_past_4_gib"])
+def test_large_strides(handle, case):
+    """Leading dimensions far beyond the sizes: row offsets past 2^31 elements
+    in A and C (64-bit addressing), and a stride so large that one K step of
+    any MFMA tile spans more than 4 GiB, which the host sends to the guarded
+    instance (direct loads use 32-bit lane offsets).  Only the used windows of
+    the multi-GiB buffers are written; C's padding must stay untouched."""
+    if case == "rows_past_2_31":
+        M, N, K = 4100, 256, 96
+        lda, ldb, ldc = (1 << 19) + 3, N + 7, (1 << 19) + 1
+    else:
+        M, N, K = 70, 160, 40
+        lda, ldb, ldc = (1 << 24) + (1 << 20) + 3, N, N + 5
+    w = wl.Workload("big", 5100 if case == "rows_past_2_31" else 5101, M, N, K, 1.5, 0.5,
+                    "int4")
+    a = wl.draw(w.cfg_id, wl.ROLE_A, M, K, w.dist)
+    b = wl.draw(w.cfg_id, wl.ROLE_B, K, N, w.dist)
+    c = wl.draw(w.cfg_id, wl.ROLE_C, M, N, w.dist)
+    dev = torch.device("cuda", 0)
+    A = torch.empty((M - 1) * lda + K, device=dev)
+    B = torch.empty((K - 1) * ldb + N, device=dev)
+    C = torch.full(((M - 1) * ldc + N,), float("nan"), device=dev)
+    A.as_strided((M, K), (lda, 1)).copy_(torch.from_numpy(a))
+    B.as_strided((K, N), (ldb, 1)).copy_(torch.from_numpy(b))
+    C.as_strided((M, N), (ldc, 1)).copy_(torch.from_numpy(c))
+    sel = sg.sgemm_select_kernel(0, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                 C.data_ptr(), ldc)
+    mode = sg.sgemm_kernel_info(sel)["mode"]
+    if case == "rows_past_2_31":
+        assert (M - 1) * lda > 2 ** 31 and mode != sg.SGEMM_MODE_GUARDED
+    else:
+        assert mode == sg.SGEMM_MODE_GUARDED
+    handle.gemm(A, B, C, w.alpha, w.beta, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
+    torch.cuda.synchronize()
+    got = C.as_strided((M, N), (ldc, 1)).cpu().numpy()
+    R, T = oracle.gemm(M, N, K, w.alpha, a, K, b, N, w.beta, c, N)
+    gu.check(got, R, T, K, w.alpha, w.beta, c, exact=True, what=case)
+    if ldc > N:  # padding after a few rows, including the last full one
+        width = min(ldc - N, 64)
+        for row in (0, M // 2, M - 2):
+            pad = C[row * ldc + N: row * ldc + N + width].cpu().numpy()
+            assert np.all(np.isnan(pad)), f"{case}: C padding written in row {row}"
+    del A, B, C
+    torch.cuda.empty_cache()
+
+
 def test_misaligned_base_pointers(handle):
     w = wl.Workload("mis", 5006, 256, 256, 256, 1.0, 0.0, "int4")
     ops = wl.operands(w)
