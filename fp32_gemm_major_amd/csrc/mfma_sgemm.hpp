@@ -35,9 +35,14 @@
 //     M x N, which are never stored, so clamping the address is enough and no
 //     zero fill is needed.  The partial K step at the end (K not a multiple of
 //     the stage's K range) goes through registers with zero fill, since there
-//     both operands must be exactly zero past K.  A unit that runs along M or N
-//     (B as stored, or A^T) must not be split by the edge, so this mode needs
-//     that extent to be a multiple of 4.
+//     both operands must be exactly zero past K.  A unit that runs along M or
+//     N (B as stored, or A^T) may straddle the edge when that extent is not a
+//     multiple of 4: its elements past the edge again only feed outputs that
+//     are never stored, and the 16-byte read stays inside the operand as long
+//     as the row is not the last one (the read ends at most 3 floats into the
+//     next row).  In that case the last K row always goes through the
+//     zero-filled register step, which then covers the last partial or whole
+//     K step.  This mode needs that extent to be at least 4.
 //   - guarded (MODE 2): every unit through registers, 16-byte loads where the
 //     whole unit is inside the operand, element loads with zero fill elsewhere
 //     ("GEMM 优化之路", exercise 2: out-of-range loads become zeros; no thread
@@ -208,9 +213,13 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   // Direct loads: a wave-uniform base per operand (the tile's origin at K
   // step 0, advanced by a fixed stride per step) and per-lane byte offsets
   // that stay fixed; LDS destinations are wave-uniform.  The host keeps every
-  // offset below 2^32.  Edge kernels move a unit past the last row
-  // (K-contiguous) or column (outer-contiguous, whose extent is a multiple
-  // of 4) onto the last valid one.
+  // offset below 2^32, and no offset may be negative (it would wrap).  Edge
+  // kernels move a unit wholly past the last row (K-contiguous) onto the last
+  // valid row, and one wholly past the last column (outer-contiguous, extent
+  // at least 4) onto the last four columns, or onto the tile's first column
+  // when those start left of the tile (extent not a multiple of 4: that unit
+  // then straddles the edge, which the K-row limit below allows); a unit that
+  // straddles the last column is read as it is.
   const float* a_base = TA ? A + m0 : A + (size_t)m0 * lda;
   const float* b_base = TB ? B + (size_t)n0 * ldb : B + n0;
   unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
@@ -218,14 +227,14 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v) {
       int o = a_o[v];
-      if (EDGE && m0 + o >= M) o = (A_KC ? M - 1 : M - 4) - m0;
+      if (EDGE && m0 + o >= M) o = A_KC ? M - 1 - m0 : (M - 4 > m0 ? M - 4 - m0 : 0);
       a_voff[v] = 4u * (TA ? (unsigned)a_k[v] * (unsigned)lda + (unsigned)o
                            : (unsigned)o * (unsigned)lda + (unsigned)a_k[v]);
     }
 #pragma unroll
     for (int v = 0; v < T::B_VEC; ++v) {
       int o = b_o[v];
-      if (EDGE && n0 + o >= N) o = (B_KC ? N - 1 : N - 4) - n0;
+      if (EDGE && n0 + o >= N) o = B_KC ? N - 1 - n0 : (N - 4 > n0 ? N - 4 - n0 : 0);
       b_voff[v] = 4u * (TB ? (unsigned)o * (unsigned)ldb + (unsigned)b_k[v]
                            : (unsigned)b_k[v] * (unsigned)ldb + (unsigned)o);
     }
@@ -354,8 +363,13 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 
 
   // K steps: all of them for guarded kernels; the whole ones for the direct
-  // loads (aligned kernels have no partial step).
-  const int ktiles = GUARD ? (K + T::BKS - 1) / T::BKS : K / T::BKS;
+  // loads (aligned kernels have no partial step).  When a unit can straddle
+  // the last column of an outer-contiguous operand, the direct loads stop
+  // short of the last K row (see the edge mode above).
+  const bool straddle = EDGE && ((!A_KC && (M & 3) != 0) || (!B_KC && (N & 3) != 0));
+  const int ktiles = GUARD      ? (K + T::BKS - 1) / T::BKS
+                     : straddle ? (K > 0 ? (K - 1) / T::BKS : 0)
+                                : K / T::BKS;
   // No scalar load may be in flight inside the K loop.  The epilogue's kernel
   // arguments are otherwise fetched just before the loop, and scalar loads
   // complete out of order, so one still pending there turns every LDS-read

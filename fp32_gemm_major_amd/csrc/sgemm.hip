@@ -150,10 +150,9 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
     case SGEMM_MODE_GUARDED:
       return true;
     case SGEMM_MODE_EDGE:
-      // 16-byte units along M (A^T) or N (B as stored) must not straddle
-      // the edge
-      return (!a.ta || a.M % 4 == 0) && (a.tb || a.N % 4 == 0) &&
-             offsets_fit(k, a);
+      // a 16-byte unit along M (A^T) or N (B as stored) needs 4 elements
+      // to clamp onto
+      return (!a.ta || a.M >= 4) && (a.tb || a.N >= 4) && offsets_fit(k, a);
     default:
       if (a.M % k.bm != 0 || a.N % k.bn != 0 || a.K % k.bk != 0) return false;
       if (k.variant == SGEMM_VARIANT_VALU)

@@ -83,12 +83,14 @@ enum sgemm_variant {
  *   ALIGNED: M % bm == N % bn == K % bk == 0 (the VALU kernel also needs lda
  *            and ldb multiples of 4 and 16-byte aligned A and B).  All
  *            operand tiles move by direct global-to-LDS loads.
- *   EDGE:    any M, N, K as long as a 16-byte piece along M or N never
- *            straddles the edge: M % 4 == 0 when A is stored transposed,
- *            N % 4 == 0 when B is stored as stated.  Whole K steps use
- *            direct loads (rows and columns past the edge read the last valid
- *            one, which only feeds outputs that are never stored); a partial
- *            last K step goes through registers with zero fill.
+ *   EDGE:    any M, N, K with M >= 4 when A is stored transposed and N >= 4
+ *            when B is stored as stated (the extents along which 16-byte
+ *            pieces run).  Whole K steps use direct loads (rows and columns
+ *            past the edge read the last valid one, or the piece that
+ *            straddles the edge is read as it is; either only feeds outputs
+ *            that are never stored); a partial last K step, and the last K
+ *            row when a piece can straddle, go through registers with zero
+ *            fill.
  *   GUARDED: any sizes; every operand tile goes through registers with zero
  *            fill past the edges ("GEMM 优化之路", exercise 2).
  * MFMA kernels need only 4-byte aligned A and B (16-byte global loads on

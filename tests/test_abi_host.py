@@ -148,8 +148,11 @@ def test_select_kernel():
         # ragged sizes, rows of A only 4-byte aligned: the MFMA edge instance
         k = sg.sgemm_kernel_info(sel(variant, 1000, 1500, 777, A, 777, B, 1500, C, 1500))
         assert k["mode"] == (sg.SGEMM_MODE_EDGE if mfma else sg.SGEMM_MODE_GUARDED)
-        # N not a multiple of 4 with B as stored: only the guarded instance
+        # N not a multiple of 4 with B as stored: still the edge instance
         k = sg.sgemm_kernel_info(sel(variant, 1000, 1501, 777, A, 777, B, 1501, C, 1501))
+        assert k["mode"] == (sg.SGEMM_MODE_EDGE if mfma else sg.SGEMM_MODE_GUARDED)
+        # fewer than 4 columns with B as stored: only the guarded instance
+        k = sg.sgemm_kernel_info(sel(variant, 1000, 3, 777, A, 777, B, 3, C, 3))
         assert k["mode"] == sg.SGEMM_MODE_GUARDED
         # a base pointer off 16-byte alignment: MFMA direct loads take it
         k = sg.sgemm_kernel_info(sel(variant, 1024, 1024, 1024, A + 4, 1024, B, 1024, C, 1024))

@@ -42,13 +42,13 @@ KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.kernel_tabl
 
 
 def edge_fit(k, M, N):
-    """Round M / N up to what an edge instance takes: a multiple of 4 along
-    the operand whose 16-byte pieces run along M (A^T) or N (B as stored)."""
+    """Raise M / N to what an edge instance takes: at least 4 along the
+    operand whose 16-byte pieces run along M (A^T) or N (B as stored)."""
     if k["mode"] == sg.SGEMM_MODE_EDGE:
         if k["transa"]:
-            M = (M + 3) // 4 * 4
+            M = max(M, 4)
         if not k["transb"]:
-            N = (N + 3) // 4 * 4
+            N = max(N, 4)
     return M, N
 
 
@@ -226,6 +226,21 @@ def test_every_edge_and_guarded_kernel_on_tiny_tails(handle):
                               ldc=N + 3, ta=ta, tb=tb)
             gu.check_full(ops, gu.run(handle, ops), exact=True,
                           what=f"{k['name']} {M}x{N}x{K}")
+
+
+def test_edge_kernels_with_straddling_pieces(handle):
+    """Extents along which 16-byte pieces run (N for B as stored, M for A^T)
+    two past a multiple of 4, K exactly two K steps and no row padding: the
+    first step's direct loads read pieces that straddle the edge, and the
+    last step (which holds the last K row) goes through registers."""
+    for k in (k for k in KERNELS if k["mode"] == sg.SGEMM_MODE_EDGE):
+        handle.set_kernel(k["id"])
+        ta, tb = bool(k["transa"]), bool(k["transb"])
+        M, N, K = k["bm"] + 6, k["bn"] + 6, 2 * k["bk"]
+        w = wl.Workload("straddle", 4100 + k["id"], M, N, K, 1.0, 1.0, "int4")
+        ops = wl.operands(w, ta=ta, tb=tb)  # minimal leading dimensions
+        gu.check_full(ops, gu.run(handle, ops), exact=True,
+                      what=f"{k['name']} {M}x{N}x{K}")
 
 
 def test_empty_problems_touch_nothing(handle):
