@@ -36,12 +36,17 @@ SGEMM_MODE_ALIGNED = 0
 SGEMM_MODE_EDGE = 1
 SGEMM_MODE_GUARDED = 2
 
+SGEMM_SCHEDULE_TILES = 0
+SGEMM_SCHEDULE_STREAM_K = 1
+
 EXPORTED = [
     "sgemm_create", "sgemm_run", "sgemm_run_ex", "sgemm_destroy", "sgemm_validate",
     "sgemm_validate_ex", "sgemm_plan_ex",
     "sgemm_status_string", "sgemm_num_kernels", "sgemm_kernel_name",
     "sgemm_kernel_info", "sgemm_plan", "sgemm_select_kernel", "sgemm_tile_coords",
     "sgemm_set_variant", "sgemm_set_kernel", "sgemm_diag_mfma_chain",
+    "sgemm_set_workspace", "sgemm_workspace_size", "sgemm_plan_handle",
+    "sgemm_kernel_schedule",
 ]
 
 
@@ -77,11 +82,16 @@ def _bind(lib):
     lib.sgemm_set_variant.argtypes = [p, i]
     lib.sgemm_set_kernel.argtypes = [p, i]
     lib.sgemm_diag_mfma_chain.argtypes = [i, i, p, p]
+    lib.sgemm_set_workspace.argtypes = [p, p, ctypes.c_size_t]
+    lib.sgemm_workspace_size.argtypes = [p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.sgemm_plan_handle.argtypes = [p, i, i, i, i, i, p, i, p, i, p, i, ip, ip]
+    lib.sgemm_kernel_schedule.argtypes = [i]
     for name in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
                  "sgemm_num_kernels", "sgemm_kernel_info", "sgemm_select_kernel",
                  "sgemm_plan", "sgemm_diag_mfma_chain", "sgemm_run_ex",
                  "sgemm_validate_ex", "sgemm_plan_ex",
-                 "sgemm_set_variant", "sgemm_set_kernel"):
+                 "sgemm_set_variant", "sgemm_set_kernel", "sgemm_set_workspace",
+                 "sgemm_workspace_size", "sgemm_plan_handle", "sgemm_kernel_schedule"):
         getattr(lib, name).restype = i
     return lib
 
@@ -130,6 +140,37 @@ def sgemm_destroy(h) -> int:
     return library().sgemm_destroy(h)
 
 
+def sgemm_set_workspace(h, ptr, nbytes) -> int:
+    """Device memory (address, bytes) for stream-K partial tiles; 0, 0 removes it."""
+    return _check(library().sgemm_set_workspace(h, ptr or None, nbytes),
+                  "sgemm_set_workspace")
+
+
+def sgemm_workspace_size(h) -> int:
+    n = ctypes.c_size_t()
+    _check(library().sgemm_workspace_size(h, ctypes.byref(n)), "sgemm_workspace_size")
+    return n.value
+
+
+def sgemm_plan_handle(h, M, N, K, A, lda, B, ldb, C, ldc, transa=0, transb=0):
+    """The launches sgemm_run_ex makes on handle h: [(kernel, first column,
+    columns), ...]."""
+    ks = (ctypes.c_int * 2)()
+    n_split = ctypes.c_int()
+    n = _check(library().sgemm_plan_handle(h, transa, transb, M, N, K, A, lda, B, ldb,
+                                           C, ldc, ks, ctypes.byref(n_split)),
+               "sgemm_plan_handle")
+    if n == 0:
+        return []
+    if n == 1:
+        return [(ks[0], 0, N)]
+    return [(ks[0], 0, n_split.value), (ks[1], n_split.value, N - n_split.value)]
+
+
+def sgemm_kernel_schedule(kernel_id: int) -> int:
+    return _check(library().sgemm_kernel_schedule(kernel_id), "sgemm_kernel_schedule")
+
+
 def sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc) -> int:
     return library().sgemm_validate(M, N, K, A, lda, B, ldb, beta, C, ldc)
 
@@ -161,6 +202,7 @@ def sgemm_kernel_info(kernel_id: int) -> dict:
            "sgemm_kernel_info")
     keys = ("variant", "bm", "bn", "bk", "threads", "mode", "transa", "transb")
     d = {k: v.value for k, v in zip(keys, vals)}
+    d["schedule"] = sgemm_kernel_schedule(kernel_id)
     d["name"] = sgemm_kernel_name(kernel_id)
     d["id"] = kernel_id
     return d
@@ -227,19 +269,42 @@ def mfma_chain_tflops(workgroups=1024, iterations=4096, reps=3):
 # ---- torch-tensor convenience ------------------------------------------------
 
 class Handle:
-    """Owns one sgemm handle; usable as a context manager."""
+    """Owns one sgemm handle; usable as a context manager.
 
-    def __init__(self, variant: int = SGEMM_VARIANT_AUTO, kernel: int = -1):
+    With ``workspace=True`` (the default) it also owns a device tensor of
+    sgemm_workspace_size bytes, set as the handle's stream-K workspace, so
+    stream-K plans are available.  Calls through one Handle share it: use
+    separate Handles for calls that may overlap on different streams."""
+
+    def __init__(self, variant: int = SGEMM_VARIANT_AUTO, kernel: int = -1,
+                 workspace: bool = True):
         self.h = sgemm_create()
+        self.workspace = None
         if variant != SGEMM_VARIANT_AUTO:
             sgemm_set_variant(self.h, variant)
         if kernel >= 0:
             sgemm_set_kernel(self.h, kernel)
+        if workspace:
+            self.set_workspace(sgemm_workspace_size(self.h))
+
+    def set_workspace(self, nbytes: int):
+        """Give the handle a fresh workspace of ``nbytes`` (0: none)."""
+        sgemm_set_workspace(self.h, 0, 0)
+        self.workspace = None
+        if nbytes:
+            self.workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32,
+                                         device="cuda")
+            sgemm_set_workspace(self.h, self.workspace.data_ptr(), nbytes)
+
+    def plan(self, M, N, K, A, lda, B, ldb, C, ldc, transa=False, transb=False):
+        return sgemm_plan_handle(self.h, M, N, K, A, lda, B, ldb, C, ldc,
+                                 int(bool(transa)), int(bool(transb)))
 
     def close(self):
         if self.h:
             sgemm_destroy(self.h)
             self.h = None
+        self.workspace = None
 
     def __enter__(self):
         return self

@@ -120,6 +120,12 @@ struct MfmaTile {
   // floats the K groups 1..KG-1 leave in LDS for group 0
   static constexpr int RED_ELEMS = (KG - 1) * WAVES_MN * 64 * 16 * FM * FN;
   static_assert(RED_ELEMS <= 2 * STAGE, "reduction fits in LDS");
+  // Stream-K: workgroups per CU in the persistent grid (one when a
+  // workgroup already has 8 waves or more, so the kernel keeps the
+  // registers of two waves per SIMD or more), and the waves per SIMD the
+  // stream-K kernel's registers are sized for.
+  static constexpr int SK_PER_CU = WAVES >= 8 ? 1 : 2;
+  static constexpr int SK_OCC = (WAVES * SK_PER_CU + 3) / 4;
 };
 
 // K-contiguous tile: float offset of unit c (four k) of outer row r.
@@ -166,24 +172,51 @@ __device__ __forceinline__ void dma16(const float* base, unsigned voff,
 
 enum { MODE_ALIGNED = 0, MODE_EDGE = 1, MODE_GUARDED = 2 };
 
+// The operation's arguments, as the C ABI receives them.
+struct GemmArgs {
+  int M, N, K;
+  float alpha, beta;
+  const float* A;
+  int lda;
+  const float* B;
+  int ldb;
+  float* C;
+  int ldc;
+};
+
+// LDS floats a kernel of tile T in mode MODE uses.
+template <class T, int MODE>
+struct TileLds {
+  static constexpr int NST = MODE == MODE_GUARDED ? 2 : T::S;  // stages in use
+  static constexpr int FLOATS = NST * T::STAGE;
+};
+
+// K steps of one tile: ceil(K / (K values per stage)).  The direct loads
+// cover the first ones; a partial last step (and, when a 16-byte piece can
+// straddle the edge, the step holding the last K row) goes through registers.
+template <class T>
+__host__ __device__ inline int tile_k_steps(int K) {
+  return (K + T::BKS - 1) / T::BKS;
+}
+
 // TA: A stored K x M (op(A) = A^T).  TB: B stored N x K (op(B) = B^T).
+// Accumulate the output tile at (m0, n0) over K steps [s0, s1) into acc (the
+// caller zeroes it).  On return the first K group's waves (kg == 0) hold the
+// tile's partial sum over those steps; the LDS is still in use by the K-group
+// reduction, so a caller that reuses it must pass a barrier first.
 template <class T, int MODE, bool TA, bool TB>
-__global__ void __launch_bounds__(T::THREADS, T::OCC)
-    mfma_sgemm_kernel(int M, int N, int K, float alpha,
-                      const float* __restrict__ A, int lda,
-                      const float* __restrict__ B, int ldb, float beta,
-                      float* __restrict__ C, int ldc, int tiles_m,
-                      int tiles_n, int band) {
+__device__ __forceinline__ void tile_accumulate(
+    const GemmArgs& g, float* lds, int m0, int n0, int s0, int s1,
+    f32x16 (&acc)[T::FM][T::FN]) {
   constexpr bool A_KC = !TA;  // A tile K-contiguous
   constexpr bool B_KC = TB;   // B tile K-contiguous
   constexpr bool GUARD = MODE == MODE_GUARDED;  // no direct loads
   constexpr bool EDGE = MODE == MODE_EDGE;
-  constexpr int NST = GUARD ? 2 : T::S;  // LDS stages in use
-  __shared__ __attribute__((aligned(1024))) float lds[NST * T::STAGE];
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  constexpr int NST = TileLds<T, MODE>::NST;
+  const int M = g.M, N = g.N, K = g.K;
+  const float* __restrict__ A = g.A;
+  const float* __restrict__ B = g.B;
+  const int lda = g.lda, ldb = g.ldb;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -308,12 +341,6 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
                                 4 * lane) = rb[v];
   };
 
-  f32x16 acc[T::FM][T::FN];
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x16(0.0f);
-
   // Wait until at most N of this wave's LDS-bound loads are still in flight
   // (vmcnt(N); the other counters are left at their maxima).
   constexpr int PER_STEP = T::A_VEC + T::B_VEC;  // direct loads per K step
@@ -367,42 +394,45 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   // the last column of an outer-contiguous operand, the direct loads stop
   // short of the last K row (see the edge mode above).
   const bool straddle = EDGE && ((!A_KC && (M & 3) != 0) || (!B_KC && (N & 3) != 0));
-  const int ktiles = GUARD      ? (K + T::BKS - 1) / T::BKS
-                     : straddle ? (K > 0 ? (K - 1) / T::BKS : 0)
-                                : K / T::BKS;
+  // direct-load steps: [0, kd); guarded kernels load every step through
+  // registers
+  const int kd = GUARD      ? tile_k_steps<T>(K)
+                 : straddle ? (K > 0 ? (K - 1) / T::BKS : 0)
+                            : K / T::BKS;
   // No scalar load may be in flight inside the K loop.  The epilogue's kernel
   // arguments are otherwise fetched just before the loop, and scalar loads
   // complete out of order, so one still pending there turns every LDS-read
   // wait inside the loop into a full lgkmcnt(0) (measured: 4096^3 at 89% of
   // peak instead of 92%).  Make them live here and wait once.
-  asm volatile("" ::"s"(C), "s"(ldc), "s"(alpha), "s"(beta), "s"(M), "s"(N));
+  asm volatile("" ::"s"(g.C), "s"(g.ldc), "s"(g.alpha), "s"(g.beta), "s"(M), "s"(N));
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   if (GUARD) {
-    if (ktiles > 0) {
-      load_regs(0);
+    if (s0 < s1) {
+      load_regs(s0);
       store_regs(0);
     }
     __syncthreads();
-    for (int kt = 0; kt < ktiles; ++kt) {
-      const int stage = kt & 1;
-      const bool more = kt + 1 < ktiles;
+    for (int kt = s0; kt < s1; ++kt) {
+      const int stage = (kt - s0) & 1;
+      const bool more = kt + 1 < s1;
       if (more) load_regs(kt + 1);
       compute(stage);
       if (more) store_regs(stage ^ 1);
       __syncthreads();
     }
   } else {
-    // Prologue: K steps 0 .. NST-2 in flight, wait for step 0.
+    const int e = s1 < kd ? s1 : kd;  // direct-load steps [s0, e)
+    // Prologue: K steps s0 .. s0+NST-2 in flight, wait for step s0.
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
-      if (s < ktiles) issue_dma(s, s);
-    if (ktiles >= NST - 1) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
+      if (s0 + s < e) issue_dma(s0 + s, s);
+    if (e - s0 >= NST - 1) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
     else wait_all();
     __syncthreads();
     int stage = 0, next = NST - 1;  // next = stage that receives step kt+NST-1
-    for (int kt = 0; kt < ktiles; ++kt) {
+    for (int kt = s0; kt < e; ++kt) {
       // next's previous contents (step kt-1) were read before the last barrier
-      const bool issue = kt + NST - 1 < ktiles;
+      const bool issue = kt + NST - 1 < e;
       if (issue) issue_dma(kt + NST - 1, next);
       compute(stage);
       // step kt+1 must be in LDS: steps kt+2 .. kt+NST-1 may still be in flight
@@ -412,10 +442,11 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
       stage = stage + 1 == NST ? 0 : stage + 1;
       next = next + 1 == NST ? 0 : next + 1;
     }
-    // Edge kernels: the partial last K step, zero-filled past K.  The stages
-    // are free after the loop's last barrier.
-    if (EDGE && ktiles * T::BKS < K) {
-      load_regs(ktiles);
+    // Edge kernels: the last step through registers, zero-filled past K,
+    // when it is partial or holds the last K row of a straddling operand.
+    // The stages are free after the loop's last barrier.
+    if (EDGE && kd * T::BKS < K && s0 <= kd && kd < s1) {
+      load_regs(kd);
       store_regs(0);
       __syncthreads();
       compute(0);
@@ -434,16 +465,16 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int e4 = (i * T::FN + j) * 4 + g;
+          for (int gq = 0; gq < 4; ++gq) {
+            const int e4 = (i * T::FN + j) * 4 + gq;
             f32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+            for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e];
             red[(((kg - 1) * T::WAVES_MN + wmn) * PER_WAVE + e4) * 64 + lane] = v;
           }
     }
     __syncthreads();
-    if (kg > 0) return;
+    if (kg == 0) {
 #pragma unroll
     for (int src = 1; src < T::KG; ++src)
 #pragma unroll
@@ -451,19 +482,47 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 #pragma unroll
         for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int e4 = (i * T::FN + j) * 4 + g;
+          for (int gq = 0; gq < 4; ++gq) {
+            const int e4 = (i * T::FN + j) * 4 + gq;
             const f32x4 v =
                 red[(((src - 1) * T::WAVES_MN + wmn) * PER_WAVE + e4) * 64 + lane];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * gq + e] += v[e];
           }
+    }
   }
+}
 
-  // Epilogue.  Block (i, j), register 4g + e of lane (li, lh) holds
-  // C(row, col) with row = li and col = 8g + 4lh + e inside the block.
-  const int crow = m0 + wm * T::WM + li;
-  const int ccol = n0 + wn * T::WN + lh * 4;
+// Lane layout of a wave's tile (the same in every kernel of tile T).
+template <class T>
+struct WaveCoords {
+  int lane, wave, kg, wmn, wm, wn, li, lh;
+  __device__ __forceinline__ WaveCoords() {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    kg = wave / T::WAVES_MN;
+    wmn = wave % T::WAVES_MN;
+    wm = wmn / T::WAVES_N;
+    wn = wmn % T::WAVES_N;
+    li = lane & 31;
+    lh = lane >> 5;
+  }
+};
+
+// C = alpha*acc + beta*C for the tile at (m0, n0), by the waves of the first
+// K group.  Block (i, j), register 4g + e of lane (li, lh) holds C(row, col)
+// with row = li and col = 8g + 4lh + e inside the block.
+template <class T, int MODE>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, int m0, int n0,
+                                           const f32x16 (&acc)[T::FM][T::FN]) {
+  constexpr bool GUARD = MODE == MODE_GUARDED;
+  constexpr bool EDGE = MODE == MODE_EDGE;
+  const WaveCoords<T> w;
+  const int M = g.M, N = g.N, ldc = g.ldc;
+  const float alpha = g.alpha, beta = g.beta;
+  float* __restrict__ C = g.C;
+  const int crow = m0 + w.wm * T::WM + w.li;
+  const int ccol = n0 + w.wn * T::WN + w.lh * 4;
   const bool c_vec =
       (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
   // stores need bounds checks: guarded kernels, and edge tiles of edge kernels
@@ -480,40 +539,180 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
         f32x4 cin[4];
         if (beta != 0.0f) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) cin[g] = *reinterpret_cast<const f32x4*>(p + 8 * g);
+          for (int q = 0; q < 4; ++q) cin[q] = *reinterpret_cast<const f32x4*>(p + 8 * q);
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int q = 0; q < 4; ++q) {
           f32x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[e] = alpha * acc[i][j][4 * g + e];
-            if (beta != 0.0f) o[e] = fmaf(beta, cin[g][e], o[e]);
+            o[e] = alpha * acc[i][j][4 * q + e];
+            if (beta != 0.0f) o[e] = fmaf(beta, cin[q][e], o[e]);
           }
-          *reinterpret_cast<f32x4*>(p + 8 * g) = o;
+          *reinterpret_cast<f32x4*>(p + 8 * q) = o;
         }
       } else if (!masked || row < M) {
         float cin[16];
         if (beta != 0.0f) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (!masked || col + 8 * g + e < N) cin[4 * g + e] = p[8 * g + e];
+              if (!masked || col + 8 * q + e < N) cin[4 * q + e] = p[8 * q + e];
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (masked && col + 8 * g + e >= N) continue;
-            float o = alpha * acc[i][j][4 * g + e];
-            if (beta != 0.0f) o = fmaf(beta, cin[4 * g + e], o);
-            p[8 * g + e] = o;
+            if (masked && col + 8 * q + e >= N) continue;
+            float o = alpha * acc[i][j][4 * q + e];
+            if (beta != 0.0f) o = fmaf(beta, cin[4 * q + e], o);
+            p[8 * q + e] = o;
           }
       }
       // keep one block's C traffic in registers at a time
       __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+template <class T>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x16(0.0f);
+}
+
+// One tile per workgroup: workgroup -> tile through the XCD-aware order.
+template <class T, int MODE, bool TA, bool TB>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+    mfma_sgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int band) {
+  __shared__ __attribute__((aligned(1024))) float lds[TileLds<T, MODE>::FLOATS];
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
+  f32x16 acc[T::FM][T::FN];
+  zero_acc<T>(acc);
+  tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, 0,
+                                   tile_k_steps<T>(g.K), acc);
+  if (threadIdx.x / 64 / T::WAVES_MN == 0) store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
+}
+
+// ---- stream-K ------------------------------------------------------------
+//
+// The tiles x K-steps iteration space (W = tiles * steps, tile-major) is cut
+// into G equal contiguous ranges, one per workgroup of a grid of G: the
+// workgroup at position h (xcd_position: one XCD's workgroups hold
+// consecutive positions) owns iterations [b(h), b(h+1)) with
+// b(h) = floor(h*W/G), and tile t is tile t of the band walk, so an XCD
+// works on a compact block of C.  It
+// walks them tile by tile; a tile it covers whole is stored at once, a part
+// of a tile is a partial sum written to the workspace.  A workgroup writes
+// at most two partials: slot 2h for a part that starts at b(h) (its first
+// part) and slot 2h+1 for a part that ends at b(h+1) inside a tile (its
+// last).  The fixup kernel then adds each split tile's partials in K order
+// and stores the tile, so the result does not depend on timing.
+//
+// Slot layout: the first K group's accumulators as the waves hold them,
+// f32x4 per lane, (wave, block, quad) major -- BM*BN floats per slot.
+
+__host__ __device__ inline long long sk_bound(long long W, int G, int h) {
+  return W * h / G;
+}
+
+template <class T>
+__device__ __forceinline__ void store_partial(float* slot,
+                                              const f32x16 (&acc)[T::FM][T::FN]) {
+  const WaveCoords<T> w;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+        *reinterpret_cast<f32x4*>(
+            slot + (((w.wmn * T::FM + i) * T::FN + j) * 4 + q) * 256 + 4 * w.lane) = v;
+      }
+}
+
+template <class T>
+__device__ __forceinline__ void add_partial(const float* slot,
+                                            f32x16 (&acc)[T::FM][T::FN]) {
+  const WaveCoords<T> w;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(
+            slot + (((w.wmn * T::FM + i) * T::FN + j) * 4 + q) * 256 + 4 * w.lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+      }
+}
+
+template <class T, int MODE, bool TA, bool TB>
+__global__ void __launch_bounds__(T::THREADS, T::SK_OCC)
+    mfma_sgemm_sk_kernel(GemmArgs g, int tiles_m, int tiles_n, int band,
+                         int steps, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(1024))) float lds[TileLds<T, MODE>::FLOATS];
+  const int tiles = tiles_m * tiles_n;
+  const long long W = (long long)tiles * steps;
+  const int G = gridDim.x, h = xcd_position(blockIdx.x, gridDim.x);
+  const long long b0 = sk_bound(W, G, h), b1 = sk_bound(W, G, h + 1);
+  const bool first_group = threadIdx.x / 64 / T::WAVES_MN == 0;
+  for (long long i = b0; i < b1;) {
+    const int t = (int)(i / steps);
+    const long long ts = (long long)t * steps;
+    const int s0 = (int)(i - ts);
+    const int s1 = (int)(b1 - ts < steps ? b1 - ts : steps);
+    int tm, tn;
+    band_walk(t, tiles_m, tiles_n, band, tm, tn);
+    f32x16 acc[T::FM][T::FN];
+    zero_acc<T>(acc);
+    tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, s0, s1, acc);
+    if (first_group) {
+      if (s0 == 0 && s1 == steps)
+        store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
+      else
+        store_partial<T>(ws + (size_t)(2 * h + (i == b0 ? 0 : 1)) * (T::BM * T::BN), acc);
+    }
+    __syncthreads();  // the next part reuses the LDS
+    i = ts + s1;
+  }
+}
+
+// Workgroup h fixes the tile its range starts inside, when its range reaches
+// that tile's end (it is then the tile's last owner, so each split tile is
+// fixed exactly once).  The owners run from the one holding the tile's first
+// iteration, owner(i) = floor(((i+1)*G - 1) / W), up to h.
+template <class T, int MODE>
+__global__ void __launch_bounds__(T::THREADS, T::SK_OCC)
+    mfma_sgemm_fixup_kernel(GemmArgs g, int tiles_m, int tiles_n, int band,
+                            int steps, const float* __restrict__ ws) {
+  const int tiles = tiles_m * tiles_n;
+  const long long W = (long long)tiles * steps;
+  const int G = gridDim.x, h = xcd_position(blockIdx.x, gridDim.x);
+  const long long b0 = sk_bound(W, G, h), b1 = sk_bound(W, G, h + 1);
+  if (b0 >= b1) return;
+  const int t = (int)(b0 / steps);
+  const long long ts = (long long)t * steps;
+  if (b0 == ts || b1 < ts + steps) return;
+  if (threadIdx.x / 64 / T::WAVES_MN != 0) return;  // first K group only
+  const int first = (int)(((ts + 1) * G - 1) / W);
+  f32x16 acc[T::FM][T::FN];
+  zero_acc<T>(acc);
+  for (int o = first; o <= h; ++o) {
+    const long long bo = sk_bound(W, G, o);
+    if (bo >= sk_bound(W, G, o + 1)) continue;  // empty range
+    add_partial<T>(ws + (size_t)(2 * o + (bo >= ts ? 0 : 1)) * (T::BM * T::BN), acc);
+  }
+  int tm, tn;
+  band_walk(t, tiles_m, tiles_n, band, tm, tn);
+  store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
 }
 
 }  // namespace sgemm

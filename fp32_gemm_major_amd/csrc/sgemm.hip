@@ -27,6 +27,8 @@ struct sgemm_handle_s {
   int cus;
   int variant;       // SGEMM_VARIANT_*
   int forced_kernel; // -1 = automatic
+  void* workspace;   // caller's device memory for stream-K partials, or null
+  size_t workspace_bytes;
 };
 
 namespace {
@@ -43,8 +45,16 @@ struct RunArgs {
   int ldc;
 };
 
+// What a launch needs besides the problem: the device's CU count and the
+// stream-K workspace.
+struct LaunchCtx {
+  int cus;
+  float* ws;
+  size_t ws_bytes;
+};
+
 typedef hipError_t (*launch_fn)(const RunArgs&, int tiles_m, int tiles_n,
-                                hipStream_t);
+                                const LaunchCtx&, hipStream_t);
 
 struct KernelDesc {
   const char* name;
@@ -54,24 +64,68 @@ struct KernelDesc {
   int bk;      // K values per LDS stage: K must be a multiple when aligned
   int threads;
   int mode;    // SGEMM_MODE_*: which problem sizes the kernel takes
+  int schedule;  // SGEMM_SCHEDULE_*: one tile per workgroup, or stream-K
+  int sk_per_cu;  // stream-K workgroups per CU (the grid is cus * sk_per_cu)
   float rel_rate;  // relative per-CU throughput, used by the tile choice
   launch_fn launch;
 };
 
+GemmArgs gemm_args(const RunArgs& a) {
+  GemmArgs g;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = a.K;
+  g.alpha = a.alpha;
+  g.beta = a.beta;
+  g.A = a.A;
+  g.lda = a.lda;
+  g.B = a.B;
+  g.ldb = a.ldb;
+  g.C = a.C;
+  g.ldc = a.ldc;
+  return g;
+}
+
 template <class T, int MODE, bool TA, bool TB>
 hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
-                       hipStream_t s) {
+                       const LaunchCtx&, hipStream_t s) {
   const int nwg = tiles_m * tiles_n;
   hipLaunchKernelGGL((mfma_sgemm_kernel<T, MODE, TA, TB>), dim3(nwg),
-                     dim3(T::THREADS), 0, s, a.M, a.N, a.K, a.alpha, a.A,
-                     a.lda, a.B, a.ldb, a.beta, a.C, a.ldc, tiles_m, tiles_n,
+                     dim3(T::THREADS), 0, s, gemm_args(a), tiles_m, tiles_n,
                      band_rows(tiles_m, nwg));
+  return hipGetLastError();
+}
+
+// Stream-K workgroups per CU for tile T (the grid is cus * this).
+template <class T>
+constexpr int sk_per_cu() {
+  return T::SK_PER_CU;
+}
+
+// Stream-K: the persistent kernel over the tiles x K-steps space, then the
+// fixup of the split tiles.  The host has checked the workspace size.
+template <class T, int MODE, bool TA, bool TB>
+hipError_t launch_mfma_sk(const RunArgs& a, int tiles_m, int tiles_n,
+                          const LaunchCtx& c, hipStream_t s) {
+  const int tiles = tiles_m * tiles_n;
+  const int grid = c.cus * sk_per_cu<T>();
+  const int band = band_rows(tiles_m, tiles);
+  const int steps = tile_k_steps<T>(a.K);
+  const GemmArgs g = gemm_args(a);
+  hipLaunchKernelGGL((mfma_sgemm_sk_kernel<T, MODE, TA, TB>), dim3(grid),
+                     dim3(T::THREADS), 0, s, g, tiles_m, tiles_n, band, steps,
+                     c.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_sgemm_fixup_kernel<T, MODE>), dim3(grid),
+                     dim3(T::THREADS), 0, s, g, tiles_m, tiles_n, band, steps,
+                     static_cast<const float*>(c.ws));
   return hipGetLastError();
 }
 
 template <class T, bool G>
 hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
-                       hipStream_t s) {
+                       const LaunchCtx&, hipStream_t s) {
   const int nwg = tiles_m * tiles_n;
   hipLaunchKernelGGL((valu_sgemm_kernel<T, G>), dim3(nwg), dim3(T::THREADS),
                      0, s, a.M, a.N, a.K, a.alpha, a.A, a.lda, a.B, a.ldb,
@@ -97,11 +151,18 @@ typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
 #define MFMA_ONE(T, TAG, TA, TB, MODE, rate)                                 \
   {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
-   T::THREADS, MODE, rate, launch_mfma<T, MODE, TA, TB>}
+   T::THREADS, MODE, SGEMM_SCHEDULE_TILES, sk_per_cu<T>(), rate,             \
+   launch_mfma<T, MODE, TA, TB>}
+#define MFMA_SK(T, TAG, TA, TB, MODE, rate)                                  \
+  {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
+   T::THREADS, MODE, SGEMM_SCHEDULE_STREAM_K, sk_per_cu<T>(), rate,          \
+   launch_mfma_sk<T, MODE, TA, TB>}
 #define MFMA_STORAGE(T, PRE, TA, TB, rate)                                   \
   MFMA_ONE(T, PRE "aligned", TA, TB, SGEMM_MODE_ALIGNED, rate),              \
   MFMA_ONE(T, PRE "edge", TA, TB, SGEMM_MODE_EDGE, rate),                    \
-  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED, rate)
+  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED, rate),              \
+  MFMA_SK(T, PRE "sk_aligned", TA, TB, SGEMM_MODE_ALIGNED, rate),            \
+  MFMA_SK(T, PRE "sk_edge", TA, TB, SGEMM_MODE_EDGE, rate)
 #define MFMA_SET(T, rate)                                                    \
   MFMA_STORAGE(T, "", false, false, rate),                                   \
   MFMA_STORAGE(T, "tn_", true, false, rate),                                 \
@@ -117,11 +178,11 @@ const KernelDesc kKernels[] = {
     MFMA_SET(M128x128, 0.991f),
     MFMA_SET(M64x64, 0.918f),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
-     V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_ALIGNED, 1.0f,
-     launch_valu<V128x128, false>},
+     V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_ALIGNED,
+     SGEMM_SCHEDULE_TILES, 1, 1.0f, launch_valu<V128x128, false>},
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
-     V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED, 1.0f,
-     launch_valu<V128x128, true>},
+     V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED,
+     SGEMM_SCHEDULE_TILES, 1, 1.0f, launch_valu<V128x128, true>},
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -144,8 +205,17 @@ bool offsets_fit(const KernelDesc& k, const RunArgs& a) {
 // Can kernel k run these arguments?  MFMA kernels read A and B with 16-byte
 // loads that need only 4-byte alignment; the VALU kernel's aligned instance
 // wants 16-byte aligned rows.
-bool kernel_fits(const KernelDesc& k, const RunArgs& a) {
+// Workspace a stream-K launch of kernel k uses: two partial tiles per
+// workgroup.
+size_t sk_workspace_bytes(const KernelDesc& k, int cus) {
+  return 2ull * (size_t)cus * k.sk_per_cu * k.bm * k.bn * sizeof(float);
+}
+
+bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
   if (k.ta != a.ta || k.tb != a.tb) return false;
+  if (k.schedule == SGEMM_SCHEDULE_STREAM_K &&
+      (a.K <= 0 || c.ws == nullptr || c.ws_bytes < sk_workspace_bytes(k, c.cus)))
+    return false;
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
       return true;
@@ -174,22 +244,41 @@ double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   return (double)per_cu * k.bm * k.bn / k.rel_rate;
 }
 
-// Aligned kernels of the variant and operand storage (the tile shapes).
-bool is_shape(const KernelDesc& k, int variant, const RunArgs& a) {
-  return k.variant == variant && k.mode == SGEMM_MODE_ALIGNED && k.ta == a.ta &&
-         k.tb == a.tb;
+// Seconds one output unit of the model costs on one CU: 2K flops at about
+// 0.55 TFLOP/s per CU.
+double unit_seconds(const RunArgs& a) { return 2.0 * a.K / 5.5e11; }
+
+// Modelled stream-K time, in the same units: the tiles spread evenly over the
+// CUs (no rounding up to whole rounds), at 97% of the shape's one-tile rate
+// (each workgroup runs several tile parts back to back), plus the fixup
+// launch (~4 us) and the partial tiles written and read back (two per
+// workgroup, at ~4 TB/s).
+double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
+  const double tiles = (double)ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
+  const double work = tiles / cus * k.bm * k.bn / (0.97 * k.rel_rate);
+  const double traffic_s = 2.0 * (double)sk_workspace_bytes(k, cus) / 4e12;
+  return work + (4e-6 + traffic_s) / unit_seconds(a);
 }
 
-// Instance of tile shape `shape` (an aligned kernel id) for these arguments:
-// the first of its aligned, edge and guarded instances that can run them.
-int instance_for(int shape, const RunArgs& a) {
+// Aligned one-tile-per-workgroup kernels of the variant and operand storage
+// (the tile shapes).
+bool is_shape(const KernelDesc& k, int variant, const RunArgs& a) {
+  return k.variant == variant && k.mode == SGEMM_MODE_ALIGNED &&
+         k.schedule == SGEMM_SCHEDULE_TILES && k.ta == a.ta && k.tb == a.tb;
+}
+
+// Instance of tile shape `shape` (an aligned kernel id) with this schedule
+// for these arguments: the first of its aligned, edge and guarded instances
+// that can run them.
+int instance_for(int shape, const RunArgs& a, const LaunchCtx& c,
+                 int schedule = SGEMM_SCHEDULE_TILES) {
   const KernelDesc& s = kKernels[shape];
   for (int mode = SGEMM_MODE_ALIGNED; mode <= SGEMM_MODE_GUARDED; ++mode) {
     for (int i = 0; i < kNumKernels; ++i) {
       const KernelDesc& k = kKernels[i];
-      if (k.mode == mode && k.variant == s.variant && k.ta == s.ta &&
-          k.tb == s.tb && k.bm == s.bm && k.bn == s.bn && k.bk == s.bk &&
-          k.threads == s.threads && kernel_fits(k, a))
+      if (k.mode == mode && k.schedule == schedule && k.variant == s.variant &&
+          k.ta == s.ta && k.tb == s.tb && k.bm == s.bm && k.bn == s.bn &&
+          k.bk == s.bk && k.threads == s.threads && kernel_fits(k, a, c))
         return i;
     }
   }
@@ -219,8 +308,10 @@ struct Plan {
 // empty, the columns can instead be split: the first launch covers whole
 // rounds of a large tile (a multiple of `cus` tiles) and the second the
 // remaining columns with any shape.  A second launch costs about 4 us, which
-// the model converts into output units at this K.
-int make_plan(int variant, const RunArgs& a, int cus, Plan* plan) {
+// the model converts into output units at this K.  With a workspace, a
+// stream-K launch of any shape is a third kind of plan.
+int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
+  const int cus = ctx.cus;
   if (variant == SGEMM_VARIANT_AUTO) variant = SGEMM_VARIANT_MFMA;
   if (variant != SGEMM_VARIANT_MFMA && variant != SGEMM_VARIANT_VALU)
     return SGEMM_ERR_VALUE;
@@ -236,11 +327,10 @@ int make_plan(int variant, const RunArgs& a, int cus, Plan* plan) {
   }
   if (best < 0) return SGEMM_ERR_UNSUPPORTED;  // e.g. VALU with transposes
   plan->count = 1;
-  plan->part[0] = Launch{instance_for(best, a), 0, a.N};
+  plan->part[0] = Launch{instance_for(best, a, ctx), 0, a.N};
   if (plan->part[0].kernel < 0) return plan->part[0].kernel;
   if (a.K <= 0 || a.M <= 0) return SGEMM_OK;
-  // time of one output unit ~ 2K flops at ~0.55 TFLOP/s per CU
-  const double second_launch = 4e-6 / (2.0 * a.K / 5.5e11);
+  const double second_launch = 4e-6 / unit_seconds(a);
   for (int i = 0; i < kNumKernels; ++i) {
     const KernelDesc& k1 = kKernels[i];
     if (!is_shape(k1, variant, a)) continue;
@@ -257,13 +347,27 @@ int make_plan(int variant, const RunArgs& a, int cus, Plan* plan) {
         if (!is_shape(k2, variant, a)) continue;
         const double c = c1 + tile_cost(k2, p2, cus) + second_launch;
         if (c < best_cost) {
-          const int i1 = instance_for(i, p1), i2 = instance_for(j, p2);
+          const int i1 = instance_for(i, p1, ctx), i2 = instance_for(j, p2, ctx);
           if (i1 < 0 || i2 < 0) continue;
           best_cost = c;
           plan->count = 2;
           plan->part[0] = Launch{i1, 0, n1};
           plan->part[1] = Launch{i2, n1, a.N - n1};
         }
+      }
+    }
+  }
+  if (ctx.ws != nullptr) {
+    for (int i = 0; i < kNumKernels; ++i) {
+      const KernelDesc& k = kKernels[i];
+      if (!is_shape(k, variant, a)) continue;
+      const double c = sk_cost(k, a, cus);
+      if (c < best_cost) {
+        const int id = instance_for(i, a, ctx, SGEMM_SCHEDULE_STREAM_K);
+        if (id < 0) continue;
+        best_cost = c;
+        plan->count = 1;
+        plan->part[0] = Launch{id, 0, a.N};
       }
     }
   }
@@ -283,6 +387,40 @@ Range window(const void* p, int rows, int cols, int ld) {
 }
 bool overlap(Range x, Range y) {
   return x.lo < x.hi && y.lo < y.hi && x.lo < y.hi && y.lo < x.hi;
+}
+
+LaunchCtx handle_ctx(const sgemm_handle_s* h) {
+  LaunchCtx c = {h->cus, static_cast<float*>(h->workspace), h->workspace_bytes};
+  return c;
+}
+
+// The plan sgemm_run_ex follows on handle h: the forced kernel, or the
+// cheapest plan for the handle's variant, CU count and workspace.
+int handle_plan(const sgemm_handle_s* h, const RunArgs& a, const LaunchCtx& ctx,
+                Plan* plan) {
+  if (h->forced_kernel >= 0) {
+    if (!kernel_fits(kKernels[h->forced_kernel], a, ctx)) return SGEMM_ERR_UNSUPPORTED;
+    plan->count = 1;
+    plan->part[0] = Launch{h->forced_kernel, 0, a.N};
+  } else {
+    const int ps = make_plan(h->variant, a, ctx, plan);
+    if (ps != SGEMM_OK) return ps;
+  }
+  for (int p = 0; p < plan->count; ++p) {
+    const KernelDesc& k = kKernels[plan->part[p].kernel];
+    if (ceil_div(a.M, k.bm) * ceil_div(plan->part[p].n, k.bn) > INT_MAX)
+      return SGEMM_ERR_UNSUPPORTED;
+  }
+  return SGEMM_OK;
+}
+
+int plan_out(const Plan& plan, int N, int* kernels, int* n_split) {
+  if (kernels) {
+    kernels[0] = plan.part[0].kernel;
+    kernels[1] = plan.count > 1 ? plan.part[1].kernel : -1;
+  }
+  if (n_split) *n_split = plan.count > 1 ? plan.part[1].n0 : N;
+  return plan.count;
 }
 
 }  // namespace
@@ -366,14 +504,53 @@ int sgemm_plan_ex(int variant, int transa, int transb, int M, int N, int K,
   const RunArgs a = {transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
                      const_cast<float*>(C), ldc};
   Plan plan;
-  const int st = make_plan(variant, a, kChipCus, &plan);
+  const LaunchCtx ctx = {kChipCus, nullptr, 0};
+  const int st = make_plan(variant, a, ctx, &plan);
   if (st != SGEMM_OK) return st;
-  if (kernels) {
-    kernels[0] = plan.part[0].kernel;
-    kernels[1] = plan.count > 1 ? plan.part[1].kernel : -1;
-  }
-  if (n_split) *n_split = plan.count > 1 ? plan.part[1].n0 : N;
-  return plan.count;
+  return plan_out(plan, N, kernels, n_split);
+}
+
+int sgemm_plan_handle(sgemm_handle_t h, int transa, int transb, int M, int N,
+                      int K, const float* A, int lda, const float* B, int ldb,
+                      const float* C, int ldc, int* kernels, int* n_split) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  const int st = sgemm_validate_ex(transa, transb, M, N, K, A, lda, B, ldb,
+                                   1.0f, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0) return 0;
+  const RunArgs a = {transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
+                     const_cast<float*>(C), ldc};
+  Plan plan;
+  const int ps = handle_plan(h, a, handle_ctx(h), &plan);
+  if (ps != SGEMM_OK) return ps;
+  return plan_out(plan, N, kernels, n_split);
+}
+
+int sgemm_kernel_schedule(int id) {
+  return (id >= 0 && id < kNumKernels) ? kKernels[id].schedule : SGEMM_ERR_VALUE;
+}
+
+int sgemm_workspace_size(sgemm_handle_t h, size_t* bytes) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  if (bytes == nullptr) return SGEMM_ERR_NULL;
+  size_t most = 0;
+  for (int i = 0; i < kNumKernels; ++i)
+    if (kKernels[i].schedule == SGEMM_SCHEDULE_STREAM_K) {
+      const size_t b = sk_workspace_bytes(kKernels[i], h->cus);
+      if (b > most) most = b;
+    }
+  *bytes = most;
+  return SGEMM_OK;
+}
+
+int sgemm_set_workspace(sgemm_handle_t h, void* workspace, size_t bytes) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  if (workspace == nullptr && bytes != 0) return SGEMM_ERR_NULL;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return SGEMM_ERR_VALUE;
+  h->workspace = bytes ? workspace : nullptr;
+  h->workspace_bytes = bytes;
+  return SGEMM_OK;
 }
 
 int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
@@ -423,6 +600,8 @@ int sgemm_create(sgemm_handle_t* out) {
   h->cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kChipCus;
   h->variant = SGEMM_VARIANT_AUTO;
   h->forced_kernel = -1;
+  h->workspace = nullptr;
+  h->workspace_bytes = 0;
   *out = h;
   return SGEMM_OK;
 }
@@ -458,20 +637,10 @@ int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
   if (M == 0 || N == 0) return SGEMM_OK;
   const RunArgs a = {transa, transb, M, N, K, alpha, beta, A, lda, B, ldb,
                      C, ldc};
+  const LaunchCtx ctx = handle_ctx(h);
   Plan plan;
-  if (h->forced_kernel >= 0) {
-    if (!kernel_fits(kKernels[h->forced_kernel], a)) return SGEMM_ERR_UNSUPPORTED;
-    plan.count = 1;
-    plan.part[0] = Launch{h->forced_kernel, 0, N};
-  } else {
-    const int ps = make_plan(h->variant, a, h->cus, &plan);
-    if (ps != SGEMM_OK) return ps;
-  }
-  for (int p = 0; p < plan.count; ++p) {
-    const KernelDesc& k = kKernels[plan.part[p].kernel];
-    if (ceil_div(M, k.bm) * ceil_div(plan.part[p].n, k.bn) > INT_MAX)
-      return SGEMM_ERR_UNSUPPORTED;
-  }
+  const int ps = handle_plan(h, a, ctx, &plan);
+  if (ps != SGEMM_OK) return ps;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return SGEMM_ERR_DEVICE;
@@ -479,7 +648,7 @@ int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
     const Launch& l = plan.part[p];
     const KernelDesc& k = kKernels[l.kernel];
     const RunArgs part = column_part(a, l.n0, l.n);
-    if (k.launch(part, (int)ceil_div(M, k.bm), (int)ceil_div(l.n, k.bn),
+    if (k.launch(part, (int)ceil_div(M, k.bm), (int)ceil_div(l.n, k.bn), ctx,
                  stream) != hipSuccess)
       return SGEMM_ERR_HIP;
   }

@@ -24,6 +24,19 @@ __host__ __device__ inline int band_rows(int tiles_m, int nwg) {
   return g;
 }
 
+// Tile `lin` of the band walk: bands of `band` tile rows, column-major
+// inside a band, so a contiguous run of `lin` is a compact block of C.
+__host__ __device__ inline void band_walk(int lin, int tiles_m, int tiles_n,
+                                          int band, int& tm, int& tn) {
+  const int per_band = band * tiles_n;
+  const int b = lin / per_band;
+  const int first = b * band;
+  const int rows = tiles_m - first < band ? tiles_m - first : band;
+  const int in = lin - b * per_band;
+  tm = first + in % rows;
+  tn = in / rows;
+}
+
 // Bijection from workgroup id `wg` in [0, nwg) to tile (tm, tn), with
 // nwg == tiles_m * tiles_n and band >= 1.
 __host__ __device__ inline void tile_coords(int wg, int nwg, int tiles_m,
@@ -33,14 +46,14 @@ __host__ __device__ inline void tile_coords(int wg, int nwg, int tiles_m,
   const int xcd = wg % kXcds, idx = wg / kXcds;
   // XCD x owns ids [start(x), start(x) + count(x)), count = q + (x < r).
   const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-  const int lin = start + idx;
-  const int per_band = band * tiles_n;
-  const int b = lin / per_band;
-  const int first = b * band;
-  const int rows = tiles_m - first < band ? tiles_m - first : band;
-  const int in = lin - b * per_band;
-  tm = first + in % rows;
-  tn = in / rows;
+  band_walk(start + idx, tiles_m, tiles_n, band, tm, tn);
+}
+
+// Workgroup position in a persistent grid of G (the stream-K kernels):
+// renumbered so that the workgroups of one XCD (ids x, x+8, ...) hold one
+// contiguous run of positions, and so one contiguous share of the work.
+__host__ __device__ inline int xcd_position(int wg, int G) {
+  return G % kXcds == 0 ? (wg % kXcds) * (G / kXcds) + wg / kXcds : wg;
 }
 
 }  // namespace sgemm

@@ -43,6 +43,7 @@
 #define SGEMM_H_
 
 #include <hip/hip_runtime_api.h> /* hipStream_t */
+#include <stddef.h>                /* size_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -101,6 +102,23 @@ enum sgemm_mode {
   SGEMM_MODE_GUARDED = 2
 };
 
+/* How a kernel spreads work over workgroups (sgemm_kernel_schedule).
+ *   TILES:    one output tile per workgroup, all of K.
+ *   STREAM_K: a grid of (CUs x a small count) workgroups that each take an
+ *             equal, contiguous share of the tiles x K-steps iteration space,
+ *             so a tile count that is not a multiple of the CU count leaves
+ *             no CU idle.  A tile split between workgroups is written as
+ *             partial sums to the handle's workspace (sgemm_set_workspace)
+ *             and a second kernel adds them in K order and applies alpha and
+ *             beta: the result is deterministic.  Chosen only when the
+ *             handle has a workspace of sgemm_workspace_size bytes (the
+ *             load-balancing schedule of the tiles-and-K-steps split; the
+ *             pages' "split-K" next step). */
+enum sgemm_schedule {
+  SGEMM_SCHEDULE_TILES = 0,
+  SGEMM_SCHEDULE_STREAM_K = 1
+};
+
 /* Create a handle bound to the current HIP device, which must be gfx950.
  * On success *out receives the handle.  Returns SGEMM_ERR_HANDLE if out is
  * NULL, SGEMM_ERR_DEVICE or SGEMM_ERR_HIP if the device cannot be used. */
@@ -123,8 +141,24 @@ int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
                  int K, float alpha, const float* A, int lda, const float* B,
                  int ldb, float beta, float* C, int ldc, hipStream_t stream);
 
-/* Free the handle.  NULL is a no-op returning SGEMM_OK. */
+/* Free the handle.  NULL is a no-op returning SGEMM_OK.  A workspace set on
+ * the handle stays the caller's to free. */
 int sgemm_destroy(sgemm_handle_t h);
+
+/* Device memory the stream-K kernels may use for partial tiles: `bytes` at
+ * `workspace` (16-byte aligned, on the handle's device, owned by the caller
+ * and kept alive while calls that may use it are in flight).  NULL with
+ * bytes 0 removes it.  Without a workspace of at least sgemm_workspace_size
+ * bytes no stream-K kernel is planned (a forced one returns
+ * SGEMM_ERR_UNSUPPORTED).  Calls on one handle share the workspace: calls
+ * that may overlap in time (different streams) need handles with separate
+ * workspaces.  SGEMM_ERR_NULL for NULL with bytes > 0, SGEMM_ERR_VALUE for a
+ * misaligned pointer. */
+int sgemm_set_workspace(sgemm_handle_t h, void* workspace, size_t bytes);
+
+/* Bytes of workspace that let every stream-K kernel run on the handle's
+ * device (two partial tiles per stream-K workgroup; 128 MiB on 256 CUs). */
+int sgemm_workspace_size(sgemm_handle_t h, size_t* bytes);
 
 /* ---- host-only helpers (no HIP call, no device needed) ---------------- */
 
@@ -162,10 +196,20 @@ int sgemm_kernel_info(int kernel_id, int* variant, int* bm, int* bn, int* bk,
 int sgemm_plan(int variant, int M, int N, int K, const float* A, int lda,
                const float* B, int ldb, const float* C, int ldc,
                int* kernels, int* n_split);
-/* sgemm_plan for sgemm_run_ex's operand storage. */
+/* sgemm_plan for sgemm_run_ex's operand storage.  sgemm_plan and
+ * sgemm_plan_ex plan for 256 CUs and no workspace (so never stream-K). */
 int sgemm_plan_ex(int variant, int transa, int transb, int M, int N, int K,
                   const float* A, int lda, const float* B, int ldb,
                   const float* C, int ldc, int* kernels, int* n_split);
+/* Exactly the plan sgemm_run_ex follows on handle h: its variant, forced
+ * kernel, CU count and workspace.  Returns the number of launches (0 when M
+ * or N is 0) or the status sgemm_run_ex would return; launches nothing. */
+int sgemm_plan_handle(sgemm_handle_t h, int transa, int transb, int M, int N,
+                      int K, const float* A, int lda, const float* B, int ldb,
+                      const float* C, int ldc, int* kernels, int* n_split);
+
+/* SGEMM_SCHEDULE_* of a kernel, or SGEMM_ERR_VALUE for a bad id. */
+int sgemm_kernel_schedule(int kernel_id);
 
 /* The kernel of sgemm_run's first launch for these arguments and variant
  * (SGEMM_VARIANT_*), or a negative status.  Pure function of its inputs. */

@@ -239,3 +239,35 @@ def test_huge_strides_go_to_the_guarded_instance():
     ldb = (1 << 28) + 3
     huge_b = sg.sgemm_kernel_info(sg.sgemm_select_kernel(0, M, N, K, A, K, B, ldb, C, N))
     assert huge_b["mode"] == sg.SGEMM_MODE_GUARDED
+
+
+def test_stream_k_instances_and_schedules():
+    """Every MFMA tile shape and storage has stream-K instances for the
+    aligned and edge modes; the host-only planners never pick them (they
+    plan without a workspace)."""
+    table = sg.kernel_table()
+    assert sg.library().sgemm_kernel_schedule(-1) == sg.SGEMM_ERR_VALUE
+    sk = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_STREAM_K]
+    assert sk and all(k["variant"] == sg.SGEMM_VARIANT_MFMA for k in sk)
+    assert all(k["mode"] in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE) for k in sk)
+    shapes = {(k["bm"], k["bn"], k["bk"]) for k in table if k["variant"] == sg.SGEMM_VARIANT_MFMA}
+    for shape in shapes:
+        got = {(k["transa"], k["transb"], k["mode"]) for k in sk
+               if (k["bm"], k["bn"], k["bk"]) == shape}
+        assert got == {(a, b, m) for a in (0, 1) for b in (0, 1)
+                       for m in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE)}, shape
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    for M, N, K in ((4100, 4100, 4100), (1000, 1500, 777)):
+        for kid, _, _ in sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N):
+            assert sg.sgemm_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_TILES
+
+
+def test_workspace_calls_without_a_device():
+    """Null-handle and argument errors of the workspace calls (no GPU)."""
+    lib = sg.library()
+    import ctypes
+    n = ctypes.c_size_t()
+    assert lib.sgemm_workspace_size(None, ctypes.byref(n)) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_set_workspace(None, None, 0) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_plan_handle(None, 0, 0, 8, 8, 8, None, 8, None, 8, None, 8,
+                                 None, None) == sg.SGEMM_ERR_HANDLE

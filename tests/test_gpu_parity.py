@@ -367,6 +367,64 @@ def test_misaligned_base_pointers(handle):
     gu.check_full(ops, out, exact=True, what="misaligned")
 
 
+@pytest.mark.parametrize("shape", [(16, 4096, 4096), (64, 4096, 4096), (100, 1000, 3000),
+                                   (256, 256, 16384), (512, 512, 8192)])
+def test_stream_k_plans(handle, shape):
+    """Few output tiles over a long K (skinny M, or a small C with a deep
+    contraction) leave most CUs idle with one tile per workgroup, so the
+    planner runs them stream-K when the handle has a workspace: integer
+    inputs, so the split-and-added tiles must still be bit-exact, and two
+    runs must agree bit for bit."""
+    M, N, K = shape
+    w = wl.Workload("sk", 6000 + M % 97 + N % 89, M, N, K, 1.5, 0.5, "int4")
+    ops = wl.operands(w)
+    A, B, C = gu.to_device(ops)
+    plan = handle.plan(M, N, K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                       C.data_ptr(), ops.ldc)
+    assert any(sg.sgemm_kernel_schedule(k) == sg.SGEMM_SCHEDULE_STREAM_K
+               for k, _, _ in plan), [sg.sgemm_kernel_name(k) for k, _, _ in plan]
+    out = gu.run(handle, ops, dev=(A, B, C))
+    gu.check_full(ops, out, exact=True, what=f"stream-K {shape}")
+    C.copy_(torch.from_numpy(ops.C).cuda())
+    again = gu.run(handle, ops, dev=(A, B, C))
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+
+
+def test_stream_k_uniform_values(handle):
+    """Uniform values through a stream-K plan on a ragged shape: within the
+    FP32 bound."""
+    w = wl.Workload("sku", 6101, 90, 2001, 3001, 1.0, 1.0, "uniform")
+    ops = wl.operands(w)
+    A, B, C = gu.to_device(ops)
+    plan = handle.plan(w.M, w.N, w.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                       C.data_ptr(), ops.ldc)
+    assert [sg.sgemm_kernel_schedule(k) for k, _, _ in plan] == [sg.SGEMM_SCHEDULE_STREAM_K]
+    gu.check_full(ops, gu.run(handle, ops, dev=(A, B, C)), what="stream-K uniform")
+
+
+def test_no_workspace_no_stream_k():
+    """Without a workspace no stream-K kernel is planned, and a forced one is
+    refused before anything is launched."""
+    h = sg.Handle(workspace=False)
+    try:
+        M, N, K = 1000, 1500, 777
+        A = torch.ones(M * K, device="cuda")
+        B = torch.ones(K * N, device="cuda")
+        C = torch.full((M * N,), 3.0, device="cuda")
+        plan = h.plan(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)
+        assert all(sg.sgemm_kernel_schedule(k) == sg.SGEMM_SCHEDULE_TILES for k, _, _ in plan)
+        sk = next(k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_STREAM_K
+                  and k["mode"] == sg.SGEMM_MODE_EDGE and not k["transa"] and not k["transb"])
+        h.set_kernel(sk["id"])
+        with pytest.raises(sg.SgemmError) as e:
+            h.gemm(A, B, C, 1.0, 1.0, M=M, N=N, K=K, lda=K, ldb=N, ldc=N)
+        assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+        assert torch.all(C == 3.0)
+    finally:
+        h.close()
+
+
 def test_deterministic(handle):
     ops = wl.operands(wl.Workload("det", 2, 1024, 1024, 1024, 1.0, 0.0, "uniform"))
     A, B, C = gu.to_device(ops)
