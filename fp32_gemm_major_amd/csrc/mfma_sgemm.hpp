@@ -77,7 +77,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2, int BK_ = 16,
-          int KG_ = 1>
+          int KG_ = 1, int PF_ = 0>
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
@@ -89,6 +89,12 @@ struct MfmaTile {
   // This multiplies the waves per tile for problems with few tiles without a
   // workspace or a second pass.
   static constexpr int KG = KG_;
+  // Fragment prefetch (two stages only): each wave reads the next K step's
+  // fragments from LDS into a second register set while its MFMAs run on
+  // the current step's, so after a barrier the MFMAs start at once instead
+  // of waiting for LDS reads.  Pays where a step is short (few MFMAs per
+  // wave between barriers) and the registers are there.
+  static constexpr bool PF = PF_ != 0;
   static constexpr int BKS = KG * BK;  // K values per LDS stage
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int WAVES_MN = WAVES_M * WAVES_N;  // waves of one K group
@@ -117,6 +123,7 @@ struct MfmaTile {
   static_assert(BK == 16 || BK == 32 || BK == 64, "K step");
   static_assert(BKS <= 64, "K-contiguous rows of at most 16 units");
   static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
+  static_assert(!PF || S == 2, "fragment prefetch uses two stages");
   // floats the K groups 1..KG-1 leave in LDS for group 0
   static constexpr int RED_ELEMS = (KG - 1) * WAVES_MN * 64 * 16 * FM * FN;
   static_assert(RED_ELEMS <= 2 * STAGE, "reduction fits in LDS");
@@ -348,44 +355,71 @@ __device__ __forceinline__ void tile_accumulate(
   constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
   auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  // MFMAs of one LDS stage.
-  auto compute = [&](int stage) {
+  // Fragments of four k (one per MFMA lane half) of LDS stage `stage`.  They
+  // are kept as separate floats, not 4-vectors: an outer-contiguous fragment
+  // is gathered by 4-byte reads that the compiler pairs, and a 4-vector would
+  // force register copies of the pairs (and waits for them) when two
+  // fragment sets alternate.
+  auto read_q = [&](int stage, int q, float (&a)[T::FM][4], float (&b)[T::FN][4]) {
     const float* As = lds + stage * T::STAGE;
     const float* Bs = As + T::A_ELEMS;
+    // lane half lh of K group kg covers k = kg*BK + lh*KH + 4q .. +3
+    const int kq = kg * T::BK + lh * T::KH + q * 4;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int m = wm * T::WM + i * 32 + li;
+      if (A_KC) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(As + kc_unit_off<T>(m, kq / 4));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[i][u] = v[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[i][u] = As[oc_elem_off<T, T::BM>(kq + u, m)];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int n = wn * T::WN + j * 32 + li;
+      if (B_KC) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(Bs + kc_unit_off<T>(n, kq / 4));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[j][u] = v[u];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) b[j][u] = Bs[oc_elem_off<T, T::BN>(kq + u, n)];
+      }
+    }
+  };
+  auto mma_q = [&](const float (&a)[T::FM][4], const float (&b)[T::FN][4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j][u], a[i][u],
+                                                          acc[i][j], 0, 0, 0);
+  };
+  // MFMAs of one LDS stage.
+  auto compute = [&](int stage) {
 #pragma unroll
     for (int q = 0; q < T::QN; ++q) {
-      // lane half lh of K group kg covers k = kg*BK + lh*KH + 4q .. +3
-      const int kq = kg * T::BK + lh * T::KH + q * 4;
-      f32x4 a[T::FM], b[T::FN];
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        const int m = wm * T::WM + i * 32 + li;
-        if (A_KC) {
-          a[i] = *reinterpret_cast<const f32x4*>(As + kc_unit_off<T>(m, kq / 4));
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) a[i][u] = As[oc_elem_off<T, T::BM>(kq + u, m)];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) {
-        const int n = wn * T::WN + j * 32 + li;
-        if (B_KC) {
-          b[j] = *reinterpret_cast<const f32x4*>(Bs + kc_unit_off<T>(n, kq / 4));
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) b[j][u] = Bs[oc_elem_off<T, T::BN>(kq + u, n)];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b[j][u], a[i][u],
-                                                            acc[i][j], 0, 0, 0);
+      float a[T::FM][4], b[T::FN][4];
+      read_q(stage, q, a, b);
+      mma_q(a, b);
     }
+  };
+  // A whole stage's fragments, for the prefetching loop.
+  struct Frags {
+    float a[T::QN][T::FM][4], b[T::QN][T::FN][4];
+  };
+  auto read_frags = [&](int stage, Frags& f) {
+#pragma unroll
+    for (int q = 0; q < T::QN; ++q) read_q(stage, q, f.a[q], f.b[q]);
+  };
+  auto mma_frags = [&](const Frags& f) {
+#pragma unroll
+    for (int q = 0; q < T::QN; ++q) mma_q(f.a[q], f.b[q]);
   };
 
 
@@ -420,6 +454,42 @@ __device__ __forceinline__ void tile_accumulate(
       if (more) store_regs(stage ^ 1);
       __syncthreads();
     }
+  } else if (T::PF) {
+    // Two stages and two register sets.  Step kt's fragments are read during
+    // step kt-1; step kt+2's direct loads go into step kt's stage as soon as
+    // the barrier after those reads has passed (the barrier also waits for
+    // the wave's LDS reads), and must have landed by the next barrier.
+    const int e = s1 < kd ? s1 : kd;  // direct-load steps [s0, e)
+    if (s0 < e) issue_dma(s0, 0);
+    if (s0 + 1 < e) issue_dma(s0 + 1, 1);
+    wait_all();
+    __syncthreads();
+    Frags f0, f1;
+    if (s0 < e) read_frags(0, f0);
+    // Every wave's reads of stage 0 must be done before the first step's
+    // direct loads overwrite it.
+    __syncthreads();
+    // One step: MFMAs on `cur` (stage `st`'s data), the next step's
+    // fragments into `nxt`, the step after next into stage `st`.  The
+    // scheduling barriers keep the MFMAs between the loads and the wait:
+    // MFMAs touch no memory, and the compiler would otherwise move most of
+    // them past the wait and the barrier, leaving the direct loads nothing
+    // to hide behind.
+    auto step = [&](int kt, int st, const Frags& cur, Frags& nxt) {
+      if (kt + 1 < e) read_frags(st ^ 1, nxt);
+      if (kt + 2 < e) issue_dma(kt + 2, st);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_frags(cur);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_all();
+      __syncthreads();
+    };
+    int kt = s0;
+    for (; kt + 1 < e; kt += 2) {
+      step(kt, 0, f0, f1);
+      step(kt + 1, 1, f1, f0);
+    }
+    if (kt < e) step(kt, 0, f0, f1);
   } else {
     const int e = s1 < kd ? s1 : kd;  // direct-load steps [s0, e)
     // Prologue: K steps s0 .. s0+NST-2 in flight, wait for step s0.
@@ -442,16 +512,16 @@ __device__ __forceinline__ void tile_accumulate(
       stage = stage + 1 == NST ? 0 : stage + 1;
       next = next + 1 == NST ? 0 : next + 1;
     }
-    // Edge kernels: the last step through registers, zero-filled past K,
-    // when it is partial or holds the last K row of a straddling operand.
-    // The stages are free after the loop's last barrier.
-    if (EDGE && kd * T::BKS < K && s0 <= kd && kd < s1) {
-      load_regs(kd);
-      store_regs(0);
-      __syncthreads();
-      compute(0);
-      if (T::KG > 1) __syncthreads();  // the K-group reduction reuses the LDS
-    }
+  }
+  // Edge kernels: the last step through registers, zero-filled past K, when
+  // it is partial or holds the last K row of a straddling operand.  The
+  // stages are free after the direct-load loop's last barrier.
+  if (EDGE && kd * T::BKS < K && s0 <= kd && kd < s1) {
+    load_regs(kd);
+    store_regs(0);
+    __syncthreads();
+    compute(0);
+    if (T::KG > 1) __syncthreads();  // the K-group reduction reuses the LDS
   }
 
   // K groups 1..KG-1 hand their partial sums to group 0 through LDS (the
