@@ -669,12 +669,15 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 
 // ---- stream-K ------------------------------------------------------------
 //
-// The tiles x K-steps iteration space (W = tiles * steps, tile-major) is cut
-// into G equal contiguous ranges, one per workgroup of a grid of G: the
-// workgroup at position h (xcd_position: one XCD's workgroups hold
-// consecutive positions) owns iterations [b(h), b(h+1)) with
-// b(h) = floor(h*W/G), and tile t is tile t of the band walk, so an XCD
-// works on a compact block of C.  It
+// A persistent grid of G workgroups.  Tiles [0, D) of the band walk (D a
+// multiple of G, from sk_dp_tiles) are whole-tile work: the workgroup at
+// position h (xcd_position: one XCD's workgroups hold consecutive
+// positions) computes tiles h, h+G, ... and stores them.  The iteration
+// space of the other tiles times their K steps (W = (tiles-D) * steps,
+// tile-major) is cut into G equal contiguous ranges: workgroup h owns
+// iterations [b(h), b(h+1)) with b(h) = floor(h*W/G), iteration i being
+// step i % steps of tile D + i / steps, so an XCD works on a compact block
+// of C in both parts.  It
 // walks them tile by tile; a tile it covers whole is stored at once, a part
 // of a tile is a partial sum written to the workspace.  A workgroup writes
 // at most two partials: slot 2h for a part that starts at b(h) (its first
@@ -687,6 +690,20 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 
 __host__ __device__ inline long long sk_bound(long long W, int G, int h) {
   return W * h / G;
+}
+
+// Whole tiles before the split ones.  Splitting only the last, partial
+// round keeps the partial sums few; when that round is so small that each
+// workgroup's share would be under a quarter of a tile's K steps (or two
+// steps), the round before it is split too.  No whole rounds: every tile
+// is split; no partial round: no tile is.
+__host__ __device__ inline int sk_dp_tiles(int tiles, int G, int steps) {
+  const int full = tiles / G, rem = tiles % G;
+  if (full == 0) return 0;
+  if (rem == 0) return tiles;
+  const int min_share = steps / 4 > 2 ? steps / 4 : 2;
+  if ((long long)rem * steps >= (long long)G * min_share) return full * G;
+  return (full - 1) * G;
 }
 
 template <class T>
@@ -707,82 +724,119 @@ __device__ __forceinline__ void store_partial(float* slot,
       }
 }
 
-template <class T>
-__device__ __forceinline__ void add_partial(const float* slot,
-                                            f32x16 (&acc)[T::FM][T::FN]) {
-  const WaveCoords<T> w;
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(
-            slot + (((w.wmn * T::FM + i) * T::FN + j) * 4 + q) * 256 + 4 * w.lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
-      }
-}
-
 template <class T, int MODE, bool TA, bool TB>
 __global__ void __launch_bounds__(T::THREADS, T::SK_OCC)
     mfma_sgemm_sk_kernel(GemmArgs g, int tiles_m, int tiles_n, int band,
-                         int steps, float* __restrict__ ws) {
+                         int steps, int dp, float* __restrict__ ws) {
   __shared__ __attribute__((aligned(1024))) float lds[TileLds<T, MODE>::FLOATS];
   const int tiles = tiles_m * tiles_n;
-  const long long W = (long long)tiles * steps;
+  const long long W = (long long)(tiles - dp) * steps;
   const int G = gridDim.x, h = xcd_position(blockIdx.x, gridDim.x);
   const long long b0 = sk_bound(W, G, h), b1 = sk_bound(W, G, h + 1);
   const bool first_group = threadIdx.x / 64 / T::WAVES_MN == 0;
-  for (long long i = b0; i < b1;) {
-    const int t = (int)(i / steps);
-    const long long ts = (long long)t * steps;
-    const int s0 = (int)(i - ts);
-    const int s1 = (int)(b1 - ts < steps ? b1 - ts : steps);
+  // One loop over this workgroup's work items (its whole tiles, then the
+  // parts of its range), so the K loop is inlined once.
+  int next_whole = h;
+  long long i = b0;
+  while (true) {
+    int t, s0, s1, slot = -1;  // slot < 0: the item covers its whole tile
+    if (next_whole < dp) {
+      t = next_whole;
+      s0 = 0;
+      s1 = steps;
+      next_whole += G;
+    } else if (i < b1) {
+      const int ti = (int)(i / steps);
+      const long long ts = (long long)ti * steps;
+      s0 = (int)(i - ts);
+      s1 = (int)(b1 - ts < steps ? b1 - ts : steps);
+      if (s0 != 0 || s1 != steps) slot = 2 * h + (i == b0 ? 0 : 1);
+      t = dp + ti;
+      i = ts + s1;
+    } else {
+      break;
+    }
     int tm, tn;
     band_walk(t, tiles_m, tiles_n, band, tm, tn);
     f32x16 acc[T::FM][T::FN];
     zero_acc<T>(acc);
     tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, s0, s1, acc);
     if (first_group) {
-      if (s0 == 0 && s1 == steps)
+      if (slot < 0)
         store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
       else
-        store_partial<T>(ws + (size_t)(2 * h + (i == b0 ? 0 : 1)) * (T::BM * T::BN), acc);
+        store_partial<T>(ws + (size_t)slot * (T::BM * T::BN), acc);
     }
-    __syncthreads();  // the next part reuses the LDS
-    i = ts + s1;
+    __syncthreads();  // the next item reuses the LDS
   }
 }
 
-// Workgroup h fixes the tile its range starts inside, when its range reaches
-// that tile's end (it is then the tile's last owner, so each split tile is
-// fixed exactly once).  The owners run from the one holding the tile's first
-// iteration, owner(i) = floor(((i+1)*G - 1) / W), up to h.
+// Elementwise fixup of the split tiles: each thread takes 16-byte pieces
+// (chunk c of a slot: the four floats at 4c) of split tiles, adds the
+// partials of that piece from every owner of the tile in K order, applies
+// alpha and beta and stores.  The owners of split tile u (iterations
+// [u*steps, (u+1)*steps)) run from owner(u*steps) to owner((u+1)*steps - 1),
+// owner(i) = floor(((i+1)*G - 1) / W); a tile with a single owner was stored
+// by it.  Owner o's part of the tile is in its first slot (2o) when o's
+// range starts inside the tile, else in its last (2o+1).
 template <class T, int MODE>
-__global__ void __launch_bounds__(T::THREADS, T::SK_OCC)
+__global__ void __launch_bounds__(256)
     mfma_sgemm_fixup_kernel(GemmArgs g, int tiles_m, int tiles_n, int band,
-                            int steps, const float* __restrict__ ws) {
+                            int steps, int dp, int G,
+                            const float* __restrict__ ws) {
+  constexpr int CHUNKS = T::BM * T::BN / 4;
+  constexpr bool EDGE = MODE == MODE_EDGE;
   const int tiles = tiles_m * tiles_n;
-  const long long W = (long long)tiles * steps;
-  const int G = gridDim.x, h = xcd_position(blockIdx.x, gridDim.x);
-  const long long b0 = sk_bound(W, G, h), b1 = sk_bound(W, G, h + 1);
-  if (b0 >= b1) return;
-  const int t = (int)(b0 / steps);
-  const long long ts = (long long)t * steps;
-  if (b0 == ts || b1 < ts + steps) return;
-  if (threadIdx.x / 64 / T::WAVES_MN != 0) return;  // first K group only
-  const int first = (int)(((ts + 1) * G - 1) / W);
-  f32x16 acc[T::FM][T::FN];
-  zero_acc<T>(acc);
-  for (int o = first; o <= h; ++o) {
-    const long long bo = sk_bound(W, G, o);
-    if (bo >= sk_bound(W, G, o + 1)) continue;  // empty range
-    add_partial<T>(ws + (size_t)(2 * o + (bo >= ts ? 0 : 1)) * (T::BM * T::BN), acc);
+  const long long W = (long long)(tiles - dp) * steps;
+  const long long total = (long long)(tiles - dp) * CHUNKS;
+  const int M = g.M, N = g.N, ldc = g.ldc;
+  const float alpha = g.alpha, beta = g.beta;
+  float* __restrict__ C = g.C;
+  const bool c_vec = (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+  for (long long x = (long long)blockIdx.x * 256 + threadIdx.x; x < total;
+       x += (long long)gridDim.x * 256) {
+    const int u = (int)(x / CHUNKS), c = (int)(x - (long long)u * CHUNKS);
+    const long long ts = (long long)u * steps;
+    const int first = (int)(((ts + 1) * G - 1) / W);
+    const int last = (int)(((ts + steps) * G - 1) / W);
+    if (first == last) continue;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int o = first; o <= last; ++o) {
+      const long long bo = sk_bound(W, G, o);
+      if (bo >= sk_bound(W, G, o + 1)) continue;  // empty range
+      acc += *reinterpret_cast<const f32x4*>(
+          ws + (size_t)(2 * o + (bo >= ts ? 0 : 1)) * (T::BM * T::BN) + 4 * c);
+    }
+    // chunk c = (((wmn * FM + i) * FN + j) * 4 + q) * 64 + lane: four
+    // consecutive columns of one row of the tile
+    const int lane = c & 63, q = (c >> 6) & 3;
+    const int j = (c >> 8) % T::FN, i = (c >> 8) / T::FN % T::FM;
+    const int wmn = (c >> 8) / (T::FN * T::FM);
+    int tm, tn;
+    band_walk(dp + u, tiles_m, tiles_n, band, tm, tn);
+    const int row = tm * T::BM + (wmn / T::WAVES_N) * T::WM + i * 32 + (lane & 31);
+    const int col = tn * T::BN + (wmn % T::WAVES_N) * T::WN + j * 32 + (lane >> 5) * 4 + 8 * q;
+    if (EDGE && row >= M) continue;
+    float* p = C + (size_t)row * ldc + col;
+    if (c_vec && (!EDGE || col + 3 < N)) {
+      f32x4 o;
+      const f32x4 cin = beta != 0.0f ? *reinterpret_cast<const f32x4*>(p) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = alpha * acc[e];
+        if (beta != 0.0f) o[e] = fmaf(beta, cin[e], o[e]);
+      }
+      *reinterpret_cast<f32x4*>(p) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (EDGE && col + e >= N) continue;
+        float o = alpha * acc[e];
+        if (beta != 0.0f) o = fmaf(beta, p[e], o);
+        p[e] = o;
+      }
+    }
   }
-  int tm, tn;
-  band_walk(t, tiles_m, tiles_n, band, tm, tn);
-  store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
 }
 
 }  // namespace sgemm

@@ -66,7 +66,6 @@ struct KernelDesc {
   int mode;    // SGEMM_MODE_*: which problem sizes the kernel takes
   int schedule;  // SGEMM_SCHEDULE_*: one tile per workgroup, or stream-K
   int sk_per_cu;  // stream-K workgroups per CU (the grid is cus * sk_per_cu)
-  float rel_rate;  // relative per-CU throughput, used by the tile choice
   launch_fn launch;
 };
 
@@ -111,15 +110,21 @@ hipError_t launch_mfma_sk(const RunArgs& a, int tiles_m, int tiles_n,
   const int grid = c.cus * sk_per_cu<T>();
   const int band = band_rows(tiles_m, tiles);
   const int steps = tile_k_steps<T>(a.K);
+  const int dp = sk_dp_tiles(tiles, grid, steps);
   const GemmArgs g = gemm_args(a);
   hipLaunchKernelGGL((mfma_sgemm_sk_kernel<T, MODE, TA, TB>), dim3(grid),
                      dim3(T::THREADS), 0, s, g, tiles_m, tiles_n, band, steps,
-                     c.ws);
+                     dp, c.ws);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mfma_sgemm_fixup_kernel<T, MODE>), dim3(grid),
-                     dim3(T::THREADS), 0, s, g, tiles_m, tiles_n, band, steps,
-                     static_cast<const float*>(c.ws));
+  if (e != hipSuccess || dp == tiles) return e;
+  // one 16-byte piece of a split tile per thread, up to 16 workgroups of
+  // 256 per CU (a grid-stride loop covers the rest)
+  const long long pieces = (long long)(tiles - dp) * (T::BM * T::BN / 4);
+  const long long want = (pieces + 255) / 256;
+  const int fix_grid = (int)(want < 16LL * c.cus ? want : 16LL * c.cus);
+  hipLaunchKernelGGL((mfma_sgemm_fixup_kernel<T, MODE>), dim3(fix_grid),
+                     dim3(256), 0, s, g, tiles_m, tiles_n, band, steps, dp,
+                     grid, static_cast<const float*>(c.ws));
   return hipGetLastError();
 }
 
@@ -152,40 +157,38 @@ typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
 typedef MfmaTile<64, 64, 32, 32, 8, 2, 16, 4, 1> M64x64;  // 16 waves
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
-#define MFMA_ONE(T, TAG, TA, TB, MODE, rate)                                 \
+#define MFMA_ONE(T, TAG, TA, TB, MODE)                                       \
   {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
-   T::THREADS, MODE, SGEMM_SCHEDULE_TILES, sk_per_cu<T>(), rate,             \
+   T::THREADS, MODE, SGEMM_SCHEDULE_TILES, sk_per_cu<T>(),                   \
    launch_mfma<T, MODE, TA, TB>}
-#define MFMA_SK(T, TAG, TA, TB, MODE, rate)                                  \
+#define MFMA_SK(T, TAG, TA, TB, MODE)                                        \
   {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
-   T::THREADS, MODE, SGEMM_SCHEDULE_STREAM_K, sk_per_cu<T>(), rate,          \
+   T::THREADS, MODE, SGEMM_SCHEDULE_STREAM_K, sk_per_cu<T>(),                \
    launch_mfma_sk<T, MODE, TA, TB>}
-#define MFMA_STORAGE(T, PRE, TA, TB, rate)                                   \
-  MFMA_ONE(T, PRE "aligned", TA, TB, SGEMM_MODE_ALIGNED, rate),              \
-  MFMA_ONE(T, PRE "edge", TA, TB, SGEMM_MODE_EDGE, rate),                    \
-  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED, rate),              \
-  MFMA_SK(T, PRE "sk_aligned", TA, TB, SGEMM_MODE_ALIGNED, rate),            \
-  MFMA_SK(T, PRE "sk_edge", TA, TB, SGEMM_MODE_EDGE, rate)
-#define MFMA_SET(T, rate)                                                    \
-  MFMA_STORAGE(T, "", false, false, rate),                                   \
-  MFMA_STORAGE(T, "tn_", true, false, rate),                                 \
-  MFMA_STORAGE(T, "nt_", false, true, rate),                                 \
-  MFMA_STORAGE(T, "tt_", true, true, rate)
+#define MFMA_STORAGE(T, PRE, TA, TB)                                         \
+  MFMA_ONE(T, PRE "aligned", TA, TB, SGEMM_MODE_ALIGNED),                    \
+  MFMA_ONE(T, PRE "edge", TA, TB, SGEMM_MODE_EDGE),                          \
+  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED),                    \
+  MFMA_SK(T, PRE "sk_aligned", TA, TB, SGEMM_MODE_ALIGNED),                  \
+  MFMA_SK(T, PRE "sk_edge", TA, TB, SGEMM_MODE_EDGE)
+#define MFMA_SET(T)                                                          \
+  MFMA_STORAGE(T, "", false, false),                                         \
+  MFMA_STORAGE(T, "tn_", true, false),                                       \
+  MFMA_STORAGE(T, "nt_", false, true),                                       \
+  MFMA_STORAGE(T, "tt_", true, true)
 
-// Relative rates: throughput of each shape on 4096^3 (a grid that fills the
-// chip for all of them), normalised to the best (MI355X, graph-replayed
-// launches: 937, 949, 946 and 1020 us).
+// Largest shape first: ties in the modelled time keep the larger tile.
 const KernelDesc kKernels[] = {
-    MFMA_SET(M256x256, 1.000f),
-    MFMA_SET(M256x128, 0.987f),
-    MFMA_SET(M128x128, 0.991f),
-    MFMA_SET(M64x64, 0.918f),
+    MFMA_SET(M256x256),
+    MFMA_SET(M256x128),
+    MFMA_SET(M128x128),
+    MFMA_SET(M64x64),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_ALIGNED,
-     SGEMM_SCHEDULE_TILES, 1, 1.0f, launch_valu<V128x128, false>},
+     SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, false>},
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED,
-     SGEMM_SCHEDULE_TILES, 1, 1.0f, launch_valu<V128x128, true>},
+     SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, true>},
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -237,30 +240,65 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-// Modelled time of a tile shape: the busiest CU runs ceil(tiles / cus)
-// tiles, each of bm*bn outputs, at the shape's relative per-CU rate (measured
-// on MI355X with the grid filling the chip; it folds in how well the shape's
-// occupancy hides latency).  Ties keep the earlier, larger shape.
-double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
-  const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
-  const long long per_cu = ceil_div(tiles, cus);
-  return (double)per_cu * k.bm * k.bn / k.rel_rate;
+// Launch-time model, in microseconds.  A CU holds up to R workgroups of a
+// shape at once; with c of them resident it finishes the c tiles of a
+// problem of depth K in about a[c-1]*K + b[c-1] us.  Fitted per shape from
+// MI355X runs at K = 512 and 2048 with exactly c tiles per CU (so b holds
+// the launch, the pipeline fill and the epilogue, and the rates hold how
+// well c workgroups hide each other's latency: one 4-wave 128x128 tile per
+// CU runs at 78% of peak, four at 91%).  The operand storages and the edge
+// instances run within a few percent of these.
+struct ShapeModel {
+  int bm, bn, resident;
+  double a[4], b[4];
+};
+const ShapeModel kModels[] = {
+    {256, 256, 1, {0.21732}, {43.23}},
+    {256, 128, 2, {0.11621, 0.22572}, {17.80, 23.73}},
+    {128, 128, 4, {0.063737, 0.11647, 0.17279, 0.22721}, {9.87, 13.57, 12.13, 15.97}},
+    {64, 64, 2, {0.015951, 0.028906}, {4.53, 6.80}},
+};
+
+// The kernel's model: its shape's, or for the VALU kernel one resident tile
+// at its measured 58% of peak.
+ShapeModel model_of(const KernelDesc& k) {
+  if (k.variant == SGEMM_VARIANT_MFMA)
+    for (const ShapeModel& m : kModels)
+      if (m.bm == k.bm && m.bn == k.bn) return m;
+  ShapeModel m = {k.bm, k.bn, 1, {2.0 * k.bm * k.bn / (157.3e6 / 256 * 0.58)}, {10.0}};
+  return m;
 }
 
-// Seconds one output unit of the model costs on one CU: 2K flops at about
-// 0.55 TFLOP/s per CU.
-double unit_seconds(const RunArgs& a) { return 2.0 * a.K / 5.5e11; }
+constexpr double kSecondLaunchUs = 3.0;
 
-// Modelled stream-K time, in the same units: the tiles spread evenly over the
-// CUs (no rounding up to whole rounds), at 97% of the shape's one-tile rate
-// (each workgroup runs several tile parts back to back), plus the fixup
-// launch (~4 us) and the partial tiles written and read back (two per
-// workgroup, at ~4 TB/s).
+// One-tile-per-workgroup launch: the busiest CU runs t = ceil(tiles / cus)
+// tiles, R at a time, then the t mod R left over together.
+double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
+  const ShapeModel m = model_of(k);
+  const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
+  const long long t = ceil_div(tiles, cus);
+  const long long rounds = t / m.resident, rest = t % m.resident;
+  double us = (double)rounds * (m.a[m.resident - 1] * a.K + m.b[m.resident - 1]);
+  if (rest > 0) us += m.a[rest - 1] * a.K + m.b[rest - 1];
+  return us;
+}
+
+// Stream-K launch: the work spread evenly over the CUs, sk_per_cu
+// workgroups at a time, 2% slower than the same tiles launched one per
+// workgroup (a persistent workgroup runs its tiles' fills and epilogues in
+// series), plus (when tiles are split) ~5 us for the fixup and the partial
+// tiles written and read back at ~5 TB/s: about one per split tile and one
+// per workgroup.
 double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
-  const double tiles = (double)ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
-  const double work = tiles / cus * k.bm * k.bn / (0.97 * k.rel_rate);
-  const double traffic_s = 2.0 * (double)sk_workspace_bytes(k, cus) / 4e12;
-  return work + (4e-6 + traffic_s) / unit_seconds(a);
+  const ShapeModel m = model_of(k);
+  const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
+  const int c = k.sk_per_cu < m.resident ? k.sk_per_cu : m.resident;
+  const int G = cus * k.sk_per_cu;
+  double us = 1.02 * (double)tiles / cus / c * (m.a[c - 1] * a.K + m.b[c - 1]);
+  const int steps = (int)ceil_div(a.K, k.bk);
+  const long long split = tiles - sk_dp_tiles((int)tiles, G, steps);
+  if (split > 0) us += 5.0 + 2.0 * (double)(split + G) * k.bm * k.bn * 4 / 5e12 * 1e6;
+  return us;
 }
 
 // Aligned one-tile-per-workgroup kernels of the variant and operand storage
@@ -306,13 +344,13 @@ struct Plan {
   Launch part[2];
 };
 
-// Pick the launch plan with the lowest modelled cost.  A single launch uses
+// Pick the launch plan with the lowest modelled time.  A single launch uses
 // the best tile shape.  When that leaves the last round of workgroups part
 // empty, the columns can instead be split: the first launch covers whole
 // rounds of a large tile (a multiple of `cus` tiles) and the second the
-// remaining columns with any shape.  A second launch costs about 4 us, which
-// the model converts into output units at this K.  With a workspace, a
-// stream-K launch of any shape is a third kind of plan.
+// remaining columns with any shape (each launch pays its own fixed time in
+// the model).  With a workspace, a stream-K launch of any shape is a third
+// kind of plan.
 int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
   const int cus = ctx.cus;
   if (variant == SGEMM_VARIANT_AUTO) variant = SGEMM_VARIANT_MFMA;
@@ -333,7 +371,6 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
   plan->part[0] = Launch{instance_for(best, a, ctx), 0, a.N};
   if (plan->part[0].kernel < 0) return plan->part[0].kernel;
   if (a.K <= 0 || a.M <= 0) return SGEMM_OK;
-  const double second_launch = 4e-6 / unit_seconds(a);
   for (int i = 0; i < kNumKernels; ++i) {
     const KernelDesc& k1 = kKernels[i];
     if (!is_shape(k1, variant, a)) continue;
@@ -348,7 +385,8 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
       for (int j = 0; j < kNumKernels; ++j) {
         const KernelDesc& k2 = kKernels[j];
         if (!is_shape(k2, variant, a)) continue;
-        const double c = c1 + tile_cost(k2, p2, cus) + second_launch;
+        // a second launch must win by more than the model's error
+        const double c = (c1 + tile_cost(k2, p2, cus)) * 1.01 + kSecondLaunchUs;
         if (c < best_cost) {
           const int i1 = instance_for(i, p1, ctx), i2 = instance_for(j, p2, ctx);
           if (i1 < 0 || i2 < 0) continue;

@@ -271,3 +271,18 @@ def test_workspace_calls_without_a_device():
     assert lib.sgemm_set_workspace(None, None, 0) == sg.SGEMM_ERR_HANDLE
     assert lib.sgemm_plan_handle(None, 0, 0, 8, 8, 8, None, 8, None, 8, None, 8,
                                  None, None) == sg.SGEMM_ERR_HANDLE
+
+
+def test_plans_follow_measured_winners():
+    """Shapes where the launch-time model must pick what measured fastest on
+    MI355X: one 128x128 tile per CU leaves too few waves resident, so 2048^3
+    and 4096 x 1024 x 4096 go to 64x64 tiles; an exact number of 128x128
+    rounds stays one launch."""
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    name = lambda M, N, K: [sg.sgemm_kernel_name(k) for k, _, _ in
+                            sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N)]
+    assert name(2048, 2048, 2048) == ["mfma_M64x64_aligned"]
+    assert name(4096, 1024, 4096) == ["mfma_M64x64_aligned"]
+    assert name(6144, 6144, 2048) == ["mfma_M128x128_aligned"]
+    assert name(4096, 2048, 2048) == ["mfma_M128x128_aligned"]
+    assert name(4096, 4096, 4096) == ["mfma_M256x256_aligned"]

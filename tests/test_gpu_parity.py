@@ -156,8 +156,8 @@ def test_transposed_edges_integer(handle, ta, tb):
 
 @pytest.mark.parametrize("ta,tb", OPS, ids=["nt", "tn", "tt"])
 def test_transposed_4096_split_plan(handle, ta, tb):
-    """4096 x 11008 x 512 runs as two column launches; op(B) = B^T offsets B by rows."""
-    w = wl.Workload("trans", 6002, 4096, 11008, 512, 1.0, 0.0, "normal", "nan")
+    """4096 x 4352 x 512 runs as two column launches; op(B) = B^T offsets B by rows."""
+    w = wl.Workload("trans", 6002, 4096, 4352, 512, 1.0, 0.0, "normal", "nan")
     ops = wl.operands(w, ta=ta, tb=tb)
     plan = sg.sgemm_plan(0, w.M, w.N, w.K, 0x10000000, ops.lda, 0x20000000, ops.ldb,
                          0x40000000, ops.ldc, transa=int(ta), transb=int(tb))
