@@ -232,6 +232,12 @@ __device__ __forceinline__ void tile_accumulate(
   const int wmn = wave % T::WAVES_MN;
   const int wm = wmn / T::WAVES_N, wn = wmn % T::WAVES_N;
   const int li = lane & 31, lh = lane >> 5;
+  // LDS: the A tiles of all stages, then the B tiles, so that a stage's
+  // offset from the first stage of its operand stays below 64 KiB and can
+  // ride in a read's immediate offset when the stage is known at compile
+  // time (the loops below are unrolled by stage).
+  auto a_stage_off = [](int stage) { return stage * T::A_ELEMS; };
+  auto b_stage_off = [](int stage) { return NST * T::A_ELEMS + stage * T::B_ELEMS; };
 
   // Tile coordinates of the units this lane moves.
   int a_o[T::A_VEC], a_k[T::A_VEC], b_o[T::B_VEC], b_k[T::B_VEC];
@@ -285,13 +291,13 @@ __device__ __forceinline__ void tile_accumulate(
 
   // Direct load d of K step kt (the A units first, then the B units).
   auto issue_one = [&](int d, int kt, int stage) {
-    const unsigned st = lds_u + 4u * (unsigned)(stage * T::STAGE);
     if (d < T::A_VEC)
       dma16(a_base + (size_t)kt * a_step, a_voff[d],
-            st + 1024u * (unsigned)(d * T::WAVES + wave_u));
+            lds_u + 4u * (unsigned)a_stage_off(stage) +
+                1024u * (unsigned)(d * T::WAVES + wave_u));
     else
       dma16(b_base + (size_t)kt * b_step, b_voff[d - T::A_VEC],
-            st + 4u * T::A_ELEMS +
+            lds_u + 4u * (unsigned)b_stage_off(stage) +
                 1024u * (unsigned)((d - T::A_VEC) * T::WAVES + wave_u));
   };
   auto issue_dma = [&](int kt, int stage) {
@@ -338,13 +344,13 @@ __device__ __forceinline__ void tile_accumulate(
                         k0 + b_k[v]);
   };
   auto store_regs = [&](int stage) {
-    float* st = lds + stage * T::STAGE;
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v)
-      *reinterpret_cast<f32x4*>(st + 256 * (v * T::WAVES + wave) + 4 * lane) = ra[v];
+      *reinterpret_cast<f32x4*>(lds + a_stage_off(stage) + 256 * (v * T::WAVES + wave) +
+                                4 * lane) = ra[v];
 #pragma unroll
     for (int v = 0; v < T::B_VEC; ++v)
-      *reinterpret_cast<f32x4*>(st + T::A_ELEMS + 256 * (v * T::WAVES + wave) +
+      *reinterpret_cast<f32x4*>(lds + b_stage_off(stage) + 256 * (v * T::WAVES + wave) +
                                 4 * lane) = rb[v];
   };
 
@@ -361,8 +367,8 @@ __device__ __forceinline__ void tile_accumulate(
   // force register copies of the pairs (and waits for them) when two
   // fragment sets alternate.
   auto read_q = [&](int stage, int q, float (&a)[T::FM][4], float (&b)[T::FN][4]) {
-    const float* As = lds + stage * T::STAGE;
-    const float* Bs = As + T::A_ELEMS;
+    const float* As = lds + a_stage_off(stage);
+    const float* Bs = lds + b_stage_off(stage);
     // lane half lh of K group kg covers k = kg*BK + lh*KH + 4q .. +3
     const int kq = kg * T::BK + lh * T::KH + q * 4;
 #pragma unroll
@@ -499,18 +505,31 @@ __device__ __forceinline__ void tile_accumulate(
     if (e - s0 >= NST - 1) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
     else wait_all();
     __syncthreads();
-    int stage = 0, next = NST - 1;  // next = stage that receives step kt+NST-1
-    for (int kt = s0; kt < e; ++kt) {
-      // next's previous contents (step kt-1) were read before the last barrier
+    // One K step from `stage`, loading step kt+NST-1 into `next`, whose
+    // previous contents (step kt-1) were read before the last barrier; step
+    // kt+1 must be in LDS at the barrier, later ones may still be in flight.
+    auto step = [&](int kt, int stage, int next) {
       const bool issue = kt + NST - 1 < e;
       if (issue) issue_dma(kt + NST - 1, next);
       compute(stage);
-      // step kt+1 must be in LDS: steps kt+2 .. kt+NST-1 may still be in flight
       if (issue) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
       else wait_all();
       __syncthreads();
-      stage = stage + 1 == NST ? 0 : stage + 1;
-      next = next + 1 == NST ? 0 : next + 1;
+    };
+    if (NST == 2) {
+      int kt = s0;
+      for (; kt + 1 < e; kt += 2) {
+        step(kt, 0, 1);
+        step(kt + 1, 1, 0);
+      }
+      if (kt < e) step(kt, 0, 1);
+    } else {
+      int stage = 0, next = NST - 1;
+      for (int kt = s0; kt < e; ++kt) {
+        step(kt, stage, next);
+        stage = stage + 1 == NST ? 0 : stage + 1;
+        next = next + 1 == NST ? 0 : next + 1;
+      }
     }
   }
   // Edge kernels: the last step through registers, zero-filled past K, when

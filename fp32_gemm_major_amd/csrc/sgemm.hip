@@ -165,24 +165,29 @@ typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
   {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
    T::THREADS, MODE, SGEMM_SCHEDULE_STREAM_K, sk_per_cu<T>(),                \
    launch_mfma_sk<T, MODE, TA, TB>}
-#define MFMA_STORAGE(T, PRE, TA, TB)                                         \
+#define MFMA_TILES(T, PRE, TA, TB)                                           \
   MFMA_ONE(T, PRE "aligned", TA, TB, SGEMM_MODE_ALIGNED),                    \
   MFMA_ONE(T, PRE "edge", TA, TB, SGEMM_MODE_EDGE),                          \
-  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED),                    \
+  MFMA_ONE(T, PRE "guarded", TA, TB, SGEMM_MODE_GUARDED)
+#define MFMA_STORAGE(T, PRE, TA, TB)                                         \
+  MFMA_TILES(T, PRE, TA, TB),                                                \
   MFMA_SK(T, PRE "sk_aligned", TA, TB, SGEMM_MODE_ALIGNED),                  \
   MFMA_SK(T, PRE "sk_edge", TA, TB, SGEMM_MODE_EDGE)
-#define MFMA_SET(T)                                                          \
-  MFMA_STORAGE(T, "", false, false),                                         \
-  MFMA_STORAGE(T, "tn_", true, false),                                       \
-  MFMA_STORAGE(T, "nt_", false, true),                                       \
-  MFMA_STORAGE(T, "tt_", true, true)
+#define MFMA_SET(T, STORAGE)                                                 \
+  STORAGE(T, "", false, false),                                              \
+  STORAGE(T, "tn_", true, false),                                            \
+  STORAGE(T, "nt_", false, true),                                            \
+  STORAGE(T, "tt_", true, true)
 
-// Largest shape first: ties in the modelled time keep the larger tile.
+// Largest shape first: ties in the modelled time keep the larger tile.  The
+// 256x256 tile has no stream-K instances: with 128 accumulator registers per
+// lane its stream-K kernel does not fit the register file, and it never
+// measured fastest (the 128x128 and 64x64 stream-K kernels cover its cases).
 const KernelDesc kKernels[] = {
-    MFMA_SET(M256x256),
-    MFMA_SET(M256x128),
-    MFMA_SET(M128x128),
-    MFMA_SET(M64x64),
+    MFMA_SET(M256x256, MFMA_TILES),
+    MFMA_SET(M256x128, MFMA_STORAGE),
+    MFMA_SET(M128x128, MFMA_STORAGE),
+    MFMA_SET(M64x64, MFMA_STORAGE),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_ALIGNED,
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, false>},
@@ -241,22 +246,28 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 // Launch-time model, in microseconds.  A CU holds up to R workgroups of a
-// shape at once; with c of them resident it finishes the c tiles of a
-// problem of depth K in about a[c-1]*K + b[c-1] us.  Fitted per shape from
-// MI355X runs at K = 512 and 2048 with exactly c tiles per CU (so b holds
-// the launch, the pipeline fill and the epilogue, and the rates hold how
-// well c workgroups hide each other's latency: one 4-wave 128x128 tile per
-// CU runs at 78% of peak, four at 91%).  The operand storages and the edge
-// instances run within a few percent of these.
+// shape at once.  The first round, with c <= R of them resident, takes
+// a[c-1]*K + b[c-1] us, fitted per shape from MI355X runs at K = 512 and 2048
+// with exactly c tiles per CU (so b holds the launch, the pipeline fill and
+// the epilogue, and the rates hold how well c workgroups hide each other's
+// latency: at K = 2048 one 4-wave 128x128 tile per CU runs at 85% of peak,
+// four at 93%).  Every further round of R tiles per CU takes as*K + bs, fitted
+// from the difference between 8192x8192 (or 4096x8192) and 4096x4096 at
+// K = 1024 and 4096: rounds after the first run at a steadier rate, higher
+// than the first for the 256x128 and 64x64 tiles and lower for 128x128
+// (e.g. 256x128 over 8192x8192x4096 at 96% of peak).  The operand storages
+// and the edge instances run within a few percent of these.
 struct ShapeModel {
   int bm, bn, resident;
-  double a[4], b[4];
+  double a[4], b[4];  // first round with c resident
+  double as, bs;      // each further round
 };
 const ShapeModel kModels[] = {
-    {256, 256, 1, {0.21732}, {43.23}},
-    {256, 128, 2, {0.11621, 0.22572}, {17.80, 23.73}},
-    {128, 128, 4, {0.063737, 0.11647, 0.17279, 0.22721}, {9.87, 13.57, 12.13, 15.97}},
-    {64, 64, 2, {0.015951, 0.028906}, {4.53, 6.80}},
+    {256, 256, 1, {0.215192}, {45.04}, 0.22295, 15.9},
+    {256, 128, 2, {0.117583, 0.216994}, {18.26, 28.46}, 0.21732, 13.1},
+    {128, 128, 4, {0.058030, 0.111957, 0.164966, 0.220629}, {9.41, 11.61, 15.98, 17.97},
+     0.23415, 3.8},
+    {64, 64, 2, {0.016331, 0.029669}, {3.96, 6.24}, 0.028646, 4.67},
 };
 
 // The kernel's model: its shape's, or for the VALU kernel one resident tile
@@ -265,25 +276,31 @@ ShapeModel model_of(const KernelDesc& k) {
   if (k.variant == SGEMM_VARIANT_MFMA)
     for (const ShapeModel& m : kModels)
       if (m.bm == k.bm && m.bn == k.bn) return m;
-  ShapeModel m = {k.bm, k.bn, 1, {2.0 * k.bm * k.bn / (157.3e6 / 256 * 0.58)}, {10.0}};
+  const double a = 2.0 * k.bm * k.bn / (157.3e6 / 256 * 0.58);
+  ShapeModel m = {k.bm, k.bn, 1, {a}, {10.0}, a, 2.0};
   return m;
 }
 
 constexpr double kSecondLaunchUs = 3.0;
 
-// One-tile-per-workgroup launch: the busiest CU runs t = ceil(tiles / cus)
-// tiles, R at a time, then the t mod R left over together.
-double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
-  const ShapeModel m = model_of(k);
-  const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
-  const long long t = ceil_div(tiles, cus);
-  const long long rounds = t / m.resident, rest = t % m.resident;
-  double us = (double)rounds * (m.a[m.resident - 1] * a.K + m.b[m.resident - 1]);
-  if (rest > 0) us += m.a[rest - 1] * a.K + m.b[rest - 1];
+// c tiles per CU run together, then `more` further tiles per CU in rounds of
+// R (a partial last round costs its share of a round).
+double rounds_us(const ShapeModel& m, int c, double more, int K) {
+  double us = m.a[c - 1] * K + m.b[c - 1];
+  if (more > 0) us += more / m.resident * (m.as * K + m.bs);
   return us;
 }
 
-// Stream-K launch: the work spread evenly over the CUs, sk_per_cu
+// One-tile-per-workgroup launch: the busiest CU runs t = ceil(tiles / cus)
+// tiles.
+double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
+  const ShapeModel m = model_of(k);
+  const long long t = ceil_div(ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn), cus);
+  const int c = t < m.resident ? (int)t : m.resident;
+  return rounds_us(m, c, (double)(t - c), a.K);
+}
+
+// Stream-K launch: the tiles spread evenly over the CUs (w per CU), sk_per_cu
 // workgroups at a time, 2% slower than the same tiles launched one per
 // workgroup (a persistent workgroup runs its tiles' fills and epilogues in
 // series), plus (when tiles are split) ~5 us for the fixup and the partial
@@ -293,8 +310,11 @@ double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   const ShapeModel m = model_of(k);
   const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
   const int c = k.sk_per_cu < m.resident ? k.sk_per_cu : m.resident;
+  const double w = (double)tiles / cus;
+  double us = w <= c ? w / c * (m.a[c - 1] * a.K + m.b[c - 1])
+                     : rounds_us(m, c, w - c, a.K);
+  us *= 1.02;
   const int G = cus * k.sk_per_cu;
-  double us = 1.02 * (double)tiles / cus / c * (m.a[c - 1] * a.K + m.b[c - 1]);
   const int steps = (int)ceil_div(a.K, k.bk);
   const long long split = tiles - sk_dp_tiles((int)tiles, G, steps);
   if (split > 0) us += 5.0 + 2.0 * (double)(split + G) * k.bm * k.bn * 4 / 5e12 * 1e6;

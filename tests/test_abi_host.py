@@ -158,13 +158,14 @@ def test_select_kernel():
         k = sg.sgemm_kernel_info(sel(variant, 1024, 1024, 1024, A + 4, 1024, B, 1024, C, 1024))
         assert k["mode"] == (sg.SGEMM_MODE_ALIGNED if mfma else sg.SGEMM_MODE_GUARDED)
     assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
-    # tile shapes the cost model picks for the measured workloads: 4096^3 on one
-    # 256 x 256 tile per CU, and the problems that would leave CUs idle on
-    # 64 x 64 (4096 x 11008 is covered by the launch-plan test)
+    # tile shapes the cost model picks for the measured workloads: 4096^3 on a
+    # large tile filling whole rounds, and the problems that would leave CUs
+    # idle on 64 x 64 (4096 x 11008 is covered by the launch-plan test)
     def shape(M, N, K):
         k = sg.sgemm_kernel_info(sel(0, M, N, K, A, K, B, N, C, N))
         return k["bm"], k["bn"]
-    assert shape(4096, 4096, 4096) == (256, 256)
+    bm, bn = shape(4096, 4096, 4096)
+    assert bm * bn >= 128 * 128 and (4096 // bm) * (4096 // bn) % 256 == 0
     assert shape(1024, 1024, 1024) == (64, 64)
     assert shape(128, 128, 128) == (64, 64)
     assert shape(1000, 1500, 777) == (64, 64)
@@ -173,7 +174,7 @@ def test_select_kernel():
 def test_plan_splits_only_when_rounds_are_ragged():
     A, B, C = 0x10000000, 0x20000000, 0x40000000
     plan = lambda M, N, K: sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N)
-    # 4096^3 on 256 x 256 tiles is exactly one round: one launch
+    # 4096^3 fills whole rounds of any tile: one launch
     assert len(plan(4096, 4096, 4096)) == 1
     for M, N, K in [(128, 128, 128), (1024, 1024, 1024), (1000, 1500, 777)]:
         assert len(plan(M, N, K)) == 1
@@ -242,16 +243,18 @@ def test_huge_strides_go_to_the_guarded_instance():
 
 
 def test_stream_k_instances_and_schedules():
-    """Every MFMA tile shape and storage has stream-K instances for the
-    aligned and edge modes; the host-only planners never pick them (they
-    plan without a workspace)."""
+    """Every MFMA tile shape but 256x256 (whose stream-K kernel would not fit
+    its registers) has stream-K instances for every storage in the aligned
+    and edge modes; the host-only planners never pick them (they plan
+    without a workspace)."""
     table = sg.kernel_table()
     assert sg.library().sgemm_kernel_schedule(-1) == sg.SGEMM_ERR_VALUE
     sk = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_STREAM_K]
     assert sk and all(k["variant"] == sg.SGEMM_VARIANT_MFMA for k in sk)
     assert all(k["mode"] in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE) for k in sk)
     shapes = {(k["bm"], k["bn"], k["bk"]) for k in table if k["variant"] == sg.SGEMM_VARIANT_MFMA}
-    for shape in shapes:
+    assert not any((k["bm"], k["bn"]) == (256, 256) for k in sk)
+    for shape in (s for s in shapes if s[:2] != (256, 256)):
         got = {(k["transa"], k["transb"], k["mode"]) for k in sk
                if (k["bm"], k["bn"], k["bk"]) == shape}
         assert got == {(a, b, m) for a in (0, 1) for b in (0, 1)
@@ -275,14 +278,13 @@ def test_workspace_calls_without_a_device():
 
 def test_plans_follow_measured_winners():
     """Shapes where the launch-time model must pick what measured fastest on
-    MI355X: one 128x128 tile per CU leaves too few waves resident, so 2048^3
-    and 4096 x 1024 x 4096 go to 64x64 tiles; an exact number of 128x128
-    rounds stays one launch."""
+    MI355X: 4096 x 11008 x 4096 as five rounds of 256x128 then 64x64 tiles
+    (2461 us, against 2620 for one 128x128 launch), 8192^2 x 4096 on 256x128
+    (96% of peak), the small and ragged workloads on 64x64."""
     A, B, C = 0x10000000, 0x20000000, 0x40000000
     name = lambda M, N, K: [sg.sgemm_kernel_name(k) for k, _, _ in
                             sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N)]
-    assert name(2048, 2048, 2048) == ["mfma_M64x64_aligned"]
-    assert name(4096, 1024, 4096) == ["mfma_M64x64_aligned"]
-    assert name(6144, 6144, 2048) == ["mfma_M128x128_aligned"]
-    assert name(4096, 2048, 2048) == ["mfma_M128x128_aligned"]
-    assert name(4096, 4096, 4096) == ["mfma_M256x256_aligned"]
+    assert name(4096, 11008, 4096) == ["mfma_M256x128_aligned", "mfma_M64x64_aligned"]
+    assert name(8192, 8192, 4096) == ["mfma_M256x128_aligned"]
+    assert name(1024, 1024, 1024) == ["mfma_M64x64_aligned"]
+    assert name(3000, 3000, 3000) == ["mfma_M64x64_edge"]
