@@ -37,7 +37,7 @@ def test_cpu_baseline_fields():
 
 
 def test_kernel_source_hash_and_traffic_record():
-    hm = bench.kernel_source_hash("mfma_M256x256_aligned")
+    hm = bench.kernel_source_hash("mfma_M256x128_aligned")
     hv = bench.kernel_source_hash("valu_V128x128_aligned")
     assert len(hm) == 16 and hm != hv
     assert hm == bench.kernel_source_hash("mfma_M64x64_edge")  # one family, one hash
