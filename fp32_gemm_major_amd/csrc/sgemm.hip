@@ -17,6 +17,7 @@
 
 #include "diag.hpp"
 #include "mfma_sgemm.hpp"
+#include "skinny_sgemm.hpp"
 #include "tile_map.hpp"
 #include "valu_sgemm.hpp"
 
@@ -139,6 +140,40 @@ hipError_t launch_valu(const RunArgs& a, int tiles_m, int tiles_n,
   return hipGetLastError();
 }
 
+// Split-K ranges of a small-M launch: as many workgroups (256 columns each)
+// as fit one per CU (a second round would double the time), each K range at
+// least SKINNY_KC rows, and no more ranges than the workspace holds (one
+// range needs none).
+int skinny_splits(const RunArgs& a, const LaunchCtx& c) {
+  const long long col_blocks = (a.N + SKINNY_COLS - 1) / SKINNY_COLS;
+  long long s = c.cus / col_blocks;
+  const long long by_k = a.K / SKINNY_KC > 1 ? a.K / SKINNY_KC : 1;
+  if (s > by_k) s = by_k;
+  const size_t per_split = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
+  const long long fit = c.ws == nullptr ? 1 : (long long)(c.ws_bytes / per_split);
+  if (s > fit) s = fit;
+  if (s < 1) s = 1;
+  const long long kps = (a.K + s - 1) / s;
+  return (int)((a.K + kps - 1) / kps);  // no empty range
+}
+
+template <int MT, bool TA>
+hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
+                         hipStream_t s) {
+  const int col_blocks = (a.N + SKINNY_COLS - 1) / SKINNY_COLS;
+  const int splits = skinny_splits(a, c);
+  const int kps = (a.K + splits - 1) / splits;
+  const GemmArgs g = gemm_args(a);
+  hipLaunchKernelGGL((skinny_sgemm_kernel<MT, TA>), dim3(col_blocks * splits),
+                     dim3(SKINNY_THREADS), 0, s, g, col_blocks, kps, c.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const long long groups = (long long)a.M * (skinny_ws_stride(a.N) / 4);
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((groups + 255) / 256)),
+                     dim3(256), 0, s, g, splits, static_cast<const float*>(c.ws));
+  return hipGetLastError();
+}
+
 // Tile shapes.  MfmaTile<BM, BN, WM, WN, OCC, S, BK, KG>: block tile, wave
 // tile, the waves per SIMD the register budget is sized for, LDS stages, K
 // step and K groups.
@@ -179,6 +214,12 @@ typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
   STORAGE(T, "nt_", false, true),                                            \
   STORAGE(T, "tt_", true, true)
 
+// Small-M kernels: bm = the most rows of C they take.
+#define SKINNY(MT, PRE, TA)                                                  \
+  {"valu_S" #MT "x256_" PRE "splitk", SGEMM_VARIANT_VALU, TA, false, MT,    \
+   SKINNY_COLS, SKINNY_KC, SKINNY_THREADS, SGEMM_MODE_EDGE,                  \
+   SGEMM_SCHEDULE_SPLIT_K, 0, launch_skinny<MT, TA>}
+
 // Largest shape first: ties in the modelled time keep the larger tile.  The
 // 256x256 tile has no stream-K instances: with 128 accumulator registers per
 // lane its stream-K kernel does not fit the register file, and it never
@@ -194,6 +235,8 @@ const KernelDesc kKernels[] = {
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED,
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, true>},
+    SKINNY(4, "", false), SKINNY(8, "", false), SKINNY(16, "", false),
+    SKINNY(4, "tn_", true), SKINNY(8, "tn_", true), SKINNY(16, "tn_", true),
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -227,6 +270,7 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
   if (k.schedule == SGEMM_SCHEDULE_STREAM_K &&
       (a.K <= 0 || c.ws == nullptr || c.ws_bytes < sk_workspace_bytes(k, c.cus)))
     return false;
+  if (k.schedule == SGEMM_SCHEDULE_SPLIT_K) return a.K > 0 && a.M <= k.bm;
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
       return true;
@@ -321,6 +365,21 @@ double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   return us;
 }
 
+// Small-M split-K launch: B streamed once at ~4.5 TB/s when at least half
+// the CUs have a workgroup (proportionally less with fewer), ~4 us of launch
+// and fill, and with several K ranges ~3 us for the second kernel plus the
+// partial sums written and read back at ~5 TB/s (measured on MI355X: 1 x
+// 4096 x 4096 in 20 us, 4 x 4096 x 16384 at 5.8 TB/s).
+double skinny_cost(const RunArgs& a, const LaunchCtx& c) {
+  const int splits = skinny_splits(a, c);
+  const double wgs = (double)((a.N + SKINNY_COLS - 1) / SKINNY_COLS) * splits;
+  const double fill = 2 * wgs < c.cus ? 2 * wgs / c.cus : 1.0;
+  double us = 4.0 + (double)a.K * a.N * 4 / (4.5e12 * fill) * 1e6;
+  if (splits > 1)
+    us += 3.0 + 2.0 * splits * a.M * skinny_ws_stride(a.N) * 4.0 / 5e12 * 1e6;
+  return us;
+}
+
 // Aligned one-tile-per-workgroup kernels of the variant and operand storage
 // (the tile shapes).
 bool is_shape(const KernelDesc& k, int variant, const RunArgs& a) {
@@ -373,9 +432,16 @@ struct Plan {
 // kind of plan.
 int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
   const int cus = ctx.cus;
-  if (variant == SGEMM_VARIANT_AUTO) variant = SGEMM_VARIANT_MFMA;
+  const bool any_variant = variant == SGEMM_VARIANT_AUTO;
+  if (any_variant) variant = SGEMM_VARIANT_MFMA;
   if (variant != SGEMM_VARIANT_MFMA && variant != SGEMM_VARIANT_VALU)
     return SGEMM_ERR_VALUE;
+  // the small-M kernel for these arguments (the fewest rows that hold M)
+  int skinny = -1;
+  if (any_variant || variant == SGEMM_VARIANT_VALU)
+    for (int i = 0; i < kNumKernels && skinny < 0; ++i)
+      if (kKernels[i].schedule == SGEMM_SCHEDULE_SPLIT_K && kernel_fits(kKernels[i], a, ctx))
+        skinny = i;
   int best = -1;
   double best_cost = 0.0;
   for (int i = 0; i < kNumKernels; ++i) {
@@ -386,7 +452,12 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
       best_cost = c;
     }
   }
-  if (best < 0) return SGEMM_ERR_UNSUPPORTED;  // e.g. VALU with transposes
+  if (best < 0) {  // e.g. VALU with transposes
+    if (skinny < 0) return SGEMM_ERR_UNSUPPORTED;
+    plan->count = 1;
+    plan->part[0] = Launch{skinny, 0, a.N};
+    return SGEMM_OK;
+  }
   plan->count = 1;
   plan->part[0] = Launch{instance_for(best, a, ctx), 0, a.N};
   if (plan->part[0].kernel < 0) return plan->part[0].kernel;
@@ -431,6 +502,10 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
         plan->part[0] = Launch{id, 0, a.N};
       }
     }
+  }
+  if (skinny >= 0 && skinny_cost(a, ctx) < best_cost) {
+    plan->count = 1;
+    plan->part[0] = Launch{skinny, 0, a.N};
   }
   return SGEMM_OK;
 }

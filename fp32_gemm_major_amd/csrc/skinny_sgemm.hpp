@@ -1,0 +1,225 @@
+// Small-M SGEMM (M <= 16, B stored K x N) on the vector ALUs.
+//
+// With a handful of rows in A the product is bound by reading B once from
+// HBM (2*M flops per 4 bytes of B, far under the MFMA ridge), so the matrix
+// cores do not help and an output tile of 64 or more rows would waste most
+// of their work; what matters is streaming B with wide, coalesced loads and
+// enough of them in flight.  The problem definition is the pages' ("GEMM
+// 优化之路", problem statement): C = alpha * op(A) * B + beta * C.
+//
+// A workgroup of 8 waves takes 256 columns of C (64 lanes x 4 adjacent
+// columns, one 16-byte load of a B row per lane) and one K range of a
+// split-K decomposition.  Its waves take the range's rows of B in turn
+// (wave w: rows w, w+8, ...), eight rows in flight per wave, and multiply
+// each with the matching column of A, which the workgroup stages in LDS as
+// [k][m] so one 16-byte broadcast read gives four rows' values.  The waves'
+// partial sums are added through LDS in a fixed tree, and the workgroup then
+// either applies alpha and beta (one K range) or writes its partial sums to
+// the workspace as [split][m][n] (row stride N rounded up to 4); a second
+// kernel adds the splits in order and applies alpha and beta.  Every sum is
+// taken in a fixed order, so results do not depend on timing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mfma_sgemm.hpp"  // f32x4, f32x4u, GemmArgs
+
+namespace sgemm {
+
+constexpr int SKINNY_COLS = 256;    // columns of C per workgroup
+constexpr int SKINNY_WAVES = 8;     // waves per workgroup, interleaved over k
+constexpr int SKINNY_THREADS = 64 * SKINNY_WAVES;
+constexpr int SKINNY_UNROLL = 8;    // rows of B in flight per wave
+constexpr int SKINNY_KC = 256;      // rows of A staged in LDS at a time
+
+// Row stride of a partial-sum row in the workspace: N rounded up to 4, so
+// every 4-column group starts 16-byte aligned.
+__host__ __device__ inline int skinny_ws_stride(int N) { return (N + 3) & ~3; }
+
+template <int MT>
+struct SkinnyLds {
+  // the A chunk ([k][m]) and, after the K loop, the waves' partial sums
+  static constexpr int A_FLOATS = SKINNY_KC * MT;
+  static constexpr int RED_FLOATS = (SKINNY_WAVES / 2) * MT * 64 * 4;
+  static constexpr int FLOATS = A_FLOATS > RED_FLOATS ? A_FLOATS : RED_FLOATS;
+};
+
+// 16 bytes of a row of B at column n (any 4-byte alignment), zero past N.
+__device__ __forceinline__ f32x4 skinny_load_b(const float* p, int n, int N) {
+  if (n + 3 < N) {
+    const f32x4u v = *reinterpret_cast<const f32x4u*>(p);
+    return f32x4{v[0], v[1], v[2], v[3]};
+  }
+  f32x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = n + e < N ? p[e] : 0.0f;
+  return x;
+}
+
+// Grid: splits * column blocks; split s covers rows [s*kps, min(K, (s+1)*kps))
+// of B.  MT >= M (rows of A past M are zero in LDS and never stored).  TA: A
+// stored K x M.  ws: the workspace when splits > 1, else unused.
+template <int MT, bool TA>
+__global__ void __launch_bounds__(SKINNY_THREADS)
+    skinny_sgemm_kernel(GemmArgs g, int col_blocks, int kps, float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(16))) float lds[SkinnyLds<MT>::FLOATS];
+  const int M = g.M, N = g.N, K = g.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s = blockIdx.x / col_blocks, cb = blockIdx.x - s * col_blocks;
+  const int splits = gridDim.x / col_blocks;
+  const int k0 = s * kps, k1 = k0 + kps < K ? k0 + kps : K;
+  const int n = cb * SKINNY_COLS + 4 * lane;
+  const float* __restrict__ A = g.A;
+  const float* __restrict__ B = g.B;
+  const int lda = g.lda, ldb = g.ldb;
+
+  float acc[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[m][e] = 0.0f;
+
+  constexpr int STEP = SKINNY_WAVES * SKINNY_UNROLL;
+  for (int kc = k0; kc < k1; kc += SKINNY_KC) {
+    const int kn = k1 - kc < SKINNY_KC ? k1 - kc : SKINNY_KC;
+    const float* bp = B + (size_t)kc * ldb + n;
+    // rows kk + u*SKINNY_WAVES of the chunk, loaded together, then multiplied
+    auto load = [&](int kk, f32x4 (&b)[SKINNY_UNROLL]) {
+#pragma unroll
+      for (int u = 0; u < SKINNY_UNROLL; ++u) {
+        const int k = kk + u * SKINNY_WAVES;
+        b[u] = k < kn ? skinny_load_b(bp + (size_t)k * ldb, n, N) : f32x4{};
+      }
+    };
+    auto multiply = [&](int kk, const f32x4 (&b)[SKINNY_UNROLL]) {
+#pragma unroll
+      for (int u = 0; u < SKINNY_UNROLL; ++u) {
+        const int k = kk + u * SKINNY_WAVES;
+        if (k < kn) {
+#pragma unroll
+          for (int m4 = 0; m4 < MT; m4 += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&lds[k * MT + m4]);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[m4 + mi][e] = fmaf(a[mi], b[u][e], acc[m4 + mi][e]);
+          }
+        }
+      }
+    };
+    // the chunk's first rows of B are requested before A is staged, so their
+    // latency overlaps the staging and its barrier
+    f32x4 b[SKINNY_UNROLL];
+    load(wave, b);
+    // stage A(0..MT-1, kc..kc+kn) as lds[k][m], zero past M and past kn
+    for (int i = threadIdx.x; i < SKINNY_KC * MT; i += SKINNY_THREADS) {
+      int k, m;
+      if (TA) {  // A(m, k) = A[k*lda + m]: m fastest reads a row of A^T
+        k = i / MT;
+        m = i - k * MT;
+      } else {   // A(m, k) = A[m*lda + k]: k fastest reads a row of A
+        m = i / SKINNY_KC;
+        k = i - m * SKINNY_KC;
+      }
+      float v = 0.0f;
+      if (m < M && k < kn)
+        v = TA ? A[(size_t)(kc + k) * lda + m] : A[(size_t)m * lda + (kc + k)];
+      lds[k * MT + m] = v;
+    }
+    __syncthreads();
+    for (int kk = wave; kk < kn; kk += STEP) {
+      if (kk != wave) load(kk, b);
+      multiply(kk, b);
+    }
+    __syncthreads();  // the next chunk, or the reduction, reuses the LDS
+  }
+
+  // waves [h, 2h) hand their sums to waves [0, h), h = 4, 2, 1
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+  for (int h = SKINNY_WAVES / 2; h >= 1; h /= 2) {
+    if (wave >= h && wave < 2 * h) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        red[((wave - h) * MT + m) * 64 + lane] =
+            f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+    }
+    __syncthreads();
+    if (wave < h) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const f32x4 v = red[(wave * MT + m) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[m][e] += v[e];
+      }
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || n >= N) return;
+
+  if (splits > 1) {
+    const int stride = skinny_ws_stride(N);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      if (m < M)
+        *reinterpret_cast<f32x4*>(ws + ((size_t)s * M + m) * stride + n) =
+            f32x4{acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+    return;
+  }
+  const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < M) {
+      float* p = g.C + (size_t)m * g.ldc + n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < N) {
+          float o = alpha * acc[m][e];
+          if (beta != 0.0f) o = fmaf(beta, p[e], o);
+          p[e] = o;
+        }
+      }
+    }
+  }
+}
+
+// Adds the splits' partial sums in split order and applies alpha and beta:
+// one thread per 4-column group of one row of C.
+__global__ void __launch_bounds__(256)
+    skinny_reduce_kernel(GemmArgs g, int splits, const float* __restrict__ ws) {
+  const int M = g.M, N = g.N;
+  const int stride = skinny_ws_stride(N);
+  const int groups = stride / 4;
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (x >= (long long)M * groups) return;
+  const int m = (int)(x / groups), n = 4 * (int)(x - (long long)m * groups);
+  // eight independent loads at a time, added in split order
+  const float* p0 = ws + (size_t)m * stride + n;
+  const size_t split_stride = (size_t)M * stride;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int s = 0;
+  for (; s + 8 <= splits; s += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const f32x4*>(p0 + (size_t)(s + j) * split_stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+  }
+  for (; s < splits; ++s)
+    acc += *reinterpret_cast<const f32x4*>(p0 + (size_t)s * split_stride);
+  const float alpha = g.alpha, beta = g.beta;
+  float* p = g.C + (size_t)m * g.ldc + n;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (n + e >= N) break;
+    float o = alpha * acc[e];
+    if (beta != 0.0f) o = fmaf(beta, p[e], o);
+    p[e] = o;
+  }
+}
+
+}  // namespace sgemm

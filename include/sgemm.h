@@ -113,10 +113,20 @@ enum sgemm_mode {
  *             beta: the result is deterministic.  Chosen only when the
  *             handle has a workspace of sgemm_workspace_size bytes (the
  *             load-balancing schedule of the tiles-and-K-steps split; the
- *             pages' "split-K" next step). */
+ *             pages' "split-K" next step).
+ *   SPLIT_K:  small M only (M <= the kernel's bm, at most 16; B stored
+ *             K x N): vector-ALU kernels that stream B once with 16-byte
+ *             loads, 256 columns of C per workgroup, K split over enough
+ *             workgroups to fill the CUs.  With more than one K range the
+ *             ranges' sums go to the workspace and a second kernel adds them
+ *             in range order and applies alpha and beta (deterministic);
+ *             without a workspace (or when it is too small) the K ranges are
+ *             merged until they fit, down to one.  Chosen for the AUTO and
+ *             VALU variants only. */
 enum sgemm_schedule {
   SGEMM_SCHEDULE_TILES = 0,
-  SGEMM_SCHEDULE_STREAM_K = 1
+  SGEMM_SCHEDULE_STREAM_K = 1,
+  SGEMM_SCHEDULE_SPLIT_K = 2
 };
 
 /* Create a handle bound to the current HIP device, which must be gfx950.
@@ -157,7 +167,7 @@ int sgemm_destroy(sgemm_handle_t h);
 int sgemm_set_workspace(sgemm_handle_t h, void* workspace, size_t bytes);
 
 /* Bytes of workspace that let every stream-K kernel run on the handle's
- * device (two partial tiles per stream-K workgroup; 128 MiB on 256 CUs). */
+ * device (two partial tiles per stream-K workgroup; 64 MiB on 256 CUs). */
 int sgemm_workspace_size(sgemm_handle_t h, size_t* bytes);
 
 /* ---- host-only helpers (no HIP call, no device needed) ---------------- */

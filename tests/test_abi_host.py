@@ -122,11 +122,18 @@ def test_kernel_table():
     for k in table:
         assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
     # every MFMA tile shape has an aligned, an edge and a guarded instance for
-    # each storage; the VALU shape an aligned and a guarded one
-    shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table}
+    # each storage; the VALU shape an aligned and a guarded one; the small-M
+    # split-K kernels (4, 8 and 16 rows) one edge instance for A as stored and
+    # one for A^T, B as stored
+    skinny = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_SPLIT_K]
+    assert {(k["bm"], k["transa"], k["transb"], k["mode"], k["variant"]) for k in skinny} == {
+        (m, a, 0, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU) for m in (4, 8, 16) for a in (0, 1)}
+    shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table
+              if k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K}
     for s in shapes:
         inst = {(k["transa"], k["transb"], k["mode"]) for k in table
-                if (k["variant"], k["bm"], k["bn"], k["bk"]) == s}
+                if (k["variant"], k["bm"], k["bn"], k["bk"]) == s
+                and k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K}
         if s[0] == sg.SGEMM_VARIANT_VALU:
             want = {(0, 0, sg.SGEMM_MODE_ALIGNED), (0, 0, sg.SGEMM_MODE_GUARDED)}
         else:
@@ -288,3 +295,26 @@ def test_plans_follow_measured_winners():
     assert name(8192, 8192, 4096) == ["mfma_M256x128_aligned"]
     assert name(1024, 1024, 1024) == ["mfma_M64x64_aligned"]
     assert name(3000, 3000, 3000) == ["mfma_M64x64_edge"]
+
+
+def test_small_m_plans():
+    """A few rows of A against a wide B plan the small-M split-K kernel with
+    the fewest rows that hold M, for A as stored or transposed; B stored
+    transposed, M past 16, or an explicit MFMA variant never do."""
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    def plan(M, N, K, variant=0, ta=0, tb=0):
+        lda = M if ta else K
+        ldb = K if tb else N
+        return [sg.sgemm_kernel_info(k) for k, _, _ in
+                sg.sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, N, transa=ta, transb=tb)]
+    for M, bm in ((1, 4), (4, 4), (5, 8), (16, 16)):
+        for ta in (0, 1):
+            p = plan(M, 65536, 1024, ta=ta)
+            assert [(k["schedule"], k["bm"], k["transa"]) for k in p] == \
+                [(sg.SGEMM_SCHEDULE_SPLIT_K, bm, ta)], (M, ta)
+    assert plan(17, 65536, 1024)[0]["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K
+    assert plan(4, 65536, 1024, tb=1)[0]["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K
+    assert plan(4, 65536, 1024, variant=sg.SGEMM_VARIANT_MFMA)[0]["variant"] == \
+        sg.SGEMM_VARIANT_MFMA
+    assert plan(4, 65536, 1024, variant=sg.SGEMM_VARIANT_VALU)[0]["schedule"] == \
+        sg.SGEMM_SCHEDULE_SPLIT_K

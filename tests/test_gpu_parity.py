@@ -58,7 +58,10 @@ def edge_fit(k, M, N):
 @pytest.mark.parametrize("dist", ["uniform", "int4"])
 def test_each_kernel(handle, k, dist):
     handle.set_kernel(k["id"])
-    if k["mode"] != sg.SGEMM_MODE_ALIGNED:
+    if k["schedule"] == sg.SGEMM_SCHEDULE_SPLIT_K:  # at most bm rows
+        M, N, K = k["bm"], 2 * k["bn"] + 19, 3 * k["bk"] + 5
+        lda, ldb, ldc = K + 3, N + 1, N + 5
+    elif k["mode"] != sg.SGEMM_MODE_ALIGNED:
         M, N = edge_fit(k, 2 * k["bm"] + 37, k["bn"] + 19)
         K = 3 * k["bk"] + 5
         lda, ldb, ldc = K + 3, N + 1, N + 5
@@ -214,7 +217,8 @@ def test_every_edge_and_guarded_kernel_on_tiny_tails(handle):
     """Sizes below one tile and one K step, and one past them, on every
     instance that takes ragged sizes (edge instances: only a partial K step,
     or one whole step plus one)."""
-    for k in (k for k in KERNELS if k["mode"] != sg.SGEMM_MODE_ALIGNED):
+    for k in (k for k in KERNELS if k["mode"] != sg.SGEMM_MODE_ALIGNED
+              and k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K):
         handle.set_kernel(k["id"])
         for i, (M, N, K) in enumerate([(1, 1, 1), (k["bm"] - 1, k["bn"] + 1, k["bk"] - 1),
                                        (k["bm"] + 1, k["bn"] - 1, k["bk"] + 1),
@@ -233,7 +237,8 @@ def test_edge_kernels_with_straddling_pieces(handle):
     two past a multiple of 4, K exactly two K steps and no row padding: the
     first step's direct loads read pieces that straddle the edge, and the
     last step (which holds the last K row) goes through registers."""
-    for k in (k for k in KERNELS if k["mode"] == sg.SGEMM_MODE_EDGE):
+    for k in (k for k in KERNELS if k["mode"] == sg.SGEMM_MODE_EDGE
+              and k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K):
         handle.set_kernel(k["id"])
         ta, tb = bool(k["transa"]), bool(k["transb"])
         M, N, K = k["bm"] + 6, k["bn"] + 6, 2 * k["bk"]
@@ -367,11 +372,12 @@ def test_misaligned_base_pointers(handle):
     gu.check_full(ops, out, exact=True, what="misaligned")
 
 
-@pytest.mark.parametrize("shape", [(16, 4096, 4096), (64, 4096, 4096), (100, 1000, 3000),
+@pytest.mark.parametrize("shape", [(32, 4096, 4096), (64, 4096, 4096), (100, 1000, 3000),
                                    (256, 256, 16384), (512, 512, 8192)])
 def test_stream_k_plans(handle, shape):
-    """Few output tiles over a long K (skinny M, or a small C with a deep
-    contraction) leave most CUs idle with one tile per workgroup, so the
+    """Few output tiles over a long K (skinny M past the small-M kernels' 16
+    rows, or a small C with a deep contraction) leave most CUs idle with one
+    tile per workgroup, so the
     planner runs them stream-K when the handle has a workspace: integer
     inputs, so the split-and-added tiles must still be bit-exact, and two
     runs must agree bit for bit."""
@@ -423,6 +429,57 @@ def test_no_workspace_no_stream_k():
         assert torch.all(C == 3.0)
     finally:
         h.close()
+
+
+SPLIT_K = [k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SPLIT_K]
+
+
+@pytest.mark.parametrize("k", SPLIT_K, ids=[k["name"] for k in SPLIT_K])
+@pytest.mark.parametrize("workspace", [True, False], ids=["ws", "nows"])
+def test_split_k_kernels(k, workspace):
+    """Every small-M kernel on ragged sizes: 1 and bm rows, columns short of,
+    at and past a 256-column block and not a multiple of 4, K below and past
+    one staged chunk of A, padded leading dimensions; integer inputs (exact)
+    and uniform ones (bound).  With a workspace K is split over workgroups
+    and a second kernel adds the ranges; without one a single range runs."""
+    h = sg.Handle(workspace=workspace)
+    try:
+        h.set_kernel(k["id"])
+        ta = bool(k["transa"])
+        cases = [(1, 1, 1), (k["bm"], 3, 7), (k["bm"] - 1, 255, 300), (1, 257, 1025),
+                 (k["bm"], 1000, 777), (k["bm"], 4096, 2048)]
+        for i, (M, N, K) in enumerate(cases):
+            M = max(M, 1)
+            for dist in ("int4", "uniform"):
+                w = wl.Workload("skinny", 7000 + 10 * i + k["id"], M, N, K, 1.5, -0.5, dist)
+                ops = wl.operands(w, lda=(M if ta else K) + 3, ldb=N + 1, ldc=N + 2, ta=ta)
+                gu.check_full(ops, gu.run(h, ops), exact=(dist == "int4"),
+                              what=f"{k['name']} ws={workspace} {M}x{N}x{K} {dist}")
+    finally:
+        h.close()
+
+
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (16, 4096, 4096), (7, 11008, 4096),
+                                   (16, 2000, 8192)])
+def test_split_k_plans(handle, shape):
+    """Decode-like shapes (a few rows of A against a large B) plan the
+    small-M kernel; bit-exact on integer inputs, bitwise repeatable, and
+    within the bound on normal(0, 0.02) inputs."""
+    M, N, K = shape
+    w = wl.Workload("skinnyplan", 7100 + M + N % 97, M, N, K, 1.0, 1.0, "int4")
+    ops = wl.operands(w)
+    A, B, C = gu.to_device(ops)
+    plan = handle.plan(M, N, K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                       C.data_ptr(), ops.ldc)
+    assert [sg.sgemm_kernel_schedule(k) for k, _, _ in plan] == [sg.SGEMM_SCHEDULE_SPLIT_K]
+    out = gu.run(handle, ops, dev=(A, B, C))
+    gu.check_full(ops, out, exact=True, what=f"split-K plan {shape}")
+    C.copy_(torch.from_numpy(ops.C).cuda())
+    again = gu.run(handle, ops, dev=(A, B, C))
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+    w = wl.Workload("skinnyplan", 7200 + M, M, N, K, 1.0, 0.0, "normal", "nan")
+    ops = wl.operands(w)
+    gu.check_full(ops, gu.run(handle, ops), what=f"split-K plan {shape} normal")
 
 
 def test_deterministic(handle):
