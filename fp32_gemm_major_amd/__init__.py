@@ -38,7 +38,7 @@ SGEMM_MODE_GUARDED = 2
 
 SGEMM_SCHEDULE_TILES = 0
 SGEMM_SCHEDULE_STREAM_K = 1
-SGEMM_SCHEDULE_SPLIT_K = 2
+SGEMM_SCHEDULE_SMALL_M = 2
 
 EXPORTED = [
     "sgemm_create", "sgemm_run", "sgemm_run_ex", "sgemm_destroy", "sgemm_validate",

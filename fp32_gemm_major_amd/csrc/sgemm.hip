@@ -158,6 +158,15 @@ int skinny_splits(const RunArgs& a, const LaunchCtx& c) {
 }
 
 template <int MT, bool TA>
+hipError_t launch_skinny_nt(const RunArgs& a, int, int, const LaunchCtx&,
+                            hipStream_t s) {
+  const int blocks = (a.N + SKINNY_NT_COLS - 1) / SKINNY_NT_COLS;
+  hipLaunchKernelGGL((skinny_nt_kernel<MT, TA>), dim3(blocks), dim3(SKINNY_NT_THREADS),
+                     0, s, gemm_args(a));
+  return hipGetLastError();
+}
+
+template <int MT, bool TA>
 hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
                          hipStream_t s) {
   const int col_blocks = (a.N + SKINNY_COLS - 1) / SKINNY_COLS;
@@ -214,11 +223,18 @@ typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
   STORAGE(T, "nt_", false, true),                                            \
   STORAGE(T, "tt_", true, true)
 
-// Small-M kernels: bm = the most rows of C they take.
+// Small-M kernels: bm = the most rows of C they take, bn = the columns of C
+// per workgroup.  With B stored N x K every workgroup stages all of A, whose
+// traffic grows with M: past 4 rows the MFMA stream-K kernels measured
+// faster (16 x 4096 x 4096: 42 against 26 us), so those kernels stop at 4.
 #define SKINNY(MT, PRE, TA)                                                  \
-  {"valu_S" #MT "x256_" PRE "splitk", SGEMM_VARIANT_VALU, TA, false, MT,    \
+  {"valu_S" #MT "x256_" PRE "small", SGEMM_VARIANT_VALU, TA, false, MT,     \
    SKINNY_COLS, SKINNY_KC, SKINNY_THREADS, SGEMM_MODE_EDGE,                  \
-   SGEMM_SCHEDULE_SPLIT_K, 0, launch_skinny<MT, TA>}
+   SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny<MT, TA>}
+#define SKINNY_NT(MT, PRE, TA)                                               \
+  {"valu_S" #MT "x16_" PRE "small", SGEMM_VARIANT_VALU, TA, true, MT,       \
+   SKINNY_NT_COLS, SKINNY_NT_KC, SKINNY_NT_THREADS, SGEMM_MODE_EDGE,         \
+   SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny_nt<MT, TA>}
 
 // Largest shape first: ties in the modelled time keep the larger tile.  The
 // 256x256 tile has no stream-K instances: with 128 accumulator registers per
@@ -237,6 +253,7 @@ const KernelDesc kKernels[] = {
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, true>},
     SKINNY(4, "", false), SKINNY(8, "", false), SKINNY(16, "", false),
     SKINNY(4, "tn_", true), SKINNY(8, "tn_", true), SKINNY(16, "tn_", true),
+    SKINNY_NT(4, "nt_", false), SKINNY_NT(4, "tt_", true),
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -270,7 +287,7 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
   if (k.schedule == SGEMM_SCHEDULE_STREAM_K &&
       (a.K <= 0 || c.ws == nullptr || c.ws_bytes < sk_workspace_bytes(k, c.cus)))
     return false;
-  if (k.schedule == SGEMM_SCHEDULE_SPLIT_K) return a.K > 0 && a.M <= k.bm;
+  if (k.schedule == SGEMM_SCHEDULE_SMALL_M) return a.K > 0 && a.M <= k.bm;
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
       return true;
@@ -365,16 +382,20 @@ double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   return us;
 }
 
-// Small-M split-K launch: B streamed once at ~4.5 TB/s when at least half
+// Small-M launch: B streamed once at ~4.5 TB/s when at least half
 // the CUs have a workgroup (proportionally less with fewer), ~4 us of launch
 // and fill, and with several K ranges ~3 us for the second kernel plus the
 // partial sums written and read back at ~5 TB/s (measured on MI355X: 1 x
 // 4096 x 4096 in 20 us, 4 x 4096 x 16384 at 5.8 TB/s).
 double skinny_cost(const RunArgs& a, const LaunchCtx& c) {
-  const int splits = skinny_splits(a, c);
-  const double wgs = (double)((a.N + SKINNY_COLS - 1) / SKINNY_COLS) * splits;
+  const int splits = a.tb ? 1 : skinny_splits(a, c);
+  const double wgs = a.tb ? (double)((a.N + SKINNY_NT_COLS - 1) / SKINNY_NT_COLS)
+                          : (double)((a.N + SKINNY_COLS - 1) / SKINNY_COLS) * splits;
   const double fill = 2 * wgs < c.cus ? 2 * wgs / c.cus : 1.0;
-  double us = 4.0 + (double)a.K * a.N * 4 / (4.5e12 * fill) * 1e6;
+  // B once; with B stored N x K every workgroup also reads all of A, mostly
+  // from L2 (counted at half the cost of HBM bytes)
+  const double bytes = (double)a.K * a.N * 4 + (a.tb ? 0.5 * wgs * a.M * a.K * 4.0 : 0.0);
+  double us = 4.0 + bytes / (4.5e12 * fill) * 1e6;
   if (splits > 1)
     us += 3.0 + 2.0 * splits * a.M * skinny_ws_stride(a.N) * 4.0 / 5e12 * 1e6;
   return us;
@@ -440,7 +461,7 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
   int skinny = -1;
   if (any_variant || variant == SGEMM_VARIANT_VALU)
     for (int i = 0; i < kNumKernels && skinny < 0; ++i)
-      if (kKernels[i].schedule == SGEMM_SCHEDULE_SPLIT_K && kernel_fits(kKernels[i], a, ctx))
+      if (kKernels[i].schedule == SGEMM_SCHEDULE_SMALL_M && kernel_fits(kKernels[i], a, ctx))
         skinny = i;
   int best = -1;
   double best_cost = 0.0;

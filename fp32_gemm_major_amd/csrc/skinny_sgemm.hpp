@@ -1,4 +1,4 @@
-// Small-M SGEMM (M <= 16, B stored K x N) on the vector ALUs.
+// Small-M SGEMM (M <= 16) on the vector ALUs.
 //
 // With a handful of rows in A the product is bound by reading B once from
 // HBM (2*M flops per 4 bytes of B, far under the MFMA ridge), so the matrix
@@ -219,6 +219,130 @@ __global__ void __launch_bounds__(256)
     float o = alpha * acc[e];
     if (beta != 0.0f) o = fmaf(beta, p[e], o);
     p[e] = o;
+  }
+}
+
+// ---- small M, B stored N x K ------------------------------------------------
+//
+// Row n of B is then contiguous along K, so the lanes of a wave split K: each
+// lane takes 4 consecutive k of every 256, reads 16 bytes of each of the
+// wave's 4 rows of B (1 KB per row per wave per step, SKINNY_NT_STEPS steps
+// in flight) and the matching 16 bytes of every row of A from LDS, and keeps
+// MT x 4 dot-product sums.  A workgroup of 4 waves takes 16 rows of B (16
+// columns of C) over all of K, so no workspace is needed; the lanes' sums
+// are added by an xor butterfly (a fixed order) and lane 0 applies alpha and
+// beta.  A is staged in LDS as [m][k], SKINNY_NT_KC k at a time.
+
+constexpr int SKINNY_NT_WAVES = 4;
+constexpr int SKINNY_NT_THREADS = 64 * SKINNY_NT_WAVES;
+constexpr int SKINNY_NT_ROWS = 4;     // rows of B per wave
+constexpr int SKINNY_NT_STEPS = 4;    // 256-k steps in flight per lane
+constexpr int SKINNY_NT_KC = 256 * SKINNY_NT_STEPS;
+constexpr int SKINNY_NT_COLS = SKINNY_NT_WAVES * SKINNY_NT_ROWS;  // per workgroup
+static_assert(SKINNY_NT_KC == 4 * SKINNY_NT_THREADS, "one 4-k piece of A per thread");
+
+// 16 bytes of row p of B^T at k (any 4-byte alignment), zero past kn.
+__device__ __forceinline__ f32x4 skinny_load_bt(const float* p, int k, int kn) {
+  if (k + 3 < kn) {
+    const f32x4u v = *reinterpret_cast<const f32x4u*>(p);
+    return f32x4{v[0], v[1], v[2], v[3]};
+  }
+  f32x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = k + e < kn ? p[e] : 0.0f;
+  return x;
+}
+
+template <int MT, bool TA>
+__global__ void __launch_bounds__(SKINNY_NT_THREADS)
+    skinny_nt_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) float lds[MT * SKINNY_NT_KC];
+  const int M = g.M, N = g.N, K = g.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * SKINNY_NT_WAVES + wave) * SKINNY_NT_ROWS;
+  const float* __restrict__ A = g.A;
+  const float* __restrict__ B = g.B;
+  const int lda = g.lda, ldb = g.ldb;
+
+  float acc[MT][SKINNY_NT_ROWS];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < SKINNY_NT_ROWS; ++r) acc[m][r] = 0.0f;
+
+  for (int kc = 0; kc < K; kc += SKINNY_NT_KC) {
+    const int kn = K - kc < SKINNY_NT_KC ? K - kc : SKINNY_NT_KC;
+    // this chunk's rows of B, requested before A is staged
+    f32x4 b[SKINNY_NT_STEPS][SKINNY_NT_ROWS];
+#pragma unroll
+    for (int t = 0; t < SKINNY_NT_STEPS; ++t) {
+      const int k = 256 * t + 4 * lane;
+#pragma unroll
+      for (int r = 0; r < SKINNY_NT_ROWS; ++r)
+        b[t][r] = (k < kn && n0 + r < N)
+                      ? skinny_load_bt(B + (size_t)(n0 + r) * ldb + kc + k, k, kn)
+                      : f32x4{};
+    }
+    // stage A(0..MT-1, kc..kc+kn) as lds[m][k], zero past M and past kn:
+    // thread i takes k = 4i .. 4i+3 of every row, all loads independent
+    {
+      const int k = 4 * threadIdx.x;
+      f32x4 v[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m >= M || k >= kn) {
+          v[m] = f32x4{};
+        } else if (!TA) {  // A(m, k) = A[m*lda + k]: 16 bytes of row m
+          v[m] = skinny_load_bt(A + (size_t)m * lda + kc + k, k, kn);
+        } else {           // A(m, k) = A[k*lda + m]: one float per k
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[m][e] = k + e < kn ? A[(size_t)(kc + k + e) * lda + m] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        *reinterpret_cast<f32x4*>(&lds[m * SKINNY_NT_KC + k]) = v[m];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < SKINNY_NT_STEPS; ++t) {
+      const int k = 256 * t + 4 * lane;
+      if (k < kn) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(&lds[m * SKINNY_NT_KC + k]);
+#pragma unroll
+          for (int r = 0; r < SKINNY_NT_ROWS; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[m][r] = fmaf(a[e], b[t][r][e], acc[m][r]);
+        }
+      }
+    }
+    __syncthreads();  // the next chunk reuses the LDS
+  }
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < SKINNY_NT_ROWS; ++r)
+#pragma unroll
+      for (int off = 32; off >= 1; off /= 2) acc[m][r] += __shfl_xor(acc[m][r], off);
+  if (lane != 0) return;
+  const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    if (m < M) {
+#pragma unroll
+      for (int r = 0; r < SKINNY_NT_ROWS; ++r) {
+        if (n0 + r < N) {
+          float* p = g.C + (size_t)m * g.ldc + n0 + r;
+          float o = alpha * acc[m][r];
+          if (beta != 0.0f) o = fmaf(beta, *p, o);
+          *p = o;
+        }
+      }
+    }
   }
 }
 

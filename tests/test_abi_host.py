@@ -123,17 +123,18 @@ def test_kernel_table():
         assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
     # every MFMA tile shape has an aligned, an edge and a guarded instance for
     # each storage; the VALU shape an aligned and a guarded one; the small-M
-    # split-K kernels (4, 8 and 16 rows) one edge instance for A as stored and
-    # one for A^T, B as stored
-    skinny = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_SPLIT_K]
-    assert {(k["bm"], k["transa"], k["transb"], k["mode"], k["variant"]) for k in skinny} == {
-        (m, a, 0, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU) for m in (4, 8, 16) for a in (0, 1)}
+    # kernels one edge instance per storage: 4, 8 and 16 rows with B as
+    # stored, 4 rows with B transposed
+    skinny = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
+    assert sorted((k["bm"], k["transa"], k["transb"], k["mode"], k["variant"]) for k in skinny) == \
+        sorted((m, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU)
+               for a in (0, 1) for b in (0, 1) for m in ((4,) if b else (4, 8, 16)))
     shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table
-              if k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K}
+              if k["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M}
     for s in shapes:
         inst = {(k["transa"], k["transb"], k["mode"]) for k in table
                 if (k["variant"], k["bm"], k["bn"], k["bk"]) == s
-                and k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K}
+                and k["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M}
         if s[0] == sg.SGEMM_VARIANT_VALU:
             want = {(0, 0, sg.SGEMM_MODE_ALIGNED), (0, 0, sg.SGEMM_MODE_GUARDED)}
         else:
@@ -298,9 +299,10 @@ def test_plans_follow_measured_winners():
 
 
 def test_small_m_plans():
-    """A few rows of A against a wide B plan the small-M split-K kernel with
-    the fewest rows that hold M, for A as stored or transposed; B stored
-    transposed, M past 16, or an explicit MFMA variant never do."""
+    """A few rows of A against a wide B plan the small-M kernel with the
+    fewest rows that hold M, for every storage (up to 16 rows with B as
+    stored, 4 with B transposed); more rows or an explicit MFMA variant
+    never do."""
     A, B, C = 0x10000000, 0x20000000, 0x40000000
     def plan(M, N, K, variant=0, ta=0, tb=0):
         lda = M if ta else K
@@ -309,12 +311,16 @@ def test_small_m_plans():
                 sg.sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, N, transa=ta, transb=tb)]
     for M, bm in ((1, 4), (4, 4), (5, 8), (16, 16)):
         for ta in (0, 1):
-            p = plan(M, 65536, 1024, ta=ta)
-            assert [(k["schedule"], k["bm"], k["transa"]) for k in p] == \
-                [(sg.SGEMM_SCHEDULE_SPLIT_K, bm, ta)], (M, ta)
-    assert plan(17, 65536, 1024)[0]["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K
-    assert plan(4, 65536, 1024, tb=1)[0]["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K
+            for tb in (0, 1):
+                if tb and M > 4:
+                    continue
+                # no workspace here: one K range for B as stored, so a wide B
+                p = plan(M, 4096, 16384, ta=ta, tb=tb) if tb else plan(M, 65536, 1024, ta=ta)
+                assert [(k["schedule"], k["bm"], k["transa"], k["transb"]) for k in p] == \
+                    [(sg.SGEMM_SCHEDULE_SMALL_M, bm, ta, tb)], (M, ta, tb)
+    assert plan(17, 65536, 1024)[0]["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M
+    assert plan(5, 4096, 16384, tb=1)[0]["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M
     assert plan(4, 65536, 1024, variant=sg.SGEMM_VARIANT_MFMA)[0]["variant"] == \
         sg.SGEMM_VARIANT_MFMA
     assert plan(4, 65536, 1024, variant=sg.SGEMM_VARIANT_VALU)[0]["schedule"] == \
-        sg.SGEMM_SCHEDULE_SPLIT_K
+        sg.SGEMM_SCHEDULE_SMALL_M

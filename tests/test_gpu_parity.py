@@ -58,7 +58,7 @@ def edge_fit(k, M, N):
 @pytest.mark.parametrize("dist", ["uniform", "int4"])
 def test_each_kernel(handle, k, dist):
     handle.set_kernel(k["id"])
-    if k["schedule"] == sg.SGEMM_SCHEDULE_SPLIT_K:  # at most bm rows
+    if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M:  # at most bm rows
         M, N, K = k["bm"], 2 * k["bn"] + 19, 3 * k["bk"] + 5
         lda, ldb, ldc = K + 3, N + 1, N + 5
     elif k["mode"] != sg.SGEMM_MODE_ALIGNED:
@@ -218,7 +218,7 @@ def test_every_edge_and_guarded_kernel_on_tiny_tails(handle):
     instance that takes ragged sizes (edge instances: only a partial K step,
     or one whole step plus one)."""
     for k in (k for k in KERNELS if k["mode"] != sg.SGEMM_MODE_ALIGNED
-              and k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K):
+              and k["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M):
         handle.set_kernel(k["id"])
         for i, (M, N, K) in enumerate([(1, 1, 1), (k["bm"] - 1, k["bn"] + 1, k["bk"] - 1),
                                        (k["bm"] + 1, k["bn"] - 1, k["bk"] + 1),
@@ -238,7 +238,7 @@ def test_edge_kernels_with_straddling_pieces(handle):
     first step's direct loads read pieces that straddle the edge, and the
     last step (which holds the last K row) goes through registers."""
     for k in (k for k in KERNELS if k["mode"] == sg.SGEMM_MODE_EDGE
-              and k["schedule"] != sg.SGEMM_SCHEDULE_SPLIT_K):
+              and k["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M):
         handle.set_kernel(k["id"])
         ta, tb = bool(k["transa"]), bool(k["transb"])
         M, N, K = k["bm"] + 6, k["bn"] + 6, 2 * k["bk"]
@@ -431,54 +431,59 @@ def test_no_workspace_no_stream_k():
         h.close()
 
 
-SPLIT_K = [k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SPLIT_K]
+SMALL_M = [k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
 
 
-@pytest.mark.parametrize("k", SPLIT_K, ids=[k["name"] for k in SPLIT_K])
+@pytest.mark.parametrize("k", SMALL_M, ids=[k["name"] for k in SMALL_M])
 @pytest.mark.parametrize("workspace", [True, False], ids=["ws", "nows"])
 def test_split_k_kernels(k, workspace):
     """Every small-M kernel on ragged sizes: 1 and bm rows, columns short of,
-    at and past a 256-column block and not a multiple of 4, K below and past
-    one staged chunk of A, padded leading dimensions; integer inputs (exact)
-    and uniform ones (bound).  With a workspace K is split over workgroups
-    and a second kernel adds the ranges; without one a single range runs."""
+    at and past a workgroup's block and not a multiple of 4, K below, at and
+    past one staged chunk of A and not a multiple of 4, padded leading
+    dimensions; integer inputs (exact) and uniform ones (bound).  B as
+    stored: with a workspace K is split over workgroups and a second kernel
+    adds the ranges, without one a single range runs (B transposed needs no
+    workspace either way)."""
     h = sg.Handle(workspace=workspace)
     try:
         h.set_kernel(k["id"])
-        ta = bool(k["transa"])
+        ta, tb = bool(k["transa"]), bool(k["transb"])
         cases = [(1, 1, 1), (k["bm"], 3, 7), (k["bm"] - 1, 255, 300), (1, 257, 1025),
-                 (k["bm"], 1000, 777), (k["bm"], 4096, 2048)]
+                 (k["bm"], 1000, 777), (k["bm"], 4096, 2048), (2, 33, 2049)]
         for i, (M, N, K) in enumerate(cases):
             M = max(M, 1)
             for dist in ("int4", "uniform"):
                 w = wl.Workload("skinny", 7000 + 10 * i + k["id"], M, N, K, 1.5, -0.5, dist)
-                ops = wl.operands(w, lda=(M if ta else K) + 3, ldb=N + 1, ldc=N + 2, ta=ta)
+                ops = wl.operands(w, lda=(M if ta else K) + 3, ldb=(K if tb else N) + 1,
+                                  ldc=N + 2, ta=ta, tb=tb)
                 gu.check_full(ops, gu.run(h, ops), exact=(dist == "int4"),
                               what=f"{k['name']} ws={workspace} {M}x{N}x{K} {dist}")
     finally:
         h.close()
 
 
-@pytest.mark.parametrize("shape", [(1, 4096, 4096), (16, 4096, 4096), (7, 11008, 4096),
-                                   (16, 2000, 8192)])
-def test_split_k_plans(handle, shape):
-    """Decode-like shapes (a few rows of A against a large B) plan the
-    small-M kernel; bit-exact on integer inputs, bitwise repeatable, and
-    within the bound on normal(0, 0.02) inputs."""
+@pytest.mark.parametrize("tb,shape", [(False, (1, 4096, 4096)), (False, (16, 4096, 4096)),
+                                      (False, (7, 11008, 4096)), (False, (16, 2000, 8192)),
+                                      (True, (1, 4096, 4096)), (True, (4, 4096, 4096)),
+                                      (True, (3, 11008, 4096)), (True, (2, 4096, 16384))])
+def test_split_k_plans(handle, shape, tb):
+    """Decode-like shapes (a few rows of A against a large B, stored K x N or
+    N x K) plan the small-M kernel; bit-exact on integer inputs, bitwise
+    repeatable, and within the bound on normal(0, 0.02) inputs."""
     M, N, K = shape
     w = wl.Workload("skinnyplan", 7100 + M + N % 97, M, N, K, 1.0, 1.0, "int4")
-    ops = wl.operands(w)
+    ops = wl.operands(w, tb=tb)
     A, B, C = gu.to_device(ops)
     plan = handle.plan(M, N, K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
-                       C.data_ptr(), ops.ldc)
-    assert [sg.sgemm_kernel_schedule(k) for k, _, _ in plan] == [sg.SGEMM_SCHEDULE_SPLIT_K]
+                       C.data_ptr(), ops.ldc, transb=int(tb))
+    assert [sg.sgemm_kernel_schedule(k) for k, _, _ in plan] == [sg.SGEMM_SCHEDULE_SMALL_M]
     out = gu.run(handle, ops, dev=(A, B, C))
-    gu.check_full(ops, out, exact=True, what=f"split-K plan {shape}")
+    gu.check_full(ops, out, exact=True, what=f"small-M plan {shape} tb={tb}")
     C.copy_(torch.from_numpy(ops.C).cuda())
     again = gu.run(handle, ops, dev=(A, B, C))
     assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
     w = wl.Workload("skinnyplan", 7200 + M, M, N, K, 1.0, 0.0, "normal", "nan")
-    ops = wl.operands(w)
+    ops = wl.operands(w, tb=tb)
     gu.check_full(ops, gu.run(handle, ops), what=f"split-K plan {shape} normal")
 
 
