@@ -35,8 +35,8 @@ TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 
 
 # sgemm.hip holds the tile shapes and launch parameters of every kernel
-KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp", "sgemm.hip"),
-                  "valu": ("valu_sgemm.hpp", "tile_map.hpp", "sgemm.hip")}
+KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp", "tiles.hpp"),
+                  "valu": ("valu_sgemm.hpp", "tile_map.hpp", "tiles.hpp")}
 
 
 def kernel_source_hash(kernel: str) -> str:

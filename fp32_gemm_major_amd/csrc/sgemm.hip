@@ -19,6 +19,7 @@
 #include "mfma_sgemm.hpp"
 #include "skinny_sgemm.hpp"
 #include "tile_map.hpp"
+#include "tiles.hpp"
 #include "valu_sgemm.hpp"
 
 using namespace sgemm;
@@ -183,23 +184,6 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   return hipGetLastError();
 }
 
-// Tile shapes.  MfmaTile<BM, BN, WM, WN, OCC, S, BK, KG>: block tile, wave
-// tile, the waves per SIMD the register budget is sized for, LDS stages, K
-// step and K groups.
-// 8 waves, 1 WG/CU; a K step of 32 halves the barriers per K (0.8% faster
-// at 4096^3 than 16, with 128 KB of LDS for the two stages)
-typedef MfmaTile<256, 256, 128, 64, 2, 2, 32> M256x256;
-typedef MfmaTile<256, 128, 64, 64, 4> M256x128;   // 8 waves, 2 WG/CU
-typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
-// Small tiles serve problems with about one tile per CU.  Four K groups of
-// four waves each take a quarter of every 64-wide K step, so a CU runs 16
-// waves on one tile (1024^3: 61% of peak, against 51% for one group with a
-// K step of 16).  A step is only eight MFMAs per wave, so the fragments of
-// the next step are read during the current one (1024^3 and 2048^3 3.4%
-// faster); registers are capped for 8 waves per SIMD so that two
-// workgroups still share a CU.
-typedef MfmaTile<64, 64, 32, 32, 8, 2, 16, 4, 1> M64x64;  // 16 waves
-typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
 #define MFMA_ONE(T, TAG, TA, TB, MODE)                                       \
   {"mfma_" #T "_" TAG, SGEMM_VARIANT_MFMA, TA, TB, T::BM, T::BN, T::BKS,    \
