@@ -487,6 +487,61 @@ def test_split_k_plans(handle, shape, tb):
     gu.check_full(ops, gu.run(handle, ops), what=f"split-K plan {shape} normal")
 
 
+def random_problems(seed, count):
+    """Seeded random problems that reach every kind of plan: small M against
+    wide B, ragged and aligned sizes around the tile edges, deep K with few
+    tiles, large M and N (the big tiles, split plans) with a short K, every
+    operand storage, padded leading dimensions, varied alpha and beta (beta
+    = 0 with a NaN-filled C)."""
+    rng = np.random.default_rng(seed)
+    picks = []
+    for i in range(count):
+        kind = i % 5
+        if kind == 0:    # small M
+            M = int(rng.integers(1, 17))
+            N = int(rng.integers(1, 5000))
+            K = int(rng.integers(1, 4000))
+        elif kind == 1:  # around tile multiples
+            M = int(rng.choice([64, 128, 256])) * int(rng.integers(1, 6)) + int(rng.integers(-3, 4))
+            N = int(rng.choice([64, 128, 256])) * int(rng.integers(1, 6)) + int(rng.integers(-3, 4))
+            K = int(rng.choice([16, 32, 64])) * int(rng.integers(1, 24)) + int(rng.integers(-2, 3))
+        elif kind == 2:  # few tiles, deep K
+            M = int(rng.integers(17, 300))
+            N = int(rng.integers(17, 300))
+            K = int(rng.integers(1000, 6000))
+        elif kind == 3:  # large M and N, short K
+            M = int(rng.integers(1500, 4200))
+            N = int(rng.integers(1500, 4200))
+            K = int(rng.integers(16, 160))
+        else:            # anything up to mid sizes
+            M, N, K = (int(x) for x in rng.integers(1, 1200, size=3))
+        M, N, K = max(M, 1), max(N, 1), max(K, 1)
+        ta, tb = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        alpha = float(rng.choice([1.0, -1.5, 0.5]))
+        beta = float(rng.choice([0.0, 1.0, -0.5]))
+        pads = [int(x) for x in rng.integers(0, 5, size=3)]
+        picks.append((M, N, K, ta, tb, alpha, beta, pads))
+    return picks
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_random_problems_integer_exact(handle, chunk):
+    """60 seeded random problems through the planner (with a workspace, so
+    stream-K and the small-M kernels are candidates): bit-exact on integer
+    inputs, the padding of C untouched."""
+    for i, (M, N, K, ta, tb, alpha, beta, pads) in enumerate(random_problems(8100 + chunk, 15)):
+        w = wl.Workload("rand", 8200 + 16 * chunk + i, M, N, K, alpha, beta, "int4",
+                        "nan" if beta == 0.0 else "dist")
+        ops = wl.operands(w, lda=(M if ta else K) + pads[0], ldb=(K if tb else N) + pads[1],
+                          ldc=N + pads[2], ta=ta, tb=tb)
+        plan = handle.plan(M, N, K, 0x10000000, ops.lda, 0x20000000, ops.ldb, 0x40000000,
+                           ops.ldc, transa=ta, transb=tb)
+        what = (f"{M}x{N}x{K} ta={ta} tb={tb} a={alpha} b={beta} pads={pads} "
+                f"plan={[sg.sgemm_kernel_name(k) for k, _, _ in plan]}")
+        print(what, flush=True)
+        gu.check_full(ops, gu.run(handle, ops), exact=True, what=what)
+
+
 def test_deterministic(handle):
     ops = wl.operands(wl.Workload("det", 2, 1024, 1024, 1024, 1.0, 0.0, "uniform"))
     A, B, C = gu.to_device(ops)
