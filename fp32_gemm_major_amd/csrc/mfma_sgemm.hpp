@@ -8,13 +8,14 @@
 // stages with one barrier per K step, fused alpha/beta update -- with each
 // level shaped for gfx950:
 //
-// * Block tile BM x BN, K step BK (16, 32 or 64).  Each wave owns a WM x WN
-//   sub-tile of 32x32 MFMA blocks (16 accumulators per lane per block).
+// * Block tile BM x BN, K step BK (16, 32 or 64) per K group; a stage holds
+//   BKS = KG * BK values of k.  Each wave owns a WM x WN sub-tile of 32x32
+//   MFMA blocks (16 accumulators per lane per block).
 // * An operand tile in LDS has one of two unpadded layouts, chosen by how the
 //   operand is stored, with 16-byte units XOR-swizzled instead of padding:
 //   - K-contiguous (A as stored, or B^T): rows of the outer index (m or n)
-//     holding BK/4 units of four consecutive k; unit c of row r sits at
-//     c ^ ((r / (64/BK)) & (BK/4 - 1)), so the 16-byte reads of 16
+//     holding BKS/4 units of four consecutive k; unit c of row r sits at
+//     c ^ ((r / (64/BKS)) & (BKS/4 - 1)), so the 16-byte reads of 16
 //     consecutive rows at one column group hit 16 distinct bank groups.
 //   - outer-contiguous (B as stored, or A^T): rows of k holding the outer
 //     index; the second k half of every K step has its 32-float halves
@@ -24,8 +25,13 @@
 //   read consecutive 16-byte pieces of a stored row: loads stay coalesced.
 // * Loader, aligned and edge kernels: global_load_lds_dwordx4, which
 //   writes lane l's 16 bytes to LDS at M0 + 16*l with no register staging.
-//   The loads of step t+S-1 go out before the MFMAs of step t and are waited
-//   for (vmcnt) before the barrier that ends step t+S-2.
+//   Two stages: the loads of step t+1 go out before the MFMAs of step t and
+//   are waited for (vmcnt) before the barrier that ends step t.  The LDS
+//   holds the A tiles of both stages, then the B tiles, and the K loop is
+//   unrolled by stage, so fragment reads take the stage in their immediate
+//   offsets.  The 64x64 tile also reads step t+1's fragments into a second
+//   register set during step t (its steps are short), and its loads run two
+//   steps ahead.
 // * Three modes per tile shape:
 //   - aligned (MODE 0): M, N and K are whole multiples of the tile and of the
 //     stage's K range; every load is a direct load.

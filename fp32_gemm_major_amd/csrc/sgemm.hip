@@ -29,7 +29,7 @@ struct sgemm_handle_s {
   int cus;
   int variant;       // SGEMM_VARIANT_*
   int forced_kernel; // -1 = automatic
-  void* workspace;   // caller's device memory for stream-K partials, or null
+  void* workspace;   // caller's device memory for partial sums, or null
   size_t workspace_bytes;
 };
 

@@ -157,12 +157,13 @@ int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
  * the handle stays the caller's to free. */
 int sgemm_destroy(sgemm_handle_t h);
 
-/* Device memory the stream-K kernels may use for partial tiles: `bytes` at
- * `workspace` (16-byte aligned, on the handle's device, owned by the caller
- * and kept alive while calls that may use it are in flight).  NULL with
- * bytes 0 removes it.  Without a workspace of at least sgemm_workspace_size
- * bytes no stream-K kernel is planned (a forced one returns
- * SGEMM_ERR_UNSUPPORTED).  Calls on one handle share the workspace: calls
+/* Device memory the stream-K kernels (partial tiles) and the small-M kernels
+ * (partial sums of K ranges) may use: `bytes` at `workspace` (16-byte
+ * aligned, on the handle's device, owned by the caller and kept alive while
+ * calls that may use it are in flight).  NULL with bytes 0 removes it.
+ * Without a workspace of at least sgemm_workspace_size bytes no stream-K
+ * kernel is planned (a forced one returns SGEMM_ERR_UNSUPPORTED); the
+ * small-M kernels split K only as far as the workspace holds.  Calls on one handle share the workspace: calls
  * that may overlap in time (different streams) need handles with separate
  * workspaces.  SGEMM_ERR_NULL for NULL with bytes > 0, SGEMM_ERR_VALUE for a
  * misaligned pointer. */
