@@ -34,18 +34,30 @@ PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 
 
-# sgemm.hip holds the tile shapes and launch parameters of every kernel
+# the kernel code, the tile order and the tile shapes of each family
 KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp", "tiles.hpp"),
                   "valu": ("valu_sgemm.hpp", "tile_map.hpp", "tiles.hpp")}
 
 
+def code_lines(text: str) -> str:
+    """The source without // comments and blank lines: what the compiler sees
+    of these headers (they hold no // inside string literals)."""
+    out = []
+    for line in text.splitlines():
+        line = line.split("//", 1)[0].rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """Hash of the sources that define a kernel family's code and tile order."""
+    """Hash of the code that defines a kernel family and its tile order
+    (comments excluded, so documentation edits keep traffic records valid)."""
     csrc = os.path.join(ROOT, "fp32_gemm_major_amd", "csrc")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel.split("_")[0]]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_lines(f.read()).encode())
     return h.hexdigest()[:16]
 
 
