@@ -20,6 +20,10 @@ Integer variants draw from {-4, ..., 4}; every partial sum of such inputs at
 these sizes is an integer below 2**24, so any summation order is exact.
 Every operand is drawn from ``default_rng([cfg_id, role])`` with role A=1,
 B=2, C=3, so values do not depend on the leading dimensions chosen.
+
+Products with 16-bit A and B (bfloat16 or IEEE binary16, FP32 C) draw the same
+FP32 values and round them to the 16-bit format, nearest-even
+(``round16``); the bit patterns are what both sides receive.
 """
 from __future__ import annotations
 
@@ -74,6 +78,40 @@ def draw(cfg_id: int, role: int, rows: int, cols: int, dist: str) -> np.ndarray:
     if dist == "int4":
         return rng.integers(-4, 5, size=shape).astype(np.float32)
     raise ValueError(f"unknown distribution {dist!r}")
+
+
+FORMATS16 = ("bf16", "f16")
+
+
+def round16(values: np.ndarray, dt: str) -> np.ndarray:
+    """Bit patterns (uint16) of FP32 ``values`` rounded to the nearest bfloat16
+    or IEEE binary16 value, ties to even (inputs must be finite).
+
+    binary16 is numpy's own conversion.  bfloat16 keeps the upper half of the
+    binary32 pattern after adding half an ulp of the kept part (0x7FFF plus the
+    kept part's lowest bit, which sends ties to the even neighbour).
+    """
+    x = np.ascontiguousarray(values, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("round16 takes finite values only")
+    if dt == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dt == "bf16":
+        w = x.view(np.uint32).astype(np.uint64)
+        w = (w + 0x7FFF + ((w >> 16) & 1)) >> 16
+        return w.astype(np.uint16)
+    raise ValueError(f"unknown 16-bit format {dt!r}")
+
+
+def place16(bits: np.ndarray, ld: int, pad_value=0x7FC0) -> np.ndarray:
+    """``place`` for 16-bit patterns; padding defaults to a NaN pattern of both
+    formats (0x7FC0 is a quiet NaN in bfloat16 and in binary16)."""
+    rows, cols = bits.shape
+    if ld < cols:
+        raise ValueError("ld < cols")
+    buf = np.full((rows, ld), pad_value, dtype=np.uint16)
+    buf[:, :cols] = bits
+    return buf.reshape(-1)
 
 
 def place(values: np.ndarray, ld: int, pad_value=np.nan) -> np.ndarray:
@@ -135,3 +173,47 @@ def operands(w: Workload, lda=None, ldb=None, ldc=None, pad_value=np.nan,
                     place(a, lda, pad_value), lda,
                     place(b, ldb, pad_value), ldb,
                     place(c, ldc, pad_value), ldc, ta, tb)
+
+
+@dataclass
+class Operands16:
+    """Operands of the product with 16-bit A and B (bit patterns) and FP32 C."""
+    dt: str
+    M: int
+    N: int
+    K: int
+    alpha: float
+    beta: float
+    A: np.ndarray  # flat uint16: M rows of lda (K rows of lda when ta)
+    lda: int
+    B: np.ndarray  # flat uint16: K rows of ldb (N rows of ldb when tb)
+    ldb: int
+    C: np.ndarray  # flat FP32, M*ldc (C_in)
+    ldc: int
+    ta: bool = False
+    tb: bool = False
+
+
+def operands16(w: Workload, dt: str, lda=None, ldb=None, ldc=None, M=None, N=None,
+               K=None, ta=False, tb=False) -> Operands16:
+    """Inputs of workload ``w`` with A and B rounded to the 16-bit format ``dt``;
+    C is drawn exactly as in ``operands``."""
+    if M is not None or N is not None or K is not None:
+        w = replace(w, M=w.M if M is None else M, N=w.N if N is None else N,
+                    K=w.K if K is None else K)
+    lda = max(w.M if ta else w.K, 1) if lda is None else lda
+    ldb = max(w.K if tb else w.N, 1) if ldb is None else ldb
+    ldc = max(w.N, 1) if ldc is None else ldc
+    a = round16(draw(w.cfg_id, ROLE_A, w.M, w.K, w.dist), dt)
+    b = round16(draw(w.cfg_id, ROLE_B, w.K, w.N, w.dist), dt)
+    if ta:
+        a = np.ascontiguousarray(a.T)
+    if tb:
+        b = np.ascontiguousarray(b.T)
+    if w.c_fill == "nan":
+        c = np.full((w.M, w.N), np.nan, dtype=np.float32)
+    else:
+        c = draw(w.cfg_id, ROLE_C, w.M, w.N, w.dist)
+    return Operands16(dt, w.M, w.N, w.K, w.alpha, w.beta,
+                      place16(a, lda), lda, place16(b, ldb), ldb,
+                      place(c, ldc), ldc, ta, tb)

@@ -13,6 +13,11 @@ row-major FP32 operands, A M x K, B K x N, C M x N.  See the C source for the
 exact arithmetic.  Results come back unrounded (FP64) as ``r``; the FP32
 result of the operation is ``r`` rounded to nearest-even (``to_f32``).
 
+``gemm_lowp`` is the same product with A and B stored as 16-bit patterns
+(bfloat16 or IEEE binary16, ``DT_BF16`` / ``DT_F16``), C and the sums as
+above: the mixed-precision matrix-unit product of the gsyq.cn guide,
+section 5.1.
+
 Pins (tests/test_oracle_pins.py) tie it to exact rational brute force, integer
 arithmetic, identity and permutation matrices, the rank-1 closed form and the
 alpha/beta semantics, none of which share code with it.
@@ -67,6 +72,12 @@ def _bind(lib):
     lib.oracle_sgemm_points_ex.argtypes = [i, i, i, i, i, f, p, i, p, i, f, p, i,
                                            i, p, p, p, p, i]
     lib.oracle_sgemm_points_ex.restype = i
+    lib.oracle_gemm_lowp.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i, p, i,
+                                     p, i, i]
+    lib.oracle_gemm_lowp.restype = i
+    lib.oracle_gemm_lowp_points.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i,
+                                            i, p, p, p, p, i]
+    lib.oracle_gemm_lowp_points.restype = i
     return lib
 
 
@@ -175,6 +186,82 @@ def gemm_points(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
     return r, t
 
 
+DT_BF16 = 1
+DT_F16 = 2
+_DT_NAMES = {"bf16": DT_BF16, "f16": DT_F16, DT_BF16: DT_BF16, DT_F16: DT_F16}
+
+
+def _dt(dt):
+    try:
+        return _DT_NAMES[dt]
+    except (KeyError, TypeError):
+        raise ValueError(f"unknown 16-bit format {dt!r}") from None
+
+
+def _u16(x, name):
+    a = np.ascontiguousarray(x).reshape(-1)
+    if a.dtype != np.uint16:
+        raise ValueError(f"{name}: 16-bit bit patterns (uint16) expected, got {a.dtype}")
+    return a
+
+
+def gemm_lowp(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
+              nthreads=None, lib=None, ta=False, tb=False):
+    """Full product with A and B stored as 16-bit patterns (uint16 arrays).
+
+    ``dt``: "bf16" / DT_BF16 or "f16" / DT_F16.  Everything else as ``gemm``.
+    """
+    dt = _dt(dt)
+    lib = lib or load()
+    A = _u16(A, "A")
+    B = _u16(B, "B")
+    _need_ops(A, B, M, N, K, lda, ldb, ta, tb)
+    if C is not None:
+        C = _f32(C, "C")
+        if beta != 0:
+            _need(C, M, ldc, N, "C")
+    elif beta != 0:
+        raise ValueError("C is required when beta != 0")
+    R = np.zeros((M, N), dtype=np.float64)
+    T = np.zeros((M, N), dtype=np.float64) if with_t else None
+    rc = lib.oracle_gemm_lowp(dt, int(bool(ta)), int(bool(tb)), M, N, K, float(alpha),
+                              _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+                              _ptr(R), max(N, 1), _ptr(T), max(N, 1),
+                              nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_lowp rejected the arguments (code {rc})")
+    return R, T
+
+
+def gemm_lowp_points(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
+                     nthreads=None, lib=None, ta=False, tb=False):
+    """Outputs of the 16-bit product at (rows[p], cols[p]) only."""
+    dt = _dt(dt)
+    lib = lib or load()
+    A = _u16(A, "A")
+    B = _u16(B, "B")
+    _need_ops(A, B, M, N, K, lda, ldb, ta, tb)
+    if C is not None:
+        C = _f32(C, "C")
+    elif beta != 0:
+        raise ValueError("C is required when beta != 0")
+    rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1)
+    cols = np.ascontiguousarray(cols, dtype=np.int32).reshape(-1)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    n = rows.size
+    r = np.zeros(n, dtype=np.float64)
+    t = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_gemm_lowp_points(dt, int(bool(ta)), int(bool(tb)), M, N, K,
+                                     float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                                     float(beta), _ptr(C), ldc, n, _ptr(rows),
+                                     _ptr(cols), _ptr(r), _ptr(t),
+                                     nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_lowp_points rejected the arguments (code {rc})")
+    return r, t
+
+
 def to_f32(r):
     """Round FP64 results to FP32, nearest-even (the oracle's FP32 output)."""
     return np.asarray(r, dtype=np.float64).astype(np.float32)
@@ -187,7 +274,9 @@ def error_bound(K, alpha, beta, t, c_in):
     beta term taken as 0 when beta == 0 (C is then not read and may hold NaN).
     The form is the standard a-priori bound for a length-K FP32 dot product
     (gamma_K = K*u/(1 - K*u), u = 2**-24) widened to cover the few roundings of
-    the alpha/beta update.
+    the alpha/beta update.  It holds unchanged for 16-bit A and B accumulated
+    in FP32: the product of two bfloat16 or binary16 values is exact in FP32
+    (at most 22 significant bits), so again only the FP32 additions round.
     """
     t = np.asarray(t, dtype=np.float64)
     scale = abs(float(alpha)) * t

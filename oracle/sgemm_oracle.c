@@ -27,6 +27,17 @@
  * only the additions round.  r_ij is returned unrounded; the caller rounds it
  * to FP32 when it needs the FP32 result.
  *
+ * Low-precision inputs (oracle_gemm_lowp): the mixed-precision product of
+ * the gsyq.cn guide, section 5.1 (matrix units take 16-bit A and B and
+ * accumulate into FP32), with A and B stored as 16-bit patterns in one of two
+ * formats, decoded exactly from their definitions:
+ *   - bfloat16: the upper 16 bits of an IEEE binary32 number;
+ *   - IEEE binary16: 1 sign bit, 5 exponent bits with bias 15, 10 fraction
+ *     bits; exponent 0 holds subnormals (fraction * 2^-24), exponent 31
+ *     infinities and NaNs.
+ * C, alpha and beta stay FP32 and the sums are the FP64 sums above: the
+ * product of two 16-bit values is exact in FP64 as well.
+ *
  * The loop nest follows the CPU reference on the same page (its complete
  * listing): rows outer, then k, then columns, with a row of accumulators.
  * Threads split the rows; nothing else is blocked, fused or reordered.
@@ -36,6 +47,7 @@
 #include <math.h>
 #include <pthread.h>
 #include <stddef.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -44,6 +56,9 @@ typedef struct {
   int ta, tb;  /* transposed storage of A / B */
   double alpha, beta;
   const float *A, *B, *C;
+  /* 16-bit storage of A and B (dt != DT_F32): bit patterns, same indexing */
+  int dt;
+  const uint16_t *A16, *B16;
   long lda, ldb, ldc;
   double *R, *T;
   long ldr, ldt;
@@ -54,11 +69,46 @@ typedef struct {
   int first, last;
 } job_t;
 
+/* Element formats. */
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+/* bfloat16: the pattern is the upper half of an IEEE binary32 number. */
+static double bf16_value(uint16_t h) {
+  const uint32_t w = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+/* IEEE binary16: (-1)^s * 2^(e-15) * (1 + m/1024) for 0 < e < 31,
+ * (-1)^s * 2^-14 * (m/1024) for e == 0, infinity or NaN for e == 31. */
+static double f16_value(uint16_t h) {
+  const int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+static double value16(int dt, uint16_t h) {
+  return dt == DT_BF16 ? bf16_value(h) : f16_value(h);
+}
+
 /* Element (i,k) of A and (k,j) of B under the storage flags. */
 static double a_at(const job_t *j, int i, int k) {
+  if (j->dt != DT_F32)
+    return value16(j->dt, j->ta ? j->A16[(long)k * j->lda + i]
+                                : j->A16[(long)i * j->lda + k]);
   return (double)(j->ta ? j->A[(long)k * j->lda + i] : j->A[(long)i * j->lda + k]);
 }
 static double b_at(const job_t *j, int k, int c) {
+  if (j->dt != DT_F32)
+    return value16(j->dt, j->tb ? j->B16[(long)c * j->ldb + k]
+                                : j->B16[(long)k * j->ldb + c]);
   return (double)(j->tb ? j->B[(long)c * j->ldb + k] : j->B[(long)k * j->ldb + c]);
 }
 
@@ -205,4 +255,54 @@ int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
                         int nthreads) {
   return oracle_sgemm_points_ex(0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
                                 ldc, npts, rows, cols, r_out, t_out, nthreads);
+}
+
+/*
+ * The same products with A and B in a 16-bit format: dt = 1 for bfloat16,
+ * 2 for IEEE binary16 (bit patterns as stored).  C, alpha, beta, R and T as
+ * in oracle_sgemm_ex.  Returns 0, -1/-2 as there, or -4 for an unknown dt.
+ */
+int oracle_gemm_lowp(int dt, int ta, int tb, int M, int N, int K, float alpha,
+                     const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                     float beta, const float *C, int ldc, double *R, int ldr,
+                     double *T, int ldt, int nthreads) {
+  if (dt != DT_BF16 && dt != DT_F16) return -4;
+  int e = check_args(ta, tb, M, N, K, lda, ldb, ldc);
+  if (e) return e;
+  if (ldr < N || (T && ldt < N)) return -2;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.M = M; j.N = N; j.K = K;
+  j.ta = ta != 0; j.tb = tb != 0;
+  j.alpha = (double)alpha; j.beta = (double)beta;
+  j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.R = R; j.T = T; j.ldr = ldr; j.ldt = ldt;
+  if (N > 0) run_split(full_rows, &j, M, nthreads);
+  return 0;
+}
+
+/* Selected outputs of the 16-bit product, as oracle_sgemm_points_ex. */
+int oracle_gemm_lowp_points(int dt, int ta, int tb, int M, int N, int K,
+                            float alpha, const uint16_t *A, int lda,
+                            const uint16_t *B, int ldb, float beta,
+                            const float *C, int ldc, int npts, const int *rows,
+                            const int *cols, double *r_out, double *t_out,
+                            int nthreads) {
+  if (dt != DT_BF16 && dt != DT_F16) return -4;
+  int e = check_args(ta, tb, M, N, K, lda, ldb, ldc);
+  if (e) return e;
+  for (int p = 0; p < npts; ++p)
+    if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -3;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.M = M; j.N = N; j.K = K;
+  j.ta = ta != 0; j.tb = tb != 0;
+  j.alpha = (double)alpha; j.beta = (double)beta;
+  j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.npts = npts; j.rows = rows; j.cols = cols;
+  j.R = r_out; j.T = t_out;
+  run_split(points, &j, npts, nthreads);
+  return 0;
 }

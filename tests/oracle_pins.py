@@ -7,7 +7,9 @@ the oracle's loop: they use exact rational arithmetic, Python integers,
 closed forms of special matrices, and invariants such as (AB)^T = B^T A^T.
 
 What the oracle computes is C = alpha*A*B + beta*C for row-major FP32 operands
-("GEMM 优化之路", problem statement), with beta == 0 meaning C is not read.
+("GEMM 优化之路", problem statement), with beta == 0 meaning C is not read,
+and the same product with A and B in bfloat16 or IEEE binary16 (the gsyq.cn
+guide, section 5.1: 16-bit inputs, FP32 accumulation).
 """
 from __future__ import annotations
 
@@ -304,6 +306,132 @@ def pin_transposed_bruteforce(lib, seed=41, cases=12):
                                                    for k in range(K)))), (case, i, j)
 
 
+# ---- 16-bit A and B (bfloat16, IEEE binary16), FP32 C ---------------------
+#
+# What the oracle decodes is fixed by the formats' definitions; the pins take
+# the decoded values from library conversions (numpy's float16, torch's
+# bfloat16), not from the oracle's own formulas.
+
+F16_ONE = 0x3C00   # 1.0 in binary16
+BF16_ONE = 0x3F80  # 1.0 in bfloat16
+
+
+def values16(bits, dt):
+    """FP64 values of 16-bit patterns by library conversion."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dt == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    import torch
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _same_values(got, want):
+    both_nan = np.isnan(got) & np.isnan(want)
+    return bool(np.all(both_nan | (got == want)))
+
+
+def pin_lowp_decode(lib):
+    """Every one of the 65536 patterns of each format, as an A element and as a
+    B element (product with 1.0), equals the library conversion; NaN patterns
+    give NaN, infinities infinities, binary16 subnormals their exact value."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dt, one in (("bf16", BF16_ONE), ("f16", F16_ONE)):
+        want = values16(allbits, dt)
+        onev = np.array([one], np.uint16)
+        R, _ = oracle.gemm_lowp(dt, 65536, 1, 1, 1.0, allbits, 1, onev, 1, 0.0, None,
+                                1, with_t=False, lib=lib)
+        assert _same_values(R[:, 0], want), f"{dt}: A-side decode differs"
+        R, _ = oracle.gemm_lowp(dt, 1, 65536, 1, 1.0, onev, 1, allbits, 65536, 0.0,
+                                None, 65536, with_t=False, lib=lib)
+        assert _same_values(R[0, :], want), f"{dt}: B-side decode differs"
+        # transposed storage reads the same patterns
+        R, _ = oracle.gemm_lowp(dt, 65536, 1, 1, 1.0, allbits, 65536, onev, 1, 0.0,
+                                None, 1, with_t=False, lib=lib, ta=True, tb=True)
+        assert _same_values(R[:, 0], want), f"{dt}: transposed decode differs"
+
+
+def _pattern_pair(rng, shape, dt):
+    """Random finite 16-bit patterns of moderate magnitude and their values."""
+    x = (2.0 * rng.random(shape) - 1.0).astype(np.float32)
+    x *= np.float32(2.0) ** rng.integers(-12, 4, shape).astype(np.float32)
+    from fp32_gemm_major_amd import workloads as wl
+    bits = wl.round16(x, dt)
+    return bits, values16(bits, dt).astype(np.float32)
+
+
+def pin_lowp_matches_f32(lib, seed=43):
+    """On values the 16-bit formats hold exactly, the 16-bit product equals
+    the FP32 oracle's (itself pinned above) bit for bit, in both modes, for
+    every storage, padded leading dimensions and alpha/beta."""
+    rng = np.random.default_rng(seed)
+    cases = [(5, 7, 9, 1.0, 0.0), (17, 3, 33, 1.5, 0.5), (1, 11, 4, -0.75, 1.0),
+             (9, 1, 1, 2.0, -1.25), (6, 6, 0, 1.0, 0.5)]
+    for dt in ("bf16", "f16"):
+        for ci, (M, N, K, alpha, beta) in enumerate(cases):
+            for ta in (False, True):
+                for tb in (False, True):
+                    a_bits, a_val = _pattern_pair(rng, (K, M) if ta else (M, K), dt)
+                    b_bits, b_val = _pattern_pair(rng, (N, K) if tb else (K, N), dt)
+                    C = _dyadic(rng, (M, N))
+                    pa, pb = 2, 3  # padded leading dimensions
+                    lda = (M if ta else K) + pa
+                    ldb = (K if tb else N) + pb
+                    A16 = np.zeros((a_bits.shape[0], lda), np.uint16)
+                    A16[:, :a_bits.shape[1]] = a_bits
+                    B16 = np.zeros((b_bits.shape[0], ldb), np.uint16)
+                    B16[:, :b_bits.shape[1]] = b_bits
+                    A32 = np.zeros(A16.shape, np.float32)
+                    A32[:, :a_val.shape[1]] = a_val
+                    B32 = np.zeros(B16.shape, np.float32)
+                    B32[:, :b_val.shape[1]] = b_val
+                    R16, T16 = oracle.gemm_lowp(dt, M, N, K, alpha, A16, lda, B16, ldb,
+                                                beta, C, N, lib=lib, ta=ta, tb=tb)
+                    R32, T32 = oracle.gemm(M, N, K, alpha, A32, lda, B32, ldb, beta,
+                                           C, N, lib=lib, ta=ta, tb=tb)
+                    tag = f"{dt} case {ci} ta={ta} tb={tb}"
+                    assert np.array_equal(R16, R32), tag + ": r differs"
+                    assert np.array_equal(T16, T32), tag + ": t differs"
+                    if M and N:
+                        rows = rng.integers(0, M, 8)
+                        cols = rng.integers(0, N, 8)
+                        rp, tp = oracle.gemm_lowp_points(dt, M, N, K, alpha, A16, lda,
+                                                         B16, ldb, beta, C, N, rows,
+                                                         cols, lib=lib, ta=ta, tb=tb)
+                        assert np.array_equal(rp, R32[rows, cols]), tag + ": points r"
+                        assert np.array_equal(tp, T32[rows, cols]), tag + ": points t"
+
+
+def pin_lowp_bruteforce(lib, seed=47, cases=16):
+    """Tiny 16-bit products, binary16 subnormals and bfloat16 extremes
+    included, against exact rational sums of the library-decoded values."""
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        dt = "f16" if case % 2 else "bf16"
+        M, N, K = (int(x) for x in rng.integers(1, 6, size=3))
+        if dt == "f16":
+            # any finite pattern: exponent field 0..30 (subnormals included)
+            a_bits = rng.integers(0, 0x7C00, (M, K)).astype(np.uint16)
+            b_bits = rng.integers(0, 0x7C00, (K, N)).astype(np.uint16)
+        else:
+            # exponent fields 0x20..0xDF keep every product and sum finite
+            a_bits = rng.integers(0x1000, 0x7000, (M, K)).astype(np.uint16)
+            b_bits = rng.integers(0x1000, 0x7000, (K, N)).astype(np.uint16)
+        a_bits |= (rng.integers(0, 2, a_bits.shape) << 15).astype(np.uint16)
+        b_bits |= (rng.integers(0, 2, b_bits.shape) << 15).astype(np.uint16)
+        av, bv = values16(a_bits, dt), values16(b_bits, dt)
+        R, _ = oracle.gemm_lowp(dt, M, N, K, 1.0, a_bits, K, b_bits, N, 0.0, None, N,
+                                lib=lib)
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(float(av[i, k])) * Fraction(float(bv[k, j]))
+                         for k in range(K)]
+                exact = sum(terms, Fraction(0))
+                t = float(sum((abs(x) for x in terms), Fraction(0)))
+                err = abs(Fraction(float(R[i, j])) - exact)
+                assert err <= Fraction((K + 3) * U * t), (dt, case, i, j)
+
+
 ALL_PINS = [pin_bruteforce_exact, pin_integer_exact, pin_identity,
             pin_permutation, pin_rank1, pin_alpha_beta, pin_transpose,
-            pin_leading_dims, pin_transposed_storage, pin_transposed_bruteforce]
+            pin_leading_dims, pin_transposed_storage, pin_transposed_bruteforce,
+            pin_lowp_decode, pin_lowp_matches_f32, pin_lowp_bruteforce]

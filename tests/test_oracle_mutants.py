@@ -2,7 +2,8 @@
 
 Each mutant is a one-spot textual change to oracle/sgemm_oracle.c of the kind
 a plausible slip would make (a dropped term, a wrong sign or index, a
-transposed operand, a lost scale, an FP32 accumulator).  It is compiled on the
+transposed operand, a lost scale, an FP32 accumulator, a wrong field of a
+16-bit format).  It is compiled on the
 CPU into a temporary library and every pin runs against it; the test passes
 only if some pin rejects the mutant.
 """
@@ -39,6 +40,20 @@ MUTANTS = {
     "t_signed": ("if (t) t[c] += fabs(p);", "if (t) t[c] += p;"),
     "row_offset": ("double *r = j->R + (long)i * j->ldr;",
                    "double *r = j->R + (long)(i > 0 ? i - 1 : 0) * j->ldr;"),
+    # 16-bit formats
+    "bf16_shift": ("(uint32_t)h << 16;", "(uint32_t)h << 15;"),
+    "f16_bias": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    "f16_no_hidden_bit": ("ldexp((double)(1024 + m), e - 25)", "ldexp((double)m, e - 25)"),
+    "f16_subnormal_as_normal": ("v = ldexp((double)m, -24);",
+                                "v = ldexp((double)(1024 + m), -25);"),
+    "f16_sign_dropped": ("return s ? -v : v;", "return v;"),
+    "f16_exponent_bits": ("e = (h >> 10) & 31", "e = (h >> 10) & 15"),
+    "lowp_formats_swapped": ("return dt == DT_BF16 ? bf16_value(h)", "return dt == DT_F16 ? bf16_value(h)"),
+    "lowp_ta_ignored": ("j->ta ? j->A16[(long)k * j->lda + i]", "j->ta ? j->A16[(long)i * j->lda + k]"),
+    "lowp_tb_ignored": ("j->tb ? j->B16[(long)c * j->ldb + k]", "j->tb ? j->B16[(long)k * j->ldb + c]"),
+    "lowp_b_ld": ("j->B16[(long)k * j->ldb + c]", "j->B16[(long)k * j->lda + c]"),
+    "lowp_points_no_flags": ("  j.M = M; j.N = N; j.K = K;\n  j.ta = ta != 0; j.tb = tb != 0;\n  j.alpha = (double)alpha; j.beta = (double)beta;\n  j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;\n  j.lda = lda; j.ldb = ldb; j.ldc = ldc;\n  j.npts",
+                             "  j.M = M; j.N = N; j.K = K;\n  j.alpha = (double)alpha; j.beta = (double)beta;\n  j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;\n  j.lda = lda; j.ldb = ldb; j.ldc = ldc;\n  j.npts"),
 }
 
 

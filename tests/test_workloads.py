@@ -1,5 +1,6 @@
 """Seeded input generators: determinism, ranges, layout."""
 import numpy as np
+import pytest
 
 from fp32_gemm_major_amd import workloads as wl
 
@@ -43,3 +44,32 @@ def test_registry_matches_configs():
     assert (w["c4_edge"].M, w["c4_edge"].N, w["c4_edge"].K) == (1000, 1500, 777)
     assert (w["c5_mlp"].N, w["c5_mlp"].dist) == (11008, "normal")
     assert w["c2_1024"].c_fill == "nan" and w["c2_1024"].beta == 0.0
+
+
+def test_round16_nearest_even():
+    """The 16-bit input rounding agrees with library conversions (torch's
+    bfloat16, numpy's float16), ties included."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(200000).astype(np.float32) * np.float32(3.0)
+    ties = np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** -130,
+                       1 + 2 ** -11, 1 + 3 * 2 ** -11, 0.0, -0.0, 65504.0, 3e38])
+    x = np.concatenate([x, ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(wl.round16(x, "bf16"), want.view(np.uint16))
+    assert np.array_equal(wl.round16(x[:-1], "f16"),
+                          x[:-1].astype(np.float16).view(np.uint16))
+    with pytest.raises(ValueError):
+        wl.round16(np.float32([np.nan]), "bf16")
+
+
+def test_operands16_values():
+    """16-bit operands hold the rounded FP32 draws; storage flags transpose."""
+    w = wl.WORKLOADS["c4_edge"]
+    o = wl.operands16(w, "bf16", M=40, N=24, K=33)
+    o_t = wl.operands16(w, "bf16", M=40, N=24, K=33, ta=True, tb=True)
+    a = o.A.reshape(40, 33)
+    assert np.array_equal(a, wl.round16(wl.draw(w.cfg_id, wl.ROLE_A, 40, 33, w.dist), "bf16"))
+    assert np.array_equal(o_t.A.reshape(33, 40).T, a)
+    assert np.array_equal(o_t.B.reshape(24, 33).T, o.B.reshape(33, 24))
+    assert o.C.dtype == np.float32 and o.A.dtype == np.uint16
