@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_4096]
                     [--variant mfma|valu] [--no-cpu-baseline] [--no-per-config]
+                    [--lowp all|bf16|f16|none] [--lowp-only]
 
 A step is one SGEMM call, C = alpha*A*B + beta*C, on the headline workload
 (M = N = K = 4096, alpha = 1.5, beta = 0.5, uniform [-1, 1) inputs, C
@@ -13,7 +14,9 @@ problem statement; the alpha/beta update is not counted).
 Output: one JSON line with the throughput, the kernel's roofline position
 (HIP events around every launch on the stream the kernel runs on), the CPU
 oracle timed on a bounded sample of the same workload, and per-workload
-GFLOPS for the other problem shapes.
+GFLOPS for the other problem shapes; then the same problems with bfloat16
+and binary16 A and B and FP32 C (the "lowp" object: the headline problem's
+roofline against the dense 16-bit matrix-core peak, and the other shapes).
 """
 from __future__ import annotations
 
@@ -36,7 +39,8 @@ TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 
 # the kernel code, the tile order and the tile shapes of each family
 KERNEL_SOURCES = {"mfma": ("mfma_sgemm.hpp", "tile_map.hpp", "tiles.hpp"),
-                  "valu": ("valu_sgemm.hpp", "tile_map.hpp", "tiles.hpp")}
+                  "valu": ("valu_sgemm.hpp", "tile_map.hpp", "tiles.hpp"),
+                  "lp": ("lowp_gemm.hpp", "mfma_sgemm.hpp", "tile_map.hpp")}
 
 
 def code_lines(text: str) -> str:
@@ -169,6 +173,82 @@ def cpu_baseline(ops, target_s: float):
     }
 
 
+def lowp_section(args, sg, rf, wl, torch):
+    """The products with 16-bit A and B (bfloat16 / binary16) and FP32 C: the
+    headline problem timed launch by launch with HIP events, as its own
+    roofline against the dense 16-bit matrix-core peak, and the other
+    workloads (and transposed storage) from replayed HIP graphs."""
+    formats = {"all": ("bf16", "f16"), "bf16": ("bf16",), "f16": ("f16",),
+               "none": ()}[args.lowp]
+    if not formats:
+        return None
+    t16 = {"bf16": torch.bfloat16, "f16": torch.float16}
+    peaks = {"bf16": rf.PEAK_BF16_FLOPS, "f16": rf.PEAK_F16_FLOPS}
+    h = sg.Handle(workspace=False)
+    out = {}
+
+    def prepare(name, dt, ta=False, tb=False):
+        w = wl.WORKLOADS[name]
+        ops = wl.operands16(w, dt, ta=ta, tb=tb)
+        A = torch.from_numpy(ops.A.view("int16")).cuda().view(t16[dt])
+        B = torch.from_numpy(ops.B.view("int16")).cuda().view(t16[dt])
+        C = torch.from_numpy(ops.C).cuda()
+        kid = sg.sgemm_lowp_select_kernel(
+            sg.SGEMM_DTYPE_BF16 if dt == "bf16" else sg.SGEMM_DTYPE_F16, int(ta),
+            int(tb), w.M, w.N, w.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+            C.data_ptr(), ops.ldc)
+
+        def launch():
+            h.gemm_lowp(A, B, C, w.alpha, w.beta, M=w.M, N=w.N, K=w.K, lda=ops.lda,
+                        ldb=ops.ldb, ldc=ops.ldc, transa=ta, transb=tb)
+        return w, (A, B, C), kid, launch
+
+    for dt in formats:
+        peak = peaks[dt]
+        w, dev, kid, launch = prepare(args.workload, dt)
+        steps = max(args.steps // 2, 10)
+        _, per = time_launches(launch, steps, max(args.warmup, 5), torch)
+        kms = sum(per) / len(per)
+        achieved = rf.flops(w.M, w.N, w.K) / (kms * 1e-3)
+        sec = {"roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": peak / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.label + "_" + dt, sg.sgemm_lowp_kernel_name(kid)),
+            "kernel": sg.sgemm_lowp_kernel_name(kid),
+            "kernel_ms_mean": round(kms, 5),
+            "kernel_ms_min": round(min(per), 5),
+            "kernel_ms_median": round(statistics.median(per), 5),
+            "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta, ab_bytes=2),
+            "flops_per_launch": rf.flops(w.M, w.N, w.K),
+            "launches": steps,
+        }}
+        del dev
+        per_config = {}
+        if not args.no_per_config:
+            cases = [("c1_128", False, False, 200), ("c2_1024", False, False, 200),
+                     ("c4_edge", False, False, 100), ("c5_mlp", False, False, 20),
+                     (args.workload, False, True, 20), (args.workload, True, False, 20),
+                     (args.workload, True, True, 20)]
+            for name, ta, tb, reps in cases:
+                w2, dev2, kid2, launch2 = prepare(name, dt, ta, tb)
+                ms = time_graph(launch2, reps, torch)
+                gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
+                tag = name + ({(False, False): "", (False, True): "_nt",
+                               (True, False): "_tn", (True, True): "_tt"}[(ta, tb)])
+                per_config[tag] = {"gflops": round(gf, 1),
+                                   "frac_of_peak": round(gf * 1e9 / peak, 4),
+                                   "kernel_ms": round(ms, 5),
+                                   "kernel": sg.sgemm_lowp_kernel_name(kid2)}
+                del dev2
+        sec["per_config"] = per_config
+        out[dt] = sec
+    h.close()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +260,10 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--lowp", choices=["all", "bf16", "f16", "none"], default="all",
+                    help="which 16-bit-input products to time after the FP32 ones")
+    ap.add_argument("--lowp-only", action="store_true",
+                    help="time only the 16-bit-input products (for profiler runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run one plain device copy of this "
                          "many bytes (a reference dispatch for HBM byte counters)")
@@ -216,6 +300,12 @@ def main(argv=None):
             h.gemm(dev[0], dev[1], dev[2], w.alpha, w.beta, M=w.M, N=w.N, K=w.K,
                    lda=ops.lda, ldb=ops.ldb, ldc=ops.ldc, transa=ta, transb=tb)
         return w, ops, dev, kid, launch
+
+    if args.lowp_only:
+        lowp = lowp_section(args, sg, rf, wl, torch)
+        h.close()
+        print(json.dumps({"lowp": lowp}), flush=True)
+        return 0
 
     w, ops, dev, kid, launch = prepare(args.workload)
     kname = sg.sgemm_kernel_name(kid)
@@ -290,6 +380,7 @@ def main(argv=None):
             h.set_variant(variant)
             del dev3
     h.close()
+    lowp = lowp_section(args, sg, rf, wl, torch)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(ops, args.cpu_seconds)
 
@@ -313,6 +404,7 @@ def main(argv=None):
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "lowp": lowp,
     }
     print(json.dumps(line), flush=True)
     return 0

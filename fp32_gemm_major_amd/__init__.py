@@ -1,7 +1,8 @@
 """MI355X (gfx950) FP32 GEMM: Python binding of the C ABI in include/sgemm.h.
 
 C = alpha * A * B + beta * C for row-major FP32 operands ("GEMM 优化之路",
-problem statement).  Every step runs in the HIP library ``libsgemm.so``; this
+problem statement), and the same product with bfloat16 or float16 A and B and
+FP32 C (the gsyq.cn guide, section 5.1).  Every step runs in the HIP library ``libsgemm.so``; this
 module only marshals arguments.  PyTorch provides device memory and streams.
 There is no fallback: if the library is missing, loading fails loudly.
 """
@@ -36,6 +37,9 @@ SGEMM_MODE_ALIGNED = 0
 SGEMM_MODE_EDGE = 1
 SGEMM_MODE_GUARDED = 2
 
+SGEMM_DTYPE_BF16 = 1
+SGEMM_DTYPE_F16 = 2
+
 SGEMM_SCHEDULE_TILES = 0
 SGEMM_SCHEDULE_STREAM_K = 1
 SGEMM_SCHEDULE_SMALL_M = 2
@@ -47,7 +51,9 @@ EXPORTED = [
     "sgemm_kernel_info", "sgemm_plan", "sgemm_select_kernel", "sgemm_tile_coords",
     "sgemm_set_variant", "sgemm_set_kernel", "sgemm_diag_mfma_chain",
     "sgemm_set_workspace", "sgemm_workspace_size", "sgemm_plan_handle",
-    "sgemm_kernel_schedule",
+    "sgemm_kernel_schedule", "sgemm_run_lowp", "sgemm_validate_lowp",
+    "sgemm_lowp_num_kernels", "sgemm_lowp_kernel_name", "sgemm_lowp_kernel_info",
+    "sgemm_lowp_select_kernel", "sgemm_set_lowp_kernel",
 ]
 
 
@@ -87,6 +93,18 @@ def _bind(lib):
     lib.sgemm_workspace_size.argtypes = [p, ctypes.POINTER(ctypes.c_size_t)]
     lib.sgemm_plan_handle.argtypes = [p, i, i, i, i, i, p, i, p, i, p, i, ip, ip]
     lib.sgemm_kernel_schedule.argtypes = [i]
+    lib.sgemm_run_lowp.argtypes = [p, i, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_validate_lowp.argtypes = [i, i, i, i, i, i, p, i, p, i, f, p, i]
+    lib.sgemm_lowp_num_kernels.argtypes = []
+    lib.sgemm_lowp_kernel_name.argtypes = [i]
+    lib.sgemm_lowp_kernel_name.restype = ctypes.c_char_p
+    lib.sgemm_lowp_kernel_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip, ip]
+    lib.sgemm_lowp_select_kernel.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i]
+    lib.sgemm_set_lowp_kernel.argtypes = [p, i]
+    for name in ("sgemm_run_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
+                 "sgemm_lowp_kernel_info", "sgemm_lowp_select_kernel",
+                 "sgemm_set_lowp_kernel"):
+        getattr(lib, name).restype = i
     for name in ("sgemm_create", "sgemm_run", "sgemm_destroy", "sgemm_validate",
                  "sgemm_num_kernels", "sgemm_kernel_info", "sgemm_select_kernel",
                  "sgemm_plan", "sgemm_diag_mfma_chain", "sgemm_run_ex",
@@ -135,6 +153,51 @@ def sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
     return _check(library().sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda,
                                          B, ldb, beta, C, ldc, stream),
                   "sgemm_run_ex")
+
+
+def sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                   ldc, stream=0) -> int:
+    """The product with 16-bit A and B (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16) and
+    FP32 C; A, B, C are device addresses."""
+    return _check(library().sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha,
+                                           A, lda, B, ldb, beta, C, ldc, stream),
+                  "sgemm_run_lowp")
+
+
+def sgemm_validate_lowp(dtype, transa, transb, M, N, K, A, lda, B, ldb, beta, C,
+                        ldc) -> int:
+    return library().sgemm_validate_lowp(dtype, transa, transb, M, N, K, A, lda, B,
+                                         ldb, beta, C, ldc)
+
+
+def sgemm_lowp_num_kernels() -> int:
+    return library().sgemm_lowp_num_kernels()
+
+
+def sgemm_lowp_kernel_name(kernel_id: int):
+    s = library().sgemm_lowp_kernel_name(kernel_id)
+    return s.decode() if s is not None else None
+
+
+def sgemm_lowp_kernel_info(kernel_id: int) -> dict:
+    vals = [ctypes.c_int() for _ in range(8)]
+    _check(library().sgemm_lowp_kernel_info(kernel_id, *[ctypes.byref(v) for v in vals]),
+           "sgemm_lowp_kernel_info")
+    keys = ("dtype", "bm", "bn", "bk", "threads", "mode", "transa", "transb")
+    d = {k: v.value for k, v in zip(keys, vals)}
+    d["name"] = sgemm_lowp_kernel_name(kernel_id)
+    d["id"] = kernel_id
+    return d
+
+
+def sgemm_lowp_select_kernel(dtype, transa, transb, M, N, K, A, lda, B, ldb, C,
+                             ldc) -> int:
+    return library().sgemm_lowp_select_kernel(dtype, transa, transb, M, N, K, A, lda,
+                                              B, ldb, C, ldc)
+
+
+def sgemm_set_lowp_kernel(h, kernel_id: int) -> int:
+    return _check(library().sgemm_set_lowp_kernel(h, kernel_id), "sgemm_set_lowp_kernel")
 
 
 def sgemm_destroy(h) -> int:
@@ -341,20 +404,8 @@ class Handle:
                 raise TypeError(f"{name} must be a float32 CUDA tensor")
             if t.dim() == 2 and t.numel() and t.stride(1) != 1:
                 raise ValueError(f"{name} must be row-major (unit column stride)")
-        if A.dim() == 2:
-            ra, ca = A.shape
-            M = (ca if transa else ra) if M is None else M
-            K = (ra if transa else ca) if K is None else K
-            lda = max(A.stride(0), 1) if lda is None else lda
-        if B.dim() == 2:
-            rb, cb = B.shape
-            K = (cb if transb else rb) if K is None else K
-            N = (rb if transb else cb) if N is None else N
-            ldb = max(B.stride(0), 1) if ldb is None else ldb
-        if C.dim() == 2:
-            ldc = max(C.stride(0), 1) if ldc is None else ldc
-        if None in (M, N, K, lda, ldb, ldc):
-            raise ValueError("sizes and leading dimensions are needed for 1-D buffers")
+        M, N, K, lda, ldb, ldc = _shapes(A, B, C, M, N, K, lda, ldb, ldc, transa,
+                                         transb)
         if stream is None:
             stream = torch.cuda.current_stream(C.device).cuda_stream
         elif isinstance(stream, torch.cuda.Stream):
@@ -364,5 +415,59 @@ class Handle:
                             float(beta), C.data_ptr(), ldc, stream)
 
 
+    def set_lowp_kernel(self, kernel_id: int):
+        sgemm_set_lowp_kernel(self.h, kernel_id)
+
+    def gemm_lowp(self, A, B, C, alpha=1.0, beta=0.0, M=None, N=None, K=None,
+                  lda=None, ldb=None, ldc=None, stream=None, transa=False,
+                  transb=False):
+        """C[:M, :N] = alpha * op(A) @ op(B) + beta * C with A and B bfloat16 or
+        float16 CUDA tensors (both the same format) and C a float32 CUDA tensor;
+        shapes, leading dimensions and ``stream`` as in ``gemm``."""
+        formats = {torch.bfloat16: SGEMM_DTYPE_BF16, torch.float16: SGEMM_DTYPE_F16}
+        if A.dtype != B.dtype or A.dtype not in formats:
+            raise TypeError("A and B must both be bfloat16 or both float16")
+        for name, t in (("A", A), ("B", B), ("C", C)):
+            if not t.is_cuda:
+                raise TypeError(f"{name} must be a CUDA tensor")
+            if t.dim() == 2 and t.numel() and t.stride(1) != 1:
+                raise ValueError(f"{name} must be row-major (unit column stride)")
+        if C.dtype != torch.float32:
+            raise TypeError("C must be a float32 CUDA tensor")
+        M, N, K, lda, ldb, ldc = _shapes(A, B, C, M, N, K, lda, ldb, ldc, transa,
+                                         transb)
+        if stream is None:
+            stream = torch.cuda.current_stream(C.device).cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        return sgemm_run_lowp(self.h, formats[A.dtype], int(bool(transa)),
+                              int(bool(transb)), M, N, K, float(alpha), A.data_ptr(),
+                              lda, B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
+                              stream)
+
+
+def _shapes(A, B, C, M, N, K, lda, ldb, ldc, transa, transb):
+    """Sizes and leading dimensions from 2-D tensors where not given."""
+    if A.dim() == 2:
+        ra, ca = A.shape
+        M = (ca if transa else ra) if M is None else M
+        K = (ra if transa else ca) if K is None else K
+        lda = max(A.stride(0), 1) if lda is None else lda
+    if B.dim() == 2:
+        rb, cb = B.shape
+        K = (cb if transb else rb) if K is None else K
+        N = (rb if transb else cb) if N is None else N
+        ldb = max(B.stride(0), 1) if ldb is None else ldb
+    if C.dim() == 2:
+        ldc = max(C.stride(0), 1) if ldc is None else ldc
+    if None in (M, N, K, lda, ldb, ldc):
+        raise ValueError("sizes and leading dimensions are needed for 1-D buffers")
+    return M, N, K, lda, ldb, ldc
+
+
 def kernel_table() -> list:
     return [sgemm_kernel_info(i) for i in range(sgemm_num_kernels())]
+
+
+def lowp_kernel_table() -> list:
+    return [sgemm_lowp_kernel_info(i) for i in range(sgemm_lowp_num_kernels())]

@@ -1,0 +1,386 @@
+// Products with 16-bit A and B (bfloat16 or IEEE binary16) and FP32 C on the
+// CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x16_f16).
+//
+// C = alpha*op(A)*op(B) + beta*C with op(A), op(B) as in the FP32 kernels and
+// C, alpha, beta in FP32: the mixed-precision matrix-unit product of the
+// gsyq.cn guide, section 5.1 (16-bit inputs, FP32 accumulation).  The
+// structure is the FP32 kernels' -- block tile staged in LDS, per-wave
+// register tile of 32x32 MFMA blocks, two LDS stages with one barrier per K
+// step, fused alpha/beta update -- with the operand tiles reshaped for the
+// 16-bit instructions:
+//
+// * A K step is 64 values of k.  Each lane of a 32x32x16 MFMA supplies eight
+//   consecutive k of one row of A and of one column of B (lanes 0-31 one half
+//   of the 16, lanes 32-63 the other; which half is free as long as A and B
+//   agree), so both operand tiles are K-contiguous in LDS: one 128-byte row
+//   of 64 k per row of A and per column of B, eight 16-byte units per row.
+//   Unit c of row r sits at c ^ ((r / 2) & 7): the 16-byte fragment reads of
+//   16 consecutive rows at one unit then hit 16 distinct 16-byte bank groups.
+// * An operand stored K-contiguous (A as stored, B stored N x K) moves by
+//   direct global-to-LDS loads (global_load_lds_dwordx4, as in the FP32
+//   kernels): lane l's 16 bytes land in slot 64*i + l of the tile, and the
+//   lane reads the global unit that the swizzle puts in that slot, so eight
+//   consecutive lanes read one 128-byte row segment.
+// * An operand stored outer-contiguous (B stored K x N, A stored K x M) is
+//   transposed on its way through registers.  A wave moves a region of
+//   64 k x 64 outer indices; lane (kb, ob) = (l % 8, l / 8) loads the 8 x 8
+//   block at k = 8kb, outer = 8ob (eight 16-byte loads, one per k row, each
+//   load instruction reading eight 128-byte row segments) and writes its
+//   eight outer rows as 16-byte units of eight k.  Lanes with odd ob write
+//   their rows in pair-swapped order (1, 0, 3, 2, ...), so the 16 lanes of
+//   one LDS write cover both row parities and all 16 bank groups.  The swap
+//   costs nothing: only the byte selector of the v_perm that builds each
+//   output dword differs between the two kinds of lanes.
+// * MFMA operands are swapped (the B fragment first), so a 32x32 result is
+//   the transpose of its C block and the FP32 kernels' epilogue applies as it
+//   is: lane (li, lh) holds row li and columns 8g + 4lh + e of the block.
+// * Two modes:
+//   - aligned (MODE_ALIGNED): M, N and K whole multiples of the tile and of
+//     64, leading dimensions multiples of 8 elements and 16-byte aligned A
+//     and B, so every unit is a whole, aligned 16-byte piece;
+//   - guarded (MODE_GUARDED): any sizes and any 2-byte aligned operands.
+//     Every operand goes through registers: a 16-byte load where the unit
+//     lies wholly inside the operand and is 16-byte aligned, element loads
+//     with zero fill past the edges elsewhere (no lane leaves before the
+//     barriers), masked stores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mfma_sgemm.hpp"
+#include "tile_map.hpp"
+
+namespace sgemm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Element formats of A and B.
+enum { LP_BF16 = 1, LP_F16 = 2 };
+
+// The operation's arguments: A and B as 16-bit patterns.
+struct LpArgs {
+  int M, N, K;
+  float alpha, beta;
+  const uint16_t* A;
+  int lda;
+  const uint16_t* B;
+  int ldb;
+  float* C;
+  int ldc;
+};
+
+// Block tile BM x BN, wave tile WM x WN of 32x32 blocks, registers sized for
+// OCC waves per SIMD.  The member names the FP32 epilogue (store_tile) and
+// WaveCoords read are the same as MfmaTile's (one K group).
+template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+struct LpTile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, OCC = OCC_;
+  static constexpr int BK = 64;  // k per K step: one 128-byte LDS row
+  static constexpr int KG = 1;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
+  static constexpr int WAVES_MN = WAVES_M * WAVES_N, WAVES = WAVES_MN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;  // one stage
+  static constexpr int LDS_BYTES = 2 * (A_BYTES + B_BYTES);
+  // K-contiguous loader: 16-byte units per lane per K step
+  static constexpr int A_VEC = BM * 8 / THREADS, B_VEC = BN * 8 / THREADS;
+  // transposing loader: waves that move the operand (64 outer indices each)
+  static constexpr int A_TW = BM / 64, B_TW = BN / 64;
+  static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
+  static_assert(A_VEC >= 1 && A_VEC * THREADS == BM * 8, "A loader");
+  static_assert(B_VEC >= 1 && B_VEC * THREADS == BN * 8, "B loader");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "transposing loader regions");
+  static_assert(A_TW <= WAVES && B_TW <= WAVES, "transposing loader waves");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
+  static_assert(A_VEC + B_VEC <= 63, "vmcnt range");
+};
+
+// Byte offset of 16-byte unit c (k = 8c .. 8c+7) of row r in an operand tile.
+__device__ __forceinline__ int lp_unit_off(int r, int c) {
+  return r * 128 + 16 * (c ^ ((r >> 1) & 7));
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 lp_mfma(u32x4 x, u32x4 y, f32x16 acc) {
+  if constexpr (DT == LP_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        __builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
+}
+
+// Eight 16-bit elements at p (2-byte aligned): a 16-byte load when all eight
+// are wanted and p is 16-byte aligned, else element loads of the first n (n
+// may be <= 0) with zeros after them.
+__device__ __forceinline__ u32x4 lp_load8(const uint16_t* p, int n) {
+  if (n >= 8 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0)
+    return *reinterpret_cast<const u32x4*>(p);
+  unsigned h[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) h[t] = t < n ? (unsigned)p[t] : 0u;
+  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+               h[6] | (h[7] << 16)};
+}
+
+// Accumulate the output tile at (m0, n0) over all of K into acc (zeroed by
+// the caller).  TA: A stored K x M; TB: B stored N x K.
+template <class T, int DT, int MODE, bool TA, bool TB>
+__device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
+                                                   int m0, int n0,
+                                                   f32x16 (&acc)[T::FM][T::FN]) {
+  constexpr bool GUARD = MODE == MODE_GUARDED;
+  constexpr bool A_KC = !TA;  // A stored K-contiguous
+  constexpr bool B_KC = TB;   // B stored K-contiguous
+  const int M = g.M, N = g.N, K = g.K;
+  const uint16_t* __restrict__ A = g.A;
+  const uint16_t* __restrict__ B = g.B;
+  const int lda = g.lda, ldb = g.ldb;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+  const int li = lane & 31, lh = lane >> 5;
+  const int kb = lane & 7, ob = lane >> 3;  // transposing loader block
+  const int nk = (K + T::BK - 1) / T::BK;
+
+  // LDS: the A tiles of both stages, then the B tiles.
+  auto a_off = [](int st) { return st * T::A_BYTES; };
+  auto b_off = [](int st) { return 2 * T::A_BYTES + st * T::B_BYTES; };
+
+  // ---- K-contiguous operands: slot u of the tile holds (row, unit) ------
+  int a_r[T::A_VEC], a_c[T::A_VEC], b_r[T::B_VEC], b_c[T::B_VEC];
+#pragma unroll
+  for (int v = 0; v < T::A_VEC; ++v) {
+    const int u = (v * T::WAVES + wave) * 64 + lane;
+    a_r[v] = u >> 3;
+    a_c[v] = (u & 7) ^ ((a_r[v] >> 1) & 7);
+  }
+#pragma unroll
+  for (int v = 0; v < T::B_VEC; ++v) {
+    const int u = (v * T::WAVES + wave) * 64 + lane;
+    b_r[v] = u >> 3;
+    b_c[v] = (u & 7) ^ ((b_r[v] >> 1) & 7);
+  }
+  // Direct loads (aligned mode): wave-uniform base at the tile's origin,
+  // advanced 64 elements per K step, and fixed per-lane byte offsets (the
+  // host keeps them below 2^32).
+  const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
+  unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
+  if (!GUARD) {
+#pragma unroll
+    for (int v = 0; v < T::A_VEC; ++v)
+      a_voff[v] = 2u * ((unsigned)a_r[v] * (unsigned)lda + 8u * (unsigned)a_c[v]);
+#pragma unroll
+    for (int v = 0; v < T::B_VEC; ++v)
+      b_voff[v] = 2u * ((unsigned)b_r[v] * (unsigned)ldb + 8u * (unsigned)b_c[v]);
+  }
+  const uint16_t* a_kc_base = A + (size_t)m0 * lda;  // used when A_KC
+  const uint16_t* b_kc_base = B + (size_t)n0 * ldb;  // used when B_KC
+  auto issue_direct = [&](int kt, int st) {
+    if (A_KC) {
+#pragma unroll
+      for (int v = 0; v < T::A_VEC; ++v)
+        dma16(reinterpret_cast<const float*>(a_kc_base + (size_t)kt * T::BK), a_voff[v],
+              lds_u + (unsigned)a_off(st) + 1024u * (unsigned)(v * T::WAVES + wave_u));
+    }
+    if (B_KC) {
+#pragma unroll
+      for (int v = 0; v < T::B_VEC; ++v)
+        dma16(reinterpret_cast<const float*>(b_kc_base + (size_t)kt * T::BK), b_voff[v],
+              lds_u + (unsigned)b_off(st) + 1024u * (unsigned)(v * T::WAVES + wave_u));
+    }
+  };
+
+  // ---- register-staged operands --------------------------------------------
+  // K-contiguous operands in guarded mode: one unit per slot.
+  constexpr int A_RK = (GUARD && A_KC) ? T::A_VEC : 1;
+  constexpr int B_RK = (GUARD && B_KC) ? T::B_VEC : 1;
+  u32x4 ra_kc[A_RK], rb_kc[B_RK];
+  // Outer-contiguous operands: one 8 x 8 block per lane of the loading waves.
+  u32x4 ra_t[TA ? 8 : 1], rb_t[TB ? 1 : 8];
+  const bool a_tw = wave < T::A_TW, b_tw = wave < T::B_TW;
+  const int a_to = 64 * wave + 8 * ob;  // tile-relative outer index of the block
+  const int b_to = 64 * wave + 8 * ob;
+
+  auto load_regs = [&](int kt) {
+    const int k0 = kt * T::BK;
+    if (GUARD && A_KC) {
+#pragma unroll
+      for (int v = 0; v < T::A_VEC; ++v) {
+        const int row = m0 + a_r[v], k = k0 + 8 * a_c[v];
+        ra_kc[v] = lp_load8(A + (size_t)(row < M ? row : 0) * lda + k,
+                            row < M ? K - k : 0);
+      }
+    }
+    if (GUARD && B_KC) {
+#pragma unroll
+      for (int v = 0; v < T::B_VEC; ++v) {
+        const int row = n0 + b_r[v], k = k0 + 8 * b_c[v];
+        rb_kc[v] = lp_load8(B + (size_t)(row < N ? row : 0) * ldb + k,
+                            row < N ? K - k : 0);
+      }
+    }
+    if constexpr (TA) {
+      if (a_tw) {
+        const int o = m0 + a_to;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = k0 + 8 * kb + j;
+          const uint16_t* p = A + (size_t)(k < K ? k : 0) * lda + o;
+          if (GUARD)
+            ra_t[j] = lp_load8(p, k < K ? M - o : 0);
+          else
+            ra_t[j] = *reinterpret_cast<const u32x4*>(p);
+        }
+      }
+    }
+    if constexpr (!TB) {
+      if (b_tw) {
+        const int o = n0 + b_to;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = k0 + 8 * kb + j;
+          const uint16_t* p = B + (size_t)(k < K ? k : 0) * ldb + o;
+          if (GUARD)
+            rb_t[j] = lp_load8(p, k < K ? N - o : 0);
+          else
+            rb_t[j] = *reinterpret_cast<const u32x4*>(p);
+        }
+      }
+    }
+  };
+  // Output row e of a block (its outer index 8ob + e, eight k) from the eight
+  // loaded k rows: dword d packs k = 2d (low half) and 2d + 1 (high half),
+  // each the half e & 1 of dword e / 2 of its row.
+  const unsigned sel_even = 0x05040100u, sel_odd = 0x07060302u;
+  auto store_block = [&](char* tile, const u32x4 (&in)[8], int to) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = i ^ (ob & 1);  // pair-swapped order on odd ob
+      const unsigned sel = ((i ^ ob) & 1) ? sel_odd : sel_even;
+      u32x4 out;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        out[d] = __builtin_amdgcn_perm(in[2 * d + 1][i >> 1], in[2 * d][i >> 1], sel);
+      *reinterpret_cast<u32x4*>(tile + lp_unit_off(to + e, kb)) = out;
+    }
+  };
+  auto store_regs = [&](int st) {
+    if (GUARD && A_KC) {
+#pragma unroll
+      for (int v = 0; v < T::A_VEC; ++v)
+        *reinterpret_cast<u32x4*>(lds + a_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
+            ra_kc[v];
+    }
+    if (GUARD && B_KC) {
+#pragma unroll
+      for (int v = 0; v < T::B_VEC; ++v)
+        *reinterpret_cast<u32x4*>(lds + b_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
+            rb_kc[v];
+    }
+    if constexpr (TA) {
+      if (a_tw) store_block(lds + a_off(st), ra_t, a_to);
+    }
+    if constexpr (!TB) {
+      if (b_tw) store_block(lds + b_off(st), rb_t, b_to);
+    }
+  };
+
+  // ---- MFMAs of one stage: four groups of 16 k -----------------------------
+  auto compute = [&](int st) {
+    const char* As = lds + a_off(st);
+    const char* Bs = lds + b_off(st);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 2 * q + lh;
+      u32x4 a[T::FM], b[T::FN];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+        a[i] = *reinterpret_cast<const u32x4*>(As + lp_unit_off(wm * T::WM + i * 32 + li, c));
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j)
+        b[j] = *reinterpret_cast<const u32x4*>(Bs + lp_unit_off(wn * T::WN + j * 32 + li, c));
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = lp_mfma<DT>(b[j], a[i], acc[i][j]);
+    }
+  };
+
+  auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  // No scalar load may be in flight inside the K loop (the epilogue's
+  // arguments would otherwise be fetched just before it, and a pending
+  // scalar load turns every LDS-read wait into a full lgkmcnt(0)).
+  asm volatile("" ::"s"(g.C), "s"(g.ldc), "s"(g.alpha), "s"(g.beta), "s"(M), "s"(N));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+
+  if (nk > 0) {
+    if (!GUARD) issue_direct(0, 0);
+    load_regs(0);
+    store_regs(0);
+    wait_all();
+    __syncthreads();
+  }
+  // One K step from stage st; step kt+1 goes into the other stage, whose
+  // previous contents were read before the last barrier.
+  auto step = [&](int kt, int st) {
+    const bool more = kt + 1 < nk;
+    if (more) {
+      if (!GUARD) issue_direct(kt + 1, st ^ 1);
+      load_regs(kt + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) store_regs(st ^ 1);
+    wait_all();
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
+  }
+  if (kt < nk) step(kt, 0);
+}
+
+template <class T, int DT, int MODE, bool TA, bool TB>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+    lp_gemm_kernel(LpArgs g, int tiles_m, int tiles_n, int band) {
+  __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
+  f32x16 acc[T::FM][T::FN];
+  zero_acc<T>(acc);
+  lp_tile_accumulate<T, DT, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, acc);
+  GemmArgs e;
+  e.M = g.M;
+  e.N = g.N;
+  e.K = g.K;
+  e.alpha = g.alpha;
+  e.beta = g.beta;
+  e.A = nullptr;
+  e.lda = 0;
+  e.B = nullptr;
+  e.ldb = 0;
+  e.C = g.C;
+  e.ldc = g.ldc;
+  store_tile<T, MODE>(e, tm * T::BM, tn * T::BN, acc);
+}
+
+// Tile shapes: LpTile<BM, BN, WM, WN, OCC>.
+// 4 waves of 128x128 (256 accumulators per lane), one workgroup per CU,
+// 128 KB of LDS for the two stages.
+typedef LpTile<256, 256, 128, 128, 1> L256x256;
+// 4 waves of 64x64, for problems with fewer than one 256x256 tile per CU.
+typedef LpTile<128, 128, 64, 64, 2> L128x128;
+
+}  // namespace sgemm

@@ -16,6 +16,7 @@
 #include <new>
 
 #include "diag.hpp"
+#include "lowp_gemm.hpp"
 #include "mfma_sgemm.hpp"
 #include "skinny_sgemm.hpp"
 #include "tile_map.hpp"
@@ -31,6 +32,7 @@ struct sgemm_handle_s {
   int forced_kernel; // -1 = automatic
   void* workspace;   // caller's device memory for partial sums, or null
   size_t workspace_bytes;
+  int forced_lowp;   // 16-bit product kernel, -1 = automatic
 };
 
 namespace {
@@ -564,6 +566,116 @@ int plan_out(const Plan& plan, int N, int* kernels, int* n_split) {
   return plan.count;
 }
 
+// ---- products with 16-bit A and B ------------------------------------------
+
+struct LpRun {
+  int dt;      // SGEMM_DTYPE_*
+  int ta, tb;  // A stored K x M / B stored N x K
+  int M, N, K;
+  float alpha, beta;
+  const void* A;
+  int lda;
+  const void* B;
+  int ldb;
+  float* C;
+  int ldc;
+};
+
+typedef hipError_t (*lp_launch_fn)(const LpRun&, int tiles_m, int tiles_n,
+                                   hipStream_t);
+
+struct LpKernelDesc {
+  const char* name;
+  int dt;
+  int ta, tb;
+  int bm, bn, bk;
+  int threads;
+  int mode;  // SGEMM_MODE_ALIGNED or SGEMM_MODE_GUARDED
+  lp_launch_fn launch;
+};
+
+template <class T, int DT, int MODE, bool TA, bool TB>
+hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
+  LpArgs g;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = a.K;
+  g.alpha = a.alpha;
+  g.beta = a.beta;
+  g.A = static_cast<const uint16_t*>(a.A);
+  g.lda = a.lda;
+  g.B = static_cast<const uint16_t*>(a.B);
+  g.ldb = a.ldb;
+  g.C = a.C;
+  g.ldc = a.ldc;
+  const int nwg = tiles_m * tiles_n;
+  hipLaunchKernelGGL((lp_gemm_kernel<T, DT, MODE, TA, TB>), dim3(nwg),
+                     dim3(T::THREADS), 0, s, g, tiles_m, tiles_n,
+                     band_rows(tiles_m, nwg));
+  return hipGetLastError();
+}
+
+#define LP_ONE(T, DT, DTAG, STAG, TA, TB, MODE, MTAG)                        \
+  {"lp_" DTAG "_" #T "_" STAG MTAG, DT, TA, TB, T::BM, T::BN, T::BK,        \
+   T::THREADS, MODE, launch_lp<T, DT, MODE, TA, TB>}
+#define LP_STORAGE(T, DT, DTAG, MODE, MTAG)                                  \
+  LP_ONE(T, DT, DTAG, "", false, false, MODE, MTAG),                         \
+  LP_ONE(T, DT, DTAG, "tn_", true, false, MODE, MTAG),                       \
+  LP_ONE(T, DT, DTAG, "nt_", false, true, MODE, MTAG),                       \
+  LP_ONE(T, DT, DTAG, "tt_", true, true, MODE, MTAG)
+#define LP_FORMAT(DT, DTAG)                                                  \
+  LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
+  LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
+  LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),             \
+  LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_GUARDED, "guarded")
+
+const LpKernelDesc kLpKernels[] = {
+    LP_FORMAT(SGEMM_DTYPE_BF16, "bf16"),
+    LP_FORMAT(SGEMM_DTYPE_F16, "f16"),
+};
+constexpr int kNumLpKernels = sizeof(kLpKernels) / sizeof(kLpKernels[0]);
+
+// Direct loads of a K-contiguous operand: the farthest byte of one K step of
+// a tile must lie within 4 GiB of the tile's origin.
+bool lp_offsets_fit(const LpKernelDesc& k, const LpRun& a) {
+  const long long a_far = (long long)(k.bm - 1) * a.lda + k.bk;
+  const long long b_far = (long long)(k.bn - 1) * a.ldb + k.bk;
+  return (a.ta || 2 * a_far < (1LL << 32)) && (!a.tb || 2 * b_far < (1LL << 32));
+}
+
+bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
+  if (k.dt != a.dt || k.ta != a.ta || k.tb != a.tb) return false;
+  if (ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn) > INT_MAX) return false;
+  if (k.mode == SGEMM_MODE_GUARDED) return true;
+  return a.K > 0 && a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
+         a.lda % 8 == 0 && a.ldb % 8 == 0 && ptr_aligned16(a.A) &&
+         ptr_aligned16(a.B) && lp_offsets_fit(k, a);
+}
+
+// The kernel for these arguments: the 256x256 tile when it gives every CU
+// of the chip a tile, else the 128x128 tile; the aligned instance when it
+// fits, else the guarded one.
+int lp_select(const LpRun& a, int cus) {
+  const bool big = ceil_div(a.M, 256) * ceil_div(a.N, 256) >= cus;
+  int best = -1;
+  for (int id = 0; id < kNumLpKernels; ++id) {
+    const LpKernelDesc& k = kLpKernels[id];
+    if (!lp_fits(k, a) || (k.bm == 256) != big) continue;
+    if (best < 0 || (k.mode == SGEMM_MODE_ALIGNED &&
+                     kLpKernels[best].mode != SGEMM_MODE_ALIGNED))
+      best = id;
+  }
+  return best;
+}
+
+Range window_bytes(const void* p, int rows, int cols, int ld, unsigned elem) {
+  Range r = {0, 0};
+  if (p == nullptr || rows <= 0 || cols <= 0) return r;
+  r.lo = reinterpret_cast<uintptr_t>(p);
+  r.hi = r.lo + ((uintptr_t)(rows - 1) * (uintptr_t)ld + (uintptr_t)cols) * elem;
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -743,6 +855,7 @@ int sgemm_create(sgemm_handle_t* out) {
   h->forced_kernel = -1;
   h->workspace = nullptr;
   h->workspace_bytes = 0;
+  h->forced_lowp = -1;
   *out = h;
   return SGEMM_OK;
 }
@@ -801,6 +914,102 @@ int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
               float* C, int ldc, hipStream_t stream) {
   return sgemm_run_ex(h, SGEMM_OP_N, SGEMM_OP_N, M, N, K, alpha, A, lda, B,
                       ldb, beta, C, ldc, stream);
+}
+
+// ---- products with 16-bit A and B ------------------------------------------
+
+int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
+                        const void* A, int lda, const void* B, int ldb,
+                        float beta, const float* C, int ldc) {
+  if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_ERR_VALUE;
+  if ((transa != SGEMM_OP_N && transa != SGEMM_OP_T) ||
+      (transb != SGEMM_OP_N && transb != SGEMM_OP_T))
+    return SGEMM_ERR_VALUE;
+  if (M < 0 || N < 0 || K < 0) return SGEMM_ERR_SIZE;
+  const int a_rows = transa ? K : M, a_cols = transa ? M : K;
+  const int b_rows = transb ? N : K, b_cols = transb ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+      ldc < (N > 1 ? N : 1))
+    return SGEMM_ERR_LD;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  if (C == nullptr) return SGEMM_ERR_NULL;
+  if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_NULL;
+  if (K > 0 && (((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 1u) != 0))
+    return SGEMM_ERR_VALUE;
+  const Range rc = window_bytes(C, M, N, ldc, 4);
+  if (K > 0 && (overlap(rc, window_bytes(A, a_rows, a_cols, lda, 2)) ||
+                overlap(rc, window_bytes(B, b_rows, b_cols, ldb, 2))))
+    return SGEMM_ERR_ALIAS;
+  (void)beta;
+  return SGEMM_OK;
+}
+
+int sgemm_lowp_num_kernels(void) { return kNumLpKernels; }
+
+const char* sgemm_lowp_kernel_name(int id) {
+  return id >= 0 && id < kNumLpKernels ? kLpKernels[id].name : nullptr;
+}
+
+int sgemm_lowp_kernel_info(int id, int* dtype, int* bm, int* bn, int* bk,
+                           int* threads, int* mode, int* transa, int* transb) {
+  if (id < 0 || id >= kNumLpKernels) return SGEMM_ERR_VALUE;
+  const LpKernelDesc& k = kLpKernels[id];
+  if (dtype) *dtype = k.dt;
+  if (bm) *bm = k.bm;
+  if (bn) *bn = k.bn;
+  if (bk) *bk = k.bk;
+  if (threads) *threads = k.threads;
+  if (mode) *mode = k.mode;
+  if (transa) *transa = k.ta;
+  if (transb) *transb = k.tb;
+  return SGEMM_OK;
+}
+
+int sgemm_lowp_select_kernel(int dtype, int transa, int transb, int M, int N,
+                             int K, const void* A, int lda, const void* B,
+                             int ldb, const float* C, int ldc) {
+  const int st = sgemm_validate_lowp(dtype, transa, transb, M, N, K, A, lda, B,
+                                     ldb, 0.0f, C, ldc);
+  if (st != SGEMM_OK) return st;
+  const LpRun a = {dtype, transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
+                   const_cast<float*>(C), ldc};
+  const int id = lp_select(a, kChipCus);
+  return id >= 0 ? id : SGEMM_ERR_UNSUPPORTED;
+}
+
+int sgemm_set_lowp_kernel(sgemm_handle_t h, int kernel_id) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  if (kernel_id < -1 || kernel_id >= kNumLpKernels) return SGEMM_ERR_VALUE;
+  h->forced_lowp = kernel_id;
+  return SGEMM_OK;
+}
+
+int sgemm_run_lowp(sgemm_handle_t h, int dtype, int transa, int transb, int M,
+                   int N, int K, float alpha, const void* A, int lda,
+                   const void* B, int ldb, float beta, float* C, int ldc,
+                   hipStream_t stream) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  const int st = sgemm_validate_lowp(dtype, transa, transb, M, N, K, A, lda, B,
+                                     ldb, beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  const LpRun a = {dtype, transa, transb, M, N, K, alpha, beta, A, lda, B, ldb,
+                   C, ldc};
+  int id = h->forced_lowp;
+  if (id >= 0) {
+    if (!lp_fits(kLpKernels[id], a)) return SGEMM_ERR_UNSUPPORTED;
+  } else {
+    id = lp_select(a, h->cus);
+    if (id < 0) return SGEMM_ERR_UNSUPPORTED;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return SGEMM_ERR_DEVICE;
+  const LpKernelDesc& k = kLpKernels[id];
+  if (k.launch(a, (int)ceil_div(M, k.bm), (int)ceil_div(N, k.bn), stream) !=
+      hipSuccess)
+    return SGEMM_ERR_HIP;
+  return SGEMM_OK;
 }
 
 }  // extern "C"

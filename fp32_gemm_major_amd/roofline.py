@@ -17,6 +17,10 @@ FP32 = 4  # bytes
 # matrix cores; packed FP32 vector FMA has the same peak), and HBM3E.
 PEAK_FP32_FLOPS = 157.3e12
 PEAK_FP32_VALU_UNPACKED_FLOPS = PEAK_FP32_FLOPS / 2  # one FMA per lane per clock
+# Dense (no sparsity) matrix-core peaks for 16-bit inputs with FP32
+# accumulation: bfloat16 and binary16 alike.
+PEAK_BF16_FLOPS = 2.5e15
+PEAK_F16_FLOPS = 2.5e15
 PEAK_HBM_BYTES = 8.0e12
 CUS = 256
 CLOCK_HZ = 2.4e9
@@ -26,10 +30,11 @@ def flops(M: int, N: int, K: int) -> int:
     return 2 * M * N * K
 
 
-def alg_bytes(M: int, N: int, K: int, beta: float) -> int:
-    """Least HBM traffic: A and B read once, C written (and read if beta != 0)."""
+def alg_bytes(M: int, N: int, K: int, beta: float, ab_bytes: int = FP32) -> int:
+    """Least HBM traffic: A and B read once (``ab_bytes`` per element: 2 for
+    16-bit operands), FP32 C written (and read if beta != 0)."""
     c_passes = 2 if beta != 0 else 1
-    return FP32 * (M * K + K * N + c_passes * M * N)
+    return ab_bytes * (M * K + K * N) + FP32 * c_passes * M * N
 
 
 def arithmetic_intensity(M: int, N: int, K: int, beta: float) -> float:

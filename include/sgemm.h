@@ -249,6 +249,68 @@ void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
 int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
                           hipStream_t stream);
 
+/* ---- products with 16-bit A and B ------------------------------------------
+ *
+ * Operation (the gsyq.cn GEMM guide, section 5.1: matrix units multiply
+ * 16-bit inputs and accumulate in FP32):
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * with A and B stored in a 16-bit format (dtype) and C, alpha, beta FP32.
+ * Storage, leading dimensions (in elements), transa / transb, the M x N
+ * window of C, the beta == 0 and K == 0 conventions and the determinism of
+ * sgemm_run_ex hold unchanged.  A and B hold bit patterns: SGEMM_DTYPE_BF16
+ * is bfloat16 (the upper half of an IEEE binary32), SGEMM_DTYPE_F16 IEEE
+ * binary16.  Every product of two such values is exact in FP32, so the
+ * accuracy statement of sgemm_run holds as it is: |C - exact| <=
+ * 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj| + |beta*c_ij|) against the
+ * exact product of the stored 16-bit values.  Infinities and NaNs in A or B
+ * propagate as the matrix unit's FP32 arithmetic makes them; finite inputs
+ * whose products or sums overflow FP32 give infinities.
+ *
+ * Memory: A and B are device pointers to 2-byte elements, at least 2-byte
+ * aligned (SGEMM_ERR_VALUE otherwise); the fastest kernels need 16-byte
+ * aligned A and B with lda and ldb multiples of 8, and M, N multiples of 128
+ * and K of 64 (other arguments run the guarded kernels).  Ownership, streams,
+ * errors and threading as for sgemm_run. */
+enum sgemm_dtype {
+  SGEMM_DTYPE_BF16 = 1,
+  SGEMM_DTYPE_F16 = 2
+};
+
+/* Enqueue the 16-bit product on `stream` and return without waiting.
+ * SGEMM_ERR_VALUE for an unknown dtype or storage flag or a misaligned A or
+ * B; other statuses as sgemm_run_ex. */
+int sgemm_run_lowp(sgemm_handle_t h, int dtype, int transa, int transb, int M,
+                   int N, int K, float alpha, const void* A, int lda,
+                   const void* B, int ldb, float beta, float* C, int ldc,
+                   hipStream_t stream);
+
+/* The argument checks of sgemm_run_lowp (host only, no HIP call). */
+int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
+                        const void* A, int lda, const void* B, int ldb,
+                        float beta, const float* C, int ldc);
+
+/* Kernel table of the 16-bit product (ids 0 .. sgemm_lowp_num_kernels()-1).
+ * *mode is SGEMM_MODE_ALIGNED or SGEMM_MODE_GUARDED; bk = 64. */
+int sgemm_lowp_num_kernels(void);
+const char* sgemm_lowp_kernel_name(int kernel_id); /* NULL for a bad id */
+int sgemm_lowp_kernel_info(int kernel_id, int* dtype, int* bm, int* bn,
+                           int* bk, int* threads, int* mode, int* transa,
+                           int* transb);
+
+/* The kernel sgemm_run_lowp picks for these arguments on a 256-CU device, or
+ * a negative status.  Pure function of its inputs. */
+int sgemm_lowp_select_kernel(int dtype, int transa, int transb, int M, int N,
+                             int K, const void* A, int lda, const void* B,
+                             int ldb, const float* C, int ldc);
+
+/* Force one 16-bit product kernel on this handle (kernel_id >= 0) or go back
+ * to automatic selection (-1).  A forced kernel whose mode, format or
+ * storage cannot take the arguments makes sgemm_run_lowp return
+ * SGEMM_ERR_UNSUPPORTED. */
+int sgemm_set_lowp_kernel(sgemm_handle_t h, int kernel_id);
+
 /* ---- handle options ----------------------------------------------------- */
 
 /* Choose the kernel family used by sgemm_run on this handle. */

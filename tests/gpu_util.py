@@ -107,3 +107,66 @@ def edge_rows(M, extra=12, seed=1):
     rng = np.random.default_rng(seed)
     base |= set(int(x) for x in rng.integers(0, M, extra))
     return sorted(x for x in base if 0 <= x < M)
+
+
+# ---- products with 16-bit A and B -------------------------------------------
+
+def to_device16(ops: wl.Operands16):
+    """A and B as bfloat16 / float16 device tensors holding the given bit
+    patterns; C as float32."""
+    dev = torch.device("cuda", 0)
+    t16 = torch.bfloat16 if ops.dt == "bf16" else torch.float16
+
+    def half(bits):
+        if not bits.size:
+            return torch.empty(8, dtype=t16, device=dev)
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(t16)
+
+    C = torch.from_numpy(ops.C).to(dev) if ops.C.size else torch.empty(1, device=dev)
+    return half(ops.A), half(ops.B), C
+
+
+def run16(h: sg.Handle, ops: wl.Operands16, dev=None, stream=None):
+    """Run the 16-bit product on the GPU; returns the whole C buffer (flat numpy)."""
+    A, B, C = dev if dev is not None else to_device16(ops)
+    h.gemm_lowp(A, B, C, ops.alpha, ops.beta, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
+                ldb=ops.ldb, ldc=ops.ldc, stream=stream, transa=ops.ta, transb=ops.tb)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()[: ops.C.size].copy()
+
+
+def check_full16(ops: wl.Operands16, out_flat, exact=False, what=""):
+    """The whole M x N window against the 16-bit oracle; C padding untouched."""
+    M, N, K = ops.M, ops.N, ops.K
+    R, T = oracle.gemm_lowp(ops.dt, M, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb,
+                            ops.beta, ops.C, ops.ldc, ta=ops.ta, tb=ops.tb)
+    got = window(out_flat, M, N, ops.ldc)
+    c_in = window(ops.C, M, N, ops.ldc)
+    worst = check(got, R, T, K, ops.alpha, ops.beta, c_in, exact, what)
+    if ops.ldc > N and M:
+        pad_in = ops.C[: M * ops.ldc].reshape(M, ops.ldc)[:, N:]
+        pad_out = out_flat[: M * ops.ldc].reshape(M, ops.ldc)[:, N:]
+        assert np.array_equal(pad_in.view(np.uint32), pad_out.view(np.uint32)), \
+            f"{what}: C padding was written"
+    return worst
+
+
+def check_sampled16(ops: wl.Operands16, out_flat, rows, cols, npoints=4096, seed=0,
+                    exact=False, what=""):
+    """Full rows ``rows``, full columns ``cols`` and random points of the
+    16-bit product, each from the oracle's point mode."""
+    M, N, K = ops.M, ops.N, ops.K
+    got_all = window(out_flat, M, N, ops.ldc)
+    c_all = window(ops.C, M, N, ops.ldc)
+    rng = np.random.default_rng(seed)
+    rows = np.asarray(sorted(set(int(x) for x in rows)), np.int64)
+    cols = np.asarray(sorted(set(int(x) for x in cols)), np.int64)
+    pr = np.concatenate([np.repeat(rows, N), np.repeat(np.arange(M), len(cols)),
+                         rng.integers(0, M, npoints)])
+    pc = np.concatenate([np.tile(np.arange(N), len(rows)), np.tile(cols, M),
+                         rng.integers(0, N, npoints)])
+    r, t = oracle.gemm_lowp_points(ops.dt, M, N, K, ops.alpha, ops.A, ops.lda, ops.B,
+                                   ops.ldb, ops.beta, ops.C, ops.ldc, pr, pc, ta=ops.ta,
+                                   tb=ops.tb)
+    return check(got_all[pr, pc], r, t, K, ops.alpha, ops.beta, c_all[pr, pc], exact,
+                 what + " points")

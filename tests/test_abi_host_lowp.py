@@ -1,0 +1,100 @@
+"""Host-side checks of the 16-bit product's C ABI (no GPU, nothing launched)."""
+import pytest
+
+import fp32_gemm_major_amd as sg
+
+BF16, F16 = sg.SGEMM_DTYPE_BF16, sg.SGEMM_DTYPE_F16
+
+
+def test_validate_lowp():
+    v = sg.sgemm_validate_lowp
+    A, B, C = 0x10000, 0x20000, 0x40000  # disjoint fake addresses (never touched)
+    ok = sg.SGEMM_OK
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == ok
+    assert v(F16, 1, 1, 4, 5, 6, A, 4, B, 6, 0.0, C, 5) == ok
+    assert v(0, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(3, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(BF16, 2, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(BF16, 0, 0, -1, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_SIZE
+    assert v(BF16, 0, 0, 4, 5, 6, A, 5, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD
+    assert v(BF16, 1, 0, 4, 5, 6, A, 3, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD  # K x M: lda >= M
+    assert v(BF16, 0, 1, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD  # N x K: ldb >= K
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 4) == sg.SGEMM_ERR_LD
+    assert v(BF16, 0, 0, 4, 5, 6, None, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_NULL
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, None, 5) == sg.SGEMM_ERR_NULL
+    assert v(BF16, 0, 0, 4, 5, 0, None, 1, None, 5, 1.0, C, 5) == ok  # K == 0
+    assert v(BF16, 0, 0, 0, 5, 6, None, 6, None, 5, 1.0, None, 5) == ok  # empty
+    # 2-byte elements must be 2-byte aligned
+    assert v(BF16, 0, 0, 4, 5, 6, A + 1, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(F16, 0, 0, 4, 5, 6, A, 6, B + 3, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(F16, 0, 0, 4, 5, 6, A + 2, 6, B + 6, 5, 0.0, C, 5) == ok
+    # overlap is measured in bytes: A spans 4*6 two-byte elements
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, A + 46, 5) == sg.SGEMM_ERR_ALIAS
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, A + 48, 5) == ok
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, B + 2 * 29, 5) == sg.SGEMM_ERR_ALIAS
+    assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, B + 2 * 30, 5) == ok
+
+
+def test_null_handle():
+    lib = sg.library()
+    assert lib.sgemm_run_lowp(None, BF16, 0, 0, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 4096, 4,
+                              None) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_set_lowp_kernel(None, 0) == sg.SGEMM_ERR_HANDLE
+
+
+def test_kernel_table():
+    t = sg.lowp_kernel_table()
+    names = [k["name"] for k in t]
+    assert len(set(names)) == len(names) == sg.sgemm_lowp_num_kernels()
+    combos = {(k["dtype"], k["transa"], k["transb"], k["bm"], k["mode"]) for k in t}
+    for dt in (BF16, F16):
+        for ta in (0, 1):
+            for tb in (0, 1):
+                for bm in (128, 256):
+                    for mode in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_GUARDED):
+                        assert (dt, ta, tb, bm, mode) in combos
+    for k in t:
+        assert k["bk"] == 64 and k["threads"] == 256 and k["bm"] == k["bn"]
+        assert ("bf16" in k["name"]) == (k["dtype"] == BF16)
+    assert sg.sgemm_lowp_kernel_name(-1) is None
+    assert sg.sgemm_lowp_kernel_name(len(t)) is None
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_lowp_kernel_info(len(t))
+
+
+def _pick(dt, M, N, K, lda=None, ldb=None, ta=0, tb=0, A=1 << 20, B=1 << 33,
+          C=1 << 38):
+    lda = lda or (M if ta else K)
+    ldb = ldb or (K if tb else N)
+    kid = sg.sgemm_lowp_select_kernel(dt, ta, tb, M, N, K, A, lda, B, ldb, C, N)
+    return sg.sgemm_lowp_kernel_info(kid) if kid >= 0 else kid
+
+
+@pytest.mark.parametrize("dt", [BF16, F16])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_select(dt, ta, tb):
+    k = _pick(dt, 4096, 4096, 4096, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"], k["dtype"]) == (256, sg.SGEMM_MODE_ALIGNED, dt)
+    assert (k["transa"], k["transb"]) == (ta, tb)
+    k = _pick(dt, 1024, 1024, 1024, ta=ta, tb=tb)  # 16 tiles of 256: use 128
+    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_ALIGNED)
+    k = _pick(dt, 1000, 1500, 777, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_GUARDED)
+    k = _pick(dt, 4100, 4100, 4100, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (256, sg.SGEMM_MODE_GUARDED)
+    # leading dimensions that are not multiples of 8 or a base off 16 bytes
+    k = _pick(dt, 4096, 4096, 4096, lda=4100, ta=ta, tb=tb)
+    assert k["mode"] == sg.SGEMM_MODE_GUARDED
+    k = _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 8, ta=ta, tb=tb)
+    assert k["mode"] == sg.SGEMM_MODE_GUARDED
+    assert _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 1) == sg.SGEMM_ERR_VALUE
+
+
+def test_huge_strides_go_to_the_guarded_kernel():
+    """A K-contiguous operand whose tile spans more than 4 GiB cannot use the
+    32-bit lane offsets of the direct loads."""
+    k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8)
+    assert k["mode"] == sg.SGEMM_MODE_GUARDED
+    # the transposed-storage operand does not use direct loads: no limit there
+    k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8, ta=1)
+    assert k["mode"] == sg.SGEMM_MODE_ALIGNED

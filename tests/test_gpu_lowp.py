@@ -1,0 +1,200 @@
+"""Parity of the HIP product with 16-bit A and B (bfloat16 / binary16) and
+FP32 C, through the C ABI, with the FP64 CPU oracle on the same 16-bit
+patterns (the gsyq.cn guide, section 5.1: 16-bit inputs, FP32 accumulation).
+
+Acceptance is that of the FP32 product: every product of two 16-bit values
+is exact in FP32, so |C_gpu - r| <= 4*max(K,1)*2^-24*(|alpha|*t + |beta*c|)
+elementwise against the unrounded FP64 r of the stored 16-bit values, and
+bit-exact results for integer inputs (every partial sum an integer below
+2^24, which an accumulator narrower than FP32 would not keep at these K).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import fp32_gemm_major_amd as sg  # noqa: E402
+from fp32_gemm_major_amd import workloads as wl  # noqa: E402
+from tests import gpu_util as gu  # noqa: E402
+
+W = wl.WORKLOADS
+FORMATS = wl.FORMATS16
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    h = sg.Handle(workspace=False)
+    yield h
+    h.close()
+
+
+@pytest.fixture(autouse=True)
+def _auto_kernel(handle):
+    handle.set_lowp_kernel(-1)
+    yield
+    handle.set_lowp_kernel(-1)
+
+
+KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.lowp_kernel_table()
+DT_NAME = {sg.SGEMM_DTYPE_BF16: "bf16", sg.SGEMM_DTYPE_F16: "f16"}
+
+
+@pytest.mark.parametrize("k", KERNELS, ids=[k["name"] for k in KERNELS])
+@pytest.mark.parametrize("dist", ["uniform", "int4"])
+def test_each_kernel(handle, k, dist):
+    """Every kernel of the table on a problem of several tiles (guarded
+    kernels: ragged sizes, odd leading dimensions, a partial K step)."""
+    handle.set_lowp_kernel(k["id"])
+    ta, tb = bool(k["transa"]), bool(k["transb"])
+    if k["mode"] == sg.SGEMM_MODE_ALIGNED:
+        M, N, K = 2 * k["bm"], 3 * k["bn"], 4 * k["bk"]
+        pad_a, pad_b, ldc = 8, 16, N + 4
+    else:
+        M, N, K = 2 * k["bm"] + 37, k["bn"] + 19, 3 * k["bk"] + 5
+        pad_a, pad_b, ldc = 3, 1, N + 5
+    lda = (M if ta else K) + pad_a
+    ldb = (K if tb else N) + pad_b
+    w = wl.Workload("case", 700 + k["id"], M, N, K, 1.5, 0.5, dist)
+    ops = wl.operands16(w, DT_NAME[k["dtype"]], lda=lda, ldb=ldb, ldc=ldc, ta=ta, tb=tb)
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, exact=(dist == "int4"), what=k["name"])
+
+
+# ---- the benchmark's workloads with 16-bit A and B ---------------------------
+
+@pytest.mark.parametrize("dt", FORMATS)
+@pytest.mark.parametrize("name", ["c1_128", "c1_128_int", "c2_1024", "c4_edge",
+                                  "c4_edge_int"])
+def test_small_workloads_full(handle, dt, name):
+    ops = wl.operands16(W[name], dt)
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, exact=W[name].dist == "int4", what=f"{name} {dt}")
+
+
+@pytest.mark.parametrize("dt", FORMATS)
+@pytest.mark.parametrize("name", ["c3_4096", "c3_4096_int", "c5_mlp"])
+def test_large_workloads_sampled(handle, dt, name):
+    ops = wl.operands16(W[name], dt)
+    out = gu.run16(handle, ops)
+    rows = gu.edge_rows(ops.M, extra=4)[:10]
+    cols = [0, 1, 127, 128, 255, 256, ops.N // 2, ops.N - 1]
+    gu.check_sampled16(ops, out, rows, cols, exact=W[name].dist == "int4",
+                       what=f"{name} {dt}")
+
+
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)],
+                         ids=["tn", "nt", "tt"])
+@pytest.mark.parametrize("dt", FORMATS)
+def test_transposed_4096_sampled(handle, dt, ta, tb):
+    ops = wl.operands16(W["c3_4096"], dt, ta=ta, tb=tb)
+    out = gu.run16(handle, ops)
+    gu.check_sampled16(ops, out, [0, 255, 256, 2047, 4095], [0, 256, 4095],
+                       npoints=2048, what=f"4096 {dt} ta={ta} tb={tb}")
+
+
+# ---- edge cases ----------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", FORMATS)
+def test_tiny_sizes_integer_exact(handle, dt):
+    rng = np.random.default_rng(61)
+    for case in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 71, size=3))
+        ta, tb = bool(case & 1), bool(case & 2)
+        w = wl.Workload("tiny", 3000 + case, M, N, K, 1.0, 1.0, "int4")
+        ops = wl.operands16(w, dt, ta=ta, tb=tb)
+        out = gu.run16(handle, ops)
+        gu.check_full16(ops, out, exact=True, what=f"tiny {dt} {M}x{N}x{K} {ta}{tb}")
+
+
+@pytest.mark.parametrize("dt", FORMATS)
+def test_nan_c_with_beta_zero(handle, dt):
+    ops = wl.operands16(W["c2_1024"], dt, M=300, N=260, K=200)
+    assert np.isnan(ops.C).all()
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, what="beta 0 with NaN C")
+
+
+@pytest.mark.parametrize("dt", FORMATS)
+def test_k_zero_and_empty(handle, dt):
+    w = W["c4_edge"]
+    ops = wl.operands16(w, dt, M=70, N=50, K=0, ldc=53)
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, what="K = 0")  # C = beta * C
+    for M, N in ((0, 50), (70, 0)):
+        ops = wl.operands16(w, dt, M=M, N=N, K=16)
+        A, B, C = gu.to_device16(ops)
+        before = C.clone()
+        handle.gemm_lowp(A, B, C, 1.0, 1.0, M=M, N=N, K=16, lda=ops.lda, ldb=ops.ldb,
+                         ldc=ops.ldc)
+        torch.cuda.synchronize()
+        assert torch.equal(before.view(torch.int32), C.view(torch.int32))
+
+
+@pytest.mark.parametrize("dt", FORMATS)
+def test_misaligned_operands_and_sentinels(handle, dt):
+    """A and B starting one element past a 16-byte boundary, odd leading
+    dimensions and padded C: the guarded kernels, element loads, untouched
+    C padding (NaN-filled padding in A and B never reaches an output)."""
+    w = wl.Workload("mis", 77, 300, 270, 150, 1.25, -0.5, "uniform")
+    ops = wl.operands16(w, dt, lda=151, ldb=273, ldc=275)
+    A, B, C = gu.to_device16(ops)
+    t16 = A.dtype
+    A1 = torch.empty(A.numel() + 1, dtype=t16, device=A.device)
+    A1[1:] = A
+    B1 = torch.empty(B.numel() + 1, dtype=t16, device=B.device)
+    B1[1:] = B
+    out = gu.run16(handle, ops, dev=(A1[1:], B1[1:], C))
+    gu.check_full16(ops, out, what="misaligned")
+
+
+@pytest.mark.parametrize("dt", FORMATS)
+def test_alpha_zero_beta_one_keeps_c(handle, dt):
+    w = wl.Workload("keep", 78, 256, 256, 128, 0.0, 1.0, "uniform")
+    ops = wl.operands16(w, dt)
+    out = gu.run16(handle, ops)
+    assert np.array_equal(out, ops.C)
+
+
+def test_deterministic(handle):
+    ops = wl.operands16(W["c4_edge"], "bf16")
+    dev = gu.to_device16(ops)
+    c0 = dev[2].clone()
+    first = gu.run16(handle, ops, dev=dev)
+    for _ in range(3):
+        dev[2].copy_(c0)
+        again = gu.run16(handle, ops, dev=dev)
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+def test_forced_kernel_that_cannot_run(handle):
+    aligned = [k for k in KERNELS if k["mode"] == sg.SGEMM_MODE_ALIGNED and
+               k["dtype"] == sg.SGEMM_DTYPE_BF16 and not k["transa"] and
+               not k["transb"]][0]
+    handle.set_lowp_kernel(aligned["id"])
+    ops = wl.operands16(W["c4_edge"], "bf16")
+    A, B, C = gu.to_device16(ops)
+    with pytest.raises(sg.SgemmError) as e:
+        handle.gemm_lowp(A, B, C, 1.0, 1.0, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
+                         ldb=ops.ldb, ldc=ops.ldc)
+    assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+    # the wrong format is unsupported too
+    f16 = [k for k in KERNELS if k["dtype"] == sg.SGEMM_DTYPE_F16][0]
+    handle.set_lowp_kernel(f16["id"])
+    with pytest.raises(sg.SgemmError):
+        handle.gemm_lowp(A, B, C, 1.0, 1.0, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
+                         ldb=ops.ldb, ldc=ops.ldc)
+
+
+def test_torch_tensor_shapes(handle):
+    """2-D tensors give sizes and leading dimensions; the result matches the
+    oracle on the same values."""
+    ops = wl.operands16(W["c4_edge"], "f16", M=200, N=136, K=96)
+    A, B, C = gu.to_device16(ops)
+    A2, B2, C2 = A.view(200, 96), B.view(96, 136), C.view(200, 136)
+    handle.gemm_lowp(A2, B2, C2, ops.alpha, ops.beta)
+    torch.cuda.synchronize()
+    gu.check_full16(ops, C.cpu().numpy(), what="2-D tensors")
