@@ -224,6 +224,10 @@ def lowp_section(args, sg, rf, wl, torch):
             "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta, ab_bytes=2),
             "flops_per_launch": rf.flops(w.M, w.N, w.K),
             "launches": steps,
+            # sustained rate of a 16-bit MFMA chain with no memory traffic
+            "mfma_chain_tflops": round(sg.mfma_chain_tflops(
+                iterations=1024, dtype=sg.SGEMM_DTYPE_BF16 if dt == "bf16"
+                else sg.SGEMM_DTYPE_F16), 1),
         }}
         del dev
         per_config = {}

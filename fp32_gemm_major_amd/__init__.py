@@ -53,7 +53,7 @@ EXPORTED = [
     "sgemm_set_workspace", "sgemm_workspace_size", "sgemm_plan_handle",
     "sgemm_kernel_schedule", "sgemm_run_lowp", "sgemm_validate_lowp",
     "sgemm_lowp_num_kernels", "sgemm_lowp_kernel_name", "sgemm_lowp_kernel_info",
-    "sgemm_lowp_select_kernel", "sgemm_set_lowp_kernel",
+    "sgemm_lowp_select_kernel", "sgemm_set_lowp_kernel", "sgemm_diag_mfma_chain_lowp",
 ]
 
 
@@ -101,7 +101,8 @@ def _bind(lib):
     lib.sgemm_lowp_kernel_info.argtypes = [i, ip, ip, ip, ip, ip, ip, ip, ip]
     lib.sgemm_lowp_select_kernel.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i]
     lib.sgemm_set_lowp_kernel.argtypes = [p, i]
-    for name in ("sgemm_run_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
+    lib.sgemm_diag_mfma_chain_lowp.argtypes = [i, i, i, p, p]
+    for name in ("sgemm_run_lowp", "sgemm_diag_mfma_chain_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
                  "sgemm_lowp_kernel_info", "sgemm_lowp_select_kernel",
                  "sgemm_set_lowp_kernel"):
         getattr(lib, name).restype = i
@@ -311,22 +312,42 @@ def sgemm_diag_mfma_chain(workgroups, iterations, out, stream=0) -> int:
 CHAIN_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 2  # eight 32x32x2 MFMAs
 
 
-def mfma_chain_tflops(workgroups=1024, iterations=4096, reps=3):
-    """Sustained FP32 MFMA TFLOP/s of the device (best of ``reps`` timed runs)."""
+def sgemm_diag_mfma_chain_lowp(dtype, workgroups, iterations, out, stream=0) -> int:
+    return _check(library().sgemm_diag_mfma_chain_lowp(dtype, workgroups, iterations,
+                                                       out, stream),
+                  "sgemm_diag_mfma_chain_lowp")
+
+
+CHAIN16_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 16  # eight 32x32x16 MFMAs
+
+
+def mfma_chain_tflops(workgroups=1024, iterations=4096, reps=3, dtype=None):
+    """Sustained MFMA TFLOP/s of the device (best of ``reps`` timed runs):
+    FP32 32x32x2 by default, or the 16-bit 32x32x16 instruction of ``dtype``
+    (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16)."""
     out = torch.empty(workgroups * 256, device="cuda")
     stream = torch.cuda.current_stream()
-    sgemm_diag_mfma_chain(workgroups, iterations, out.data_ptr(), stream.cuda_stream)
+
+    def run():
+        if dtype is None:
+            sgemm_diag_mfma_chain(workgroups, iterations, out.data_ptr(),
+                                  stream.cuda_stream)
+        else:
+            sgemm_diag_mfma_chain_lowp(dtype, workgroups, iterations, out.data_ptr(),
+                                       stream.cuda_stream)
+    run()
     best = None
     for _ in range(reps):
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
-        sgemm_diag_mfma_chain(workgroups, iterations, out.data_ptr(), stream.cuda_stream)
+        run()
         e.record()
         torch.cuda.synchronize()
         ms = s.elapsed_time(e)
         best = ms if best is None else min(best, ms)
-    flops = CHAIN_FLOPS_PER_WAVE_ITER * iterations * workgroups * 4
+    per = CHAIN_FLOPS_PER_WAVE_ITER if dtype is None else CHAIN16_FLOPS_PER_WAVE_ITER
+    flops = per * iterations * workgroups * 4
     return flops / (best * 1e-3) / 1e12
 
 

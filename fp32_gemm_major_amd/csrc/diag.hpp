@@ -30,4 +30,38 @@ __global__ void __launch_bounds__(kChainThreads)
   out[blockIdx.x * kChainThreads + threadIdx.x] = s;
 }
 
+// The same chain for 16-bit inputs: v_mfma_f32_32x32x16_bf16 (DT16 = 1) or
+// v_mfma_f32_32x32x16_f16 (DT16 = 2), 32768 flops per MFMA per wave.
+template <int DT16>
+__global__ void __launch_bounds__(kChainThreads)
+    mfma_chain16_kernel(float* __restrict__ out, int iters) {
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  f32x16_t acc[kChainAcc];
+#pragma unroll
+  for (int i = 0; i < kChainAcc; ++i) acc[i] = f32x16_t(0.0f);
+  // small finite values in both formats (0x3C00 + lane bits: about 1)
+  const unsigned w = 0x3C003C00u | (threadIdx.x & 7u);
+  const u32x4_t x = {w, w, w, w};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < kChainAcc; ++i) {
+      if constexpr (DT16 == 1)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, x), __builtin_bit_cast(bf16x8_t, x), acc[i], 0,
+            0, 0);
+      else
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+            __builtin_bit_cast(f16x8_t, x), __builtin_bit_cast(f16x8_t, x), acc[i], 0, 0,
+            0);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kChainAcc; ++i) s += acc[i][threadIdx.x & 15];
+  out[blockIdx.x * kChainThreads + threadIdx.x] = s;
+}
+
 }  // namespace sgemm

@@ -49,6 +49,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mfma_sgemm.hpp"
 #include "tile_map.hpp"
 
@@ -184,21 +186,6 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   }
   const uint16_t* a_kc_base = A + (size_t)m0 * lda;  // used when A_KC
   const uint16_t* b_kc_base = B + (size_t)n0 * ldb;  // used when B_KC
-  auto issue_direct = [&](int kt, int st) {
-    if (A_KC) {
-#pragma unroll
-      for (int v = 0; v < T::A_VEC; ++v)
-        dma16(reinterpret_cast<const float*>(a_kc_base + (size_t)kt * T::BK), a_voff[v],
-              lds_u + (unsigned)a_off(st) + 1024u * (unsigned)(v * T::WAVES + wave_u));
-    }
-    if (B_KC) {
-#pragma unroll
-      for (int v = 0; v < T::B_VEC; ++v)
-        dma16(reinterpret_cast<const float*>(b_kc_base + (size_t)kt * T::BK), b_voff[v],
-              lds_u + (unsigned)b_off(st) + 1024u * (unsigned)(v * T::WAVES + wave_u));
-    }
-  };
-
   // ---- register-staged operands --------------------------------------------
   // K-contiguous operands in guarded mode: one unit per slot.
   constexpr int A_RK = (GUARD && A_KC) ? T::A_VEC : 1;
@@ -206,10 +193,19 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   u32x4 ra_kc[A_RK], rb_kc[B_RK];
   // Outer-contiguous operands: one 8 x 8 block per lane of the loading waves.
   u32x4 ra_t[TA ? 8 : 1], rb_t[TB ? 1 : 8];
-  const bool a_tw = wave < T::A_TW, b_tw = wave < T::B_TW;
+  // (every wave when the tile has as many 64-wide regions as waves)
+  const bool a_tw = T::A_TW >= T::WAVES || wave < T::A_TW;
+  const bool b_tw = T::B_TW >= T::WAVES || wave < T::B_TW;
   const int a_to = 64 * wave + 8 * ob;  // tile-relative outer index of the block
   const int b_to = 64 * wave + 8 * ob;
 
+  // Aligned mode: per-lane pointers to the lane's first k row of its block at
+  // K step 0 (advanced 64 rows per step); no bounds to check.
+  const uint16_t* a_t0 = TA ? A + (size_t)(8 * kb) * lda + m0 + a_to : A;
+  const uint16_t* b_t0 = TB ? B : B + (size_t)(8 * kb) * ldb + n0 + b_to;
+
+  // Register loads of K step kt: all of them (guarded mode), or transposed
+  // row j of the lane's block (aligned mode).
   auto load_regs = [&](int kt) {
     const int k0 = kt * T::BK;
     if (GUARD && A_KC) {
@@ -234,11 +230,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int k = k0 + 8 * kb + j;
-          const uint16_t* p = A + (size_t)(k < K ? k : 0) * lda + o;
-          if (GUARD)
-            ra_t[j] = lp_load8(p, k < K ? M - o : 0);
-          else
-            ra_t[j] = *reinterpret_cast<const u32x4*>(p);
+          ra_t[j] = lp_load8(A + (size_t)(k < K ? k : 0) * lda + o, k < K ? M - o : 0);
         }
       }
     }
@@ -248,32 +240,61 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int k = k0 + 8 * kb + j;
-          const uint16_t* p = B + (size_t)(k < K ? k : 0) * ldb + o;
-          if (GUARD)
-            rb_t[j] = lp_load8(p, k < K ? N - o : 0);
-          else
-            rb_t[j] = *reinterpret_cast<const u32x4*>(p);
+          rb_t[j] = lp_load8(B + (size_t)(k < K ? k : 0) * ldb + o, k < K ? N - o : 0);
         }
       }
     }
   };
-  // Output row e of a block (its outer index 8ob + e, eight k) from the eight
-  // loaded k rows: dword d packs k = 2d (low half) and 2d + 1 (high half),
-  // each the half e & 1 of dword e / 2 of its row.
-  const unsigned sel_even = 0x05040100u, sel_odd = 0x07060302u;
-  auto store_block = [&](char* tile, const u32x4 (&in)[8], int to) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = i ^ (ob & 1);  // pair-swapped order on odd ob
-      const unsigned sel = ((i ^ ob) & 1) ? sel_odd : sel_even;
-      u32x4 out;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        out[d] = __builtin_amdgcn_perm(in[2 * d + 1][i >> 1], in[2 * d][i >> 1], sel);
-      *reinterpret_cast<u32x4*>(tile + lp_unit_off(to + e, kb)) = out;
+  auto load_t_row = [&](int kt, int j, bool is_a) {  // aligned mode
+    if (is_a) {
+      if constexpr (TA)
+        ra_t[j] = *reinterpret_cast<const u32x4*>(a_t0 + (size_t)(kt * T::BK + j) * lda);
+    } else {
+      if constexpr (!TB)
+        rb_t[j] = *reinterpret_cast<const u32x4*>(b_t0 + (size_t)(kt * T::BK + j) * ldb);
     }
   };
-  auto store_regs = [&](int st) {
+  // Direct load d of K step kt into stage st (the A units, then the B units).
+  constexpr int ND_A = A_KC ? T::A_VEC : 0;
+  constexpr int ND = ND_A + (B_KC ? T::B_VEC : 0);
+  auto direct_one = [&](int kt, int st, int d) {
+    if (d < ND_A)
+      dma16(reinterpret_cast<const float*>(a_kc_base + (size_t)kt * T::BK), a_voff[d],
+            lds_u + (unsigned)a_off(st) + 1024u * (unsigned)(d * T::WAVES + wave_u));
+    else
+      dma16(reinterpret_cast<const float*>(b_kc_base + (size_t)kt * T::BK), b_voff[d - ND_A],
+            lds_u + (unsigned)b_off(st) + 1024u * (unsigned)((d - ND_A) * T::WAVES + wave_u));
+  };
+
+  // Output row e of a block (its outer index 8ob + e, eight k) from the eight
+  // loaded k rows: dword d packs k = 2d (low half) and 2d + 1 (high half),
+  // each the half e & 1 of dword e / 2 of its row.  Lanes with odd ob write
+  // row i ^ 1 when asked for row i (pair-swapped order).
+  const unsigned sel_even = 0x05040100u, sel_odd = 0x07060302u;
+  auto store_row = [&](char* tile, const u32x4 (&in)[8], int to, int i) {
+    const int e = i ^ (ob & 1);
+    const unsigned sel = ((i ^ ob) & 1) ? sel_odd : sel_even;
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      out[d] = __builtin_amdgcn_perm(in[2 * d + 1][i >> 1], in[2 * d][i >> 1], sel);
+    *reinterpret_cast<u32x4*>(tile + lp_unit_off(to + e, kb)) = out;
+  };
+  // Transposed row r of the step's register blocks (A's rows first) into
+  // stage st.
+  constexpr int NS = (TA ? 8 : 0) + (TB ? 0 : 8);
+  auto store_t_row = [&](int st, int r) {
+    if (TA && r < 8) {
+      if constexpr (TA) {
+        if (a_tw) store_row(lds + a_off(st), ra_t, a_to, r);
+      }
+    } else {
+      if constexpr (!TB) {
+        if (b_tw) store_row(lds + b_off(st), rb_t, b_to, TA ? r - 8 : r);
+      }
+    }
+  };
+  auto store_regs = [&](int st) {  // everything loaded by load_regs
     if (GUARD && A_KC) {
 #pragma unroll
       for (int v = 0; v < T::A_VEC; ++v)
@@ -286,70 +307,174 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         *reinterpret_cast<u32x4*>(lds + b_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
             rb_kc[v];
     }
-    if constexpr (TA) {
-      if (a_tw) store_block(lds + a_off(st), ra_t, a_to);
-    }
-    if constexpr (!TB) {
-      if (b_tw) store_block(lds + b_off(st), rb_t, b_to);
-    }
+#pragma unroll
+    for (int r = 0; r < NS; ++r) store_t_row(st, r);
   };
 
-  // ---- MFMAs of one stage: four groups of 16 k -----------------------------
-  auto compute = [&](int st) {
-    const char* As = lds + a_off(st);
-    const char* Bs = lds + b_off(st);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = 2 * q + lh;
-      u32x4 a[T::FM], b[T::FN];
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-        a[i] = *reinterpret_cast<const u32x4*>(As + lp_unit_off(wm * T::WM + i * 32 + li, c));
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j)
-        b[j] = *reinterpret_cast<const u32x4*>(Bs + lp_unit_off(wn * T::WN + j * 32 + li, c));
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) acc[i][j] = lp_mfma<DT>(b[j], a[i], acc[i][j]);
+  // ---- fragments and MFMAs: four groups of 16 k per K step ------------------
+  struct Frag {
+    u32x4 a[T::FM], b[T::FN];
+  };
+  constexpr int NF = T::FM + T::FN;  // fragment reads per group
+  constexpr int SL = T::FM * T::FN;  // MFMAs per group
+  // Read r of a group, in the order the MFMAs (i-major) first need them:
+  // a[0], b[0 .. FN-1], then a[1 .. FM-1].
+  auto read_one = [&](int st, int q, int r, Frag& f) {
+    const int c = 2 * q + lh;
+    if (r >= 1 && r <= T::FN) {
+      const int j = r - 1;
+      f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
+                                               lp_unit_off(wn * T::WN + j * 32 + li, c));
+    } else {
+      const int i = r == 0 ? 0 : r - T::FN;
+      f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
+                                               lp_unit_off(wm * T::WM + i * 32 + li, c));
     }
+  };
+  auto read_frag = [&](int st, int q, Frag& f) {
+#pragma unroll
+    for (int r = 0; r < NF; ++r) read_one(st, q, r, f);
+  };
+  auto mma_one = [&](const Frag& f, int m) {
+    const int i = m / T::FN, j = m % T::FN;
+    acc[i][j] = lp_mfma<DT>(f.b[j], f.a[i], acc[i][j]);
   };
 
   auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+  auto wait_lds = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };  // lgkmcnt(0)
   // No scalar load may be in flight inside the K loop (the epilogue's
   // arguments would otherwise be fetched just before it, and a pending
   // scalar load turns every LDS-read wait into a full lgkmcnt(0)).
   asm volatile("" ::"s"(g.C), "s"(g.ldc), "s"(g.alpha), "s"(g.beta), "s"(M), "s"(N));
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  if (nk > 0) {
-    if (!GUARD) issue_direct(0, 0);
-    load_regs(0);
-    store_regs(0);
-    wait_all();
-    __syncthreads();
-  }
-  // One K step from stage st; step kt+1 goes into the other stage, whose
-  // previous contents were read before the last barrier.
-  auto step = [&](int kt, int st) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      if (!GUARD) issue_direct(kt + 1, st ^ 1);
-      load_regs(kt + 1);
+  if constexpr (GUARD) {
+    // Guarded mode: every load through registers, one step ahead.
+    if (nk > 0) {
+      load_regs(0);
+      store_regs(0);
+      wait_lds();
+      __syncthreads();
     }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(st);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) store_regs(st ^ 1);
+    auto step = [&](int kt, int st) {
+      const bool more = kt + 1 < nk;
+      if (more) load_regs(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        Frag f;
+        read_frag(st, q, f);
+#pragma unroll
+        for (int m = 0; m < SL; ++m) mma_one(f, m);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) store_regs(st ^ 1);
+      wait_lds();
+      __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, 0);
+      step(kt + 1, 1);
+    }
+    if (kt < nk) step(kt, 0);
+  } else {
+    // Aligned mode.  Every group of MFMAs is issued one MFMA at a time with
+    // other work in the slots between them, in a fixed order (scheduling
+    // barriers), so that with one wave per SIMD the matrix pipe is never
+    // left idle while the wave issues loads, reads or permutes:
+    //   groups 0-2 of step kt: the next group's fragment reads, and (in
+    //     groups 1-2) the transposed rows of step kt+1 (loaded into registers
+    //     during step kt-1) written to the other stage;
+    //   barrier of step kt: every wave has read all of stage kt (lgkmcnt(0)),
+    //     written step kt+1's rows and seen its direct loads of step kt+1
+    //     land (vmcnt(0));
+    //   group 3 of step kt: step kt+1's first fragments, now visible, and
+    //     step kt+2's global loads -- direct ones into stage kt, now free,
+    //     and register ones -- which so have a whole step to land.
+    constexpr int NR = (TA ? 8 : 0) + (TB ? 0 : 8);  // register rows per step
+    auto vmem_one = [&](int kt, int st, int o) {
+      if (o < ND) {
+        direct_one(kt, st, o);
+      } else if (TA && o - ND < 8) {
+        if (a_tw) load_t_row(kt, o - ND, true);
+      } else {
+        if (b_tw) load_t_row(kt, o - ND - (TA ? 8 : 0), false);
+      }
+    };
+    auto issue_step = [&](int kt, int st) {
+#pragma unroll
+      for (int o = 0; o < ND + NR; ++o) vmem_one(kt, st, o);
+    };
+    // Group q of step kt on fragments cur; fills the slots as described.
+    // kn = step kt+1 and kl = step kt+2, both clamped to the last step: past
+    // the end of K the same (in-bounds) work is repeated into a stage that is
+    // never read again, which keeps the slots free of branches.
+    auto group = [&](int kn, int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
+      constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
+      (void)kn;
+#pragma unroll
+      for (int m = 0; m < SL; ++m) {
+        mma_one(cur, m);
+        if (q < 3) {
+#pragma unroll
+          for (int r = 0; r < NF; ++r)
+            if (r * SL / NF == m) read_one(st, q + 1, r, nxt);
+          // rows of step kt+1, as late as possible: in group 2 (eight rows)
+          // or groups 1 and 2 (sixteen).  The compiler cannot see the direct
+          // loads, so its wait before the first permute is vmcnt(0); this
+          // late, that waits only for loads that had three groups to land,
+          // the same ones the barrier waits for.
+          constexpr int G0 = NS > 8 ? 1 : 2;  // first group with rows
+          constexpr int r0 = q < G0 ? 0 : (q - G0) * NS / (3 - G0);
+          constexpr int r1 = q < G0 ? 0 : (q - G0 + 1) * NS / (3 - G0);
+#pragma unroll
+          for (int r = r0; r < r1; ++r)
+            if ((2 * (r - r0) + 1) * SL / (2 * (r1 - r0)) == m) store_t_row(st ^ 1, r);
+        } else {
+#pragma unroll
+          for (int r = 0; r < NF; ++r)
+            if (r * SL / NF == m) read_one(st ^ 1, 0, r, nxt);
+#pragma unroll
+          for (int o = 0; o < ND + NR; ++o)
+            if (o * SL / (ND + NR) == m) vmem_one(kl, st, o);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, 1> I1;
+    typedef std::integral_constant<int, 2> I2;
+    typedef std::integral_constant<int, 3> I3;
+    Frag f0, f1;
+    auto step = [&](int kt, auto st_c) {
+      const int kn = kt + 1 < nk ? kt + 1 : nk - 1;
+      const int kl = kt + 2 < nk ? kt + 2 : nk - 1;
+      group(kn, kl, st_c, I0{}, f0, f1);
+      group(kn, kl, st_c, I1{}, f1, f0);
+      group(kn, kl, st_c, I2{}, f0, f1);
+      wait_lds();
+      wait_all();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      group(kn, kl, st_c, I3{}, f1, f0);
+    };
+    // (aligned kernels run with K >= 64, so nk >= 1)
+    issue_step(0, 0);
+#pragma unroll
+    for (int r = 0; r < NS; ++r) store_t_row(0, r);
+    issue_step(nk > 1 ? 1 : 0, 1);  // rows stored during step 0
     wait_all();
+    wait_lds();
     __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, 0);
-    step(kt + 1, 1);
+    read_frag(0, 0, f0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, I0{});
+      step(kt + 1, I1{});
+    }
+    if (kt < nk) step(kt, I0{});
   }
-  if (kt < nk) step(kt, 0);
 }
 
 template <class T, int DT, int MODE, bool TA, bool TB>

@@ -305,6 +305,14 @@ int sgemm_lowp_select_kernel(int dtype, int transa, int transb, int M, int N,
                              int K, const void* A, int lda, const void* B,
                              int ldb, const float* C, int ldc);
 
+/* Diagnostics: as sgemm_diag_mfma_chain with v_mfma_f32_32x32x16_bf16
+ * (dtype SGEMM_DTYPE_BF16) or v_mfma_f32_32x32x16_f16 (SGEMM_DTYPE_F16):
+ * 32768 flops per MFMA per wave, eight independent accumulators, no memory
+ * traffic; the ceiling for the 16-bit product kernels.  SGEMM_ERR_VALUE for
+ * another dtype. */
+int sgemm_diag_mfma_chain_lowp(int dtype, int workgroups, int iterations,
+                               float* out, hipStream_t stream);
+
 /* Force one 16-bit product kernel on this handle (kernel_id >= 0) or go back
  * to automatic selection (-1).  A forced kernel whose mode, format or
  * storage cannot take the arguments makes sgemm_run_lowp return

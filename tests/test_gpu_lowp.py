@@ -198,3 +198,19 @@ def test_torch_tensor_shapes(handle):
     handle.gemm_lowp(A2, B2, C2, ops.alpha, ops.beta)
     torch.cuda.synchronize()
     gu.check_full16(ops, C.cpu().numpy(), what="2-D tensors")
+
+
+@pytest.mark.parametrize("nk", [1, 2, 3, 5])
+def test_aligned_kernels_short_k(handle, nk):
+    """Aligned kernels with one to five K steps: the software pipeline's
+    start and end (steps past the last one repeat it into an unused stage)."""
+    for k in KERNELS:
+        if k["mode"] != sg.SGEMM_MODE_ALIGNED:
+            continue
+        handle.set_lowp_kernel(k["id"])
+        ta, tb = bool(k["transa"]), bool(k["transb"])
+        M, N, K = k["bm"], 2 * k["bn"], nk * k["bk"]
+        w = wl.Workload("shortk", 800 + 10 * nk + k["id"] % 10, M, N, K, 1.0, 1.0, "int4")
+        ops = wl.operands16(w, DT_NAME[k["dtype"]], ta=ta, tb=tb)
+        out = gu.run16(handle, ops)
+        gu.check_full16(ops, out, exact=True, what=f"{k['name']} nk={nk}")
