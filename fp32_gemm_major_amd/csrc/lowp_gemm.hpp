@@ -174,18 +174,39 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // Direct loads (aligned mode): wave-uniform base at the tile's origin,
   // advanced 64 elements per K step, and fixed per-lane byte offsets (the
   // host keeps them below 2^32).
+  // An operand stored outer-contiguous keeps that layout in aligned mode:
+  // rows of k holding X outer indices, 16-byte unit p of row k at
+  // p ^ (4 * (k & 3)).  Slot u of such a tile is row u / (X/8), physical unit
+  // u % (X/8).
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
   unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
   if (!GUARD) {
 #pragma unroll
-    for (int v = 0; v < T::A_VEC; ++v)
-      a_voff[v] = 2u * ((unsigned)a_r[v] * (unsigned)lda + 8u * (unsigned)a_c[v]);
+    for (int v = 0; v < T::A_VEC; ++v) {
+      if (A_KC) {
+        a_voff[v] = 2u * ((unsigned)a_r[v] * (unsigned)lda + 8u * (unsigned)a_c[v]);
+      } else {
+        const int u = (v * T::WAVES + wave) * 64 + lane;
+        const int k = u / (T::BM / 8), c = (u % (T::BM / 8)) ^ (4 * (k & 3));
+        a_voff[v] = 2u * ((unsigned)k * (unsigned)lda + 8u * (unsigned)c);
+      }
+    }
 #pragma unroll
-    for (int v = 0; v < T::B_VEC; ++v)
-      b_voff[v] = 2u * ((unsigned)b_r[v] * (unsigned)ldb + 8u * (unsigned)b_c[v]);
+    for (int v = 0; v < T::B_VEC; ++v) {
+      if (B_KC) {
+        b_voff[v] = 2u * ((unsigned)b_r[v] * (unsigned)ldb + 8u * (unsigned)b_c[v]);
+      } else {
+        const int u = (v * T::WAVES + wave) * 64 + lane;
+        const int k = u / (T::BN / 8), c = (u % (T::BN / 8)) ^ (4 * (k & 3));
+        b_voff[v] = 2u * ((unsigned)k * (unsigned)ldb + 8u * (unsigned)c);
+      }
+    }
   }
-  const uint16_t* a_kc_base = A + (size_t)m0 * lda;  // used when A_KC
-  const uint16_t* b_kc_base = B + (size_t)n0 * ldb;  // used when B_KC
+  // Tile origins and the advance per K step of the direct loads.
+  const uint16_t* a_dbase = A_KC ? A + (size_t)m0 * lda : A + m0;
+  const uint16_t* b_dbase = B_KC ? B + (size_t)n0 * ldb : B + n0;
+  const size_t a_dstep = A_KC ? (size_t)T::BK : (size_t)T::BK * lda;
+  const size_t b_dstep = B_KC ? (size_t)T::BK : (size_t)T::BK * ldb;
   // ---- register-staged operands --------------------------------------------
   // K-contiguous operands in guarded mode: one unit per slot.
   constexpr int A_RK = (GUARD && A_KC) ? T::A_VEC : 1;
@@ -199,13 +220,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   const int a_to = 64 * wave + 8 * ob;  // tile-relative outer index of the block
   const int b_to = 64 * wave + 8 * ob;
 
-  // Aligned mode: per-lane pointers to the lane's first k row of its block at
-  // K step 0 (advanced 64 rows per step); no bounds to check.
-  const uint16_t* a_t0 = TA ? A + (size_t)(8 * kb) * lda + m0 + a_to : A;
-  const uint16_t* b_t0 = TB ? B : B + (size_t)(8 * kb) * ldb + n0 + b_to;
-
-  // Register loads of K step kt: all of them (guarded mode), or transposed
-  // row j of the lane's block (aligned mode).
+  // Register loads of K step kt (guarded mode).
   auto load_regs = [&](int kt) {
     const int k0 = kt * T::BK;
     if (GUARD && A_KC) {
@@ -245,24 +260,16 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       }
     }
   };
-  auto load_t_row = [&](int kt, int j, bool is_a) {  // aligned mode
-    if (is_a) {
-      if constexpr (TA)
-        ra_t[j] = *reinterpret_cast<const u32x4*>(a_t0 + (size_t)(kt * T::BK + j) * lda);
-    } else {
-      if constexpr (!TB)
-        rb_t[j] = *reinterpret_cast<const u32x4*>(b_t0 + (size_t)(kt * T::BK + j) * ldb);
-    }
-  };
-  // Direct load d of K step kt into stage st (the A units, then the B units).
-  constexpr int ND_A = A_KC ? T::A_VEC : 0;
-  constexpr int ND = ND_A + (B_KC ? T::B_VEC : 0);
+  // Direct load d of K step kt into stage st (aligned mode: the A units,
+  // then the B units, whatever their storage).
+  constexpr int ND_A = T::A_VEC;
+  constexpr int ND = T::A_VEC + T::B_VEC;
   auto direct_one = [&](int kt, int st, int d) {
     if (d < ND_A)
-      dma16(reinterpret_cast<const float*>(a_kc_base + (size_t)kt * T::BK), a_voff[d],
+      dma16(reinterpret_cast<const float*>(a_dbase + (size_t)kt * a_dstep), a_voff[d],
             lds_u + (unsigned)a_off(st) + 1024u * (unsigned)(d * T::WAVES + wave_u));
     else
-      dma16(reinterpret_cast<const float*>(b_kc_base + (size_t)kt * T::BK), b_voff[d - ND_A],
+      dma16(reinterpret_cast<const float*>(b_dbase + (size_t)kt * b_dstep), b_voff[d - ND_A],
             lds_u + (unsigned)b_off(st) + 1024u * (unsigned)((d - ND_A) * T::WAVES + wave_u));
   };
 
@@ -317,18 +324,49 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   };
   constexpr int NF = T::FM + T::FN;  // fragment reads per group
   constexpr int SL = T::FM * T::FN;  // MFMAs per group
+  // A fragment of 32 outer indices from an outer-contiguous tile of width X
+  // (aligned mode), by two transposing reads (ds_read_b64_tr_b16).  In each
+  // group of 16 lanes such a read hands lane i, element e, element i % 4 of
+  // the four that lane 4e + i / 4 points at.  So lane 4e + r points at row
+  // k + e and outer indices 4r .. 4r+3 of the lane group's 16 (lanes 0-15
+  // and 32-47 the block's first 16, the others the next 16; lanes 32-63 the
+  // k half 8 .. 15), and lane i receives k + 0 .. 3 of outer index i: the
+  // same k order as a K-contiguous fragment.  With the unit swizzle the four
+  // rows of a lane group fall on distinct bank groups.
+  const int tr_e = (lane & 15) >> 2, tr_r = lane & 3;
+  const int tr_o = 16 * ((lane >> 4) & 1) + 4 * tr_r;  // outer index in the block
+  auto read_tr = [&](const char* tile, int X, int o_block, int q) -> u32x4 {
+    const int k = 16 * q + 8 * lh + tr_e;
+    const int o = o_block + tr_o;
+    const int off = k * 2 * X + 16 * ((o >> 3) ^ (4 * (k & 3))) + 2 * (o & 7);
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(lds_void_t*)(tile + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16*)(lds_void_t*)(tile + off + 4 * 2 * X));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
   // Read r of a group, in the order the MFMAs (i-major) first need them:
   // a[0], b[0 .. FN-1], then a[1 .. FM-1].
   auto read_one = [&](int st, int q, int r, Frag& f) {
     const int c = 2 * q + lh;
     if (r >= 1 && r <= T::FN) {
       const int j = r - 1;
-      f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
-                                               lp_unit_off(wn * T::WN + j * 32 + li, c));
+      if (!GUARD && !B_KC)
+        f.b[j] = read_tr(lds + b_off(st), T::BN, wn * T::WN + j * 32, q);
+      else
+        f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
+                                                 lp_unit_off(wn * T::WN + j * 32 + li, c));
     } else {
       const int i = r == 0 ? 0 : r - T::FN;
-      f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
-                                               lp_unit_off(wm * T::WM + i * 32 + li, c));
+      if (!GUARD && !A_KC)
+        f.a[i] = read_tr(lds + a_off(st), T::BM, wm * T::WM + i * 32, q);
+      else
+        f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
+                                                 lp_unit_off(wm * T::WM + i * 32 + li, c));
     }
   };
   auto read_frag = [&](int st, int q, Frag& f) {
@@ -379,40 +417,28 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     }
     if (kt < nk) step(kt, 0);
   } else {
-    // Aligned mode.  Every group of MFMAs is issued one MFMA at a time with
-    // other work in the slots between them, in a fixed order (scheduling
-    // barriers), so that with one wave per SIMD the matrix pipe is never
-    // left idle while the wave issues loads, reads or permutes:
-    //   groups 0-2 of step kt: the next group's fragment reads, and (in
-    //     groups 1-2) the transposed rows of step kt+1 (loaded into registers
-    //     during step kt-1) written to the other stage;
-    //   barrier of step kt: every wave has read all of stage kt (lgkmcnt(0)),
-    //     written step kt+1's rows and seen its direct loads of step kt+1
-    //     land (vmcnt(0));
+    // Aligned mode: every operand tile arrives by direct loads.  Every group
+    // of MFMAs is issued one MFMA at a time with other work in the slots
+    // between them, in a fixed order (scheduling barriers), so that with one
+    // wave per SIMD the matrix pipe is not left idle while the wave issues
+    // reads or loads:
+    //   groups 0-2 of step kt: the next group's fragment reads;
+    //   barrier of step kt: every wave has read all of stage kt (lgkmcnt(0))
+    //     and seen its direct loads of step kt+1 land (vmcnt(0));
     //   group 3 of step kt: step kt+1's first fragments, now visible, and
-    //     step kt+2's global loads -- direct ones into stage kt, now free,
-    //     and register ones -- which so have a whole step to land.
-    constexpr int NR = (TA ? 8 : 0) + (TB ? 0 : 8);  // register rows per step
-    auto vmem_one = [&](int kt, int st, int o) {
-      if (o < ND) {
-        direct_one(kt, st, o);
-      } else if (TA && o - ND < 8) {
-        if (a_tw) load_t_row(kt, o - ND, true);
-      } else {
-        if (b_tw) load_t_row(kt, o - ND - (TA ? 8 : 0), false);
-      }
-    };
+    //     step kt+2's direct loads into stage kt, now free, which so have a
+    //     whole step to land.
     auto issue_step = [&](int kt, int st) {
 #pragma unroll
-      for (int o = 0; o < ND + NR; ++o) vmem_one(kt, st, o);
+      for (int o = 0; o < ND; ++o) direct_one(kt, st, o);
     };
     // Group q of step kt on fragments cur; fills the slots as described.
-    // kn = step kt+1 and kl = step kt+2, both clamped to the last step: past
-    // the end of K the same (in-bounds) work is repeated into a stage that is
-    // never read again, which keeps the slots free of branches.
-    auto group = [&](int kn, int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
+    // kl = step kt+2 clamped to the last step: past the end of K the same
+    // (in-bounds) loads are repeated into a stage that is never read again,
+    // and step kt+1's first fragments are read even at the last step, which
+    // keeps the slots free of branches.
+    auto group = [&](int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
       constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
-      (void)kn;
 #pragma unroll
       for (int m = 0; m < SL; ++m) {
         mma_one(cur, m);
@@ -420,24 +446,13 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
           for (int r = 0; r < NF; ++r)
             if (r * SL / NF == m) read_one(st, q + 1, r, nxt);
-          // rows of step kt+1, as late as possible: in group 2 (eight rows)
-          // or groups 1 and 2 (sixteen).  The compiler cannot see the direct
-          // loads, so its wait before the first permute is vmcnt(0); this
-          // late, that waits only for loads that had three groups to land,
-          // the same ones the barrier waits for.
-          constexpr int G0 = NS > 8 ? 1 : 2;  // first group with rows
-          constexpr int r0 = q < G0 ? 0 : (q - G0) * NS / (3 - G0);
-          constexpr int r1 = q < G0 ? 0 : (q - G0 + 1) * NS / (3 - G0);
-#pragma unroll
-          for (int r = r0; r < r1; ++r)
-            if ((2 * (r - r0) + 1) * SL / (2 * (r1 - r0)) == m) store_t_row(st ^ 1, r);
         } else {
 #pragma unroll
           for (int r = 0; r < NF; ++r)
             if (r * SL / NF == m) read_one(st ^ 1, 0, r, nxt);
 #pragma unroll
-          for (int o = 0; o < ND + NR; ++o)
-            if (o * SL / (ND + NR) == m) vmem_one(kl, st, o);
+          for (int o = 0; o < ND; ++o)
+            if (o * SL / ND == m) direct_one(kl, st, o);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -448,22 +463,19 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     typedef std::integral_constant<int, 3> I3;
     Frag f0, f1;
     auto step = [&](int kt, auto st_c) {
-      const int kn = kt + 1 < nk ? kt + 1 : nk - 1;
       const int kl = kt + 2 < nk ? kt + 2 : nk - 1;
-      group(kn, kl, st_c, I0{}, f0, f1);
-      group(kn, kl, st_c, I1{}, f1, f0);
-      group(kn, kl, st_c, I2{}, f0, f1);
+      group(kl, st_c, I0{}, f0, f1);
+      group(kl, st_c, I1{}, f1, f0);
+      group(kl, st_c, I2{}, f0, f1);
       wait_lds();
       wait_all();
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      group(kn, kl, st_c, I3{}, f1, f0);
+      group(kl, st_c, I3{}, f1, f0);
     };
     // (aligned kernels run with K >= 64, so nk >= 1)
     issue_step(0, 0);
-#pragma unroll
-    for (int r = 0; r < NS; ++r) store_t_row(0, r);
-    issue_step(nk > 1 ? 1 : 0, 1);  // rows stored during step 0
+    issue_step(nk > 1 ? 1 : 0, 1);
     wait_all();
     wait_lds();
     __syncthreads();

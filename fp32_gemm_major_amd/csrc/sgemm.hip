@@ -635,12 +635,14 @@ const LpKernelDesc kLpKernels[] = {
 };
 constexpr int kNumLpKernels = sizeof(kLpKernels) / sizeof(kLpKernels[0]);
 
-// Direct loads of a K-contiguous operand: the farthest byte of one K step of
-// a tile must lie within 4 GiB of the tile's origin.
+// Direct loads (aligned kernels, both operands in any storage): the farthest
+// byte of one K step of a tile must lie within 4 GiB of the tile's origin.
 bool lp_offsets_fit(const LpKernelDesc& k, const LpRun& a) {
-  const long long a_far = (long long)(k.bm - 1) * a.lda + k.bk;
-  const long long b_far = (long long)(k.bn - 1) * a.ldb + k.bk;
-  return (a.ta || 2 * a_far < (1LL << 32)) && (!a.tb || 2 * b_far < (1LL << 32));
+  const long long a_far = a.ta ? (long long)(k.bk - 1) * a.lda + k.bm
+                               : (long long)(k.bm - 1) * a.lda + k.bk;
+  const long long b_far = a.tb ? (long long)(k.bn - 1) * a.ldb + k.bk
+                               : (long long)(k.bk - 1) * a.ldb + k.bn;
+  return 2 * a_far < (1LL << 32) && 2 * b_far < (1LL << 32);
 }
 
 bool lp_fits(const LpKernelDesc& k, const LpRun& a) {

@@ -95,6 +95,8 @@ def test_huge_strides_go_to_the_guarded_kernel():
     32-bit lane offsets of the direct loads."""
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8)
     assert k["mode"] == sg.SGEMM_MODE_GUARDED
-    # the transposed-storage operand does not use direct loads: no limit there
+    # stored K x M, one K step of a tile spans 63 rows of A
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8, ta=1)
     assert k["mode"] == sg.SGEMM_MODE_ALIGNED
+    k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 26) + 8, ta=1, B=1 << 42, C=1 << 44)
+    assert k["mode"] == sg.SGEMM_MODE_GUARDED
