@@ -50,6 +50,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mfma_sgemm.hpp"
 #include "tile_map.hpp"
@@ -78,9 +79,12 @@ struct LpArgs {
 // Block tile BM x BN, wave tile WM x WN of 32x32 blocks, registers sized for
 // OCC waves per SIMD.  The member names the FP32 epilogue (store_tile) and
 // WaveCoords read are the same as MfmaTile's (one K group).
-template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2>
 struct LpTile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, OCC = OCC_;
+  // LDS stages of the aligned kernels: their direct loads run S-1 K steps
+  // ahead (guarded kernels use two stages).
+  static constexpr int S = S_;
   static constexpr int BK = 64;  // k per K step: one 128-byte LDS row
   static constexpr int KG = 1;
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
@@ -88,7 +92,7 @@ struct LpTile {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;  // one stage
-  static constexpr int LDS_BYTES = 2 * (A_BYTES + B_BYTES);
+  static constexpr int LDS_BYTES = S * (A_BYTES + B_BYTES);
   // K-contiguous loader: 16-byte units per lane per K step
   static constexpr int A_VEC = BM * 8 / THREADS, B_VEC = BN * 8 / THREADS;
   // transposing loader: waves that move the operand (64 outer indices each)
@@ -100,8 +104,32 @@ struct LpTile {
   static_assert(BM % 64 == 0 && BN % 64 == 0, "transposing loader regions");
   static_assert(A_TW <= WAVES && B_TW <= WAVES, "transposing loader waves");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
-  static_assert(A_VEC + B_VEC <= 63, "vmcnt range");
+  static_assert(S >= 2, "stages");
+  static_assert((S - 1) * (A_VEC + B_VEC) <= 63, "vmcnt range");
 };
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order.
+template <class F, int... I>
+__device__ __forceinline__ void lp_static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void lp_static_for(F&& f) {
+  lp_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Outer-contiguous tiles (aligned mode): rows of k holding X outer indices,
+// X / 8 units of 16 bytes per row; unit p of row k sits at p ^ lp_oc_swz.
+// A transposing read of 16 lanes touches four consecutive rows (k & 3 = 0..3)
+// at the same units.  Rows of at least 16 units map every row onto the same
+// 16 bank groups, so the XOR takes bits 2-3 of the unit from k & 3; rows of
+// 8 units (X = 64) alternate between two halves of the bank groups by k & 1,
+// so the XOR takes bit 2 from k & 2 (and stays inside the row).
+template <int X>
+__device__ __forceinline__ int lp_oc_swz(int k) {
+  static_assert(X == 64 || X % 128 == 0, "outer-contiguous tile width");
+  return X >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
 
 // Byte offset of 16-byte unit c (k = 8c .. 8c+7) of row r in an operand tile.
 __device__ __forceinline__ int lp_unit_off(int r, int c) {
@@ -118,12 +146,18 @@ __device__ __forceinline__ f32x16 lp_mfma(u32x4 x, u32x4 y, f32x16 acc) {
         __builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
 }
 
-// Eight 16-bit elements at p (2-byte aligned): a 16-byte load when all eight
-// are wanted and p is 16-byte aligned, else element loads of the first n (n
-// may be <= 0) with zeros after them.
+// A 16-byte piece that may be only 2-byte aligned: 16-byte global loads on
+// gfx950 take any 2-byte aligned address (checked with an in-bounds probe).
+typedef unsigned u32x4u2 __attribute__((ext_vector_type(4), aligned(2)));
+
+// Eight 16-bit elements at p (2-byte aligned): one 16-byte load when all
+// eight are wanted, else element loads of the first n (n may be <= 0) with
+// zeros after them.
 __device__ __forceinline__ u32x4 lp_load8(const uint16_t* p, int n) {
-  if (n >= 8 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0)
-    return *reinterpret_cast<const u32x4*>(p);
+  if (n >= 8) {
+    const u32x4u2 v = *reinterpret_cast<const u32x4u2*>(p);
+    return u32x4{v[0], v[1], v[2], v[3]};
+  }
   unsigned h[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) h[t] = t < n ? (unsigned)p[t] : 0u;
@@ -153,9 +187,10 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   const int kb = lane & 7, ob = lane >> 3;  // transposing loader block
   const int nk = (K + T::BK - 1) / T::BK;
 
-  // LDS: the A tiles of both stages, then the B tiles.
+  // LDS: the A tiles of all stages, then the B tiles.
   auto a_off = [](int st) { return st * T::A_BYTES; };
-  auto b_off = [](int st) { return 2 * T::A_BYTES + st * T::B_BYTES; };
+  constexpr int NST = GUARD ? 2 : T::S;  // stages in use
+  auto b_off = [](int st) { return NST * T::A_BYTES + st * T::B_BYTES; };
 
   // ---- K-contiguous operands: slot u of the tile holds (row, unit) ------
   int a_r[T::A_VEC], a_c[T::A_VEC], b_r[T::B_VEC], b_c[T::B_VEC];
@@ -174,10 +209,9 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // Direct loads (aligned mode): wave-uniform base at the tile's origin,
   // advanced 64 elements per K step, and fixed per-lane byte offsets (the
   // host keeps them below 2^32).
-  // An operand stored outer-contiguous keeps that layout in aligned mode:
-  // rows of k holding X outer indices, 16-byte unit p of row k at
-  // p ^ (4 * (k & 3)).  Slot u of such a tile is row u / (X/8), physical unit
-  // u % (X/8).
+  // An operand stored outer-contiguous keeps that layout in aligned mode
+  // (rows of k, units swizzled by lp_oc_swz).  Slot u of such a tile is row
+  // u / (X/8), physical unit u % (X/8).
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
   unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
   if (!GUARD) {
@@ -187,7 +221,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         a_voff[v] = 2u * ((unsigned)a_r[v] * (unsigned)lda + 8u * (unsigned)a_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
-        const int k = u / (T::BM / 8), c = (u % (T::BM / 8)) ^ (4 * (k & 3));
+        const int k = u / (T::BM / 8), c = (u % (T::BM / 8)) ^ lp_oc_swz<T::BM>(k);
         a_voff[v] = 2u * ((unsigned)k * (unsigned)lda + 8u * (unsigned)c);
       }
     }
@@ -197,7 +231,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         b_voff[v] = 2u * ((unsigned)b_r[v] * (unsigned)ldb + 8u * (unsigned)b_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
-        const int k = u / (T::BN / 8), c = (u % (T::BN / 8)) ^ (4 * (k & 3));
+        const int k = u / (T::BN / 8), c = (u % (T::BN / 8)) ^ lp_oc_swz<T::BN>(k);
         b_voff[v] = 2u * ((unsigned)k * (unsigned)ldb + 8u * (unsigned)c);
       }
     }
@@ -335,10 +369,12 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // rows of a lane group fall on distinct bank groups.
   const int tr_e = (lane & 15) >> 2, tr_r = lane & 3;
   const int tr_o = 16 * ((lane >> 4) & 1) + 4 * tr_r;  // outer index in the block
-  auto read_tr = [&](const char* tile, int X, int o_block, int q) -> u32x4 {
+  auto read_tr = [&](const char* tile, auto x_c, int o_block, int q) -> u32x4 {
+    constexpr int X = decltype(x_c)::value;
     const int k = 16 * q + 8 * lh + tr_e;
     const int o = o_block + tr_o;
-    const int off = k * 2 * X + 16 * ((o >> 3) ^ (4 * (k & 3))) + 2 * (o & 7);
+    // (rows k and k + 4 share the swizzle)
+    const int off = k * 2 * X + 16 * ((o >> 3) ^ lp_oc_swz<X>(k)) + 2 * (o & 7);
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -356,14 +392,16 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     if (r >= 1 && r <= T::FN) {
       const int j = r - 1;
       if (!GUARD && !B_KC)
-        f.b[j] = read_tr(lds + b_off(st), T::BN, wn * T::WN + j * 32, q);
+        f.b[j] = read_tr(lds + b_off(st), std::integral_constant<int, T::BN>{},
+                         wn * T::WN + j * 32, q);
       else
         f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
                                                  lp_unit_off(wn * T::WN + j * 32 + li, c));
     } else {
       const int i = r == 0 ? 0 : r - T::FN;
       if (!GUARD && !A_KC)
-        f.a[i] = read_tr(lds + a_off(st), T::BM, wm * T::WM + i * 32, q);
+        f.a[i] = read_tr(lds + a_off(st), std::integral_constant<int, T::BM>{},
+                         wm * T::WM + i * 32, q);
       else
         f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
                                                  lp_unit_off(wm * T::WM + i * 32 + li, c));
@@ -432,13 +470,15 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
       for (int o = 0; o < ND; ++o) direct_one(kt, st, o);
     };
-    // Group q of step kt on fragments cur; fills the slots as described.
-    // kl = step kt+2 clamped to the last step: past the end of K the same
-    // (in-bounds) loads are repeated into a stage that is never read again,
-    // and step kt+1's first fragments are read even at the last step, which
-    // keeps the slots free of branches.
+    // Group q of step kt (stage st) on fragments cur; fills the slots as
+    // described.  kl = step kt+S clamped to the last step: past the end of K
+    // the same (in-bounds) loads are repeated into a stage that is never read
+    // again, and step kt+1's first fragments are read even at the last step,
+    // which keeps the slots free of branches.
+    constexpr int S = T::S;
     auto group = [&](int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
       constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
+      constexpr int st1 = st + 1 == S ? 0 : st + 1;
 #pragma unroll
       for (int m = 0; m < SL; ++m) {
         mma_one(cur, m);
@@ -449,7 +489,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         } else {
 #pragma unroll
           for (int r = 0; r < NF; ++r)
-            if (r * SL / NF == m) read_one(st ^ 1, 0, r, nxt);
+            if (r * SL / NF == m) read_one(st1, 0, r, nxt);
 #pragma unroll
           for (int o = 0; o < ND; ++o)
             if (o * SL / ND == m) direct_one(kl, st, o);
@@ -461,38 +501,48 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     typedef std::integral_constant<int, 1> I1;
     typedef std::integral_constant<int, 2> I2;
     typedef std::integral_constant<int, 3> I3;
+    // vmcnt(N) before a barrier: step kt+1's loads have landed once at most
+    // the S-2 later steps' loads are still in flight.
+    constexpr int AHEAD = (S - 2) * ND;
+    constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
     Frag f0, f1;
     auto step = [&](int kt, auto st_c) {
-      const int kl = kt + 2 < nk ? kt + 2 : nk - 1;
+      const int kl = kt + S < nk ? kt + S : nk - 1;
       group(kl, st_c, I0{}, f0, f1);
       group(kl, st_c, I1{}, f1, f0);
       group(kl, st_c, I2{}, f0, f1);
       wait_lds();
-      wait_all();
+      __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       group(kl, st_c, I3{}, f1, f0);
     };
-    // (aligned kernels run with K >= 64, so nk >= 1)
-    issue_step(0, 0);
-    issue_step(nk > 1 ? 1 : 0, 1);
-    wait_all();
+    // (aligned kernels run with K >= 64, so nk >= 1)  Steps 0 .. S-1 go
+    // out first; step 0 must have landed before the first barrier.
+    lp_static_for<S>([&](auto i) {
+      constexpr int st = decltype(i)::value;
+      issue_step(st < nk ? st : nk - 1, st);
+    });
+    constexpr int FIRST = (S - 1) * ND;
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (FIRST & 15) | ((FIRST >> 4) << 14));
     wait_lds();
     __syncthreads();
     read_frag(0, 0, f0);
     int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, I0{});
-      step(kt + 1, I1{});
-    }
-    if (kt < nk) step(kt, I0{});
+    for (; kt + S <= nk; kt += S)
+      lp_static_for<S>([&](auto i) { step(kt + decltype(i)::value, i); });
+    lp_static_for<S - 1>([&](auto i) {
+      if (kt + decltype(i)::value < nk) step(kt + decltype(i)::value, i);
+    });
   }
 }
 
 template <class T, int DT, int MODE, bool TA, bool TB>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
     lp_gemm_kernel(LpArgs g, int tiles_m, int tiles_n, int band) {
-  __shared__ __attribute__((aligned(1024))) char lds[T::LDS_BYTES];
+  // guarded kernels use two stages
+  __shared__ __attribute__((aligned(1024)))
+  char lds[MODE == MODE_GUARDED ? 2 * (T::A_BYTES + T::B_BYTES) : T::LDS_BYTES];
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
   f32x16 acc[T::FM][T::FN];
@@ -517,7 +567,11 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
 // 4 waves of 128x128 (256 accumulators per lane), one workgroup per CU,
 // 128 KB of LDS for the two stages.
 typedef LpTile<256, 256, 128, 128, 1> L256x256;
-// 4 waves of 64x64, for problems with fewer than one 256x256 tile per CU.
-typedef LpTile<128, 128, 64, 64, 2> L128x128;
+// 4 waves of 64x64, four LDS stages (128 KB): problems with fewer than one
+// 256x256 tile per CU.
+typedef LpTile<128, 128, 64, 64, 2, 4> L128x128;
+// 4 waves of 32x32, four LDS stages (64 KB): small problems, whose K steps
+// are short, so the loads run three steps ahead.
+typedef LpTile<64, 64, 32, 32, 2, 4> L64x64;
 
 }  // namespace sgemm

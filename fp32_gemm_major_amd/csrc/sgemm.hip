@@ -626,8 +626,10 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
 #define LP_FORMAT(DT, DTAG)                                                  \
   LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
   LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
+  LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),               \
   LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),             \
-  LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_GUARDED, "guarded")
+  LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),             \
+  LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded")
 
 const LpKernelDesc kLpKernels[] = {
     LP_FORMAT(SGEMM_DTYPE_BF16, "bf16"),
@@ -654,15 +656,20 @@ bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
          ptr_aligned16(a.B) && lp_offsets_fit(k, a);
 }
 
-// The kernel for these arguments: the 256x256 tile when it gives every CU
-// of the chip a tile, else the 128x128 tile; the aligned instance when it
-// fits, else the guarded one.
+// The kernel for these arguments: the largest tile (256, 128, then 64
+// square) that still gives every CU a tile, else the 64x64 one; the aligned
+// instance when it fits, else the guarded one.
 int lp_select(const LpRun& a, int cus) {
-  const bool big = ceil_div(a.M, 256) * ceil_div(a.N, 256) >= cus;
+  int bm = 64;
+  for (int t = 256; t >= 128; t /= 2)
+    if (ceil_div(a.M, t) * ceil_div(a.N, t) >= cus) {
+      bm = t;
+      break;
+    }
   int best = -1;
   for (int id = 0; id < kNumLpKernels; ++id) {
     const LpKernelDesc& k = kLpKernels[id];
-    if (!lp_fits(k, a) || (k.bm == 256) != big) continue;
+    if (!lp_fits(k, a) || k.bm != bm) continue;
     if (best < 0 || (k.mode == SGEMM_MODE_ALIGNED &&
                      kLpKernels[best].mode != SGEMM_MODE_ALIGNED))
       best = id;

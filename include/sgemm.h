@@ -269,10 +269,10 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
  * whose products or sums overflow FP32 give infinities.
  *
  * Memory: A and B are device pointers to 2-byte elements, at least 2-byte
- * aligned (SGEMM_ERR_VALUE otherwise); the fastest kernels need 16-byte
- * aligned A and B with lda and ldb multiples of 8, and M, N multiples of 128
- * and K of 64 (other arguments run the guarded kernels).  Ownership, streams,
- * errors and threading as for sgemm_run. */
+ * aligned (SGEMM_ERR_VALUE otherwise); the fastest (aligned) kernels need
+ * 16-byte aligned A and B with lda and ldb multiples of 8, M and N multiples
+ * of the tile (64, 128 or 256) and K of 64; other arguments run the guarded
+ * kernels.  Ownership, streams, errors and threading as for sgemm_run. */
 enum sgemm_dtype {
   SGEMM_DTYPE_BF16 = 1,
   SGEMM_DTYPE_F16 = 2

@@ -50,7 +50,7 @@ def test_kernel_table():
     for dt in (BF16, F16):
         for ta in (0, 1):
             for tb in (0, 1):
-                for bm in (128, 256):
+                for bm in (64, 128, 256):
                     for mode in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_GUARDED):
                         assert (dt, ta, tb, bm, mode) in combos
     for k in t:
@@ -76,10 +76,12 @@ def test_select(dt, ta, tb):
     k = _pick(dt, 4096, 4096, 4096, ta=ta, tb=tb)
     assert (k["bm"], k["mode"], k["dtype"]) == (256, sg.SGEMM_MODE_ALIGNED, dt)
     assert (k["transa"], k["transb"]) == (ta, tb)
-    k = _pick(dt, 1024, 1024, 1024, ta=ta, tb=tb)  # 16 tiles of 256: use 128
+    k = _pick(dt, 2048, 2048, 1024, ta=ta, tb=tb)  # 64 tiles of 256, 256 of 128
     assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_ALIGNED)
+    k = _pick(dt, 1024, 1024, 1024, ta=ta, tb=tb)  # 64 tiles of 128: use 64
+    assert (k["bm"], k["mode"]) == (64, sg.SGEMM_MODE_ALIGNED)
     k = _pick(dt, 1000, 1500, 777, ta=ta, tb=tb)
-    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_GUARDED)
+    assert (k["bm"], k["mode"]) == (64, sg.SGEMM_MODE_GUARDED)
     k = _pick(dt, 4100, 4100, 4100, ta=ta, tb=tb)
     assert (k["bm"], k["mode"]) == (256, sg.SGEMM_MODE_GUARDED)
     # leading dimensions that are not multiples of 8 or a base off 16 bytes
