@@ -5,44 +5,46 @@
 // C, alpha, beta in FP32: the mixed-precision matrix-unit product of the
 // gsyq.cn guide, section 5.1 (16-bit inputs, FP32 accumulation).  The
 // structure is the FP32 kernels' -- block tile staged in LDS, per-wave
-// register tile of 32x32 MFMA blocks, two LDS stages with one barrier per K
-// step, fused alpha/beta update -- with the operand tiles reshaped for the
-// 16-bit instructions:
+// register tile of 32x32 MFMA blocks, one barrier per K step, fused
+// alpha/beta update -- with the operand tiles reshaped for the 16-bit
+// instructions:
 //
 // * A K step is 64 values of k.  Each lane of a 32x32x16 MFMA supplies eight
 //   consecutive k of one row of A and of one column of B (lanes 0-31 one half
 //   of the 16, lanes 32-63 the other; which half is free as long as A and B
-//   agree), so both operand tiles are K-contiguous in LDS: one 128-byte row
-//   of 64 k per row of A and per column of B, eight 16-byte units per row.
-//   Unit c of row r sits at c ^ ((r / 2) & 7): the 16-byte fragment reads of
-//   16 consecutive rows at one unit then hit 16 distinct 16-byte bank groups.
-// * An operand stored K-contiguous (A as stored, B stored N x K) moves by
+//   agree).
+// * An operand stored K-contiguous (A as stored, B stored N x K) sits in LDS
+//   as one 128-byte row of 64 k per row of A or column of B, eight 16-byte
+//   units per row, unit c of row r at c ^ ((r / 2) & 7): a fragment is one
+//   ds_read_b128, and the reads of 16 consecutive rows at one unit hit 16
+//   distinct 16-byte bank groups.
+// * Aligned kernels: an operand stored outer-contiguous (B stored K x N, A
+//   stored K x M) keeps that layout in LDS -- rows of k holding the tile's
+//   outer indices, units XOR-swizzled per row (lp_oc_swz) -- and its
+//   fragments come from pairs of transposing reads (ds_read_b64_tr_b16), which
+//   hand each lane four k of one column.  Every operand tile then arrives by
 //   direct global-to-LDS loads (global_load_lds_dwordx4, as in the FP32
 //   kernels): lane l's 16 bytes land in slot 64*i + l of the tile, and the
-//   lane reads the global unit that the swizzle puts in that slot, so eight
-//   consecutive lanes read one 128-byte row segment.
-// * An operand stored outer-contiguous (B stored K x N, A stored K x M) is
-//   transposed on its way through registers.  A wave moves a region of
-//   64 k x 64 outer indices; lane (kb, ob) = (l % 8, l / 8) loads the 8 x 8
-//   block at k = 8kb, outer = 8ob (eight 16-byte loads, one per k row, each
-//   load instruction reading eight 128-byte row segments) and writes its
-//   eight outer rows as 16-byte units of eight k.  Lanes with odd ob write
-//   their rows in pair-swapped order (1, 0, 3, 2, ...), so the 16 lanes of
-//   one LDS write cover both row parities and all 16 bank groups.  The swap
-//   costs nothing: only the byte selector of the v_perm that builds each
-//   output dword differs between the two kinds of lanes.
+//   lane reads the global piece that the swizzle puts in that slot.
+// * Aligned kernels keep S LDS stages (two for the 256x256 tile, four for the
+//   smaller ones); the loads of step k+S go out right after step k's barrier
+//   and have S-1 steps to land.  The barrier sits before a step's last group
+//   of MFMAs, and every group issues its MFMAs one at a time with the next
+//   group's fragment reads and the loads in the slots between them, in a
+//   fixed order: one wave per SIMD keeps the matrix pipe busy without
+//   another wave to hide its reads and loads.
+// * Guarded kernels (any sizes, any 2-byte aligned operands) load every
+//   operand through registers, one step ahead, with zero fill past the edges
+//   (no lane leaves before the barriers): K-contiguous pieces go to LDS as
+//   they are; outer-contiguous ones are transposed in registers -- each lane
+//   loads an 8 x 8 block (eight 16-byte loads of k rows) and writes eight
+//   16-byte units of eight k, built by v_perm; lanes with odd block column
+//   write their rows pair-swapped, so one LDS write of 16 lanes covers all 16
+//   bank groups (only the v_perm byte selector differs).  Their stores are
+//   masked.
 // * MFMA operands are swapped (the B fragment first), so a 32x32 result is
 //   the transpose of its C block and the FP32 kernels' epilogue applies as it
 //   is: lane (li, lh) holds row li and columns 8g + 4lh + e of the block.
-// * Two modes:
-//   - aligned (MODE_ALIGNED): M, N and K whole multiples of the tile and of
-//     64, leading dimensions multiples of 8 elements and 16-byte aligned A
-//     and B, so every unit is a whole, aligned 16-byte piece;
-//   - guarded (MODE_GUARDED): any sizes and any 2-byte aligned operands.
-//     Every operand goes through registers: a 16-byte load where the unit
-//     lies wholly inside the operand and is 16-byte aligned, element loads
-//     with zero fill past the edges elsewhere (no lane leaves before the
-//     barriers), masked stores.
 #pragma once
 
 #include <hip/hip_runtime.h>
