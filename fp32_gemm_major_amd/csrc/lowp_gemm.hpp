@@ -33,15 +33,27 @@
 //   group's fragment reads and the loads in the slots between them, in a
 //   fixed order: one wave per SIMD keeps the matrix pipe busy without
 //   another wave to hide its reads and loads.
-// * Guarded kernels (any sizes, any 2-byte aligned operands) load every
-//   operand through registers, one step ahead, with zero fill past the edges
-//   (no lane leaves before the barriers): K-contiguous pieces go to LDS as
-//   they are; outer-contiguous ones are transposed in registers -- each lane
-//   loads an 8 x 8 block (eight 16-byte loads of k rows) and writes eight
-//   16-byte units of eight k, built by v_perm; lanes with odd block column
-//   write their rows pair-swapped, so one LDS write of 16 lanes covers all 16
-//   bank groups (only the v_perm byte selector differs).  Their stores are
-//   masked.
+// * Edge kernels (any sizes; M >= 8 when A is stored K x M, N >= 8 when B
+//   is stored K x N) run the whole K steps on the aligned kernels' schedule,
+//   with what lies past M or N clamped (a K-contiguous row past the edge
+//   reads the last valid row, an outer-contiguous piece wholly past the edge
+//   the last eight valid indices, a piece that straddles the edge is read as
+//   it is and runs into the next k row -- so, when one can straddle, the
+//   step holding the last K row is left out); those values only feed outputs
+//   that are never stored.  The rest of K goes through registers, zero-filled,
+//   in the K-contiguous layout, and stores are masked on edge tiles.
+// * Guarded kernels (any sizes and strides) load every operand through
+//   registers, one step ahead, with zero fill past the edges (no lane leaves
+//   before the barriers): K-contiguous pieces go to LDS as they are;
+//   outer-contiguous ones are transposed in registers -- each lane loads an
+//   8 x 8 block (eight 16-byte loads of k rows) and writes eight 16-byte units
+//   of eight k, built by v_perm; lanes with odd block column write their rows
+//   pair-swapped, so one LDS write of 16 lanes covers all 16 bank groups (only
+//   the v_perm byte selector differs).  The edge kernels' register step uses
+//   the same loads.  Their stores are masked.
+// * Global loads of both kinds, direct-to-LDS ones included, take any 2-byte
+//   aligned address on gfx950 (checked with in-bounds probes): no kernel
+//   needs aligned leading dimensions or base pointers.
 // * MFMA operands are swapped (the B fragment first), so a 32x32 result is
 //   the transpose of its C block and the FP32 kernels' epilogue applies as it
 //   is: lane (li, lh) holds row li and columns 8g + 4lh + e of the block.
@@ -174,6 +186,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
                                                    int m0, int n0,
                                                    f32x16 (&acc)[T::FM][T::FN]) {
   constexpr bool GUARD = MODE == MODE_GUARDED;
+  constexpr bool EDGE = MODE == MODE_EDGE;
   constexpr bool A_KC = !TA;  // A stored K-contiguous
   constexpr bool B_KC = TB;   // B stored K-contiguous
   const int M = g.M, N = g.N, K = g.K;
@@ -216,25 +229,39 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // u / (X/8), physical unit u % (X/8).
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
   unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
+  // Edge kernels clamp what lies past M or N: a K-contiguous row past the
+  // edge reads the last valid row; an outer-contiguous piece wholly past the
+  // edge reads the last eight valid indices (or the tile's first eight when
+  // fewer remain), and one that straddles the edge is read as it is (its
+  // elements past the edge come from the next k row).  Either kind only feeds
+  // outputs that are never stored.
   if (!GUARD) {
 #pragma unroll
     for (int v = 0; v < T::A_VEC; ++v) {
       if (A_KC) {
-        a_voff[v] = 2u * ((unsigned)a_r[v] * (unsigned)lda + 8u * (unsigned)a_c[v]);
+        int r = a_r[v];
+        if (EDGE && m0 + r >= M) r = M - 1 - m0;
+        a_voff[v] = 2u * ((unsigned)r * (unsigned)lda + 8u * (unsigned)a_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
         const int k = u / (T::BM / 8), c = (u % (T::BM / 8)) ^ lp_oc_swz<T::BM>(k);
-        a_voff[v] = 2u * ((unsigned)k * (unsigned)lda + 8u * (unsigned)c);
+        int o = 8 * c;
+        if (EDGE && m0 + o >= M) o = M - 8 > m0 ? M - 8 - m0 : 0;
+        a_voff[v] = 2u * ((unsigned)k * (unsigned)lda + (unsigned)o);
       }
     }
 #pragma unroll
     for (int v = 0; v < T::B_VEC; ++v) {
       if (B_KC) {
-        b_voff[v] = 2u * ((unsigned)b_r[v] * (unsigned)ldb + 8u * (unsigned)b_c[v]);
+        int r = b_r[v];
+        if (EDGE && n0 + r >= N) r = N - 1 - n0;
+        b_voff[v] = 2u * ((unsigned)r * (unsigned)ldb + 8u * (unsigned)b_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
         const int k = u / (T::BN / 8), c = (u % (T::BN / 8)) ^ lp_oc_swz<T::BN>(k);
-        b_voff[v] = 2u * ((unsigned)k * (unsigned)ldb + 8u * (unsigned)c);
+        int o = 8 * c;
+        if (EDGE && n0 + o >= N) o = N - 8 > n0 ? N - 8 - n0 : 0;
+        b_voff[v] = 2u * ((unsigned)k * (unsigned)ldb + (unsigned)o);
       }
     }
   }
@@ -244,9 +271,9 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   const size_t a_dstep = A_KC ? (size_t)T::BK : (size_t)T::BK * lda;
   const size_t b_dstep = B_KC ? (size_t)T::BK : (size_t)T::BK * ldb;
   // ---- register-staged operands --------------------------------------------
-  // K-contiguous operands in guarded mode: one unit per slot.
-  constexpr int A_RK = (GUARD && A_KC) ? T::A_VEC : 1;
-  constexpr int B_RK = (GUARD && B_KC) ? T::B_VEC : 1;
+  // K-contiguous operands in guarded and edge mode: one unit per slot.
+  constexpr int A_RK = ((GUARD || EDGE) && A_KC) ? T::A_VEC : 1;
+  constexpr int B_RK = ((GUARD || EDGE) && B_KC) ? T::B_VEC : 1;
   u32x4 ra_kc[A_RK], rb_kc[B_RK];
   // Outer-contiguous operands: one 8 x 8 block per lane of the loading waves.
   u32x4 ra_t[TA ? 8 : 1], rb_t[TB ? 1 : 8];
@@ -256,10 +283,11 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   const int a_to = 64 * wave + 8 * ob;  // tile-relative outer index of the block
   const int b_to = 64 * wave + 8 * ob;
 
-  // Register loads of K step kt (guarded mode).
-  auto load_regs = [&](int kt) {
+  // Register loads of K step kt (guarded mode; the last step of edge mode).
+  // ops: 1 = A, 2 = B, 3 = both.
+  auto load_regs = [&](int kt, int ops = 3) {
     const int k0 = kt * T::BK;
-    if (GUARD && A_KC) {
+    if ((GUARD || EDGE) && A_KC && (ops & 1)) {
 #pragma unroll
       for (int v = 0; v < T::A_VEC; ++v) {
         const int row = m0 + a_r[v], k = k0 + 8 * a_c[v];
@@ -267,7 +295,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
                             row < M ? K - k : 0);
       }
     }
-    if (GUARD && B_KC) {
+    if ((GUARD || EDGE) && B_KC && (ops & 2)) {
 #pragma unroll
       for (int v = 0; v < T::B_VEC; ++v) {
         const int row = n0 + b_r[v], k = k0 + 8 * b_c[v];
@@ -276,7 +304,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       }
     }
     if constexpr (TA) {
-      if (a_tw) {
+      if (a_tw && (ops & 1)) {
         const int o = m0 + a_to;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -286,7 +314,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       }
     }
     if constexpr (!TB) {
-      if (b_tw) {
+      if (b_tw && (ops & 2)) {
         const int o = n0 + b_to;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -337,21 +365,22 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       }
     }
   };
-  auto store_regs = [&](int st) {  // everything loaded by load_regs
-    if (GUARD && A_KC) {
+  auto store_regs = [&](int st, int ops = 3) {  // what load_regs loaded
+    if ((GUARD || EDGE) && A_KC && (ops & 1)) {
 #pragma unroll
       for (int v = 0; v < T::A_VEC; ++v)
         *reinterpret_cast<u32x4*>(lds + a_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
             ra_kc[v];
     }
-    if (GUARD && B_KC) {
+    if ((GUARD || EDGE) && B_KC && (ops & 2)) {
 #pragma unroll
       for (int v = 0; v < T::B_VEC; ++v)
         *reinterpret_cast<u32x4*>(lds + b_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
             rb_kc[v];
     }
 #pragma unroll
-    for (int r = 0; r < NS; ++r) store_t_row(st, r);
+    for (int r = 0; r < NS; ++r)
+      if ((TA && r < 8) ? (ops & 1) : (ops & 2)) store_t_row(st, r);
   };
 
   // ---- fragments and MFMAs: four groups of 16 k per K step ------------------
@@ -413,6 +442,19 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
     for (int r = 0; r < NF; ++r) read_one(st, q, r, f);
   };
+  // Fragments of a stage in the K-contiguous layout whatever the storage (the
+  // register-staged step of guarded and edge kernels).
+  auto read_frag_kc = [&](int st, int q, Frag& f) {
+    const int c = 2 * q + lh;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+      f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
+                                               lp_unit_off(wm * T::WM + i * 32 + li, c));
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+      f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
+                                               lp_unit_off(wn * T::WN + j * 32 + li, c));
+  };
   auto mma_one = [&](const Frag& f, int m) {
     const int i = m / T::FN, j = m % T::FN;
     acc[i][j] = lp_mfma<DT>(f.b[j], f.a[i], acc[i][j]);
@@ -441,7 +483,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         Frag f;
-        read_frag(st, q, f);
+        read_frag_kc(st, q, f);
 #pragma unroll
         for (int m = 0; m < SL; ++m) mma_one(f, m);
       }
@@ -478,6 +520,14 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     // again, and step kt+1's first fragments are read even at the last step,
     // which keeps the slots free of branches.
     constexpr int S = T::S;
+    // Direct-load steps: all of them (aligned), the whole ones (edge), and
+    // not the one holding the last K row when an outer-contiguous piece can
+    // straddle the M or N edge (its read runs into the next k row).
+    int kd = nk;
+    if (EDGE) {
+      const bool straddle = (!A_KC && (M & 7) != 0) || (!B_KC && (N & 7) != 0);
+      kd = straddle ? (K - 1) / T::BK : K / T::BK;
+    }
     auto group = [&](int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
       constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
       constexpr int st1 = st + 1 == S ? 0 : st + 1;
@@ -509,7 +559,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
     Frag f0, f1;
     auto step = [&](int kt, auto st_c) {
-      const int kl = kt + S < nk ? kt + S : nk - 1;
+      const int kl = kt + S < kd ? kt + S : kd - 1;
       group(kl, st_c, I0{}, f0, f1);
       group(kl, st_c, I1{}, f1, f0);
       group(kl, st_c, I2{}, f0, f1);
@@ -519,23 +569,48 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       __builtin_amdgcn_sched_barrier(0);
       group(kl, st_c, I3{}, f1, f0);
     };
-    // (aligned kernels run with K >= 64, so nk >= 1)  Steps 0 .. S-1 go
-    // out first; step 0 must have landed before the first barrier.
-    lp_static_for<S>([&](auto i) {
-      constexpr int st = decltype(i)::value;
-      issue_step(st < nk ? st : nk - 1, st);
-    });
-    constexpr int FIRST = (S - 1) * ND;
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (FIRST & 15) | ((FIRST >> 4) << 14));
-    wait_lds();
-    __syncthreads();
-    read_frag(0, 0, f0);
-    int kt = 0;
-    for (; kt + S <= nk; kt += S)
-      lp_static_for<S>([&](auto i) { step(kt + decltype(i)::value, i); });
-    lp_static_for<S - 1>([&](auto i) {
-      if (kt + decltype(i)::value < nk) step(kt + decltype(i)::value, i);
-    });
+    if (!EDGE || kd > 0) {  // (aligned kernels run with K >= 64)
+      // Steps 0 .. S-1 go out first; step 0 must have landed before the
+      // first barrier.
+      lp_static_for<S>([&](auto i) {
+        constexpr int st = decltype(i)::value;
+        issue_step(st < kd ? st : kd - 1, st);
+      });
+      constexpr int FIRST = (S - 1) * ND;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (FIRST & 15) | ((FIRST >> 4) << 14));
+      wait_lds();
+      __syncthreads();
+      read_frag(0, 0, f0);
+      int kt = 0;
+      for (; kt + S <= kd; kt += S)
+        lp_static_for<S>([&](auto i) { step(kt + decltype(i)::value, i); });
+      lp_static_for<S - 1>([&](auto i) {
+        if (kt + decltype(i)::value < kd) step(kt + decltype(i)::value, i);
+      });
+    }
+    if (EDGE && kd < nk) {
+      // The rest of K (at most one step) through registers, zero-filled past
+      // K, M and N, in the K-contiguous layout.  The loop's clamped
+      // look-ahead loads may still be landing: every wave waits for its own
+      // and for every other wave's reads before the stage is rewritten.
+      wait_all();
+      wait_lds();
+      __syncthreads();
+      // (A, then B: the two register sets are not live at once)
+      load_regs(kd, 1);
+      store_regs(0, 1);
+      load_regs(kd, 2);
+      store_regs(0, 2);
+      wait_lds();
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        Frag f;
+        read_frag_kc(0, q, f);
+#pragma unroll
+        for (int m = 0; m < SL; ++m) mma_one(f, m);
+      }
+    }
   }
 }
 

@@ -623,12 +623,17 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
   LP_ONE(T, DT, DTAG, "tn_", true, false, MODE, MTAG),                       \
   LP_ONE(T, DT, DTAG, "nt_", false, true, MODE, MTAG),                       \
   LP_ONE(T, DT, DTAG, "tt_", true, true, MODE, MTAG)
+// Every tile in aligned instances; the 128x128 and 64x64 tiles in edge
+// instances (a 256x256 edge kernel spills registers); the guarded instance
+// (only the 64x64 tile) takes what the others cannot: an extent under 8
+// along which an outer-contiguous operand's pieces run, or strides whose
+// tile span passes the 32-bit offsets of the direct loads.
 #define LP_FORMAT(DT, DTAG)                                                  \
   LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
   LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),               \
-  LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),             \
-  LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),             \
+  LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                   \
+  LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                     \
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded")
 
 const LpKernelDesc kLpKernels[] = {
@@ -647,18 +652,29 @@ bool lp_offsets_fit(const LpKernelDesc& k, const LpRun& a) {
   return 2 * a_far < (1LL << 32) && 2 * b_far < (1LL << 32);
 }
 
+// Direct loads (global_load_lds_dwordx4) take any 2-byte aligned address on
+// gfx950 (checked with an in-bounds probe), so no kernel needs more than the
+// 2-byte alignment every call has.
 bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
   if (k.dt != a.dt || k.ta != a.ta || k.tb != a.tb) return false;
   if (ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn) > INT_MAX) return false;
-  if (k.mode == SGEMM_MODE_GUARDED) return true;
-  return a.K > 0 && a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
-         a.lda % 8 == 0 && a.ldb % 8 == 0 && ptr_aligned16(a.A) &&
-         ptr_aligned16(a.B) && lp_offsets_fit(k, a);
+  switch (k.mode) {
+    case SGEMM_MODE_GUARDED:
+      return true;
+    case SGEMM_MODE_EDGE:
+      // an outer-contiguous piece of 8 elements needs 8 to clamp onto
+      return a.K > 0 && (!a.ta || a.M >= 8) && (a.tb || a.N >= 8) &&
+             lp_offsets_fit(k, a);
+    default:
+      return a.K > 0 && a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
+             lp_offsets_fit(k, a);
+  }
 }
 
 // The kernel for these arguments: the largest tile (256, 128, then 64
-// square) that still gives every CU a tile, else the 64x64 one; the aligned
-// instance when it fits, else the guarded one.
+// square) that still gives every CU a tile, else the 64x64 one, in its
+// aligned instance when that fits, else the edge instance of that tile (of
+// the 128x128 one in place of 256x256); else the guarded 64x64 kernel.
 int lp_select(const LpRun& a, int cus) {
   int bm = 64;
   for (int t = 256; t >= 128; t /= 2)
@@ -666,15 +682,15 @@ int lp_select(const LpRun& a, int cus) {
       bm = t;
       break;
     }
-  int best = -1;
-  for (int id = 0; id < kNumLpKernels; ++id) {
-    const LpKernelDesc& k = kLpKernels[id];
-    if (!lp_fits(k, a) || k.bm != bm) continue;
-    if (best < 0 || (k.mode == SGEMM_MODE_ALIGNED &&
-                     kLpKernels[best].mode != SGEMM_MODE_ALIGNED))
-      best = id;
-  }
-  return best;
+  static const int kOrder[3] = {SGEMM_MODE_ALIGNED, SGEMM_MODE_EDGE, SGEMM_MODE_GUARDED};
+  for (int o = 0; o < 3; ++o)
+    for (int id = 0; id < kNumLpKernels; ++id) {
+      const LpKernelDesc& k = kLpKernels[id];
+      const int want = kOrder[o] == SGEMM_MODE_EDGE && bm > 128 ? 128 : bm;
+      if (k.mode != kOrder[o] || (k.mode != SGEMM_MODE_GUARDED && k.bm != want)) continue;
+      if (lp_fits(k, a)) return id;
+    }
+  return -1;
 }
 
 Range window_bytes(const void* p, int rows, int cols, int ld, unsigned elem) {

@@ -269,10 +269,11 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
  * whose products or sums overflow FP32 give infinities.
  *
  * Memory: A and B are device pointers to 2-byte elements, at least 2-byte
- * aligned (SGEMM_ERR_VALUE otherwise); the fastest (aligned) kernels need
- * 16-byte aligned A and B with lda and ldb multiples of 8, M and N multiples
- * of the tile (64, 128 or 256) and K of 64; other arguments run the guarded
- * kernels.  Ownership, streams, errors and threading as for sgemm_run. */
+ * aligned (SGEMM_ERR_VALUE otherwise); no kernel needs more.  Kernels
+ * (sgemm_lowp_kernel_info): ALIGNED takes M and N multiples of the tile (64,
+ * 128 or 256) and K a multiple of 64; EDGE any sizes with M >= 8 when A is
+ * stored K x M and N >= 8 when B is stored K x N; GUARDED (64 x 64 only) any
+ * sizes.  Ownership, streams, errors and threading as for sgemm_run. */
 enum sgemm_dtype {
   SGEMM_DTYPE_BF16 = 1,
   SGEMM_DTYPE_F16 = 2
@@ -292,7 +293,8 @@ int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
                         float beta, const float* C, int ldc);
 
 /* Kernel table of the 16-bit product (ids 0 .. sgemm_lowp_num_kernels()-1).
- * *mode is SGEMM_MODE_ALIGNED or SGEMM_MODE_GUARDED; bk = 64. */
+ * *mode is SGEMM_MODE_ALIGNED, SGEMM_MODE_EDGE or SGEMM_MODE_GUARDED;
+ * bk = 64. */
 int sgemm_lowp_num_kernels(void);
 const char* sgemm_lowp_kernel_name(int kernel_id); /* NULL for a bad id */
 int sgemm_lowp_kernel_info(int kernel_id, int* dtype, int* bm, int* bn,

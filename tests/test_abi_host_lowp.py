@@ -51,8 +51,10 @@ def test_kernel_table():
         for ta in (0, 1):
             for tb in (0, 1):
                 for bm in (64, 128, 256):
-                    for mode in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_GUARDED):
-                        assert (dt, ta, tb, bm, mode) in combos
+                    assert (dt, ta, tb, bm, sg.SGEMM_MODE_ALIGNED) in combos
+                for bm in (64, 128):
+                    assert (dt, ta, tb, bm, sg.SGEMM_MODE_EDGE) in combos
+                assert (dt, ta, tb, 64, sg.SGEMM_MODE_GUARDED) in combos
     for k in t:
         assert k["bk"] == 64 and k["threads"] == 256 and k["bm"] == k["bn"]
         assert ("bf16" in k["name"]) == (k["dtype"] == BF16)
@@ -73,29 +75,40 @@ def _pick(dt, M, N, K, lda=None, ldb=None, ta=0, tb=0, A=1 << 20, B=1 << 33,
 @pytest.mark.parametrize("dt", [BF16, F16])
 @pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_select(dt, ta, tb):
+    A, E, G = sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE, sg.SGEMM_MODE_GUARDED
     k = _pick(dt, 4096, 4096, 4096, ta=ta, tb=tb)
-    assert (k["bm"], k["mode"], k["dtype"]) == (256, sg.SGEMM_MODE_ALIGNED, dt)
+    assert (k["bm"], k["mode"], k["dtype"]) == (256, A, dt)
     assert (k["transa"], k["transb"]) == (ta, tb)
     k = _pick(dt, 2048, 2048, 1024, ta=ta, tb=tb)  # 64 tiles of 256, 256 of 128
-    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_ALIGNED)
+    assert (k["bm"], k["mode"]) == (128, A)
     k = _pick(dt, 1024, 1024, 1024, ta=ta, tb=tb)  # 64 tiles of 128: use 64
-    assert (k["bm"], k["mode"]) == (64, sg.SGEMM_MODE_ALIGNED)
+    assert (k["bm"], k["mode"]) == (64, A)
     k = _pick(dt, 1000, 1500, 777, ta=ta, tb=tb)
-    assert (k["bm"], k["mode"]) == (64, sg.SGEMM_MODE_GUARDED)
-    k = _pick(dt, 4100, 4100, 4100, ta=ta, tb=tb)
-    assert (k["bm"], k["mode"]) == (256, sg.SGEMM_MODE_GUARDED)
-    # leading dimensions that are not multiples of 8 or a base off 16 bytes
-    k = _pick(dt, 4096, 4096, 4096, lda=4100, ta=ta, tb=tb)
-    assert k["mode"] == sg.SGEMM_MODE_GUARDED
-    k = _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 8, ta=ta, tb=tb)
-    assert k["mode"] == sg.SGEMM_MODE_GUARDED
+    assert (k["bm"], k["mode"]) == (64, E)
+    k = _pick(dt, 4100, 4100, 4100, ta=ta, tb=tb)  # edge kernels stop at 128
+    assert (k["bm"], k["mode"]) == (128, E)
+    # direct loads take any 2-byte alignment: odd leading dimensions and a
+    # base off 16 bytes stay aligned
+    k = _pick(dt, 4096, 4096, 4096, lda=4099, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (256, A)
+    k = _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 2, ta=ta, tb=tb)
+    assert k["mode"] == A
     assert _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 1) == sg.SGEMM_ERR_VALUE
+    # an extent under 8 along an outer-contiguous operand's pieces
+    k = _pick(dt, 7 if ta else 300, 300 if ta else (300 if tb else 7), 100, ta=ta, tb=tb)
+    if ta or not tb:
+        assert (k["bm"], k["mode"]) == (64, G)
+    else:
+        assert k["mode"] == E
 
 
 def test_huge_strides_go_to_the_guarded_kernel():
-    """A K-contiguous operand whose tile spans more than 4 GiB cannot use the
-    32-bit lane offsets of the direct loads."""
+    """An operand whose tile spans more than 4 GiB in one K step cannot use
+    the 32-bit lane offsets of the direct loads."""
+    # 255 rows of lda 2^24 + 8 pass 4 GiB, 127 rows (the 128x128 edge kernel) do not
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8)
+    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_EDGE)
+    k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 25) + 8, B=1 << 42, C=1 << 44)
     assert k["mode"] == sg.SGEMM_MODE_GUARDED
     # stored K x M, one K step of a tile spans 63 rows of A
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8, ta=1)
