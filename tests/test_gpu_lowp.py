@@ -214,3 +214,24 @@ def test_aligned_kernels_short_k(handle, nk):
         ops = wl.operands16(w, DT_NAME[k["dtype"]], ta=ta, tb=tb)
         out = gu.run16(handle, ops)
         gu.check_full16(ops, out, exact=True, what=f"{k['name']} nk={nk}")
+
+
+@pytest.mark.parametrize("case", ["k_whole_straddle", "k_whole_no_straddle", "k_short",
+                                  "k_one_past"])
+def test_edge_kernels_k_cases(handle, case):
+    """Edge kernels: K a multiple of 64 with an M or N edge that is not a
+    multiple of 8 (the last whole K step goes through registers), the same
+    with multiples of 8 (every step a direct load), K under 64 (no direct
+    steps at all) and K one past a multiple of 64."""
+    M, N, K = {"k_whole_straddle": (150, 133, 192), "k_whole_no_straddle": (152, 136, 192),
+               "k_short": (150, 133, 40), "k_one_past": (150, 133, 129)}[case]
+    for k in KERNELS:
+        if k["mode"] != sg.SGEMM_MODE_EDGE:
+            continue
+        handle.set_lowp_kernel(k["id"])
+        ta, tb = bool(k["transa"]), bool(k["transb"])
+        w = wl.Workload("edgek", 850 + k["id"] % 50, M, N, K, 1.5, -0.5, "int4")
+        ops = wl.operands16(w, DT_NAME[k["dtype"]], ta=ta, tb=tb,
+                            lda=(M if ta else K) + 1, ldb=(K if tb else N) + 3, ldc=N + 2)
+        out = gu.run16(handle, ops)
+        gu.check_full16(ops, out, exact=True, what=f"{k['name']} {case}")
