@@ -1,0 +1,107 @@
+"""CPU model of the 16-bit kernels' direct (global-to-LDS) loads: for every
+tile, every 16-byte piece and every K step that the aligned and edge
+instances load without bounds checks -- including the look-ahead steps past
+the end of K, which the kernel clamps to the last direct-load step -- the
+8 elements read must lie inside the stored operand.  The model follows the
+kernel's own arithmetic (lowp_gemm.hpp): the slot-to-piece mapping of each
+layout, the row clamp (K-contiguous) and the piece clamp (outer-contiguous)
+of the edge kernels, the 32-bit per-lane byte offsets added to a wave-uniform
+base, and the rule that leaves the last K row out of the direct loads when a
+piece can straddle the M or N edge.  It needs the built library only for the
+kernel table; it launches nothing."""
+import numpy as np
+import pytest
+
+import fp32_gemm_major_amd as sg
+
+KERNELS = sg.lowp_kernel_table() if __import__("os").path.exists(sg.LIBRARY) else []
+DIRECT = [k for k in KERNELS if k["mode"] in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE)
+          and k["dtype"] == sg.SGEMM_DTYPE_BF16]
+BK = 64
+
+
+def oc_swz(X, k):
+    return 4 * (k & 3) if X >= 128 else 4 * ((k >> 1) & 1)
+
+
+def direct_steps(edge, M, N, K, ta, tb):
+    """K steps the direct loads cover (the kernel's kd)."""
+    if not edge:
+        return K // BK
+    straddle = (ta and M % 8) or (not tb and N % 8)
+    return (K - 1) // BK if straddle else K // BK
+
+
+def piece_offsets(kcontig, X, extent, origin, ld, edge):
+    """Element offset, relative to the tile's origin at K step 0, of the
+    first of the 8 elements of every slot of one operand tile."""
+    units = X * BK // 8
+    u = np.arange(units)
+    if kcontig:                       # row r = u // 8, unit c = (u % 8) ^ ((r // 2) % 8)
+        r = u // 8
+        c = (u % 8) ^ ((r >> 1) & 7)
+        if edge:
+            r = np.where(origin + r >= extent, extent - 1 - origin, r)
+        return r * ld + 8 * c
+    k = u // (X // 8)                 # outer-contiguous: row k, unit swizzled by k
+    c = (u % (X // 8)) ^ np.array([oc_swz(X, int(x)) for x in k])
+    o = 8 * c
+    if edge:
+        past = origin + o >= extent
+        o = np.where(past, extent - 8 - origin if extent - 8 > origin else 0, o)
+    return k * ld + o
+
+
+def operand_reads(kcontig, X, extent, K, ld, steps, edge):
+    """[first, last] element of every direct load of one operand, relative
+    to its base, over all tiles and every step the kernel issues (0 .. kd-1,
+    and the clamped look-ahead steps, which repeat step kd-1)."""
+    lo, hi = [], []
+    for origin in range(0, extent, X):
+        off = piece_offsets(kcontig, X, extent, origin, ld, edge)
+        # the per-lane byte offsets are 32-bit: negative ones would wrap
+        assert off.min() >= 0 and 2 * off.max() < 2 ** 32
+        base = origin * ld if kcontig else origin
+        for kt in range(steps):       # look-ahead steps repeat steps-1: nothing new
+            step = kt * BK if kcontig else kt * BK * ld
+            first = base + step + off
+            lo.append(first.min())
+            hi.append((first + 7).max())
+    return (min(lo), max(hi)) if lo else (0, -1)
+
+
+CASES = [(4096, 4096, 4096), (1000, 1500, 777), (150, 133, 192), (152, 136, 192),
+         (150, 133, 40), (150, 133, 129), (64, 64, 64), (8, 9, 65), (300, 8, 128),
+         (257, 255, 1000)]
+
+
+@pytest.mark.parametrize("k", DIRECT, ids=[k["name"] for k in DIRECT])
+def test_direct_loads_stay_inside_the_operands(k):
+    edge = k["mode"] == sg.SGEMM_MODE_EDGE
+    ta, tb = bool(k["transa"]), bool(k["transb"])
+    for (M, N, K) in CASES:
+        if not edge and (M % k["bm"] or N % k["bn"] or K % BK):
+            continue
+        if edge and ((ta and M < 8) or (not tb and N < 8)):
+            continue
+        for pad in (0, 1, 7):
+            lda = (M if ta else K) + pad
+            ldb = (K if tb else N) + pad
+            kd = direct_steps(edge, M, N, K, ta, tb)
+            a_rows, a_cols = (K, M) if ta else (M, K)
+            b_rows, b_cols = (N, K) if tb else (K, N)
+            a_lo, a_hi = operand_reads(not ta, k["bm"], M, K, lda, kd, edge)
+            b_lo, b_hi = operand_reads(tb, k["bn"], N, K, ldb, kd, edge)
+            tag = f"{k['name']} {M}x{N}x{K} pad {pad}"
+            assert a_lo >= 0 and a_hi <= (a_rows - 1) * lda + a_cols - 1, tag + " A"
+            assert b_lo >= 0 and b_hi <= (b_rows - 1) * ldb + b_cols - 1, tag + " B"
+
+
+def test_straddle_rule_is_needed():
+    """Without leaving the last K row out, a straddling piece of the last row
+    would read past the end of B (the model catches it)."""
+    M, N, K = 150, 133, 192
+    ldb = N
+    with pytest.raises(AssertionError):
+        lo, hi = operand_reads(False, 64, N, K, ldb, K // BK, True)
+        assert hi <= (K - 1) * ldb + N - 1
