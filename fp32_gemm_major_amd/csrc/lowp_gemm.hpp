@@ -221,12 +221,12 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     b_r[v] = u >> 3;
     b_c[v] = (u & 7) ^ ((b_r[v] >> 1) & 7);
   }
-  // Direct loads (aligned mode): wave-uniform base at the tile's origin,
-  // advanced 64 elements per K step, and fixed per-lane byte offsets (the
-  // host keeps them below 2^32).
-  // An operand stored outer-contiguous keeps that layout in aligned mode
-  // (rows of k, units swizzled by lp_oc_swz).  Slot u of such a tile is row
-  // u / (X/8), physical unit u % (X/8).
+  // Direct loads (aligned and edge modes): a wave-uniform base at the tile's
+  // origin, advanced one K step per step, and fixed per-lane byte offsets
+  // (the host keeps them below 2^32).  An operand stored outer-contiguous
+  // keeps that layout in these modes (rows of k, units swizzled by
+  // lp_oc_swz): slot u of such a tile is row u / (X/8), physical unit
+  // u % (X/8).
   const unsigned lds_u = (unsigned)(uintptr_t)(lds_void_t*)lds;
   unsigned a_voff[T::A_VEC], b_voff[T::B_VEC];
   // Edge kernels clamp what lies past M or N: a K-contiguous row past the

@@ -23,7 +23,9 @@ B=2, C=3, so values do not depend on the leading dimensions chosen.
 
 Products with 16-bit A and B (bfloat16 or IEEE binary16, FP32 C) draw the same
 FP32 values and round them to the 16-bit format, nearest-even
-(``round16``); the bit patterns are what both sides receive.
+(``round16``); the bit patterns are what both sides receive.  Products with
+8-bit A and B (the OCP E4M3 and E5M2 formats) round them the same way with
+torch's conversions (``round8``).
 """
 from __future__ import annotations
 
@@ -103,13 +105,35 @@ def round16(values: np.ndarray, dt: str) -> np.ndarray:
     raise ValueError(f"unknown 16-bit format {dt!r}")
 
 
-def place16(bits: np.ndarray, ld: int, pad_value=0x7FC0) -> np.ndarray:
-    """``place`` for 16-bit patterns; padding defaults to a NaN pattern of both
-    formats (0x7FC0 is a quiet NaN in bfloat16 and in binary16)."""
+FORMATS8 = ("fp8e4m3", "fp8e5m2")
+
+
+def round8(values: np.ndarray, dt: str) -> np.ndarray:
+    """Bit patterns (uint8) of FP32 ``values`` rounded to the nearest E4M3 or
+    E5M2 value, ties to even (torch's conversions; values must lie inside the
+    format's finite range)."""
+    import torch
+
+    x = np.ascontiguousarray(values, dtype=np.float32)
+    tdt = {"fp8e4m3": torch.float8_e4m3fn, "fp8e5m2": torch.float8_e5m2}.get(dt)
+    if tdt is None:
+        raise ValueError(f"unknown 8-bit format {dt!r}")
+    limit = 448.0 if dt == "fp8e4m3" else 57344.0
+    if not np.all(np.isfinite(x)) or np.abs(x).max(initial=0.0) > limit:
+        raise ValueError("round8 takes values inside the format's finite range")
+    return torch.from_numpy(x).to(tdt).view(torch.uint8).numpy().copy()
+
+
+def place16(bits: np.ndarray, ld: int, pad_value=None) -> np.ndarray:
+    """``place`` for 16-bit or 8-bit patterns; padding defaults to a NaN
+    pattern of the formats of that width (0x7FC0 is a quiet NaN in bfloat16
+    and binary16, 0x7F in E4M3 and E5M2)."""
+    if pad_value is None:
+        pad_value = 0x7F if bits.dtype == np.uint8 else 0x7FC0
     rows, cols = bits.shape
     if ld < cols:
         raise ValueError("ld < cols")
-    buf = np.full((rows, ld), pad_value, dtype=np.uint16)
+    buf = np.full((rows, ld), pad_value, dtype=bits.dtype)
     buf[:, :cols] = bits
     return buf.reshape(-1)
 
@@ -177,16 +201,17 @@ def operands(w: Workload, lda=None, ldb=None, ldc=None, pad_value=np.nan,
 
 @dataclass
 class Operands16:
-    """Operands of the product with 16-bit A and B (bit patterns) and FP32 C."""
+    """Operands of the product with 16-bit or 8-bit A and B (bit patterns)
+    and FP32 C."""
     dt: str
     M: int
     N: int
     K: int
     alpha: float
     beta: float
-    A: np.ndarray  # flat uint16: M rows of lda (K rows of lda when ta)
+    A: np.ndarray  # flat uint16 / uint8: M rows of lda (K rows of lda when ta)
     lda: int
-    B: np.ndarray  # flat uint16: K rows of ldb (N rows of ldb when tb)
+    B: np.ndarray  # flat uint16 / uint8: K rows of ldb (N rows of ldb when tb)
     ldb: int
     C: np.ndarray  # flat FP32, M*ldc (C_in)
     ldc: int
@@ -196,16 +221,17 @@ class Operands16:
 
 def operands16(w: Workload, dt: str, lda=None, ldb=None, ldc=None, M=None, N=None,
                K=None, ta=False, tb=False) -> Operands16:
-    """Inputs of workload ``w`` with A and B rounded to the 16-bit format ``dt``;
-    C is drawn exactly as in ``operands``."""
+    """Inputs of workload ``w`` with A and B rounded to the 16-bit or 8-bit
+    format ``dt``; C is drawn exactly as in ``operands``."""
     if M is not None or N is not None or K is not None:
         w = replace(w, M=w.M if M is None else M, N=w.N if N is None else N,
                     K=w.K if K is None else K)
     lda = max(w.M if ta else w.K, 1) if lda is None else lda
     ldb = max(w.K if tb else w.N, 1) if ldb is None else ldb
     ldc = max(w.N, 1) if ldc is None else ldc
-    a = round16(draw(w.cfg_id, ROLE_A, w.M, w.K, w.dist), dt)
-    b = round16(draw(w.cfg_id, ROLE_B, w.K, w.N, w.dist), dt)
+    rnd = round8 if dt in FORMATS8 else round16
+    a = rnd(draw(w.cfg_id, ROLE_A, w.M, w.K, w.dist), dt)
+    b = rnd(draw(w.cfg_id, ROLE_B, w.K, w.N, w.dist), dt)
     if ta:
         a = np.ascontiguousarray(a.T)
     if tb:

@@ -14,8 +14,9 @@ exact arithmetic.  Results come back unrounded (FP64) as ``r``; the FP32
 result of the operation is ``r`` rounded to nearest-even (``to_f32``).
 
 ``gemm_lowp`` is the same product with A and B stored as 16-bit patterns
-(bfloat16 or IEEE binary16, ``DT_BF16`` / ``DT_F16``), C and the sums as
-above: the mixed-precision matrix-unit product of the gsyq.cn guide,
+(bfloat16 or IEEE binary16, ``DT_BF16`` / ``DT_F16``) or 8-bit patterns (the
+OCP E4M3 and E5M2 formats, ``DT_FP8_E4M3`` / ``DT_FP8_E5M2``), C and the sums
+as above: the mixed-precision matrix-unit product of the gsyq.cn guide,
 section 5.1.
 
 Pins (tests/test_oracle_pins.py) tie it to exact rational brute force, integer
@@ -78,6 +79,10 @@ def _bind(lib):
     lib.oracle_gemm_lowp_points.argtypes = [i, i, i, i, i, i, f, p, i, p, i, f, p, i,
                                             i, p, p, p, p, i]
     lib.oracle_gemm_lowp_points.restype = i
+    lib.oracle_gemm_fp8.argtypes = lib.oracle_gemm_lowp.argtypes
+    lib.oracle_gemm_fp8.restype = i
+    lib.oracle_gemm_fp8_points.argtypes = lib.oracle_gemm_lowp_points.argtypes
+    lib.oracle_gemm_fp8_points.restype = i
     return lib
 
 
@@ -188,7 +193,11 @@ def gemm_points(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
 
 DT_BF16 = 1
 DT_F16 = 2
-_DT_NAMES = {"bf16": DT_BF16, "f16": DT_F16, DT_BF16: DT_BF16, DT_F16: DT_F16}
+DT_FP8_E4M3 = 3
+DT_FP8_E5M2 = 4
+_DT_NAMES = {"bf16": DT_BF16, "f16": DT_F16, "fp8e4m3": DT_FP8_E4M3,
+             "fp8e5m2": DT_FP8_E5M2, DT_BF16: DT_BF16, DT_F16: DT_F16,
+             DT_FP8_E4M3: DT_FP8_E4M3, DT_FP8_E5M2: DT_FP8_E5M2}
 
 
 def _dt(dt):
@@ -198,23 +207,28 @@ def _dt(dt):
         raise ValueError(f"unknown 16-bit format {dt!r}") from None
 
 
-def _u16(x, name):
+def _bits(x, name, dt):
+    """Flat bit-pattern array: uint16 for the 16-bit formats, uint8 for the
+    8-bit ones."""
+    want = np.uint8 if dt >= DT_FP8_E4M3 else np.uint16
     a = np.ascontiguousarray(x).reshape(-1)
-    if a.dtype != np.uint16:
-        raise ValueError(f"{name}: 16-bit bit patterns (uint16) expected, got {a.dtype}")
+    if a.dtype != want:
+        raise ValueError(f"{name}: {np.dtype(want).name} bit patterns expected, got {a.dtype}")
     return a
 
 
 def gemm_lowp(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
               nthreads=None, lib=None, ta=False, tb=False):
-    """Full product with A and B stored as 16-bit patterns (uint16 arrays).
+    """Full product with A and B stored as 16-bit patterns (uint16 arrays) or
+    8-bit patterns (uint8 arrays).
 
-    ``dt``: "bf16" / DT_BF16 or "f16" / DT_F16.  Everything else as ``gemm``.
+    ``dt``: "bf16" / DT_BF16, "f16" / DT_F16, "fp8e4m3" / DT_FP8_E4M3 or
+    "fp8e5m2" / DT_FP8_E5M2.  Everything else as ``gemm``.
     """
     dt = _dt(dt)
     lib = lib or load()
-    A = _u16(A, "A")
-    B = _u16(B, "B")
+    A = _bits(A, "A", dt)
+    B = _bits(B, "B", dt)
     _need_ops(A, B, M, N, K, lda, ldb, ta, tb)
     if C is not None:
         C = _f32(C, "C")
@@ -224,7 +238,8 @@ def gemm_lowp(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
         raise ValueError("C is required when beta != 0")
     R = np.zeros((M, N), dtype=np.float64)
     T = np.zeros((M, N), dtype=np.float64) if with_t else None
-    rc = lib.oracle_gemm_lowp(dt, int(bool(ta)), int(bool(tb)), M, N, K, float(alpha),
+    fn = lib.oracle_gemm_fp8 if dt >= DT_FP8_E4M3 else lib.oracle_gemm_lowp
+    rc = fn(dt, int(bool(ta)), int(bool(tb)), M, N, K, float(alpha),
                               _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
                               _ptr(R), max(N, 1), _ptr(T), max(N, 1),
                               nthreads or default_threads())
@@ -235,11 +250,11 @@ def gemm_lowp(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, *, with_t=True,
 
 def gemm_lowp_points(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, cols, *,
                      nthreads=None, lib=None, ta=False, tb=False):
-    """Outputs of the 16-bit product at (rows[p], cols[p]) only."""
+    """Outputs of the 16-bit or 8-bit product at (rows[p], cols[p]) only."""
     dt = _dt(dt)
     lib = lib or load()
-    A = _u16(A, "A")
-    B = _u16(B, "B")
+    A = _bits(A, "A", dt)
+    B = _bits(B, "B", dt)
     _need_ops(A, B, M, N, K, lda, ldb, ta, tb)
     if C is not None:
         C = _f32(C, "C")
@@ -252,7 +267,8 @@ def gemm_lowp_points(dt, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, rows, col
     n = rows.size
     r = np.zeros(n, dtype=np.float64)
     t = np.zeros(n, dtype=np.float64)
-    rc = lib.oracle_gemm_lowp_points(dt, int(bool(ta)), int(bool(tb)), M, N, K,
+    fn = lib.oracle_gemm_fp8_points if dt >= DT_FP8_E4M3 else lib.oracle_gemm_lowp_points
+    rc = fn(dt, int(bool(ta)), int(bool(tb)), M, N, K,
                                      float(alpha), _ptr(A), lda, _ptr(B), ldb,
                                      float(beta), _ptr(C), ldc, n, _ptr(rows),
                                      _ptr(cols), _ptr(r), _ptr(t),
@@ -274,9 +290,10 @@ def error_bound(K, alpha, beta, t, c_in):
     beta term taken as 0 when beta == 0 (C is then not read and may hold NaN).
     The form is the standard a-priori bound for a length-K FP32 dot product
     (gamma_K = K*u/(1 - K*u), u = 2**-24) widened to cover the few roundings of
-    the alpha/beta update.  It holds unchanged for 16-bit A and B accumulated
-    in FP32: the product of two bfloat16 or binary16 values is exact in FP32
-    (at most 22 significant bits), so again only the FP32 additions round.
+    the alpha/beta update.  It holds unchanged for 16-bit or 8-bit A and B
+    accumulated in FP32: the product of two bfloat16, binary16, E4M3 or E5M2
+    values is exact in FP32 (at most 22 significant bits), so again only the
+    FP32 additions round.
     """
     t = np.asarray(t, dtype=np.float64)
     scale = abs(float(alpha)) * t

@@ -37,6 +37,13 @@
  *     infinities and NaNs.
  * C, alpha and beta stay FP32 and the sums are the FP64 sums above: the
  * product of two 16-bit values is exact in FP64 as well.
+ * The same with 8-bit A and B (oracle_gemm_fp8), in the two OCP 8-bit
+ * floating-point formats:
+ *   - E4M3: 1 sign, 4 exponent bits with bias 7, 3 fraction bits; exponent 0
+ *     holds subnormals (fraction * 2^-9); the pattern with all exponent and
+ *     fraction bits set is NaN; there are no infinities;
+ *   - E5M2: 1 sign, 5 exponent bits with bias 15, 2 fraction bits; exponent 0
+ *     holds subnormals (fraction * 2^-16), exponent 31 infinities and NaNs.
  *
  * The loop nest follows the CPU reference on the same page (its complete
  * listing): rows outer, then k, then columns, with a row of accumulators.
@@ -56,9 +63,11 @@ typedef struct {
   int ta, tb;  /* transposed storage of A / B */
   double alpha, beta;
   const float *A, *B, *C;
-  /* 16-bit storage of A and B (dt != DT_F32): bit patterns, same indexing */
+  /* 16-bit or 8-bit storage of A and B (dt != DT_F32): bit patterns, same
+   * indexing */
   int dt;
   const uint16_t *A16, *B16;
+  const uint8_t *A8, *B8;
   long lda, ldb, ldc;
   double *R, *T;
   long ldr, ldt;
@@ -70,7 +79,7 @@ typedef struct {
 } job_t;
 
 /* Element formats. */
-enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 
 /* bfloat16: the pattern is the upper half of an IEEE binary32 number. */
 static double bf16_value(uint16_t h) {
@@ -98,14 +107,52 @@ static double value16(int dt, uint16_t h) {
   return dt == DT_BF16 ? bf16_value(h) : f16_value(h);
 }
 
+/* E4M3: (-1)^s * 2^(e-7) * (1 + m/8) for e > 0, (-1)^s * 2^-6 * (m/8) for
+ * e == 0; exponent and fraction all ones is NaN. */
+static double e4m3_value(uint8_t b) {
+  const int s = (b >> 7) & 1, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10);
+  return s != 0 ? -v : v;
+}
+
+/* E5M2: (-1)^s * 2^(e-15) * (1 + m/4) for 0 < e < 31, (-1)^s * 2^-14 * (m/4)
+ * for e == 0, infinity or NaN for e == 31. */
+static double e5m2_value(uint8_t b) {
+  const int s = (b >> 7) & 1, e = (b >> 2) & 31, m = b & 3;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -16);
+  else
+    v = ldexp((double)(4 + m), e - 17);
+  return (s != 0) ? -v : v;
+}
+
+static double value8(int dt, uint8_t b) {
+  return dt == DT_E4M3 ? e4m3_value(b) : e5m2_value(b);
+}
+
 /* Element (i,k) of A and (k,j) of B under the storage flags. */
 static double a_at(const job_t *j, int i, int k) {
+  if (j->dt >= DT_E4M3)
+    return value8(j->dt, j->ta ? j->A8[(long)k * j->lda + i]
+                               : j->A8[(long)i * j->lda + k]);
   if (j->dt != DT_F32)
     return value16(j->dt, j->ta ? j->A16[(long)k * j->lda + i]
                                 : j->A16[(long)i * j->lda + k]);
   return (double)(j->ta ? j->A[(long)k * j->lda + i] : j->A[(long)i * j->lda + k]);
 }
 static double b_at(const job_t *j, int k, int c) {
+  if (j->dt >= DT_E4M3)
+    return value8(j->dt, j->tb ? j->B8[(long)c * j->ldb + k]
+                               : j->B8[(long)k * j->ldb + c]);
   if (j->dt != DT_F32)
     return value16(j->dt, j->tb ? j->B16[(long)c * j->ldb + k]
                                 : j->B16[(long)k * j->ldb + c]);
@@ -302,6 +349,56 @@ int oracle_gemm_lowp_points(int dt, int ta, int tb, int M, int N, int K,
   j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;
   j.lda = lda; j.ldb = ldb; j.ldc = ldc;
   j.npts = npts; j.rows = rows; j.cols = cols;
+  j.R = r_out; j.T = t_out;
+  run_split(points, &j, npts, nthreads);
+  return 0;
+}
+
+/*
+ * The same products with A and B in an 8-bit format: dt = 3 for E4M3, 4 for
+ * E5M2 (bit patterns as stored).  C, alpha, beta, R and T as in
+ * oracle_sgemm_ex.  Returns 0, -1/-2 as there, or -4 for an unknown dt.
+ */
+int oracle_gemm_fp8(int dt, int ta, int tb, int M, int N, int K, float alpha,
+                    const uint8_t *A, int lda, const uint8_t *B, int ldb,
+                    float beta, const float *C, int ldc, double *R, int ldr,
+                    double *T, int ldt, int nthreads) {
+  if (dt != DT_E4M3 && dt != DT_E5M2) return -4;
+  int e = check_args(ta, tb, M, N, K, lda, ldb, ldc);
+  if (e) return e;
+  if (ldr < N || (T && ldt < N)) return -2;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.M = M; j.N = N; j.K = K;
+  j.ta = ta != 0; j.tb = tb != 0;
+  j.alpha = (double)alpha; j.beta = (double)beta;
+  j.dt = dt; j.A8 = A; j.B8 = B; j.C = C;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.R = R; j.T = T; j.ldr = ldr; j.ldt = ldt;
+  if (N > 0) run_split(full_rows, &j, M, nthreads);
+  return 0;
+}
+
+/* Selected outputs of the 8-bit product, as oracle_sgemm_points_ex. */
+int oracle_gemm_fp8_points(int dt, int ta, int tb, int M, int N, int K,
+                           float alpha, const uint8_t *A, int lda,
+                           const uint8_t *B, int ldb, float beta,
+                           const float *C, int ldc, int npts, const int *rows,
+                           const int *cols, double *r_out, double *t_out,
+                           int nthreads) {
+  if (dt != DT_E4M3 && dt != DT_E5M2) return -4;
+  int e = check_args(ta, tb, M, N, K, lda, ldb, ldc);
+  if (e) return e;
+  for (int p = 0; p < npts; ++p)
+    if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N) return -3;
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.M = M; j.N = N; j.K = K;
+  j.ta = ta != 0; j.tb = tb != 0;
+  j.alpha = (double)alpha; j.beta = (double)beta;
+  j.dt = dt; j.A8 = A; j.B8 = B; j.C = C;
+  j.lda = lda; j.ldb = ldb; j.ldc = ldc;
+  j.rows = rows; j.cols = cols; j.npts = npts;
   j.R = r_out; j.T = t_out;
   run_split(points, &j, npts, nthreads);
   return 0;

@@ -431,7 +431,104 @@ def pin_lowp_bruteforce(lib, seed=47, cases=16):
                 assert err <= Fraction((K + 3) * U * t), (dt, case, i, j)
 
 
+# ---- 8-bit A and B (OCP E4M3, E5M2), FP32 C ---------------------------------
+
+FP8_ONE = {"fp8e4m3": 0x38, "fp8e5m2": 0x3C}  # 1.0
+
+
+def values8(bits, dt):
+    """FP64 values of 8-bit patterns by torch's conversions."""
+    import torch
+    tdt = {"fp8e4m3": torch.float8_e4m3fn, "fp8e5m2": torch.float8_e5m2}[dt]
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    return torch.from_numpy(bits).view(tdt).double().numpy()
+
+
+def pin_fp8_decode(lib):
+    """All 256 patterns of each 8-bit format, as an A element and as a B
+    element (product with 1.0), and in transposed storage, equal torch's
+    conversions (NaN for NaN, infinities for E5M2's)."""
+    allbits = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    for dt, one in FP8_ONE.items():
+        want = values8(allbits, dt)
+        onev = np.array([one], np.uint8)
+        R, _ = oracle.gemm_lowp(dt, 256, 1, 1, 1.0, allbits, 1, onev, 1, 0.0, None, 1,
+                                with_t=False, lib=lib)
+        assert _same_values(R[:, 0], want), f"{dt}: A-side decode differs"
+        R, _ = oracle.gemm_lowp(dt, 1, 256, 1, 1.0, onev, 1, allbits, 256, 0.0, None, 256,
+                                with_t=False, lib=lib)
+        assert _same_values(R[0, :], want), f"{dt}: B-side decode differs"
+        R, _ = oracle.gemm_lowp(dt, 256, 1, 1, 1.0, allbits, 256, onev, 1, 0.0, None, 1,
+                                with_t=False, lib=lib, ta=True, tb=True)
+        assert _same_values(R[:, 0], want), f"{dt}: transposed decode differs"
+
+
+def pin_fp8_matches_f32(lib, seed=53):
+    """On values the 8-bit formats hold exactly, the 8-bit product equals the
+    FP32 oracle's bit for bit (full and point modes, every storage, padded
+    leading dimensions)."""
+    from fp32_gemm_major_amd import workloads as wl
+    rng = np.random.default_rng(seed)
+    for dt in wl.FORMATS8:
+        for ci, (M, N, K, alpha, beta) in enumerate([(5, 7, 9, 1.0, 0.0),
+                                                     (13, 4, 21, 1.5, 0.5),
+                                                     (3, 11, 1, -2.0, 1.0)]):
+            for ta in (False, True):
+                for tb in (False, True):
+                    def operand(rows, cols):
+                        x = (2.0 * rng.random((rows, cols)) - 1.0).astype(np.float32)
+                        x *= np.float32(2.0) ** rng.integers(-6, 4, (rows, cols)).astype(np.float32)
+                        bits = wl.round8(x, dt)
+                        buf = np.zeros((rows, cols + 3), np.uint8)
+                        buf[:, :cols] = bits
+                        val = np.zeros((rows, cols + 3), np.float32)
+                        val[:, :cols] = values8(bits, dt)
+                        return buf, val
+                    A8, A32 = operand(*((K, M) if ta else (M, K)))
+                    B8, B32 = operand(*((N, K) if tb else (K, N)))
+                    C = _dyadic(rng, (M, N))
+                    lda, ldb = A8.shape[1], B8.shape[1]
+                    R8, T8 = oracle.gemm_lowp(dt, M, N, K, alpha, A8, lda, B8, ldb, beta, C,
+                                              N, lib=lib, ta=ta, tb=tb)
+                    R32, T32 = oracle.gemm(M, N, K, alpha, A32, lda, B32, ldb, beta, C, N,
+                                           lib=lib, ta=ta, tb=tb)
+                    tag = f"{dt} case {ci} ta={ta} tb={tb}"
+                    assert np.array_equal(R8, R32) and np.array_equal(T8, T32), tag
+                    rows, cols = rng.integers(0, M, 6), rng.integers(0, N, 6)
+                    rp, tp = oracle.gemm_lowp_points(dt, M, N, K, alpha, A8, lda, B8, ldb,
+                                                     beta, C, N, rows, cols, lib=lib,
+                                                     ta=ta, tb=tb)
+                    assert np.array_equal(rp, R32[rows, cols]), tag + " points"
+                    assert np.array_equal(tp, T32[rows, cols]), tag + " points t"
+
+
+def pin_fp8_bruteforce(lib, seed=59, cases=12):
+    """Tiny 8-bit products over every finite pattern class (subnormals
+    included) against exact rational sums of torch-decoded values."""
+    rng = np.random.default_rng(seed)
+    for case in range(cases):
+        dt = "fp8e5m2" if case % 2 else "fp8e4m3"
+        M, N, K = (int(x) for x in rng.integers(1, 6, size=3))
+        top = 0x7E if dt == "fp8e4m3" else 0x7B   # largest finite magnitude
+        a_bits = rng.integers(0, top + 1, (M, K)).astype(np.uint8)
+        b_bits = rng.integers(0, top + 1, (K, N)).astype(np.uint8)
+        a_bits |= (rng.integers(0, 2, a_bits.shape) << 7).astype(np.uint8)
+        b_bits |= (rng.integers(0, 2, b_bits.shape) << 7).astype(np.uint8)
+        av, bv = values8(a_bits, dt), values8(b_bits, dt)
+        R, _ = oracle.gemm_lowp(dt, M, N, K, 1.0, a_bits, K, b_bits, N, 0.0, None, N,
+                                lib=lib)
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(float(av[i, k])) * Fraction(float(bv[k, j]))
+                         for k in range(K)]
+                exact = sum(terms, Fraction(0))
+                t = float(sum((abs(x) for x in terms), Fraction(0)))
+                assert abs(Fraction(float(R[i, j])) - exact) <= Fraction((K + 3) * U * t), \
+                    (dt, case, i, j)
+
+
 ALL_PINS = [pin_bruteforce_exact, pin_integer_exact, pin_identity,
             pin_permutation, pin_rank1, pin_alpha_beta, pin_transpose,
             pin_leading_dims, pin_transposed_storage, pin_transposed_bruteforce,
-            pin_lowp_decode, pin_lowp_matches_f32, pin_lowp_bruteforce]
+            pin_lowp_decode, pin_lowp_matches_f32, pin_lowp_bruteforce,
+            pin_fp8_decode, pin_fp8_matches_f32, pin_fp8_bruteforce]

@@ -52,6 +52,17 @@ MUTANTS = {
     "lowp_ta_ignored": ("j->ta ? j->A16[(long)k * j->lda + i]", "j->ta ? j->A16[(long)i * j->lda + k]"),
     "lowp_tb_ignored": ("j->tb ? j->B16[(long)c * j->ldb + k]", "j->tb ? j->B16[(long)k * j->ldb + c]"),
     "lowp_b_ld": ("j->B16[(long)k * j->ldb + c]", "j->B16[(long)k * j->lda + c]"),
+    # 8-bit formats
+    "e4m3_sign_dropped": ("  return s != 0 ? -v : v;", "  return v;"),
+    "e5m2_sign_dropped": ("  return (s != 0) ? -v : v;", "  return v;"),
+    "e4m3_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 9)"),
+    "e4m3_nan_rule": ("if (e == 15 && m == 7)", "if (e == 15)"),
+    "e4m3_subnormal": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "e5m2_bias": ("ldexp((double)(4 + m), e - 17)", "ldexp((double)(4 + m), e - 16)"),
+    "e5m2_fraction_bits": ("m = b & 3;", "m = b & 7;"),
+    "fp8_formats_swapped": ("return dt == DT_E4M3 ? e4m3_value(b)", "return dt == DT_E5M2 ? e4m3_value(b)"),
+    "fp8_ta_ignored": ("j->ta ? j->A8[(long)k * j->lda + i]", "j->ta ? j->A8[(long)i * j->lda + k]"),
+    "fp8_b_index": ("j->B8[(long)k * j->ldb + c]", "j->B8[(long)c * j->ldb + k]"),
     "lowp_points_no_flags": ("  j.M = M; j.N = N; j.K = K;\n  j.ta = ta != 0; j.tb = tb != 0;\n  j.alpha = (double)alpha; j.beta = (double)beta;\n  j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;\n  j.lda = lda; j.ldb = ldb; j.ldc = ldc;\n  j.npts",
                              "  j.M = M; j.N = N; j.K = K;\n  j.alpha = (double)alpha; j.beta = (double)beta;\n  j.dt = dt; j.A16 = A; j.B16 = B; j.C = C;\n  j.lda = lda; j.ldb = ldb; j.ldc = ldc;\n  j.npts"),
 }

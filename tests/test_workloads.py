@@ -73,3 +73,23 @@ def test_operands16_values():
     assert np.array_equal(o_t.A.reshape(33, 40).T, a)
     assert np.array_equal(o_t.B.reshape(24, 33).T, o.B.reshape(33, 24))
     assert o.C.dtype == np.float32 and o.A.dtype == np.uint16
+
+
+def test_round8_nearest_even():
+    """The 8-bit input rounding is torch's (checked here against an exact
+    nearest-even search over each format's finite values)."""
+    import torch
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(3000) * 3.0).astype(np.float32)
+    for dt, tdt in (("fp8e4m3", torch.float8_e4m3fn), ("fp8e5m2", torch.float8_e5m2)):
+        bits = wl.round8(x, dt)
+        allv = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(tdt).double().numpy()
+        finite = [(abs(float(v)), b) for b, v in enumerate(allv) if np.isfinite(v) and b < 128]
+        for xi, bi in zip(x[:400], bits[:400]):
+            a = abs(float(xi))
+            best = min(finite, key=lambda vb: (abs(Fraction(vb[0]) - Fraction(a)), vb[1] & 1))
+            got = float(allv[bi])
+            assert abs(got) == best[0] and (got == 0 or np.sign(got) == np.sign(xi)), (dt, xi)
+    with pytest.raises(ValueError):
+        wl.round8(np.float32([1000.0]), "fp8e4m3")
