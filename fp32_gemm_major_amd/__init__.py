@@ -39,6 +39,8 @@ SGEMM_MODE_GUARDED = 2
 
 SGEMM_DTYPE_BF16 = 1
 SGEMM_DTYPE_F16 = 2
+SGEMM_DTYPE_FP8_E4M3 = 3
+SGEMM_DTYPE_FP8_E5M2 = 4
 
 SGEMM_SCHEDULE_TILES = 0
 SGEMM_SCHEDULE_STREAM_K = 1
@@ -442,12 +444,16 @@ class Handle:
     def gemm_lowp(self, A, B, C, alpha=1.0, beta=0.0, M=None, N=None, K=None,
                   lda=None, ldb=None, ldc=None, stream=None, transa=False,
                   transb=False):
-        """C[:M, :N] = alpha * op(A) @ op(B) + beta * C with A and B bfloat16 or
-        float16 CUDA tensors (both the same format) and C a float32 CUDA tensor;
-        shapes, leading dimensions and ``stream`` as in ``gemm``."""
-        formats = {torch.bfloat16: SGEMM_DTYPE_BF16, torch.float16: SGEMM_DTYPE_F16}
+        """C[:M, :N] = alpha * op(A) @ op(B) + beta * C with A and B bfloat16,
+        float16, float8_e4m3fn or float8_e5m2 CUDA tensors (both the same
+        format; 8-bit ones with transb=True and transa=False) and C a float32
+        CUDA tensor; shapes, leading dimensions and ``stream`` as in ``gemm``."""
+        formats = {torch.bfloat16: SGEMM_DTYPE_BF16, torch.float16: SGEMM_DTYPE_F16,
+                   torch.float8_e4m3fn: SGEMM_DTYPE_FP8_E4M3,
+                   torch.float8_e5m2: SGEMM_DTYPE_FP8_E5M2}
         if A.dtype != B.dtype or A.dtype not in formats:
-            raise TypeError("A and B must both be bfloat16 or both float16")
+            raise TypeError("A and B must have one format: bfloat16, float16, "
+                            "float8_e4m3fn or float8_e5m2")
         for name, t in (("A", A), ("B", B), ("C", C)):
             if not t.is_cuda:
                 raise TypeError(f"{name} must be a CUDA tensor")

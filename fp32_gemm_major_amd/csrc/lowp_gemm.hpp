@@ -75,16 +75,34 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// Element formats of A and B.
-enum { LP_BF16 = 1, LP_F16 = 2 };
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// The operation's arguments: A and B as 16-bit patterns.
+// Element formats of A and B: 16-bit (bfloat16, binary16) and 8-bit (OCP
+// E4M3, E5M2).
+enum { LP_BF16 = 1, LP_F16 = 2, LP_E4M3 = 3, LP_E5M2 = 4 };
+
+// What a format changes.  An LDS row is always 128 bytes of k, eight 16-byte
+// units; a K step is one such row: 64 k of a 16-bit format, 128 of an 8-bit
+// one.  A 16-bit MFMA (32x32x16) takes eight k per lane, one unit; an 8-bit
+// one (32x32x64) takes 32 k per lane, two units, so a K step holds four
+// groups of 16-bit MFMAs or two of 8-bit ones.
+template <int DT>
+struct LpFmt {
+  static constexpr int ESZ = DT >= LP_E4M3 ? 1 : 2;  // bytes per element
+  static constexpr int UE = 16 / ESZ;                // elements per unit
+  static constexpr int BKE = 128 / ESZ;              // k per K step
+  static constexpr int FU = 3 - ESZ;                 // units per lane per fragment
+  static constexpr int QG = ESZ == 2 ? 4 : 2;        // MFMA groups per K step
+  typedef typename std::conditional<ESZ == 1, uint8_t, uint16_t>::type E;
+};
+
+// The operation's arguments: A and B as bit patterns of the format.
 struct LpArgs {
   int M, N, K;
   float alpha, beta;
-  const uint16_t* A;
+  const void* A;
   int lda;
-  const uint16_t* B;
+  const void* B;
   int ldb;
   float* C;
   int ldc;
@@ -150,33 +168,49 @@ __device__ __forceinline__ int lp_unit_off(int r, int c) {
   return r * 128 + 16 * (c ^ ((r >> 1) & 7));
 }
 
+// One MFMA on fragments x (first operand) and y of FU units each.  8-bit
+// formats use the scaled 32x32x64 instruction with both E8M0 scales 127
+// (2^0), i.e. unscaled; its format fields select E4M3 (0) or E5M2 (1).
 template <int DT>
-__device__ __forceinline__ f32x16 lp_mfma(u32x4 x, u32x4 y, f32x16 acc) {
-  if constexpr (DT == LP_BF16)
+__device__ __forceinline__ f32x16 lp_mfma(const u32x4* x, const u32x4* y, f32x16 acc) {
+  if constexpr (DT == LP_BF16) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        __builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
-  else
+        __builtin_bit_cast(bf16x8, x[0]), __builtin_bit_cast(bf16x8, y[0]), acc, 0, 0, 0);
+  } else if constexpr (DT == LP_F16) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(
-        __builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
+        __builtin_bit_cast(f16x8, x[0]), __builtin_bit_cast(f16x8, y[0]), acc, 0, 0, 0);
+  } else {
+    constexpr int fmt = DT == LP_E4M3 ? 0 : 1;
+    const i32x8 xa = {(int)x[0][0], (int)x[0][1], (int)x[0][2], (int)x[0][3],
+                      (int)x[1][0], (int)x[1][1], (int)x[1][2], (int)x[1][3]};
+    const i32x8 ya = {(int)y[0][0], (int)y[0][1], (int)y[0][2], (int)y[0][3],
+                      (int)y[1][0], (int)y[1][1], (int)y[1][2], (int)y[1][3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(xa, ya, acc, fmt, fmt, 0, 127, 0,
+                                                           127);
+  }
 }
 
-// A 16-byte piece that may be only 2-byte aligned: 16-byte global loads on
-// gfx950 take any 2-byte aligned address (checked with an in-bounds probe).
-typedef unsigned u32x4u2 __attribute__((ext_vector_type(4), aligned(2)));
+// A 16-byte piece at any byte address: 16-byte global loads on gfx950 take
+// any alignment (checked with in-bounds probes at 1- and 2-byte offsets).
+typedef unsigned u32x4u1 __attribute__((ext_vector_type(4), aligned(1)));
 
-// Eight 16-bit elements at p (2-byte aligned): one 16-byte load when all
-// eight are wanted, else element loads of the first n (n may be <= 0) with
-// zeros after them.
-__device__ __forceinline__ u32x4 lp_load8(const uint16_t* p, int n) {
-  if (n >= 8) {
-    const u32x4u2 v = *reinterpret_cast<const u32x4u2*>(p);
+// One 16-byte unit of elements of type E at p: one 16-byte load when all
+// 16 / sizeof(E) elements are wanted, else element loads of the first n (n
+// may be <= 0) with zeros after them.
+template <class E>
+__device__ __forceinline__ u32x4 lp_load_unit(const E* p, int n) {
+  constexpr int UE = 16 / sizeof(E), BITS = 8 * sizeof(E);
+  if (n >= UE) {
+    const u32x4u1 v = *reinterpret_cast<const u32x4u1*>(p);
     return u32x4{v[0], v[1], v[2], v[3]};
   }
-  unsigned h[8];
+  u32x4 out = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int t = 0; t < 8; ++t) h[t] = t < n ? (unsigned)p[t] : 0u;
-  return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-               h[6] | (h[7] << 16)};
+  for (int t = 0; t < UE; ++t) {
+    const unsigned h = t < n ? (unsigned)p[t] : 0u;
+    out[t / (32 / BITS)] |= h << (BITS * (t % (32 / BITS)));
+  }
+  return out;
 }
 
 // Accumulate the output tile at (m0, n0) over all of K into acc (zeroed by
@@ -185,13 +219,17 @@ template <class T, int DT, int MODE, bool TA, bool TB>
 __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
                                                    int m0, int n0,
                                                    f32x16 (&acc)[T::FM][T::FN]) {
+  typedef LpFmt<DT> F;
+  typedef typename F::E E;
+  constexpr int ESZ = F::ESZ, UE = F::UE, BKE = F::BKE, FU = F::FU, QG = F::QG;
   constexpr bool GUARD = MODE == MODE_GUARDED;
   constexpr bool EDGE = MODE == MODE_EDGE;
   constexpr bool A_KC = !TA;  // A stored K-contiguous
   constexpr bool B_KC = TB;   // B stored K-contiguous
+  static_assert(ESZ == 2 || (A_KC && B_KC), "8-bit operands are stored K-contiguous");
   const int M = g.M, N = g.N, K = g.K;
-  const uint16_t* __restrict__ A = g.A;
-  const uint16_t* __restrict__ B = g.B;
+  const E* __restrict__ A = static_cast<const E*>(g.A);
+  const E* __restrict__ B = static_cast<const E*>(g.B);
   const int lda = g.lda, ldb = g.ldb;
 
   const int tid = threadIdx.x;
@@ -200,7 +238,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
   const int li = lane & 31, lh = lane >> 5;
   const int kb = lane & 7, ob = lane >> 3;  // transposing loader block
-  const int nk = (K + T::BK - 1) / T::BK;
+  const int nk = (K + BKE - 1) / BKE;
 
   // LDS: the A tiles of all stages, then the B tiles.
   auto a_off = [](int st) { return st * T::A_BYTES; };
@@ -241,13 +279,13 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       if (A_KC) {
         int r = a_r[v];
         if (EDGE && m0 + r >= M) r = M - 1 - m0;
-        a_voff[v] = 2u * ((unsigned)r * (unsigned)lda + 8u * (unsigned)a_c[v]);
+        a_voff[v] = ESZ * ((unsigned)r * (unsigned)lda + UE * (unsigned)a_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
         const int k = u / (T::BM / 8), c = (u % (T::BM / 8)) ^ lp_oc_swz<T::BM>(k);
         int o = 8 * c;
         if (EDGE && m0 + o >= M) o = M - 8 > m0 ? M - 8 - m0 : 0;
-        a_voff[v] = 2u * ((unsigned)k * (unsigned)lda + (unsigned)o);
+        a_voff[v] = ESZ * ((unsigned)k * (unsigned)lda + (unsigned)o);
       }
     }
 #pragma unroll
@@ -255,21 +293,21 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       if (B_KC) {
         int r = b_r[v];
         if (EDGE && n0 + r >= N) r = N - 1 - n0;
-        b_voff[v] = 2u * ((unsigned)r * (unsigned)ldb + 8u * (unsigned)b_c[v]);
+        b_voff[v] = ESZ * ((unsigned)r * (unsigned)ldb + UE * (unsigned)b_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
         const int k = u / (T::BN / 8), c = (u % (T::BN / 8)) ^ lp_oc_swz<T::BN>(k);
         int o = 8 * c;
         if (EDGE && n0 + o >= N) o = N - 8 > n0 ? N - 8 - n0 : 0;
-        b_voff[v] = 2u * ((unsigned)k * (unsigned)ldb + (unsigned)o);
+        b_voff[v] = ESZ * ((unsigned)k * (unsigned)ldb + (unsigned)o);
       }
     }
   }
   // Tile origins and the advance per K step of the direct loads.
-  const uint16_t* a_dbase = A_KC ? A + (size_t)m0 * lda : A + m0;
-  const uint16_t* b_dbase = B_KC ? B + (size_t)n0 * ldb : B + n0;
-  const size_t a_dstep = A_KC ? (size_t)T::BK : (size_t)T::BK * lda;
-  const size_t b_dstep = B_KC ? (size_t)T::BK : (size_t)T::BK * ldb;
+  const E* a_dbase = A_KC ? A + (size_t)m0 * lda : A + m0;
+  const E* b_dbase = B_KC ? B + (size_t)n0 * ldb : B + n0;
+  const size_t a_dstep = A_KC ? (size_t)BKE : (size_t)BKE * lda;
+  const size_t b_dstep = B_KC ? (size_t)BKE : (size_t)BKE * ldb;
   // ---- register-staged operands --------------------------------------------
   // K-contiguous operands in guarded and edge mode: one unit per slot.
   constexpr int A_RK = ((GUARD || EDGE) && A_KC) ? T::A_VEC : 1;
@@ -286,21 +324,21 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // Register loads of K step kt (guarded mode; the last step of edge mode).
   // ops: 1 = A, 2 = B, 3 = both.
   auto load_regs = [&](int kt, int ops = 3) {
-    const int k0 = kt * T::BK;
+    const int k0 = kt * BKE;
     if ((GUARD || EDGE) && A_KC && (ops & 1)) {
 #pragma unroll
       for (int v = 0; v < T::A_VEC; ++v) {
-        const int row = m0 + a_r[v], k = k0 + 8 * a_c[v];
-        ra_kc[v] = lp_load8(A + (size_t)(row < M ? row : 0) * lda + k,
-                            row < M ? K - k : 0);
+        const int row = m0 + a_r[v], k = k0 + UE * a_c[v];
+        ra_kc[v] = lp_load_unit(A + (size_t)(row < M ? row : 0) * lda + k,
+                                row < M ? K - k : 0);
       }
     }
     if ((GUARD || EDGE) && B_KC && (ops & 2)) {
 #pragma unroll
       for (int v = 0; v < T::B_VEC; ++v) {
-        const int row = n0 + b_r[v], k = k0 + 8 * b_c[v];
-        rb_kc[v] = lp_load8(B + (size_t)(row < N ? row : 0) * ldb + k,
-                            row < N ? K - k : 0);
+        const int row = n0 + b_r[v], k = k0 + UE * b_c[v];
+        rb_kc[v] = lp_load_unit(B + (size_t)(row < N ? row : 0) * ldb + k,
+                                row < N ? K - k : 0);
       }
     }
     if constexpr (TA) {
@@ -309,7 +347,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int k = k0 + 8 * kb + j;
-          ra_t[j] = lp_load8(A + (size_t)(k < K ? k : 0) * lda + o, k < K ? M - o : 0);
+          ra_t[j] = lp_load_unit(A + (size_t)(k < K ? k : 0) * lda + o, k < K ? M - o : 0);
         }
       }
     }
@@ -319,7 +357,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int k = k0 + 8 * kb + j;
-          rb_t[j] = lp_load8(B + (size_t)(k < K ? k : 0) * ldb + o, k < K ? N - o : 0);
+          rb_t[j] = lp_load_unit(B + (size_t)(k < K ? k : 0) * ldb + o, k < K ? N - o : 0);
         }
       }
     }
@@ -385,7 +423,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 
   // ---- fragments and MFMAs: four groups of 16 k per K step ------------------
   struct Frag {
-    u32x4 a[T::FM], b[T::FN];
+    u32x4 a[T::FM][FU], b[T::FN][FU];
   };
   constexpr int NF = T::FM + T::FN;  // fragment reads per group
   constexpr int SL = T::FM * T::FN;  // MFMAs per group
@@ -418,24 +456,29 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   };
   // Read r of a group, in the order the MFMAs (i-major) first need them:
   // a[0], b[0 .. FN-1], then a[1 .. FM-1].
+  // K-contiguous fragment units: lane half lh of group q holds units
+  // FU*(2q + lh) .. +FU-1 of its row (8 k of a 16-bit format, 32 of an 8-bit
+  // one).
+  auto kc_frag = [&](const char* tile, int row, int q, u32x4 (&out)[FU]) {
+#pragma unroll
+    for (int u = 0; u < FU; ++u)
+      out[u] = *reinterpret_cast<const u32x4*>(tile + lp_unit_off(row, FU * (2 * q + lh) + u));
+  };
   auto read_one = [&](int st, int q, int r, Frag& f) {
-    const int c = 2 * q + lh;
     if (r >= 1 && r <= T::FN) {
       const int j = r - 1;
-      if (!GUARD && !B_KC)
-        f.b[j] = read_tr(lds + b_off(st), std::integral_constant<int, T::BN>{},
-                         wn * T::WN + j * 32, q);
+      if constexpr (!GUARD && !B_KC)
+        f.b[j][0] = read_tr(lds + b_off(st), std::integral_constant<int, T::BN>{},
+                            wn * T::WN + j * 32, q);
       else
-        f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
-                                                 lp_unit_off(wn * T::WN + j * 32 + li, c));
+        kc_frag(lds + b_off(st), wn * T::WN + j * 32 + li, q, f.b[j]);
     } else {
       const int i = r == 0 ? 0 : r - T::FN;
-      if (!GUARD && !A_KC)
-        f.a[i] = read_tr(lds + a_off(st), std::integral_constant<int, T::BM>{},
-                         wm * T::WM + i * 32, q);
+      if constexpr (!GUARD && !A_KC)
+        f.a[i][0] = read_tr(lds + a_off(st), std::integral_constant<int, T::BM>{},
+                            wm * T::WM + i * 32, q);
       else
-        f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
-                                                 lp_unit_off(wm * T::WM + i * 32 + li, c));
+        kc_frag(lds + a_off(st), wm * T::WM + i * 32 + li, q, f.a[i]);
     }
   };
   auto read_frag = [&](int st, int q, Frag& f) {
@@ -445,15 +488,10 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // Fragments of a stage in the K-contiguous layout whatever the storage (the
   // register-staged step of guarded and edge kernels).
   auto read_frag_kc = [&](int st, int q, Frag& f) {
-    const int c = 2 * q + lh;
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-      f.a[i] = *reinterpret_cast<const u32x4*>(lds + a_off(st) +
-                                               lp_unit_off(wm * T::WM + i * 32 + li, c));
+    for (int i = 0; i < T::FM; ++i) kc_frag(lds + a_off(st), wm * T::WM + i * 32 + li, q, f.a[i]);
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j)
-      f.b[j] = *reinterpret_cast<const u32x4*>(lds + b_off(st) +
-                                               lp_unit_off(wn * T::WN + j * 32 + li, c));
+    for (int j = 0; j < T::FN; ++j) kc_frag(lds + b_off(st), wn * T::WN + j * 32 + li, q, f.b[j]);
   };
   auto mma_one = [&](const Frag& f, int m) {
     const int i = m / T::FN, j = m % T::FN;
@@ -481,7 +519,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       if (more) load_regs(kt + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < QG; ++q) {
         Frag f;
         read_frag_kc(st, q, f);
 #pragma unroll
@@ -526,7 +564,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     int kd = nk;
     if (EDGE) {
       const bool straddle = (!A_KC && (M & 7) != 0) || (!B_KC && (N & 7) != 0);
-      kd = straddle ? (K - 1) / T::BK : K / T::BK;
+      kd = straddle ? (K - 1) / BKE : K / BKE;
     }
     auto group = [&](int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
       constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
@@ -534,7 +572,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
       for (int m = 0; m < SL; ++m) {
         mma_one(cur, m);
-        if (q < 3) {
+        if (q < QG - 1) {
 #pragma unroll
           for (int r = 0; r < NF; ++r)
             if (r * SL / NF == m) read_one(st, q + 1, r, nxt);
@@ -549,10 +587,6 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    typedef std::integral_constant<int, 0> I0;
-    typedef std::integral_constant<int, 1> I1;
-    typedef std::integral_constant<int, 2> I2;
-    typedef std::integral_constant<int, 3> I3;
     // vmcnt(N) before a barrier: step kt+1's loads have landed once at most
     // the S-2 later steps' loads are still in flight.
     constexpr int AHEAD = (S - 2) * ND;
@@ -560,14 +594,18 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     Frag f0, f1;
     auto step = [&](int kt, auto st_c) {
       const int kl = kt + S < kd ? kt + S : kd - 1;
-      group(kl, st_c, I0{}, f0, f1);
-      group(kl, st_c, I1{}, f1, f0);
-      group(kl, st_c, I2{}, f0, f1);
+      // groups 0 .. QG-2, alternating the two fragment sets
+      lp_static_for<QG - 1>([&](auto q_c) {
+        if constexpr (decltype(q_c)::value % 2 == 0)
+          group(kl, st_c, q_c, f0, f1);
+        else
+          group(kl, st_c, q_c, f1, f0);
+      });
       wait_lds();
       __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      group(kl, st_c, I3{}, f1, f0);
+      group(kl, st_c, std::integral_constant<int, QG - 1>{}, f1, f0);  // (QG is even)
     };
     if (!EDGE || kd > 0) {  // (aligned kernels run with K >= 64)
       // Steps 0 .. S-1 go out first; step 0 must have landed before the
@@ -604,7 +642,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       wait_lds();
       __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < QG; ++q) {
         Frag f;
         read_frag_kc(0, q, f);
 #pragma unroll

@@ -616,8 +616,8 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
 }
 
 #define LP_ONE(T, DT, DTAG, STAG, TA, TB, MODE, MTAG)                        \
-  {"lp_" DTAG "_" #T "_" STAG MTAG, DT, TA, TB, T::BM, T::BN, T::BK,        \
-   T::THREADS, MODE, launch_lp<T, DT, MODE, TA, TB>}
+  {"lp_" DTAG "_" #T "_" STAG MTAG, DT, TA, TB, T::BM, T::BN,                \
+   LpFmt<DT>::BKE, T::THREADS, MODE, launch_lp<T, DT, MODE, TA, TB>}
 #define LP_STORAGE(T, DT, DTAG, MODE, MTAG)                                  \
   LP_ONE(T, DT, DTAG, "", false, false, MODE, MTAG),                         \
   LP_ONE(T, DT, DTAG, "tn_", true, false, MODE, MTAG),                       \
@@ -636,20 +636,35 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                     \
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded")
 
+// 8-bit formats: A stored M x K and B stored N x K only (both K-contiguous,
+// the storage 8-bit GEMMs use); the same tiles and modes.
+#define LP_FORMAT8(DT, DTAG)                                                 \
+  LP_ONE(L256x256, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"), \
+  LP_ONE(L128x128, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"), \
+  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"),   \
+  LP_ONE(L128x128, DT, DTAG, "nt_", false, true, SGEMM_MODE_EDGE, "edge"),       \
+  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_EDGE, "edge"),         \
+  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_GUARDED, "guarded")
+
 const LpKernelDesc kLpKernels[] = {
     LP_FORMAT(SGEMM_DTYPE_BF16, "bf16"),
     LP_FORMAT(SGEMM_DTYPE_F16, "f16"),
+    LP_FORMAT8(SGEMM_DTYPE_FP8_E4M3, "e4m3"),
+    LP_FORMAT8(SGEMM_DTYPE_FP8_E5M2, "e5m2"),
 };
 constexpr int kNumLpKernels = sizeof(kLpKernels) / sizeof(kLpKernels[0]);
 
 // Direct loads (aligned kernels, both operands in any storage): the farthest
 // byte of one K step of a tile must lie within 4 GiB of the tile's origin.
+int lp_elem_bytes(int dt) { return dt >= SGEMM_DTYPE_FP8_E4M3 ? 1 : 2; }
+
 bool lp_offsets_fit(const LpKernelDesc& k, const LpRun& a) {
   const long long a_far = a.ta ? (long long)(k.bk - 1) * a.lda + k.bm
                                : (long long)(k.bm - 1) * a.lda + k.bk;
   const long long b_far = a.tb ? (long long)(k.bn - 1) * a.ldb + k.bk
                                : (long long)(k.bk - 1) * a.ldb + k.bn;
-  return 2 * a_far < (1LL << 32) && 2 * b_far < (1LL << 32);
+  const long long esz = lp_elem_bytes(a.dt);
+  return esz * a_far < (1LL << 32) && esz * b_far < (1LL << 32);
 }
 
 // Direct loads (global_load_lds_dwordx4) take any 2-byte aligned address on
@@ -960,7 +975,7 @@ int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
 int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
                         const void* A, int lda, const void* B, int ldb,
                         float beta, const float* C, int ldc) {
-  if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_ERR_VALUE;
+  if (dtype < SGEMM_DTYPE_BF16 || dtype > SGEMM_DTYPE_FP8_E5M2) return SGEMM_ERR_VALUE;
   if ((transa != SGEMM_OP_N && transa != SGEMM_OP_T) ||
       (transb != SGEMM_OP_N && transb != SGEMM_OP_T))
     return SGEMM_ERR_VALUE;
@@ -973,11 +988,13 @@ int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
   if (M == 0 || N == 0) return SGEMM_OK;
   if (C == nullptr) return SGEMM_ERR_NULL;
   if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_ERR_NULL;
-  if (K > 0 && (((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 1u) != 0))
+  const unsigned esz = (unsigned)lp_elem_bytes(dtype);
+  if (K > 0 && (((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) &
+                 (esz - 1)) != 0))
     return SGEMM_ERR_VALUE;
   const Range rc = window_bytes(C, M, N, ldc, 4);
-  if (K > 0 && (overlap(rc, window_bytes(A, a_rows, a_cols, lda, 2)) ||
-                overlap(rc, window_bytes(B, b_rows, b_cols, ldb, 2))))
+  if (K > 0 && (overlap(rc, window_bytes(A, a_rows, a_cols, lda, esz)) ||
+                overlap(rc, window_bytes(B, b_rows, b_cols, ldb, esz))))
     return SGEMM_ERR_ALIAS;
   (void)beta;
   return SGEMM_OK;

@@ -249,39 +249,47 @@ void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
 int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
                           hipStream_t stream);
 
-/* ---- products with 16-bit A and B ------------------------------------------
+/* ---- products with 16-bit or 8-bit A and B --------------------------------
  *
  * Operation (the gsyq.cn GEMM guide, section 5.1: matrix units multiply
  * 16-bit inputs and accumulate in FP32):
  *
  *     C = alpha * op(A) * op(B) + beta * C
  *
- * with A and B stored in a 16-bit format (dtype) and C, alpha, beta FP32.
- * Storage, leading dimensions (in elements), transa / transb, the M x N
- * window of C, the beta == 0 and K == 0 conventions and the determinism of
- * sgemm_run_ex hold unchanged.  A and B hold bit patterns: SGEMM_DTYPE_BF16
- * is bfloat16 (the upper half of an IEEE binary32), SGEMM_DTYPE_F16 IEEE
- * binary16.  Every product of two such values is exact in FP32, so the
+ * with A and B stored in a 16-bit or 8-bit format (dtype) and C, alpha, beta
+ * FP32.  Storage, leading dimensions (in elements), transa / transb, the
+ * M x N window of C, the beta == 0 and K == 0 conventions and the
+ * determinism of sgemm_run_ex hold unchanged.  A and B hold bit patterns:
+ * SGEMM_DTYPE_BF16 is bfloat16 (the upper half of an IEEE binary32),
+ * SGEMM_DTYPE_F16 IEEE binary16, SGEMM_DTYPE_FP8_E4M3 and _E5M2 the OCP
+ * 8-bit formats.  Every product of two such values is exact in FP32, so the
  * accuracy statement of sgemm_run holds as it is: |C - exact| <=
  * 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj| + |beta*c_ij|) against the
- * exact product of the stored 16-bit values.  Infinities and NaNs in A or B
+ * exact product of the stored values.  Infinities and NaNs in A or B
  * propagate as the matrix unit's FP32 arithmetic makes them; finite inputs
- * whose products or sums overflow FP32 give infinities.
+ * whose products or sums overflow FP32 give infinities.  8-bit formats take
+ * only transa = SGEMM_OP_N and transb = SGEMM_OP_T (A stored M x K, B stored
+ * N x K: both K-contiguous); other storages return SGEMM_ERR_UNSUPPORTED.
  *
- * Memory: A and B are device pointers to 2-byte elements, at least 2-byte
- * aligned (SGEMM_ERR_VALUE otherwise); no kernel needs more.  Kernels
- * (sgemm_lowp_kernel_info): ALIGNED takes M and N multiples of the tile (64,
- * 128 or 256) and K a multiple of 64; EDGE any sizes with M >= 8 when A is
- * stored K x M and N >= 8 when B is stored K x N; GUARDED (64 x 64 only) any
- * sizes.  Ownership, streams, errors and threading as for sgemm_run. */
+ * Memory: A and B are device pointers to 2-byte (16-bit formats) or 1-byte
+ * elements, 16-bit ones at least 2-byte aligned (SGEMM_ERR_VALUE otherwise);
+ * no kernel needs more.  Kernels (sgemm_lowp_kernel_info): ALIGNED takes M
+ * and N multiples of the tile (64, 128 or 256) and K a multiple of the K
+ * step (bk: 64 for 16-bit formats, 128 for 8-bit ones); EDGE any sizes with
+ * M >= 8 when A is stored K x M and N >= 8 when B is stored K x N; GUARDED
+ * (64 x 64 only) any sizes.  Ownership, streams, errors and threading as for
+ * sgemm_run. */
 enum sgemm_dtype {
   SGEMM_DTYPE_BF16 = 1,
-  SGEMM_DTYPE_F16 = 2
+  SGEMM_DTYPE_F16 = 2,
+  SGEMM_DTYPE_FP8_E4M3 = 3, /* OCP 8-bit: 4 exponent bits, bias 7, no inf */
+  SGEMM_DTYPE_FP8_E5M2 = 4  /* OCP 8-bit: 5 exponent bits, bias 15 */
 };
 
-/* Enqueue the 16-bit product on `stream` and return without waiting.
- * SGEMM_ERR_VALUE for an unknown dtype or storage flag or a misaligned A or
- * B; other statuses as sgemm_run_ex. */
+/* Enqueue the 16-bit or 8-bit product on `stream` and return without
+ * waiting.  SGEMM_ERR_VALUE for an unknown dtype or storage flag or a
+ * misaligned A or B; SGEMM_ERR_UNSUPPORTED for an 8-bit format in a storage
+ * it does not take; other statuses as sgemm_run_ex. */
 int sgemm_run_lowp(sgemm_handle_t h, int dtype, int transa, int transb, int M,
                    int N, int K, float alpha, const void* A, int lda,
                    const void* B, int ldb, float beta, float* C, int ldc,
@@ -294,7 +302,7 @@ int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
 
 /* Kernel table of the 16-bit product (ids 0 .. sgemm_lowp_num_kernels()-1).
  * *mode is SGEMM_MODE_ALIGNED, SGEMM_MODE_EDGE or SGEMM_MODE_GUARDED;
- * bk = 64. */
+ * bk is the K step (64 for 16-bit formats, 128 for 8-bit ones). */
 int sgemm_lowp_num_kernels(void);
 const char* sgemm_lowp_kernel_name(int kernel_id); /* NULL for a bad id */
 int sgemm_lowp_kernel_info(int kernel_id, int* dtype, int* bm, int* bn,

@@ -32,9 +32,10 @@ def window(flat, rows, cols, ld):
         np.zeros((rows, cols), np.float32)
 
 
-def check(got, r, t, K, alpha, beta, c_in, exact=False, what=""):
-    """Elementwise acceptance: within the FP32 bound of the unrounded FP64 r,
-    and equal to r rounded to FP32 when ``exact``.  Returns max(err/bound)."""
+def check(got, r, t, K, alpha, beta, c_in, exact=False, what="", extra=None):
+    """Elementwise acceptance: within the FP32 bound of the unrounded FP64 r
+    (plus ``extra`` where given), and equal to r rounded to FP32 when
+    ``exact``.  Returns max(err/bound)."""
     got = np.asarray(got, np.float32)
     r = np.asarray(r, np.float64)
     assert got.shape == r.shape, (got.shape, r.shape)
@@ -46,6 +47,8 @@ def check(got, r, t, K, alpha, beta, c_in, exact=False, what=""):
                                f"result, first at {bad[0].tolist()}: "
                                f"{got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}")
     bound = oracle.error_bound(K, alpha, beta, t, c_in)
+    if extra is not None:
+        bound = bound + extra
     err = np.abs(got.astype(np.float64) - r)
     zero = bound == 0
     assert np.all(err[zero] == 0), f"{what}: nonzero error where the bound is 0"
@@ -109,21 +112,63 @@ def edge_rows(M, extra=12, seed=1):
     return sorted(x for x in base if 0 <= x < M)
 
 
-# ---- products with 16-bit A and B -------------------------------------------
+# ---- products with 16-bit or 8-bit A and B ----------------------------------
+
+TORCH_FORMATS = {"bf16": torch.bfloat16, "f16": torch.float16,
+                 "fp8e4m3": torch.float8_e4m3fn, "fp8e5m2": torch.float8_e5m2}
+
 
 def to_device16(ops: wl.Operands16):
-    """A and B as bfloat16 / float16 device tensors holding the given bit
-    patterns; C as float32."""
+    """A and B as bfloat16 / float16 / float8 device tensors holding the given
+    bit patterns; C as float32."""
     dev = torch.device("cuda", 0)
-    t16 = torch.bfloat16 if ops.dt == "bf16" else torch.float16
+    t16 = TORCH_FORMATS[ops.dt]
 
     def half(bits):
         if not bits.size:
             return torch.empty(8, dtype=t16, device=dev)
+        if bits.dtype == np.uint8:
+            return torch.from_numpy(bits).to(dev).view(t16)
         return torch.from_numpy(bits.view(np.int16)).to(dev).view(t16)
 
     C = torch.from_numpy(ops.C).to(dev) if ops.C.size else torch.empty(1, device=dev)
     return half(ops.A), half(ops.B), C
+
+
+# The 8-bit matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4) sums each
+# block of 64 products in a fixed-point window below the block's largest
+# product before adding the block to the FP32 accumulator: measured over
+# uniform, one-signed and wide-range inputs of both formats, its error stays
+# under 2**-11.2 times that largest product (the FP32 bound alone would call
+# for about 2**-24 times the sum of |products|).  The acceptance of the 8-bit
+# kernels adds 2**-9 * |alpha| * ceil(K/64) * max_k|a_ik| * max_k|b_kj| per
+# element (each block's largest product is at most the row maximum of |A|
+# times the column maximum of |B|), over four times the worst measured.
+# Integer inputs are still checked bit-exact: there every product and every
+# partial sum fits that window.
+FP8_BLOCK_ALLOWANCE = 2.0 ** -9
+
+
+def _abs_max_rows(bits, dt, rows, ld, cols):
+    """max |x| over the first ``cols`` entries of each of ``rows`` stored
+    rows of 8-bit patterns (decoded by torch)."""
+    if rows == 0 or cols == 0:
+        return np.zeros(rows)
+    x = torch.from_numpy(bits[: rows * ld].reshape(rows, ld)[:, :cols].copy())
+    v = x.view(TORCH_FORMATS[dt]).to(torch.float64).abs()
+    return v.max(dim=1).values.numpy()
+
+
+def fp8_extra(ops: wl.Operands16, pr, pc):
+    """The 8-bit block allowance at outputs (pr, pc), or None for 16-bit
+    formats.  8-bit A is stored M x K and B N x K."""
+    if ops.dt not in wl.FORMATS8:
+        return None
+    assert not ops.ta and ops.tb
+    amax = _abs_max_rows(ops.A, ops.dt, ops.M, ops.lda, ops.K)
+    bmax = _abs_max_rows(ops.B, ops.dt, ops.N, ops.ldb, ops.K)
+    blocks = -(-ops.K // 64)
+    return FP8_BLOCK_ALLOWANCE * abs(ops.alpha) * blocks * amax[pr] * bmax[pc]
 
 
 def run16(h: sg.Handle, ops: wl.Operands16, dev=None, stream=None):
@@ -142,7 +187,8 @@ def check_full16(ops: wl.Operands16, out_flat, exact=False, what=""):
                             ops.beta, ops.C, ops.ldc, ta=ops.ta, tb=ops.tb)
     got = window(out_flat, M, N, ops.ldc)
     c_in = window(ops.C, M, N, ops.ldc)
-    worst = check(got, R, T, K, ops.alpha, ops.beta, c_in, exact, what)
+    extra = fp8_extra(ops, np.arange(M)[:, None], np.arange(N)[None, :])
+    worst = check(got, R, T, K, ops.alpha, ops.beta, c_in, exact, what, extra)
     if ops.ldc > N and M:
         pad_in = ops.C[: M * ops.ldc].reshape(M, ops.ldc)[:, N:]
         pad_out = out_flat[: M * ops.ldc].reshape(M, ops.ldc)[:, N:]
@@ -169,4 +215,4 @@ def check_sampled16(ops: wl.Operands16, out_flat, rows, cols, npoints=4096, seed
                                    ops.ldb, ops.beta, ops.C, ops.ldc, pr, pc, ta=ops.ta,
                                    tb=ops.tb)
     return check(got_all[pr, pc], r, t, K, ops.alpha, ops.beta, c_all[pr, pc], exact,
-                 what + " points")
+                 what + " points", fp8_extra(ops, pr, pc))

@@ -4,6 +4,7 @@ import pytest
 import fp32_gemm_major_amd as sg
 
 BF16, F16 = sg.SGEMM_DTYPE_BF16, sg.SGEMM_DTYPE_F16
+E4M3, E5M2 = sg.SGEMM_DTYPE_FP8_E4M3, sg.SGEMM_DTYPE_FP8_E5M2
 
 
 def test_validate_lowp():
@@ -13,7 +14,11 @@ def test_validate_lowp():
     assert v(BF16, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == ok
     assert v(F16, 1, 1, 4, 5, 6, A, 4, B, 6, 0.0, C, 5) == ok
     assert v(0, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
-    assert v(3, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    assert v(5, 0, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
+    # 8-bit formats: 1-byte elements, no alignment, windows in bytes
+    assert v(E4M3, 0, 1, 4, 5, 6, A + 1, 6, B + 3, 6, 0.0, C, 5) == ok
+    assert v(E5M2, 0, 1, 4, 5, 6, A, 6, B, 6, 0.0, A + 23, 5) == sg.SGEMM_ERR_ALIAS
+    assert v(E5M2, 0, 1, 4, 5, 6, A, 6, B, 6, 0.0, A + 24, 5) == ok
     assert v(BF16, 2, 0, 4, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_VALUE
     assert v(BF16, 0, 0, -1, 5, 6, A, 6, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_SIZE
     assert v(BF16, 0, 0, 4, 5, 6, A, 5, B, 5, 0.0, C, 5) == sg.SGEMM_ERR_LD
@@ -56,8 +61,17 @@ def test_kernel_table():
                     assert (dt, ta, tb, bm, sg.SGEMM_MODE_EDGE) in combos
                 assert (dt, ta, tb, 64, sg.SGEMM_MODE_GUARDED) in combos
     for k in t:
-        assert k["bk"] == 64 and k["threads"] == 256 and k["bm"] == k["bn"]
+        assert k["bk"] == (128 if k["dtype"] >= E4M3 else 64)
+        assert k["threads"] == 256 and k["bm"] == k["bn"]
         assert ("bf16" in k["name"]) == (k["dtype"] == BF16)
+        if k["dtype"] >= E4M3:  # 8-bit: A stored M x K, B stored N x K only
+            assert (k["transa"], k["transb"]) == (0, 1)
+    for dt in (E4M3, E5M2):
+        for bm in (64, 128, 256):
+            assert (dt, 0, 1, bm, sg.SGEMM_MODE_ALIGNED) in combos
+        for bm in (64, 128):
+            assert (dt, 0, 1, bm, sg.SGEMM_MODE_EDGE) in combos
+        assert (dt, 0, 1, 64, sg.SGEMM_MODE_GUARDED) in combos
     assert sg.sgemm_lowp_kernel_name(-1) is None
     assert sg.sgemm_lowp_kernel_name(len(t)) is None
     with pytest.raises(sg.SgemmError):
@@ -115,3 +129,16 @@ def test_huge_strides_go_to_the_guarded_kernel():
     assert k["mode"] == sg.SGEMM_MODE_ALIGNED
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 26) + 8, ta=1, B=1 << 42, C=1 << 44)
     assert k["mode"] == sg.SGEMM_MODE_GUARDED
+
+
+@pytest.mark.parametrize("dt", [E4M3, E5M2])
+def test_select_fp8(dt):
+    A, E = sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE
+    k = _pick(dt, 4096, 4096, 4096, tb=1)
+    assert (k["bm"], k["mode"], k["dtype"], k["bk"]) == (256, A, dt, 128)
+    k = _pick(dt, 4096, 4096, 4160, tb=1)   # K not a multiple of 128
+    assert (k["bm"], k["mode"]) == (128, E)
+    k = _pick(dt, 1024, 1024, 1024, tb=1, A=(1 << 20) + 1, B=(1 << 33) + 3)
+    assert (k["bm"], k["mode"]) == (64, A)
+    for ta, tb in ((0, 0), (1, 0), (1, 1)):
+        assert _pick(dt, 256, 256, 256, ta=ta, tb=tb) == sg.SGEMM_ERR_UNSUPPORTED

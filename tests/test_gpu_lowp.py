@@ -1,12 +1,17 @@
-"""Parity of the HIP product with 16-bit A and B (bfloat16 / binary16) and
-FP32 C, through the C ABI, with the FP64 CPU oracle on the same 16-bit
-patterns (the gsyq.cn guide, section 5.1: 16-bit inputs, FP32 accumulation).
+"""Parity of the HIP product with 16-bit A and B (bfloat16 / binary16) or
+8-bit A and B (OCP E4M3 / E5M2) and FP32 C, through the C ABI, with the FP64
+CPU oracle on the same bit patterns (the gsyq.cn guide, section 5.1:
+low-precision inputs, FP32 accumulation).
 
-Acceptance is that of the FP32 product: every product of two 16-bit values
-is exact in FP32, so |C_gpu - r| <= 4*max(K,1)*2^-24*(|alpha|*t + |beta*c|)
+Acceptance is that of the FP32 product: every product of two 16-bit (or
+8-bit) values is exact in FP32, so |C_gpu - r| <= 4*max(K,1)*2^-24*(|alpha|*t + |beta*c|)
 elementwise against the unrounded FP64 r of the stored 16-bit values, and
 bit-exact results for integer inputs (every partial sum an integer below
 2^24, which an accumulator narrower than FP32 would not keep at these K).
+The 8-bit kernels' matrix instruction sums each block of 64 products in a
+narrower fixed-point window; their acceptance adds a per-block allowance
+(``gpu_util.FP8_BLOCK_ALLOWANCE``, derived there) and keeps integer inputs
+bit-exact.
 """
 import numpy as np
 import pytest
@@ -40,7 +45,9 @@ def _auto_kernel(handle):
 
 
 KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.lowp_kernel_table()
-DT_NAME = {sg.SGEMM_DTYPE_BF16: "bf16", sg.SGEMM_DTYPE_F16: "f16"}
+DT_NAME = {sg.SGEMM_DTYPE_BF16: "bf16", sg.SGEMM_DTYPE_F16: "f16",
+           sg.SGEMM_DTYPE_FP8_E4M3: "fp8e4m3", sg.SGEMM_DTYPE_FP8_E5M2: "fp8e5m2"}
+FORMATS8 = wl.FORMATS8
 
 
 @pytest.mark.parametrize("k", KERNELS, ids=[k["name"] for k in KERNELS])
@@ -110,26 +117,27 @@ def test_tiny_sizes_integer_exact(handle, dt):
         gu.check_full16(ops, out, exact=True, what=f"tiny {dt} {M}x{N}x{K} {ta}{tb}")
 
 
-@pytest.mark.parametrize("dt", FORMATS)
+@pytest.mark.parametrize("dt", FORMATS + FORMATS8)
 def test_nan_c_with_beta_zero(handle, dt):
-    ops = wl.operands16(W["c2_1024"], dt, M=300, N=260, K=200)
+    ops = wl.operands16(W["c2_1024"], dt, M=300, N=260, K=200, tb=dt in FORMATS8)
     assert np.isnan(ops.C).all()
     out = gu.run16(handle, ops)
     gu.check_full16(ops, out, what="beta 0 with NaN C")
 
 
-@pytest.mark.parametrize("dt", FORMATS)
+@pytest.mark.parametrize("dt", FORMATS + FORMATS8)
 def test_k_zero_and_empty(handle, dt):
     w = W["c4_edge"]
-    ops = wl.operands16(w, dt, M=70, N=50, K=0, ldc=53)
+    tb = dt in FORMATS8
+    ops = wl.operands16(w, dt, M=70, N=50, K=0, ldc=53, tb=tb)
     out = gu.run16(handle, ops)
     gu.check_full16(ops, out, what="K = 0")  # C = beta * C
     for M, N in ((0, 50), (70, 0)):
-        ops = wl.operands16(w, dt, M=M, N=N, K=16)
+        ops = wl.operands16(w, dt, M=M, N=N, K=16, tb=tb)
         A, B, C = gu.to_device16(ops)
         before = C.clone()
         handle.gemm_lowp(A, B, C, 1.0, 1.0, M=M, N=N, K=16, lda=ops.lda, ldb=ops.ldb,
-                         ldc=ops.ldc)
+                         ldc=ops.ldc, transb=tb)
         torch.cuda.synchronize()
         assert torch.equal(before.view(torch.int32), C.view(torch.int32))
 
@@ -235,3 +243,87 @@ def test_edge_kernels_k_cases(handle, case):
                             lda=(M if ta else K) + 1, ldb=(K if tb else N) + 3, ldc=N + 2)
         out = gu.run16(handle, ops)
         gu.check_full16(ops, out, exact=True, what=f"{k['name']} {case}")
+
+
+
+# ---- 8-bit formats (A stored M x K, B stored N x K) ----------------------------
+
+@pytest.mark.parametrize("dt", FORMATS8)
+@pytest.mark.parametrize("name", ["c1_128", "c1_128_int", "c2_1024", "c4_edge",
+                                  "c4_edge_int"])
+def test_fp8_small_workloads_full(handle, dt, name):
+    ops = wl.operands16(W[name], dt, tb=True)
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, exact=W[name].dist == "int4", what=f"{name} {dt}")
+
+
+@pytest.mark.parametrize("dt", FORMATS8)
+@pytest.mark.parametrize("name", ["c3_4096", "c3_4096_int", "c5_mlp"])
+def test_fp8_large_workloads_sampled(handle, dt, name):
+    ops = wl.operands16(W[name], dt, tb=True)
+    out = gu.run16(handle, ops)
+    rows = gu.edge_rows(ops.M, extra=4)[:10]
+    cols = [0, 1, 127, 128, 255, 256, ops.N // 2, ops.N - 1]
+    gu.check_sampled16(ops, out, rows, cols, exact=W[name].dist == "int4",
+                       what=f"{name} {dt}")
+
+
+@pytest.mark.parametrize("dt", FORMATS8)
+def test_fp8_tiny_sizes_integer_exact(handle, dt):
+    rng = np.random.default_rng(67)
+    for case in range(30):
+        M, N, K = (int(x) for x in rng.integers(1, 71, size=3))
+        w = wl.Workload("tiny8", 3100 + case, M, N, K, 1.0, 1.0, "int4")
+        ops = wl.operands16(w, dt, tb=True)
+        out = gu.run16(handle, ops)
+        gu.check_full16(ops, out, exact=True, what=f"tiny {dt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dt", FORMATS8)
+def test_fp8_odd_offsets_and_k_cases(handle, dt):
+    """A and B starting at odd byte addresses, odd leading dimensions, K one
+    past a K step and K under one step."""
+    for (M, N, K) in ((300, 270, 129), (150, 133, 40), (256, 256, 256)):
+        w = wl.Workload("odd8", 79, M, N, K, 1.25, -0.5, "uniform")
+        ops = wl.operands16(w, dt, tb=True, lda=K + 3, ldb=K + 5, ldc=N + 1)
+        A, B, C = gu.to_device16(ops)
+        t8, u8 = A.dtype, torch.uint8
+        A1 = torch.empty(A.numel() + 1, dtype=u8, device=A.device)
+        A1[1:] = A.view(u8)
+        B1 = torch.empty(B.numel() + 3, dtype=u8, device=B.device)
+        B1[3:] = B.view(u8)
+        out = gu.run16(handle, ops, dev=(A1.view(t8)[1:], B1.view(t8)[3:], C))
+        gu.check_full16(ops, out, what=f"{dt} odd offsets {M}x{N}x{K}")
+
+
+def test_fp8_other_storages_unsupported(handle):
+    for ta, tb in ((False, False), (True, False), (True, True)):
+        ops = wl.operands16(W["c1_128_int"], "fp8e4m3", ta=ta, tb=tb)
+        A, B, C = gu.to_device16(ops)
+        with pytest.raises(sg.SgemmError) as e:
+            handle.gemm_lowp(A, B, C, 1.0, 0.0, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
+                             ldb=ops.ldb, ldc=ops.ldc, transa=ta, transb=tb)
+        assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dt", FORMATS8)
+@pytest.mark.parametrize("K", [64, 128, 1000])
+def test_fp8_wide_range_and_one_signed(handle, dt, K):
+    """Inputs spread over seven binades and inputs of one sign: where the
+    8-bit instruction's block window loses the most, the results stay inside
+    the block allowance of the acceptance."""
+    rng = np.random.default_rng([71, K])
+    M, N = 192, 160
+    for kind in ("wide", "positive"):
+        if kind == "wide":
+            a = rng.uniform(-1, 1, (M, K)) * 2.0 ** rng.integers(-6, 1, (M, K))
+            b = rng.uniform(-1, 1, (N, K)) * 2.0 ** rng.integers(-6, 1, (N, K))
+        else:
+            a, b = rng.uniform(0, 1, (M, K)), rng.uniform(0, 1, (N, K))
+        c = rng.uniform(-1, 1, (M, N)).astype(np.float32)
+        ops = wl.Operands16(dt, M, N, K, 0.75, 0.25,
+                            wl.place16(wl.round8(a.astype(np.float32), dt), K), K,
+                            wl.place16(wl.round8(b.astype(np.float32), dt), K), K,
+                            wl.place(c, N), N, False, True)
+        out = gu.run16(handle, ops)
+        gu.check_full16(ops, out, what=f"{dt} {kind} K={K}")
