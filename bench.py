@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_4096]
                     [--variant mfma|valu] [--no-cpu-baseline] [--no-per-config]
-                    [--lowp all|bf16|f16|none] [--lowp-only]
+                    [--lowp all|bf16|f16|fp8|fp8e4m3|fp8e5m2|none] [--lowp-only]
 
 A step is one SGEMM call, C = alpha*A*B + beta*C, on the headline workload
 (M = N = K = 4096, alpha = 1.5, beta = 0.5, uniform [-1, 1) inputs, C
@@ -14,9 +14,10 @@ problem statement; the alpha/beta update is not counted).
 Output: one JSON line with the throughput, the kernel's roofline position
 (HIP events around every launch on the stream the kernel runs on), the CPU
 oracle timed on a bounded sample of the same workload, and per-workload
-GFLOPS for the other problem shapes; then the same problems with bfloat16
-and binary16 A and B and FP32 C (the "lowp" object: the headline problem's
-roofline against the dense 16-bit matrix-core peak, and the other shapes).
+GFLOPS for the other problem shapes; then the same problems with bfloat16,
+binary16, E4M3 or E5M2 A and B and FP32 C (the "lowp" object: per format,
+the headline problem's roofline against the dense matrix-core peak of that
+format, and the other shapes).
 """
 from __future__ import annotations
 
@@ -190,29 +191,37 @@ def cpu_baseline(ops, target_s: float):
 
 
 def lowp_section(args, sg, rf, wl, torch):
-    """The products with 16-bit A and B (bfloat16 / binary16) and FP32 C: the
-    headline problem timed launch by launch with HIP events, as its own
-    roofline against the dense 16-bit matrix-core peak, and the other
-    workloads (and transposed storage) from replayed HIP graphs."""
-    formats = {"all": ("bf16", "f16"), "bf16": ("bf16",), "f16": ("f16",),
-               "none": ()}[args.lowp]
+    """The products with 16-bit A and B (bfloat16 / binary16) or 8-bit A and
+    B (E4M3 / E5M2) and FP32 C: the headline problem timed back to back on
+    the launch stream, as its own roofline against the dense matrix-core
+    peak of its input format, and the other workloads (and, for 16-bit
+    formats, transposed storage) from replayed HIP graphs.  8-bit operands
+    are stored K-contiguous (A as M x K, B as N x K), the one storage their
+    kernels take."""
+    formats = {"all": ("bf16", "f16", "fp8e4m3", "fp8e5m2"), "bf16": ("bf16",),
+               "f16": ("f16",), "fp8": ("fp8e4m3", "fp8e5m2"),
+               "fp8e4m3": ("fp8e4m3",), "fp8e5m2": ("fp8e5m2",), "none": ()}[args.lowp]
     if not formats:
         return None
-    t16 = {"bf16": torch.bfloat16, "f16": torch.float16}
-    peaks = {"bf16": rf.PEAK_BF16_FLOPS, "f16": rf.PEAK_F16_FLOPS}
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16,
+           "fp8e4m3": torch.float8_e4m3fn, "fp8e5m2": torch.float8_e5m2}
+    codes = {"bf16": sg.SGEMM_DTYPE_BF16, "f16": sg.SGEMM_DTYPE_F16,
+             "fp8e4m3": sg.SGEMM_DTYPE_FP8_E4M3, "fp8e5m2": sg.SGEMM_DTYPE_FP8_E5M2}
+    peaks = {"bf16": rf.PEAK_BF16_FLOPS, "f16": rf.PEAK_F16_FLOPS,
+             "fp8e4m3": rf.PEAK_FP8_FLOPS, "fp8e5m2": rf.PEAK_FP8_FLOPS}
     h = sg.Handle(workspace=False)
     out = {}
 
     def prepare(name, dt, ta=False, tb=False):
         w = wl.WORKLOADS[name]
         ops = wl.operands16(w, dt, ta=ta, tb=tb)
-        A = torch.from_numpy(ops.A.view("int16")).cuda().view(t16[dt])
-        B = torch.from_numpy(ops.B.view("int16")).cuda().view(t16[dt])
+        raw = "uint8" if dt in wl.FORMATS8 else "int16"
+        A = torch.from_numpy(ops.A.view(raw)).cuda().view(tdt[dt])
+        B = torch.from_numpy(ops.B.view(raw)).cuda().view(tdt[dt])
         C = torch.from_numpy(ops.C).cuda()
         kid = sg.sgemm_lowp_select_kernel(
-            sg.SGEMM_DTYPE_BF16 if dt == "bf16" else sg.SGEMM_DTYPE_F16, int(ta),
-            int(tb), w.M, w.N, w.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
-            C.data_ptr(), ops.ldc)
+            codes[dt], int(ta), int(tb), w.M, w.N, w.K, A.data_ptr(), ops.lda,
+            B.data_ptr(), ops.ldb, C.data_ptr(), ops.ldc)
 
         def launch():
             h.gemm_lowp(A, B, C, w.alpha, w.beta, M=w.M, N=w.N, K=w.K, lda=ops.lda,
@@ -221,7 +230,8 @@ def lowp_section(args, sg, rf, wl, torch):
 
     for dt in formats:
         peak = peaks[dt]
-        w, dev, kid, launch = prepare(args.workload, dt)
+        fp8 = dt in wl.FORMATS8
+        w, dev, kid, launch = prepare(args.workload, dt, tb=fp8)
         steps = max(args.steps // 2, 10)
         # Back-to-back launches between two events on the launch stream: a
         # ~130 us kernel bracketed by its own events measured ~5 us longer
@@ -237,27 +247,30 @@ def lowp_section(args, sg, rf, wl, torch):
             "traffic": measured_traffic(w.label + "_" + dt, sg.sgemm_lowp_kernel_name(kid)),
             "kernel": sg.sgemm_lowp_kernel_name(kid),
             "kernel_ms_mean": round(kms, 5),
-            "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta, ab_bytes=2),
+            "alg_bytes": rf.alg_bytes(w.M, w.N, w.K, w.beta, ab_bytes=1 if fp8 else 2),
             "flops_per_launch": rf.flops(w.M, w.N, w.K),
             "launches": steps,
-            # sustained rate of a 16-bit MFMA chain with no memory traffic
+            # sustained rate of this format's MFMA chain with no memory traffic
             "mfma_chain_tflops": round(sg.mfma_chain_tflops(
-                iterations=1024, dtype=sg.SGEMM_DTYPE_BF16 if dt == "bf16"
-                else sg.SGEMM_DTYPE_F16), 1),
+                iterations=256 if fp8 else 1024, dtype=codes[dt]), 1),
         }}
+        if fp8:
+            sec["storage"] = "A M x K, B N x K"
         del dev
         per_config = {}
         if not args.no_per_config:
-            cases = [("c1_128", False, False, 200), ("c2_1024", False, False, 200),
-                     ("c4_edge", False, False, 100), ("c5_mlp", False, False, 20),
-                     (args.workload, False, True, 20), (args.workload, True, False, 20),
-                     (args.workload, True, True, 20)]
+            cases = [("c1_128", False, fp8, 200), ("c2_1024", False, fp8, 200),
+                     ("c4_edge", False, fp8, 100), ("c5_mlp", False, fp8, 20)]
+            if not fp8:
+                cases += [(args.workload, False, True, 20), (args.workload, True, False, 20),
+                          (args.workload, True, True, 20)]
             for name, ta, tb, reps in cases:
                 w2, dev2, kid2, launch2 = prepare(name, dt, ta, tb)
                 ms = time_graph(launch2, reps, torch)
                 gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
                 tag = name + ({(False, False): "", (False, True): "_nt",
-                               (True, False): "_tn", (True, True): "_tt"}[(ta, tb)])
+                               (True, False): "_tn", (True, True): "_tt"}[(ta, tb)]
+                              if not fp8 else "")
                 per_config[tag] = {"gflops": round(gf, 1),
                                    "frac_of_peak": round(gf * 1e9 / peak, 4),
                                    "kernel_ms": round(ms, 5),
@@ -280,10 +293,12 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--lowp", choices=["all", "bf16", "f16", "none"], default="all",
-                    help="which 16-bit-input products to time after the FP32 ones")
+    ap.add_argument("--lowp", choices=["all", "bf16", "f16", "fp8", "fp8e4m3", "fp8e5m2",
+                                       "none"], default="all",
+                    help="which 16-bit- or 8-bit-input products to time after the FP32 ones")
     ap.add_argument("--lowp-only", action="store_true",
-                    help="time only the 16-bit-input products (for profiler runs)")
+                    help="time only the 16-bit- and 8-bit-input products (for profiler "
+                         "runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run one plain device copy of this "
                          "many bytes (a reference dispatch for HBM byte counters)")

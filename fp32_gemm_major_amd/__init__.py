@@ -321,12 +321,14 @@ def sgemm_diag_mfma_chain_lowp(dtype, workgroups, iterations, out, stream=0) -> 
 
 
 CHAIN16_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 16  # eight 32x32x16 MFMAs
+CHAIN8_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 64  # eight 32x32x64 MFMAs
 
 
 def mfma_chain_tflops(workgroups=1024, iterations=4096, reps=3, dtype=None):
     """Sustained MFMA TFLOP/s of the device (best of ``reps`` timed runs):
     FP32 32x32x2 by default, or the 16-bit 32x32x16 instruction of ``dtype``
-    (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16)."""
+    (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16), or the 8-bit 32x32x64 one
+    (SGEMM_DTYPE_FP8_E4M3 / SGEMM_DTYPE_FP8_E5M2)."""
     out = torch.empty(workgroups * 256, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -348,7 +350,9 @@ def mfma_chain_tflops(workgroups=1024, iterations=4096, reps=3, dtype=None):
         torch.cuda.synchronize()
         ms = s.elapsed_time(e)
         best = ms if best is None else min(best, ms)
-    per = CHAIN_FLOPS_PER_WAVE_ITER if dtype is None else CHAIN16_FLOPS_PER_WAVE_ITER
+    per = (CHAIN_FLOPS_PER_WAVE_ITER if dtype is None else
+           CHAIN8_FLOPS_PER_WAVE_ITER if dtype >= SGEMM_DTYPE_FP8_E4M3 else
+           CHAIN16_FLOPS_PER_WAVE_ITER)
     flops = per * iterations * workgroups * 4
     return flops / (best * 1e-3) / 1e12
 

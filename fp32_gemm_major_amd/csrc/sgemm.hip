@@ -881,15 +881,14 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
 
 int sgemm_diag_mfma_chain_lowp(int dtype, int workgroups, int iterations,
                                float* out, hipStream_t stream) {
-  if (dtype != SGEMM_DTYPE_BF16 && dtype != SGEMM_DTYPE_F16) return SGEMM_ERR_VALUE;
+  if (dtype < SGEMM_DTYPE_BF16 || dtype > SGEMM_DTYPE_FP8_E5M2) return SGEMM_ERR_VALUE;
   if (workgroups <= 0 || iterations < 0) return SGEMM_ERR_SIZE;
   if (out == nullptr) return SGEMM_ERR_NULL;
-  if (dtype == SGEMM_DTYPE_BF16)
-    hipLaunchKernelGGL(mfma_chain16_kernel<1>, dim3(workgroups), dim3(kChainThreads),
-                       0, stream, out, iterations);
-  else
-    hipLaunchKernelGGL(mfma_chain16_kernel<2>, dim3(workgroups), dim3(kChainThreads),
-                       0, stream, out, iterations);
+  static void (*const kChains[4])(float*, int) = {
+      mfma_chain16_kernel<1>, mfma_chain16_kernel<2>, mfma_chain16_kernel<3>,
+      mfma_chain16_kernel<4>};
+  hipLaunchKernelGGL(kChains[dtype - SGEMM_DTYPE_BF16], dim3(workgroups),
+                     dim3(kChainThreads), 0, stream, out, iterations);
   return hipGetLastError() == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 

@@ -21,6 +21,8 @@ PEAK_FP32_VALU_UNPACKED_FLOPS = PEAK_FP32_FLOPS / 2  # one FMA per lane per cloc
 # accumulation: bfloat16 and binary16 alike.
 PEAK_BF16_FLOPS = 2.5e15
 PEAK_F16_FLOPS = 2.5e15
+# ... and for 8-bit (OCP E4M3 / E5M2) inputs.
+PEAK_FP8_FLOPS = 5.0e15
 PEAK_HBM_BYTES = 8.0e12
 CUS = 256
 CLOCK_HZ = 2.4e9
@@ -32,7 +34,8 @@ def flops(M: int, N: int, K: int) -> int:
 
 def alg_bytes(M: int, N: int, K: int, beta: float, ab_bytes: int = FP32) -> int:
     """Least HBM traffic: A and B read once (``ab_bytes`` per element: 2 for
-    16-bit operands), FP32 C written (and read if beta != 0)."""
+    16-bit operands, 1 for 8-bit ones), FP32 C written (and read if
+    beta != 0)."""
     c_passes = 2 if beta != 0 else 1
     return ab_bytes * (M * K + K * N) + FP32 * c_passes * M * N
 

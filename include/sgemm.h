@@ -316,9 +316,11 @@ int sgemm_lowp_select_kernel(int dtype, int transa, int transb, int M, int N,
                              int ldb, const float* C, int ldc);
 
 /* Diagnostics: as sgemm_diag_mfma_chain with v_mfma_f32_32x32x16_bf16
- * (dtype SGEMM_DTYPE_BF16) or v_mfma_f32_32x32x16_f16 (SGEMM_DTYPE_F16):
- * 32768 flops per MFMA per wave, eight independent accumulators, no memory
- * traffic; the ceiling for the 16-bit product kernels.  SGEMM_ERR_VALUE for
+ * (dtype SGEMM_DTYPE_BF16) or v_mfma_f32_32x32x16_f16 (SGEMM_DTYPE_F16),
+ * 32768 flops per MFMA per wave, or v_mfma_scale_f32_32x32x64_f8f6f4 with
+ * unit scales (SGEMM_DTYPE_FP8_E4M3 / SGEMM_DTYPE_FP8_E5M2), 131072 flops
+ * per MFMA per wave; eight independent accumulators, no memory traffic: the
+ * ceiling for the 16-bit and 8-bit product kernels.  SGEMM_ERR_VALUE for
  * another dtype. */
 int sgemm_diag_mfma_chain_lowp(int dtype, int workgroups, int iterations,
                                float* out, hipStream_t stream);

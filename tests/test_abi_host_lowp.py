@@ -142,3 +142,14 @@ def test_select_fp8(dt):
     assert (k["bm"], k["mode"]) == (64, A)
     for ta, tb in ((0, 0), (1, 0), (1, 1)):
         assert _pick(dt, 256, 256, 256, ta=ta, tb=tb) == sg.SGEMM_ERR_UNSUPPORTED
+
+
+def test_diag_chain_argument_errors():
+    """Argument checks of the low-precision MFMA chain come before any HIP call."""
+    f = sg.library().sgemm_diag_mfma_chain_lowp  # raw status codes
+    assert f(0, 1, 1, 0x1000, 0) == sg.SGEMM_ERR_VALUE
+    assert f(E5M2 + 1, 1, 1, 0x1000, 0) == sg.SGEMM_ERR_VALUE
+    for dt in (BF16, F16, E4M3, E5M2):
+        assert f(dt, 0, 1, 0x1000, 0) == sg.SGEMM_ERR_SIZE
+        assert f(dt, 1, -1, 0x1000, 0) == sg.SGEMM_ERR_SIZE
+        assert f(dt, 1, 1, 0, 0) == sg.SGEMM_ERR_NULL

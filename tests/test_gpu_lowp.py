@@ -327,3 +327,14 @@ def test_fp8_wide_range_and_one_signed(handle, dt, K):
                             wl.place(c, N), N, False, True)
         out = gu.run16(handle, ops)
         gu.check_full16(ops, out, what=f"{dt} {kind} K={K}")
+
+
+@pytest.mark.parametrize("dt", [sg.SGEMM_DTYPE_BF16, sg.SGEMM_DTYPE_F16,
+                                sg.SGEMM_DTYPE_FP8_E4M3, sg.SGEMM_DTYPE_FP8_E5M2])
+def test_mfma_chain_rate_below_peak(dt):
+    """The diagnostic chain of each format runs and its rate is plausible:
+    above a third of the dense peak and below the peak itself."""
+    from fp32_gemm_major_amd import roofline as rf
+    peak = rf.PEAK_FP8_FLOPS if dt >= sg.SGEMM_DTYPE_FP8_E4M3 else rf.PEAK_BF16_FLOPS
+    tf = sg.mfma_chain_tflops(workgroups=512, iterations=128, reps=2, dtype=dt)
+    assert peak / 3e12 < tf < peak / 1e12, tf
