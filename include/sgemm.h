@@ -262,10 +262,16 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
  * determinism of sgemm_run_ex hold unchanged.  A and B hold bit patterns:
  * SGEMM_DTYPE_BF16 is bfloat16 (the upper half of an IEEE binary32),
  * SGEMM_DTYPE_F16 IEEE binary16, SGEMM_DTYPE_FP8_E4M3 and _E5M2 the OCP
- * 8-bit formats.  Every product of two such values is exact in FP32, so the
- * accuracy statement of sgemm_run holds as it is: |C - exact| <=
- * 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj| + |beta*c_ij|) against the
- * exact product of the stored values.  Infinities and NaNs in A or B
+ * 8-bit formats.  Every product of two such values is exact in FP32, so for
+ * the 16-bit formats the accuracy statement of sgemm_run holds as it is:
+ * |C - exact| <= 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj| + |beta*c_ij|)
+ * against the exact product of the stored values.  The 8-bit matrix
+ * instruction sums each block of 64 consecutive products in a fixed-point
+ * window below the block's largest product before the FP32 accumulation;
+ * measured, that adds under 2^-11 of the block's largest product per block,
+ * and the library is tested to the bound above plus
+ * 2^-9*|alpha|*ceil(K/64)*max_k|a_ik|*max_k|b_kj| (integer-valued inputs
+ * whose partial sums stay below 2^24 are exact).  Infinities and NaNs in A or B
  * propagate as the matrix unit's FP32 arithmetic makes them; finite inputs
  * whose products or sums overflow FP32 give infinities.  8-bit formats take
  * only transa = SGEMM_OP_N and transb = SGEMM_OP_T (A stored M x K, B stored
