@@ -687,16 +687,21 @@ bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
 }
 
 // The kernel for these arguments: the largest tile (256, 128, then 64
-// square) that still gives every CU a tile, else the 64x64 one, in its
-// aligned instance when that fits, else the edge instance of that tile (of
-// the 128x128 one in place of 256x256); else the guarded 64x64 kernel.
+// square) that still gives every CU a tile, else the 64x64 one -- except
+// that the 256x256 tile is also taken when the 128x128 tiling needs three or
+// more rounds of the CUs (one partial round of the larger tile is then the
+// shorter: a 128x128 round costs about 1.4 quarters of a 256x256 one) --
+// in its aligned instance when that fits, else the edge instance of that
+// tile (of the 128x128 one in place of 256x256); else the guarded 64x64
+// kernel.
 int lp_select(const LpRun& a, int cus) {
+  const long long t256 = ceil_div(a.M, 256) * ceil_div(a.N, 256);
+  const long long t128 = ceil_div(a.M, 128) * ceil_div(a.N, 128);
   int bm = 64;
-  for (int t = 256; t >= 128; t /= 2)
-    if (ceil_div(a.M, t) * ceil_div(a.N, t) >= cus) {
-      bm = t;
-      break;
-    }
+  if (t256 >= cus || t128 > 2LL * cus)
+    bm = 256;
+  else if (t128 >= cus)
+    bm = 128;
   static const int kOrder[3] = {SGEMM_MODE_ALIGNED, SGEMM_MODE_EDGE, SGEMM_MODE_GUARDED};
   for (int o = 0; o < 3; ++o)
     for (int id = 0; id < kNumLpKernels; ++id) {

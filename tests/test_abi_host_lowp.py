@@ -97,6 +97,15 @@ def test_select(dt, ta, tb):
     assert (k["bm"], k["mode"]) == (128, A)
     k = _pick(dt, 1024, 1024, 1024, ta=ta, tb=tb)  # 64 tiles of 128: use 64
     assert (k["bm"], k["mode"]) == (64, A)
+    # 144 tiles of 256 (one partial round) against 576 of 128 (three rounds)
+    k = _pick(dt, 3072, 3072, 1024, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (256, A)
+    # 128 tiles of 256 against 512 of 128: two rounds of the smaller tile
+    k = _pick(dt, 2048, 4096, 1024, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (128, A)
+    # not tile multiples: the 128x128 edge kernel stands in for 256x256
+    k = _pick(dt, 3000, 3000, 1000, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (128, E)
     k = _pick(dt, 1000, 1500, 777, ta=ta, tb=tb)
     assert (k["bm"], k["mode"]) == (64, E)
     k = _pick(dt, 4100, 4100, 4100, ta=ta, tb=tb)  # edge kernels stop at 128
