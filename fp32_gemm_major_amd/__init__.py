@@ -160,8 +160,9 @@ def sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
 
 def sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
                    ldc, stream=0) -> int:
-    """The product with 16-bit A and B (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16) and
-    FP32 C; A, B, C are device addresses."""
+    """The product with 16-bit A and B (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16) or
+    8-bit A and B (SGEMM_DTYPE_FP8_E4M3 / SGEMM_DTYPE_FP8_E5M2, transa 0 and
+    transb 1 only) and FP32 C; A, B, C are device addresses."""
     return _check(library().sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha,
                                            A, lda, B, ldb, beta, C, ldc, stream),
                   "sgemm_run_lowp")

@@ -32,7 +32,7 @@ struct sgemm_handle_s {
   int forced_kernel; // -1 = automatic
   void* workspace;   // caller's device memory for partial sums, or null
   size_t workspace_bytes;
-  int forced_lowp;   // 16-bit product kernel, -1 = automatic
+  int forced_lowp;   // low-precision product kernel, -1 = automatic
 };
 
 namespace {
@@ -566,7 +566,7 @@ int plan_out(const Plan& plan, int N, int* kernels, int* n_split) {
   return plan.count;
 }
 
-// ---- products with 16-bit A and B ------------------------------------------
+// ---- products with 16-bit or 8-bit A and B -----------------------------------
 
 struct LpRun {
   int dt;      // SGEMM_DTYPE_*
@@ -974,7 +974,7 @@ int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,
                       ldb, beta, C, ldc, stream);
 }
 
-// ---- products with 16-bit A and B ------------------------------------------
+// ---- products with 16-bit or 8-bit A and B -----------------------------------
 
 int sgemm_validate_lowp(int dtype, int transa, int transb, int M, int N, int K,
                         const void* A, int lda, const void* B, int ldb,

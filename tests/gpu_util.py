@@ -172,7 +172,8 @@ def fp8_extra(ops: wl.Operands16, pr, pc):
 
 
 def run16(h: sg.Handle, ops: wl.Operands16, dev=None, stream=None):
-    """Run the 16-bit product on the GPU; returns the whole C buffer (flat numpy)."""
+    """Run the 16-bit or 8-bit product on the GPU; returns the whole C buffer
+    (flat numpy)."""
     A, B, C = dev if dev is not None else to_device16(ops)
     h.gemm_lowp(A, B, C, ops.alpha, ops.beta, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
                 ldb=ops.ldb, ldc=ops.ldc, stream=stream, transa=ops.ta, transb=ops.tb)
@@ -181,7 +182,8 @@ def run16(h: sg.Handle, ops: wl.Operands16, dev=None, stream=None):
 
 
 def check_full16(ops: wl.Operands16, out_flat, exact=False, what=""):
-    """The whole M x N window against the 16-bit oracle; C padding untouched."""
+    """The whole M x N window against the 16-bit or 8-bit oracle (plus the 8-bit
+    block allowance); C padding untouched."""
     M, N, K = ops.M, ops.N, ops.K
     R, T = oracle.gemm_lowp(ops.dt, M, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb,
                             ops.beta, ops.C, ops.ldc, ta=ops.ta, tb=ops.tb)
@@ -200,7 +202,7 @@ def check_full16(ops: wl.Operands16, out_flat, exact=False, what=""):
 def check_sampled16(ops: wl.Operands16, out_flat, rows, cols, npoints=4096, seed=0,
                     exact=False, what=""):
     """Full rows ``rows``, full columns ``cols`` and random points of the
-    16-bit product, each from the oracle's point mode."""
+    16-bit or 8-bit product, each from the oracle's point mode."""
     M, N, K = ops.M, ops.N, ops.K
     got_all = window(out_flat, M, N, ops.ldc)
     c_all = window(ops.C, M, N, ops.ldc)

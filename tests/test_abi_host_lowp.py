@@ -1,4 +1,5 @@
-"""Host-side checks of the 16-bit product's C ABI (no GPU, nothing launched)."""
+"""Host-side checks of the 16-bit and 8-bit products' C ABI (no GPU, nothing
+launched)."""
 import pytest
 
 import fp32_gemm_major_amd as sg
