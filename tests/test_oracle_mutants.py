@@ -102,3 +102,58 @@ def test_mutant_is_caught(name, tmp_path):
     line = [l for l in proc.stdout.splitlines() if l.startswith("CAUGHT")][-1]
     caught = [c for c in line[len("CAUGHT "):].split(",") if c]
     assert caught, f"mutant {name} passed every pin"
+
+
+# ---- the acceptance bound (oracle.error_bound) --------------------------------
+
+BOUND_MUTANTS = {
+    "unit_2^-23": ("2.0 ** -24", "2.0 ** -23"),
+    "unit_2^-25": ("2.0 ** -24", "2.0 ** -25"),
+    "k_squared": ("4.0 * max(int(K), 1) *", "4.0 * max(int(K), 1) * max(int(K), 1) *"),
+    "k_sqrt": ("4.0 * max(int(K), 1) *", "4.0 * max(int(K), 1) ** 0.5 *"),
+    "no_k_floor": ("4.0 * max(int(K), 1) *", "4.0 * int(K) *"),
+    "factor_1": ("return 4.0 *", "return 1.0 *"),
+    "factor_8": ("return 4.0 *", "return 8.0 *"),
+    "beta_term_dropped": ("        scale = scale + np.abs(", "        scale = scale + 0 * np.abs("),
+    "beta_term_always": ("    if beta != 0:\n        scale", "    if True:\n        scale"),
+    "alpha_signed": ("scale = abs(float(alpha)) * t", "scale = float(alpha) * t"),
+    "beta_signed": ("scale + np.abs(float(beta) * np.asarray(c_in, dtype=np.float64))",
+                    "scale + float(beta) * np.asarray(c_in, dtype=np.float64)"),
+}
+
+
+def _bound_source():
+    import inspect
+    return inspect.getsource(oracle.error_bound)
+
+
+@pytest.mark.parametrize("name", sorted(BOUND_MUTANTS))
+def test_bound_mutant_is_caught(name):
+    """A planted mistake in the acceptance bound fails at least one of the
+    bound pins (tests/bound_pins.py)."""
+    import numpy as np
+    from tests import bound_pins
+    src = _bound_source()
+    old, new = BOUND_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    mutant = ns["error_bound"]
+    caught = []
+    for pin in bound_pins.ALL_BOUND_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mutant)
+        except (AssertionError, ValueError, ZeroDivisionError, OverflowError):
+            caught.append(pin.__name__)
+    assert caught, f"bound mutant {name} passed every pin"
+
+
+def test_bound_pins_pass_on_the_bound_itself():
+    """The unmutated source, run the same way, passes every bound pin."""
+    import numpy as np
+    from tests import bound_pins
+    ns = {"np": np}
+    exec(_bound_source(), ns)
+    for pin in bound_pins.ALL_BOUND_PINS:
+        pin(ns["error_bound"])
