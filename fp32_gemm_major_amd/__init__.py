@@ -56,6 +56,7 @@ EXPORTED = [
     "sgemm_kernel_schedule", "sgemm_run_lowp", "sgemm_validate_lowp",
     "sgemm_lowp_num_kernels", "sgemm_lowp_kernel_name", "sgemm_lowp_kernel_info",
     "sgemm_lowp_select_kernel", "sgemm_set_lowp_kernel", "sgemm_diag_mfma_chain_lowp",
+    "sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz",
 ]
 
 
@@ -104,7 +105,10 @@ def _bind(lib):
     lib.sgemm_lowp_select_kernel.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i]
     lib.sgemm_set_lowp_kernel.argtypes = [p, i]
     lib.sgemm_diag_mfma_chain_lowp.argtypes = [i, i, i, p, p]
-    for name in ("sgemm_run_lowp", "sgemm_diag_mfma_chain_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
+    lib.sgemm_diag_run_clocked.argtypes = [p, i, i, i, i, i, f, p, i, p, i, f, p, i, p, i, p]
+    lib.sgemm_diag_wall_clock_khz.argtypes = [ip]
+    for name in ("sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz",
+                 "sgemm_run_lowp", "sgemm_diag_mfma_chain_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
                  "sgemm_lowp_kernel_info", "sgemm_lowp_select_kernel",
                  "sgemm_set_lowp_kernel"):
         getattr(lib, name).restype = i
@@ -321,6 +325,35 @@ def sgemm_diag_mfma_chain_lowp(dtype, workgroups, iterations, out, stream=0) -> 
                   "sgemm_diag_mfma_chain_lowp")
 
 
+def sgemm_diag_run_clocked(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                           ldc, stamps, stamp_slots, stream=0) -> int:
+    """sgemm_run_ex that also stores per-workgroup clock stamps; returns the
+    number of workgroups stamped."""
+    return _check(library().sgemm_diag_run_clocked(h, transa, transb, M, N, K, alpha, A,
+                                                   lda, B, ldb, beta, C, ldc, stamps,
+                                                   stamp_slots, stream),
+                  "sgemm_diag_run_clocked")
+
+
+def sgemm_diag_wall_clock_khz() -> int:
+    khz = ctypes.c_int()
+    _check(library().sgemm_diag_wall_clock_khz(ctypes.byref(khz)),
+           "sgemm_diag_wall_clock_khz")
+    return khz.value
+
+
+def clock_from_stamps(stamps, workgroups, wall_khz):
+    """(median shader clock in GHz over the workgroups, the launch's span in
+    microseconds from the first start to the last end) from the stamps of
+    sgemm_diag_run_clocked (a CPU int64 tensor or array of 4 per workgroup)."""
+    t = torch.as_tensor(stamps).view(-1, 4)[:workgroups].double()
+    cycles, ticks = t[:, 1] - t[:, 0], t[:, 3] - t[:, 2]
+    ok = ticks > 0
+    ghz = float((cycles[ok] / ticks[ok]).median()) * wall_khz * 1e3 / 1e9
+    span_us = float(t[:, 3].max() - t[:, 2].min()) / (wall_khz * 1e3) * 1e6
+    return ghz, span_us
+
+
 CHAIN16_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 16  # eight 32x32x16 MFMAs
 CHAIN8_FLOPS_PER_WAVE_ITER = 8 * 2 * 32 * 32 * 64  # eight 32x32x64 MFMAs
 
@@ -372,6 +405,7 @@ class Handle:
                  workspace: bool = True):
         self.h = sgemm_create()
         self.workspace = None
+        self._stamps = None
         if variant != SGEMM_VARIANT_AUTO:
             sgemm_set_variant(self.h, variant)
         if kernel >= 0:
@@ -397,6 +431,7 @@ class Handle:
             sgemm_destroy(self.h)
             self.h = None
         self.workspace = None
+        self._stamps = None
 
     def __enter__(self):
         return self
@@ -443,6 +478,35 @@ class Handle:
                             float(beta), C.data_ptr(), ldc, stream)
 
 
+    def gemm_stamped(self, A, B, C, stamps, alpha=1.0, beta=0.0, M=None, N=None, K=None,
+                     lda=None, ldb=None, ldc=None, transa=False, transb=False):
+        """``gemm`` through sgemm_diag_run_clocked: the product kernel also
+        writes its clock stamps into ``stamps`` (an int64 CUDA tensor of
+        4 per workgroup).  Returns the number of workgroups stamped without
+        waiting; ``clock_from_stamps`` turns the stamps into a clock once the
+        stream has finished the call."""
+        for name, t in (("A", A), ("B", B), ("C", C)):
+            if t.dtype != torch.float32 or not t.is_cuda:
+                raise TypeError(f"{name} must be a float32 CUDA tensor")
+        if stamps.dtype != torch.int64 or not stamps.is_cuda or not stamps.is_contiguous():
+            raise TypeError("stamps must be a contiguous int64 CUDA tensor")
+        M, N, K, lda, ldb, ldc = _shapes(A, B, C, M, N, K, lda, ldb, ldc, transa,
+                                         transb)
+        return sgemm_diag_run_clocked(self.h, int(bool(transa)), int(bool(transb)), M, N, K,
+                                      float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                                      float(beta), C.data_ptr(), ldc, stamps.data_ptr(),
+                                      stamps.numel() // 4,
+                                      torch.cuda.current_stream(C.device).cuda_stream)
+
+    def gemm_clocked(self, A, B, C, alpha=1.0, beta=0.0, **kw):
+        """``gemm_stamped`` into a buffer of the handle's, then wait: returns
+        (shader clock in GHz, the launch's span in microseconds) of that call,
+        from the product kernel's own clock stamps."""
+        if self._stamps is None:
+            self._stamps = torch.zeros(4 * 65536, dtype=torch.int64, device="cuda")
+        n = self.gemm_stamped(A, B, C, self._stamps, alpha, beta, **kw)
+        return clock_from_stamps(self._stamps[: 4 * n].cpu(), n, sgemm_diag_wall_clock_khz())
+
     def set_lowp_kernel(self, kernel_id: int):
         sgemm_set_lowp_kernel(self.h, kernel_id)
 
@@ -478,23 +542,69 @@ class Handle:
                               stream)
 
 
+def _span(rows, cols, ld):
+    """Elements from the first to the last one a rows x cols window at
+    leading dimension ``ld`` touches (0 for an empty window)."""
+    return 0 if rows <= 0 or cols <= 0 else (rows - 1) * ld + cols
+
+
+def _elements_from_pointer(t):
+    """Elements of the tensor's storage from its data pointer to the end: the
+    most any window starting at ``t.data_ptr()`` may span."""
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
 def _shapes(A, B, C, M, N, K, lda, ldb, ldc, transa, transb):
-    """Sizes and leading dimensions from 2-D tensors where not given."""
+    """Sizes and leading dimensions from 2-D tensors where not given, checked
+    against the tensors: a 2-D operand must hold its stored window (A: M x K,
+    or K x M when ``transa``; B: K x N, or N x K when ``transb``; C: M x N),
+    2-D A and B must agree on K unless K is given, and every operand's window
+    must fit in its storage from the data pointer on.  Raises ValueError
+    otherwise, before anything reaches the device."""
+    k_from = {}
     if A.dim() == 2:
         ra, ca = A.shape
         M = (ca if transa else ra) if M is None else M
-        K = (ra if transa else ca) if K is None else K
+        k_from["A"] = ra if transa else ca
         lda = max(A.stride(0), 1) if lda is None else lda
     if B.dim() == 2:
         rb, cb = B.shape
-        K = (cb if transb else rb) if K is None else K
+        k_from["B"] = cb if transb else rb
         N = (rb if transb else cb) if N is None else N
         ldb = max(B.stride(0), 1) if ldb is None else ldb
+    if K is None:
+        if len(set(k_from.values())) > 1:
+            raise ValueError(f"A and B disagree on K: {k_from['A']} (A) and "
+                             f"{k_from['B']} (B)")
+        K = next(iter(k_from.values()), None)
     if C.dim() == 2:
         ldc = max(C.stride(0), 1) if ldc is None else ldc
     if None in (M, N, K, lda, ldb, ldc):
         raise ValueError("sizes and leading dimensions are needed for 1-D buffers")
+    check_extents(A, B, C, M, N, K, lda, ldb, ldc, transa, transb)
     return M, N, K, lda, ldb, ldc
+
+
+def check_extents(A, B, C, M, N, K, lda, ldb, ldc, transa, transb):
+    """Raise ValueError if a tensor cannot hold the window the call would read
+    or write (see ``_shapes``).  Negative sizes and short leading dimensions
+    are left to the library's own checks, which return a status."""
+    if min(M, N, K) < 0:
+        return
+    touched = M > 0 and N > 0
+    stored = (("A", A, K if transa else M, M if transa else K, lda, touched and K > 0),
+              ("B", B, N if transb else K, K if transb else N, ldb, touched and K > 0),
+              ("C", C, M, N, ldc, touched))
+    for name, t, rows, cols, ld, used in stored:
+        if not used:
+            continue
+        if t.dim() == 2 and (rows > t.shape[0] or cols > t.shape[1]):
+            raise ValueError(f"{name}: a {rows} x {cols} window does not fit its "
+                             f"{t.shape[0]} x {t.shape[1]} tensor")
+        need, have = _span(rows, cols, ld), _elements_from_pointer(t)
+        if need > have:
+            raise ValueError(f"{name}: the {rows} x {cols} window at leading dimension "
+                             f"{ld} spans {need} elements, the tensor holds {have}")
 
 
 def kernel_table() -> list:
