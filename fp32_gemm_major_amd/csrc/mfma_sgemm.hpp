@@ -87,8 +87,8 @@ template <int BM_, int BN_, int WM_, int WN_, int OCC_, int S_ = 2, int BK_ = 16
 struct MfmaTile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr int OCC = OCC_;  // waves per SIMD the registers are sized for
-  // LDS stages of the aligned (direct-load) kernels: loads run S-1 K steps
-  // ahead of the MFMAs.  Guarded kernels use 2.
+  // LDS stages: two, so the direct loads run one K step ahead of the MFMAs
+  // (three and four stages measured slower on every tile).
   static constexpr int S = S_;
   // K groups: KG groups of waves split every stage's K range (KG*BK values)
   // and their partial sums are added through LDS at the end, group 1 first.
@@ -124,12 +124,11 @@ struct MfmaTile {
   static_assert(A_VEC >= 1 && A_VEC * THREADS == A_UNITS, "A loader");
   static_assert(B_VEC >= 1 && B_VEC * THREADS == B_UNITS, "B loader");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
-  static_assert(S >= 2, "stages");
-  static_assert((S - 1) * (A_VEC + B_VEC) <= 63, "vmcnt range");
+  static_assert(S == 2, "two LDS stages");
+  static_assert(A_VEC + B_VEC <= 63, "vmcnt range");
   static_assert(BK == 16 || BK == 32 || BK == 64, "K step");
   static_assert(BKS <= 64, "K-contiguous rows of at most 16 units");
   static_assert(KG == 1 || KG == 2 || KG == 4, "K groups");
-  static_assert(!PF || S == 2, "fragment prefetch uses two stages");
   // floats the K groups 1..KG-1 leave in LDS for group 0
   static constexpr int RED_ELEMS = (KG - 1) * WAVES_MN * 64 * 16 * FM * FN;
   static_assert(RED_ELEMS <= 2 * STAGE, "reduction fits in LDS");
@@ -197,10 +196,10 @@ struct GemmArgs {
   int ldc;
 };
 
-// LDS floats a kernel of tile T in mode MODE uses.
+// LDS floats a kernel of tile T in mode MODE uses (two stages).
 template <class T, int MODE>
 struct TileLds {
-  static constexpr int NST = MODE == MODE_GUARDED ? 2 : T::S;  // stages in use
+  static constexpr int NST = T::S;
   static constexpr int FLOATS = NST * T::STAGE;
 };
 
@@ -360,11 +359,8 @@ __device__ __forceinline__ void tile_accumulate(
                                 4 * lane) = rb[v];
   };
 
-  // Wait until at most N of this wave's LDS-bound loads are still in flight
-  // (vmcnt(N); the other counters are left at their maxima).
-  constexpr int PER_STEP = T::A_VEC + T::B_VEC;  // direct loads per K step
-  constexpr int AHEAD = (NST - 2) * PER_STEP;
-  constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
+  // Wait until none of this wave's LDS-bound loads is still in flight
+  // (vmcnt(0); the other counters are left at their maxima).
   auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   // Fragments of four k (one per MFMA lane half) of LDS stage `stage`.  They
@@ -504,39 +500,25 @@ __device__ __forceinline__ void tile_accumulate(
     if (kt < e) step(kt, 0, f0, f1);
   } else {
     const int e = s1 < kd ? s1 : kd;  // direct-load steps [s0, e)
-    // Prologue: K steps s0 .. s0+NST-2 in flight, wait for step s0.
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-      if (s0 + s < e) issue_dma(s0 + s, s);
-    if (e - s0 >= NST - 1) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
-    else wait_all();
+    // Prologue: K step s0 into stage 0.
+    if (s0 < e) issue_dma(s0, 0);
+    wait_all();
     __syncthreads();
-    // One K step from `stage`, loading step kt+NST-1 into `next`, whose
-    // previous contents (step kt-1) were read before the last barrier; step
-    // kt+1 must be in LDS at the barrier, later ones may still be in flight.
+    // One K step from `stage`, loading step kt+1 into `next`, whose previous
+    // contents (step kt-1) were read before the last barrier; step kt+1 must
+    // be in LDS at the barrier that ends the step.
     auto step = [&](int kt, int stage, int next) {
-      const bool issue = kt + NST - 1 < e;
-      if (issue) issue_dma(kt + NST - 1, next);
+      if (kt + 1 < e) issue_dma(kt + 1, next);
       compute(stage);
-      if (issue) __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
-      else wait_all();
+      wait_all();
       __syncthreads();
     };
-    if (NST == 2) {
-      int kt = s0;
-      for (; kt + 1 < e; kt += 2) {
-        step(kt, 0, 1);
-        step(kt + 1, 1, 0);
-      }
-      if (kt < e) step(kt, 0, 1);
-    } else {
-      int stage = 0, next = NST - 1;
-      for (int kt = s0; kt < e; ++kt) {
-        step(kt, stage, next);
-        stage = stage + 1 == NST ? 0 : stage + 1;
-        next = next + 1 == NST ? 0 : next + 1;
-      }
+    int kt = s0;
+    for (; kt + 1 < e; kt += 2) {
+      step(kt, 0, 1);
+      step(kt + 1, 1, 0);
     }
+    if (kt < e) step(kt, 0, 1);
   }
   // Edge kernels: the last step through registers, zero-filled past K, when
   // it is partial or holds the last K row of a straddling operand.  The
@@ -678,11 +660,28 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x16(0.0f);
 }
 
+// Clock stamps (diagnostic): the shader cycle counter (s_memtime) at p[0]
+// and the constant-rate wall clock (s_memrealtime) at p[2], written by the
+// calling lane with vector stores.
+__device__ __forceinline__ void clock_stamp(long long* p) {
+  const long long c = (long long)__builtin_amdgcn_s_memtime();
+  const long long w = (long long)__builtin_amdgcn_s_memrealtime();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): both readings are in
+  p[0] = c;
+  p[2] = w;
+}
+
 // One tile per workgroup: workgroup -> tile through the XCD-aware order.
+// With `stamps` (a diagnostic; null in every product call) the first lane
+// records {cycles, cycles, wall, wall} at stamps[4*workgroup]: the counters
+// when the workgroup starts and after all its waves are done, so cycles over
+// wall ticks is the shader clock the tile ran at.
 template <class T, int MODE, bool TA, bool TB>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
-    mfma_sgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int band) {
+    mfma_sgemm_kernel(GemmArgs g, int tiles_m, int tiles_n, int band,
+                      long long* __restrict__ stamps) {
   __shared__ __attribute__((aligned(1024))) float lds[TileLds<T, MODE>::FLOATS];
+  if (stamps != nullptr && threadIdx.x == 0) clock_stamp(stamps + 4 * blockIdx.x);
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
   f32x16 acc[T::FM][T::FN];
@@ -690,6 +689,10 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, 0,
                                    tile_k_steps<T>(g.K), acc);
   if (threadIdx.x / 64 / T::WAVES_MN == 0) store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
+  if (stamps != nullptr) {
+    __syncthreads();
+    if (threadIdx.x == 0) clock_stamp(stamps + 4 * blockIdx.x + 1);
+  }
 }
 
 // ---- stream-K ------------------------------------------------------------

@@ -49,12 +49,14 @@ struct RunArgs {
   int ldc;
 };
 
-// What a launch needs besides the problem: the device's CU count and the
-// stream-K workspace.
+// What a launch needs besides the problem: the device's CU count, the
+// stream-K workspace and (diagnostic runs only) the clock-stamp buffer of
+// the one-tile-per-workgroup MFMA kernels.
 struct LaunchCtx {
   int cus;
   float* ws;
   size_t ws_bytes;
+  long long* stamps;
 };
 
 typedef hipError_t (*launch_fn)(const RunArgs&, int tiles_m, int tiles_n,
@@ -91,11 +93,11 @@ GemmArgs gemm_args(const RunArgs& a) {
 
 template <class T, int MODE, bool TA, bool TB>
 hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
-                       const LaunchCtx&, hipStream_t s) {
+                       const LaunchCtx& c, hipStream_t s) {
   const int nwg = tiles_m * tiles_n;
   hipLaunchKernelGGL((mfma_sgemm_kernel<T, MODE, TA, TB>), dim3(nwg),
                      dim3(T::THREADS), 0, s, gemm_args(a), tiles_m, tiles_n,
-                     band_rows(tiles_m, nwg));
+                     band_rows(tiles_m, nwg), c.stamps);
   return hipGetLastError();
 }
 
@@ -533,7 +535,7 @@ bool overlap(Range x, Range y) {
 }
 
 LaunchCtx handle_ctx(const sgemm_handle_s* h) {
-  LaunchCtx c = {h->cus, static_cast<float*>(h->workspace), h->workspace_bytes};
+  LaunchCtx c = {h->cus, static_cast<float*>(h->workspace), h->workspace_bytes, nullptr};
   return c;
 }
 
@@ -690,10 +692,11 @@ bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
 // square) that still gives every CU a tile, else the 64x64 one -- except
 // that the 256x256 tile is also taken when the 128x128 tiling needs three or
 // more rounds of the CUs (one partial round of the larger tile is then the
-// shorter: a 128x128 round costs about 1.4 quarters of a 256x256 one) --
-// in its aligned instance when that fits, else the edge instance of that
-// tile (of the 128x128 one in place of 256x256); else the guarded 64x64
-// kernel.
+// shorter: a 128x128 round costs about 1.4 quarters of a 256x256 one).  The
+// first instance that fits, in this order: the aligned instance of that
+// tile; for 256x256, the aligned 128x128 one (sizes that are multiples of
+// 128 but not of 256); the edge instance (of the 128x128 tile in place of
+// 256x256, which has none); the guarded 64x64 kernel.
 int lp_select(const LpRun& a, int cus) {
   const long long t256 = ceil_div(a.M, 256) * ceil_div(a.N, 256);
   const long long t128 = ceil_div(a.M, 128) * ceil_div(a.N, 128);
@@ -702,12 +705,15 @@ int lp_select(const LpRun& a, int cus) {
     bm = 256;
   else if (t128 >= cus)
     bm = 128;
-  static const int kOrder[3] = {SGEMM_MODE_ALIGNED, SGEMM_MODE_EDGE, SGEMM_MODE_GUARDED};
-  for (int o = 0; o < 3; ++o)
+  const int edge_bm = bm > 128 ? 128 : bm;
+  const int order[4][2] = {{SGEMM_MODE_ALIGNED, bm},
+                           {SGEMM_MODE_ALIGNED, bm > 128 ? 128 : bm},
+                           {SGEMM_MODE_EDGE, edge_bm},
+                           {SGEMM_MODE_GUARDED, 64}};
+  for (int o = 0; o < 4; ++o)
     for (int id = 0; id < kNumLpKernels; ++id) {
       const LpKernelDesc& k = kLpKernels[id];
-      const int want = kOrder[o] == SGEMM_MODE_EDGE && bm > 128 ? 128 : bm;
-      if (k.mode != kOrder[o] || (k.mode != SGEMM_MODE_GUARDED && k.bm != want)) continue;
+      if (k.mode != order[o][0] || k.bm != order[o][1]) continue;
       if (lp_fits(k, a)) return id;
     }
   return -1;
@@ -802,7 +808,7 @@ int sgemm_plan_ex(int variant, int transa, int transb, int M, int N, int K,
   const RunArgs a = {transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
                      const_cast<float*>(C), ldc};
   Plan plan;
-  const LaunchCtx ctx = {kChipCus, nullptr, 0};
+  const LaunchCtx ctx = {kChipCus, nullptr, 0, nullptr};
   const int st = make_plan(variant, a, ctx, &plan);
   if (st != SGEMM_OK) return st;
   return plan_out(plan, N, kernels, n_split);
@@ -882,6 +888,15 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
   hipLaunchKernelGGL(mfma_chain_kernel, dim3(workgroups), dim3(kChainThreads),
                      0, stream, out, iterations, 1.0f, 1.0f);
   return hipGetLastError() == hipSuccess ? SGEMM_OK : SGEMM_ERR_HIP;
+}
+
+int sgemm_diag_wall_clock_khz(int* khz) {
+  if (khz == nullptr) return SGEMM_ERR_NULL;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SGEMM_ERR_DEVICE;
+  if (hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return SGEMM_ERR_HIP;
+  return *khz > 0 ? SGEMM_OK : SGEMM_ERR_HIP;
 }
 
 int sgemm_diag_mfma_chain_lowp(int dtype, int workgroups, int iterations,
@@ -965,6 +980,36 @@ int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
       return SGEMM_ERR_HIP;
   }
   return SGEMM_OK;
+}
+
+int sgemm_diag_run_clocked(sgemm_handle_t h, int transa, int transb, int M, int N,
+                           int K, float alpha, const float* A, int lda,
+                           const float* B, int ldb, float beta, float* C, int ldc,
+                           long long* stamps, int stamp_slots, hipStream_t stream) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  const int st = sgemm_validate_ex(transa, transb, M, N, K, A, lda, B, ldb,
+                                   beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (stamps == nullptr) return SGEMM_ERR_NULL;
+  if (M == 0 || N == 0) return SGEMM_ERR_UNSUPPORTED;
+  const RunArgs a = {transa, transb, M, N, K, alpha, beta, A, lda, B, ldb, C, ldc};
+  LaunchCtx ctx = handle_ctx(h);
+  Plan plan;
+  const int ps = handle_plan(h, a, ctx, &plan);
+  if (ps != SGEMM_OK) return ps;
+  const KernelDesc& k = kKernels[plan.part[0].kernel];
+  if (plan.count != 1 || k.variant != SGEMM_VARIANT_MFMA ||
+      k.schedule != SGEMM_SCHEDULE_TILES)
+    return SGEMM_ERR_UNSUPPORTED;
+  const long long nwg = ceil_div(M, k.bm) * ceil_div(N, k.bn);
+  if (nwg > stamp_slots) return SGEMM_ERR_SIZE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return SGEMM_ERR_DEVICE;
+  ctx.stamps = stamps;
+  if (k.launch(a, (int)ceil_div(M, k.bm), (int)ceil_div(N, k.bn), ctx, stream) !=
+      hipSuccess)
+    return SGEMM_ERR_HIP;
+  return (int)nwg;
 }
 
 int sgemm_run(sgemm_handle_t h, int M, int N, int K, float alpha,

@@ -27,17 +27,28 @@
  *
  * Memory: A, B and C are device pointers owned by the caller, who also owns
  * the stream.  C must not overlap A or B.  The library allocates no device
- * memory: the handle holds only host-side state (device id, properties,
- * kernel choice).
+ * memory.  The handle holds host-side state (device id, CU count, kernel
+ * choice) and, only if the caller sets one with sgemm_set_workspace, the
+ * address and size of a caller-owned device workspace.  Only two kinds of
+ * plan touch that workspace: STREAM_K launches (partial tiles) and SMALL_M
+ * launches with more than one K range (partial sums of the ranges); every
+ * other plan neither reads nor writes it.  Problems such as 128^3, 1024^3,
+ * 4096^3, 1000 x 1500 x 777 and 4096 x 11008 x 4096 plan one output tile per
+ * workgroup (TILES) and never use it, with or without a workspace.
  *
  * Errors: every function returns SGEMM_OK (0) or a negative status; no
  * function aborts or prints.  Argument errors are found on the host before
  * any HIP call.  sgemm_run is asynchronous: a fault during execution shows
  * up at the next synchronisation of the stream, as for any HIP kernel.
  *
- * Threading: sgemm_run does not modify the handle, so concurrent calls on one
- * handle are allowed.  sgemm_set_variant / sgemm_set_kernel / sgemm_destroy
- * must not race with sgemm_run on the same handle.
+ * Threading: sgemm_run does not modify the handle.  Calls on one handle may
+ * overlap in time (several host threads, or several streams) only when the
+ * handle has no workspace: with one, STREAM_K and multi-range SMALL_M plans
+ * of overlapping calls write the same partial-sum slots and corrupt each
+ * other's results, so calls that may overlap need separate handles, each
+ * with its own workspace (or none).  sgemm_set_variant / sgemm_set_kernel /
+ * sgemm_set_workspace / sgemm_destroy must not race with sgemm_run on the
+ * same handle.
  */
 #ifndef SGEMM_H_
 #define SGEMM_H_
@@ -249,6 +260,29 @@ void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
 int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
                           hipStream_t stream);
 
+/* Diagnostics: the shader clock the product itself runs at.  The same
+ * call as sgemm_run_ex (same checks, same plan on handle h), when that plan
+ * is one launch of a one-tile-per-workgroup MFMA kernel; the first lane of
+ * workgroup w also stores the shader cycle counter and the constant-rate
+ * wall clock when the workgroup starts and after all its waves are done:
+ * stamps[4*w .. 4*w+3] = {cycles_start, cycles_end, wall_start, wall_end}.
+ * (cycles_end - cycles_start) / (wall_end - wall_start) * the wall clock's
+ * rate (sgemm_diag_wall_clock_khz) is the clock that tile ran at.  `stamps`
+ * is caller-owned device memory of 4*stamp_slots long longs.  Returns the
+ * number of workgroups stamped (> 0), SGEMM_ERR_NULL for null stamps,
+ * SGEMM_ERR_SIZE if stamp_slots is smaller than that number,
+ * SGEMM_ERR_UNSUPPORTED for an empty problem or any other plan, or the
+ * status sgemm_run_ex would return.  Asynchronous. */
+int sgemm_diag_run_clocked(sgemm_handle_t h, int transa, int transb, int M, int N,
+                           int K, float alpha, const float* A, int lda,
+                           const float* B, int ldb, float beta, float* C, int ldc,
+                           long long* stamps, int stamp_slots, hipStream_t stream);
+
+/* The current device's wall-clock counter rate in kHz (the rate of the
+ * counter sgemm_diag_run_clocked reads as wall time).  SGEMM_ERR_NULL for a null
+ * out-pointer, SGEMM_ERR_DEVICE / SGEMM_ERR_HIP if it cannot be queried. */
+int sgemm_diag_wall_clock_khz(int* khz);
+
 /* ---- products with 16-bit or 8-bit A and B --------------------------------
  *
  * Operation (the gsyq.cn GEMM guide, section 5.1: matrix units multiply
@@ -265,13 +299,18 @@ int sgemm_diag_mfma_chain(int workgroups, int iterations, float* out,
  * 8-bit formats.  Every product of two such values is exact in FP32, so for
  * the 16-bit formats the accuracy statement of sgemm_run holds as it is:
  * |C - exact| <= 4*max(K,1)*2^-24*(|alpha|*sum_k|a_ik*b_kj| + |beta*c_ij|)
- * against the exact product of the stored values.  The 8-bit matrix
- * instruction sums each block of 64 consecutive products in a fixed-point
- * window below the block's largest product before the FP32 accumulation;
- * measured, that adds under 2^-11 of the block's largest product per block,
- * and the library is tested to the bound above plus
- * 2^-9*|alpha|*ceil(K/64)*max_k|a_ik|*max_k|b_kj| (integer-valued inputs
- * whose partial sums stay below 2^24 are exact).  Infinities and NaNs in A or B
+ * against the exact product of the stored values.  The 8-bit formats carry
+ * no such bound: their matrix instruction sums each block of 64 consecutive
+ * products in a fixed-point window below the block's largest product before
+ * the FP32 accumulation, and its rounding there is not documented.  For
+ * them the library gives only a measured envelope: on uniform, one-signed,
+ * small-normal and seven-binade inputs the error stayed under 2^-11 of each
+ * block's largest product, and the tests accept the bound above plus
+ * 2^-9*|alpha|*ceil(K/64)*max_k|a_ik|*max_k|b_kj|.  What is exact: integer
+ * inputs in [-4, 4] (every product and block sum far inside the window) give
+ * bit-exact results, as for FP32; a block that holds products of very
+ * different size (448*448 beside 1*1) may lose the small ones.  Infinities
+ * and NaNs in A or B
  * propagate as the matrix unit's FP32 arithmetic makes them; finite inputs
  * whose products or sums overflow FP32 give infinities.  8-bit formats take
  * only transa = SGEMM_OP_N and transb = SGEMM_OP_T (A stored M x K, B stored

@@ -34,6 +34,9 @@ def test_null_handle_and_destroy():
     assert lib.sgemm_set_variant(None, 1) == sg.SGEMM_ERR_HANDLE
     assert lib.sgemm_set_kernel(None, 0) == sg.SGEMM_ERR_HANDLE
     assert lib.sgemm_create(None) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_diag_run_clocked(None, 0, 0, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 4096, 4,
+                                      8192, 1, None) == sg.SGEMM_ERR_HANDLE
+    assert lib.sgemm_diag_wall_clock_khz(None) == sg.SGEMM_ERR_NULL
 
 
 def test_validate():

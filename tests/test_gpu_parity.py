@@ -408,6 +408,59 @@ def test_stream_k_uniform_values(handle):
     gu.check_full(ops, gu.run(handle, ops, dev=(A, B, C)), what="stream-K uniform")
 
 
+@pytest.mark.parametrize("name", ["c1_128", "c2_1024", "c3_4096", "c4_edge", "c5_mlp"])
+def test_benchmark_problems_never_use_the_workspace(handle, name):
+    """The five benchmark problems plan one-tile-per-workgroup launches even
+    on a handle with a workspace, in every operand storage: the workspace is
+    never touched for them."""
+    w = W[name]
+    assert handle.workspace is not None
+    for ta in (False, True):
+        for tb in (False, True):
+            lda = w.M if ta else w.K
+            ldb = w.K if tb else w.N
+            plan = handle.plan(w.M, w.N, w.K, 0x10000000, lda, 0x20000000, ldb,
+                               0x40000000, w.N, transa=ta, transb=tb)
+            assert all(sg.sgemm_kernel_schedule(k) == sg.SGEMM_SCHEDULE_TILES
+                       for k, _, _ in plan), (name, ta, tb, plan)
+
+
+def test_clocked_run_matches_and_reads_a_clock(handle):
+    """sgemm_diag_run_clocked runs the same plan as sgemm_run (bit-identical
+    output), stamps every workgroup, and reads a shader clock in a plausible
+    range; plans that are not one tile-per-workgroup MFMA launch are refused
+    before anything runs."""
+    w = wl.Workload("clk", 5300, 1024, 768, 512, 1.5, 0.5, "uniform")
+    ops = wl.operands(w)
+    A, B, C = gu.to_device(ops)
+    c0 = C.clone()
+    ref = gu.run(handle, ops, dev=(A, B, C))
+    C.copy_(c0)
+    ghz, span_us = handle.gemm_clocked(A, B, C, w.alpha, w.beta, M=w.M, N=w.N, K=w.K,
+                                       lda=ops.lda, ldb=ops.ldb, ldc=ops.ldc)
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    assert 0.5 < ghz < 3.5 and 0 < span_us < 1e5, (ghz, span_us)
+    assert 1000 < sg.sgemm_diag_wall_clock_khz() < 10 ** 7
+    stamps = torch.zeros(4 * 8, dtype=torch.int64, device="cuda")
+    with pytest.raises(sg.SgemmError) as e:  # more workgroups than slots
+        sg.sgemm_diag_run_clocked(handle.h, 0, 0, w.M, w.N, w.K, 1.0, A.data_ptr(), ops.lda,
+                                  B.data_ptr(), ops.ldb, 0.0, C.data_ptr(), ops.ldc,
+                                  stamps.data_ptr(), 8)
+    assert e.value.status == sg.SGEMM_ERR_SIZE
+    # one row of C plans a stream-K or small-M launch, not tiles
+    plan = handle.plan(1, w.N, w.K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                       C.data_ptr(), ops.ldc)
+    assert sg.sgemm_kernel_schedule(plan[0][0]) != sg.SGEMM_SCHEDULE_TILES
+    with pytest.raises(sg.SgemmError) as e:
+        sg.sgemm_diag_run_clocked(handle.h, 0, 0, 1, w.N, w.K, 1.0, A.data_ptr(), ops.lda,
+                                  B.data_ptr(), ops.ldb, 0.0, C.data_ptr(), ops.ldc,
+                                  stamps.data_ptr(), 8)
+    assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(stamps == 0)
+
+
 def test_no_workspace_no_stream_k():
     """Without a workspace no stream-K kernel is planned, and a forced one is
     refused before anything is launched."""
