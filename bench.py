@@ -1,14 +1,18 @@
 """Benchmark: FP32 SGEMM GFLOPS on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_4096]
-                    [--variant mfma|valu] [--no-cpu-baseline] [--no-per-config]
-                    [--lowp all|bf16|f16|fp8|fp8e4m3|fp8e5m2|none] [--lowp-only]
+                    [--prewarm-s S] [--variant mfma|valu] [--no-cpu-baseline]
+                    [--no-per-config] [--lowp all|bf16|f16|fp8|fp8e4m3|fp8e5m2|none]
+                    [--lowp-only]
 
 A step is one SGEMM call, C = alpha*A*B + beta*C, on the headline workload
 (M = N = K = 4096, alpha = 1.5, beta = 0.5, uniform [-1, 1) inputs, C
-prefilled), with every operand already resident in device memory.  W untimed
-steps run first, then exactly K timed steps bracketed by device
-synchronisations.  The work count is 2*M*N*K per step ("GEMM 优化之路",
+prefilled), with every operand already resident in device memory.  The same
+call first runs back to back for S seconds (the pre-warm: a GPU that has
+just come out of idle runs its first launches at a lower shader clock), then
+W untimed steps, then exactly K timed steps bracketed by device
+synchronisations.  The shader clock is measured right before and right after
+the timed region.  The work count is 2*M*N*K per step ("GEMM 优化之路",
 problem statement; the alpha/beta update is not counted).
 
 Output: one JSON line with the throughput, the kernel's roofline position
@@ -81,11 +85,27 @@ def measured_traffic(workload: str, kernel: str):
     return None
 
 
-def time_launches(launch, steps, warmup, torch):
-    """Run `launch` warmup + steps times; return (total_ms, per-launch ms list)."""
+def prewarm(launch, seconds, torch):
+    """Run `launch` back to back, ten at a time, until `seconds` have passed;
+    returns (launches, seconds taken)."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            launch()
+        n += 10
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def time_launches(launch, steps, warmup, torch, before_timed=None):
+    """Run `launch` warmup + steps times; return (total_ms, per-launch ms list).
+    ``before_timed`` runs after the warmup, outside the timed region."""
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
+    if before_timed is not None:
+        before_timed()
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
@@ -142,15 +162,18 @@ def time_graph(launch, reps, torch):
 def time_oracle(ops, target_s: float, threads: int):
     """Time the CPU oracle (FP64 triple loop, no error-bound pass) on the first
     rows of a problem with `threads` threads, growing the row count until one
-    run takes about `target_s` seconds.  Returns (GFLOPS, rows, seconds)."""
+    run takes about `target_s` seconds; when the whole problem takes less, it
+    is repeated until the repetitions take about `target_s`.  Returns
+    (GFLOPS, rows, repetitions, seconds)."""
     import oracle
 
     M, N, K = ops.M, ops.N, ops.K
 
-    def run(rows):
+    def run(rows, reps=1):
         t0 = time.perf_counter()
-        oracle.gemm(rows, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb, ops.beta,
-                    ops.C, ops.ldc, with_t=False, nthreads=threads)
+        for _ in range(reps):
+            oracle.gemm(rows, N, K, ops.alpha, ops.A, ops.lda, ops.B, ops.ldb, ops.beta,
+                        ops.C, ops.ldc, with_t=False, nthreads=threads)
         return time.perf_counter() - t0
 
     rows = min(threads, M)
@@ -162,7 +185,11 @@ def time_oracle(ops, target_s: float, threads: int):
         rows = max(rows + threads, min(M, (want // threads) * threads))
         rows = min(rows, M)
         t = run(rows)
-    return 2.0 * rows * N * K / t / 1e9, rows, t
+    reps = 1
+    if rows >= M and t < 0.6 * target_s:
+        reps = max(2, int(round(target_s / max(t, 1e-6))))
+        t = run(rows, reps)
+    return 2.0 * rows * N * K * reps / t / 1e9, rows, reps, t
 
 
 def cpu_baseline(ops, target_s: float):
@@ -172,20 +199,21 @@ def cpu_baseline(ops, target_s: float):
     from fp32_gemm_major_amd import workloads as wl
 
     cores = oracle.default_threads()
-    gf, rows, t = time_oracle(ops, target_s, cores)
+    gf, rows, reps, t = time_oracle(ops, target_s, cores)
     single = {}
     for name in ("c1_128", "c2_1024", "c4_edge"):
         w = wl.WORKLOADS[name]
-        g1, r1, t1 = time_oracle(wl.operands(w), 1.5, 1)
+        g1, r1, n1, t1 = time_oracle(wl.operands(w), 1.5, 1)
         single[name] = {"gflops": round(g1, 3), "rows": r1, "of_rows": w.M,
-                        "seconds": round(t1, 2)}
+                        "repetitions": n1, "seconds": round(t1, 2)}
     return {
         "value": round(gf, 3),
         "unit": "GFLOPS",
         "cores": cores,
         "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of the {ops.M}x{ops.N}x{ops.K} problem ({rows}x{ops.N} "
-                  f"outputs, full K), FP64 accumulation, {t:.1f} s",
+                  f"outputs, full K){f' x {reps} repetitions' if reps > 1 else ''}, "
+                  f"FP64 accumulation, {t:.1f} s",
         "single_core": single,
     }
 
@@ -233,6 +261,10 @@ def lowp_section(args, sg, rf, wl, torch):
         fp8 = dt in wl.FORMATS8
         w, dev, kid, launch = prepare(args.workload, dt, tb=fp8)
         steps = max(args.steps // 2, 10)
+        # A change of workload restarts the GPU's clock ramp (tens of
+        # milliseconds): the same pre-warm as the FP32 call, shorter.
+        if args.prewarm_s > 0:
+            prewarm(launch, min(args.prewarm_s, 0.3), torch)
         # Back-to-back launches between two events on the launch stream: a
         # ~130 us kernel bracketed by its own events measured ~5 us longer
         # than the profiler's duration for it.
@@ -288,6 +320,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3_4096")
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of back-to-back launches before the warmup steps")
     ap.add_argument("--variant", choices=["mfma", "valu"], default="mfma")
     ap.add_argument("--kernel", type=int, default=-1, help="force a kernel id")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -356,13 +390,54 @@ def main(argv=None):
 
     w, ops, dev, kid, launch = prepare(args.workload)
     kname = sg.sgemm_kernel_name(kid)
-    total_ms, per = time_launches(launch, args.steps, args.warmup, torch)
+    clock = {}
+    # The shader clock as this call runs it: the same call with the kernel's
+    # own clock stamps, twice right before the timed region and twice right
+    # after it, launched without waiting (an idle gap, or any other work,
+    # restarts the GPU's clock ramp) and read back after the timed region.
+    # Their buffers are allocated first: from the pre-warm to the end of the
+    # timed region nothing but this call runs on the GPU.
+    clocked = sg.sgemm_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_TILES and \
+        sg.sgemm_kernel_info(kid)["variant"] == sg.SGEMM_VARIANT_MFMA
+    stamp_bufs = [torch.zeros(4 * 65536, dtype=torch.int64, device="cuda")
+                  for _ in range(4)] if clocked else []
+    stamped = []
+    torch.cuda.synchronize()
+    pw_launches, pw_s = prewarm(launch, args.prewarm_s, torch) if args.prewarm_s > 0 \
+        else (0, 0.0)
+
+    def stamp(bufs):
+        for b in bufs:
+            stamped.append((b, h.gemm_stamped(dev[0], dev[1], dev[2], b, w.alpha, w.beta,
+                                              M=w.M, N=w.N, K=w.K, lda=ops.lda,
+                                              ldb=ops.ldb, ldc=ops.ldc)))
+
+    total_ms, per = time_launches(launch, args.steps, args.warmup, torch,
+                                  before_timed=lambda: stamp(stamp_bufs[:2]))
+    stamp(stamp_bufs[2:])
+    torch.cuda.synchronize()
+    if stamped:
+        khz = sg.sgemm_diag_wall_clock_khz()
+        reads = [sg.clock_from_stamps(b[: 4 * n].cpu(), n, khz) for b, n in stamped]
+        for when, part in (("before", reads[:2]), ("after", reads[2:])):
+            clock[when + "_ghz"] = statistics.mean(g for g, _ in part)
+            clock[when + "_span_us"] = statistics.mean(u for _, u in part)
+    del stamp_bufs, stamped
     flops = rf.flops(w.M, w.N, w.K)
     ms_per_step = total_ms / args.steps
     kernel_ms = sum(per) / len(per)
     value = flops / (ms_per_step * 1e-3) / 1e9
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = rf.PEAK_FP32_FLOPS / 1e12
+    head = min(5, len(per))
+    clock["spec_ghz"] = rf.CLOCK_HZ / 1e9
+    if "before_ghz" in clock:
+        observed_ghz = (clock["before_ghz"] + clock["after_ghz"]) / 2
+        peak_at_clock = rf.CUS * rf.FP32_FLOPS_PER_CU_CLOCK * observed_ghz * 1e9
+        clock["peak_tflops_at_observed"] = round(peak_at_clock / 1e12, 2)
+        clock["pct_of_peak_at_observed"] = round(100.0 * value * 1e9 / peak_at_clock, 2)
+    trend = {"first5_ms": round(sum(per[:head]) / head, 5),
+             "last5_ms": round(sum(per[-head:]) / head, 5)}
     roof = {
         "bound": "mfma" if variant == sg.SGEMM_VARIANT_MFMA else "alu",
         "achieved": round(achieved, 3),
@@ -438,6 +513,9 @@ def main(argv=None):
         "dtype": "f32",
         "data": "synthetic",
         "pct_of_fp32_peak": round(100.0 * value * 1e9 / rf.PEAK_FP32_FLOPS, 2),
+        "prewarm": {"seconds": round(pw_s, 2), "launches": pw_launches},
+        "clock": {k: round(v, 3) if isinstance(v, float) else v for k, v in clock.items()},
+        "launch_trend": trend,
         "config": {"workload": w.label, "M": w.M, "N": w.N, "K": w.K,
                    "alpha": w.alpha, "beta": w.beta, "kernel": kname,
                    "parallelism": "single-gpu"},

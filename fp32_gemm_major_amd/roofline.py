@@ -26,6 +26,7 @@ PEAK_FP8_FLOPS = 5.0e15
 PEAK_HBM_BYTES = 8.0e12
 CUS = 256
 CLOCK_HZ = 2.4e9
+FP32_FLOPS_PER_CU_CLOCK = 256  # 157.3e12 = 256 CUs x 2.4e9 x 256
 
 
 def flops(M: int, N: int, K: int) -> int:

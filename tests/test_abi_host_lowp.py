@@ -111,6 +111,11 @@ def test_select(dt, ta, tb):
     assert (k["bm"], k["mode"]) == (64, E)
     k = _pick(dt, 4100, 4100, 4100, ta=ta, tb=tb)  # edge kernels stop at 128
     assert (k["bm"], k["mode"]) == (128, E)
+    # multiples of 128 but not of 256, with the 256x256 tile preferred (three
+    # or more rounds of 128x128 tiles): the aligned 128x128 instance, not an
+    # edge one
+    k = _pick(dt, 3200, 3200, 1024, ta=ta, tb=tb)
+    assert (k["bm"], k["mode"]) == (128, A)
     # direct loads take any 2-byte alignment: odd leading dimensions and a
     # base off 16 bytes stay aligned
     k = _pick(dt, 4096, 4096, 4096, lda=4099, ta=ta, tb=tb)
@@ -129,9 +134,10 @@ def test_select(dt, ta, tb):
 def test_huge_strides_go_to_the_guarded_kernel():
     """An operand whose tile spans more than 4 GiB in one K step cannot use
     the 32-bit lane offsets of the direct loads."""
-    # 255 rows of lda 2^24 + 8 pass 4 GiB, 127 rows (the 128x128 edge kernel) do not
+    # 255 rows of lda 2^24 + 8 pass 4 GiB, 127 rows (the 128x128 tiles) do not:
+    # the aligned 128x128 instance takes it
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 24) + 8)
-    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_EDGE)
+    assert (k["bm"], k["mode"]) == (128, sg.SGEMM_MODE_ALIGNED)
     k = _pick(BF16, 4096, 4096, 4096, lda=(1 << 25) + 8, B=1 << 42, C=1 << 44)
     assert k["mode"] == sg.SGEMM_MODE_GUARDED
     # stored K x M, one K step of a tile spans 63 rows of A

@@ -22,8 +22,16 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def test_time_oracle_on_a_small_problem():
     ops = wl.operands(wl.Workload("t", 7, 64, 48, 40, 1.0, 0.0, "uniform"))
-    gflops, rows, seconds = bench.time_oracle(ops, 0.05, 1)
-    assert gflops > 0 and 1 <= rows <= 64 and seconds > 0
+    gflops, rows, reps, seconds = bench.time_oracle(ops, 0.05, 1)
+    assert gflops > 0 and 1 <= rows <= 64 and reps >= 1 and seconds > 0
+
+
+def test_time_oracle_repeats_a_short_whole_problem():
+    """A problem whose whole run is far under the target is repeated, so the
+    figure does not rest on a single run of a few milliseconds."""
+    ops = wl.operands(wl.Workload("t", 9, 32, 32, 32, 1.0, 0.0, "uniform"))
+    gflops, rows, reps, seconds = bench.time_oracle(ops, 0.2, 1)
+    assert rows == 32 and reps >= 2 and seconds >= 0.1 and gflops > 0
 
 
 def test_cpu_baseline_fields():
@@ -33,7 +41,7 @@ def test_cpu_baseline_fields():
     assert cb["cores"] >= 1 and "rows 0.." in cb["sample"]
     assert set(cb["single_core"]) == {"c1_128", "c2_1024", "c4_edge"}
     for v in cb["single_core"].values():
-        assert v["gflops"] > 0 and 1 <= v["rows"] <= v["of_rows"]
+        assert v["gflops"] > 0 and 1 <= v["rows"] <= v["of_rows"] and v["repetitions"] >= 1
 
 
 def test_kernel_source_hash_and_traffic_record():
