@@ -25,6 +25,8 @@ SGEMM_ERR_DEVICE = -6
 SGEMM_ERR_VALUE = -7
 SGEMM_ERR_ALIAS = -8
 SGEMM_ERR_UNSUPPORTED = -9
+SGEMM_ERR_SCRATCH = -10
+SGEMM_SCRATCH_BYTES = 16 << 20
 
 SGEMM_OP_N = 0
 SGEMM_OP_T = 1
@@ -56,7 +58,7 @@ EXPORTED = [
     "sgemm_kernel_schedule", "sgemm_run_lowp", "sgemm_validate_lowp",
     "sgemm_lowp_num_kernels", "sgemm_lowp_kernel_name", "sgemm_lowp_kernel_info",
     "sgemm_lowp_select_kernel", "sgemm_set_lowp_kernel", "sgemm_diag_mfma_chain_lowp",
-    "sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz",
+    "sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz", "sgemm_run_ex_noalloc",
 ]
 
 
@@ -75,6 +77,7 @@ def _bind(lib):
     lib.sgemm_create.argtypes = [ctypes.POINTER(p)]
     lib.sgemm_run.argtypes = [p, i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_run_ex.argtypes = [p, i, i, i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_run_ex_noalloc.argtypes = lib.sgemm_run_ex.argtypes
     lib.sgemm_validate_ex.argtypes = [i, i, i, i, i, p, i, p, i, f, p, i]
     lib.sgemm_plan_ex.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, ip, ip]
     lib.sgemm_destroy.argtypes = [p]
@@ -107,7 +110,7 @@ def _bind(lib):
     lib.sgemm_diag_mfma_chain_lowp.argtypes = [i, i, i, p, p]
     lib.sgemm_diag_run_clocked.argtypes = [p, i, i, i, i, i, f, p, i, p, i, f, p, i, p, i, p]
     lib.sgemm_diag_wall_clock_khz.argtypes = [ip]
-    for name in ("sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz",
+    for name in ("sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz", "sgemm_run_ex_noalloc",
                  "sgemm_run_lowp", "sgemm_diag_mfma_chain_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
                  "sgemm_lowp_kernel_info", "sgemm_lowp_select_kernel",
                  "sgemm_set_lowp_kernel"):
@@ -160,6 +163,16 @@ def sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc
     return _check(library().sgemm_run_ex(h, transa, transb, M, N, K, alpha, A, lda,
                                          B, ldb, beta, C, ldc, stream),
                   "sgemm_run_ex")
+
+
+def sgemm_run_ex_noalloc(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                         ldc, stream=0) -> int:
+    """sgemm_run_ex with the library's fixed scratch buffer in place of the
+    handle's workspace (no device allocation anywhere in the call); A, B, C
+    are device addresses."""
+    return _check(library().sgemm_run_ex_noalloc(h, transa, transb, M, N, K, alpha, A,
+                                                 lda, B, ldb, beta, C, ldc, stream),
+                  "sgemm_run_ex_noalloc")
 
 
 def sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,

@@ -13,6 +13,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 
 #include "diag.hpp"
@@ -568,6 +570,55 @@ int plan_out(const Plan& plan, int N, int* kernels, int* n_split) {
   return plan.count;
 }
 
+// Launch every part of a plan on `stream`.
+int launch_plan(const Plan& plan, const RunArgs& a, const LaunchCtx& ctx,
+                hipStream_t stream) {
+  for (int p = 0; p < plan.count; ++p) {
+    const Launch& l = plan.part[p];
+    const KernelDesc& k = kKernels[l.kernel];
+    const RunArgs part = column_part(a, l.n0, l.n);
+    if (k.launch(part, (int)ceil_div(a.M, k.bm), (int)ceil_div(l.n, k.bn), ctx,
+                 stream) != hipSuccess)
+      return SGEMM_ERR_HIP;
+  }
+  return SGEMM_OK;
+}
+
+// ---- the library's own scratch buffer (sgemm_run_ex_noalloc) ----------------
+//
+// A fixed device array that the stream-K and small-M kernels use in place of
+// a caller's workspace.  In host code `scratch` names a host-side stand-in,
+// not the device address: its address on each device is looked up once,
+// with that device current (sgemm_create), and only that address is handed
+// to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<float*> g_scratch_addr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[SGEMM_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+// Look up `scratch` on device `dev` (which must be current) unless done.
+// Returns SGEMM_OK or SGEMM_ERR_HIP; a failed lookup is tried again on the
+// next call.
+int scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return SGEMM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev].load() != nullptr) return SGEMM_OK;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+    return SGEMM_ERR_HIP;
+  g_scratch_addr[dev].store(static_cast<float*>(p));
+  return SGEMM_OK;
+}
+
+float* scratch_of(int dev) {
+  return dev >= 0 && dev < kMaxDevices ? g_scratch_addr[dev].load() : nullptr;
+}
+
 // ---- products with 16-bit or 8-bit A and B -----------------------------------
 
 struct LpRun {
@@ -774,6 +825,8 @@ const char* sgemm_status_string(int status) {
     case SGEMM_ERR_VALUE: return "unknown variant or kernel id";
     case SGEMM_ERR_ALIAS: return "C overlaps A or B";
     case SGEMM_ERR_UNSUPPORTED: return "forced kernel cannot run these arguments";
+    case SGEMM_ERR_SCRATCH:
+      return "the forced kernel needs more scratch than the library's fixed buffer holds";
     default: return "unknown status";
   }
 }
@@ -920,6 +973,9 @@ int sgemm_create(sgemm_handle_t* out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SGEMM_ERR_HIP;
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SGEMM_ERR_DEVICE;
+  // Set-up of the fixed scratch buffer on this device (once per device);
+  // a failure only disables sgemm_run_ex_noalloc, which then reports it.
+  (void)scratch_setup(dev);
   sgemm_handle_s* h = new (std::nothrow) sgemm_handle_s;
   if (h == nullptr) return SGEMM_ERR_HIP;
   h->device = dev;
@@ -971,15 +1027,37 @@ int sgemm_run_ex(sgemm_handle_t h, int transa, int transb, int M, int N,
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return SGEMM_ERR_DEVICE;
-  for (int p = 0; p < plan.count; ++p) {
-    const Launch& l = plan.part[p];
-    const KernelDesc& k = kKernels[l.kernel];
-    const RunArgs part = column_part(a, l.n0, l.n);
-    if (k.launch(part, (int)ceil_div(M, k.bm), (int)ceil_div(l.n, k.bn), ctx,
-                 stream) != hipSuccess)
-      return SGEMM_ERR_HIP;
+  return launch_plan(plan, a, ctx, stream);
+}
+
+int sgemm_run_ex_noalloc(sgemm_handle_t h, int transa, int transb, int M, int N,
+                         int K, float alpha, const float* A, int lda, const float* B,
+                         int ldb, float beta, float* C, int ldc, hipStream_t stream) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  const int st = sgemm_validate_ex(transa, transb, M, N, K, A, lda, B, ldb,
+                                   beta, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0) return SGEMM_OK;
+  float* scr = scratch_of(h->device);
+  if (scr == nullptr) return SGEMM_ERR_HIP;  // the set-up lookup failed
+  // A forced stream-K kernel whose partial tiles do not fit the fixed
+  // buffer is refused (the planner itself only plans what fits).
+  if (h->forced_kernel >= 0) {
+    const KernelDesc& f = kKernels[h->forced_kernel];
+    if (f.schedule == SGEMM_SCHEDULE_STREAM_K &&
+        sk_workspace_bytes(f, h->cus) > SGEMM_SCRATCH_BYTES)
+      return SGEMM_ERR_SCRATCH;
   }
-  return SGEMM_OK;
+  const RunArgs a = {transa, transb, M, N, K, alpha, beta, A, lda, B, ldb,
+                     C, ldc};
+  const LaunchCtx ctx = {h->cus, scr, SGEMM_SCRATCH_BYTES, nullptr};
+  Plan plan;
+  const int ps = handle_plan(h, a, ctx, &plan);
+  if (ps != SGEMM_OK) return ps;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
+    return SGEMM_ERR_DEVICE;
+  return launch_plan(plan, a, ctx, stream);
 }
 
 int sgemm_diag_run_clocked(sgemm_handle_t h, int transa, int transb, int M, int N,

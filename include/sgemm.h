@@ -72,7 +72,9 @@ enum sgemm_status {
   SGEMM_ERR_DEVICE = -6, /* no device, not gfx950, or not the handle's device */
   SGEMM_ERR_VALUE = -7,  /* unknown variant or kernel id */
   SGEMM_ERR_ALIAS = -8,  /* the C window overlaps the A or B window */
-  SGEMM_ERR_UNSUPPORTED = -9 /* forced kernel cannot run these arguments */
+  SGEMM_ERR_UNSUPPORTED = -9, /* forced kernel cannot run these arguments */
+  SGEMM_ERR_SCRATCH = -10  /* sgemm_run_ex_noalloc: forced kernel needs more
+                              than SGEMM_SCRATCH_BYTES of scratch */
 };
 
 /* Operand storage for sgemm_run_ex: as stated (N) or transposed (T). */
@@ -179,6 +181,26 @@ int sgemm_destroy(sgemm_handle_t h);
  * workspaces.  SGEMM_ERR_NULL for NULL with bytes > 0, SGEMM_ERR_VALUE for a
  * misaligned pointer. */
 int sgemm_set_workspace(sgemm_handle_t h, void* workspace, size_t bytes);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as sgemm_run_ex, with the same checks, results and determinism, but
+ * the stream-K and small-M kernels keep their partial sums in a buffer of
+ * the library's own -- a fixed device array of SGEMM_SCRATCH_BYTES (16 MiB)
+ * per GPU, set up by sgemm_create and held until the process ends -- in
+ * place of the handle's workspace, which this call ignores.  It calls no
+ * allocating routine.  Plans are made for that buffer's size (stream-K with
+ * 64 x 64 tiles, small-M K splits up to 16 MiB of partial sums); a forced
+ * stream-K kernel that needs more returns SGEMM_ERR_SCRATCH before anything
+ * is launched.  Every call on one GPU shares that GPU's buffer and leaves
+ * its contents behind (no kernel needs it zeroed): calls that may overlap
+ * in time on one GPU (several streams or host threads) race on it and must
+ * not be made.  SGEMM_ERR_HIP if the buffer's set-up failed on this device.
+ * Other statuses as sgemm_run_ex. */
+#define SGEMM_SCRATCH_BYTES (16u << 20)
+int sgemm_run_ex_noalloc(sgemm_handle_t h, int transa, int transb, int M, int N,
+                         int K, float alpha, const float* A, int lda, const float* B,
+                         int ldb, float beta, float* C, int ldc, hipStream_t stream);
 
 /* Bytes of workspace that let every stream-K kernel run on the handle's
  * device (two partial tiles per stream-K workgroup; 64 MiB on 256 CUs). */

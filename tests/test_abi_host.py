@@ -37,6 +37,8 @@ def test_null_handle_and_destroy():
     assert lib.sgemm_diag_run_clocked(None, 0, 0, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 4096, 4,
                                       8192, 1, None) == sg.SGEMM_ERR_HANDLE
     assert lib.sgemm_diag_wall_clock_khz(None) == sg.SGEMM_ERR_NULL
+    assert lib.sgemm_run_ex_noalloc(None, 0, 0, 4, 4, 4, 1.0, 16, 4, 16, 4, 0.0, 4096, 4,
+                                    None) == sg.SGEMM_ERR_HANDLE
 
 
 def test_validate():
@@ -110,7 +112,7 @@ def test_aligned_kernels_need_whole_stages_of_k():
 
 
 def test_status_strings():
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         s = sg.sgemm_status_string(code)
         assert s and s != "unknown status"
     assert sg.sgemm_status_string(-100) == "unknown status"
