@@ -357,13 +357,17 @@ def main(argv=None):
     variant = sg.SGEMM_VARIANT_MFMA if args.variant == "mfma" else sg.SGEMM_VARIANT_VALU
     h = sg.Handle(variant=variant, kernel=args.kernel)
 
+    launches = {}  # launches per call of each prepared problem
+
     def prepare(name, ta=False, tb=False):
         w = wl.WORKLOADS[name]
         ops = wl.operands(w, ta=ta, tb=tb)
         dev = [torch.from_numpy(x).cuda() for x in (ops.A, ops.B, ops.C)]
-        kid = args.kernel if args.kernel >= 0 else sg.sgemm_plan(
-            variant, w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(),
-            ops.ldb, dev[2].data_ptr(), ops.ldc, transa=int(ta), transb=int(tb))[0][0]
+        plan = [(args.kernel, 0, w.N)] if args.kernel >= 0 else h.plan(
+            w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(), ops.ldb,
+            dev[2].data_ptr(), ops.ldc, transa=ta, transb=tb)
+        kid = plan[0][0]
+        launches[name if not (ta or tb) else f"{name}_{int(ta)}{int(tb)}"] = len(plan)
 
         def launch():
             h.gemm(dev[0], dev[1], dev[2], w.alpha, w.beta, M=w.M, N=w.N, K=w.K,
@@ -397,7 +401,8 @@ def main(argv=None):
     # restarts the GPU's clock ramp) and read back after the timed region.
     # Their buffers are allocated first: from the pre-warm to the end of the
     # timed region nothing but this call runs on the GPU.
-    clocked = sg.sgemm_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_TILES and \
+    clocked = launches[args.workload] == 1 and \
+        sg.sgemm_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_TILES and \
         sg.sgemm_kernel_info(kid)["variant"] == sg.SGEMM_VARIANT_MFMA
     stamp_bufs = [torch.zeros(4 * 65536, dtype=torch.int64, device="cuda")
                   for _ in range(4)] if clocked else []

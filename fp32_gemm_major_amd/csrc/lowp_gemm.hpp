@@ -685,7 +685,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   e.ldb = 0;
   e.C = g.C;
   e.ldc = g.ldc;
-  store_tile<T, MODE>(e, tm * T::BM, tn * T::BN, acc);
+  store_tile<T, MODE>(e, tm * T::BM, tn * T::BN, acc, acc);
 }
 
 // Tile shapes: LpTile<BM, BN, WM, WN, OCC>.

@@ -119,7 +119,7 @@ struct MfmaTile {
   static constexpr int RPG = 16 / UPR; // such rows per 256-byte bank sweep
   static_assert(BM % WM == 0 && BN % WN == 0, "wave grid");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-  static_assert(BM >= 64 && (BM & (BM - 1)) == 0, "outer-contiguous A swizzle");
+  static_assert(BM >= 32 && (BM & (BM - 1)) == 0, "tile rows");
   static_assert(BN >= 64 && (BN & (BN - 1)) == 0, "outer-contiguous B swizzle");
   static_assert(A_VEC >= 1 && A_VEC * THREADS == A_UNITS, "A loader");
   static_assert(B_VEC >= 1 && B_VEC * THREADS == B_UNITS, "B loader");
@@ -211,17 +211,91 @@ __host__ __device__ inline int tile_k_steps(int K) {
   return (K + T::BKS - 1) / T::BKS;
 }
 
+// Lane layout of a wave's tile (the same in every kernel of tile T).
+template <class T>
+struct WaveCoords {
+  int lane, wave, kg, wmn, wm, wn, li, lh;
+  __device__ __forceinline__ WaveCoords() {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    kg = wave / T::WAVES_MN;
+    wmn = wave % T::WAVES_MN;
+    wm = wmn / T::WAVES_N;
+    wn = wmn % T::WAVES_N;
+    li = lane & 31;
+    lh = lane >> 5;
+  }
+};
+
+// Whether a tile's C accesses need bounds checks (guarded kernels, and edge
+// tiles of edge kernels), and whether they can be 16 bytes wide.
+template <class T, int MODE>
+__device__ __forceinline__ bool c_masked(const GemmArgs& g, int m0, int n0) {
+  return MODE == MODE_GUARDED ||
+         (MODE == MODE_EDGE && (m0 + T::BM > g.M || n0 + T::BN > g.N));
+}
+__device__ __forceinline__ bool c_vector(const GemmArgs& g) {
+  return (g.ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(g.C) & 15u) == 0);
+}
+
+// Read C at this wave's blocks of the tile at (m0, n0) (callers do so only
+// when beta != 0): block (i, j), register 4q + e of lane (li, lh) is
+// C(row, col) with row = li and col = 8q + 4lh + e inside the block, the
+// accumulators' layout.  Each group of four columns is one 16-byte read when
+// it lies wholly inside M x N (and C allows 16-byte accesses), else element
+// reads of the columns inside; nothing outside M x N is read.
+template <class T, int MODE>
+__device__ __forceinline__ void load_c(const GemmArgs& g, int m0, int n0,
+                                       f32x16 (&cin)[T::FM][T::FN]) {
+  const WaveCoords<T> w;
+  const bool masked = c_masked<T, MODE>(g, m0, n0);
+  const bool vec = c_vector(g);
+  const float* __restrict__ C = g.C;
+  const int crow = m0 + w.wm * T::WM + w.li;
+  const int ccol = n0 + w.wn * T::WN + w.lh * 4;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int row = crow + i * 32, col = ccol + j * 32;
+      const float* p = C + (size_t)row * g.ldc + (masked && row >= g.M ? 0 : col);
+      const bool row_in = !masked || row < g.M;
+      // the block is built in a register vector and stored whole, so that
+      // it stays in registers
+      f32x16 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (row_in && vec && (!masked || col + 8 * q + 3 < g.N)) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(p + 8 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[4 * q + e] = row_in && (!masked || col + 8 * q + e < g.N) ? p[8 * q + e] : 0.0f;
+        }
+      }
+      cin[i][j] = v;
+    }
+}
+
 // TA: A stored K x M (op(A) = A^T).  TB: B stored N x K (op(B) = B^T).
 // Accumulate the output tile at (m0, n0) over K steps [s0, s1) into acc (the
 // caller zeroes it).  On return the first K group's waves (kg == 0) hold the
 // tile's partial sum over those steps; the LDS is still in use by the K-group
-// reduction, so a caller that reuses it must pass a barrier first.
-template <class T, int MODE, bool TA, bool TB>
+// reduction, so a caller that reuses it must pass a barrier first.  With
+// LOADC (tiles with K groups, whose registers have room for it), the first
+// group's waves also read their C blocks into cv (when beta != 0) before the
+// K loop: every workgroup otherwise reads C in one burst after the loop,
+// with nothing left to overlap it.  Without LOADC cv is not touched.
+template <class T, int MODE, bool TA, bool TB, bool LOADC = false>
 __device__ __forceinline__ void tile_accumulate(
     const GemmArgs& g, float* lds, int m0, int n0, int s0, int s1,
-    f32x16 (&acc)[T::FM][T::FN]) {
+    f32x16 (&acc)[T::FM][T::FN], f32x16 (&cv)[T::FM][T::FN]) {
   constexpr bool A_KC = !TA;  // A tile K-contiguous
   constexpr bool B_KC = TB;   // B tile K-contiguous
+  // the outer-contiguous swizzle exchanges 32-float halves of a row
+  static_assert(A_KC || T::BM >= 64, "A stored K x M needs tiles of 64 rows or more");
   constexpr bool GUARD = MODE == MODE_GUARDED;  // no direct loads
   constexpr bool EDGE = MODE == MODE_EDGE;
   constexpr int NST = TileLds<T, MODE>::NST;
@@ -448,6 +522,8 @@ __device__ __forceinline__ void tile_accumulate(
   // peak instead of 92%).  Make them live here and wait once.
   asm volatile("" ::"s"(g.C), "s"(g.ldc), "s"(g.alpha), "s"(g.beta), "s"(M), "s"(N));
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  // C for the epilogue, read now so that it arrives during the K loop
+  if (LOADC && kg == 0 && g.beta != 0.0f) load_c<T, MODE>(g, m0, n0, cv);
   if (GUARD) {
     if (s0 < s1) {
       load_regs(s0);
@@ -527,9 +603,12 @@ __device__ __forceinline__ void tile_accumulate(
     load_regs(kd);
     store_regs(0);
     __syncthreads();
-    compute(0);
+    // a K group whose whole k range in this step lies past K holds only
+    // zeros there: its waves skip the MFMAs
+    if (kg * T::BK < K - kd * T::BKS) compute(0);
     if (T::KG > 1) __syncthreads();  // the K-group reduction reuses the LDS
   }
+
 
   // K groups 1..KG-1 hand their partial sums to group 0 through LDS (the
   // stages are free after the last barrier); group 0 adds them in order.
@@ -570,41 +649,23 @@ __device__ __forceinline__ void tile_accumulate(
   }
 }
 
-// Lane layout of a wave's tile (the same in every kernel of tile T).
-template <class T>
-struct WaveCoords {
-  int lane, wave, kg, wmn, wm, wn, li, lh;
-  __device__ __forceinline__ WaveCoords() {
-    lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
-    kg = wave / T::WAVES_MN;
-    wmn = wave % T::WAVES_MN;
-    wm = wmn / T::WAVES_N;
-    wn = wmn % T::WAVES_N;
-    li = lane & 31;
-    lh = lane >> 5;
-  }
-};
-
 // C = alpha*acc + beta*C for the tile at (m0, n0), by the waves of the first
 // K group.  Block (i, j), register 4g + e of lane (li, lh) holds C(row, col)
-// with row = li and col = 8g + 4lh + e inside the block.
-template <class T, int MODE>
+// with row = li and col = 8g + 4lh + e inside the block.  C is read here,
+// one block at a time, unless HAVE_C: then cv holds it already (load_c).
+template <class T, int MODE, bool HAVE_C = false>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, int m0, int n0,
-                                           const f32x16 (&acc)[T::FM][T::FN]) {
-  constexpr bool GUARD = MODE == MODE_GUARDED;
-  constexpr bool EDGE = MODE == MODE_EDGE;
+                                           const f32x16 (&acc)[T::FM][T::FN],
+                                           const f32x16 (&cv)[T::FM][T::FN]) {
   const WaveCoords<T> w;
   const int M = g.M, N = g.N, ldc = g.ldc;
   const float alpha = g.alpha, beta = g.beta;
   float* __restrict__ C = g.C;
   const int crow = m0 + w.wm * T::WM + w.li;
   const int ccol = n0 + w.wn * T::WN + w.lh * 4;
-  const bool c_vec =
-      (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+  const bool c_vec = c_vector(g);
   // stores need bounds checks: guarded kernels, and edge tiles of edge kernels
-  const bool masked =
-      GUARD || (EDGE && (m0 + T::BM > M || n0 + T::BN > N));
+  const bool masked = c_masked<T, MODE>(g, m0, n0);
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -612,40 +673,37 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int m0, int n0,
       const int row = crow + i * 32;
       const int col = ccol + j * 32;
       float* p = C + (size_t)row * ldc + col;
-      if (!masked && c_vec) {
-        f32x4 cin[4];
-        if (beta != 0.0f) {
+      if (masked && row >= M) continue;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) cin[q] = *reinterpret_cast<const f32x4*>(p + 8 * q);
-        }
+      for (int q = 0; q < 4; ++q) {
+        // a group of four columns wholly inside M x N: 16-byte accesses
+        if (c_vec && (!masked || col + 8 * q + 3 < N)) {
+          f32x4 cin = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (beta != 0.0f) {
+            if (HAVE_C) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+              for (int e = 0; e < 4; ++e) cin[e] = cv[i][j][4 * q + e];
+            } else {
+              cin = *reinterpret_cast<const f32x4*>(p + 8 * q);
+            }
+          }
           f32x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             o[e] = alpha * acc[i][j][4 * q + e];
-            if (beta != 0.0f) o[e] = fmaf(beta, cin[q][e], o[e]);
+            if (beta != 0.0f) o[e] = fmaf(beta, cin[e], o[e]);
           }
           *reinterpret_cast<f32x4*>(p + 8 * q) = o;
-        }
-      } else if (!masked || row < M) {
-        float cin[16];
-        if (beta != 0.0f) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (!masked || col + 8 * q + e < N) cin[4 * q + e] = p[8 * q + e];
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
+        } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (masked && col + 8 * q + e >= N) continue;
             float o = alpha * acc[i][j][4 * q + e];
-            if (beta != 0.0f) o = fmaf(beta, cin[4 * q + e], o);
+            if (beta != 0.0f)
+              o = fmaf(beta, HAVE_C ? cv[i][j][4 * q + e] : p[8 * q + e], o);
             p[8 * q + e] = o;
           }
+        }
       }
       // keep one block's C traffic in registers at a time
       __builtin_amdgcn_sched_barrier(0);
@@ -686,9 +744,15 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
   f32x16 acc[T::FM][T::FN];
   zero_acc<T>(acc);
-  tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, 0,
-                                   tile_k_steps<T>(g.K), acc);
-  if (threadIdx.x / 64 / T::WAVES_MN == 0) store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
+  // Tiles with K groups read C before their K loop (see tile_accumulate)
+  // when the 16 registers per block fit their budget: at 6 waves per SIMD
+  // (85 registers a lane) they do; at 8 (the 64x64 tile's 64) they spill.
+  constexpr bool LOADC = T::KG > 1 && T::OCC <= 6;
+  f32x16 cv[T::FM][T::FN];
+  tile_accumulate<T, MODE, TA, TB, LOADC>(g, lds, tm * T::BM, tn * T::BN, 0,
+                                          tile_k_steps<T>(g.K), acc, cv);
+  if (threadIdx.x / 64 / T::WAVES_MN == 0)
+    store_tile<T, MODE, LOADC>(g, tm * T::BM, tn * T::BN, acc, cv);
   if (stamps != nullptr) {
     __syncthreads();
     if (threadIdx.x == 0) clock_stamp(stamps + 4 * blockIdx.x + 1);
@@ -788,10 +852,10 @@ __global__ void __launch_bounds__(T::THREADS, T::SK_OCC)
     band_walk(t, tiles_m, tiles_n, band, tm, tn);
     f32x16 acc[T::FM][T::FN];
     zero_acc<T>(acc);
-    tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, s0, s1, acc);
+    tile_accumulate<T, MODE, TA, TB>(g, lds, tm * T::BM, tn * T::BN, s0, s1, acc, acc);
     if (first_group) {
       if (slot < 0)
-        store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc);
+        store_tile<T, MODE>(g, tm * T::BM, tn * T::BN, acc, acc);
       else
         store_partial<T>(ws + (size_t)slot * (T::BM * T::BN), acc);
     }

@@ -212,6 +212,10 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   STORAGE(T, "tn_", true, false),                                            \
   STORAGE(T, "nt_", false, true),                                            \
   STORAGE(T, "tt_", true, true)
+// Tiles of fewer than 64 rows: only A stored M x K.
+#define MFMA_SET_A_STORED(T, STORAGE)                                        \
+  STORAGE(T, "", false, false),                                              \
+  STORAGE(T, "nt_", false, true)
 
 // Small-M kernels: bm = the most rows of C they take, bn = the columns of C
 // per workgroup.  With B stored N x K every workgroup stages all of A, whose
@@ -235,6 +239,7 @@ const KernelDesc kKernels[] = {
     MFMA_SET(M256x128, MFMA_STORAGE),
     MFMA_SET(M128x128, MFMA_STORAGE),
     MFMA_SET(M64x64, MFMA_STORAGE),
+    MFMA_SET_A_STORED(M32x64, MFMA_TILES),
     {"valu_V128x128_aligned", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_ALIGNED,
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, false>},
@@ -319,6 +324,7 @@ const ShapeModel kModels[] = {
     {128, 128, 4, {0.058030, 0.111957, 0.164966, 0.220629}, {9.41, 11.61, 15.98, 17.97},
      0.23415, 3.8},
     {64, 64, 2, {0.016331, 0.029669}, {3.96, 6.24}, 0.028646, 4.67},
+    {32, 64, 3, {0.009037, 0.015286, 0.023123}, {2.75, 4.19, 4.81}, 0.024563, 2.22},
 };
 
 // The kernel's model: its shape's, or for the VALU kernel one resident tile
@@ -343,12 +349,20 @@ double rounds_us(const ShapeModel& m, int c, double more, int K) {
 }
 
 // One-tile-per-workgroup launch: the busiest CU runs t = ceil(tiles / cus)
-// tiles.
+// tiles.  The rates above are those of full tiles, which are bound by the
+// matrix cores; a launch also cannot beat reading its operands and C from
+// HBM once, counted at the ~4 TB/s these kernels stream at when there is
+// little work per byte (a few rows of A against a wide B), plus the launch.
+// (C is counted once whatever beta is, so that a plan never depends on
+// beta: sgemm_plan_handle takes none.)
 double tile_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   const ShapeModel m = model_of(k);
   const long long t = ceil_div(ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn), cus);
   const int c = t < m.resident ? (int)t : m.resident;
-  return rounds_us(m, c, (double)(t - c), a.K);
+  const double us = rounds_us(m, c, (double)(t - c), a.K);
+  const double bytes = 4.0 * ((double)a.M * a.K + (double)a.K * a.N + (double)a.M * a.N);
+  const double floor_us = 4.0 + bytes / 4e12 * 1e6;
+  return us > floor_us ? us : floor_us;
 }
 
 // Stream-K launch: the tiles spread evenly over the CUs (w per CU), sk_per_cu

@@ -24,6 +24,12 @@ typedef MfmaTile<128, 128, 64, 64, 4> M128x128;   // 4 waves, 4 WG/CU
 // faster); registers are capped for 8 waves per SIMD so that two
 // workgroups still share a CU.
 typedef MfmaTile<64, 64, 32, 32, 8, 2, 16, 4, 1> M64x64;  // 16 waves
+// Half of that tile along M, for problems whose 64x64 tile count leaves a
+// partial round of the CUs (e.g. 384 tiles on 256 CUs: half the CUs run two
+// tiles while the rest idle): two waves of 32x32 per K group, four K
+// groups, registers and LDS (48 KB) sized for three workgroups per CU.
+// Only for A stored M x K (its rows are K-contiguous in LDS).
+typedef MfmaTile<32, 64, 32, 32, 6, 2, 16, 4, 1> M32x64;  // 8 waves
 typedef ValuTile<128, 128, 8> V128x128;            // 256 lanes of 8x8
 
 }  // namespace sgemm

@@ -143,7 +143,8 @@ def test_kernel_table():
         if s[0] == sg.SGEMM_VARIANT_VALU:
             want = {(0, 0, sg.SGEMM_MODE_ALIGNED), (0, 0, sg.SGEMM_MODE_GUARDED)}
         else:
-            want = {(a, b, m) for a in (0, 1) for b in (0, 1)
+            # tiles of fewer than 64 rows take only A stored M x K
+            want = {(a, b, m) for a in ((0, 1) if s[1] >= 64 else (0,)) for b in (0, 1)
                     for m in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE,
                               sg.SGEMM_MODE_GUARDED)}
         assert inst == want, s
@@ -172,16 +173,18 @@ def test_select_kernel():
         assert k["mode"] == (sg.SGEMM_MODE_ALIGNED if mfma else sg.SGEMM_MODE_GUARDED)
     assert sel(7, 64, 64, 64, A, 64, B, 64, C, 64) == sg.SGEMM_ERR_VALUE
     # tile shapes the cost model picks for the measured workloads: 4096^3 on a
-    # large tile filling whole rounds, and the problems that would leave CUs
-    # idle on 64 x 64 (4096 x 11008 is covered by the launch-plan test)
+    # large tile filling whole rounds, and 32 x 64 for the small and ragged
+    # problems (1000 x 1500: 768 tiles, three per CU, where 64 x 64 leaves
+    # half the CUs with two tiles and half with one; 4096 x 11008 is covered
+    # by the launch-plan test)
     def shape(M, N, K):
         k = sg.sgemm_kernel_info(sel(0, M, N, K, A, K, B, N, C, N))
         return k["bm"], k["bn"]
     bm, bn = shape(4096, 4096, 4096)
     assert bm * bn >= 128 * 128 and (4096 // bm) * (4096 // bn) % 256 == 0
-    assert shape(1024, 1024, 1024) == (64, 64)
-    assert shape(128, 128, 128) == (64, 64)
-    assert shape(1000, 1500, 777) == (64, 64)
+    assert shape(1024, 1024, 1024) == (32, 64)
+    assert shape(128, 128, 128) == (32, 64)
+    assert shape(1000, 1500, 777) == (32, 64)
 
 
 def test_plan_splits_only_when_rounds_are_ragged():
@@ -246,7 +249,7 @@ def test_huge_strides_go_to_the_guarded_instance():
     M, N, K = 70, 160, 40
     small = sg.sgemm_kernel_info(sg.sgemm_select_kernel(0, M, N, K, A, 1 << 19, B, N, C, N))
     assert small["mode"] == sg.SGEMM_MODE_EDGE
-    lda = (1 << 24) + (1 << 20) + 3  # 63 rows of it exceed 4 GiB
+    lda = (1 << 25) + (1 << 22) + 3  # 31 rows of it (32-row tiles) exceed 4 GiB
     huge = sg.sgemm_kernel_info(sg.sgemm_select_kernel(0, M, N, K, A, lda, B, N, C, N))
     assert huge["mode"] == sg.SGEMM_MODE_GUARDED
     # the same through B's stride (B stored as K x N: K-step rows of ldb)
@@ -257,17 +260,18 @@ def test_huge_strides_go_to_the_guarded_instance():
 
 def test_stream_k_instances_and_schedules():
     """Every MFMA tile shape but 256x256 (whose stream-K kernel would not fit
-    its registers) has stream-K instances for every storage in the aligned
-    and edge modes; the host-only planners never pick them (they plan
-    without a workspace)."""
+    its registers) and 32x64 (three resident one-tile workgroups per CU
+    already balance the CUs) has stream-K instances for every storage in the
+    aligned and edge modes; the host-only planners never pick them (they
+    plan without a workspace)."""
     table = sg.kernel_table()
     assert sg.library().sgemm_kernel_schedule(-1) == sg.SGEMM_ERR_VALUE
     sk = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_STREAM_K]
     assert sk and all(k["variant"] == sg.SGEMM_VARIANT_MFMA for k in sk)
     assert all(k["mode"] in (sg.SGEMM_MODE_ALIGNED, sg.SGEMM_MODE_EDGE) for k in sk)
     shapes = {(k["bm"], k["bn"], k["bk"]) for k in table if k["variant"] == sg.SGEMM_VARIANT_MFMA}
-    assert not any((k["bm"], k["bn"]) == (256, 256) for k in sk)
-    for shape in (s for s in shapes if s[:2] != (256, 256)):
+    assert not any((k["bm"], k["bn"]) in ((256, 256), (32, 64)) for k in sk)
+    for shape in (s for s in shapes if s[:2] not in ((256, 256), (32, 64))):
         got = {(k["transa"], k["transb"], k["mode"]) for k in sk
                if (k["bm"], k["bn"], k["bk"]) == shape}
         assert got == {(a, b, m) for a in (0, 1) for b in (0, 1)
@@ -293,13 +297,15 @@ def test_plans_follow_measured_winners():
     """Shapes where the launch-time model must pick what measured fastest on
     MI355X: 4096 x 11008 x 4096 as five rounds of 256x128 then 64x64 tiles
     (2461 us, against 2620 for one 128x128 launch), 8192^2 x 4096 on 256x128
-    (96% of peak), the small and ragged workloads on 64x64."""
+    (96% of peak), 1024^3 on 32x64 (19.8 against 20.5 us on 64x64), 3000^3
+    on 64x64."""
     A, B, C = 0x10000000, 0x20000000, 0x40000000
     name = lambda M, N, K: [sg.sgemm_kernel_name(k) for k, _, _ in
                             sg.sgemm_plan(0, M, N, K, A, K, B, N, C, N)]
     assert name(4096, 11008, 4096) == ["mfma_M256x128_aligned", "mfma_M64x64_aligned"]
     assert name(8192, 8192, 4096) == ["mfma_M256x128_aligned"]
-    assert name(1024, 1024, 1024) == ["mfma_M64x64_aligned"]
+    assert name(1024, 1024, 1024) == ["mfma_M32x64_aligned"]
+    assert name(1000, 1500, 777) == ["mfma_M32x64_edge"]
     assert name(3000, 3000, 3000) == ["mfma_M64x64_edge"]
 
 

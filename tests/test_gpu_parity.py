@@ -322,7 +322,7 @@ def test_large_strides(handle, case):
         lda, ldb, ldc = (1 << 19) + 3, N + 7, (1 << 19) + 1
     else:
         M, N, K = 70, 160, 40
-        lda, ldb, ldc = (1 << 24) + (1 << 20) + 3, N, N + 5
+        lda, ldb, ldc = (1 << 25) + (1 << 22) + 3, N, N + 5
     w = wl.Workload("big", 5100 if case == "rows_past_2_31" else 5101, M, N, K, 1.5, 0.5,
                     "int4")
     a = wl.draw(w.cfg_id, wl.ROLE_A, M, K, w.dist)
