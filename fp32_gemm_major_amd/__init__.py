@@ -59,6 +59,7 @@ EXPORTED = [
     "sgemm_lowp_num_kernels", "sgemm_lowp_kernel_name", "sgemm_lowp_kernel_info",
     "sgemm_lowp_select_kernel", "sgemm_set_lowp_kernel", "sgemm_diag_mfma_chain_lowp",
     "sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz", "sgemm_run_ex_noalloc",
+    "sgemm_lowp_kernel_schedule", "sgemm_lowp_plan_handle",
 ]
 
 
@@ -108,9 +109,12 @@ def _bind(lib):
     lib.sgemm_lowp_select_kernel.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i]
     lib.sgemm_set_lowp_kernel.argtypes = [p, i]
     lib.sgemm_diag_mfma_chain_lowp.argtypes = [i, i, i, p, p]
+    lib.sgemm_lowp_kernel_schedule.argtypes = [i]
+    lib.sgemm_lowp_plan_handle.argtypes = [p, i, i, i, i, i, i, p, i, p, i, p, i, ip, ip]
     lib.sgemm_diag_run_clocked.argtypes = [p, i, i, i, i, i, f, p, i, p, i, f, p, i, p, i, p]
     lib.sgemm_diag_wall_clock_khz.argtypes = [ip]
-    for name in ("sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz", "sgemm_run_ex_noalloc",
+    for name in ("sgemm_lowp_kernel_schedule", "sgemm_lowp_plan_handle",
+                 "sgemm_diag_run_clocked", "sgemm_diag_wall_clock_khz", "sgemm_run_ex_noalloc",
                  "sgemm_run_lowp", "sgemm_diag_mfma_chain_lowp", "sgemm_validate_lowp", "sgemm_lowp_num_kernels",
                  "sgemm_lowp_kernel_info", "sgemm_lowp_select_kernel",
                  "sgemm_set_lowp_kernel"):
@@ -200,12 +204,28 @@ def sgemm_lowp_kernel_name(kernel_id: int):
     return s.decode() if s is not None else None
 
 
+def sgemm_lowp_kernel_schedule(kernel_id: int) -> int:
+    return _check(library().sgemm_lowp_kernel_schedule(kernel_id),
+                  "sgemm_lowp_kernel_schedule")
+
+
+def sgemm_lowp_plan_handle(h, dtype, transa, transb, M, N, K, A, lda, B, ldb, C, ldc):
+    """(kernel id, K splits) of the launch sgemm_run_lowp makes on handle h."""
+    kid, splits = ctypes.c_int(), ctypes.c_int()
+    _check(library().sgemm_lowp_plan_handle(h, dtype, transa, transb, M, N, K, A, lda, B,
+                                            ldb, C, ldc, ctypes.byref(kid),
+                                            ctypes.byref(splits)),
+           "sgemm_lowp_plan_handle")
+    return kid.value, splits.value
+
+
 def sgemm_lowp_kernel_info(kernel_id: int) -> dict:
     vals = [ctypes.c_int() for _ in range(8)]
     _check(library().sgemm_lowp_kernel_info(kernel_id, *[ctypes.byref(v) for v in vals]),
            "sgemm_lowp_kernel_info")
     keys = ("dtype", "bm", "bn", "bk", "threads", "mode", "transa", "transb")
     d = {k: v.value for k, v in zip(keys, vals)}
+    d["schedule"] = sgemm_lowp_kernel_schedule(kernel_id)
     d["name"] = sgemm_lowp_kernel_name(kernel_id)
     d["id"] = kernel_id
     return d

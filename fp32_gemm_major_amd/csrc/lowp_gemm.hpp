@@ -77,6 +77,7 @@
 #include <utility>
 
 #include "mfma_sgemm.hpp"
+#include "skinny_sgemm.hpp"  // skinny_ws_stride: the split-K partial-sum rows
 #include "tile_map.hpp"
 
 namespace sgemm {
@@ -686,6 +687,63 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   e.C = g.C;
   e.ldc = g.ldc;
   store_tile<T, MODE>(e, tm * T::BM, tn * T::BN, acc, acc);
+}
+
+// Split K (products with a few rows of A): workgroup b takes tile
+// b % tiles (tn = tile % tiles_n, tm = tile / tiles_n) over the K range
+// [s*kps, min((s+1)*kps, K)) of split s = b / tiles, kps a multiple of the K
+// step.  That range is the whole K of a sub-problem whose A and B start kps*s
+// values of k in, so lp_tile_accumulate runs on it unchanged (the last
+// split takes the ragged end of K, if any).  The workgroup writes its
+// partial sums, rows < M and columns < N, to ws[s][m][n] (rows of
+// skinny_ws_stride(N) floats); skinny_reduce_kernel adds the splits in split
+// order and applies alpha and beta.
+template <class T, int DT, int MODE, bool TA, bool TB>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+    lp_splitk_kernel(LpArgs g, int tiles_m, int tiles_n, int kps,
+                     float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(1024)))
+  char lds[MODE == MODE_GUARDED ? 2 * (T::A_BYTES + T::B_BYTES) : T::LDS_BYTES];
+  typedef typename LpFmt<DT>::E E;
+  const int tiles = tiles_m * tiles_n;
+  const int split = blockIdx.x / tiles, tile = blockIdx.x - split * tiles;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int k0 = split * kps;
+  LpArgs sub = g;
+  sub.K = g.K - k0 < kps ? g.K - k0 : kps;
+  sub.A = static_cast<const E*>(g.A) + (TA ? (size_t)k0 * g.lda : (size_t)k0);
+  sub.B = static_cast<const E*>(g.B) + (TB ? (size_t)k0 : (size_t)k0 * g.ldb);
+  f32x16 acc[T::FM][T::FN];
+  zero_acc<T>(acc);
+  lp_tile_accumulate<T, DT, MODE, TA, TB>(sub, lds, tm * T::BM, tn * T::BN, acc);
+  // block (i, j), register 4q + e of lane (li, lh): row li, column
+  // 8q + 4lh + e of the block (the epilogue's layout)
+  const WaveCoords<T> w;
+  const int stride = skinny_ws_stride(g.N);
+  float* part = ws + (size_t)split * g.M * stride;
+  const int crow = tm * T::BM + w.wm * T::WM + w.li;
+  const int ccol = tn * T::BN + w.wn * T::WN + w.lh * 4;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int row = crow + i * 32;
+      if (row >= g.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = ccol + j * 32 + 8 * q;
+        float* p = part + (size_t)row * stride + col;
+        if (col + 3 < g.N) {
+          *reinterpret_cast<f32x4*>(p) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < g.N) p[e] = acc[i][j][4 * q + e];
+        }
+      }
+    }
 }
 
 // Tile shapes: LpTile<BM, BN, WM, WN, OCC>.

@@ -99,7 +99,7 @@ hipError_t launch_mfma(const RunArgs& a, int tiles_m, int tiles_n,
   const int nwg = tiles_m * tiles_n;
   hipLaunchKernelGGL((mfma_sgemm_kernel<T, MODE, TA, TB>), dim3(nwg),
                      dim3(T::THREADS), 0, s, gemm_args(a), tiles_m, tiles_n,
-                     band_rows(tiles_m, nwg), c.stamps);
+                     band_rows(tiles_m, nwg, T::BM, T::BN), c.stamps);
   return hipGetLastError();
 }
 
@@ -116,7 +116,7 @@ hipError_t launch_mfma_sk(const RunArgs& a, int tiles_m, int tiles_n,
                           const LaunchCtx& c, hipStream_t s) {
   const int tiles = tiles_m * tiles_n;
   const int grid = c.cus * sk_per_cu<T>();
-  const int band = band_rows(tiles_m, tiles);
+  const int band = band_rows(tiles_m, tiles, T::BM, T::BN);
   const int steps = tile_k_steps<T>(a.K);
   const int dp = sk_dp_tiles(tiles, grid, steps);
   const GemmArgs g = gemm_args(a);
@@ -162,6 +162,44 @@ int skinny_splits(const RunArgs& a, const LaunchCtx& c) {
   if (s < 1) s = 1;
   const long long kps = (a.K + s - 1) / s;
   return (int)((a.K + kps - 1) / kps);  // no empty range
+}
+
+// K splits of an MFMA split-K launch: with one tile row, enough K ranges
+// (whole K steps, at least four each) to give every CU `per_cu` workgroups,
+// as far as the workspace holds their partial sums ([split][M][N rounded up
+// to 4] floats).  *kps receives the range length.
+int mfma_splits(const RunArgs& a, int bm, int bn, int bk, int per_cu,
+                const LaunchCtx& c, int* kps) {
+  const long long tiles = ((long long)(a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+  const long long steps = (a.K + bk - 1) / bk;
+  long long s = (long long)per_cu * c.cus / (tiles > 0 ? tiles : 1);
+  if (s > steps / 4) s = steps / 4;
+  const size_t per_split = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
+  const long long fit = c.ws == nullptr ? 0 : (long long)(c.ws_bytes / per_split);
+  if (s > fit) s = fit;
+  if (s < 1) s = 1;
+  const long long kp = (steps + s - 1) / s * bk;
+  *kps = (int)kp;
+  return (int)((a.K + kp - 1) / kp);
+}
+
+template <class T, int MODE, bool TA, bool TB>
+hipError_t launch_mfma_splitk(const RunArgs& a, int tiles_m, int tiles_n,
+                              const LaunchCtx& c, hipStream_t s) {
+  int kps = a.K;
+  // workgroups a CU holds: waves per CU at the tile's occupancy / waves per
+  // workgroup (32x64: 3, 64x64: 2)
+  const int splits = mfma_splits(a, T::BM, T::BN, T::BKS, 4 * T::OCC / T::WAVES, c, &kps);
+  const GemmArgs g = gemm_args(a);
+  hipLaunchKernelGGL((mfma_splitk_kernel<T, MODE, TA, TB>),
+                     dim3(tiles_m * tiles_n * splits), dim3(T::THREADS), 0, s, g,
+                     tiles_m, tiles_n, kps, c.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long groups = (long long)a.M * (skinny_ws_stride(a.N) / 4);
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((groups + 255) / 256)),
+                     dim3(256), 0, s, g, splits, static_cast<const float*>(c.ws));
+  return hipGetLastError();
 }
 
 template <int MT, bool TA>
@@ -229,6 +267,12 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   {"valu_S" #MT "x16_" PRE "small", SGEMM_VARIANT_VALU, TA, true, MT,       \
    SKINNY_NT_COLS, SKINNY_NT_KC, SKINNY_NT_THREADS, SGEMM_MODE_EDGE,         \
    SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny_nt<MT, TA>}
+// Small M on the matrix cores with K split (edge mode): one tile row of the
+// 32x64 tile (A stored M x K) or of the 64x64 tile (A stored K x M).
+#define MFMA_SPLITK(T, PRE, TA, TB)                                          \
+  {"mfma_" #T "_" PRE "splitk_edge", SGEMM_VARIANT_MFMA, TA, TB, T::BM,     \
+   T::BN, T::BKS, T::THREADS, SGEMM_MODE_EDGE, SGEMM_SCHEDULE_SMALL_M, 0,    \
+   launch_mfma_splitk<T, SGEMM_MODE_EDGE, TA, TB>}
 
 // Largest shape first: ties in the modelled time keep the larger tile.  The
 // 256x256 tile has no stream-K instances: with 128 accumulator registers per
@@ -249,6 +293,8 @@ const KernelDesc kKernels[] = {
     SKINNY(4, "", false), SKINNY(8, "", false), SKINNY(16, "", false),
     SKINNY(4, "tn_", true), SKINNY(8, "tn_", true), SKINNY(16, "tn_", true),
     SKINNY_NT(4, "nt_", false), SKINNY_NT(4, "tt_", true),
+    MFMA_SPLITK(M32x64, "", false, false), MFMA_SPLITK(M32x64, "nt_", false, true),
+    MFMA_SPLITK(M64x64, "tn_", true, false), MFMA_SPLITK(M64x64, "tt_", true, true),
 };
 constexpr int kNumKernels = sizeof(kKernels) / sizeof(kKernels[0]);
 constexpr int kChipCus = 256;
@@ -282,7 +328,15 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
   if (k.schedule == SGEMM_SCHEDULE_STREAM_K &&
       (a.K <= 0 || c.ws == nullptr || c.ws_bytes < sk_workspace_bytes(k, c.cus)))
     return false;
-  if (k.schedule == SGEMM_SCHEDULE_SMALL_M) return a.K > 0 && a.M <= k.bm;
+  if (k.schedule == SGEMM_SCHEDULE_SMALL_M) {
+    if (a.K <= 0 || a.M > k.bm) return false;
+    if (k.variant == SGEMM_VARIANT_VALU) return true;
+    // MFMA split-K: the edge instance's conditions, and a workspace for at
+    // least one set of partial sums
+    const size_t part = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
+    return c.ws != nullptr && c.ws_bytes >= part && (!a.ta || a.M >= 4) &&
+           (a.tb || a.N >= 4) && offsets_fit(k, a);
+  }
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
       return true;
@@ -405,6 +459,23 @@ double skinny_cost(const RunArgs& a, const LaunchCtx& c) {
   return us;
 }
 
+// MFMA split-K launch: ~8.5 us of launch, pipeline fill and second kernel,
+// B (and A once per tile column, mostly from L2: half weight) streamed at
+// ~6.7 TB/s once the workgroups fill the CUs, and the partial sums written
+// and read back at ~5 TB/s.  Fitted on MI355X with the 32x64 tile, B stored
+// N x K or K x N, M 1..32: 4096 x 4096 (64 MB of B) 19.1-19.6 us,
+// 11008 x 4096 34.7-36.4 us, 14336 x 4096 44-45 us, 4096 x 16384 49.4-50 us.
+double mfma_splitk_cost(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
+  int kps = a.K;
+  const int splits = mfma_splits(a, k.bm, k.bn, k.bk, model_of(k).resident, c, &kps);
+  const double wgs = (double)((a.M + k.bm - 1) / k.bm) * ((a.N + k.bn - 1) / k.bn) * splits;
+  const double fill = wgs < c.cus ? wgs / c.cus : 1.0;
+  const double bytes = (double)a.K * a.N * 4 + (double)a.M * a.K * 4 *
+                       ((a.N + k.bn - 1) / k.bn) * 0.5;
+  return 8.5 + bytes / (6.7e12 * fill) * 1e6 +
+         2.0 * splits * a.M * skinny_ws_stride(a.N) * 4.0 / 5e12 * 1e6;
+}
+
 // Aligned one-tile-per-workgroup kernels of the variant and operand storage
 // (the tile shapes).
 bool is_shape(const KernelDesc& k, int variant, const RunArgs& a) {
@@ -461,12 +532,25 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
   if (any_variant) variant = SGEMM_VARIANT_MFMA;
   if (variant != SGEMM_VARIANT_MFMA && variant != SGEMM_VARIANT_VALU)
     return SGEMM_ERR_VALUE;
-  // the small-M kernel for these arguments (the fewest rows that hold M)
+  // the small-M kernel for these arguments: the cheapest of the vector-ALU
+  // ones (AUTO and VALU variants; the fewest rows that hold M) and the MFMA
+  // split-K ones (AUTO and MFMA)
   int skinny = -1;
-  if (any_variant || variant == SGEMM_VARIANT_VALU)
-    for (int i = 0; i < kNumKernels && skinny < 0; ++i)
-      if (kKernels[i].schedule == SGEMM_SCHEDULE_SMALL_M && kernel_fits(kKernels[i], a, ctx))
-        skinny = i;
+  double skinny_us = 0.0;
+  for (int i = 0; i < kNumKernels; ++i) {
+    const KernelDesc& k = kKernels[i];
+    if (k.schedule != SGEMM_SCHEDULE_SMALL_M || !kernel_fits(k, a, ctx)) continue;
+    const bool valu = k.variant == SGEMM_VARIANT_VALU;
+    if (valu ? !(any_variant || variant == SGEMM_VARIANT_VALU) : variant != SGEMM_VARIANT_MFMA)
+      continue;
+    if (valu && skinny >= 0 && kKernels[skinny].variant == SGEMM_VARIANT_VALU)
+      continue;  // a VALU kernel with fewer rows already fits
+    const double us = valu ? skinny_cost(a, ctx) : mfma_splitk_cost(k, a, ctx);
+    if (skinny < 0 || us < skinny_us) {
+      skinny = i;
+      skinny_us = us;
+    }
+  }
   int best = -1;
   double best_cost = 0.0;
   for (int i = 0; i < kNumKernels; ++i) {
@@ -528,7 +612,7 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
       }
     }
   }
-  if (skinny >= 0 && skinny_cost(a, ctx) < best_cost) {
+  if (skinny >= 0 && skinny_us < best_cost) {
     plan->count = 1;
     plan->part[0] = Launch{skinny, 0, a.N};
   }
@@ -648,8 +732,15 @@ struct LpRun {
   int ldc;
 };
 
+// A launch of the split-K kernels: K split into `splits` ranges of `kps`
+// values, partial sums in `ws`.
+struct LpSplit {
+  int splits, kps;
+  float* ws;
+};
+
 typedef hipError_t (*lp_launch_fn)(const LpRun&, int tiles_m, int tiles_n,
-                                   hipStream_t);
+                                   const LpSplit&, hipStream_t);
 
 struct LpKernelDesc {
   const char* name;
@@ -657,12 +748,56 @@ struct LpKernelDesc {
   int ta, tb;
   int bm, bn, bk;
   int threads;
-  int mode;  // SGEMM_MODE_ALIGNED or SGEMM_MODE_GUARDED
+  int mode;      // SGEMM_MODE_*
+  int schedule;  // SGEMM_SCHEDULE_TILES, or SGEMM_SCHEDULE_SMALL_M (split K)
   lp_launch_fn launch;
 };
 
+LpArgs lp_args(const LpRun& a) {
+  LpArgs g;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = a.K;
+  g.alpha = a.alpha;
+  g.beta = a.beta;
+  g.A = a.A;
+  g.lda = a.lda;
+  g.B = a.B;
+  g.ldb = a.ldb;
+  g.C = a.C;
+  g.ldc = a.ldc;
+  return g;
+}
+
 template <class T, int DT, int MODE, bool TA, bool TB>
-hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
+hipError_t launch_lp_splitk(const LpRun& a, int tiles_m, int tiles_n,
+                            const LpSplit& sp, hipStream_t s) {
+  hipLaunchKernelGGL((lp_splitk_kernel<T, DT, MODE, TA, TB>),
+                     dim3(tiles_m * tiles_n * sp.splits), dim3(T::THREADS), 0, s,
+                     lp_args(a), tiles_m, tiles_n, sp.kps, sp.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmArgs r;  // the reduction reads M, N, alpha, beta, C, ldc
+  r.M = a.M;
+  r.N = a.N;
+  r.K = a.K;
+  r.alpha = a.alpha;
+  r.beta = a.beta;
+  r.A = nullptr;
+  r.lda = 0;
+  r.B = nullptr;
+  r.ldb = 0;
+  r.C = a.C;
+  r.ldc = a.ldc;
+  const long long groups = (long long)a.M * (skinny_ws_stride(a.N) / 4);
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((groups + 255) / 256)),
+                     dim3(256), 0, s, r, sp.splits, static_cast<const float*>(sp.ws));
+  return hipGetLastError();
+}
+
+template <class T, int DT, int MODE, bool TA, bool TB>
+hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, const LpSplit&,
+                     hipStream_t s) {
   LpArgs g;
   g.M = a.M;
   g.N = a.N;
@@ -684,7 +819,16 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
 
 #define LP_ONE(T, DT, DTAG, STAG, TA, TB, MODE, MTAG)                        \
   {"lp_" DTAG "_" #T "_" STAG MTAG, DT, TA, TB, T::BM, T::BN,                \
-   LpFmt<DT>::BKE, T::THREADS, MODE, launch_lp<T, DT, MODE, TA, TB>}
+   LpFmt<DT>::BKE, T::THREADS, MODE, SGEMM_SCHEDULE_TILES,                   \
+   launch_lp<T, DT, MODE, TA, TB>}
+// Split-K instances for products with few rows (edge mode only).
+#define LP_SK(T, DT, DTAG, STAG, TA, TB)                                      \
+  {"lp_" DTAG "_" #T "_" STAG "sk_edge", DT, TA, TB, T::BM, T::BN,           \
+   LpFmt<DT>::BKE, T::THREADS, SGEMM_MODE_EDGE, SGEMM_SCHEDULE_SMALL_M,       \
+   launch_lp_splitk<T, DT, SGEMM_MODE_EDGE, TA, TB>}
+#define LP_SK_STORAGE(T, DT, DTAG)                                           \
+  LP_SK(T, DT, DTAG, "", false, false), LP_SK(T, DT, DTAG, "tn_", true, false), \
+  LP_SK(T, DT, DTAG, "nt_", false, true), LP_SK(T, DT, DTAG, "tt_", true, true)
 #define LP_STORAGE(T, DT, DTAG, MODE, MTAG)                                  \
   LP_ONE(T, DT, DTAG, "", false, false, MODE, MTAG),                         \
   LP_ONE(T, DT, DTAG, "tn_", true, false, MODE, MTAG),                       \
@@ -701,7 +845,8 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),               \
   LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                   \
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                     \
-  LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded")
+  LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),               \
+  LP_SK_STORAGE(L64x64, DT, DTAG)
 
 // 8-bit formats: A stored M x K and B stored N x K only (both K-contiguous,
 // the storage 8-bit GEMMs use); the same tiles and modes.
@@ -711,7 +856,8 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, hipStream_t s) {
   LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"),   \
   LP_ONE(L128x128, DT, DTAG, "nt_", false, true, SGEMM_MODE_EDGE, "edge"),       \
   LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_EDGE, "edge"),         \
-  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_GUARDED, "guarded")
+  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_GUARDED, "guarded"),    \
+  LP_SK(L64x64, DT, DTAG, "nt_", false, true)
 
 const LpKernelDesc kLpKernels[] = {
     LP_FORMAT(SGEMM_DTYPE_BF16, "bf16"),
@@ -739,6 +885,7 @@ bool lp_offsets_fit(const LpKernelDesc& k, const LpRun& a) {
 // 2-byte alignment every call has.
 bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
   if (k.dt != a.dt || k.ta != a.ta || k.tb != a.tb) return false;
+  if (k.schedule == SGEMM_SCHEDULE_SMALL_M && a.M > k.bm) return false;
   if (ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn) > INT_MAX) return false;
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
@@ -778,10 +925,76 @@ int lp_select(const LpRun& a, int cus) {
   for (int o = 0; o < 4; ++o)
     for (int id = 0; id < kNumLpKernels; ++id) {
       const LpKernelDesc& k = kLpKernels[id];
+      if (k.schedule != SGEMM_SCHEDULE_TILES) continue;
       if (k.mode != order[o][0] || k.bm != order[o][1]) continue;
       if (lp_fits(k, a)) return id;
     }
   return -1;
+}
+
+// K splits for split-K kernel k on these arguments: with one tile row
+// (M <= bm) and tiles for at most half the CUs, K is split into ranges of
+// whole K steps, at least four steps each, so that the workgroups reach two
+// per CU (the 64x64 tile's occupancy), as far as `ws_bytes` of workspace
+// holds the partial sums ([split][M][N rounded up to 4] floats).  (With more
+// tiles one tile per workgroup already streams B at 5-6 TB/s on MI355X --
+// 4 x 11008 x 4096 in 15.0 us against 18.3 split -- and the partial sums
+// and second kernel cost more than the extra workgroups bring.)  Returns the
+// split count (1: no split) and the range length in *kps.
+int lp_splits(const LpKernelDesc& k, const LpRun& a, int cus, size_t ws_bytes,
+              int* kps) {
+  *kps = a.K;
+  if (a.M > k.bm || a.K <= 0) return 1;
+  const long long tiles = ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn);
+  if (2 * tiles > cus) return 1;
+  const long long steps = ceil_div(a.K, k.bk);
+  long long s = 2LL * cus / tiles;
+  if (s > steps / 4) s = steps / 4;
+  const size_t per_split = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
+  const long long fit = (long long)(ws_bytes / per_split);
+  if (s > fit) s = fit;
+  if (s < 2) return 1;
+  *kps = (int)(ceil_div(steps, s) * k.bk);
+  return (int)ceil_div(a.K, *kps);
+}
+
+// The launch sgemm_run_lowp makes on a handle: the forced kernel, or the
+// split-K kernel when it splits K (a workspace, few rows, few tiles), else
+// lp_select's.  *splits receives the split count (1 for one-tile-per-
+// workgroup kernels).  Returns the kernel id or a negative status.
+int lp_plan(const LpRun& a, int forced, int cus, float* ws, size_t ws_bytes,
+            int* splits, int* kps) {
+  *splits = 1;
+  *kps = a.K;
+  if (forced >= 0) {
+    const LpKernelDesc& k = kLpKernels[forced];
+    if (!lp_fits(k, a)) return SGEMM_ERR_UNSUPPORTED;
+    if (k.schedule == SGEMM_SCHEDULE_SMALL_M) {
+      if (ws == nullptr) return SGEMM_ERR_UNSUPPORTED;
+      *splits = lp_splits(k, a, cus, ws_bytes, kps);
+      if (*splits < 2) {  // runs as one range: still needs one partial set
+        const size_t need = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
+        if (ws_bytes < need) return SGEMM_ERR_UNSUPPORTED;
+        *splits = 1;
+        *kps = a.K;
+      }
+    }
+    return forced;
+  }
+  if (ws != nullptr) {
+    for (int id = 0; id < kNumLpKernels; ++id) {
+      const LpKernelDesc& k = kLpKernels[id];
+      if (k.schedule != SGEMM_SCHEDULE_SMALL_M || !lp_fits(k, a)) continue;
+      const int n = lp_splits(k, a, cus, ws_bytes, kps);
+      if (n >= 2) {
+        *splits = n;
+        return id;
+      }
+    }
+  }
+  *kps = a.K;
+  const int id = lp_select(a, cus);
+  return id >= 0 ? id : SGEMM_ERR_UNSUPPORTED;
 }
 
 Range window_bytes(const void* p, int rows, int cols, int ld, unsigned elem) {
@@ -1192,20 +1405,41 @@ int sgemm_run_lowp(sgemm_handle_t h, int dtype, int transa, int transb, int M,
   if (M == 0 || N == 0) return SGEMM_OK;
   const LpRun a = {dtype, transa, transb, M, N, K, alpha, beta, A, lda, B, ldb,
                    C, ldc};
-  int id = h->forced_lowp;
-  if (id >= 0) {
-    if (!lp_fits(kLpKernels[id], a)) return SGEMM_ERR_UNSUPPORTED;
-  } else {
-    id = lp_select(a, h->cus);
-    if (id < 0) return SGEMM_ERR_UNSUPPORTED;
-  }
+  LpSplit sp = {1, K, static_cast<float*>(h->workspace)};
+  const int id = lp_plan(a, h->forced_lowp, h->cus, sp.ws, h->workspace_bytes,
+                         &sp.splits, &sp.kps);
+  if (id < 0) return id;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != h->device)
     return SGEMM_ERR_DEVICE;
   const LpKernelDesc& k = kLpKernels[id];
-  if (k.launch(a, (int)ceil_div(M, k.bm), (int)ceil_div(N, k.bn), stream) !=
+  if (k.launch(a, (int)ceil_div(M, k.bm), (int)ceil_div(N, k.bn), sp, stream) !=
       hipSuccess)
     return SGEMM_ERR_HIP;
+  return SGEMM_OK;
+}
+
+int sgemm_lowp_kernel_schedule(int id) {
+  return id >= 0 && id < kNumLpKernels ? kLpKernels[id].schedule : SGEMM_ERR_VALUE;
+}
+
+int sgemm_lowp_plan_handle(sgemm_handle_t h, int dtype, int transa, int transb,
+                           int M, int N, int K, const void* A, int lda,
+                           const void* B, int ldb, const float* C, int ldc,
+                           int* kernel, int* splits) {
+  if (h == nullptr) return SGEMM_ERR_HANDLE;
+  const int st = sgemm_validate_lowp(dtype, transa, transb, M, N, K, A, lda, B,
+                                     ldb, 0.0f, C, ldc);
+  if (st != SGEMM_OK) return st;
+  if (M == 0 || N == 0) return SGEMM_ERR_UNSUPPORTED;
+  const LpRun a = {dtype, transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
+                   const_cast<float*>(C), ldc};
+  int n = 1, kps = K;
+  const int id = lp_plan(a, h->forced_lowp, h->cus, static_cast<float*>(h->workspace),
+                         h->workspace_bytes, &n, &kps);
+  if (id < 0) return id;
+  if (kernel) *kernel = id;
+  if (splits) *splits = n;
   return SGEMM_OK;
 }
 

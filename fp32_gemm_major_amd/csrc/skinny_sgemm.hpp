@@ -346,4 +346,61 @@ __global__ void __launch_bounds__(SKINNY_NT_THREADS)
   }
 }
 
+// ---- small M on the matrix cores, K split ---------------------------------
+//
+// For a few rows of A (at most one tile row) against a wide B in either
+// storage: workgroup b takes tile b % tiles (tn = tile % tiles_n, tm =
+// tile / tiles_n) over the K range [s*kps, min((s+1)*kps, K)) of split
+// s = b / tiles, kps a multiple of the tile's K step.  That range is the
+// whole K of a sub-problem whose A and B start kps*s values of k in, so
+// tile_accumulate runs on it unchanged (the last split takes the ragged end
+// of K).  The partial sums, rows < M and columns < N, go to ws[s][m][n]
+// (rows of skinny_ws_stride(N) floats); skinny_reduce_kernel adds the
+// splits in split order and applies alpha and beta.
+template <class T, int MODE, bool TA, bool TB>
+__global__ void __launch_bounds__(T::THREADS, T::OCC)
+    mfma_splitk_kernel(GemmArgs g, int tiles_m, int tiles_n, int kps,
+                       float* __restrict__ ws) {
+  __shared__ __attribute__((aligned(1024))) float lds[TileLds<T, MODE>::FLOATS];
+  const int tiles = tiles_m * tiles_n;
+  const int split = blockIdx.x / tiles, tile = blockIdx.x - split * tiles;
+  const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+  const int k0 = split * kps;
+  GemmArgs sub = g;
+  sub.K = g.K - k0 < kps ? g.K - k0 : kps;
+  sub.A = g.A + (TA ? (size_t)k0 * g.lda : (size_t)k0);
+  sub.B = g.B + (TB ? (size_t)k0 : (size_t)k0 * g.ldb);
+  f32x16 acc[T::FM][T::FN];
+  zero_acc<T>(acc);
+  tile_accumulate<T, MODE, TA, TB>(sub, lds, tm * T::BM, tn * T::BN, 0,
+                                   tile_k_steps<T>(sub.K), acc, acc);
+  const WaveCoords<T> w;
+  if (w.kg != 0) return;  // the first K group holds the tile's sums
+  const int stride = skinny_ws_stride(g.N);
+  float* part = ws + (size_t)split * g.M * stride;
+  const int crow = tm * T::BM + w.wm * T::WM + w.li;
+  const int ccol = tn * T::BN + w.wn * T::WN + w.lh * 4;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int row = crow + i * 32;
+      if (row >= g.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = ccol + j * 32 + 8 * q;
+        float* p = part + (size_t)row * stride + col;
+        if (col + 3 < g.N) {
+          *reinterpret_cast<f32x4*>(p) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                    acc[i][j][4 * q + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < g.N) p[e] = acc[i][j][4 * q + e];
+        }
+      }
+    }
+}
+
 }  // namespace sgemm

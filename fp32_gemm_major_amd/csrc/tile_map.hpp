@@ -4,9 +4,9 @@
 // consecutive workgroup ids to the XCDs round-robin (id % 8).  The mapping
 // first renumbers ids so that each XCD owns one contiguous run of the tile
 // sequence, then walks the tile grid in bands of `band` tile rows
-// (column-major inside a band).  With `band` near the square root of one
-// XCD's share, that share is a near-square block of tiles, so the XCD reads
-// few A rows and B columns and reuses them from its own L2.
+// (column-major inside a band).  With `band` chosen so that one XCD's share
+// is a near-square block of C, the XCD reads few A rows and B columns and
+// reuses them from its own L2.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,12 +15,18 @@ namespace sgemm {
 
 constexpr int kXcds = 8;
 
-// Tile rows per band: the largest power of two whose square fits in one
-// XCD's share of the tiles (and that does not exceed the tile rows).
-__host__ __device__ inline int band_rows(int tiles_m, int nwg) {
-  const int per_xcd = (nwg + kXcds - 1) / kXcds;
+// Tile rows per band: the largest power of two g (at most the tile rows)
+// with g*bm <= (share/g)*bn, i.e. one XCD's share of tiles of bm x bn a
+// block of C no taller than it is wide, in elements.  Rounding toward fewer
+// rows pays: each row of A gives a K step only part of a cache line (the
+// rest is used a step later, and rows with power-of-two strides compete for
+// the same L2 sets), while a row of k of B gives whole lines.  Measured on
+// 4096^3 with 256x128 tiles: 8 rows of tiles (2048 x 1024 per XCD) fetch
+// 745 MB from beyond L2 per launch, 4 rows (1024 x 2048) 603 MB, same time.
+__host__ __device__ inline int band_rows(int tiles_m, int nwg, int bm = 1, int bn = 1) {
+  const long long per_xcd = (nwg + kXcds - 1) / kXcds;
   int g = 1;
-  while (2 * g <= tiles_m && 4 * g * g <= per_xcd) g *= 2;
+  while (2 * g <= tiles_m && 4LL * g * g * bm <= per_xcd * bn) g *= 2;
   return g;
 }
 

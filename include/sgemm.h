@@ -263,11 +263,12 @@ int sgemm_select_kernel(int variant, int M, int N, int K, const float* A,
                         int lda, const float* B, int ldb, const float* C,
                         int ldc);
 
-/* Diagnostics: the workgroup -> output-tile mapping every kernel uses
- * (XCD-contiguous renumbering, then bands of tile rows sized so one XCD's
- * share of the tiles is a near-square block).  nwg must equal
- * tiles_m*tiles_n; for wg in [0, nwg) it stores the tile's row and column
- * indices. */
+/* Diagnostics: the workgroup -> output-tile mapping of the kernels with
+ * square tiles (XCD-contiguous renumbering, then bands of tile rows sized so
+ * one XCD's share of the tiles is a near-square block; kernels whose tiles
+ * are taller than wide use shorter bands, so that the block stays no taller
+ * than wide in elements).  nwg must equal tiles_m*tiles_n; for wg in
+ * [0, nwg) it stores the tile's row and column indices. */
 void sgemm_tile_coords(int wg, int nwg, int tiles_m, int tiles_n, int* tm,
                        int* tn);
 
@@ -345,7 +346,8 @@ int sgemm_diag_wall_clock_khz(int* khz);
  * step (bk: 64 for 16-bit formats, 128 for 8-bit ones); EDGE any sizes with
  * M >= 8 when A is stored K x M and N >= 8 when B is stored K x N; GUARDED
  * (64 x 64 only) any sizes.  Ownership, streams, errors and threading as for
- * sgemm_run. */
+ * sgemm_run; the handle's workspace, when set, also serves the split-K
+ * kernels of products with few rows (sgemm_lowp_kernel_schedule). */
 enum sgemm_dtype {
   SGEMM_DTYPE_BF16 = 1,
   SGEMM_DTYPE_F16 = 2,
@@ -376,8 +378,31 @@ int sgemm_lowp_kernel_info(int kernel_id, int* dtype, int* bm, int* bn,
                            int* bk, int* threads, int* mode, int* transa,
                            int* transb);
 
-/* The kernel sgemm_run_lowp picks for these arguments on a 256-CU device, or
- * a negative status.  Pure function of its inputs. */
+/* SGEMM_SCHEDULE_* of a kernel of the 16-bit/8-bit table (SGEMM_ERR_VALUE
+ * for a bad id).  SGEMM_SCHEDULE_SMALL_M marks the split-K kernels for
+ * products with few rows (M <= bm = 64): with a workspace on the handle
+ * (sgemm_set_workspace) and tiles for at most half the CUs, sgemm_run_lowp
+ * splits K into ranges of whole K steps (at least four each) so that the
+ * workgroups reach two per CU, each range's partial sums go to the
+ * workspace ([split][M][N rounded up to 4] floats), and a second kernel adds
+ * them in range order and applies alpha and beta (deterministic).  Without
+ * a workspace they are not used (a forced one returns
+ * SGEMM_ERR_UNSUPPORTED). */
+int sgemm_lowp_kernel_schedule(int kernel_id);
+
+/* The launch sgemm_run_lowp makes on handle h: *kernel receives the kernel
+ * id and *splits the number of K ranges (1 unless a split-K kernel splits
+ * K); either may be NULL.  Returns SGEMM_OK, or the status sgemm_run_lowp
+ * would return (SGEMM_ERR_UNSUPPORTED for an empty problem); launches
+ * nothing. */
+int sgemm_lowp_plan_handle(sgemm_handle_t h, int dtype, int transa, int transb,
+                           int M, int N, int K, const void* A, int lda,
+                           const void* B, int ldb, const float* C, int ldc,
+                           int* kernel, int* splits);
+
+/* The kernel sgemm_run_lowp picks for these arguments on a 256-CU device
+ * with no workspace (never a split-K kernel), or a negative status.  Pure
+ * function of its inputs. */
 int sgemm_lowp_select_kernel(int dtype, int transa, int transb, int M, int N,
                              int K, const void* A, int lda, const void* B,
                              int ldb, const float* C, int ldc);

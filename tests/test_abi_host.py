@@ -128,12 +128,15 @@ def test_kernel_table():
         assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
     # every MFMA tile shape has an aligned, an edge and a guarded instance for
     # each storage; the VALU shape an aligned and a guarded one; the small-M
-    # kernels one edge instance per storage: 4, 8 and 16 rows with B as
-    # stored, 4 rows with B transposed
+    # kernels one edge instance per storage: on the vector ALUs 4, 8 and 16
+    # rows with B as stored, 4 rows with B transposed; on the matrix cores
+    # (K split) one tile row, 32 with A as stored, 64 with A transposed
     skinny = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
     assert sorted((k["bm"], k["transa"], k["transb"], k["mode"], k["variant"]) for k in skinny) == \
-        sorted((m, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU)
-               for a in (0, 1) for b in (0, 1) for m in ((4,) if b else (4, 8, 16)))
+        sorted([(m, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU)
+                for a in (0, 1) for b in (0, 1) for m in ((4,) if b else (4, 8, 16))] +
+               [(64 if a else 32, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_MFMA)
+                for a in (0, 1) for b in (0, 1)])
     shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table
               if k["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M}
     for s in shapes:

@@ -46,7 +46,10 @@ def _auto_kernel(handle):
     handle.set_lowp_kernel(-1)
 
 
-KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.lowp_kernel_table()
+ALL_KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.lowp_kernel_table()
+# one-tile-per-workgroup kernels (the split-K ones need a workspace: below)
+KERNELS = [k for k in ALL_KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_TILES]
+SPLIT_K = [k for k in ALL_KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
 DT_NAME = {sg.SGEMM_DTYPE_BF16: "bf16", sg.SGEMM_DTYPE_F16: "f16",
            sg.SGEMM_DTYPE_FP8_E4M3: "fp8e4m3", sg.SGEMM_DTYPE_FP8_E5M2: "fp8e5m2"}
 FORMATS8 = wl.FORMATS8
@@ -415,3 +418,95 @@ def test_fp8_mixed_magnitude_integers(handle, dt):
           f"{M * N // 2} outputs with a 448*448 product exact", flush=True)
     assert exact[:, N // 2:].all()  # products of at most 16: exact
     gu.check_full16(ops, out, what=f"{dt} mixed magnitudes")
+
+
+# ---- split K for products with few rows (a workspace on the handle) ----------
+
+@pytest.fixture(scope="module")
+def ws_handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    h = sg.Handle()
+    yield h
+    h.close()
+
+
+def _plan(h, ops):
+    A, B, C = gu.to_device16(ops)
+    code = {"bf16": sg.SGEMM_DTYPE_BF16, "f16": sg.SGEMM_DTYPE_F16,
+            "fp8e4m3": sg.SGEMM_DTYPE_FP8_E4M3, "fp8e5m2": sg.SGEMM_DTYPE_FP8_E5M2}[ops.dt]
+    return sg.sgemm_lowp_plan_handle(h.h, code, int(ops.ta), int(ops.tb), ops.M, ops.N, ops.K,
+                                     A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                                     C.data_ptr(), ops.ldc), (A, B, C)
+
+
+@pytest.mark.parametrize("k", SPLIT_K, ids=[k["name"] for k in SPLIT_K])
+def test_split_k_kernels(ws_handle, k):
+    """Every split-K kernel, forced, on few-row problems: one row, a ragged
+    row count, the most rows it takes; K ragged and long enough for several
+    ranges; odd leading dimensions; integers bit-exact, uniform values within
+    the bound (the 8-bit envelope for 8-bit formats)."""
+    ta, tb = bool(k["transa"]), bool(k["transb"])
+    dt = DT_NAME[k["dtype"]]
+    ws_handle.set_lowp_kernel(k["id"])
+    try:
+        for M in ((8, 37, 64) if ta else (1, 5, 16, 64)):
+            for dist in ("int4", "uniform"):
+                N, K = 300, 40 * k["bk"] + 19
+                w = wl.Workload("lpsk", 9400 + M, M, N, K, 1.5, 0.5, dist)
+                ops = wl.operands16(w, dt, ta=ta, tb=tb, lda=(M if ta else K) + 3,
+                                    ldb=(K if tb else N) + 5, ldc=N + 2)
+                (kid, splits), dev = _plan(ws_handle, ops)
+                assert kid == k["id"] and splits >= 2, (kid, splits)
+                out = gu.run16(ws_handle, ops, dev=dev)
+                gu.check_full16(ops, out, exact=dist == "int4", what=f"{k['name']} M={M} {dist}")
+    finally:
+        ws_handle.set_lowp_kernel(-1)
+
+
+@pytest.mark.parametrize("dt", FORMATS + FORMATS8)
+@pytest.mark.parametrize("shape", [(1, 4096, 4096), (4, 11008, 4096), (16, 4096, 4096)],
+                         ids=["1x4096x4096", "4x11008x4096", "16x4096x4096"])
+def test_split_k_plans(ws_handle, dt, shape):
+    """Decode-like products (a few rows of A against a weight matrix) on a
+    handle with a workspace: K is split when the tiles fill at most half
+    the CUs (N = 4096: 64 tiles), not otherwise (N = 11008: 172 tiles);
+    results within the bound (bit-exact on integers), the same bits on
+    every run."""
+    M, N, K = shape
+    tb = dt in FORMATS8
+    for dist in ("int4", "uniform"):
+        w = wl.Workload("lpskp", 9500 + M, M, N, K, 1.0, 0.5, dist)
+        ops = wl.operands16(w, dt, tb=tb)
+        (kid, splits), dev = _plan(ws_handle, ops)
+        if N == 4096:
+            assert sg.sgemm_lowp_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_SMALL_M
+            assert splits >= 2
+        else:
+            assert sg.sgemm_lowp_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_TILES
+            assert splits == 1
+        c0 = dev[2].clone()
+        out = gu.run16(ws_handle, ops, dev=dev)
+        gu.check_full16(ops, out, exact=dist == "int4", what=f"{dt} {shape} {dist}")
+        dev[2].copy_(c0)
+        again = gu.run16(ws_handle, ops, dev=dev)
+        assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+
+
+def test_split_k_needs_a_workspace(handle):
+    """Without a workspace the planner keeps one tile per workgroup, and a
+    forced split-K kernel is refused before anything runs."""
+    ops = wl.operands16(wl.Workload("lpnows", 9600, 1, 512, 4096, 1.0, 0.0, "int4"), "bf16")
+    (kid, splits), dev = _plan(handle, ops)
+    assert sg.sgemm_lowp_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_TILES and splits == 1
+    sk = next(k for k in SPLIT_K if k["dtype"] == sg.SGEMM_DTYPE_BF16 and not k["transa"]
+              and not k["transb"])
+    handle.set_lowp_kernel(sk["id"])
+    A, B, C = dev
+    c0 = C.clone()
+    with pytest.raises(sg.SgemmError) as e:
+        handle.gemm_lowp(A, B, C, 1.0, 0.0, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
+                         ldb=ops.ldb, ldc=ops.ldc)
+    assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(C, c0)

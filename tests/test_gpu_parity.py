@@ -372,11 +372,11 @@ def test_misaligned_base_pointers(handle):
     gu.check_full(ops, out, exact=True, what="misaligned")
 
 
-@pytest.mark.parametrize("shape", [(32, 4096, 4096), (64, 4096, 4096), (100, 1000, 3000),
+@pytest.mark.parametrize("shape", [(48, 4096, 4096), (64, 4096, 4096), (100, 1000, 3000),
                                    (256, 256, 16384), (512, 512, 8192)])
 def test_stream_k_plans(handle, shape):
-    """Few output tiles over a long K (skinny M past the small-M kernels' 16
-    rows, or a small C with a deep contraction) leave most CUs idle with one
+    """Few output tiles over a long K (M past the small-M kernels' 32 rows,
+    or a small C with a deep contraction) leave most CUs idle with one
     tile per workgroup, so the
     planner runs them stream-K when the handle has a workspace: integer
     inputs, so the split-and-added tiles must still be bit-exact, and two
@@ -484,7 +484,47 @@ def test_no_workspace_no_stream_k():
         h.close()
 
 
-SMALL_M = [k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
+SMALL_M = [k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M
+           and k["variant"] == sg.SGEMM_VARIANT_VALU]
+MFMA_SPLIT_K = [k for k in KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M
+                and k["variant"] == sg.SGEMM_VARIANT_MFMA]
+
+
+@pytest.mark.parametrize("k", MFMA_SPLIT_K, ids=[k["name"] for k in MFMA_SPLIT_K])
+def test_mfma_split_k_kernels(k):
+    """The small-M kernels on the matrix cores (one tile row, K split over
+    workgroups, partial sums in the workspace), forced: 1 row (4 when A is
+    stored K x M), a ragged row count and bm rows; N short of, at and past a
+    tile and not a multiple of 4; K below one K step, ragged, and long enough
+    for many ranges; padded leading dimensions; integers exact, uniform
+    values within the bound.  Without a workspace they are refused."""
+    h = sg.Handle()
+    try:
+        h.set_kernel(k["id"])
+        ta, tb = bool(k["transa"]), bool(k["transb"])
+        m_small = 4 if ta else 1
+        cases = [(m_small, 37, 7), (k["bm"] // 2 + 1, 300, 1025), (k["bm"], 64, 4111),
+                 (m_small, 4098, 3000), (k["bm"], 1000, 777)]
+        for i, (M, N, K) in enumerate(cases):
+            for dist in ("int4", "uniform"):
+                w = wl.Workload("mfsk", 7600 + 10 * i + k["id"], M, N, K, 1.5, -0.5, dist)
+                ops = wl.operands(w, lda=(M if ta else K) + 3, ldb=(K if tb else N) + 1,
+                                  ldc=N + 2, ta=ta, tb=tb)
+                gu.check_full(ops, gu.run(h, ops), exact=(dist == "int4"),
+                              what=f"{k['name']} {M}x{N}x{K} {dist}")
+        h.set_workspace(0)
+        ops = wl.operands(wl.Workload("mfsk", 7700, k["bm"], 300, 1025, 1.0, 1.0, "int4"),
+                          ta=ta, tb=tb)
+        A, B, C = gu.to_device(ops)
+        c0 = C.clone()
+        with pytest.raises(sg.SgemmError) as e:
+            h.gemm(A, B, C, 1.0, 1.0, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda, ldb=ops.ldb,
+                   ldc=ops.ldc, transa=ta, transb=tb)
+        assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+        assert torch.equal(C, c0)
+    finally:
+        h.close()
 
 
 @pytest.mark.parametrize("k", SMALL_M, ids=[k["name"] for k in SMALL_M])
