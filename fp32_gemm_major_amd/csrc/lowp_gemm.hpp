@@ -28,12 +28,13 @@
 //   kernels): lane l's 16 bytes land in slot 64*i + l of the tile, and the
 //   lane reads the global piece that the swizzle puts in that slot.
 // * Aligned kernels keep S LDS stages (two for the 256x256 tile, four for the
-//   smaller ones); the loads of step k+S go out right after step k's barrier
-//   and have S-1 steps to land.  The barrier sits before a step's last group
-//   of MFMAs, and every group issues its MFMAs one at a time with the next
-//   group's fragment reads and the loads in the slots between them, in a
-//   fixed order: one wave per SIMD keeps the matrix pipe busy without
-//   another wave to hide its reads and loads.
+//   smaller ones); the loads of step k+S go out after step k's barrier, over
+//   the step's second half, and have about S-1 steps to land.  The barrier
+//   sits halfway through a step's groups of MFMAs, the fragment reads run
+//   half a step ahead, and every group issues its MFMAs one at a time with
+//   reads and loads in the slots between them, in a fixed order: one wave
+//   per SIMD keeps the matrix pipe busy without another wave to hide its
+//   reads and loads.
 // * Edge kernels (any sizes; M >= 8 when A is stored K x M, N >= 8 when B
 //   is stored K x N) run the whole K steps on the aligned kernels' schedule,
 //   with what lies past M or N clamped (a K-contiguous row past the edge
@@ -552,13 +553,20 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     // of MFMAs is issued one MFMA at a time with other work in the slots
     // between them, in a fixed order (scheduling barriers), so that with one
     // wave per SIMD the matrix pipe is not left idle while the wave issues
-    // reads or loads:
-    //   groups 0-2 of step kt: the next group's fragment reads;
+    // reads or loads.  Each group q has a fragment set of its own, and the
+    // reads run H = QG/2 groups ahead:
+    //   groups 0 .. H-1 of step kt: reads of groups H .. QG-1 of step kt;
     //   barrier of step kt: every wave has read all of stage kt (lgkmcnt(0))
     //     and seen its direct loads of step kt+1 land (vmcnt(0));
-    //   group 3 of step kt: step kt+1's first fragments, now visible, and
-    //     step kt+2's direct loads into stage kt, now free, which so have a
-    //     whole step to land.
+    //   groups H .. QG-1: reads of groups 0 .. H-1 of step kt+1, now
+    //     visible, and step kt+2's direct loads into stage kt, now free,
+    //     spread over those groups' slots.
+    // The LDS so takes the loads' writes over half a step: with 16-bit
+    // operands (four groups of 32-cycle MFMAs) the loads and reads that had
+    // shared the last group asked the LDS for 1.5 times the group's length
+    // (4096^3 bfloat16: 124 -> 114 us).  A barrier before group 1, with the
+    // loads over three groups, measured no better: the last loads then have
+    // a quarter step to land instead of half a step.
     auto issue_step = [&](int kt, int st) {
 #pragma unroll
       for (int o = 0; o < ND; ++o) direct_one(kt, st, o);
@@ -577,23 +585,25 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       const bool straddle = (!A_KC && (M & 7) != 0) || (!B_KC && (N & 7) != 0);
       kd = straddle ? (K - 1) / BKE : K / BKE;
     }
-    auto group = [&](int kl, auto st_c, auto q_c, const Frag& cur, Frag& nxt) {
+    constexpr int H = QG / 2;  // groups the reads run ahead (the barrier precedes group H)
+    Frag fr[QG];
+    auto group = [&](int kl, auto st_c, auto q_c) {
       constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
       constexpr int st1 = st + 1 == S ? 0 : st + 1;
+      // the group read in this one's slots, and the stage it comes from
+      constexpr int rq = (q + H) % QG;
+      constexpr int rst = q + H < QG ? st : st1;
 #pragma unroll
       for (int m = 0; m < SL; ++m) {
-        mma_one(cur, m);
-        if (q < QG - 1) {
+        mma_one(fr[q], m);
 #pragma unroll
-          for (int r = 0; r < NF; ++r)
-            if (r * SL / NF == m) read_one(st, q + 1, r, nxt);
-        } else {
-#pragma unroll
-          for (int r = 0; r < NF; ++r)
-            if (r * SL / NF == m) read_one(st1, 0, r, nxt);
+        for (int r = 0; r < NF; ++r)
+          if (r * SL / NF == m) read_one(rst, rq, r, fr[rq]);
+        if (q >= H) {
+          constexpr int SLOTS = (QG - H) * SL;
 #pragma unroll
           for (int o = 0; o < ND; ++o)
-            if (o * SL / ND == m) direct_one(kl, st, o);
+            if (o * SLOTS / ND == (q - H) * SL + m) direct_one(kl, st, o);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -602,21 +612,16 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     // the S-2 later steps' loads are still in flight.
     constexpr int AHEAD = (S - 2) * ND;
     constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
-    Frag f0, f1;
     auto step = [&](int kt, auto st_c) {
       const int kl = kt + S < kd ? kt + S : kd - 1;
-      // groups 0 .. QG-2, alternating the two fragment sets
-      lp_static_for<QG - 1>([&](auto q_c) {
-        if constexpr (decltype(q_c)::value % 2 == 0)
-          group(kl, st_c, q_c, f0, f1);
-        else
-          group(kl, st_c, q_c, f1, f0);
-      });
+      lp_static_for<H>([&](auto q_c) { group(kl, st_c, q_c); });
       wait_lds();
       __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      group(kl, st_c, std::integral_constant<int, QG - 1>{}, f1, f0);  // (QG is even)
+      lp_static_for<QG - H>([&](auto i) {
+        group(kl, st_c, std::integral_constant<int, H + decltype(i)::value>{});
+      });
     };
     if (!EDGE || kd > 0) {  // (aligned kernels run with K >= 64)
       // Steps 0 .. S-1 go out first; step 0 must have landed before the
@@ -629,7 +634,9 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       __builtin_amdgcn_s_waitcnt(0x0F70 | (FIRST & 15) | ((FIRST >> 4) << 14));
       wait_lds();
       __syncthreads();
-      read_frag(0, 0, f0);
+      lp_static_for<H>([&](auto q_c) {
+        read_frag(0, decltype(q_c)::value, fr[decltype(q_c)::value]);
+      });
       int kt = 0;
       for (; kt + S <= kd; kt += S)
         lp_static_for<S>([&](auto i) { step(kt + decltype(i)::value, i); });

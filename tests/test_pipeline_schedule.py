@@ -10,7 +10,8 @@ events in program order separates them in every wave.  Checked:
   reads).
 
 The generators mirror the loop control of `tile_accumulate` (the two-stage
-fragment-prefetch loop and the S-stage loop) step for step."""
+fragment-prefetch loop and the S-stage loop) and of the aligned loop of
+`lp_tile_accumulate` (16- and 8-bit operands) step for step."""
 
 import pytest
 
@@ -92,8 +93,9 @@ def check(ev):
             reads_since_bar = {}
         elif x[0] == "read":
             _, k, st = x
-            assert holder.get(st) == k, f"stage {st} holds {holder.get(st)}, read for {k}"
-            assert k in visible, f"step {k} read before it was waited for and a barrier passed"
+            if k is not None:  # (None: a read whose values are never used)
+                assert holder.get(st) == k, f"stage {st} holds {holder.get(st)}, read for {k}"
+                assert k in visible, f"step {k} read before it was waited for and a barrier passed"
             reads_since_bar.setdefault(st, set()).add(k)
     return ev
 
@@ -119,3 +121,62 @@ def test_the_model_sees_a_missing_barrier():
     i = max(j for j, x in enumerate(ev[:6]) if x == ("bar",))
     with pytest.raises(AssertionError, match="overwrites stage 0"):
         check(ev[:i] + ev[i + 1:])
+
+
+def lowp_schedule(kd, nst, qg, tail=False):
+    """The aligned loop of the 16- and 8-bit kernels over kd direct-load
+    steps: S = nst stages, QG groups of MFMAs per step, the barrier before
+    group H = QG/2.  Look-ahead loads past the last step repeat the last step
+    (clamped) into stages never read again; at the last step the groups after
+    the barrier still read the next stage (values never used).  `tail`: the
+    edge kernels' register-staged last step into stage 0."""
+    h = qg // 2
+    ev = []
+    if kd > 0:
+        for st in range(nst):
+            ev.append(("dma", min(st, kd - 1), st))
+        ev.append(("wait", nst - 1))
+        ev.append(("bar",))
+        for _ in range(h):  # groups 0 .. H-1 of step 0
+            ev.append(("read", 0, 0))
+        for kt in range(kd):
+            st, st1 = kt % nst, (kt + 1) % nst
+            kl = min(kt + nst, kd - 1)
+            for _ in range(h):  # groups 0 .. H-1: reads of groups H .. QG-1 of step kt
+                ev.append(("read", kt, st))
+            ev.append(("wait", nst - 2))
+            ev.append(("bar",))
+            for _ in range(qg - h):  # groups H .. QG-1
+                ev.append(("read", kt + 1 if kt + 1 < kd else None, st1))
+                ev.append(("dma", kl, st))
+    if tail:
+        ev.append(("wait", 0))
+        ev.append(("bar",))
+        ev.append(("dma", kd, 0))  # register stores, waited for (lgkmcnt(0))
+        ev.append(("wait", 0))
+        ev.append(("bar",))
+        ev.append(("read", kd, 0))
+    return ev
+
+
+@pytest.mark.parametrize("qg", [2, 4])
+@pytest.mark.parametrize("nst", [2, 4])
+@pytest.mark.parametrize("kd", range(0, 10))
+@pytest.mark.parametrize("tail", [False, True])
+def test_lowp_loop_hazards(qg, nst, kd, tail):
+    if kd == 0 and not tail:
+        return
+    ev = check(lowp_schedule(kd, nst, qg, tail))
+    want = list(range(kd + (1 if tail else 0)))
+    assert sorted({x[1] for x in ev if x[0] == "read" and x[1] is not None}) == want
+
+
+def test_the_lowp_model_sees_a_load_before_the_barrier():
+    """A step's first direct load issued before the step's barrier instead of
+    after it overwrites the stage other waves may still be reading."""
+    ev = lowp_schedule(6, 2, 4)
+    i = ev.index(("bar",), 4)          # the first step's barrier
+    j = next(k for k in range(i, len(ev)) if ev[k][0] == "dma")
+    moved = ev[:i] + [ev[j]] + ev[i:j] + ev[j + 1:]
+    with pytest.raises(AssertionError, match="overwrites stage 0"):
+        check(moved)
