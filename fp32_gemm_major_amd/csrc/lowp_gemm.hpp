@@ -694,6 +694,9 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   e.C = g.C;
   e.ldc = g.ldc;
   store_tile<T, MODE>(e, tm * T::BM, tn * T::BN, acc, acc);
+  // The K loop's last steps issue look-ahead loads into LDS that nothing
+  // waits for: they must land before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 // Split K (products with a few rows of A): workgroup b takes tile
@@ -751,6 +754,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
         }
       }
     }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the K loop's look-ahead loads into LDS
 }
 
 // Tile shapes: LpTile<BM, BN, WM, WN, OCC>.

@@ -197,8 +197,9 @@ hipError_t launch_mfma_splitk(const RunArgs& a, int tiles_m, int tiles_n,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long groups = (long long)a.M * (skinny_ws_stride(a.N) / 4);
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((groups + 255) / 256)),
-                     dim3(256), 0, s, g, splits, static_cast<const float*>(c.ws));
+  hipLaunchKernelGGL(skinny_reduce_kernel,
+                     dim3((unsigned)((groups + SKINNY_REDUCE_THREADS - 1) / SKINNY_REDUCE_THREADS)),
+                     dim3(SKINNY_REDUCE_THREADS), 0, s, g, splits, static_cast<const float*>(c.ws));
   return hipGetLastError();
 }
 
@@ -223,8 +224,9 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const long long groups = (long long)a.M * (skinny_ws_stride(a.N) / 4);
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((groups + 255) / 256)),
-                     dim3(256), 0, s, g, splits, static_cast<const float*>(c.ws));
+  hipLaunchKernelGGL(skinny_reduce_kernel,
+                     dim3((unsigned)((groups + SKINNY_REDUCE_THREADS - 1) / SKINNY_REDUCE_THREADS)),
+                     dim3(SKINNY_REDUCE_THREADS), 0, s, g, splits, static_cast<const float*>(c.ws));
   return hipGetLastError();
 }
 
@@ -790,8 +792,9 @@ hipError_t launch_lp_splitk(const LpRun& a, int tiles_m, int tiles_n,
   r.C = a.C;
   r.ldc = a.ldc;
   const long long groups = (long long)a.M * (skinny_ws_stride(a.N) / 4);
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((groups + 255) / 256)),
-                     dim3(256), 0, s, r, sp.splits, static_cast<const float*>(sp.ws));
+  hipLaunchKernelGGL(skinny_reduce_kernel,
+                     dim3((unsigned)((groups + SKINNY_REDUCE_THREADS - 1) / SKINNY_REDUCE_THREADS)),
+                     dim3(SKINNY_REDUCE_THREADS), 0, s, r, sp.splits, static_cast<const float*>(sp.ws));
   return hipGetLastError();
 }
 
