@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_4096]
                     [--prewarm-s S] [--variant mfma|valu] [--no-cpu-baseline]
                     [--no-per-config] [--lowp all|bf16|f16|fp8|fp8e4m3|fp8e5m2|none]
-                    [--lowp-only]
+                    [--lowp-only] [--lowp-k K]
 
 A step is one SGEMM call, C = alpha*A*B + beta*C, on the headline workload
 (M = N = K = 4096, alpha = 1.5, beta = 0.5, uniform [-1, 1) inputs, C
@@ -21,11 +21,14 @@ oracle timed on a bounded sample of the same workload, and per-workload
 GFLOPS for the other problem shapes; then the same problems with bfloat16,
 binary16, E4M3 or E5M2 A and B and FP32 C (the "lowp" object: per format,
 the headline problem's roofline against the dense matrix-core peak of that
-format, and the other shapes).
+format, and the other shapes).  --lowp-only --lowp-k K times only the 16/8-bit
+headline problem with K in place of 4096: two such runs under a cycle counter
+give the kernels' cost per K step apart from their fixed cost.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -240,8 +243,10 @@ def lowp_section(args, sg, rf, wl, torch):
     h = sg.Handle(workspace=False)
     out = {}
 
-    def prepare(name, dt, ta=False, tb=False):
+    def prepare(name, dt, ta=False, tb=False, k=0):
         w = wl.WORKLOADS[name]
+        if k > 0:  # the same problem at another K (--lowp-k)
+            w = dataclasses.replace(w, K=k)
         ops = wl.operands16(w, dt, ta=ta, tb=tb)
         raw = "uint8" if dt in wl.FORMATS8 else "int16"
         A = torch.from_numpy(ops.A.view(raw)).cuda().view(tdt[dt])
@@ -259,7 +264,7 @@ def lowp_section(args, sg, rf, wl, torch):
     for dt in formats:
         peak = peaks[dt]
         fp8 = dt in wl.FORMATS8
-        w, dev, kid, launch = prepare(args.workload, dt, tb=fp8)
+        w, dev, kid, launch = prepare(args.workload, dt, tb=fp8, k=args.lowp_k)
         steps = max(args.steps // 2, 10)
         # A change of workload restarts the GPU's clock ramp (tens of
         # milliseconds): the same pre-warm as the FP32 call, shorter.
@@ -290,7 +295,7 @@ def lowp_section(args, sg, rf, wl, torch):
             sec["storage"] = "A M x K, B N x K"
         del dev
         per_config = {}
-        if not args.no_per_config:
+        if not args.no_per_config and args.lowp_k <= 0:
             cases = [("c1_128", False, fp8, 200), ("c2_1024", False, fp8, 200),
                      ("c4_edge", False, fp8, 100), ("c5_mlp", False, fp8, 20)]
             if not fp8:
@@ -330,6 +335,10 @@ def main(argv=None):
     ap.add_argument("--lowp", choices=["all", "bf16", "f16", "fp8", "fp8e4m3", "fp8e5m2",
                                        "none"], default="all",
                     help="which 16-bit- or 8-bit-input products to time after the FP32 ones")
+    ap.add_argument("--lowp-k", type=int, default=0,
+                    help="time the 16/8-bit headline problem at this K instead (two "
+                         "runs at different K separate a kernel's cost per K step from "
+                         "its fixed cost); the other workloads are then skipped")
     ap.add_argument("--lowp-only", action="store_true",
                     help="time only the 16-bit- and 8-bit-input products (for profiler "
                          "runs)")
