@@ -164,23 +164,40 @@ int skinny_splits(const RunArgs& a, const LaunchCtx& c) {
   return (int)((a.K + kps - 1) / kps);  // no empty range
 }
 
-// K splits of an MFMA split-K launch: with one tile row, enough K ranges
-// (whole K steps, at least four each) to give every CU `per_cu` workgroups,
-// as far as the workspace holds their partial sums ([split][M][N rounded up
-// to 4] floats).  *kps receives the range length.
-int mfma_splits(const RunArgs& a, int bm, int bn, int bk, int per_cu,
+// K splits of an MFMA split-K launch (one tile row): the split count s that
+// minimizes the busiest CU's work, ceil(tiles*s / cus) workgroups of
+// ceil(steps/s) K steps each, with every workgroup resident at once (at most
+// `resident` per CU), K ranges of at least four steps, and the partial sums
+// ([split][M][N rounded up to 4] floats) inside the workspace; on a tie the
+// larger s (more loads in flight).  Measured on MI355X with the 32x64 tile
+// (graph replays; three workgroups fit a CU): 16 x 4096 x 4096 (64 tiles, 64
+// steps) takes 16.7-16.9 us with 4 or 8 splits against 19.0 us with 12;
+// 16 x 11008 x 4096 (172 tiles) 35 us with 4 splits (688 workgroups, at most
+// 3 x 16 steps per CU) against 38-39 with 2 or 3 (2 x 32 or 3 x 22 steps);
+// 16 x 4096 x 16384 45.6 us with 8 splits against 49.3 with 12.  *kps
+// receives the range length in k.
+int mfma_splits(const RunArgs& a, int bm, int bn, int bk, int resident,
                 const LaunchCtx& c, int* kps) {
   const long long tiles = ((long long)(a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
   const long long steps = (a.K + bk - 1) / bk;
-  long long s = (long long)per_cu * c.cus / (tiles > 0 ? tiles : 1);
-  if (s > steps / 4) s = steps / 4;
   const size_t per_split = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
-  const long long fit = c.ws == nullptr ? 0 : (long long)(c.ws_bytes / per_split);
-  if (s > fit) s = fit;
-  if (s < 1) s = 1;
-  const long long kp = (steps + s - 1) / s * bk;
-  *kps = (int)kp;
-  return (int)((a.K + kp - 1) / kp);
+  const long long fit = c.ws == nullptr ? 1 : (long long)(c.ws_bytes / per_split);
+  const long long cus = c.cus > 0 ? c.cus : 1;
+  long long best = 1, best_work = -1;
+  for (long long s = 1; s == 1 || (s <= steps / 4 && s <= fit); ++s) {
+    const long long kp = (steps + s - 1) / s;
+    const long long n = (steps + kp - 1) / kp;  // splits that range length gives
+    const long long per_cu = (tiles * n + cus - 1) / cus;
+    if (s > 1 && per_cu > resident) break;
+    const long long work = per_cu * kp;
+    if (best_work < 0 || work <= best_work) {
+      best = n;
+      best_work = work;
+    }
+  }
+  const long long kp = (steps + best - 1) / best;
+  *kps = (int)(kp * bk);
+  return (int)((a.K + *kps - 1) / *kps);
 }
 
 template <class T, int MODE, bool TA, bool TB>
@@ -461,12 +478,13 @@ double skinny_cost(const RunArgs& a, const LaunchCtx& c) {
   return us;
 }
 
-// MFMA split-K launch: ~8.5 us of launch, pipeline fill and second kernel,
+// MFMA split-K launch: ~6 us of launch, pipeline fill and second kernel,
 // B (and A once per tile column, mostly from L2: half weight) streamed at
-// ~6.7 TB/s once the workgroups fill the CUs, and the partial sums written
+// ~7.5 TB/s once the workgroups fill the CUs, and the partial sums written
 // and read back at ~5 TB/s.  Fitted on MI355X with the 32x64 tile, B stored
-// N x K or K x N, M 1..32: 4096 x 4096 (64 MB of B) 19.1-19.6 us,
-// 11008 x 4096 34.7-36.4 us, 14336 x 4096 44-45 us, 4096 x 16384 49.4-50 us.
+// N x K or K x N, M 1..32 (graph replays): 4096 x 4096 (64 MB of B)
+// 16.2-17.4 us, 11008 x 4096 34.7-36.2 us, 14336 x 4096 38.6-39.0 us,
+// 4096 x 16384 45.2-46.4 us.
 double mfma_splitk_cost(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
   int kps = a.K;
   const int splits = mfma_splits(a, k.bm, k.bn, k.bk, model_of(k).resident, c, &kps);
@@ -474,7 +492,7 @@ double mfma_splitk_cost(const KernelDesc& k, const RunArgs& a, const LaunchCtx& 
   const double fill = wgs < c.cus ? wgs / c.cus : 1.0;
   const double bytes = (double)a.K * a.N * 4 + (double)a.M * a.K * 4 *
                        ((a.N + k.bn - 1) / k.bn) * 0.5;
-  return 8.5 + bytes / (6.7e12 * fill) * 1e6 +
+  return 6.0 + bytes / (7.5e12 * fill) * 1e6 +
          2.0 * splits * a.M * skinny_ws_stride(a.N) * 4.0 / 5e12 * 1e6;
 }
 
