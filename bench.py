@@ -225,10 +225,10 @@ def lowp_section(args, sg, rf, wl, torch):
     """The products with 16-bit A and B (bfloat16 / binary16) or 8-bit A and
     B (E4M3 / E5M2) and FP32 C: the headline problem timed back to back on
     the launch stream, as its own roofline against the dense matrix-core
-    peak of its input format, and the other workloads (and, for 16-bit
-    formats, transposed storage) from replayed HIP graphs.  8-bit operands
-    are stored K-contiguous (A as M x K, B as N x K), the one storage their
-    kernels take."""
+    peak of its input format, and the other workloads and the headline
+    problem in the other storages from replayed HIP graphs.  The 8-bit
+    headline and workloads store A as M x K and B as N x K (both
+    K-contiguous), the 16-bit ones A as M x K and B as K x N."""
     formats = {"all": ("bf16", "f16", "fp8e4m3", "fp8e5m2"), "bf16": ("bf16",),
                "f16": ("f16",), "fp8": ("fp8e4m3", "fp8e5m2"),
                "fp8e4m3": ("fp8e4m3",), "fp8e5m2": ("fp8e5m2",), "none": ()}[args.lowp]
@@ -298,16 +298,17 @@ def lowp_section(args, sg, rf, wl, torch):
         if not args.no_per_config and args.lowp_k <= 0:
             cases = [("c1_128", False, fp8, 200), ("c2_1024", False, fp8, 200),
                      ("c4_edge", False, fp8, 100), ("c5_mlp", False, fp8, 20)]
-            if not fp8:
-                cases += [(args.workload, False, True, 20), (args.workload, True, False, 20),
-                          (args.workload, True, True, 20)]
+            # the headline problem in the other three storages
+            cases += [(args.workload, ta, tb, 20) for ta, tb in
+                      ((False, False), (False, True), (True, False), (True, True))
+                      if (ta, tb) != (False, fp8)]
             for name, ta, tb, reps in cases:
                 w2, dev2, kid2, launch2 = prepare(name, dt, ta, tb)
                 ms = time_graph(launch2, reps, torch)
                 gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
-                tag = name + ({(False, False): "", (False, True): "_nt",
-                               (True, False): "_tn", (True, True): "_tt"}[(ta, tb)]
-                              if not fp8 else "")
+                suffix = {(False, False): "_nn", (False, True): "_nt",
+                          (True, False): "_tn", (True, True): "_tt"}[(ta, tb)]
+                tag = name + (suffix if name == args.workload else "")
                 per_config[tag] = {"gflops": round(gf, 1),
                                    "frac_of_peak": round(gf * 1e9 / peak, 4),
                                    "kernel_ms": round(ms, 5),

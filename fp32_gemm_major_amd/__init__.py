@@ -182,8 +182,8 @@ def sgemm_run_ex_noalloc(h, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta
 def sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha, A, lda, B, ldb, beta, C,
                    ldc, stream=0) -> int:
     """The product with 16-bit A and B (SGEMM_DTYPE_BF16 / SGEMM_DTYPE_F16) or
-    8-bit A and B (SGEMM_DTYPE_FP8_E4M3 / SGEMM_DTYPE_FP8_E5M2, transa 0 and
-    transb 1 only) and FP32 C; A, B, C are device addresses."""
+    8-bit A and B (SGEMM_DTYPE_FP8_E4M3 / SGEMM_DTYPE_FP8_E5M2), any storage,
+    and FP32 C; A, B, C are device addresses."""
     return _check(library().sgemm_run_lowp(h, dtype, transa, transb, M, N, K, alpha,
                                            A, lda, B, ldb, beta, C, ldc, stream),
                   "sgemm_run_lowp")
@@ -548,8 +548,8 @@ class Handle:
                   transb=False):
         """C[:M, :N] = alpha * op(A) @ op(B) + beta * C with A and B bfloat16,
         float16, float8_e4m3fn or float8_e5m2 CUDA tensors (both the same
-        format; 8-bit ones with transb=True and transa=False) and C a float32
-        CUDA tensor; shapes, leading dimensions and ``stream`` as in ``gemm``."""
+        format, any storage) and C a float32 CUDA tensor; shapes, leading
+        dimensions and ``stream`` as in ``gemm``."""
         formats = {torch.bfloat16: SGEMM_DTYPE_BF16, torch.float16: SGEMM_DTYPE_F16,
                    torch.float8_e4m3fn: SGEMM_DTYPE_FP8_E4M3,
                    torch.float8_e5m2: SGEMM_DTYPE_FP8_E5M2}

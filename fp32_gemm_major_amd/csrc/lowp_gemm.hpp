@@ -35,18 +35,20 @@
 //   reads and loads in the slots between them, in a fixed order: one wave
 //   per SIMD keeps the matrix pipe busy without another wave to hide its
 //   reads and loads.
-// * Edge kernels (any sizes; M >= 8 when A is stored K x M, N >= 8 when B
-//   is stored K x N) run the whole K steps on the aligned kernels' schedule,
-//   with what lies past M or N clamped (a K-contiguous row past the edge
-//   reads the last valid row, an outer-contiguous piece wholly past the edge
-//   the last eight valid indices, a piece that straddles the edge is read as
-//   it is and runs into the next k row -- so, when one can straddle, the
-//   step holding the last K row is left out); those values only feed outputs
-//   that are never stored.  The rest of K goes through registers, zero-filled,
-//   in the K-contiguous layout, and stores are masked on edge tiles.
+// * Edge kernels (any sizes; M at least one 16-byte piece -- 8 elements of a
+//   16-bit format, 16 of an 8-bit one -- when A is stored K x M, N likewise
+//   when B is stored K x N) run the whole K steps on the aligned kernels'
+//   schedule, with what lies past M or N clamped (a K-contiguous row past the
+//   edge reads the last valid row, an outer-contiguous piece wholly past the
+//   edge the last piece's worth of valid indices, a piece that straddles the
+//   edge is read as it is and runs into the next k row -- so, when one can
+//   straddle, the step holding the last K row is left out); those values
+//   only feed outputs that are never stored.  The rest of K goes through
+//   registers, zero-filled, in the register-staged layout below, and stores
+//   are masked on edge tiles.
 // * Guarded kernels (any sizes and strides) load every operand through
 //   registers, one step ahead, with zero fill past the edges (no lane leaves
-//   before the barriers): K-contiguous pieces go to LDS as they are;
+//   before the barriers): K-contiguous pieces go to LDS as they are; 16-bit
 //   outer-contiguous ones are transposed in registers -- each lane loads an
 //   8 x 8 block (eight 16-byte loads of k rows) and writes eight 16-byte units
 //   of eight k, built by v_perm; lanes with odd block column write their rows
@@ -56,12 +58,16 @@
 // * Global loads of both kinds, direct-to-LDS ones included, take any byte
 //   address on gfx950 (checked with in-bounds probes at 1- and 2-byte
 //   offsets): no kernel needs aligned leading dimensions or base pointers.
-// * 8-bit operands (stored K-contiguous only: A as M x K, B as N x K) use the
-//   same kernels with the element size halved: a 16-byte unit holds 16 k, a
-//   K step is 128 k (LDS rows stay 128 bytes, same swizzle), and each lane
-//   hands the 8-bit instruction 32 consecutive bytes of k per operand (two
-//   units), with unit block scales; a step has two groups of 64 k in place
-//   of four of 16.  That instruction sums each block of 64 products in a
+// * 8-bit operands use the same kernels with the element size halved: a
+//   16-byte unit holds 16 elements, a K step is 128 k (K-contiguous LDS rows
+//   stay 128 bytes, same swizzle), and each lane hands the 8-bit instruction
+//   32 consecutive bytes of k per operand (two units), with unit block
+//   scales; a step has two groups of 64 k in place of four of 16.  An 8-bit
+//   operand stored outer-contiguous keeps its stored layout in LDS in every
+//   mode (rows of k, units swizzled by lp_oc_swz8; register-staged steps
+//   load whole 16-byte pieces into the same layout, zero-filled past the
+//   edges) and its fragments come from transposing reads
+//   (ds_read_b64_tr_b8, four per fragment).  That instruction sums each block of 64 products in a
 //   fixed-point window below the block's largest product before adding it
 //   to the FP32 accumulator (measured), so its sums carry more rounding
 //   error than an FP32 accumulation of the same products.
@@ -175,6 +181,31 @@ __device__ __forceinline__ int lp_oc_swz(int k) {
   return X >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
 }
 
+// Outer-contiguous tiles of 8-bit elements: rows of k holding X outer
+// indices in X / 16 units of 16 bytes; unit p of row k sits at p ^
+// lp_oc_swz8<X>(k).  Half a wave of a transposing read (ds_read_b64_tr_b8)
+// touches eight consecutive rows (k & 7 = 0..7) at two units c and c ^ 1 (c
+// even), so the sixteen (row, unit) pairs must land on distinct 16-byte bank
+// groups: the XOR takes even values only (c and c ^ 1 then fill complementary
+// groups) that differ between rows starting on the same group -- rows of 256
+// bytes all start on one group (2 * (k & 7)), rows of 128 bytes on two
+// (2 * (k / 2 & 3)), rows of 64 bytes on four (2 * (k / 4 & 1)); each XOR
+// stays inside its row.
+template <int X>
+__device__ __forceinline__ int lp_oc_swz8(int k) {
+  static_assert(X == 64 || X == 128 || X == 256, "8-bit outer-contiguous tile width");
+  return 2 * (X == 256 ? (k & 7) : X == 128 ? ((k >> 1) & 3) : ((k >> 2) & 1));
+}
+
+// The unit swizzle of an outer-contiguous tile of ESZ-byte elements.
+template <int ESZ, int X>
+__device__ __forceinline__ int lp_oc_unit_swz(int k) {
+  if constexpr (ESZ == 2)
+    return lp_oc_swz<X>(k);
+  else
+    return lp_oc_swz8<X>(k);
+}
+
 // Byte offset of 16-byte unit c (k = 8c .. 8c+7) of row r in an operand tile.
 __device__ __forceinline__ int lp_unit_off(int r, int c) {
   return r * 128 + 16 * (c ^ ((r >> 1) & 7));
@@ -238,7 +269,6 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   constexpr bool EDGE = MODE == MODE_EDGE;
   constexpr bool A_KC = !TA;  // A stored K-contiguous
   constexpr bool B_KC = TB;   // B stored K-contiguous
-  static_assert(ESZ == 2 || (A_KC && B_KC), "8-bit operands are stored K-contiguous");
   const int M = g.M, N = g.N, K = g.K;
   const E* __restrict__ A = static_cast<const E*>(g.A);
   const E* __restrict__ B = static_cast<const E*>(g.B);
@@ -294,9 +324,10 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         a_voff[v] = ESZ * ((unsigned)r * (unsigned)lda + UE * (unsigned)a_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
-        const int k = u / (T::BM / 8), c = (u % (T::BM / 8)) ^ lp_oc_swz<T::BM>(k);
-        int o = 8 * c;
-        if (EDGE && m0 + o >= M) o = M - 8 > m0 ? M - 8 - m0 : 0;
+        constexpr int UPR = T::BM * ESZ / 16;  // units per row of k
+        const int k = u / UPR, c = (u % UPR) ^ lp_oc_unit_swz<ESZ, T::BM>(k);
+        int o = UE * c;
+        if (EDGE && m0 + o >= M) o = M - UE > m0 ? M - UE - m0 : 0;
         a_voff[v] = ESZ * ((unsigned)k * (unsigned)lda + (unsigned)o);
       }
     }
@@ -308,9 +339,10 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         b_voff[v] = ESZ * ((unsigned)r * (unsigned)ldb + UE * (unsigned)b_c[v]);
       } else {
         const int u = (v * T::WAVES + wave) * 64 + lane;
-        const int k = u / (T::BN / 8), c = (u % (T::BN / 8)) ^ lp_oc_swz<T::BN>(k);
-        int o = 8 * c;
-        if (EDGE && n0 + o >= N) o = N - 8 > n0 ? N - 8 - n0 : 0;
+        constexpr int UPR = T::BN * ESZ / 16;  // units per row of k
+        const int k = u / UPR, c = (u % UPR) ^ lp_oc_unit_swz<ESZ, T::BN>(k);
+        int o = UE * c;
+        if (EDGE && n0 + o >= N) o = N - UE > n0 ? N - UE - n0 : 0;
         b_voff[v] = ESZ * ((unsigned)k * (unsigned)ldb + (unsigned)o);
       }
     }
@@ -325,8 +357,13 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   constexpr int A_RK = ((GUARD || EDGE) && A_KC) ? T::A_VEC : 1;
   constexpr int B_RK = ((GUARD || EDGE) && B_KC) ? T::B_VEC : 1;
   u32x4 ra_kc[A_RK], rb_kc[B_RK];
-  // Outer-contiguous operands: one 8 x 8 block per lane of the loading waves.
-  u32x4 ra_t[TA ? 8 : 1], rb_t[TB ? 1 : 8];
+  // Outer-contiguous operands: 16-bit ones as one 8 x 8 block per lane of the
+  // loading waves, transposed in registers to the K-contiguous layout; 8-bit
+  // ones as 16-byte units in their own layout (read by transposing reads).
+  constexpr bool A_T16 = TA && ESZ == 2, B_T16 = !TB && ESZ == 2;
+  constexpr bool A_O8 = TA && ESZ == 1, B_O8 = !TB && ESZ == 1;
+  u32x4 ra_t[A_T16 ? 8 : 1], rb_t[B_T16 ? 8 : 1];
+  u32x4 ra_o[A_O8 ? T::A_VEC : 1], rb_o[B_O8 ? T::B_VEC : 1];
   // (every wave when the tile has as many 64-wide regions as waves)
   const bool a_tw = T::A_TW >= T::WAVES || wave < T::A_TW;
   const bool b_tw = T::B_TW >= T::WAVES || wave < T::B_TW;
@@ -353,7 +390,33 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
                                 row < N ? K - k : 0);
       }
     }
-    if constexpr (TA) {
+    if constexpr (A_O8) {
+      if (ops & 1) {
+#pragma unroll
+        for (int v = 0; v < T::A_VEC; ++v) {
+          constexpr int UPR = T::BM / 16;
+          const int u = (v * T::WAVES + wave) * 64 + lane;
+          const int kr = u / UPR, k = k0 + kr;
+          const int o = m0 + 16 * ((u % UPR) ^ lp_oc_swz8<T::BM>(kr));
+          const bool in = k < K && o < M;
+          ra_o[v] = lp_load_unit(A + (in ? (size_t)k * lda + o : (size_t)0), in ? M - o : 0);
+        }
+      }
+    }
+    if constexpr (B_O8) {
+      if (ops & 2) {
+#pragma unroll
+        for (int v = 0; v < T::B_VEC; ++v) {
+          constexpr int UPR = T::BN / 16;
+          const int u = (v * T::WAVES + wave) * 64 + lane;
+          const int kr = u / UPR, k = k0 + kr;
+          const int o = n0 + 16 * ((u % UPR) ^ lp_oc_swz8<T::BN>(kr));
+          const bool in = k < K && o < N;
+          rb_o[v] = lp_load_unit(B + (in ? (size_t)k * ldb + o : (size_t)0), in ? N - o : 0);
+        }
+      }
+    }
+    if constexpr (A_T16) {
       if (a_tw && (ops & 1)) {
         const int o = m0 + a_to;
 #pragma unroll
@@ -363,7 +426,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
         }
       }
     }
-    if constexpr (!TB) {
+    if constexpr (B_T16) {
       if (b_tw && (ops & 2)) {
         const int o = n0 + b_to;
 #pragma unroll
@@ -403,15 +466,15 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   };
   // Transposed row r of the step's register blocks (A's rows first) into
   // stage st.
-  constexpr int NS = (TA ? 8 : 0) + (TB ? 0 : 8);
+  constexpr int NS = (A_T16 ? 8 : 0) + (B_T16 ? 8 : 0);
   auto store_t_row = [&](int st, int r) {
-    if (TA && r < 8) {
-      if constexpr (TA) {
+    if (A_T16 && r < 8) {
+      if constexpr (A_T16) {
         if (a_tw) store_row(lds + a_off(st), ra_t, a_to, r);
       }
     } else {
-      if constexpr (!TB) {
-        if (b_tw) store_row(lds + b_off(st), rb_t, b_to, TA ? r - 8 : r);
+      if constexpr (B_T16) {
+        if (b_tw) store_row(lds + b_off(st), rb_t, b_to, A_T16 ? r - 8 : r);
       }
     }
   };
@@ -430,7 +493,23 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     }
 #pragma unroll
     for (int r = 0; r < NS; ++r)
-      if ((TA && r < 8) ? (ops & 1) : (ops & 2)) store_t_row(st, r);
+      if ((A_T16 && r < 8) ? (ops & 1) : (ops & 2)) store_t_row(st, r);
+    if constexpr (A_O8) {
+      if (ops & 1) {
+#pragma unroll
+        for (int v = 0; v < T::A_VEC; ++v)
+          *reinterpret_cast<u32x4*>(lds + a_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
+              ra_o[v];
+      }
+    }
+    if constexpr (B_O8) {
+      if (ops & 2) {
+#pragma unroll
+        for (int v = 0; v < T::B_VEC; ++v)
+          *reinterpret_cast<u32x4*>(lds + b_off(st) + 16 * ((v * T::WAVES + wave) * 64 + lane)) =
+              rb_o[v];
+      }
+    }
   };
 
   // ---- fragments and MFMAs: four groups of 16 k per K step ------------------
@@ -466,6 +545,35 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return u32x4{l2[0], l2[1], h2[0], h2[1]};
   };
+  // A fragment of 32 outer indices of an 8-bit outer-contiguous tile of width
+  // X (every mode), by four transposing reads (ds_read_b64_tr_b8).  In each
+  // group of 16 lanes such a read hands lane i, as byte e, byte i % 8 of the
+  // eight that lane 2e + i / 8 points at (measured on the device with an
+  // in-bounds probe).  So lane 2e + h points at row k + e and outer indices
+  // 8h .. 8h+7 of the lane group's 16 (lanes 0-15 and 32-47 the block's first
+  // 16, the others the next 16; lanes 32-63 the k half 32 .. 63 of group q's
+  // 64), and lane i receives eight consecutive k of outer index i; read j
+  // gives k 8j .. 8j+7 of the lane's 32, the K-contiguous fragment's order.
+  const int t8_e = (lane & 15) >> 1;
+  const int t8_o = 16 * ((lane >> 4) & 1) + 8 * (lane & 1);  // outer index in the block
+  auto read_tr8 = [&](const char* tile, auto x_c, int o_block, int q, u32x4 (&out)[FU]) {
+    constexpr int X = decltype(x_c)::value;
+    typedef int v2i32 __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+    const int o = o_block + t8_o;
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      v2i32 part[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int k = 64 * q + 32 * lh + 8 * (2 * u + jj) + t8_e;
+        const int off = k * X + 16 * ((o >> 4) ^ lp_oc_swz8<X>(k)) + (o & 15);
+        part[jj] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(lds_void_t*)(tile + off));
+      }
+      out[u] = u32x4{(unsigned)part[0][0], (unsigned)part[0][1], (unsigned)part[1][0],
+                     (unsigned)part[1][1]};
+    }
+  };
   // Read r of a group, in the order the MFMAs (i-major) first need them:
   // a[0], b[0 .. FN-1], then a[1 .. FM-1].
   // K-contiguous fragment units: lane half lh of group q holds units
@@ -479,14 +587,20 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   auto read_one = [&](int st, int q, int r, Frag& f) {
     if (r >= 1 && r <= T::FN) {
       const int j = r - 1;
-      if constexpr (!GUARD && !B_KC)
+      if constexpr (B_O8)
+        read_tr8(lds + b_off(st), std::integral_constant<int, T::BN>{}, wn * T::WN + j * 32,
+                 q, f.b[j]);
+      else if constexpr (!GUARD && !B_KC)
         f.b[j][0] = read_tr(lds + b_off(st), std::integral_constant<int, T::BN>{},
                             wn * T::WN + j * 32, q);
       else
         kc_frag(lds + b_off(st), wn * T::WN + j * 32 + li, q, f.b[j]);
     } else {
       const int i = r == 0 ? 0 : r - T::FN;
-      if constexpr (!GUARD && !A_KC)
+      if constexpr (A_O8)
+        read_tr8(lds + a_off(st), std::integral_constant<int, T::BM>{}, wm * T::WM + i * 32,
+                 q, f.a[i]);
+      else if constexpr (!GUARD && !A_KC)
         f.a[i][0] = read_tr(lds + a_off(st), std::integral_constant<int, T::BM>{},
                             wm * T::WM + i * 32, q);
       else
@@ -497,13 +611,26 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
 #pragma unroll
     for (int r = 0; r < NF; ++r) read_one(st, q, r, f);
   };
-  // Fragments of a stage in the K-contiguous layout whatever the storage (the
-  // register-staged step of guarded and edge kernels).
+  // Fragments of a register-staged stage (guarded kernels; the last step of
+  // edge kernels): the K-contiguous layout, into which 16-bit outer-contiguous
+  // operands are transposed in registers; 8-bit ones keep their own layout.
   auto read_frag_kc = [&](int st, int q, Frag& f) {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) kc_frag(lds + a_off(st), wm * T::WM + i * 32 + li, q, f.a[i]);
+    for (int i = 0; i < T::FM; ++i) {
+      if constexpr (A_O8)
+        read_tr8(lds + a_off(st), std::integral_constant<int, T::BM>{}, wm * T::WM + i * 32,
+                 q, f.a[i]);
+      else
+        kc_frag(lds + a_off(st), wm * T::WM + i * 32 + li, q, f.a[i]);
+    }
 #pragma unroll
-    for (int j = 0; j < T::FN; ++j) kc_frag(lds + b_off(st), wn * T::WN + j * 32 + li, q, f.b[j]);
+    for (int j = 0; j < T::FN; ++j) {
+      if constexpr (B_O8)
+        read_tr8(lds + b_off(st), std::integral_constant<int, T::BN>{}, wn * T::WN + j * 32,
+                 q, f.b[j]);
+      else
+        kc_frag(lds + b_off(st), wn * T::WN + j * 32 + li, q, f.b[j]);
+    }
   };
   auto mma_one = [&](const Frag& f, int m) {
     const int i = m / T::FN, j = m % T::FN;
@@ -582,7 +709,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     // straddle the M or N edge (its read runs into the next k row).
     int kd = nk;
     if (EDGE) {
-      const bool straddle = (!A_KC && (M & 7) != 0) || (!B_KC && (N & 7) != 0);
+      const bool straddle = (!A_KC && (M & (UE - 1)) != 0) || (!B_KC && (N & (UE - 1)) != 0);
       kd = straddle ? (K - 1) / BKE : K / BKE;
     }
     constexpr int H = QG / 2;  // groups the reads run ahead (the barrier precedes group H)

@@ -857,9 +857,10 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, const LpSplit&,
   LP_ONE(T, DT, DTAG, "tt_", true, true, MODE, MTAG)
 // Every tile in aligned instances; the 128x128 and 64x64 tiles in edge
 // instances (a 256x256 edge kernel spills registers); the guarded instance
-// (only the 64x64 tile) takes what the others cannot: an extent under 8
-// along which an outer-contiguous operand's pieces run, or strides whose
-// tile span passes the 32-bit offsets of the direct loads.
+// (only the 64x64 tile) takes what the others cannot: an extent under one
+// 16-byte piece (8 elements of a 16-bit format, 16 of an 8-bit one) along
+// which an outer-contiguous operand's pieces run, or strides whose tile span
+// passes the 32-bit offsets of the direct loads.  Every format and storage.
 #define LP_FORMAT(DT, DTAG)                                                  \
   LP_STORAGE(L256x256, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
   LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_ALIGNED, "aligned"),             \
@@ -869,22 +870,11 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, const LpSplit&,
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),               \
   LP_SK_STORAGE(L64x64, DT, DTAG)
 
-// 8-bit formats: A stored M x K and B stored N x K only (both K-contiguous,
-// the storage 8-bit GEMMs use); the same tiles and modes.
-#define LP_FORMAT8(DT, DTAG)                                                 \
-  LP_ONE(L256x256, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"), \
-  LP_ONE(L128x128, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"), \
-  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_ALIGNED, "aligned"),   \
-  LP_ONE(L128x128, DT, DTAG, "nt_", false, true, SGEMM_MODE_EDGE, "edge"),       \
-  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_EDGE, "edge"),         \
-  LP_ONE(L64x64, DT, DTAG, "nt_", false, true, SGEMM_MODE_GUARDED, "guarded"),    \
-  LP_SK(L64x64, DT, DTAG, "nt_", false, true)
-
 const LpKernelDesc kLpKernels[] = {
     LP_FORMAT(SGEMM_DTYPE_BF16, "bf16"),
     LP_FORMAT(SGEMM_DTYPE_F16, "f16"),
-    LP_FORMAT8(SGEMM_DTYPE_FP8_E4M3, "e4m3"),
-    LP_FORMAT8(SGEMM_DTYPE_FP8_E5M2, "e5m2"),
+    LP_FORMAT(SGEMM_DTYPE_FP8_E4M3, "e4m3"),
+    LP_FORMAT(SGEMM_DTYPE_FP8_E5M2, "e5m2"),
 };
 constexpr int kNumLpKernels = sizeof(kLpKernels) / sizeof(kLpKernels[0]);
 
@@ -911,10 +901,12 @@ bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
       return true;
-    case SGEMM_MODE_EDGE:
-      // an outer-contiguous piece of 8 elements needs 8 to clamp onto
-      return a.K > 0 && (!a.ta || a.M >= 8) && (a.tb || a.N >= 8) &&
+    case SGEMM_MODE_EDGE: {
+      // an outer-contiguous 16-byte piece needs as many elements to clamp onto
+      const int piece = 16 / lp_elem_bytes(a.dt);
+      return a.K > 0 && (!a.ta || a.M >= piece) && (a.tb || a.N >= piece) &&
              lp_offsets_fit(k, a);
+    }
     default:
       return a.K > 0 && a.M % k.bm == 0 && a.N % k.bn == 0 && a.K % k.bk == 0 &&
              lp_offsets_fit(k, a);

@@ -335,17 +335,20 @@ int sgemm_diag_wall_clock_khz(int* khz);
  * different size (448*448 beside 1*1) may lose the small ones.  Infinities
  * and NaNs in A or B
  * propagate as the matrix unit's FP32 arithmetic makes them; finite inputs
- * whose products or sums overflow FP32 give infinities.  8-bit formats take
- * only transa = SGEMM_OP_N and transb = SGEMM_OP_T (A stored M x K, B stored
- * N x K: both K-contiguous); other storages return SGEMM_ERR_UNSUPPORTED.
+ * whose products or sums overflow FP32 give infinities.  Every format takes
+ * every storage; an operand stored with its outer index contiguous (A as
+ * K x M, B as K x N) is read through the LDS transposing reads, which for
+ * 8-bit formats costs some speed (4096^3: ~75 us against ~67 us with A
+ * stored M x K and B N x K).
  *
  * Memory: A and B are device pointers to 2-byte (16-bit formats) or 1-byte
  * elements, 16-bit ones at least 2-byte aligned (SGEMM_ERR_VALUE otherwise);
  * no kernel needs more.  Kernels (sgemm_lowp_kernel_info): ALIGNED takes M
  * and N multiples of the tile (64, 128 or 256) and K a multiple of the K
  * step (bk: 64 for 16-bit formats, 128 for 8-bit ones); EDGE any sizes with
- * M >= 8 when A is stored K x M and N >= 8 when B is stored K x N; GUARDED
- * (64 x 64 only) any sizes.  Ownership, streams, errors and threading as for
+ * M of at least one 16-byte piece (8 elements of a 16-bit format, 16 of an
+ * 8-bit one) when A is stored K x M and N likewise when B is stored K x N;
+ * GUARDED (64 x 64 only) any sizes.  Ownership, streams, errors and threading as for
  * sgemm_run; the handle's workspace, when set, also serves the split-K
  * kernels of products with few rows (sgemm_lowp_kernel_schedule). */
 enum sgemm_dtype {
@@ -357,8 +360,9 @@ enum sgemm_dtype {
 
 /* Enqueue the 16-bit or 8-bit product on `stream` and return without
  * waiting.  SGEMM_ERR_VALUE for an unknown dtype or storage flag or a
- * misaligned A or B; SGEMM_ERR_UNSUPPORTED for an 8-bit format in a storage
- * it does not take; other statuses as sgemm_run_ex. */
+ * misaligned A or B; SGEMM_ERR_UNSUPPORTED when a forced kernel
+ * (sgemm_set_lowp_kernel) cannot run the arguments; other statuses as
+ * sgemm_run_ex. */
 int sgemm_run_lowp(sgemm_handle_t h, int dtype, int transa, int transb, int M,
                    int N, int K, float alpha, const void* A, int lda,
                    const void* B, int ldb, float beta, float* C, int ldc,

@@ -162,30 +162,35 @@ def to_device16(ops: wl.Operands16):
 FP8_BLOCK_ALLOWANCE = 2.0 ** -9
 
 
-def _abs_max_rows(bits, dt, rows, ld, cols):
-    """max |x| over the first ``cols`` entries of each of ``rows`` stored
-    rows of 8-bit patterns (decoded by torch)."""
+def _abs_max(bits, dt, rows, ld, cols, dim):
+    """max |x| of ``rows`` stored rows of 8-bit patterns (their first
+    ``cols`` entries, decoded by torch) along ``dim``: 1 gives one value per
+    stored row, 0 one per stored column."""
     if rows == 0 or cols == 0:
-        return np.zeros(rows)
+        return np.zeros(rows if dim == 1 else cols)
     x = torch.from_numpy(bits[: rows * ld].reshape(rows, ld)[:, :cols].copy())
     v = x.view(TORCH_FORMATS[dt]).to(torch.float64).abs()
-    return v.max(dim=1).values.numpy()
+    return v.max(dim=dim).values.numpy()
 
 
 def fp8_block_units(ops: wl.Operands16, pr, pc):
     """|alpha| * ceil(K/64) * max_k|a_ik| * max_k|b_kj| at outputs (pr, pc):
-    the scale of the 8-bit block allowance.  8-bit A is stored M x K and B
-    N x K."""
-    assert not ops.ta and ops.tb
-    amax = _abs_max_rows(ops.A, ops.dt, ops.M, ops.lda, ops.K)
-    bmax = _abs_max_rows(ops.B, ops.dt, ops.N, ops.ldb, ops.K)
+    the scale of the 8-bit block allowance, in any storage of A and B."""
+    if ops.ta:   # A stored K x M: max over the stored rows
+        amax = _abs_max(ops.A, ops.dt, ops.K, ops.lda, ops.M, 0) if ops.K else np.zeros(ops.M)
+    else:
+        amax = _abs_max(ops.A, ops.dt, ops.M, ops.lda, ops.K, 1)
+    if ops.tb:   # B stored N x K
+        bmax = _abs_max(ops.B, ops.dt, ops.N, ops.ldb, ops.K, 1)
+    else:
+        bmax = _abs_max(ops.B, ops.dt, ops.K, ops.ldb, ops.N, 0) if ops.K else np.zeros(ops.N)
     blocks = -(-ops.K // 64)
     return abs(ops.alpha) * blocks * amax[pr] * bmax[pc]
 
 
 def fp8_extra(ops: wl.Operands16, pr, pc):
     """The 8-bit block allowance at outputs (pr, pc), or None for 16-bit
-    formats.  8-bit A is stored M x K and B N x K."""
+    formats."""
     if ops.dt not in wl.FORMATS8:
         return None
     return FP8_BLOCK_ALLOWANCE * fp8_block_units(ops, pr, pc)

@@ -53,7 +53,7 @@ def test_kernel_table():
     names = [k["name"] for k in t]
     assert len(set(names)) == len(names) == sg.sgemm_lowp_num_kernels()
     combos = {(k["dtype"], k["transa"], k["transb"], k["bm"], k["mode"]) for k in t}
-    for dt in (BF16, F16):
+    for dt in (BF16, F16, E4M3, E5M2):
         for ta in (0, 1):
             for tb in (0, 1):
                 for bm in (64, 128, 256):
@@ -65,14 +65,8 @@ def test_kernel_table():
         assert k["bk"] == (128 if k["dtype"] >= E4M3 else 64)
         assert k["threads"] == 256 and k["bm"] == k["bn"]
         assert ("bf16" in k["name"]) == (k["dtype"] == BF16)
-        if k["dtype"] >= E4M3:  # 8-bit: A stored M x K, B stored N x K only
-            assert (k["transa"], k["transb"]) == (0, 1)
-    for dt in (E4M3, E5M2):
-        for bm in (64, 128, 256):
-            assert (dt, 0, 1, bm, sg.SGEMM_MODE_ALIGNED) in combos
-        for bm in (64, 128):
-            assert (dt, 0, 1, bm, sg.SGEMM_MODE_EDGE) in combos
-        assert (dt, 0, 1, 64, sg.SGEMM_MODE_GUARDED) in combos
+        tag = {(0, 0): "", (1, 0): "tn_", (0, 1): "nt_", (1, 1): "tt_"}[(k["transa"], k["transb"])]
+        assert f"x{k['bn']}_{tag}" in k["name"]
     assert sg.sgemm_lowp_kernel_name(-1) is None
     assert sg.sgemm_lowp_kernel_name(len(t)) is None
     with pytest.raises(sg.SgemmError):
@@ -156,8 +150,18 @@ def test_select_fp8(dt):
     assert (k["bm"], k["mode"]) == (128, E)
     k = _pick(dt, 1024, 1024, 1024, tb=1, A=(1 << 20) + 1, B=(1 << 33) + 3)
     assert (k["bm"], k["mode"]) == (64, A)
+    # every storage: A or B stored outer-contiguous (read by transposing reads)
     for ta, tb in ((0, 0), (1, 0), (1, 1)):
-        assert _pick(dt, 256, 256, 256, ta=ta, tb=tb) == sg.SGEMM_ERR_UNSUPPORTED
+        k = _pick(dt, 4096, 4096, 4096, ta=ta, tb=tb)
+        assert (k["bm"], k["mode"], k["transa"], k["transb"]) == (256, A, ta, tb)
+        k = _pick(dt, 1000, 1500, 777, ta=ta, tb=tb)
+        assert (k["bm"], k["mode"]) == (64, E)
+    # an outer-contiguous 8-bit piece is 16 elements: 15 columns of B stored
+    # K x N go to the guarded kernel, 16 to the edge one
+    assert _pick(dt, 300, 15, 200)["mode"] == sg.SGEMM_MODE_GUARDED
+    assert _pick(dt, 300, 16, 200)["mode"] == E
+    assert _pick(dt, 15, 300, 200, ta=1, tb=1)["mode"] == sg.SGEMM_MODE_GUARDED
+    assert _pick(dt, 16, 300, 200, ta=1, tb=1)["mode"] == E
 
 
 def test_diag_chain_argument_errors():

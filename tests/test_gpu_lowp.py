@@ -229,15 +229,17 @@ def test_aligned_kernels_short_k(handle, nk):
         gu.check_full16(ops, out, exact=True, what=f"{k['name']} nk={nk}")
 
 
-@pytest.mark.parametrize("case", ["k_whole_straddle", "k_whole_no_straddle", "k_short",
-                                  "k_one_past"])
+@pytest.mark.parametrize("case", ["k_whole_straddle", "k_whole_no_straddle",
+                                  "k_piece8_not16", "k_short", "k_one_past"])
 def test_edge_kernels_k_cases(handle, case):
-    """Edge kernels: K a multiple of 64 with an M or N edge that is not a
-    multiple of 8 (the last whole K step goes through registers), the same
-    with multiples of 8 (every step a direct load), K under 64 (no direct
-    steps at all) and K one past a multiple of 64."""
-    M, N, K = {"k_whole_straddle": (150, 133, 192), "k_whole_no_straddle": (152, 136, 192),
-               "k_short": (150, 133, 40), "k_one_past": (150, 133, 129)}[case]
+    """Edge kernels: K a multiple of the K step with an M or N edge that is not
+    a multiple of one 16-byte piece (8 elements of a 16-bit format, 16 of an
+    8-bit one: the last whole K step goes through registers), the same with
+    multiples of a piece (every step a direct load), K under one step (no
+    direct steps at all) and K one past a multiple of 64."""
+    M, N, K = {"k_whole_straddle": (150, 133, 256), "k_whole_no_straddle": (160, 144, 256),
+               "k_piece8_not16": (152, 136, 256), "k_short": (150, 133, 40),
+               "k_one_past": (150, 133, 129)}[case]
     for k in KERNELS:
         if k["mode"] != sg.SGEMM_MODE_EDGE:
             continue
@@ -251,15 +253,22 @@ def test_edge_kernels_k_cases(handle, case):
 
 
 
-# ---- 8-bit formats (A stored M x K, B stored N x K) ----------------------------
+# ---- 8-bit formats ---------------------------------------------------------------
 
+STORAGES = [(False, True), (False, False), (True, False), (True, True)]
+STORAGE_IDS = ["nt", "nn", "tn", "tt"]
+
+
+@pytest.mark.parametrize("ta,tb", STORAGES, ids=STORAGE_IDS)
 @pytest.mark.parametrize("dt", FORMATS8)
 @pytest.mark.parametrize("name", ["c1_128", "c1_128_int", "c2_1024", "c4_edge",
                                   "c4_edge_int"])
-def test_fp8_small_workloads_full(handle, dt, name):
-    ops = wl.operands16(W[name], dt, tb=True)
+def test_fp8_small_workloads_full(handle, dt, name, ta, tb):
+    """Every storage: A and B stored K-contiguous (K rows of A as M x K, B as
+    N x K) or outer-contiguous (read through the 8-bit transposing LDS read)."""
+    ops = wl.operands16(W[name], dt, ta=ta, tb=tb)
     out = gu.run16(handle, ops)
-    gu.check_full16(ops, out, exact=W[name].dist == "int4", what=f"{name} {dt}")
+    gu.check_full16(ops, out, exact=W[name].dist == "int4", what=f"{name} {dt} {ta}{tb}")
 
 
 @pytest.mark.parametrize("dt", FORMATS8)
@@ -273,24 +282,39 @@ def test_fp8_large_workloads_sampled(handle, dt, name):
                        what=f"{name} {dt}")
 
 
+@pytest.mark.parametrize("ta,tb", STORAGES, ids=STORAGE_IDS)
+@pytest.mark.parametrize("dt", FORMATS8)
+def test_fp8_transposed_4096_sampled(handle, dt, ta, tb):
+    ops = wl.operands16(W["c3_4096"], dt, ta=ta, tb=tb)
+    out = gu.run16(handle, ops)
+    gu.check_sampled16(ops, out, [0, 255, 256, 2047, 4095], [0, 256, 4095],
+                       npoints=2048, what=f"4096 {dt} ta={ta} tb={tb}")
+
+
 @pytest.mark.parametrize("dt", FORMATS8)
 def test_fp8_tiny_sizes_integer_exact(handle, dt):
+    """Sizes 1..70 in every storage: under 16 along an outer-contiguous
+    operand the guarded kernel, else the edge or aligned ones."""
     rng = np.random.default_rng(67)
-    for case in range(30):
+    for case in range(48):
         M, N, K = (int(x) for x in rng.integers(1, 71, size=3))
+        ta, tb = STORAGES[case % 4]
         w = wl.Workload("tiny8", 3100 + case, M, N, K, 1.0, 1.0, "int4")
-        ops = wl.operands16(w, dt, tb=True)
+        ops = wl.operands16(w, dt, ta=ta, tb=tb)
         out = gu.run16(handle, ops)
-        gu.check_full16(ops, out, exact=True, what=f"tiny {dt} {M}x{N}x{K}")
+        gu.check_full16(ops, out, exact=True, what=f"tiny {dt} {M}x{N}x{K} {ta}{tb}")
 
 
 @pytest.mark.parametrize("dt", FORMATS8)
 def test_fp8_odd_offsets_and_k_cases(handle, dt):
     """A and B starting at odd byte addresses, odd leading dimensions, K one
     past a K step and K under one step."""
-    for (M, N, K) in ((300, 270, 129), (150, 133, 40), (256, 256, 256)):
+    for i, (M, N, K) in enumerate(((300, 270, 129), (150, 133, 40), (256, 256, 256),
+                                   (256, 512, 384))):
+        ta, tb = STORAGES[i % 4]
         w = wl.Workload("odd8", 79, M, N, K, 1.25, -0.5, "uniform")
-        ops = wl.operands16(w, dt, tb=True, lda=K + 3, ldb=K + 5, ldc=N + 1)
+        ops = wl.operands16(w, dt, ta=ta, tb=tb, lda=(M if ta else K) + 3,
+                            ldb=(K if tb else N) + 5, ldc=N + 1)
         A, B, C = gu.to_device16(ops)
         t8, u8 = A.dtype, torch.uint8
         A1 = torch.empty(A.numel() + 1, dtype=u8, device=A.device)
@@ -301,14 +325,18 @@ def test_fp8_odd_offsets_and_k_cases(handle, dt):
         gu.check_full16(ops, out, what=f"{dt} odd offsets {M}x{N}x{K}")
 
 
-def test_fp8_other_storages_unsupported(handle):
-    for ta, tb in ((False, False), (True, False), (True, True)):
-        ops = wl.operands16(W["c1_128_int"], "fp8e4m3", ta=ta, tb=tb)
-        A, B, C = gu.to_device16(ops)
-        with pytest.raises(sg.SgemmError) as e:
-            handle.gemm_lowp(A, B, C, 1.0, 0.0, M=ops.M, N=ops.N, K=ops.K, lda=ops.lda,
-                             ldb=ops.ldb, ldc=ops.ldc, transa=ta, transb=tb)
-        assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
+def test_fp8_storages_agree_bit_for_bit(handle):
+    """The same integer problem stored four ways gives the same bits (each
+    also matches the oracle exactly)."""
+    w = wl.Workload("agree8", 83, 384, 320, 640, 1.5, 0.5, "int4")
+    outs = []
+    for ta, tb in STORAGES:
+        ops = wl.operands16(w, "fp8e4m3", ta=ta, tb=tb)
+        out = gu.run16(handle, ops)
+        gu.check_full16(ops, out, exact=True, what=f"agree {ta}{tb}")
+        outs.append(gu.window(out, ops.M, ops.N, ops.ldc))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
 
 
 @pytest.mark.parametrize("dt", FORMATS8)
@@ -442,15 +470,18 @@ def _plan(h, ops):
 
 @pytest.mark.parametrize("k", SPLIT_K, ids=[k["name"] for k in SPLIT_K])
 def test_split_k_kernels(ws_handle, k):
-    """Every split-K kernel, forced, on few-row problems: one row, a ragged
-    row count, the most rows it takes; K ragged and long enough for several
+    """Every split-K kernel, forced, on few-row problems: one row (with A
+    stored K x M, the fewest rows the edge kernels take), a ragged row count,
+    the most rows it takes; K ragged and long enough for several
     ranges; odd leading dimensions; integers bit-exact, uniform values within
     the bound (the 8-bit envelope for 8-bit formats)."""
     ta, tb = bool(k["transa"]), bool(k["transb"])
     dt = DT_NAME[k["dtype"]]
     ws_handle.set_lowp_kernel(k["id"])
     try:
-        for M in ((8, 37, 64) if ta else (1, 5, 16, 64)):
+        # A stored K x M needs M of at least one 16-byte piece (8 or 16 rows)
+        piece = 16 if k["dtype"] in (sg.SGEMM_DTYPE_FP8_E4M3, sg.SGEMM_DTYPE_FP8_E5M2) else 8
+        for M in ((piece, 37, 64) if ta else (1, 5, 16, 64)):
             for dist in ("int4", "uniform"):
                 N, K = 300, 40 * k["bk"] + 19
                 w = wl.Workload("lpsk", 9400 + M, M, N, K, 1.5, 0.5, dist)

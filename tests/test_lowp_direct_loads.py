@@ -1,4 +1,4 @@
-"""CPU model of the 16-bit kernels' direct (global-to-LDS) loads: for every
+"""CPU model of the 16- and 8-bit kernels' direct (global-to-LDS) loads: for every
 tile, every 16-byte piece and every K step that the aligned and edge
 instances load without bounds checks -- including the look-ahead steps past
 the end of K, which the kernel clamps to the last direct-load step -- the
@@ -24,15 +24,19 @@ def elem_bytes(dtype):
     return 1 if dtype >= sg.SGEMM_DTYPE_FP8_E4M3 else 2
 
 
-def oc_swz(X, k):
-    return 4 * (k & 3) if X >= 128 else 4 * ((k >> 1) & 1)
+def oc_swz(X, k, UE=8):
+    """Unit swizzle of an outer-contiguous tile X elements wide (lp_oc_swz for
+    16-bit elements, lp_oc_swz8 for 8-bit ones)."""
+    if UE == 8:
+        return 4 * (k & 3) if X >= 128 else 4 * ((k >> 1) & 1)
+    return 2 * {256: k & 7, 128: (k >> 1) & 3, 64: (k >> 2) & 1}[X]
 
 
-def direct_steps(edge, M, N, K, ta, tb, BK):
+def direct_steps(edge, M, N, K, ta, tb, BK, UE=8):
     """K steps the direct loads cover (the kernel's kd)."""
     if not edge:
         return K // BK
-    straddle = (ta and M % 8) or (not tb and N % 8)
+    straddle = (ta and M % UE) or (not tb and N % UE)
     return (K - 1) // BK if straddle else K // BK
 
 
@@ -47,13 +51,12 @@ def piece_offsets(kcontig, X, extent, origin, ld, edge, BK, UE):
         if edge:
             r = np.where(origin + r >= extent, extent - 1 - origin, r)
         return r * ld + UE * c
-    assert UE == 8, "outer-contiguous tiles are 16-bit only"
-    k = u // (X // 8)                 # outer-contiguous: row k, unit swizzled by k
-    c = (u % (X // 8)) ^ np.array([oc_swz(X, int(x)) for x in k])
-    o = 8 * c
+    k = u // (X // UE)                # outer-contiguous: row k, unit swizzled by k
+    c = (u % (X // UE)) ^ np.array([oc_swz(X, int(x), UE) for x in k])
+    o = UE * c
     if edge:
         past = origin + o >= extent
-        o = np.where(past, extent - 8 - origin if extent - 8 > origin else 0, o)
+        o = np.where(past, extent - UE - origin if extent - UE > origin else 0, o)
     return k * ld + o
 
 
@@ -77,7 +80,7 @@ def operand_reads(kcontig, X, extent, K, ld, steps, edge, BK=64, UE=8):
 
 CASES = [(4096, 4096, 4096), (1000, 1500, 777), (150, 133, 192), (152, 136, 192),
          (150, 133, 40), (150, 133, 129), (64, 64, 64), (8, 9, 65), (300, 8, 128),
-         (257, 255, 1000)]
+         (257, 255, 1000), (16, 300, 256), (300, 16, 384), (136, 264, 256)]
 
 
 @pytest.mark.parametrize("k", DIRECT, ids=[k["name"] for k in DIRECT])
@@ -89,12 +92,12 @@ def test_direct_loads_stay_inside_the_operands(k):
     for (M, N, K) in CASES:
         if not edge and (M % k["bm"] or N % k["bn"] or K % BK):
             continue
-        if edge and ((ta and M < 8) or (not tb and N < 8)):
+        if edge and ((ta and M < UE) or (not tb and N < UE)):
             continue
         for pad in (0, 1, 7):
             lda = (M if ta else K) + pad
             ldb = (K if tb else N) + pad
-            kd = direct_steps(edge, M, N, K, ta, tb, BK)
+            kd = direct_steps(edge, M, N, K, ta, tb, BK, UE)
             a_rows, a_cols = (K, M) if ta else (M, K)
             b_rows, b_cols = (N, K) if tb else (K, N)
             a_lo, a_hi = operand_reads(not ta, k["bm"], M, K, lda, kd, edge, BK, UE)
@@ -111,4 +114,16 @@ def test_straddle_rule_is_needed():
     ldb = N
     with pytest.raises(AssertionError):
         lo, hi = operand_reads(False, 64, N, K, ldb, K // 64, True)
+        assert hi <= (K - 1) * ldb + N - 1
+
+
+def test_straddle_rule_is_needed_for_8bit_pieces():
+    """An 8-bit piece is 16 elements: N = 136 is a multiple of 8 but not of
+    16, so the rule must leave the last K row out there too (the model
+    catches the read past the end of B without it)."""
+    M, N, K = 150, 136, 256
+    ldb = N
+    assert direct_steps(True, M, N, K, False, False, 128, 16) == (K - 1) // 128
+    with pytest.raises(AssertionError):
+        lo, hi = operand_reads(False, 128, N, K, ldb, K // 128, True, 128, 16)
         assert hi <= (K - 1) * ldb + N - 1
