@@ -153,7 +153,9 @@ struct LpTile {
   static_assert(B_VEC >= 1 && B_VEC * THREADS == BN * 8, "B loader");
   static_assert(BM % 64 == 0 && BN % 64 == 0, "transposing loader regions");
   static_assert(A_TW <= WAVES && B_TW <= WAVES, "transposing loader waves");
-  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
+  // the stages plus the 1 KB that look-ahead loads past the end land in
+  static constexpr int LDS_ALIGNED = LDS_BYTES + 1024;
+  static_assert(LDS_ALIGNED <= 160 * 1024, "gfx950 LDS");
   static_assert(S >= 2, "stages");
   static_assert((S - 1) * (A_VEC + B_VEC) <= 63, "vmcnt range");
 };
@@ -441,13 +443,21 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   // then the B units, whatever their storage).
   constexpr int ND_A = T::A_VEC;
   constexpr int ND = T::A_VEC + T::B_VEC;
-  auto direct_one = [&](int kt, int st, int d) {
+  // Look-ahead loads past the last direct-load step repeat that step (in
+  // bounds, so that the loop's slots carry no branches); `live` false sends
+  // them to a scratch KB past the stages that nothing reads, so the stages
+  // are free for the epilogue once the loop's last barrier has passed.
+  const unsigned lds_dummy = lds_u + (unsigned)T::LDS_BYTES;
+  auto direct_one = [&](int kt, int st, int d, bool live) {
     if (d < ND_A)
       dma16(reinterpret_cast<const float*>(a_dbase + (size_t)kt * a_dstep), a_voff[d],
-            lds_u + (unsigned)a_off(st) + 1024u * (unsigned)(d * T::WAVES + wave_u));
+            live ? lds_u + (unsigned)a_off(st) + 1024u * (unsigned)(d * T::WAVES + wave_u)
+                 : lds_dummy);
     else
       dma16(reinterpret_cast<const float*>(b_dbase + (size_t)kt * b_dstep), b_voff[d - ND_A],
-            lds_u + (unsigned)b_off(st) + 1024u * (unsigned)((d - ND_A) * T::WAVES + wave_u));
+            live ? lds_u + (unsigned)b_off(st) +
+                       1024u * (unsigned)((d - ND_A) * T::WAVES + wave_u)
+                 : lds_dummy);
   };
 
   // Output row e of a block (its outer index 8ob + e, eight k) from the eight
@@ -694,9 +704,9 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     // (4096^3 bfloat16: 124 -> 114 us).  A barrier before group 1, with the
     // loads over three groups, measured no better: the last loads then have
     // a quarter step to land instead of half a step.
-    auto issue_step = [&](int kt, int st) {
+    auto issue_step = [&](int kt, int st, bool live) {
 #pragma unroll
-      for (int o = 0; o < ND; ++o) direct_one(kt, st, o);
+      for (int o = 0; o < ND; ++o) direct_one(kt, st, o, live);
     };
     // Group q of step kt (stage st) on fragments cur; fills the slots as
     // described.  kl = step kt+S clamped to the last step: past the end of K
@@ -714,7 +724,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     }
     constexpr int H = QG / 2;  // groups the reads run ahead (the barrier precedes group H)
     Frag fr[QG];
-    auto group = [&](int kl, auto st_c, auto q_c) {
+    auto group = [&](int kl, bool live, auto st_c, auto q_c) {
       constexpr int st = decltype(st_c)::value, q = decltype(q_c)::value;
       constexpr int st1 = st + 1 == S ? 0 : st + 1;
       // the group read in this one's slots, and the stage it comes from
@@ -730,7 +740,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
           constexpr int SLOTS = (QG - H) * SL;
 #pragma unroll
           for (int o = 0; o < ND; ++o)
-            if (o * SLOTS / ND == (q - H) * SL + m) direct_one(kl, st, o);
+            if (o * SLOTS / ND == (q - H) * SL + m) direct_one(kl, st, o, live);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -740,14 +750,15 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
     constexpr int AHEAD = (S - 2) * ND;
     constexpr int WAIT_AHEAD = 0x0F70 | (AHEAD & 15) | ((AHEAD >> 4) << 14);
     auto step = [&](int kt, auto st_c) {
-      const int kl = kt + S < kd ? kt + S : kd - 1;
-      lp_static_for<H>([&](auto q_c) { group(kl, st_c, q_c); });
+      const bool live = kt + S < kd;
+      const int kl = live ? kt + S : kd - 1;
+      lp_static_for<H>([&](auto q_c) { group(kl, live, st_c, q_c); });
       wait_lds();
       __builtin_amdgcn_s_waitcnt(WAIT_AHEAD);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       lp_static_for<QG - H>([&](auto i) {
-        group(kl, st_c, std::integral_constant<int, H + decltype(i)::value>{});
+        group(kl, live, st_c, std::integral_constant<int, H + decltype(i)::value>{});
       });
     };
     if (!EDGE || kd > 0) {  // (aligned kernels run with K >= 64)
@@ -755,7 +766,7 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       // first barrier.
       lp_static_for<S>([&](auto i) {
         constexpr int st = decltype(i)::value;
-        issue_step(st < kd ? st : kd - 1, st);
+        issue_step(st < kd ? st : kd - 1, st, st < kd);
       });
       constexpr int FIRST = (S - 1) * ND;
       __builtin_amdgcn_s_waitcnt(0x0F70 | (FIRST & 15) | ((FIRST >> 4) << 14));
@@ -797,12 +808,102 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
   }
 }
 
+// Epilogue through LDS, for tiles whose wave tiles are at least 64 columns
+// wide: a store of the MFMA register layout writes 32 rows x 32 bytes, one
+// piece of every 128-byte line it touches, and the lines' other pieces come
+// in three more instructions.  Here each wave stages one 32-row block row of
+// its tile at a time in LDS (rows padded by 16 bytes) and reads it back row
+// by row, so every C read and write of a wave instruction covers whole rows
+// of the wave tile (WN floats), i.e. whole lines.  Rows past M and columns
+// past N are skipped (edge tiles), and C that is not 16-byte aligned or
+// whose ldc is not a multiple of 4 takes element accesses.  Measured at
+// 4096 x 4096 with one K step (256x256 tiles): 27.1 us with beta 0.5 and
+// 16.6 us with beta 0, against 28.4 and 20.0 us through the register layout
+// (a plain device copy of the same 128 MB takes 19.6 us, a fill of the 64 MB
+// 11.2 us); 4096^3: bfloat16 114 -> 113 us, E4M3 66.8 -> 64.2 us.
+template <class T>
+__device__ __forceinline__ void lp_store_tile_lds(const GemmArgs& g, int m0, int n0,
+                                                  const f32x16 (&acc)[T::FM][T::FN],
+                                                  char* lds) {
+  constexpr int WN = T::WN, LD = WN + 4;  // LDS row: the wave tile's row + 16 bytes
+  constexpr int LPR = WN / 4;             // lanes per row, 16 bytes each
+  constexpr int RPI = 64 / LPR;           // rows per wave instruction
+  constexpr int NI = 32 / RPI;            // instructions per 32-row block row
+  static_assert(WN % 64 == 0 && T::WAVES * 32 * LD * 4 <= T::LDS_BYTES, "staging area");
+  const WaveCoords<T> w;
+  float* reg = reinterpret_cast<float*>(lds) + w.wave * 32 * LD;
+  const float alpha = g.alpha, beta = g.beta;
+  const int M = g.M, N = g.N, ldc = g.ldc;
+  const int rr = w.lane / LPR, cc = 4 * (w.lane % LPR);
+  const int col = n0 + w.wn * WN + cc;  // the lane's first column
+  const bool vec = c_vector(g) && col + 3 < N;
+  const size_t rstep = (size_t)RPI * ldc;  // rows between a lane's accesses
+  __syncthreads();  // every wave is done reading the stages
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const int row0 = m0 + w.wm * T::WM + 32 * i + rr;  // the lane's first row
+    float* p = g.C + (size_t)row0 * ldc + col;
+    f32x4 cin[NI];
+    if (beta != 0.0f) {
+#pragma unroll
+      for (int t = 0; t < NI; ++t) {
+        cin[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (row0 + t * RPI < M) {
+          if (vec) {
+            cin[t] = *reinterpret_cast<const f32x4*>(p + t * rstep);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < N) cin[t][e] = p[t * rstep + e];
+          }
+        }
+      }
+    }
+    // block (i, j), register 4q + e of lane (li, lh): row li, column
+    // 32j + 8q + 4lh + e of the block row
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(reg + w.li * LD + 32 * j + 8 * q + 4 * w.lh) =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                  acc[i][j][4 * q + 3]};
+    // the wave reads back its own writes: one wave's LDS operations complete
+    // in issue order
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(reg + (t * RPI + rr) * LD + cc);
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = alpha * v[e];
+        if (beta != 0.0f) o[e] = fmaf(beta, cin[t][e], o[e]);
+      }
+      if (row0 + t * RPI < M) {
+        if (vec) {
+          *reinterpret_cast<f32x4*>(p + t * rstep) = o;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < N) p[t * rstep + e] = o[e];
+        }
+      }
+    }
+    // one block row's C traffic at a time (reading the next block row's C
+    // before this one's stores measured slower: 4096^2 with one K step and
+    // beta 0.5, 32.5 against 27.1 us)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <class T, int DT, int MODE, bool TA, bool TB>
 __global__ void __launch_bounds__(T::THREADS, T::OCC)
     lp_gemm_kernel(LpArgs g, int tiles_m, int tiles_n, int band) {
   // guarded kernels use two stages
   __shared__ __attribute__((aligned(1024)))
-  char lds[MODE == MODE_GUARDED ? 2 * (T::A_BYTES + T::B_BYTES) : T::LDS_BYTES];
+  char lds[MODE == MODE_GUARDED ? 2 * (T::A_BYTES + T::B_BYTES) : T::LDS_ALIGNED];
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, band, tm, tn);
   f32x16 acc[T::FM][T::FN];
@@ -820,7 +921,11 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   e.ldb = 0;
   e.C = g.C;
   e.ldc = g.ldc;
-  store_tile<T, MODE>(e, tm * T::BM, tn * T::BN, acc, acc);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+  if constexpr (MODE != MODE_GUARDED && T::WN >= 64)
+    lp_store_tile_lds<T>(e, m0, n0, acc, lds);
+  else
+    store_tile<T, MODE>(e, m0, n0, acc, acc);
   // The K loop's last steps issue look-ahead loads into LDS that nothing
   // waits for: they must land before the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -840,7 +945,7 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
     lp_splitk_kernel(LpArgs g, int tiles_m, int tiles_n, int kps,
                      float* __restrict__ ws) {
   __shared__ __attribute__((aligned(1024)))
-  char lds[MODE == MODE_GUARDED ? 2 * (T::A_BYTES + T::B_BYTES) : T::LDS_BYTES];
+  char lds[MODE == MODE_GUARDED ? 2 * (T::A_BYTES + T::B_BYTES) : T::LDS_ALIGNED];
   typedef typename LpFmt<DT>::E E;
   const int tiles = tiles_m * tiles_n;
   const int split = blockIdx.x / tiles, tile = blockIdx.x - split * tiles;
