@@ -710,6 +710,99 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int m0, int n0,
     }
 }
 
+// The same epilogue staged through LDS, one 32x32 block per wave at a time
+// (the stages are free; the caller has passed a barrier after the last LDS
+// read): a store of the MFMA register layout writes 32 rows x 32 bytes, one
+// piece of each 128-byte line it touches, and the lines' other pieces come
+// in three more instructions.  Staged (rows padded by 16 bytes) and read
+// back row by row, each wave instruction reads or writes eight whole rows of
+// the block, i.e. eight whole lines.  Rows past M and columns past N are
+// skipped; C that is not 16-byte aligned, or whose ldc is not a multiple of
+// 4, takes element accesses.  With HAVE_C, cv holds C in the register
+// layout (read before the K loop) and the update is applied before staging.
+template <class T, int MODE, bool HAVE_C = false>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& g, int m0, int n0,
+                                               const f32x16 (&acc)[T::FM][T::FN],
+                                               const f32x16 (&cv)[T::FM][T::FN],
+                                               float* lds) {
+  constexpr int LD = 36;  // a staged row: 32 floats + 16 bytes
+  static_assert(T::WAVES_MN * 32 * LD * 4 <= TileLds<T, MODE>::FLOATS * 4, "staging area");
+  const WaveCoords<T> w;
+  float* reg = lds + w.wmn * 32 * LD;
+  const int M = g.M, N = g.N, ldc = g.ldc;
+  const float alpha = g.alpha, beta = g.beta;
+  const int rr = w.lane >> 3, cc = 4 * (w.lane & 7);  // row (of 8) and column read back
+  const bool c_vec = c_vector(g);
+  const size_t rstep = (size_t)8 * ldc;  // rows between a lane's accesses
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int row0 = m0 + w.wm * T::WM + i * 32 + rr;  // the lane's first row
+      const int col = n0 + w.wn * T::WN + j * 32 + cc;
+      const bool vec = c_vec && col + 3 < N;
+      float* p = g.C + (size_t)row0 * ldc + col;
+      f32x4 cin[4];
+      if (!HAVE_C && beta != 0.0f) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          cin[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if (row0 + 8 * t < M) {
+            if (vec) {
+              cin[t] = *reinterpret_cast<const f32x4*>(p + t * rstep);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < N) cin[t][e] = p[t * rstep + e];
+            }
+          }
+        }
+      }
+      // register 4q + e of lane (li, lh): row li, column 8q + 4lh + e
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * q + e];
+          if (HAVE_C) {
+            v[e] *= alpha;
+            if (beta != 0.0f) v[e] = fmaf(beta, cv[i][j][4 * q + e], v[e]);
+          }
+        }
+        *reinterpret_cast<f32x4*>(reg + w.li * LD + 8 * q + 4 * w.lh) = v;
+      }
+      // the wave reads back its own writes: one wave's LDS operations
+      // complete in issue order
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(reg + (8 * t + rr) * LD + cc);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = v[e];
+          if (!HAVE_C) {
+            o[e] *= alpha;
+            if (beta != 0.0f) o[e] = fmaf(beta, cin[t][e], o[e]);
+          }
+        }
+        if (row0 + 8 * t < M) {
+          if (vec) {
+            *reinterpret_cast<f32x4*>(p + t * rstep) = o;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (col + e < N) p[t * rstep + e] = o[e];
+          }
+        }
+      }
+      // one block's C traffic at a time
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <class T>
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[T::FM][T::FN]) {
 #pragma unroll
@@ -751,8 +844,9 @@ __global__ void __launch_bounds__(T::THREADS, T::OCC)
   f32x16 cv[T::FM][T::FN];
   tile_accumulate<T, MODE, TA, TB, LOADC>(g, lds, tm * T::BM, tn * T::BN, 0,
                                           tile_k_steps<T>(g.K), acc, cv);
+  __syncthreads();  // every wave is done with the LDS (stages, K-group sums)
   if (threadIdx.x / 64 / T::WAVES_MN == 0)
-    store_tile<T, MODE, LOADC>(g, tm * T::BM, tn * T::BN, acc, cv);
+    store_tile_lds<T, MODE, LOADC>(g, tm * T::BM, tn * T::BN, acc, cv, lds);
   if (stamps != nullptr) {
     __syncthreads();
     if (threadIdx.x == 0) clock_stamp(stamps + 4 * blockIdx.x + 1);
