@@ -714,9 +714,12 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, int m0, int n0,
 // (the stages are free; the caller has passed a barrier after the last LDS
 // read): a store of the MFMA register layout writes 32 rows x 32 bytes, one
 // piece of each 128-byte line it touches, and the lines' other pieces come
-// in three more instructions.  Staged (rows padded by 16 bytes) and read
-// back row by row, each wave instruction reads or writes eight whole rows of
-// the block, i.e. eight whole lines.  Rows past M and columns past N are
+// in three more instructions.  Staged and read back row by row, each wave
+// instruction reads or writes eight whole rows of the block, i.e. eight
+// whole lines.  A staged row is 32 floats, eight 16-byte units, unit u of
+// row r at u ^ (r / 2 % 8): the register layout's writes (16 rows of one
+// unit per 16 lanes) and the row reads (two rows of eight units per 16
+// lanes) then both fall on 16 distinct bank groups.  Rows past M and columns past N are
 // skipped; C that is not 16-byte aligned, or whose ldc is not a multiple of
 // 4, takes element accesses.  With HAVE_C, cv holds C in the register
 // layout (read before the K loop) and the update is applied before staging.
@@ -725,7 +728,7 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, int m0, int n0
                                                const f32x16 (&acc)[T::FM][T::FN],
                                                const f32x16 (&cv)[T::FM][T::FN],
                                                float* lds) {
-  constexpr int LD = 36;  // a staged row: 32 floats + 16 bytes
+  constexpr int LD = 32;  // a staged row
   static_assert(T::WAVES_MN * 32 * LD * 4 <= TileLds<T, MODE>::FLOATS * 4, "staging area");
   const WaveCoords<T> w;
   float* reg = lds + w.wmn * 32 * LD;
@@ -733,6 +736,13 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, int m0, int n0
   const float alpha = g.alpha, beta = g.beta;
   const int rr = w.lane >> 3, cc = 4 * (w.lane & 7);  // row (of 8) and column read back
   const bool c_vec = c_vector(g);
+  // the swizzle folded into per-lane constants: the lane writes unit
+  // (2q + lh) ^ (li/2 % 8) = 2q ^ xw of row li and reads unit
+  // (cc/4) ^ ((8t + rr)/2 % 8) = xr ^ 4(t % 2) of row 8t + rr
+  float* const wrow = reg + w.li * LD;
+  float* const rrow = reg + rr * LD;
+  const int xw = w.lh ^ ((w.li >> 1) & 7);
+  const int xr = (cc >> 2) ^ (rr >> 1);
   const size_t rstep = (size_t)8 * ldc;  // rows between a lane's accesses
 #pragma unroll
   for (int i = 0; i < T::FM; ++i)
@@ -770,14 +780,15 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& g, int m0, int n0
             if (beta != 0.0f) v[e] = fmaf(beta, cv[i][j][4 * q + e], v[e]);
           }
         }
-        *reinterpret_cast<f32x4*>(reg + w.li * LD + 8 * q + 4 * w.lh) = v;
+        *reinterpret_cast<f32x4*>(wrow + 4 * ((2 * q) ^ xw)) = v;
       }
       // the wave reads back its own writes: one wave's LDS operations
       // complete in issue order
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(reg + (8 * t + rr) * LD + cc);
+        const f32x4 v =
+            *reinterpret_cast<const f32x4*>(rrow + 8 * t * LD + 4 * (xr ^ (4 * (t & 1))));
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
