@@ -19,6 +19,7 @@
 
 #include "diag.hpp"
 #include "lowp_gemm.hpp"
+#include "lowp_gemv.hpp"
 #include "mfma_sgemm.hpp"
 #include "skinny_sgemm.hpp"
 #include "tile_map.hpp"
@@ -769,7 +770,8 @@ struct LpKernelDesc {
   int bm, bn, bk;
   int threads;
   int mode;      // SGEMM_MODE_*
-  int schedule;  // SGEMM_SCHEDULE_TILES, or SGEMM_SCHEDULE_SMALL_M (split K)
+  int schedule;  // SGEMM_SCHEDULE_TILES, or SGEMM_SCHEDULE_SMALL_M
+  int split;     // small M: K split over workgroups (needs the workspace)
   lp_launch_fn launch;
 };
 
@@ -816,6 +818,14 @@ hipError_t launch_lp_splitk(const LpRun& a, int tiles_m, int tiles_n,
   return hipGetLastError();
 }
 
+template <int DT, bool TA>
+hipError_t launch_lp_gemv(const LpRun& a, int, int tiles_n, const LpSplit&,
+                          hipStream_t s) {
+  hipLaunchKernelGGL((lp_gemv_kernel<DT, TA>), dim3(tiles_n), dim3(LPV_THREADS), 0, s,
+                     lp_args(a));
+  return hipGetLastError();
+}
+
 template <class T, int DT, int MODE, bool TA, bool TB>
 hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, const LpSplit&,
                      hipStream_t s) {
@@ -840,13 +850,19 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, const LpSplit&,
 
 #define LP_ONE(T, DT, DTAG, STAG, TA, TB, MODE, MTAG)                        \
   {"lp_" DTAG "_" #T "_" STAG MTAG, DT, TA, TB, T::BM, T::BN,                \
-   LpFmt<DT>::BKE, T::THREADS, MODE, SGEMM_SCHEDULE_TILES,                   \
+   LpFmt<DT>::BKE, T::THREADS, MODE, SGEMM_SCHEDULE_TILES, 0,                \
    launch_lp<T, DT, MODE, TA, TB>}
 // Split-K instances for products with few rows (edge mode only).
 #define LP_SK(T, DT, DTAG, STAG, TA, TB)                                      \
   {"lp_" DTAG "_" #T "_" STAG "sk_edge", DT, TA, TB, T::BM, T::BN,           \
-   LpFmt<DT>::BKE, T::THREADS, SGEMM_MODE_EDGE, SGEMM_SCHEDULE_SMALL_M,       \
+   LpFmt<DT>::BKE, T::THREADS, SGEMM_MODE_EDGE, SGEMM_SCHEDULE_SMALL_M, 1,    \
    launch_lp_splitk<T, DT, SGEMM_MODE_EDGE, TA, TB>}
+// One-pass matrix-core kernels for at most 16 rows of A against B stored
+// N x K (A in either storage): 16 columns per workgroup, all of K.
+#define LP_GEMV(DT, DTAG, STAG, TA)                                          \
+  {"lp_" DTAG "_G16x16_" STAG "small", DT, TA, true, LPV_MT, LPV_COLS,      \
+   LpvFmt<DT>::KB, LPV_THREADS, SGEMM_MODE_EDGE, SGEMM_SCHEDULE_SMALL_M, 0,  \
+   launch_lp_gemv<DT, TA>}
 #define LP_SK_STORAGE(T, DT, DTAG)                                           \
   LP_SK(T, DT, DTAG, "", false, false), LP_SK(T, DT, DTAG, "tn_", true, false), \
   LP_SK(T, DT, DTAG, "nt_", false, true), LP_SK(T, DT, DTAG, "tt_", true, true)
@@ -868,7 +884,8 @@ hipError_t launch_lp(const LpRun& a, int tiles_m, int tiles_n, const LpSplit&,
   LP_STORAGE(L128x128, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                   \
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_EDGE, "edge"),                     \
   LP_STORAGE(L64x64, DT, DTAG, SGEMM_MODE_GUARDED, "guarded"),               \
-  LP_SK_STORAGE(L64x64, DT, DTAG)
+  LP_SK_STORAGE(L64x64, DT, DTAG),                                           \
+  LP_GEMV(DT, DTAG, "nt_", false), LP_GEMV(DT, DTAG, "tt_", true)
 
 const LpKernelDesc kLpKernels[] = {
     LP_FORMAT(SGEMM_DTYPE_BF16, "bf16"),
@@ -897,6 +914,9 @@ bool lp_offsets_fit(const LpKernelDesc& k, const LpRun& a) {
 bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
   if (k.dt != a.dt || k.ta != a.ta || k.tb != a.tb) return false;
   if (k.schedule == SGEMM_SCHEDULE_SMALL_M && a.M > k.bm) return false;
+  // the one-pass small-M kernels take any K and any alignment, one launch
+  // of ceil(N / bn) workgroups
+  if (k.schedule == SGEMM_SCHEDULE_SMALL_M && !k.split) return a.N <= INT_MAX - k.bn;
   if (ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn) > INT_MAX) return false;
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:
@@ -971,10 +991,13 @@ int lp_splits(const LpKernelDesc& k, const LpRun& a, int cus, size_t ws_bytes,
   return (int)ceil_div(a.K, *kps);
 }
 
-// The launch sgemm_run_lowp makes on a handle: the forced kernel, or the
-// split-K kernel when it splits K (a workspace, few rows, few tiles), else
-// lp_select's.  *splits receives the split count (1 for one-tile-per-
-// workgroup kernels).  Returns the kernel id or a negative status.
+// The launch sgemm_run_lowp makes on a handle: the forced kernel; else the
+// one-pass small-M kernel when it fits (at most 16 rows of A, B stored N x K:
+// a stream of B with no second pass, workspace or LDS tiles) and 64x64 tiles
+// would fill at most half the CUs; else
+// the split-K kernel when it splits K (a workspace, few rows, few tiles);
+// else lp_select's.  *splits receives the split count (1 for kernels that do
+// not split K).  Returns the kernel id or a negative status.
 int lp_plan(const LpRun& a, int forced, int cus, float* ws, size_t ws_bytes,
             int* splits, int* kps) {
   *splits = 1;
@@ -982,7 +1005,7 @@ int lp_plan(const LpRun& a, int forced, int cus, float* ws, size_t ws_bytes,
   if (forced >= 0) {
     const LpKernelDesc& k = kLpKernels[forced];
     if (!lp_fits(k, a)) return SGEMM_ERR_UNSUPPORTED;
-    if (k.schedule == SGEMM_SCHEDULE_SMALL_M) {
+    if (k.split) {
       if (ws == nullptr) return SGEMM_ERR_UNSUPPORTED;
       *splits = lp_splits(k, a, cus, ws_bytes, kps);
       if (*splits < 2) {  // runs as one range: still needs one partial set
@@ -994,10 +1017,17 @@ int lp_plan(const LpRun& a, int forced, int cus, float* ws, size_t ws_bytes,
     }
     return forced;
   }
+  // (with more tiles one tile per workgroup streams B faster: 4 x 11008 x
+  // 4096 E4M3 in 9.2 us against 13.6 one-pass)
+  if (2 * ceil_div(a.M, 64) * ceil_div(a.N, 64) <= cus)
+    for (int id = 0; id < kNumLpKernels; ++id) {
+      const LpKernelDesc& k = kLpKernels[id];
+      if (k.schedule == SGEMM_SCHEDULE_SMALL_M && !k.split && lp_fits(k, a)) return id;
+    }
   if (ws != nullptr) {
     for (int id = 0; id < kNumLpKernels; ++id) {
       const LpKernelDesc& k = kLpKernels[id];
-      if (k.schedule != SGEMM_SCHEDULE_SMALL_M || !lp_fits(k, a)) continue;
+      if (!k.split || !lp_fits(k, a)) continue;
       const int n = lp_splits(k, a, cus, ws_bytes, kps);
       if (n >= 2) {
         *splits = n;
@@ -1396,8 +1426,8 @@ int sgemm_lowp_select_kernel(int dtype, int transa, int transb, int M, int N,
   if (st != SGEMM_OK) return st;
   const LpRun a = {dtype, transa, transb, M, N, K, 1.0f, 0.0f, A, lda, B, ldb,
                    const_cast<float*>(C), ldc};
-  const int id = lp_select(a, kChipCus);
-  return id >= 0 ? id : SGEMM_ERR_UNSUPPORTED;
+  int splits = 1, kps = K;
+  return lp_plan(a, -1, kChipCus, nullptr, 0, &splits, &kps);
 }
 
 int sgemm_set_lowp_kernel(sgemm_handle_t h, int kernel_id) {

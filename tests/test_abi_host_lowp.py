@@ -61,12 +61,26 @@ def test_kernel_table():
                 for bm in (64, 128):
                     assert (dt, ta, tb, bm, sg.SGEMM_MODE_EDGE) in combos
                 assert (dt, ta, tb, 64, sg.SGEMM_MODE_GUARDED) in combos
+    gemv = [k for k in t if "_G16x16_" in k["name"]]
     for k in t:
-        assert k["bk"] == (128 if k["dtype"] >= E4M3 else 64)
-        assert k["threads"] == 256 and k["bm"] == k["bn"]
         assert ("bf16" in k["name"]) == (k["dtype"] == BF16)
         tag = {(0, 0): "", (1, 0): "tn_", (0, 1): "nt_", (1, 1): "tt_"}[(k["transa"], k["transb"])]
         assert f"x{k['bn']}_{tag}" in k["name"]
+        if k in gemv:
+            continue
+        assert k["threads"] == 256
+        assert k["bk"] == (128 if k["dtype"] >= E4M3 else 64)
+        assert k["bm"] == k["bn"]
+    # the one-pass small-M kernels: every format, A in either storage, B
+    # stored N x K; 16 rows of A and 16 columns per workgroup of 8 waves, K
+    # in blocks of one 16 x 16 MFMA (32 k of a 16-bit format, 128 of an 8-bit
+    # one)
+    assert sorted((k["dtype"], k["transa"]) for k in gemv) == sorted(
+        (dt, ta) for dt in (BF16, F16, E4M3, E5M2) for ta in (0, 1))
+    for k in gemv:
+        assert k["transb"] == 1 and (k["bm"], k["bn"], k["threads"]) == (16, 16, 512)
+        assert k["bk"] == (128 if k["dtype"] >= E4M3 else 32)
+        assert k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M and k["name"].endswith("_small")
     assert sg.sgemm_lowp_kernel_name(-1) is None
     assert sg.sgemm_lowp_kernel_name(len(t)) is None
     with pytest.raises(sg.SgemmError):
@@ -117,9 +131,12 @@ def test_select(dt, ta, tb):
     k = _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 2, ta=ta, tb=tb)
     assert k["mode"] == A
     assert _pick(dt, 4096, 4096, 4096, A=(1 << 20) + 1) == sg.SGEMM_ERR_VALUE
-    # an extent under 8 along an outer-contiguous operand's pieces
+    # an extent under 8 along an outer-contiguous operand's pieces (seven
+    # rows of A with B stored N x K: the one-pass small-M kernel instead)
     k = _pick(dt, 7 if ta else 300, 300 if ta else (300 if tb else 7), 100, ta=ta, tb=tb)
-    if ta or not tb:
+    if ta and tb:
+        assert "_G16x16_" in k["name"]
+    elif ta or not tb:
         assert (k["bm"], k["mode"]) == (64, G)
     else:
         assert k["mode"] == E
@@ -160,8 +177,25 @@ def test_select_fp8(dt):
     # K x N go to the guarded kernel, 16 to the edge one
     assert _pick(dt, 300, 15, 200)["mode"] == sg.SGEMM_MODE_GUARDED
     assert _pick(dt, 300, 16, 200)["mode"] == E
-    assert _pick(dt, 15, 300, 200, ta=1, tb=1)["mode"] == sg.SGEMM_MODE_GUARDED
-    assert _pick(dt, 16, 300, 200, ta=1, tb=1)["mode"] == E
+    assert _pick(dt, 15, 300, 200, ta=1)["mode"] == sg.SGEMM_MODE_GUARDED
+    assert _pick(dt, 16, 300, 200, ta=1)["mode"] == E
+    assert _pick(dt, 17, 300, 200, ta=1, tb=1)["mode"] == E
+
+
+@pytest.mark.parametrize("dt", [BF16, F16, E4M3, E5M2])
+@pytest.mark.parametrize("ta", [0, 1])
+def test_select_small_m_one_pass(dt, ta):
+    """At most 16 rows of A against B stored N x K, with 64x64 tiles for at
+    most half the CUs: the one-pass matrix-core kernel, also without a
+    workspace; not with 17 rows, with B stored K x N, or with 172 tiles."""
+    for M, N, K in ((1, 4096, 4096), (16, 4096, 4096), (3, 300, 5), (1, 8192, 1000)):
+        k = _pick(dt, M, N, K, ta=ta, tb=1)
+        assert "_G16x16_" in k["name"] and k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M
+        assert (k["dtype"], k["transa"], k["transb"]) == (dt, ta, 1)
+    for M, N, K, tb in ((17, 4096, 4096, 1), (1, 4096, 4096, 0), (4, 11008, 4096, 1),
+                        (1, 8256, 4096, 1)):
+        k = _pick(dt, M, N, K, ta=ta, tb=tb)
+        assert k["schedule"] == sg.SGEMM_SCHEDULE_TILES, (M, N, K, tb, k["name"])
 
 
 def test_diag_chain_argument_errors():

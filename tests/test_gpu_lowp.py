@@ -49,7 +49,10 @@ def _auto_kernel(handle):
 ALL_KERNELS = [] if not __import__("os").path.exists(sg.LIBRARY) else sg.lowp_kernel_table()
 # one-tile-per-workgroup kernels (the split-K ones need a workspace: below)
 KERNELS = [k for k in ALL_KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_TILES]
-SPLIT_K = [k for k in ALL_KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
+SPLIT_K = [k for k in ALL_KERNELS if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M
+           and "_sk_" in k["name"]]
+# one-pass matrix-core kernels for at most 16 rows of A, B stored N x K
+GEMV = [k for k in ALL_KERNELS if "_G16x16_" in k["name"]]
 DT_NAME = {sg.SGEMM_DTYPE_BF16: "bf16", sg.SGEMM_DTYPE_F16: "f16",
            sg.SGEMM_DTYPE_FP8_E4M3: "fp8e4m3", sg.SGEMM_DTYPE_FP8_E5M2: "fp8e5m2"}
 FORMATS8 = wl.FORMATS8
@@ -391,11 +394,18 @@ def test_fp8_envelope_measurement(handle, dt):
     """The measurement behind the 8-bit envelope: the worst error of the 8-bit
     product in units of |alpha| * ceil(K/64) * max|a_i.| * max|b_.j| over
     uniform, one-signed, small-normal and seven-binade inputs, K = 64, 128,
-    1000 and 4096.  Printed as a power of two; the allowance is 2^-9."""
-    worst, where = 0.0, None
+    1000 and 4096, for the tile kernels (128 rows: the 32x32x64 instruction)
+    and the one-pass small-M kernel (16 rows: the 16x16x128 instruction).
+    Printed as a power of two; the allowance is 2^-9."""
+    for M in (128, 16):
+        _fp8_envelope(handle, dt, M)
+
+
+def _fp8_envelope(handle, dt, M):
+    worst, where, kernel = 0.0, None, None
     for K in (64, 128, 1000, 4096):
-        rng = np.random.default_rng([73, K])
-        M, N = 128, 96
+        rng = np.random.default_rng([73, K, M])
+        N = 96
         for kind in ("wide", "positive", "uniform", "normal"):
             a, b = _fp8_family(rng, kind, M, N, K)
             ops = wl.Operands16(dt, M, N, K, 1.0, 0.0,
@@ -403,6 +413,9 @@ def test_fp8_envelope_measurement(handle, dt):
                                 wl.place16(wl.round8(b, dt), K), K,
                                 wl.place(np.full((M, N), np.nan, np.float32), N), N,
                                 False, True)
+            (kid, _), _ = _plan(handle, ops)
+            kernel = sg.sgemm_lowp_kernel_name(kid)
+            assert ("_G16x16_" in kernel) == (M <= 16)
             out = gu.run16(handle, ops)
             R, _ = __import__("oracle").gemm_lowp(dt, M, N, K, 1.0, ops.A, K, ops.B, K,
                                                   0.0, None, N, tb=True, with_t=False)
@@ -411,8 +424,9 @@ def test_fp8_envelope_measurement(handle, dt):
             ratio = float(np.max(err / units))
             if ratio > worst:
                 worst, where = ratio, (kind, K)
-    print(f"\nfp8 envelope {dt}: worst error 2^{np.log2(worst):.2f} of the block "
-          f"units ({where[0]}, K={where[1]}); allowance 2^-9", flush=True)
+    print(f"\nfp8 envelope {dt}, {kernel.split('_')[2]} kernels: worst error "
+          f"2^{np.log2(worst):.2f} of the block units ({where[0]}, K={where[1]}); "
+          f"allowance 2^-9", flush=True)
     assert worst < gu.FP8_BLOCK_ALLOWANCE
 
 
@@ -500,8 +514,10 @@ def test_split_k_kernels(ws_handle, k):
                          ids=["1x4096x4096", "4x11008x4096", "16x4096x4096"])
 def test_split_k_plans(ws_handle, dt, shape):
     """Decode-like products (a few rows of A against a weight matrix) on a
-    handle with a workspace: K is split when the tiles fill at most half
-    the CUs (N = 4096: 64 tiles), not otherwise (N = 11008: 172 tiles);
+    handle with a workspace: when 64x64 tiles fill at most half the CUs
+    (N = 4096: 64 tiles), the one-pass kernel with B stored N x K (the 8-bit
+    cases) and K split otherwise; one tile per workgroup when they fill more
+    (N = 11008: 172 tiles);
     results within the bound (bit-exact on integers), the same bits on
     every run."""
     M, N, K = shape
@@ -510,7 +526,9 @@ def test_split_k_plans(ws_handle, dt, shape):
         w = wl.Workload("lpskp", 9500 + M, M, N, K, 1.0, 0.5, dist)
         ops = wl.operands16(w, dt, tb=tb)
         (kid, splits), dev = _plan(ws_handle, ops)
-        if N == 4096:
+        if tb and N == 4096:  # B stored N x K, at most 16 rows: one pass
+            assert "_G16x16_" in sg.sgemm_lowp_kernel_name(kid) and splits == 1
+        elif N == 4096:
             assert sg.sgemm_lowp_kernel_schedule(kid) == sg.SGEMM_SCHEDULE_SMALL_M
             assert splits >= 2
         else:
@@ -541,3 +559,79 @@ def test_split_k_needs_a_workspace(handle):
     assert e.value.status == sg.SGEMM_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.equal(C, c0)
+
+
+# ---- one pass on the matrix cores: at most 16 rows, B stored N x K -----------
+
+@pytest.mark.parametrize("k", GEMV, ids=[k["name"] for k in GEMV])
+def test_gemv_kernels(handle, k):
+    """Every one-pass small-M kernel, forced: 1 to 16 rows of A; N not a
+    multiple of a workgroup's 16 columns, and N under 16; K over several
+    blocks per wave plus a ragged piece, K of one block, and K under one
+    16-byte piece; odd leading dimensions.  Integers bit-exact, uniform
+    values within the bound (the 8-bit envelope for 8-bit formats)."""
+    ta, dt = bool(k["transa"]), DT_NAME[k["dtype"]]
+    ue = 16 if k["dtype"] in (sg.SGEMM_DTYPE_FP8_E4M3, sg.SGEMM_DTYPE_FP8_E5M2) else 8
+    handle.set_lowp_kernel(k["id"])
+    for M in (1, 3, 9, 16):
+        for i, (N, K) in enumerate(((300, 37 * k["bk"] + 19), (7, ue - 3), (33, k["bk"]))):
+            for dist in ("int4", "uniform"):
+                w = wl.Workload("gemv", 9700 + 10 * M + i, M, N, K, 1.5, 0.5, dist)
+                ops = wl.operands16(w, dt, ta=ta, tb=True, lda=(M if ta else K) + 3,
+                                    ldb=K + 5, ldc=N + 2)
+                out = gu.run16(handle, ops)
+                gu.check_full16(ops, out, exact=dist == "int4",
+                                what=f"{k['name']} {M}x{N}x{K} {dist}")
+
+
+@pytest.mark.parametrize("dt", FORMATS + FORMATS8)
+def test_gemv_unaligned_operands_and_beta_zero(handle, dt):
+    """A and B one byte (8-bit) or one element (16-bit) past a 16-byte
+    boundary, so every 16-byte piece is unaligned; beta 0 with NaN in C (C is
+    not read); K = 0 (C = beta * C)."""
+    w = wl.Workload("gemvmis", 9790, 5, 270, 1000, 1.25, -0.5, "uniform")
+    ops = wl.operands16(w, dt, tb=True, lda=1003, ldb=1001, ldc=273)
+    A, B, C = gu.to_device16(ops)
+    u8 = torch.uint8
+    off = 1 if dt in FORMATS8 else 2
+    na, nb = A.numel() * A.element_size(), B.numel() * B.element_size()
+    A1 = torch.empty(na + 2, dtype=u8, device=A.device)
+    B1 = torch.empty(nb + 2, dtype=u8, device=B.device)
+    A1[off:off + na] = A.view(u8).flatten()
+    B1[off:off + nb] = B.view(u8).flatten()
+    (kid, _), _ = _plan(handle, ops)
+    assert "_G16x16_" in sg.sgemm_lowp_kernel_name(kid)
+    out = gu.run16(handle, ops, dev=(A1[off:off + na].view(A.dtype),
+                                     B1[off:off + nb].view(B.dtype), C))
+    gu.check_full16(ops, out, what=f"{dt} unaligned")
+    ops = wl.operands16(W["c2_1024"], dt, M=4, N=100, K=300, tb=True)
+    assert np.isnan(ops.C).all()
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, what=f"{dt} beta 0, NaN C")
+    ops = wl.operands16(W["c4_edge"], dt, M=2, N=50, K=0, ldc=53, tb=True)
+    out = gu.run16(handle, ops)
+    gu.check_full16(ops, out, what=f"{dt} K = 0")
+
+
+@pytest.mark.parametrize("dt", FORMATS + FORMATS8)
+def test_gemv_plans(handle, ws_handle, dt):
+    """B stored N x K with at most 16 rows of A runs in one pass when 64x64
+    tiles would fill at most half the CUs (N = 4096: 64 tiles), with or
+    without a workspace on the handle; 17 rows, or N = 11008 (172 tiles),
+    do not; the same bits on every run."""
+    for h in (handle, ws_handle):
+        for M, N in ((1, 4096), (16, 4096), (17, 4096), (4, 11008)):
+            w = wl.Workload("gemvp", 9800 + M, M, N, 4096, 1.0, 0.5, "int4")
+            ops = wl.operands16(w, dt, tb=True)
+            (kid, splits), dev = _plan(h, ops)
+            one_pass = M <= 16 and N == 4096
+            assert ("_G16x16_" in sg.sgemm_lowp_kernel_name(kid)) == one_pass
+            if not one_pass:
+                continue
+            assert splits == 1
+            c0 = dev[2].clone()
+            out = gu.run16(h, ops, dev=dev)
+            gu.check_full16(ops, out, exact=True, what=f"{dt} M={M}")
+            dev[2].copy_(c0)
+            again = gu.run16(h, ops, dev=dev)
+            assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
