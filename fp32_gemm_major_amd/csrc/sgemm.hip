@@ -994,7 +994,8 @@ int lp_splits(const LpKernelDesc& k, const LpRun& a, int cus, size_t ws_bytes,
 // The launch sgemm_run_lowp makes on a handle: the forced kernel; else the
 // one-pass small-M kernel when it fits (at most 16 rows of A, B stored N x K:
 // a stream of B with no second pass, workspace or LDS tiles) and 64x64 tiles
-// would fill at most half the CUs; else
+// would fill at most half the CUs -- for 16-bit formats with more than four
+// rows only if split K does not run; else
 // the split-K kernel when it splits K (a workspace, few rows, few tiles);
 // else lp_select's.  *splits receives the split count (1 for kernels that do
 // not split K).  Returns the kernel id or a negative status.
@@ -1018,12 +1019,18 @@ int lp_plan(const LpRun& a, int forced, int cus, float* ws, size_t ws_bytes,
     return forced;
   }
   // (with more tiles one tile per workgroup streams B faster: 4 x 11008 x
-  // 4096 E4M3 in 9.2 us against 13.6 one-pass)
+  // 4096 E4M3 in 9.2 us against 13.6 one-pass).  With 16-bit formats and
+  // more than four rows every lane also loads as many bytes of A as of B,
+  // and split K wins when a workspace allows it (16 x 4096 x 4096 bfloat16:
+  // 8.9 us against 10.1 one-pass).
+  int one_pass = -1;
   if (2 * ceil_div(a.M, 64) * ceil_div(a.N, 64) <= cus)
-    for (int id = 0; id < kNumLpKernels; ++id) {
+    for (int id = 0; id < kNumLpKernels && one_pass < 0; ++id) {
       const LpKernelDesc& k = kLpKernels[id];
-      if (k.schedule == SGEMM_SCHEDULE_SMALL_M && !k.split && lp_fits(k, a)) return id;
+      if (k.schedule == SGEMM_SCHEDULE_SMALL_M && !k.split && lp_fits(k, a)) one_pass = id;
     }
+  if (one_pass >= 0 && (lp_elem_bytes(a.dt) == 1 || a.M <= 4 || ws == nullptr))
+    return one_pass;
   if (ws != nullptr) {
     for (int id = 0; id < kNumLpKernels; ++id) {
       const LpKernelDesc& k = kLpKernels[id];
@@ -1036,6 +1043,7 @@ int lp_plan(const LpRun& a, int forced, int cus, float* ws, size_t ws_bytes,
     }
   }
   *kps = a.K;
+  if (one_pass >= 0) return one_pass;
   const int id = lp_select(a, cus);
   return id >= 0 ? id : SGEMM_ERR_UNSUPPORTED;
 }

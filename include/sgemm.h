@@ -396,7 +396,8 @@ int sgemm_lowp_kernel_info(int kernel_id, int* dtype, int* bm, int* bn,
  *     workgroup takes 16 columns of C over all of K; its waves feed 16 x 16
  *     MFMAs straight from memory (no LDS tiles), split K and add their
  *     partial blocks through LDS in wave order.  No workspace, one launch,
- *     deterministic.  Taken first, with or without a workspace.
+ *     deterministic.  Taken first, with or without a workspace (16-bit
+ *     formats with more than four rows: only when split K does not run).
  *   split K ("_sk_edge"): M <= 64, any storage, a workspace on the handle
  *     (sgemm_set_workspace).  K is split into ranges of whole K steps (at
  *     least four each) so that the workgroups reach two per CU, each range's

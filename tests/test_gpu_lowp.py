@@ -616,15 +616,17 @@ def test_gemv_unaligned_operands_and_beta_zero(handle, dt):
 @pytest.mark.parametrize("dt", FORMATS + FORMATS8)
 def test_gemv_plans(handle, ws_handle, dt):
     """B stored N x K with at most 16 rows of A runs in one pass when 64x64
-    tiles would fill at most half the CUs (N = 4096: 64 tiles), with or
-    without a workspace on the handle; 17 rows, or N = 11008 (172 tiles),
-    do not; the same bits on every run."""
+    tiles would fill at most half the CUs (N = 4096: 64 tiles) -- except
+    that with 16-bit formats, more than four rows and a workspace K is split
+    instead; 17 rows, or N = 11008 (172 tiles), do not; the same bits on
+    every run."""
     for h in (handle, ws_handle):
-        for M, N in ((1, 4096), (16, 4096), (17, 4096), (4, 11008)):
+        for M, N in ((1, 4096), (4, 4096), (16, 4096), (17, 4096), (4, 11008)):
             w = wl.Workload("gemvp", 9800 + M, M, N, 4096, 1.0, 0.5, "int4")
             ops = wl.operands16(w, dt, tb=True)
             (kid, splits), dev = _plan(h, ops)
-            one_pass = M <= 16 and N == 4096
+            one_pass = M <= 16 and N == 4096 and (
+                dt in FORMATS8 or M <= 4 or h is handle)
             assert ("_G16x16_" in sg.sgemm_lowp_kernel_name(kid)) == one_pass
             if not one_pass:
                 continue
