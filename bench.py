@@ -19,8 +19,10 @@ problem statement; the alpha/beta update is not counted).
 Output: one JSON line with the throughput, the kernel's roofline position
 (HIP events around every launch on the stream the kernel runs on), the CPU
 oracle timed on a bounded sample of the same workload, and per-workload
-GFLOPS for the other problem shapes; then the same problems with bfloat16,
-binary16, E4M3 or E5M2 A and B and FP32 C (the "lowp" object: per format,
+GFLOPS for the other problem shapes and for decode-like products (1, 16 or 4
+rows of A against B stored N x K, with B's stream rate); then the same
+problems with bfloat16, binary16, E4M3 or E5M2 A and B and FP32 C (the
+"lowp" object: per format,
 the headline problem's roofline against the dense matrix-core peak of that
 format, and the other shapes).  --lowp-only --lowp-k K times only the 16/8-bit
 headline problem with K in place of 4096: two such runs under a cycle counter
@@ -48,6 +50,10 @@ TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 # that every shape is timed at the clock the GPU holds under load rather than
 # after the host-side set-up between shapes (1024^3: ~19.5 against ~20.6 us).
 PER_CONFIG_PREWARM_S = 0.2
+# Decode-like products timed beside the five workloads: (workload, rows of A)
+# with B stored N x K -- 1 x 4096 x 4096 (the headline's draws), 16 x 4096 x
+# 4096, and 4 x 11008 x 4096 (the MLP shape's draws).
+SMALL_M_CASES = (("c3_4096", 1), ("c3_4096", 16), ("c5_mlp", 4))
 
 
 # the kernel code, the tile order and the tile shapes of each family
@@ -248,10 +254,12 @@ def lowp_section(args, sg, rf, wl, torch):
     h = sg.Handle(workspace=False)
     out = {}
 
-    def prepare(name, dt, ta=False, tb=False, k=0):
+    def prepare(name, dt, ta=False, tb=False, k=0, M=None):
         w = wl.WORKLOADS[name]
         if k > 0:  # the same problem at another K (--lowp-k)
             w = dataclasses.replace(w, K=k)
+        if M is not None:  # decode-like: fewer rows of A
+            w = dataclasses.replace(w, M=M)
         ops = wl.operands16(w, dt, ta=ta, tb=tb)
         raw = "uint8" if dt in wl.FORMATS8 else "int16"
         A = torch.from_numpy(ops.A.view(raw)).cuda().view(tdt[dt])
@@ -321,6 +329,18 @@ def lowp_section(args, sg, rf, wl, torch):
                                    "kernel_ms": round(ms, 5),
                                    "kernel": sg.sgemm_lowp_kernel_name(kid2)}
                 del dev2
+            # decode-like products, B stored N x K (as for FP32)
+            for name, M in SMALL_M_CASES:
+                w2, dev2, kid2, launch2 = prepare(name, dt, tb=True, M=M)
+                if args.prewarm_s > 0:
+                    prewarm(launch2, min(args.prewarm_s, PER_CONFIG_PREWARM_S), torch)
+                ms = time_graph(launch2, 100, torch)
+                gf = rf.flops(w2.M, w2.N, w2.K) / (ms * 1e-3) / 1e9
+                per_config[f"{name}_m{M}_nt"] = {
+                    "gflops": round(gf, 1), "kernel_ms": round(ms, 5),
+                    "b_tbps": round((1 if fp8 else 2) * w2.N * w2.K / (ms * 1e-3) / 1e12, 3),
+                    "kernel": sg.sgemm_lowp_kernel_name(kid2)}
+                del dev2
         sec["per_config"] = per_config
         out[dt] = sec
     h.close()
@@ -376,15 +396,18 @@ def main(argv=None):
 
     launches = {}  # launches per call of each prepared problem
 
-    def prepare(name, ta=False, tb=False):
+    def prepare(name, ta=False, tb=False, M=None):
         w = wl.WORKLOADS[name]
+        if M is not None:  # the same draws with fewer rows of A (decode-like)
+            w = dataclasses.replace(w, M=M)
         ops = wl.operands(w, ta=ta, tb=tb)
         dev = [torch.from_numpy(x).cuda() for x in (ops.A, ops.B, ops.C)]
         plan = [(args.kernel, 0, w.N)] if args.kernel >= 0 else h.plan(
             w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(), ops.ldb,
             dev[2].data_ptr(), ops.ldc, transa=ta, transb=tb)
         kid = plan[0][0]
-        launches[name if not (ta or tb) else f"{name}_{int(ta)}{int(tb)}"] = len(plan)
+        launches[(name if not (ta or tb) else f"{name}_{int(ta)}{int(tb)}")
+                 + ("" if M is None else f"_m{M}")] = len(plan)
 
         def launch():
             h.gemm(dev[0], dev[1], dev[2], w.alpha, w.beta, M=w.M, N=w.N, K=w.K,
@@ -520,6 +543,14 @@ def main(argv=None):
             per_config[args.workload + "_valu"] = entry(w3, kid3, timed(launch3, 10))
             h.set_variant(variant)
             del dev3
+            # decode-like products: a few rows of A against B stored N x K
+            # (a Linear layer's weight), bound by reading B once
+            for name, M in SMALL_M_CASES:
+                w3, _, dev3, kid3, launch3 = prepare(name, tb=True, M=M)
+                e = entry(w3, kid3, timed(launch3, 100))
+                e["b_tbps"] = round(4.0 * w3.N * w3.K / (e["kernel_ms"] * 1e-3) / 1e12, 3)
+                per_config[f"{name}_m{M}_nt"] = e
+                del dev3
     h.close()
     lowp = lowp_section(args, sg, rf, wl, torch)
 
