@@ -241,7 +241,11 @@ typedef unsigned u32x4u1 __attribute__((ext_vector_type(4), aligned(1)));
 
 // One 16-byte unit of elements of type E at p: one 16-byte load when all
 // 16 / sizeof(E) elements are wanted, else element loads of the first n (n
-// may be <= 0) with zeros after them.
+// may be <= 0) with zeros after them.  The element loads are unconditional
+// -- element t reads p[min(t, n-1)], inside the n wanted -- and masked
+// afterwards: loads under per-element branches were each waited for before
+// the next was issued (one memory round trip per element of a partial
+// piece).
 template <class E>
 __device__ __forceinline__ u32x4 lp_load_unit(const E* p, int n) {
   constexpr int UE = 16 / sizeof(E), BITS = 8 * sizeof(E);
@@ -250,11 +254,13 @@ __device__ __forceinline__ u32x4 lp_load_unit(const E* p, int n) {
     return u32x4{v[0], v[1], v[2], v[3]};
   }
   u32x4 out = {0u, 0u, 0u, 0u};
+  if (n <= 0) return out;
+  unsigned h[UE];
 #pragma unroll
-  for (int t = 0; t < UE; ++t) {
-    const unsigned h = t < n ? (unsigned)p[t] : 0u;
-    out[t / (32 / BITS)] |= h << (BITS * (t % (32 / BITS)));
-  }
+  for (int t = 0; t < UE; ++t) h[t] = (unsigned)p[t < n ? t : n - 1];
+#pragma unroll
+  for (int t = 0; t < UE; ++t)
+    if (t < n) out[t / (32 / BITS)] |= h[t] << (BITS * (t % (32 / BITS)));
   return out;
 }
 
@@ -787,14 +793,13 @@ __device__ __forceinline__ void lp_tile_accumulate(const LpArgs& g, char* lds,
       // K, M and N, in the K-contiguous layout.  The loop's clamped
       // look-ahead loads may still be landing: every wave waits for its own
       // and for every other wave's reads before the stage is rewritten.
+      // Both operands' loads go out first and share one wait with the
+      // look-ahead loads.
+      load_regs(kd, 3);
       wait_all();
       wait_lds();
       __syncthreads();
-      // (A, then B: the two register sets are not live at once)
-      load_regs(kd, 1);
-      store_regs(0, 1);
-      load_regs(kd, 2);
-      store_regs(0, 2);
+      store_regs(0, 3);
       wait_lds();
       __syncthreads();
 #pragma unroll

@@ -125,12 +125,16 @@ __global__ void __launch_bounds__(LPV_THREADS) lp_gemv_kernel(LpArgs g) {
         if (live && a_in) {
           if (!TA) {
             v = lp_load_unit(A + (size_t)i * lda + k, K - k);
-          } else {  // A(i, k) = A[k*lda + i]: one element per k
+          } else if (k < K) {  // A(i, k) = A[k*lda + i]: one element per k
+            // unconditional loads (k clamped to K - 1), masked afterwards, so
+            // that they are all in flight at once
+            unsigned h[UE];
 #pragma unroll
-            for (int e = 0; e < UE; ++e) {
-              const unsigned h = k + e < K ? (unsigned)A[(size_t)(k + e) * lda + i] : 0u;
-              v[e / (32 / BITS)] |= h << (BITS * (e % (32 / BITS)));
-            }
+            for (int e = 0; e < UE; ++e)
+              h[e] = (unsigned)A[(size_t)(k + e < K ? k + e : K - 1) * lda + i];
+#pragma unroll
+            for (int e = 0; e < UE; ++e)
+              if (k + e < K) v[e / (32 / BITS)] |= h[e] << (BITS * (e % (32 / BITS)));
           }
         }
         y[j][p] = v;
