@@ -637,3 +637,54 @@ def test_gemv_plans(handle, ws_handle, dt):
             dev[2].copy_(c0)
             again = gu.run16(h, ops, dev=dev)
             assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+
+
+# ---- seeded random problems through the planner ------------------------------
+
+def _random_lowp_problems(seed, count):
+    rng = np.random.default_rng(seed)
+    picks = []
+    for _ in range(count):
+        kind = int(rng.integers(0, 4))
+        if kind == 0:    # a few rows against a wide B (one-pass, split-K or tiles)
+            M = int(rng.integers(1, 20))
+            N = int(rng.integers(200, 3000))
+            K = int(rng.integers(100, 3000))
+        elif kind == 1:  # tile multiples give or take a little
+            M = int(rng.choice([64, 128, 256])) * int(rng.integers(1, 5)) + int(rng.integers(-3, 4))
+            N = int(rng.choice([64, 128, 256])) * int(rng.integers(1, 5)) + int(rng.integers(-3, 4))
+            K = int(rng.choice([64, 128])) * int(rng.integers(1, 10)) + int(rng.integers(-2, 3))
+        elif kind == 2:  # few tiles, deep K
+            M = int(rng.integers(17, 200))
+            N = int(rng.integers(17, 200))
+            K = int(rng.integers(1000, 4000))
+        else:            # anything up to mid sizes
+            M, N, K = (int(x) for x in rng.integers(1, 700, size=3))
+        M, N, K = max(M, 1), max(N, 1), max(K, 1)
+        ta, tb = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        alpha = float(rng.choice([1.0, -1.5, 0.5]))
+        beta = float(rng.choice([0.0, 1.0, -0.5]))
+        pads = [int(x) for x in rng.integers(0, 5, size=3)]
+        picks.append((M, N, K, ta, tb, alpha, beta, pads))
+    return picks
+
+
+@pytest.mark.parametrize("dt", FORMATS + FORMATS8)
+def test_random_problems_integer_exact(ws_handle, dt):
+    """12 seeded random problems per format through sgemm_run_lowp's planner
+    on a handle with a workspace (so the one-pass and split-K small-M kernels
+    are candidates): random storage, sizes, strides, alpha and beta;
+    bit-exact on integer inputs, the padding of C untouched."""
+    seed = {"bf16": 0, "f16": 1, "fp8e4m3": 2, "fp8e5m2": 3}[dt]
+    for i, (M, N, K, ta, tb, alpha, beta, pads) in enumerate(
+            _random_lowp_problems(9900 + seed, 12)):
+        w = wl.Workload("lprand", 9910 + 16 * seed + i, M, N, K, alpha, beta, "int4",
+                        "nan" if beta == 0.0 else "dist")
+        ops = wl.operands16(w, dt, ta=ta, tb=tb, lda=(M if ta else K) + pads[0],
+                            ldb=(K if tb else N) + pads[1], ldc=N + pads[2])
+        (kid, splits), dev = _plan(ws_handle, ops)
+        what = (f"{dt} {M}x{N}x{K} ta={ta} tb={tb} a={alpha} b={beta} pads={pads} "
+                f"kernel={sg.sgemm_lowp_kernel_name(kid)} splits={splits}")
+        print(what, flush=True)
+        out = gu.run16(ws_handle, ops, dev=dev)
+        gu.check_full16(ops, out, exact=True, what=what)
