@@ -544,13 +544,17 @@ def main(argv=None):
             h.set_variant(variant)
             del dev3
             # decode-like products: a few rows of A against B stored N x K
-            # (a Linear layer's weight), bound by reading B once
+            # (a Linear layer's weight), bound by reading B once; the
+            # library's default plan, which picks between the matrix-core
+            # split-K kernels and the one-pass vector-ALU ones
+            h.set_variant(sg.SGEMM_VARIANT_AUTO)
             for name, M in SMALL_M_CASES:
                 w3, _, dev3, kid3, launch3 = prepare(name, tb=True, M=M)
                 e = entry(w3, kid3, timed(launch3, 100))
                 e["b_tbps"] = round(4.0 * w3.N * w3.K / (e["kernel_ms"] * 1e-3) / 1e12, 3)
                 per_config[f"{name}_m{M}_nt"] = e
                 del dev3
+            h.set_variant(variant)
     h.close()
     lowp = lowp_section(args, sg, rf, wl, torch)
 

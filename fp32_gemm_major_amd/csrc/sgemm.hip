@@ -13,6 +13,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <new>
@@ -224,7 +225,8 @@ hipError_t launch_mfma_splitk(const RunArgs& a, int tiles_m, int tiles_n,
 template <int MT, bool TA>
 hipError_t launch_skinny_nt(const RunArgs& a, int, int, const LaunchCtx&,
                             hipStream_t s) {
-  const int blocks = (a.N + SKINNY_NT_COLS - 1) / SKINNY_NT_COLS;
+  constexpr int R = skinny_nt_rows(MT);
+  const int blocks = (a.N + R - 1) / R;
   hipLaunchKernelGGL((skinny_nt_kernel<MT, TA>), dim3(blocks), dim3(SKINNY_NT_THREADS),
                      0, s, gemm_args(a));
   return hipGetLastError();
@@ -276,16 +278,17 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   STORAGE(T, "nt_", false, true)
 
 // Small-M kernels: bm = the most rows of C they take, bn = the columns of C
-// per workgroup.  With B stored N x K every workgroup stages all of A, whose
-// traffic grows with M: past 4 rows the MFMA stream-K kernels measured
-// faster (16 x 4096 x 4096: 42 against 26 us), so those kernels stop at 4.
+// per workgroup.  With B stored N x K every workgroup reads all of A (from
+// the caches), whose traffic grows with M over the few columns a workgroup
+// takes: past 8 rows the MFMA split-K kernels are faster (16 x 4096 x 4096:
+// 26.5 us on 16 rows against 17), so those kernels stop at 8.
 #define SKINNY(MT, PRE, TA)                                                  \
   {"valu_S" #MT "x256_" PRE "small", SGEMM_VARIANT_VALU, TA, false, MT,     \
    SKINNY_COLS, SKINNY_KC, SKINNY_THREADS, SGEMM_MODE_EDGE,                  \
    SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny<MT, TA>}
 #define SKINNY_NT(MT, PRE, TA)                                               \
-  {"valu_S" #MT "x16_" PRE "small", SGEMM_VARIANT_VALU, TA, true, MT,       \
-   SKINNY_NT_COLS, SKINNY_NT_KC, SKINNY_NT_THREADS, SGEMM_MODE_EDGE,         \
+  {"valu_S" #MT "_" PRE "small", SGEMM_VARIANT_VALU, TA, true, MT,          \
+   skinny_nt_rows(MT), SKINNY_NT_PIECE, SKINNY_NT_THREADS, SGEMM_MODE_EDGE,  \
    SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny_nt<MT, TA>}
 // Small M on the matrix cores with K split (edge mode): one tile row of the
 // 32x64 tile (A stored M x K) or of the 64x64 tile (A stored K x M).
@@ -312,7 +315,9 @@ const KernelDesc kKernels[] = {
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, true>},
     SKINNY(4, "", false), SKINNY(8, "", false), SKINNY(16, "", false),
     SKINNY(4, "tn_", true), SKINNY(8, "tn_", true), SKINNY(16, "tn_", true),
-    SKINNY_NT(4, "nt_", false), SKINNY_NT(4, "tt_", true),
+    SKINNY_NT(1, "nt_", false), SKINNY_NT(2, "nt_", false), SKINNY_NT(4, "nt_", false),
+    SKINNY_NT(8, "nt_", false), SKINNY_NT(1, "tt_", true), SKINNY_NT(2, "tt_", true),
+    SKINNY_NT(4, "tt_", true), SKINNY_NT(8, "tt_", true),
     MFMA_SPLITK(M32x64, "", false, false), MFMA_SPLITK(M32x64, "nt_", false, true),
     MFMA_SPLITK(M64x64, "tn_", true, false), MFMA_SPLITK(M64x64, "tt_", true, true),
 };
@@ -350,7 +355,9 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
     return false;
   if (k.schedule == SGEMM_SCHEDULE_SMALL_M) {
     if (a.K <= 0 || a.M > k.bm) return false;
-    if (k.variant == SGEMM_VARIANT_VALU) return true;
+    // (the one-pass kernels index columns and k in 32 bits, a piece past K)
+    if (k.variant == SGEMM_VARIANT_VALU)
+      return !a.tb || (a.N <= INT_MAX - k.bn && a.K <= INT_MAX - SKINNY_NT_PIECE);
     // MFMA split-K: the edge instance's conditions, and a workspace for at
     // least one set of partial sums
     const size_t part = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
@@ -460,20 +467,35 @@ double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
   return us;
 }
 
-// Small-M launch: B streamed once at ~4.5 TB/s when at least half
-// the CUs have a workgroup (proportionally less with fewer), ~4 us of launch
-// and fill, and with several K ranges ~3 us for the second kernel plus the
-// partial sums written and read back at ~5 TB/s (measured on MI355X: 1 x
-// 4096 x 4096 in 20 us, 4 x 4096 x 16384 at 5.8 TB/s).
-double skinny_cost(const RunArgs& a, const LaunchCtx& c) {
-  const int splits = a.tb ? 1 : skinny_splits(a, c);
-  const double wgs = a.tb ? (double)((a.N + SKINNY_NT_COLS - 1) / SKINNY_NT_COLS)
-                          : (double)((a.N + SKINNY_COLS - 1) / SKINNY_COLS) * splits;
+// Small-M launch, B stored K x N (skinny_sgemm_kernel): B streamed once at
+// ~4.5 TB/s when at least half the CUs have a workgroup (proportionally less
+// with fewer), ~4 us of launch and fill, and with several K ranges ~3 us for
+// the second kernel plus the partial sums written and read back at ~5 TB/s
+// (measured on MI355X: 1 x 4096 x 4096 in 20 us, 4 x 4096 x 16384 at 5.8
+// TB/s).
+//
+// B stored N x K (skinny_nt_kernel, one pass): ~3.3 us of launch and
+// reduction, and B at a rate that falls as the kernel's rows grow (its
+// loads of A and multiply-adds per byte of B): ~7.7 TB/s up to 2 rows, 7.4
+// at 4 and 6.0 at 8, once 2048 waves stream it (two workgroups per CU; a
+// wave streams only while K holds a piece for it).  Fitted on MI355X graph
+// replays: 1 row 4096 x 4096 11.9 us, 11008 x 4096 27.0, 4096 x 14336 33.7,
+// 65536 x 1024 38.5; 4 rows 4096 x 4096 12.5, 11008 x 4096 27.3; 8 rows
+// 4096 x 4096 14.7, 11008 x 4096 33.4, 14336 x 4096 40.6.
+double skinny_cost(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
+  if (a.tb) {
+    const double wgs = (double)ceil_div(a.N, k.bn);
+    const double pieces = (double)ceil_div(a.K, SKINNY_NT_PIECE);
+    const double waves = std::min(wgs, 2.0 * c.cus) *
+                         std::min(pieces, (double)SKINNY_NT_WAVES);
+    const double fill = std::min(1.0, waves / (8.0 * c.cus));
+    const double bw = k.bm <= 2 ? 7.7e12 : k.bm <= 4 ? 7.4e12 : 6.0e12;
+    return 3.3 + (double)a.K * a.N * 4 / (bw * fill) * 1e6;
+  }
+  const int splits = skinny_splits(a, c);
+  const double wgs = (double)((a.N + SKINNY_COLS - 1) / SKINNY_COLS) * splits;
   const double fill = 2 * wgs < c.cus ? 2 * wgs / c.cus : 1.0;
-  // B once; with B stored N x K every workgroup also reads all of A, mostly
-  // from L2 (counted at half the cost of HBM bytes)
-  const double bytes = (double)a.K * a.N * 4 + (a.tb ? 0.5 * wgs * a.M * a.K * 4.0 : 0.0);
-  double us = 4.0 + bytes / (4.5e12 * fill) * 1e6;
+  double us = 4.0 + (double)a.K * a.N * 4 / (4.5e12 * fill) * 1e6;
   if (splits > 1)
     us += 3.0 + 2.0 * splits * a.M * skinny_ws_stride(a.N) * 4.0 / 5e12 * 1e6;
   return us;
@@ -566,7 +588,7 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
       continue;
     if (valu && skinny >= 0 && kKernels[skinny].variant == SGEMM_VARIANT_VALU)
       continue;  // a VALU kernel with fewer rows already fits
-    const double us = valu ? skinny_cost(a, ctx) : mfma_splitk_cost(k, a, ctx);
+    const double us = valu ? skinny_cost(k, a, ctx) : mfma_splitk_cost(k, a, ctx);
     if (skinny < 0 || us < skinny_us) {
       skinny = i;
       skinny_us = us;

@@ -233,128 +233,177 @@ __global__ void __launch_bounds__(SKINNY_REDUCE_THREADS)
   }
 }
 
-// ---- small M, B stored N x K ------------------------------------------------
+// ---- small M, B stored N x K, in one pass -----------------------------------
 //
-// Row n of B is then contiguous along K, so the lanes of a wave split K: each
-// lane takes 4 consecutive k of every 256, reads 16 bytes of each of the
-// wave's 4 rows of B (1 KB per row per wave per step, SKINNY_NT_STEPS steps
-// in flight) and the matching 16 bytes of every row of A from LDS, and keeps
-// MT x 4 dot-product sums.  A workgroup of 4 waves takes 16 rows of B (16
-// columns of C) over all of K, so no workspace is needed; the lanes' sums
-// are added by an xor butterfly (a fixed order) and lane 0 applies alpha and
-// beta.  A is staged in LDS as [m][k], SKINNY_NT_KC k at a time.
+// Row n of B is then contiguous along K, so one load instruction of a wave
+// can read 1 KB of one row (64 lanes x 16 bytes, k = 256p + 4*lane ..): whole
+// cache lines, with no LDS and no workspace.  A workgroup of SKINNY_NT_WAVES
+// waves takes R rows of B (R columns of C) over all of K; its waves split K
+// into contiguous runs of 256-k pieces, and each lane multiplies its 16 bytes
+// of the R rows with the same 16 bytes of every row of A, which it loads
+// itself (A is small and read from the caches), keeping MT x R sums.  The
+// lanes' sums meet by recursive halving (each exchange step halves the sums a
+// lane holds, so MT*R sums take MT*R exchanges rather than 6*MT*R), the
+// waves' through LDS in wave order, and one thread per output applies alpha
+// and beta: every sum is taken in a fixed order.  R shrinks as MT grows so
+// that the sums, the pieces in flight and the A pieces fit 128 registers
+// (four waves per SIMD, two workgroups per CU).
 
-constexpr int SKINNY_NT_WAVES = 4;
+constexpr int SKINNY_NT_WAVES = 8;
 constexpr int SKINNY_NT_THREADS = 64 * SKINNY_NT_WAVES;
-constexpr int SKINNY_NT_ROWS = 4;     // rows of B per wave
-constexpr int SKINNY_NT_STEPS = 4;    // 256-k steps in flight per lane
-constexpr int SKINNY_NT_KC = 256 * SKINNY_NT_STEPS;
-constexpr int SKINNY_NT_COLS = SKINNY_NT_WAVES * SKINNY_NT_ROWS;  // per workgroup
-static_assert(SKINNY_NT_KC == 4 * SKINNY_NT_THREADS, "one 4-k piece of A per thread");
+constexpr int SKINNY_NT_PIECE = 256;  // k per wave load instruction
 
-// 16 bytes of row p of B^T at k (any 4-byte alignment), zero past kn.
-__device__ __forceinline__ f32x4 skinny_load_bt(const float* p, int k, int kn) {
-  if (k + 3 < kn) {
+// rows of B per workgroup for MT rows of A (measured on MI355X, 4096 x 4096
+// and 11008 x 4096: 8 rows for MT <= 2, 4 rows for MT = 4 and 8)
+__host__ __device__ constexpr int skinny_nt_rows(int mt) { return mt <= 2 ? 8 : 4; }
+
+// 16 bytes at p (any 4-byte alignment) holding n elements of the row (n <= 0:
+// none; n < 4: the rest are zero).  The partial case loads from clamped,
+// in-bounds addresses and masks afterwards, so its loads do not wait on
+// per-element branches.
+__device__ __forceinline__ f32x4 skinny_nt_load(const float* p, int n) {
+  if (n >= 4) {
     const f32x4u v = *reinterpret_cast<const f32x4u*>(p);
     return f32x4{v[0], v[1], v[2], v[3]};
   }
-  f32x4 x;
+  f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (n <= 0) return x;
+  float h[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] = k + e < kn ? p[e] : 0.0f;
+  for (int e = 0; e < 4; ++e) h[e] = p[e < n ? e : n - 1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = e < n ? h[e] : 0.0f;
   return x;
 }
 
+// Grid: ceil(N / R) workgroups, workgroup b taking rows [R*b, R*b + R) of B.
+// MT >= M >= 1; N >= 1; K <= INT_MAX - 256.  TA: A stored K x M.
 template <int MT, bool TA>
-__global__ void __launch_bounds__(SKINNY_NT_THREADS)
-    skinny_nt_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) float lds[MT * SKINNY_NT_KC];
+__global__ void __launch_bounds__(SKINNY_NT_THREADS, 4) skinny_nt_kernel(GemmArgs g) {
+  constexpr int R = skinny_nt_rows(MT);
+  constexpr int V = MT * R;  // sums per lane, a power of two up to 64
+  static_assert((V & (V - 1)) == 0 && V <= 64, "sums per lane");
+  constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : V == 16 ? 4
+                     : V == 32 ? 5 : 6;
+  __shared__ float red[SKINNY_NT_WAVES * V];
   const int M = g.M, N = g.N, K = g.K;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = (blockIdx.x * SKINNY_NT_WAVES + wave) * SKINNY_NT_ROWS;
+  const int n0 = blockIdx.x * R;
   const float* __restrict__ A = g.A;
-  const float* __restrict__ B = g.B;
-  const int lda = g.lda, ldb = g.ldb;
-
-  float acc[MT][SKINNY_NT_ROWS];
+  const int lda = g.lda;
+  // rows of B past N and of A past M are clamped to the last one: their
+  // loads stay in bounds and their sums are never stored
+  const float* brow[R];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int r = 0; r < SKINNY_NT_ROWS; ++r) acc[m][r] = 0.0f;
-
-  for (int kc = 0; kc < K; kc += SKINNY_NT_KC) {
-    const int kn = K - kc < SKINNY_NT_KC ? K - kc : SKINNY_NT_KC;
-    // this chunk's rows of B, requested before A is staged
-    f32x4 b[SKINNY_NT_STEPS][SKINNY_NT_ROWS];
-#pragma unroll
-    for (int t = 0; t < SKINNY_NT_STEPS; ++t) {
-      const int k = 256 * t + 4 * lane;
-#pragma unroll
-      for (int r = 0; r < SKINNY_NT_ROWS; ++r)
-        b[t][r] = (k < kn && n0 + r < N)
-                      ? skinny_load_bt(B + (size_t)(n0 + r) * ldb + kc + k, k, kn)
-                      : f32x4{};
-    }
-    // stage A(0..MT-1, kc..kc+kn) as lds[m][k], zero past M and past kn:
-    // thread i takes k = 4i .. 4i+3 of every row, all loads independent
-    {
-      const int k = 4 * threadIdx.x;
-      f32x4 v[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m >= M || k >= kn) {
-          v[m] = f32x4{};
-        } else if (!TA) {  // A(m, k) = A[m*lda + k]: 16 bytes of row m
-          v[m] = skinny_load_bt(A + (size_t)m * lda + kc + k, k, kn);
-        } else {           // A(m, k) = A[k*lda + m]: one float per k
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[m][e] = k + e < kn ? A[(size_t)(kc + k + e) * lda + m] : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        *reinterpret_cast<f32x4*>(&lds[m * SKINNY_NT_KC + k]) = v[m];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < SKINNY_NT_STEPS; ++t) {
-      const int k = 256 * t + 4 * lane;
-      if (k < kn) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&lds[m * SKINNY_NT_KC + k]);
-#pragma unroll
-          for (int r = 0; r < SKINNY_NT_ROWS; ++r)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[m][r] = fmaf(a[e], b[t][r][e], acc[m][r]);
-        }
-      }
-    }
-    __syncthreads();  // the next chunk reuses the LDS
-  }
-
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int r = 0; r < SKINNY_NT_ROWS; ++r)
-#pragma unroll
-      for (int off = 32; off >= 1; off /= 2) acc[m][r] += __shfl_xor(acc[m][r], off);
-  if (lane != 0) return;
-  const float alpha = g.alpha, beta = g.beta;
+  for (int r = 0; r < R; ++r) brow[r] = g.B + (size_t)(n0 + r < N ? n0 + r : N - 1) * g.ldb;
+  int am[MT];
+  const float* arow[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    if (m < M) {
+    am[m] = m < M ? m : M - 1;
+    arow[m] = A + (size_t)am[m] * lda;
+  }
+  // this wave's pieces: a contiguous run
+  const int np = K / SKINNY_NT_PIECE + (K % SKINNY_NT_PIECE != 0);
+  const int per = (np + SKINNY_NT_WAVES - 1) / SKINNY_NT_WAVES;
+  const int p0 = wave * per, p1 = p0 + per < np ? p0 + per : np;
+
+  float acc[V];  // acc[m * R + r]
 #pragma unroll
-      for (int r = 0; r < SKINNY_NT_ROWS; ++r) {
-        if (n0 + r < N) {
-          float* p = g.C + (size_t)m * g.ldc + n0 + r;
-          float o = alpha * acc[m][r];
-          if (beta != 0.0f) o = fmaf(beta, *p, o);
-          *p = o;
+  for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+  for (int p = p0; p < p1; ++p) {
+    const int k = p * SKINNY_NT_PIECE + 4 * lane;
+    f32x4 b[R], a[MT];
+    if ((p + 1) * SKINNY_NT_PIECE <= K) {
+      // a whole piece (wave-uniform): plain loads, all issued before the
+      // first multiply-add
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const f32x4u v = *reinterpret_cast<const f32x4u*>(brow[r] + k);
+        b[r] = f32x4{v[0], v[1], v[2], v[3]};
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (!TA) {
+          const f32x4u v = *reinterpret_cast<const f32x4u*>(arow[m] + k);
+          a[m] = f32x4{v[0], v[1], v[2], v[3]};
+        } else {  // A(m, k) = A[k*lda + m]: one element per k
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[m][e] = A[(size_t)(k + e) * lda + am[m]];
+        }
+      }
+    } else {  // the last piece of K
+      const int left = K - k;
+#pragma unroll
+      for (int r = 0; r < R; ++r) b[r] = skinny_nt_load(brow[r] + k, left);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (!TA) {
+          a[m] = skinny_nt_load(arow[m] + k, left);
+        } else {
+          a[m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          if (left > 0) {
+            float h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              h[e] = A[(size_t)(e < left ? k + e : k + left - 1) * lda + am[m]];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[m][e] = e < left ? h[e] : 0.0f;
+          }
         }
       }
     }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[m * R + r] = fmaf(a[m][e], b[r][e], acc[m * R + r]);
   }
+
+  // Recursive halving over the 64 lanes: at the exchange with lane l ^ off,
+  // the lane whose bit `off` is set keeps the upper half of its sums and
+  // sends the lower half (its partner the reverse) and adds what it
+  // receives.  After the first log2(V) exchanges (off = 32 down to 64 / V)
+  // lane l holds one sum, number l >> (6 - log2 V), added over the lanes
+  // that differ from it in those bits; the remaining exchanges add it over
+  // the low bits, i.e. the rest of the wave.
+  int cnt = V;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const bool up = (lane & off) != 0;
+    if (cnt > 1) {
+      const int half = cnt >> 1;
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        if (i < half) {
+          // bitwise selects: a select between two elements of the array
+          // becomes an indexed read of the whole array
+          const unsigned lo = __float_as_uint(acc[i]), hi = __float_as_uint(acc[i + half]);
+          const unsigned msk = up ? 0xFFFFFFFFu : 0u;
+          const float send = __uint_as_float((lo & msk) | (hi & ~msk));
+          const float keep = __uint_as_float((hi & msk) | (lo & ~msk));
+          acc[i] = keep + __shfl_xor(send, off);
+        }
+      }
+      cnt = half;
+    } else {
+      acc[0] += __shfl_xor(acc[0], off);
+    }
+  }
+  if ((lane & ((64 >> LOGV) - 1)) == 0) red[wave * V + (lane >> (6 - LOGV))] = acc[0];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= V) return;
+  float s = red[t];
+#pragma unroll
+  for (int w = 1; w < SKINNY_NT_WAVES; ++w) s += red[w * V + t];
+  const int m = t / R, r = t % R;
+  if (m >= M || n0 + r >= N) return;
+  float* c = g.C + (size_t)m * g.ldc + n0 + r;
+  float o = g.alpha * s;
+  if (g.beta != 0.0f) o = fmaf(g.beta, *c, o);
+  *c = o;
 }
 
 // ---- small M on the matrix cores, K split ---------------------------------

@@ -129,12 +129,16 @@ def test_kernel_table():
     # every MFMA tile shape has an aligned, an edge and a guarded instance for
     # each storage; the VALU shape an aligned and a guarded one; the small-M
     # kernels one edge instance per storage: on the vector ALUs 4, 8 and 16
-    # rows with B as stored, 4 rows with B transposed; on the matrix cores
-    # (K split) one tile row, 32 with A as stored, 64 with A transposed
+    # rows with B as stored, 1, 2, 4 and 8 rows with B transposed (one pass,
+    # 8 columns per workgroup up to 2 rows, else 4); on the matrix cores (K
+    # split) one tile row, 32 with A as stored, 64 with A transposed
     skinny = [k for k in table if k["schedule"] == sg.SGEMM_SCHEDULE_SMALL_M]
+    for k in skinny:
+        if k["variant"] == sg.SGEMM_VARIANT_VALU and k["transb"]:
+            assert k["bn"] == (8 if k["bm"] <= 2 else 4) and k["threads"] == 512, k
     assert sorted((k["bm"], k["transa"], k["transb"], k["mode"], k["variant"]) for k in skinny) == \
         sorted([(m, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU)
-                for a in (0, 1) for b in (0, 1) for m in ((4,) if b else (4, 8, 16))] +
+                for a in (0, 1) for b in (0, 1) for m in ((1, 2, 4, 8) if b else (4, 8, 16))] +
                [(64 if a else 32, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_MFMA)
                 for a in (0, 1) for b in (0, 1)])
     shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table
@@ -315,7 +319,7 @@ def test_plans_follow_measured_winners():
 def test_small_m_plans():
     """A few rows of A against a wide B plan the small-M kernel with the
     fewest rows that hold M, for every storage (up to 16 rows with B as
-    stored, 4 with B transposed); more rows or an explicit MFMA variant
+    stored, 8 with B transposed); more rows or an explicit MFMA variant
     never do."""
     A, B, C = 0x10000000, 0x20000000, 0x40000000
     def plan(M, N, K, variant=0, ta=0, tb=0):
@@ -323,17 +327,17 @@ def test_small_m_plans():
         ldb = K if tb else N
         return [sg.sgemm_kernel_info(k) for k, _, _ in
                 sg.sgemm_plan(variant, M, N, K, A, lda, B, ldb, C, N, transa=ta, transb=tb)]
-    for M, bm in ((1, 4), (4, 4), (5, 8), (16, 16)):
+    for M, bm, bm_t in ((1, 4, 1), (2, 4, 2), (4, 4, 4), (5, 8, 8), (16, 16, None)):
         for ta in (0, 1):
             for tb in (0, 1):
-                if tb and M > 4:
+                if tb and bm_t is None:
                     continue
                 # no workspace here: one K range for B as stored, so a wide B
                 p = plan(M, 4096, 16384, ta=ta, tb=tb) if tb else plan(M, 65536, 1024, ta=ta)
                 assert [(k["schedule"], k["bm"], k["transa"], k["transb"]) for k in p] == \
-                    [(sg.SGEMM_SCHEDULE_SMALL_M, bm, ta, tb)], (M, ta, tb)
+                    [(sg.SGEMM_SCHEDULE_SMALL_M, bm_t if tb else bm, ta, tb)], (M, ta, tb)
     assert plan(17, 65536, 1024)[0]["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M
-    assert plan(5, 4096, 16384, tb=1)[0]["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M
+    assert plan(9, 4096, 16384, tb=1)[0]["schedule"] != sg.SGEMM_SCHEDULE_SMALL_M
     assert plan(4, 65536, 1024, variant=sg.SGEMM_VARIANT_MFMA)[0]["variant"] == \
         sg.SGEMM_VARIANT_MFMA
     assert plan(4, 65536, 1024, variant=sg.SGEMM_VARIANT_VALU)[0]["schedule"] == \

@@ -1,8 +1,9 @@
 """Calls captured in a HIP graph and replayed.
 
 Every kind of launch plan -- one tile per workgroup, two launches over column
-ranges, stream-K with its fixup, split K with its reduction, the fixed-scratch
-entry point, and the 16/8-bit tile, split-K and one-pass kernels -- is
+ranges, stream-K with its fixup, split K with its reduction, the one-pass
+small-M kernel, the fixed-scratch entry point, and the 16/8-bit tile, split-K
+and one-pass kernels -- is
 captured once, then replayed three times with the program's own eager work
 between the replays (C restored from a copy, an unrelated product, host
 synchronisations).  Every replay must give the eager call's bits: the
@@ -69,7 +70,9 @@ FP32_CASES = [
     (wl.Workload("g_edge", 9201, 1000, 1500, 777, 1.0, 1.0, "uniform"), (False, False), None),
     (wl.Workload("g_sk", 9202, 64, 4096, 4096, 1.5, 0.5, "uniform"), (False, False),
      [sg.SGEMM_SCHEDULE_STREAM_K]),
-    (wl.Workload("g_splitk", 9203, 4, 4096, 4096, 1.0, 0.5, "uniform"), (False, True),
+    (wl.Workload("g_splitk", 9203, 16, 4096, 4096, 1.0, 0.5, "uniform"), (False, True),
+     [sg.SGEMM_SCHEDULE_SMALL_M]),
+    (wl.Workload("g_onepass", 9206, 4, 4096, 4096, 1.0, 0.5, "uniform"), (False, True),
      [sg.SGEMM_SCHEDULE_SMALL_M]),
     (wl.Workload("g_two", 9204, 2048, 5504, 2048, 1.0, 0.0, "normal"), (False, False),
      [sg.SGEMM_SCHEDULE_TILES, sg.SGEMM_SCHEDULE_TILES]),

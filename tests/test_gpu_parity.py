@@ -532,7 +532,8 @@ def test_mfma_split_k_kernels(k):
 def test_split_k_kernels(k, workspace):
     """Every small-M kernel on ragged sizes: 1 and bm rows, columns short of,
     at and past a workgroup's block and not a multiple of 4, K below, at and
-    past one staged chunk of A and not a multiple of 4, padded leading
+    past one staged chunk of A (B as stored) or one 256-k piece and a run of
+    several per wave (B transposed) and not a multiple of 4, padded leading
     dimensions; integer inputs (exact) and uniform ones (bound).  B as
     stored: with a workspace K is split over workgroups and a second kernel
     adds the ranges, without one a single range runs (B transposed needs no
@@ -544,7 +545,7 @@ def test_split_k_kernels(k, workspace):
         cases = [(1, 1, 1), (k["bm"], 3, 7), (k["bm"] - 1, 255, 300), (1, 257, 1025),
                  (k["bm"], 1000, 777), (k["bm"], 4096, 2048), (2, 33, 2049)]
         for i, (M, N, K) in enumerate(cases):
-            M = max(M, 1)
+            M = min(max(M, 1), k["bm"])
             for dist in ("int4", "uniform"):
                 w = wl.Workload("skinny", 7000 + 10 * i + k["id"], M, N, K, 1.5, -0.5, dist)
                 ops = wl.operands(w, lda=(M if ta else K) + 3, ldb=(K if tb else N) + 1,
@@ -558,7 +559,8 @@ def test_split_k_kernels(k, workspace):
 @pytest.mark.parametrize("tb,shape", [(False, (1, 4096, 4096)), (False, (16, 4096, 4096)),
                                       (False, (7, 11008, 4096)), (False, (16, 2000, 8192)),
                                       (True, (1, 4096, 4096)), (True, (4, 4096, 4096)),
-                                      (True, (3, 11008, 4096)), (True, (2, 4096, 16384))])
+                                      (True, (3, 11008, 4096)), (True, (2, 4096, 16384)),
+                                      (True, (6, 4096, 4096)), (True, (8, 14336, 4096))])
 def test_split_k_plans(handle, shape, tb):
     """Decode-like shapes (a few rows of A against a large B, stored K x N or
     N x K) plan the small-M kernel; bit-exact on integer inputs, bitwise
@@ -578,6 +580,27 @@ def test_split_k_plans(handle, shape, tb):
     w = wl.Workload("skinnyplan", 7200 + M, M, N, K, 1.0, 0.0, "normal", "nan")
     ops = wl.operands(w, tb=tb)
     gu.check_full(ops, gu.run(handle, ops), what=f"split-K plan {shape} normal")
+
+
+@pytest.mark.parametrize("shape,want", [((1, 4096, 4096), "valu_S1_nt_small"),
+                                        ((2, 4096, 4096), "valu_S2_nt_small"),
+                                        ((4, 11008, 4096), "valu_S4_nt_small"),
+                                        ((8, 4096, 4096), "valu_S8_nt_small"),
+                                        ((16, 4096, 4096), "mfma_M32x64_nt_splitk_edge")])
+def test_one_pass_plans(handle, shape, want):
+    """With B stored N x K and a workspace, the planner takes the one-pass
+    vector-ALU kernel up to 8 rows where it measured faster than split K on
+    the matrix cores (1 x 4096 x 4096: 11.9 against 16.0 us), and split K
+    past 8 rows; the planned call is exact on integers."""
+    M, N, K = shape
+    w = wl.Workload("onepass", 7300 + M, M, N, K, 1.0, 0.5, "int4")
+    ops = wl.operands(w, tb=True)
+    A, B, C = gu.to_device(ops)
+    plan = handle.plan(M, N, K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                       C.data_ptr(), ops.ldc, transb=True)
+    assert [sg.sgemm_kernel_name(k) for k, _, _ in plan] == [want]
+    gu.check_full(ops, gu.run(handle, ops, dev=(A, B, C)), exact=True,
+                  what=f"one-pass plan {shape}")
 
 
 def random_problems(seed, count):
