@@ -544,15 +544,16 @@ def main(argv=None):
             h.set_variant(variant)
             del dev3
             # decode-like products: a few rows of A against B stored N x K
-            # (a Linear layer's weight), bound by reading B once; the
+            # (a Linear layer's weight), and one row against B as stored,
+            # bound by reading B once; the
             # library's default plan, which picks between the matrix-core
             # split-K kernels and the one-pass vector-ALU ones
             h.set_variant(sg.SGEMM_VARIANT_AUTO)
-            for name, M in SMALL_M_CASES:
-                w3, _, dev3, kid3, launch3 = prepare(name, tb=True, M=M)
+            for name, M, tb in [c + (True,) for c in SMALL_M_CASES] + [("c3_4096", 1, False)]:
+                w3, _, dev3, kid3, launch3 = prepare(name, tb=tb, M=M)
                 e = entry(w3, kid3, timed(launch3, 100))
                 e["b_tbps"] = round(4.0 * w3.N * w3.K / (e["kernel_ms"] * 1e-3) / 1e12, 3)
-                per_config[f"{name}_m{M}_nt"] = e
+                per_config[f"{name}_m{M}" + ("_nt" if tb else "")] = e
                 del dev3
             h.set_variant(variant)
     h.close()

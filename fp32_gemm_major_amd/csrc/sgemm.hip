@@ -233,6 +233,15 @@ hipError_t launch_skinny_nt(const RunArgs& a, int, int, const LaunchCtx&,
 }
 
 template <int MT, bool TA>
+hipError_t launch_skinny_kn(const RunArgs& a, int, int, const LaunchCtx&,
+                            hipStream_t s) {
+  const int blocks = (a.N + SKINNY_KN_COLS - 1) / SKINNY_KN_COLS;
+  hipLaunchKernelGGL((skinny_kn_kernel<MT, TA>), dim3(blocks), dim3(SKINNY_KN_THREADS),
+                     0, s, gemm_args(a));
+  return hipGetLastError();
+}
+
+template <int MT, bool TA>
 hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
                          hipStream_t s) {
   const int col_blocks = (a.N + SKINNY_COLS - 1) / SKINNY_COLS;
@@ -278,7 +287,8 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   STORAGE(T, "nt_", false, true)
 
 // Small-M kernels: bm = the most rows of C they take, bn = the columns of C
-// per workgroup.  With B stored N x K every workgroup reads all of A (from
+// per workgroup.  B stored K x N: one pass for up to 4 rows (32 columns per
+// workgroup), K split over workgroups for up to 16 (256 columns).  With B stored N x K every workgroup reads all of A (from
 // the caches), whose traffic grows with M over the few columns a workgroup
 // takes: past 8 rows the MFMA split-K kernels are faster (16 x 4096 x 4096:
 // 26.5 us on 16 rows against 17), so those kernels stop at 8.
@@ -286,6 +296,10 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   {"valu_S" #MT "x256_" PRE "small", SGEMM_VARIANT_VALU, TA, false, MT,     \
    SKINNY_COLS, SKINNY_KC, SKINNY_THREADS, SGEMM_MODE_EDGE,                  \
    SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny<MT, TA>}
+#define SKINNY_KN(MT, PRE, TA)                                               \
+  {"valu_S" #MT "x32_" PRE "small", SGEMM_VARIANT_VALU, TA, false, MT,      \
+   SKINNY_KN_COLS, SKINNY_KN_UNIT, SKINNY_KN_THREADS, SGEMM_MODE_EDGE,       \
+   SGEMM_SCHEDULE_SMALL_M, 0, launch_skinny_kn<MT, TA>}
 #define SKINNY_NT(MT, PRE, TA)                                               \
   {"valu_S" #MT "_" PRE "small", SGEMM_VARIANT_VALU, TA, true, MT,          \
    skinny_nt_rows(MT), SKINNY_NT_PIECE, SKINNY_NT_THREADS, SGEMM_MODE_EDGE,  \
@@ -313,6 +327,8 @@ const KernelDesc kKernels[] = {
     {"valu_V128x128_guarded", SGEMM_VARIANT_VALU, 0, 0, V128x128::BM,
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED,
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, true>},
+    SKINNY_KN(1, "", false), SKINNY_KN(2, "", false), SKINNY_KN(4, "", false),
+    SKINNY_KN(1, "tn_", true), SKINNY_KN(2, "tn_", true), SKINNY_KN(4, "tn_", true),
     SKINNY(4, "", false), SKINNY(8, "", false), SKINNY(16, "", false),
     SKINNY(4, "tn_", true), SKINNY(8, "tn_", true), SKINNY(16, "tn_", true),
     SKINNY_NT(1, "nt_", false), SKINNY_NT(2, "nt_", false), SKINNY_NT(4, "nt_", false),
@@ -357,7 +373,8 @@ bool kernel_fits(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
     if (a.K <= 0 || a.M > k.bm) return false;
     // (the one-pass kernels index columns and k in 32 bits, a piece past K)
     if (k.variant == SGEMM_VARIANT_VALU)
-      return !a.tb || (a.N <= INT_MAX - k.bn && a.K <= INT_MAX - SKINNY_NT_PIECE);
+      return (k.bn != SKINNY_KN_COLS && !a.tb) ||
+             (a.N <= INT_MAX - k.bn && a.K <= INT_MAX - k.bk);
     // MFMA split-K: the edge instance's conditions, and a workspace for at
     // least one set of partial sums
     const size_t part = (size_t)a.M * skinny_ws_stride(a.N) * sizeof(float);
@@ -483,6 +500,20 @@ double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
 // 65536 x 1024 38.5; 4 rows 4096 x 4096 12.5, 11008 x 4096 27.3; 8 rows
 // 4096 x 4096 14.7, 11008 x 4096 33.4, 14336 x 4096 40.6.
 double skinny_cost(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
+  if (!a.tb && k.bn == SKINNY_KN_COLS) {
+    // B stored K x N in one pass (skinny_kn_kernel): ~2.2 us, B at ~5.8
+    // TB/s (5.3 with 4 rows of A) once 2048 waves stream it.  Fitted on
+    // MI355X graph replays: 1 row 4096 x 4096 13.2-13.7 us, 11008 x 4096
+    // 32.1-33.5, 4096 x 14336 41.9-42.5; 4 rows 4096 x 4096 14.8, 11008 x
+    // 4096 35.9.
+    const double wgs = (double)ceil_div(a.N, k.bn);
+    const double units = (double)ceil_div(a.K, SKINNY_KN_UNIT);
+    const double waves = std::min(wgs, (double)c.cus) *
+                         std::min(units, (double)SKINNY_KN_WAVES);
+    const double fill = std::min(1.0, waves / (8.0 * c.cus));
+    const double bw = k.bm <= 2 ? 5.8e12 : 5.3e12;
+    return 2.2 + (double)a.K * a.N * 4 / (bw * fill) * 1e6;
+  }
   if (a.tb) {
     const double wgs = (double)ceil_div(a.N, k.bn);
     const double pieces = (double)ceil_div(a.K, SKINNY_NT_PIECE);
@@ -575,9 +606,9 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
   if (any_variant) variant = SGEMM_VARIANT_MFMA;
   if (variant != SGEMM_VARIANT_MFMA && variant != SGEMM_VARIANT_VALU)
     return SGEMM_ERR_VALUE;
-  // the small-M kernel for these arguments: the cheapest of the vector-ALU
-  // ones (AUTO and VALU variants; the fewest rows that hold M) and the MFMA
-  // split-K ones (AUTO and MFMA)
+  // the small-M kernel for these arguments: the cheapest by the models of
+  // the vector-ALU ones (AUTO and VALU variants) and the MFMA split-K ones
+  // (AUTO and MFMA); on a tie the earlier in the table, i.e. fewer rows
   int skinny = -1;
   double skinny_us = 0.0;
   for (int i = 0; i < kNumKernels; ++i) {
@@ -586,8 +617,6 @@ int make_plan(int variant, const RunArgs& a, const LaunchCtx& ctx, Plan* plan) {
     const bool valu = k.variant == SGEMM_VARIANT_VALU;
     if (valu ? !(any_variant || variant == SGEMM_VARIANT_VALU) : variant != SGEMM_VARIANT_MFMA)
       continue;
-    if (valu && skinny >= 0 && kKernels[skinny].variant == SGEMM_VARIANT_VALU)
-      continue;  // a VALU kernel with fewer rows already fits
     const double us = valu ? skinny_cost(k, a, ctx) : mfma_splitk_cost(k, a, ctx);
     if (skinny < 0 || us < skinny_us) {
       skinny = i;

@@ -406,6 +406,174 @@ __global__ void __launch_bounds__(SKINNY_NT_THREADS, 4) skinny_nt_kernel(GemmArg
   *c = o;
 }
 
+// ---- small M, B stored K x N, in one pass -----------------------------------
+//
+// Row k of B is contiguous along N.  A workgroup of SKINNY_KN_WAVES waves
+// takes SKINNY_KN_COLS columns of C over all of K: each lane takes 4 adjacent
+// columns (16 bytes of a row, 8 lanes per 128-byte line) and, of every unit
+// of 32 rows, the 4 consecutive rows 4g .. 4g+3 of its row group g (8 row
+// groups per wave), so that its 4 k also form one 16-byte piece of each row
+// of A.  The waves split K into contiguous runs of units; each lane keeps
+// MT x 4 sums (its columns times the rows of A).  The 8 row groups' sums meet
+// by recursive halving over the lane bits that select the row group, the
+// waves' through LDS in wave order, and one thread per output applies alpha
+// and beta: every sum is taken in a fixed order, no workspace.
+
+constexpr int SKINNY_KN_WAVES = 16;
+constexpr int SKINNY_KN_THREADS = 64 * SKINNY_KN_WAVES;
+constexpr int SKINNY_KN_COLS = 32;              // columns of C per workgroup
+constexpr int SKINNY_KN_LPR = SKINNY_KN_COLS / 4;  // lanes per row of B
+constexpr int SKINNY_KN_RG = 64 / SKINNY_KN_LPR;   // row groups per wave
+constexpr int SKINNY_KN_UNIT = 4 * SKINNY_KN_RG;   // rows of B per unit
+static_assert(SKINNY_KN_RG == 8, "three halving bits");
+
+// Grid: ceil(N / SKINNY_KN_COLS) workgroups.  MT >= M >= 1, N >= 1,
+// K <= INT_MAX - SKINNY_KN_UNIT.  TA: A stored K x M.
+template <int MT, bool TA>
+__global__ void __launch_bounds__(SKINNY_KN_THREADS, 4) skinny_kn_kernel(GemmArgs g) {
+  constexpr int V = MT * 4;                  // sums per lane: acc[m * 4 + column]
+  constexpr int LOGV = V == 4 ? 2 : V == 8 ? 3 : 4;
+  static_assert(V == 4 || V == 8 || V == 16, "1, 2 or 4 rows of A");
+  constexpr int HALVE = LOGV < 3 ? LOGV : 3;  // halving exchanges of the three
+  constexpr int CF = V >> HALVE;              // sums a lane holds after them
+  // units in flight per wave: two with one row of A (registers allow)
+  constexpr int BATCH = MT == 1 ? 2 : 1;
+  __shared__ float red[SKINNY_KN_WAVES * SKINNY_KN_LPR * V];
+  const int M = g.M, N = g.N, K = g.K;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * SKINNY_KN_COLS;
+  const int cg = lane % SKINNY_KN_LPR, rg = lane / SKINNY_KN_LPR;
+  const int n = n0 + 4 * cg;
+  const int ncl = n < N ? n : N - 1;  // columns past N: clamped loads, never stored
+  const int nleft = N - n;
+  const float* __restrict__ A = g.A;
+  const float* __restrict__ B = g.B;
+  const int lda = g.lda, ldb = g.ldb;
+  int am[MT];  // rows of A past M clamped to the last one
+#pragma unroll
+  for (int m = 0; m < MT; ++m) am[m] = m < M ? m : M - 1;
+  const int nu = K / SKINNY_KN_UNIT + (K % SKINNY_KN_UNIT != 0);
+  const int per = (nu + SKINNY_KN_WAVES - 1) / SKINNY_KN_WAVES;
+  const int u0 = wave * per, u1 = u0 + per < nu ? u0 + per : nu;
+  const bool cols_whole = n0 + SKINNY_KN_COLS <= N;
+
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+  for (int u = u0; u < u1; u += BATCH) {
+    f32x4 b[BATCH][4], a[BATCH][MT];
+    if (cols_whole && u + BATCH <= u1 && (u + BATCH) * SKINNY_KN_UNIT <= K) {
+      // whole units inside N (wave-uniform): plain loads, all issued before
+      // the first multiply-add
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) {
+        const int k = (u + t) * SKINNY_KN_UNIT + 4 * rg;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4u v = *reinterpret_cast<const f32x4u*>(B + (size_t)(k + j) * ldb + n);
+          b[t][j] = f32x4{v[0], v[1], v[2], v[3]};
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (!TA) {
+            const f32x4u v = *reinterpret_cast<const f32x4u*>(A + (size_t)am[m] * lda + k);
+            a[t][m] = f32x4{v[0], v[1], v[2], v[3]};
+          } else {  // A(m, k) = A[k*lda + m]: one element per k
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[t][m][e] = A[(size_t)(k + e) * lda + am[m]];
+          }
+        }
+      }
+    } else {
+      // the last units of K, or columns past N: rows past K are zero (not
+      // loaded), partial rows and pieces of A load from clamped addresses
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) {
+        const int k = (u + t) * SKINNY_KN_UNIT + 4 * rg;
+        const int kleft = u + t < u1 ? K - k : 0;  // rows of B left from k
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          b[t][j] = j < kleft ? skinny_nt_load(B + (size_t)(k + j) * ldb + ncl, nleft)
+                              : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (!TA) {
+            a[t][m] = skinny_nt_load(A + (size_t)am[m] * lda + (kleft > 0 ? k : 0), kleft);
+          } else {
+            a[t][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (kleft > 0) {
+              float h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                h[e] = A[(size_t)(e < kleft ? k + e : k + kleft - 1) * lda + am[m]];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[t][m][e] = e < kleft ? h[e] : 0.0f;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t)
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[m * 4 + e] = fmaf(a[t][m][j], b[t][j][e], acc[m * 4 + e]);
+  }
+
+  // Recursive halving over the row-group bits of the lane (offsets 32, 16,
+  // 8), as in skinny_nt_kernel: a lane keeps the upper half of its sums when
+  // its bit is set and sends the lower half, so after HALVE exchanges it
+  // holds CF sums starting at `base`; exchanges left over (fewer sums than
+  // row groups) add whole sums.
+  int cnt = V, base = 0;
+#pragma unroll
+  for (int off = 32; off >= SKINNY_KN_LPR; off >>= 1) {
+    const bool up = (lane & off) != 0;
+    if (cnt > 1) {
+      const int half = cnt >> 1;
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        if (i < half) {
+          // bitwise selects: a select between two elements of the array
+          // becomes an indexed read of the whole array
+          const unsigned lo = __float_as_uint(acc[i]), hi = __float_as_uint(acc[i + half]);
+          const unsigned msk = up ? 0xFFFFFFFFu : 0u;
+          const float send = __uint_as_float((lo & msk) | (hi & ~msk));
+          const float keep = __uint_as_float((hi & msk) | (lo & ~msk));
+          acc[i] = keep + __shfl_xor(send, off);
+        }
+      }
+      if (up) base += half;
+      cnt = half;
+    } else {
+      acc[0] += __shfl_xor(acc[0], off);
+    }
+  }
+  // after whole-sum exchanges every lane of a pair holds the same sums: the
+  // one whose exchanged row-group bits are zero writes them
+  if ((rg & ((1 << (3 - HALVE)) - 1)) == 0) {
+#pragma unroll
+    for (int i = 0; i < CF; ++i) red[(wave * SKINNY_KN_LPR + cg) * V + base + i] = acc[i];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= SKINNY_KN_LPR * V) return;
+  const int c = t / V, v = t % V;
+  float s = red[c * V + v];
+#pragma unroll
+  for (int w = 1; w < SKINNY_KN_WAVES; ++w) s += red[(w * SKINNY_KN_LPR + c) * V + v];
+  const int m = v / 4, col = n0 + 4 * c + v % 4;
+  if (m >= M || col >= N) return;
+  float* cp = g.C + (size_t)m * g.ldc + col;
+  float o = g.alpha * s;
+  if (g.beta != 0.0f) o = fmaf(g.beta, *cp, o);
+  *cp = o;
+}
+
 // ---- small M on the matrix cores, K split ---------------------------------
 //
 // For a few rows of A (at most one tile row) against a wide B in either

@@ -130,11 +130,14 @@ enum sgemm_mode {
  *   SMALL_M:  M <= the kernel's bm (1, 2, 4, 8 or 16): vector-ALU kernels
  *             that stream B once with 16-byte loads, for decode-like
  *             products.
- *             B stored K x N: 256 columns of C per workgroup, K split over
- *             enough workgroups to give every CU one; with more than one K
- *             range the ranges' sums go to the workspace and a second kernel
- *             adds them in range order and applies alpha and beta
- *             (deterministic); without a workspace (or when it is too
+ *             B stored K x N: either one pass (bm 1, 2 or 4; bn = 32
+ *             columns of C per workgroup over all of K, its waves on
+ *             contiguous runs of K, sums added in a fixed order, no
+ *             workspace) or, bm 4, 8 or 16, 256 columns of C per workgroup
+ *             and K split over enough workgroups to give every CU one; with
+ *             more than one K range the ranges' sums go to the workspace and
+ *             a second kernel adds them in range order and applies alpha and
+ *             beta (deterministic); without a workspace (or when it is too
  *             small) the ranges are merged until they fit, down to one.
  *             B stored N x K (bm 1, 2, 4 or 8): one pass, bn = 8 (bm <= 2)
  *             or 4 columns of C per workgroup over all of K, its waves on

@@ -74,6 +74,8 @@ FP32_CASES = [
      [sg.SGEMM_SCHEDULE_SMALL_M]),
     (wl.Workload("g_onepass", 9206, 4, 4096, 4096, 1.0, 0.5, "uniform"), (False, True),
      [sg.SGEMM_SCHEDULE_SMALL_M]),
+    (wl.Workload("g_onepass_kn", 9207, 1, 4096, 4096, 1.0, 0.5, "uniform"), (False, False),
+     [sg.SGEMM_SCHEDULE_SMALL_M]),
     (wl.Workload("g_two", 9204, 2048, 5504, 2048, 1.0, 0.0, "normal"), (False, False),
      [sg.SGEMM_SCHEDULE_TILES, sg.SGEMM_SCHEDULE_TILES]),
 ]

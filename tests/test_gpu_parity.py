@@ -582,25 +582,51 @@ def test_split_k_plans(handle, shape, tb):
     gu.check_full(ops, gu.run(handle, ops), what=f"split-K plan {shape} normal")
 
 
-@pytest.mark.parametrize("shape,want", [((1, 4096, 4096), "valu_S1_nt_small"),
-                                        ((2, 4096, 4096), "valu_S2_nt_small"),
-                                        ((4, 11008, 4096), "valu_S4_nt_small"),
-                                        ((8, 4096, 4096), "valu_S8_nt_small"),
-                                        ((16, 4096, 4096), "mfma_M32x64_nt_splitk_edge")])
-def test_one_pass_plans(handle, shape, want):
-    """With B stored N x K and a workspace, the planner takes the one-pass
-    vector-ALU kernel up to 8 rows where it measured faster than split K on
-    the matrix cores (1 x 4096 x 4096: 11.9 against 16.0 us), and split K
-    past 8 rows; the planned call is exact on integers."""
+@pytest.mark.parametrize("shape,tb,want", [((1, 4096, 4096), True, "valu_S1_nt_small"),
+                                           ((2, 4096, 4096), True, "valu_S2_nt_small"),
+                                           ((4, 11008, 4096), True, "valu_S4_nt_small"),
+                                           ((8, 4096, 4096), True, "valu_S8_nt_small"),
+                                           ((16, 4096, 4096), True, "mfma_M32x64_nt_splitk_edge"),
+                                           ((1, 4096, 4096), False, "valu_S1x32_small"),
+                                           ((16, 4096, 4096), False, "mfma_M32x64_splitk_edge")])
+def test_one_pass_plans(handle, shape, tb, want):
+    """With a workspace, the planner takes the one-pass vector-ALU kernels
+    where they measured faster than split K on the matrix cores (B stored N
+    x K up to 8 rows: 1 x 4096 x 4096 11.9 against 16.0 us; B stored K x N:
+    13.2-13.7 against 16.9), and split K past their rows; the planned call is
+    exact on integers."""
     M, N, K = shape
     w = wl.Workload("onepass", 7300 + M, M, N, K, 1.0, 0.5, "int4")
-    ops = wl.operands(w, tb=True)
+    ops = wl.operands(w, tb=tb)
     A, B, C = gu.to_device(ops)
     plan = handle.plan(M, N, K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
-                       C.data_ptr(), ops.ldc, transb=True)
+                       C.data_ptr(), ops.ldc, transb=tb)
     assert [sg.sgemm_kernel_name(k) for k, _, _ in plan] == [want]
     gu.check_full(ops, gu.run(handle, ops, dev=(A, B, C)), exact=True,
-                  what=f"one-pass plan {shape}")
+                  what=f"one-pass plan {shape} tb={tb}")
+
+
+@pytest.mark.parametrize("ta", [False, True])
+def test_one_pass_without_workspace(ta):
+    """A handle with no workspace (as sgemm_create gives) plans the one-pass
+    kernel for a few rows against B stored K x N, where split K cannot run;
+    uniform inputs within the bound, integers exact."""
+    h = sg.Handle(workspace=False)
+    try:
+        for M, N, K in ((1, 4096, 4096), (3, 1000, 777), (4, 2050, 4100)):
+            w = wl.Workload("onepassnows", 7400 + M, M, N, K, 1.5, -0.5, "uniform")
+            ops = wl.operands(w, ta=ta)
+            A, B, C = gu.to_device(ops)
+            plan = h.plan(M, N, K, A.data_ptr(), ops.lda, B.data_ptr(), ops.ldb,
+                          C.data_ptr(), ops.ldc, transa=ta)
+            names = [sg.sgemm_kernel_name(k) for k, _, _ in plan]
+            assert len(names) == 1 and "x32_" in names[0] and "small" in names[0], names
+            gu.check_full(ops, gu.run(h, ops, dev=(A, B, C)), what=f"{names} {M}x{N}x{K}")
+            w = wl.Workload("onepassnows", 7500 + M, M, N, K, 1.0, 1.0, "int4")
+            ops = wl.operands(w, ta=ta)
+            gu.check_full(ops, gu.run(h, ops), exact=True, what=f"{names} {M}x{N}x{K} int")
+    finally:
+        h.close()
 
 
 def random_problems(seed, count):
