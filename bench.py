@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3_4096]
                     [--prewarm-s S] [--variant mfma|valu] [--no-cpu-baseline]
                     [--no-per-config] [--lowp all|bf16|f16|fp8|fp8e4m3|fp8e5m2|none]
-                    [--lowp-only] [--lowp-k K]
+                    [--lowp-only] [--lowp-k K] [--operand-fill draws|zeros]
 
 A step is one SGEMM call, C = alpha*A*B + beta*C, on the headline workload
 (M = N = K = 4096, alpha = 1.5, beta = 0.5, uniform [-1, 1) inputs, C
@@ -27,6 +27,9 @@ the headline problem's roofline against the dense matrix-core peak of that
 format, and the other shapes).  --lowp-only --lowp-k K times only the 16/8-bit
 headline problem with K in place of 4096: two such runs under a cycle counter
 give the kernels' cost per K step apart from their fixed cost.
+--operand-fill zeros times the same calls on all-zero A and B: the 16/8-bit
+kernels then run faster (the chip holds a higher clock when fewer operand
+bits toggle), the FP32 kernel does not.
 """
 from __future__ import annotations
 
@@ -265,6 +268,9 @@ def lowp_section(args, sg, rf, wl, torch):
         A = torch.from_numpy(ops.A.view(raw)).cuda().view(tdt[dt])
         B = torch.from_numpy(ops.B.view(raw)).cuda().view(tdt[dt])
         C = torch.from_numpy(ops.C).cuda()
+        if args.operand_fill == "zeros":
+            A.view(torch.uint8).zero_()
+            B.view(torch.uint8).zero_()
         kid = sg.sgemm_lowp_select_kernel(
             codes[dt], int(ta), int(tb), w.M, w.N, w.K, A.data_ptr(), ops.lda,
             B.data_ptr(), ops.ldb, C.data_ptr(), ops.ldc)
@@ -373,6 +379,11 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the timed region, run one plain device copy of this "
                          "many bytes (a reference dispatch for HBM byte counters)")
+    ap.add_argument("--operand-fill", choices=["draws", "zeros"], default="draws",
+                    help="zeros: time every product on all-zero A and B instead of the "
+                         "workloads' draws (the 16/8-bit kernels' time depends on the "
+                         "operand bits through the clock the chip holds; results are "
+                         "not meaningful then)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -402,6 +413,9 @@ def main(argv=None):
             w = dataclasses.replace(w, M=M)
         ops = wl.operands(w, ta=ta, tb=tb)
         dev = [torch.from_numpy(x).cuda() for x in (ops.A, ops.B, ops.C)]
+        if args.operand_fill == "zeros":
+            dev[0].zero_()
+            dev[1].zero_()
         plan = [(args.kernel, 0, w.N)] if args.kernel >= 0 else h.plan(
             w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(), ops.ldb,
             dev[2].data_ptr(), ops.ldc, transa=ta, transb=tb)
@@ -574,6 +588,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
+        "operand_fill": args.operand_fill,
         "pct_of_fp32_peak": round(100.0 * value * 1e9 / rf.PEAK_FP32_FLOPS, 2),
         "prewarm": {"seconds": round(pw_s, 2), "launches": pw_launches},
         "clock": {k: round(v, 3) if isinstance(v, float) else v for k, v in clock.items()},
