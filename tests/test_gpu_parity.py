@@ -356,6 +356,46 @@ def test_large_strides(handle, case):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("tb", [True, False], ids=["b_nk", "b_kn"])
+def test_one_pass_large_strides(tb):
+    """The one-pass small-M kernels address rows of B and C in 64 bits: row
+    offsets past 2^31 elements (B's rows along K or along N, C's rows) give
+    the oracle's result, exact on integers, and C's padding stays untouched.
+    Only the used windows of the multi-GiB buffers are written."""
+    M, N, K = 3, 40, 300
+    name = "valu_S4_nt_small" if tb else "valu_S4x32_small"
+    ldb = (1 << 26) + 5 if tb else (1 << 23) + 3
+    lda, ldc = K + 1, (1 << 30) + 3
+    w = wl.Workload("bigsmall", 5200 + int(tb), M, N, K, 1.5, 0.5, "int4")
+    a = wl.draw(w.cfg_id, wl.ROLE_A, M, K, w.dist)
+    b = wl.draw(w.cfg_id, wl.ROLE_B, K, N, w.dist)  # B(k, n)
+    c = wl.draw(w.cfg_id, wl.ROLE_C, M, N, w.dist)
+    dev = torch.device("cuda", 0)
+    rows_b, cols_b = (N, K) if tb else (K, N)
+    assert (rows_b - 1) * ldb > 2 ** 31 and (M - 1) * ldc > 2 ** 31
+    A = torch.empty((M - 1) * lda + K, device=dev)
+    B = torch.empty((rows_b - 1) * ldb + cols_b, device=dev)
+    C = torch.full(((M - 1) * ldc + N,), float("nan"), device=dev)
+    A.as_strided((M, K), (lda, 1)).copy_(torch.from_numpy(a))
+    B.as_strided((rows_b, cols_b), (ldb, 1)).copy_(torch.from_numpy(b.T.copy() if tb else b))
+    C.as_strided((M, N), (ldc, 1)).copy_(torch.from_numpy(c))
+    h = sg.Handle(workspace=False)
+    try:
+        h.set_kernel({k["name"]: k["id"] for k in KERNELS}[name])
+        h.gemm(A, B, C, w.alpha, w.beta, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc,
+               transb=tb)
+        torch.cuda.synchronize()
+    finally:
+        h.close()
+    got = C.as_strided((M, N), (ldc, 1)).cpu().numpy()
+    R, T = oracle.gemm(M, N, K, w.alpha, a, K, b, N, w.beta, c, N)
+    gu.check(got, R, T, K, w.alpha, w.beta, c, exact=True, what=name)
+    pad = C[N: N + 64].cpu().numpy()
+    assert np.all(np.isnan(pad)), f"{name}: C padding written"
+    del A, B, C
+    torch.cuda.empty_cache()
+
+
 def test_misaligned_base_pointers(handle):
     w = wl.Workload("mis", 5006, 256, 256, 256, 1.0, 0.0, "int4")
     ops = wl.operands(w)
