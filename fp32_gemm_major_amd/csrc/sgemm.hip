@@ -966,8 +966,10 @@ bool lp_fits(const LpKernelDesc& k, const LpRun& a) {
   if (k.dt != a.dt || k.ta != a.ta || k.tb != a.tb) return false;
   if (k.schedule == SGEMM_SCHEDULE_SMALL_M && a.M > k.bm) return false;
   // the one-pass small-M kernels take any K and any alignment, one launch
-  // of ceil(N / bn) workgroups
-  if (k.schedule == SGEMM_SCHEDULE_SMALL_M && !k.split) return a.N <= INT_MAX - k.bn;
+  // of ceil(N / bn) workgroups (columns and k indexed in 32 bits, a few
+  // blocks past N and K)
+  if (k.schedule == SGEMM_SCHEDULE_SMALL_M && !k.split)
+    return a.N <= INT_MAX - k.bn && a.K <= INT_MAX - 1024;
   if (ceil_div(a.M, k.bm) * ceil_div(a.N, k.bn) > INT_MAX) return false;
   switch (k.mode) {
     case SGEMM_MODE_GUARDED:

@@ -196,6 +196,12 @@ def test_select_small_m_one_pass(dt, ta):
                         (1, 8256, 4096, 1)):
         k = _pick(dt, M, N, K, ta=ta, tb=tb)
         assert k["schedule"] == sg.SGEMM_SCHEDULE_TILES, (M, N, K, tb, k["name"])
+    # K within 1024 of 2^31: the one-pass kernel's 32-bit k would pass it
+    big = (1 << 31) - 1000
+    k = _pick(dt, 1, 64, big, ta=ta, tb=1, A=1 << 20, B=1 << 40, C=1 << 46)
+    assert isinstance(k, int) or "_G16x16_" not in k["name"]
+    k = _pick(dt, 1, 64, big - 100, ta=ta, tb=1, A=1 << 20, B=1 << 40, C=1 << 46)
+    assert not isinstance(k, int) and "_G16x16_" in k["name"]
 
 
 def test_diag_chain_argument_errors():
