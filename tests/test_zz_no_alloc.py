@@ -38,7 +38,7 @@ def _call(entry, h, ops, dev):
 # small-M problem whose K ranges keep their partial sums there
 CASES = [(wl.Workload("na_sk", 9100, 64, 4096, 4096, 1.5, 0.5, "uniform"),
           sg.SGEMM_SCHEDULE_STREAM_K),
-         (wl.Workload("na_small", 9101, 3, 2048, 4096, 1.0, 1.0, "int4"),
+         (wl.Workload("na_small", 9101, 3, 2048, 8192, 1.0, 1.0, "int4"),
           sg.SGEMM_SCHEDULE_SMALL_M)]
 
 
@@ -50,6 +50,9 @@ def test_noalloc_matches_run_ex_twice_in_a_row(handle):
         plan = handle.plan(w.M, w.N, w.K, dev[0].data_ptr(), ops.lda, dev[1].data_ptr(),
                            ops.ldb, dev[2].data_ptr(), ops.ldc)
         assert [sg.sgemm_kernel_schedule(k) for k, _, _ in plan] == [schedule], plan
+        if schedule == sg.SGEMM_SCHEDULE_SMALL_M:  # a kernel that splits K, not a one-pass one
+            name = sg.sgemm_kernel_name(plan[0][0])
+            assert "splitk" in name or "x256" in name, name
         c0 = dev[2].clone()
         _call(sg.sgemm_run_ex, handle, ops, dev)
         torch.cuda.synchronize()
