@@ -287,7 +287,7 @@ hipError_t launch_skinny(const RunArgs& a, int, int, const LaunchCtx& c,
   STORAGE(T, "nt_", false, true)
 
 // Small-M kernels: bm = the most rows of C they take, bn = the columns of C
-// per workgroup.  B stored K x N: one pass for up to 4 rows (32 columns per
+// per workgroup.  B stored K x N: one pass for up to 8 rows (32 columns per
 // workgroup), K split over workgroups for up to 16 (256 columns).  With B stored N x K every workgroup reads all of A (from
 // the caches), whose traffic grows with M over the few columns a workgroup
 // takes: past 8 rows the MFMA split-K kernels are faster (16 x 4096 x 4096:
@@ -328,7 +328,8 @@ const KernelDesc kKernels[] = {
      V128x128::BN, V128x128::BK, V128x128::THREADS, SGEMM_MODE_GUARDED,
      SGEMM_SCHEDULE_TILES, 1, launch_valu<V128x128, true>},
     SKINNY_KN(1, "", false), SKINNY_KN(2, "", false), SKINNY_KN(4, "", false),
-    SKINNY_KN(1, "tn_", true), SKINNY_KN(2, "tn_", true), SKINNY_KN(4, "tn_", true),
+    SKINNY_KN(8, "", false), SKINNY_KN(1, "tn_", true), SKINNY_KN(2, "tn_", true),
+    SKINNY_KN(4, "tn_", true), SKINNY_KN(8, "tn_", true),
     SKINNY(4, "", false), SKINNY(8, "", false), SKINNY(16, "", false),
     SKINNY(4, "tn_", true), SKINNY(8, "tn_", true), SKINNY(16, "tn_", true),
     SKINNY_NT(1, "nt_", false), SKINNY_NT(2, "nt_", false), SKINNY_NT(4, "nt_", false),
@@ -502,16 +503,16 @@ double sk_cost(const KernelDesc& k, const RunArgs& a, int cus) {
 double skinny_cost(const KernelDesc& k, const RunArgs& a, const LaunchCtx& c) {
   if (!a.tb && k.bn == SKINNY_KN_COLS) {
     // B stored K x N in one pass (skinny_kn_kernel): ~2.2 us, B at ~5.8
-    // TB/s (5.3 with 4 rows of A) once 2048 waves stream it.  Fitted on
-    // MI355X graph replays: 1 row 4096 x 4096 13.2-13.7 us, 11008 x 4096
-    // 32.1-33.5, 4096 x 14336 41.9-42.5; 4 rows 4096 x 4096 14.8, 11008 x
-    // 4096 35.9.
+    // TB/s (5.3 with 4 rows of A, 4.4 with 8) once 2048 waves stream it.
+    // Fitted on MI355X graph replays: 1 row 4096 x 4096 13.2-13.7 us, 11008
+    // x 4096 32.1-33.5, 4096 x 14336 41.9-42.5; 4 rows 4096 x 4096 14.8,
+    // 11008 x 4096 35.9; 8 rows 4096 x 4096 17.5.
     const double wgs = (double)ceil_div(a.N, k.bn);
     const double units = (double)ceil_div(a.K, SKINNY_KN_UNIT);
     const double waves = std::min(wgs, (double)c.cus) *
                          std::min(units, (double)SKINNY_KN_WAVES);
     const double fill = std::min(1.0, waves / (8.0 * c.cus));
-    const double bw = k.bm <= 2 ? 5.8e12 : 5.3e12;
+    const double bw = k.bm <= 2 ? 5.8e12 : k.bm <= 4 ? 5.3e12 : 4.4e12;
     return 2.2 + (double)a.K * a.N * 4 / (bw * fill) * 1e6;
   }
   if (a.tb) {

@@ -432,8 +432,8 @@ static_assert(SKINNY_KN_RG == 8, "three halving bits");
 template <int MT, bool TA>
 __global__ void __launch_bounds__(SKINNY_KN_THREADS, 4) skinny_kn_kernel(GemmArgs g) {
   constexpr int V = MT * 4;                  // sums per lane: acc[m * 4 + column]
-  constexpr int LOGV = V == 4 ? 2 : V == 8 ? 3 : 4;
-  static_assert(V == 4 || V == 8 || V == 16, "1, 2 or 4 rows of A");
+  constexpr int LOGV = V == 4 ? 2 : V == 8 ? 3 : V == 16 ? 4 : 5;
+  static_assert(V == 4 || V == 8 || V == 16 || V == 32, "1, 2, 4 or 8 rows of A");
   constexpr int HALVE = LOGV < 3 ? LOGV : 3;  // halving exchanges of the three
   constexpr int CF = V >> HALVE;              // sums a lane holds after them
   // units in flight per wave: two with one row of A (registers allow)

@@ -130,7 +130,7 @@ enum sgemm_mode {
  *   SMALL_M:  M <= the kernel's bm (1, 2, 4, 8 or 16): vector-ALU kernels
  *             that stream B once with 16-byte loads, for decode-like
  *             products.
- *             B stored K x N: either one pass (bm 1, 2 or 4; bn = 32
+ *             B stored K x N: either one pass (bm 1, 2, 4 or 8; bn = 32
  *             columns of C per workgroup over all of K, its waves on
  *             contiguous runs of K, sums added in a fixed order, no
  *             workspace) or, bm 4, 8 or 16, 256 columns of C per workgroup

@@ -128,7 +128,7 @@ def test_kernel_table():
         assert k["bm"] > 0 and k["bn"] > 0 and k["bk"] > 0 and k["threads"] % 64 == 0
     # every MFMA tile shape has an aligned, an edge and a guarded instance for
     # each storage; the VALU shape an aligned and a guarded one; the small-M
-    # kernels one edge instance per storage: on the vector ALUs 1, 2 and 4
+    # kernels one edge instance per storage: on the vector ALUs 1, 2, 4 and 8
     # rows (one pass, 32 columns per workgroup) and 4, 8 and 16 rows (K split,
     # 256 columns) with B as stored, 1, 2, 4 and 8 rows with B transposed
     # (one pass, 8 columns per workgroup up to 2 rows, else 4); on the matrix
@@ -139,11 +139,11 @@ def test_kernel_table():
             assert k["bn"] == (8 if k["bm"] <= 2 else 4) and k["threads"] == 512, k
         elif k["variant"] == sg.SGEMM_VARIANT_VALU:
             assert (k["bn"], k["threads"]) == ((32, 1024) if "x32_" in k["name"] else (256, 512)), k
-            assert ("x32_" in k["name"]) == (k["bm"] <= 4 and k["bk"] == 32), k
+            assert ("x32_" in k["name"]) == (k["bk"] == 32), k
     assert sorted((k["bm"], k["transa"], k["transb"], k["mode"], k["variant"]) for k in skinny) == \
         sorted([(m, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_VALU)
                 for a in (0, 1) for b in (0, 1)
-                for m in ((1, 2, 4, 8) if b else (1, 2, 4, 4, 8, 16))] +
+                for m in ((1, 2, 4, 8) if b else (1, 2, 4, 8, 4, 8, 16))] +
                [(64 if a else 32, a, b, sg.SGEMM_MODE_EDGE, sg.SGEMM_VARIANT_MFMA)
                 for a in (0, 1) for b in (0, 1)])
     shapes = {(k["variant"], k["bm"], k["bn"], k["bk"]) for k in table
@@ -324,7 +324,7 @@ def test_plans_follow_measured_winners():
 def test_small_m_plans():
     """A few rows of A against a wide B plan the small-M kernel with the
     fewest rows that hold M, for every storage (up to 16 rows with B as
-    stored, one pass up to 4; 8 with B transposed); more rows or an explicit
+    stored, one pass up to 8; 8 with B transposed); more rows or an explicit
     MFMA variant never do."""
     A, B, C = 0x10000000, 0x20000000, 0x40000000
     def plan(M, N, K, variant=0, ta=0, tb=0):

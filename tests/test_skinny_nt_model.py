@@ -284,7 +284,7 @@ def halving_kn(vals, lpr):
     return [(a[:cnt], b) for a, b in zip(acc, base)]
 
 
-@pytest.mark.parametrize("mt", [1, 2, 4])
+@pytest.mark.parametrize("mt", [1, 2, 4, 8])
 def test_kn_halving_sums(mt):
     V = 4 * mt
     halve = min(V.bit_length() - 1, 3)
@@ -310,16 +310,17 @@ def test_kn_table_matches_model():
     if not KERNELS:
         pytest.skip("library not built")
     assert sorted((k["bm"], k["transa"]) for k in KN_TABLE) == \
-        sorted((m, a) for m in (1, 2, 4) for a in (0, 1))
+        sorted((m, a) for m in (1, 2, 4, 8) for a in (0, 1))
     for k in KN_TABLE:
         assert (k["bk"], k["threads"]) == (KN_UNIT, 64 * KN_WAVES)
 
 
 KN_SHAPES = [(1, 1, 1), (1, 33, 31), (2, 32, 32), (3, 37, 33), (4, 64, 300),
-             (4, 31, 513), (2, 70, 16 * 32 + 5), (1, 5, 2 * 16 * 32 + 64)]
+             (4, 31, 513), (2, 70, 16 * 32 + 5), (1, 5, 2 * 16 * 32 + 64), (8, 40, 777),
+             (7, 33, 65)]
 
 
-@pytest.mark.parametrize("mt,ta", list(itertools.product((1, 2, 4), (False, True))))
+@pytest.mark.parametrize("mt,ta", list(itertools.product((1, 2, 4, 8), (False, True))))
 def test_kn_reads_in_bounds_and_cover_k_once(mt, ta):
     for M, N, K in KN_SHAPES:
         M = min(M, mt)
