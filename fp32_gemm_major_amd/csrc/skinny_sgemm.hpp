@@ -276,6 +276,44 @@ __device__ __forceinline__ f32x4 skinny_nt_load(const float* p, int n) {
   return x;
 }
 
+// Recursive halving of V partial sums per lane over the lane bits from 32
+// down to LOWEST: at the exchange with lane l ^ off, the lane whose bit `off`
+// is set keeps the upper half of its current sums and sends the lower half
+// (its partner the reverse) and adds what it receives, so V sums take V
+// exchanges rather than log2(64 / LOWEST) per sum.  Once a lane holds one sum
+// the remaining exchanges add whole sums.  Afterwards acc[0 .. max(1, V >> n))
+// (n = the exchanges that halved) hold sums number base, base + 1, ..., each
+// added over the lanes that differ from this one in the exchanged bits;
+// returns base.  Every lane adds in the same fixed order.
+template <int V, int LOWEST>
+__device__ __forceinline__ int skinny_halve(float (&acc)[V], int lane) {
+  int cnt = V, base = 0;
+#pragma unroll
+  for (int off = 32; off >= LOWEST; off >>= 1) {
+    const bool up = (lane & off) != 0;
+    if (cnt > 1) {
+      const int half = cnt >> 1;
+#pragma unroll
+      for (int i = 0; i < V / 2; ++i) {
+        if (i < half) {
+          // bitwise selects: a select between two elements of the array
+          // becomes an indexed read of the whole array
+          const unsigned lo = __float_as_uint(acc[i]), hi = __float_as_uint(acc[i + half]);
+          const unsigned msk = up ? 0xFFFFFFFFu : 0u;
+          const float send = __uint_as_float((lo & msk) | (hi & ~msk));
+          const float keep = __uint_as_float((hi & msk) | (lo & ~msk));
+          acc[i] = keep + __shfl_xor(send, off);
+        }
+      }
+      if (up) base += half;
+      cnt = half;
+    } else {
+      acc[0] += __shfl_xor(acc[0], off);
+    }
+  }
+  return base;
+}
+
 // Grid: ceil(N / R) workgroups, workgroup b taking rows [R*b, R*b + R) of B.
 // MT >= M >= 1; N >= 1; K <= INT_MAX - 256.  TA: A stored K x M.
 template <int MT, bool TA>
@@ -361,37 +399,10 @@ __global__ void __launch_bounds__(SKINNY_NT_THREADS, 4) skinny_nt_kernel(GemmArg
         for (int e = 0; e < 4; ++e) acc[m * R + r] = fmaf(a[m][e], b[r][e], acc[m * R + r]);
   }
 
-  // Recursive halving over the 64 lanes: at the exchange with lane l ^ off,
-  // the lane whose bit `off` is set keeps the upper half of its sums and
-  // sends the lower half (its partner the reverse) and adds what it
-  // receives.  After the first log2(V) exchanges (off = 32 down to 64 / V)
-  // lane l holds one sum, number l >> (6 - log2 V), added over the lanes
-  // that differ from it in those bits; the remaining exchanges add it over
-  // the low bits, i.e. the rest of the wave.
-  int cnt = V;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const bool up = (lane & off) != 0;
-    if (cnt > 1) {
-      const int half = cnt >> 1;
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        if (i < half) {
-          // bitwise selects: a select between two elements of the array
-          // becomes an indexed read of the whole array
-          const unsigned lo = __float_as_uint(acc[i]), hi = __float_as_uint(acc[i + half]);
-          const unsigned msk = up ? 0xFFFFFFFFu : 0u;
-          const float send = __uint_as_float((lo & msk) | (hi & ~msk));
-          const float keep = __uint_as_float((hi & msk) | (lo & ~msk));
-          acc[i] = keep + __shfl_xor(send, off);
-        }
-      }
-      cnt = half;
-    } else {
-      acc[0] += __shfl_xor(acc[0], off);
-    }
-  }
-  if ((lane & ((64 >> LOGV) - 1)) == 0) red[wave * V + (lane >> (6 - LOGV))] = acc[0];
+  // the lanes' sums: after the halving lane l holds the wave's sum number
+  // l >> (6 - log2 V) (the lanes of a group of 64 / V hold the same one)
+  const int base = skinny_halve<V, 1>(acc, lane);
+  if ((lane & ((64 >> LOGV) - 1)) == 0) red[wave * V + base] = acc[0];
   __syncthreads();
   const int t = threadIdx.x;
   if (t >= V) return;
@@ -524,35 +535,9 @@ __global__ void __launch_bounds__(SKINNY_KN_THREADS, 4) skinny_kn_kernel(GemmArg
             acc[m * 4 + e] = fmaf(a[t][m][j], b[t][j][e], acc[m * 4 + e]);
   }
 
-  // Recursive halving over the row-group bits of the lane (offsets 32, 16,
-  // 8), as in skinny_nt_kernel: a lane keeps the upper half of its sums when
-  // its bit is set and sends the lower half, so after HALVE exchanges it
-  // holds CF sums starting at `base`; exchanges left over (fewer sums than
-  // row groups) add whole sums.
-  int cnt = V, base = 0;
-#pragma unroll
-  for (int off = 32; off >= SKINNY_KN_LPR; off >>= 1) {
-    const bool up = (lane & off) != 0;
-    if (cnt > 1) {
-      const int half = cnt >> 1;
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        if (i < half) {
-          // bitwise selects: a select between two elements of the array
-          // becomes an indexed read of the whole array
-          const unsigned lo = __float_as_uint(acc[i]), hi = __float_as_uint(acc[i + half]);
-          const unsigned msk = up ? 0xFFFFFFFFu : 0u;
-          const float send = __uint_as_float((lo & msk) | (hi & ~msk));
-          const float keep = __uint_as_float((hi & msk) | (lo & ~msk));
-          acc[i] = keep + __shfl_xor(send, off);
-        }
-      }
-      if (up) base += half;
-      cnt = half;
-    } else {
-      acc[0] += __shfl_xor(acc[0], off);
-    }
-  }
+  // the row groups' sums: halving over the lane bits that select the row
+  // group (offsets 32, 16, 8); afterwards a lane holds CF sums from `base`
+  const int base = skinny_halve<V, SKINNY_KN_LPR>(acc, lane);
   // after whole-sum exchanges every lane of a pair holds the same sums: the
   // one whose exchanged row-group bits are zero writes them
   if ((rg & ((1 << (3 - HALVE)) - 1)) == 0) {
