@@ -20,7 +20,8 @@ Output: one JSON line with the throughput, the kernel's roofline position
 (HIP events around every launch on the stream the kernel runs on), the CPU
 oracle timed on a bounded sample of the same workload, and per-workload
 GFLOPS for the other problem shapes and for decode-like products (1, 16 or 4
-rows of A against B stored N x K, with B's stream rate); then the same
+rows of A against B stored N x K, and one row against B as stored, with B's
+stream rate); then the same
 problems with bfloat16, binary16, E4M3 or E5M2 A and B and FP32 C (the
 "lowp" object: per format,
 the headline problem's roofline against the dense matrix-core peak of that
