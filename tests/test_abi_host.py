@@ -321,6 +321,25 @@ def test_plans_follow_measured_winners():
     assert name(3000, 3000, 3000) == ["mfma_M64x64_edge"]
 
 
+@pytest.mark.parametrize("tb", [0, 1])
+def test_decode_shapes_plan_the_one_pass_kernels(tb):
+    """Without a workspace (the host-only planner), decode-like products with
+    up to 8 rows of A take the one-pass kernel with the fewest rows that hold
+    M, for B stored N x K (valu_S<MT>_nt_small) and as stored
+    (valu_S<MT>x32_small); 9 rows do not."""
+    A, B, C = 0x10000000, 0x20000000, 0x40000000
+    for M, N, K in ((1, 4096, 4096), (2, 4096, 4096), (3, 11008, 4096), (8, 4096, 4096),
+                    (5, 14336, 4096), (1, 4096, 14336)):
+        mt = next(m for m in (1, 2, 4, 8) if m >= M)
+        kid = sg.sgemm_select_kernel(0, M, N, K, A, K, B, K if tb else N, C, N) if not tb \
+            else sg.sgemm_plan(0, M, N, K, A, K, B, K, C, N, transb=1)[0][0]
+        want = f"valu_S{mt}_nt_small" if tb else f"valu_S{mt}x32_small"
+        assert sg.sgemm_kernel_name(kid) == want, (M, N, K, tb, sg.sgemm_kernel_name(kid))
+    plan = sg.sgemm_plan(0, 9, 4096, 4096, A, 4096, B, 4096, C, 4096, transb=tb)
+    name = sg.sgemm_kernel_name(plan[0][0])
+    assert not (name.startswith("valu_S") and name.endswith("_nt_small")) and "x32_" not in name
+
+
 def test_small_m_plans():
     """A few rows of A against a wide B plan the small-M kernel with the
     fewest rows that hold M, for every storage (up to 16 rows with B as
